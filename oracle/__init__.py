@@ -1,0 +1,182 @@
+"""fp64 CPU oracle for kernelized linear attention (TEST INFRASTRUCTURE).
+
+Only tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never imports, links or calls it, and it imports nothing from
+the product.
+
+The arithmetic lives in ``la_oracle.c`` (plain fp64 loops, OpenMP over
+batch x head).  This module only builds that file with gcc and marshals
+numpy arrays into it.  Inputs are fp32 arrays, or bf16 values passed as their
+raw ``uint16`` bit patterns (widened exactly inside the C code).
+
+What each function computes, and the web pages it follows, is stated in
+``la_oracle.h`` / ``la_oracle.c``.  Every function is pinned by
+``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "la_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liblaoracle.so")
+
+F32, BF16 = 0, 1
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile la_oracle.c into liblaoracle.so (gcc -O2 -fopenmp, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wextra", _SRC, "-o", LIB_PATH, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    global _lib
+    _lib = None
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or (
+                os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.lao_num_threads.restype = I
+        lib.lao_forward.argtypes = [P, P, P, I, I64, I64, I64, I64, I64, P, I64, P]
+        lib.lao_causal.argtypes = [P, P, P, I, I64, I64, I64, I64, I64, P, I64, P, P, P]
+        lib.lao_prefix_mask.argtypes = [P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
+        lib.lao_decode_step.argtypes = [P, P, P, I, I64, I64, I64, I64, P, P, P]
+        for f in ("lao_forward", "lao_causal", "lao_prefix_mask", "lao_decode_step"):
+            getattr(lib, f).restype = None
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().lao_num_threads())
+
+
+def _inp(x):
+    """Return (contiguous array, dtype code) for an fp32 or bf16-bits input."""
+    if x is None:
+        return None, F32
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16:
+        return x, BF16
+    raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {x.dtype}")
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(rows, n):
+    if rows is None:
+        return None, n
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if r.ndim != 1 or (r.size and (r.min() < 0 or r.max() >= n or np.any(np.diff(r) <= 0))):
+        raise ValueError("rows must be strictly ascending indices in [0, n)")
+    return r, r.size
+
+
+def _check_gqa(qs, ks, vs):
+    if (len(qs) != 4 or ks != vs or qs[0] != ks[0] or qs[2:] != ks[2:]
+            or ks[1] < 1 or qs[1] % ks[1] != 0):
+        raise ValueError(f"bad shapes q{qs} k{ks} v{vs}: need q [B,Hq,n,d], "
+                         "k = v [B,Hkv,n,d], Hq a multiple of Hkv")
+
+
+def _same_dtype(*codes):
+    if len(set(c for c in codes)) != 1:
+        raise TypeError("q, k and v must share one dtype")
+    return codes[0]
+
+
+def forward(q, k, v, rows=None):
+    """Non-causal normalised linear attention; q [B,Hq,n,d], k/v [B,Hkv,n,d]."""
+    q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
+    dt = _same_dtype(cq, ck, cv)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    _check_gqa(q.shape, k.shape, v.shape)
+    r, nr = _rows(rows, n)
+    out = np.empty((B, Hq, nr, d), dtype=np.float64)
+    _load().lao_forward(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, n, d,
+                        _ptr(r), nr, _ptr(out))
+    return out
+
+
+def causal(q, k, v, rows=None, want_state=False, Hq=None):
+    """Causal normalised linear attention (query i sees keys 0..i).
+
+    q may be None for a state-only pass (then pass Hq for the head count, or
+    it defaults to Hkv).  With want_state the final (S [B,Hkv,d,d],
+    z [B,Hkv,d]) are returned as well.
+    """
+    k, ck = _inp(k); v, cv = _inp(v)
+    B, Hkv, n, d = k.shape
+    if q is not None:
+        q, cq = _inp(q)
+        dt = _same_dtype(cq, ck, cv)
+        Hq = q.shape[1]
+        _check_gqa(q.shape, k.shape, v.shape)
+    else:
+        dt = _same_dtype(ck, cv)
+        Hq = Hq or Hkv
+    r, nr = _rows(rows, n)
+    out = None if q is None else np.empty((B, Hq, nr, d), dtype=np.float64)
+    S = np.empty((B, Hkv, d, d), dtype=np.float64) if want_state else None
+    z = np.empty((B, Hkv, d), dtype=np.float64) if want_state else None
+    _load().lao_causal(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, n, d,
+                       _ptr(r), nr, _ptr(out), _ptr(S), _ptr(z))
+    if want_state:
+        return out, S, z
+    return out
+
+
+def prefix_mask(q, k, v, m, rows=None):
+    """Unnormalised Q K^T V with prefix mask m (query i sees keys 0..m[i])."""
+    q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
+    dt = _same_dtype(cq, ck, cv)
+    B, H, n, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("prefix_mask needs q, k and v of one shape [B,H,n,d]")
+    m = np.ascontiguousarray(np.asarray(m, dtype=np.int64))
+    if m.shape != (n,) or (n and (m.min() < 0 or m.max() >= n)):
+        raise ValueError("m must have shape (n,) with values in [0, n)")
+    r, nr = _rows(rows, n)
+    out = np.empty((B, H, nr, d), dtype=np.float64)
+    _load().lao_prefix_mask(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(m), B, H, n, d,
+                            _ptr(r), nr, _ptr(out))
+    return out
+
+
+def decode_step(q, k, v, S, z):
+    """One decode step: S [B,Hkv,d,d] and z [B,Hkv,d] (float64) update in place."""
+    q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
+    dt = _same_dtype(cq, ck, cv)
+    B, Hq, d = q.shape
+    Hkv = k.shape[1]
+    if (k.shape != v.shape or k.shape[0] != B or k.shape[2] != d or Hq % Hkv
+            or S.shape != (B, Hkv, d, d) or z.shape != (B, Hkv, d)):
+        raise ValueError("decode_step shapes: q [B,Hq,d], k = v [B,Hkv,d], "
+                         "S [B,Hkv,d,d], z [B,Hkv,d]")
+    if S.dtype != np.float64 or z.dtype != np.float64 or not (
+            S.flags.c_contiguous and z.flags.c_contiguous):
+        raise TypeError("S and z must be C-contiguous float64 arrays")
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    _load().lao_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, d,
+                            _ptr(S), _ptr(z), _ptr(out))
+    return out

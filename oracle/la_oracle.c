@@ -1,0 +1,228 @@
+/*
+ * la_oracle.c -- fp64 CPU oracle for kernelized linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the
+ * benchmark).  Plain loops in fp64; no blocking, chunking or reordering
+ * beyond the definitions below.  It shares no code with the HIP library.
+ *
+ * Sources (web pages this follows):
+ *  - "nx_f32_linear_attention.nx source" (nishifamily.com): the feature map
+ *    phi(x) = relu(x) + 1 (function la_phi), the key/value summary
+ *    S = sum_j phi(K_j) (x) V_j and z = sum_j phi(K_j) (the "accumulate
+ *    KV-summary" loop), and out_i = phi(Q_i) S / (phi(Q_i) . z) (the
+ *    "per-query" loop).  S is stored [a][b] row-major, as on that page.
+ *  - "trim-transformer 0.1.0" (pypi.org), section "Masking": query i attends
+ *    to keys 0..m_i; a causal mask is m = arange(n).  Its kernel is
+ *    Attn(Q,K,V) = Q K^T V with no feature map and no normaliser.
+ *  - same page, section "Key-value caching": generation reuses and updates a
+ *    cache token by token, linear in the number of generated tokens.
+ *
+ * Readings where the pages leave a step open:
+ *  - no epsilon in the normaliser (phi >= 1 keeps the denominator >= 1);
+ *  - causal queries see their own key (m_i = i is inclusive);
+ *  - query head h uses key/value head h / (Hq / Hkv) (contiguous groups);
+ *  - the decode step adds the new token to the state before reading it.
+ *
+ * Parity pins for every function here live in tests/test_oracle.py; none is
+ * "parity unpinned".
+ */
+#include "la_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int lao_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Read element idx of an input array, widening fp32 or bf16 bits to fp64. */
+static double rd(const void* p, int dtype, int64_t idx) {
+  if (dtype == LAO_F32) return (double)((const float*)p)[idx];
+  uint32_t bits = ((uint32_t)((const uint16_t*)p)[idx]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* phi(x) = relu(x) + 1; -0 and every negative value map to 1. */
+static double phi(double x) { return (x > 0.0 ? x : 0.0) + 1.0; }
+
+/* Offset of row i of head h in a [B][H][n][d] tensor. */
+static int64_t off4(int64_t b, int64_t h, int64_t i, int64_t H, int64_t n,
+                    int64_t d) {
+  return ((b * H + h) * n + i) * d;
+}
+
+/* out_row = phi(q_row) S / (phi(q_row) . z), with q_row read from q at off. */
+static void normalised_read(const void* q, int dtype, int64_t off, int64_t d,
+                            const double* S, const double* z, double* pq,
+                            double* out_row) {
+  double den = 0.0;
+  for (int64_t a = 0; a < d; ++a) {
+    pq[a] = phi(rd(q, dtype, off + a));
+    den += pq[a] * z[a];
+  }
+  for (int64_t c = 0; c < d; ++c) {
+    double num = 0.0;
+    for (int64_t a = 0; a < d; ++a) num += pq[a] * S[a * d + c];
+    out_row[c] = num / den;
+  }
+}
+
+void lao_forward(const void* q, const void* k, const void* v, int dtype,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
+                 const int64_t* rows, int64_t nrows, double* out) {
+  const int64_t R = Hq / Hkv;
+  const int64_t nr = rows ? nrows : n;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t g = h / R;
+      double* S = (double*)calloc((size_t)(d * d), sizeof(double));
+      double* z = (double*)calloc((size_t)d, sizeof(double));
+      double* pk = (double*)malloc((size_t)d * sizeof(double));
+      /* S = sum_j phi(K_j) (x) V_j, z = sum_j phi(K_j), over all n keys. */
+      for (int64_t j = 0; j < n; ++j) {
+        const int64_t o = off4(b, g, j, Hkv, n, d);
+        for (int64_t a = 0; a < d; ++a) {
+          pk[a] = phi(rd(k, dtype, o + a));
+          z[a] += pk[a];
+        }
+        for (int64_t a = 0; a < d; ++a)
+          for (int64_t c = 0; c < d; ++c)
+            S[a * d + c] += pk[a] * rd(v, dtype, o + c);
+      }
+      for (int64_t r = 0; r < nr; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        normalised_read(q, dtype, off4(b, h, i, Hq, n, d), d, S, z, pk,
+                        out + off4(b, h, r, Hq, nr, d));
+      }
+      free(S);
+      free(z);
+      free(pk);
+    }
+  }
+}
+
+void lao_causal(const void* q, const void* k, const void* v, int dtype,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
+                const int64_t* rows, int64_t nrows, double* out,
+                double* S_final, double* z_final) {
+  const int64_t R = Hq / Hkv;
+  const int64_t nr = rows ? nrows : n;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t g = 0; g < Hkv; ++g) {
+      double* S = (double*)calloc((size_t)(d * d), sizeof(double));
+      double* z = (double*)calloc((size_t)d, sizeof(double));
+      double* pk = (double*)malloc((size_t)d * sizeof(double));
+      int64_t r = 0; /* next selected row */
+      for (int64_t i = 0; i < n; ++i) {
+        /* Add key/value i to the running state, then let query i read it. */
+        const int64_t o = off4(b, g, i, Hkv, n, d);
+        for (int64_t a = 0; a < d; ++a) {
+          pk[a] = phi(rd(k, dtype, o + a));
+          z[a] += pk[a];
+        }
+        for (int64_t a = 0; a < d; ++a)
+          for (int64_t c = 0; c < d; ++c)
+            S[a * d + c] += pk[a] * rd(v, dtype, o + c);
+        if (!q || !out || r >= nr) continue;
+        if (rows && rows[r] != i) continue;
+        for (int64_t h = g * R; h < (g + 1) * R; ++h)
+          normalised_read(q, dtype, off4(b, h, i, Hq, n, d), d, S, z, pk,
+                          out + off4(b, h, r, Hq, nr, d));
+        ++r;
+      }
+      if (S_final) memcpy(S_final + (b * Hkv + g) * d * d, S, (size_t)(d * d) * sizeof(double));
+      if (z_final) memcpy(z_final + (b * Hkv + g) * d, z, (size_t)d * sizeof(double));
+      free(S);
+      free(z);
+      free(pk);
+    }
+  }
+}
+
+void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
+                     const int64_t* m, int64_t B, int64_t H, int64_t n,
+                     int64_t d, const int64_t* rows, int64_t nrows,
+                     double* out) {
+  const int64_t nr = rows ? nrows : n;
+  /* Lists L_t = {selected rows r : m[row r] == t}, as a counting sort. */
+  int64_t* start = (int64_t*)calloc((size_t)(n + 1), sizeof(int64_t));
+  int64_t* list = (int64_t*)malloc((size_t)(nr > 0 ? nr : 1) * sizeof(int64_t));
+  for (int64_t r = 0; r < nr; ++r) start[m[rows ? rows[r] : r] + 1] += 1;
+  for (int64_t t = 0; t < n; ++t) start[t + 1] += start[t];
+  int64_t* fill = (int64_t*)malloc((size_t)(n + 1) * sizeof(int64_t));
+  memcpy(fill, start, (size_t)(n + 1) * sizeof(int64_t));
+  for (int64_t r = 0; r < nr; ++r) list[fill[m[rows ? rows[r] : r]]++] = r;
+  free(fill);
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      double* P = (double*)calloc((size_t)(d * d), sizeof(double));
+      double* kt = (double*)malloc((size_t)d * sizeof(double));
+      for (int64_t t = 0; t < n; ++t) {
+        /* P = sum_{j <= t} K_j (x) V_j */
+        const int64_t o = off4(b, h, t, H, n, d);
+        for (int64_t a = 0; a < d; ++a) kt[a] = rd(k, dtype, o + a);
+        for (int64_t a = 0; a < d; ++a)
+          for (int64_t c = 0; c < d; ++c)
+            P[a * d + c] += kt[a] * rd(v, dtype, o + c);
+        /* every query whose mask ends at t reads Q_i . P */
+        for (int64_t e = start[t]; e < start[t + 1]; ++e) {
+          const int64_t r = list[e];
+          const int64_t i = rows ? rows[r] : r;
+          const int64_t oq = off4(b, h, i, H, n, d);
+          double* dst = out + off4(b, h, r, H, nr, d);
+          for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t a = 0; a < d; ++a)
+              acc += rd(q, dtype, oq + a) * P[a * d + c];
+            dst[c] = acc;
+          }
+        }
+      }
+      free(P);
+      free(kt);
+    }
+  }
+  free(start);
+  free(list);
+}
+
+void lao_decode_step(const void* q, const void* k, const void* v, int dtype,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                     double* S, double* z, double* out) {
+  const int64_t R = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t g = 0; g < Hkv; ++g) {
+      double* Sg = S + (b * Hkv + g) * d * d;
+      double* zg = z + (b * Hkv + g) * d;
+      double* pk = (double*)malloc((size_t)d * sizeof(double));
+      const int64_t o = (b * Hkv + g) * d;
+      /* The new token joins the state first; then its queries read it. */
+      for (int64_t a = 0; a < d; ++a) {
+        pk[a] = phi(rd(k, dtype, o + a));
+        zg[a] += pk[a];
+      }
+      for (int64_t a = 0; a < d; ++a)
+        for (int64_t c = 0; c < d; ++c)
+          Sg[a * d + c] += pk[a] * rd(v, dtype, o + c);
+      for (int64_t h = g * R; h < (g + 1) * R; ++h)
+        normalised_read(q, dtype, (b * Hq + h) * d, d, Sg, zg, pk,
+                        out + (b * Hq + h) * d);
+      free(pk);
+    }
+  }
+}

@@ -1,0 +1,71 @@
+/*
+ * la_oracle.h -- fp64 CPU oracle for kernelized linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
+ * or call this library: only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no header, helper or constant with the
+ * HIP library.
+ *
+ * What it computes (plain definitions, fp64 accumulation):
+ *   phi(x) = max(x, 0) + 1                       (nx_f32_linear_attention.nx,
+ *                                                 function la_phi)
+ *   S = sum_j phi(K_j) (x) V_j,  z = sum_j phi(K_j)
+ *   out_i = (phi(Q_i) S) / (phi(Q_i) . z)          (same page, header comment)
+ * in the non-causal form (all keys), the causal form (keys 0..i), the
+ * unnormalised prefix-mask form out_i = Q_i . sum_{j<=m_i} K_j (x) V_j
+ * (trim-transformer 0.1.0, "Masking"), and one recurrent decode step
+ * (trim-transformer 0.1.0, "Key-value caching").
+ *
+ * Layouts: q [B][Hq][n][d], k and v [B][Hkv][n][d], row-major, d fastest.
+ * Query head h reads key/value head h / (Hq / Hkv).  Inputs are fp32
+ * (dtype LAO_F32) or raw bf16 bit patterns (LAO_BF16), widened exactly.
+ *
+ * Row selection: `rows` (ascending, each in [0, n)) picks which query rows
+ * are produced; out is then [B][Hq][nrows][d].  rows == NULL means all rows
+ * (nrows is ignored and out is [B][Hq][n][d]).
+ */
+#ifndef LA_ORACLE_H
+#define LA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LAO_F32 = 0, LAO_BF16 = 1 };
+
+/* Number of OpenMP threads the oracle uses. */
+int lao_num_threads(void);
+
+/* Non-causal normalised form: every query sees every key. */
+void lao_forward(const void* q, const void* k, const void* v, int dtype,
+                 int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
+                 const int64_t* rows, int64_t nrows, double* out);
+
+/* Causal normalised form: query i sees keys 0..i.  q/out may be NULL (state
+ * only).  S_final [B][Hkv][d][d] and z_final [B][Hkv][d] (either may be NULL)
+ * receive the state after the last token. */
+void lao_causal(const void* q, const void* k, const void* v, int dtype,
+                int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
+                const int64_t* rows, int64_t nrows, double* out,
+                double* S_final, double* z_final);
+
+/* Unnormalised prefix-mask form, identity feature map: query i sees keys
+ * 0..m[i]; m is shared by every batch and head, each m[i] in [0, n). */
+void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
+                     const int64_t* m, int64_t B, int64_t H, int64_t n,
+                     int64_t d, const int64_t* rows, int64_t nrows,
+                     double* out);
+
+/* One recurrent decode step.  S [B][Hkv][d][d] and z [B][Hkv][d] are
+ * updated in place with the new token's key and value, then every query
+ * head reads the updated state.  q [B][Hq][d], k and v [B][Hkv][d],
+ * out [B][Hq][d]. */
+void lao_decode_step(const void* q, const void* k, const void* v, int dtype,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                     double* S, double* z, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

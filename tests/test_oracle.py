@@ -1,0 +1,303 @@
+"""Pins for the fp64 oracle, run on the CPU.
+
+Each test checks the oracle against something other than itself: values the
+pages print for their worked examples (tests/golden/), closed forms,
+invariants of the method, or an independent O(n^2) brute force written here
+with numpy.  They are chosen so that a plausible slip in the oracle (a
+dropped feature map, a transposed state, an exclusive instead of inclusive
+causal prefix, a wrong head mapping, an off-by-one in the prefix mask, a
+decode step that reads before it writes) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import la_inputs as li
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Independent brute force (pairwise weights), numpy fp64.  Not the oracle's
+# algorithm: it never forms the d x d state.
+# ---------------------------------------------------------------------------
+def _relu1(x):
+    return np.maximum(x, 0.0) + 1.0
+
+
+def brute_normalised(q, k, v, causal):
+    q, k, v = (li.to_f32(x).astype(np.float64) for x in (q, k, v))
+    B, Hq, n, d = q.shape
+    R = Hq // k.shape[1]
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // R
+            w = _relu1(q[b, h]) @ _relu1(k[b, g]).T  # w[i, j]
+            if causal:
+                w = np.tril(w)
+            out[b, h] = (w @ v[b, g]) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+def brute_prefix(q, k, v, mask2d_zeroed):
+    """out_i = sum_j [not zeroed(i, j)] (Q_i . K_j) V_j."""
+    q, k, v = (li.to_f32(x).astype(np.float64) for x in (q, k, v))
+    keep = ~np.asarray(mask2d_zeroed, dtype=bool)
+    out = np.empty_like(q)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            a = (q[b, h] @ k[b, h].T) * keep
+            out[b, h] = a @ v[b, h]
+    return out
+
+
+def mask2d_from_m(m):
+    """Two-dimensional mask of a prefix mask: element (i, j) is zeroed iff j > m_i."""
+    m = np.asarray(m)
+    n = m.size
+    return np.arange(n)[None, :] > m[:, None]
+
+
+def rel_rows(a, b):
+    """Largest row-wise max-norm relative error."""
+    num = np.abs(a - b).max(axis=-1)
+    den = np.abs(b).max(axis=-1)
+    return float((num / np.maximum(den, 1e-300)).max())
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed on the nx_f32_linear_attention.nx page.
+# ---------------------------------------------------------------------------
+def test_gate1_uniform_keys_gives_mean_of_v():
+    g = _golden("nx_hand_cases.json")
+    q, k, v = li.hand_case("zero")
+    assert np.array_equal(v[0, 0], np.array(g["V"], dtype=np.float32))
+    out = oracle.forward(q, k, v)[0, 0]
+    np.testing.assert_allclose(out, np.array(g["cases"]["zero"]["out"], float), rtol=0, atol=1e-12)
+
+
+def test_gate2_identity_state_and_output():
+    g = _golden("nx_hand_cases.json")["cases"]["identity"]
+    q, k, v = li.hand_case("identity")
+    assert np.array_equal(q[0, 0], np.array(g["Q"], dtype=np.float32))
+    out = oracle.forward(q, k, v)[0, 0]
+    want = np.array(g["out_num"], float) / g["out_den"]
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-12)
+    # The state after all keys (the causal sweep's final state) is the page's S and z.
+    _, S, z = oracle.causal(q, k, v, want_state=True)
+    np.testing.assert_array_equal(S[0, 0], np.array(g["S"], float))
+    np.testing.assert_array_equal(z[0, 0], np.array(g["z"], float))
+
+
+def test_hand_cases_causal():
+    """Causal reading of the two gates: query 0 sees only key 0 (so it returns
+    V_0 whatever its weight); query 1 sees both keys, as in the non-causal gate."""
+    q, k, v = li.hand_case("zero")
+    np.testing.assert_allclose(oracle.causal(q, k, v)[0, 0], [[2, 4], [4, 6]], atol=1e-12)
+    q, k, v = li.hand_case("identity")
+    np.testing.assert_allclose(oracle.causal(q, k, v)[0, 0],
+                               [[2, 4], [38 / 9, 56 / 9]], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("kind", ["equal_rows", "nonpositive"])
+def test_uniform_key_weights_closed_form(dtype, kind):
+    """If phi(K_j) is the same for every j, every visible key gets the same
+    weight: non-causal out_i = mean(V); causal out_i = mean(V_0..V_i)."""
+    B, Hq, Hkv, n, d = 2, 4, 2, 300, 16
+    rng = np.random.default_rng(5)
+    q = li.as_dtype(rng.standard_normal((B, Hq, n, d), dtype=np.float32), dtype)
+    v = li.as_dtype(rng.standard_normal((B, Hkv, n, d), dtype=np.float32), dtype)
+    if kind == "equal_rows":
+        row = rng.standard_normal(d, dtype=np.float32)
+        k = np.broadcast_to(row, (B, Hkv, n, d)).copy()
+    else:
+        k = -np.abs(rng.standard_normal((B, Hkv, n, d), dtype=np.float32))
+    k = li.as_dtype(k, dtype)
+    vf = li.to_f32(v).astype(np.float64)
+    R = Hq // Hkv
+    mean_all = np.repeat(vf.mean(axis=2, keepdims=True), R, axis=1)
+    mean_prefix = np.repeat(np.cumsum(vf, axis=2) / np.arange(1, n + 1)[None, None, :, None], R, axis=1)
+    np.testing.assert_allclose(oracle.forward(q, k, v), np.broadcast_to(mean_all, (B, Hq, n, d)),
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.causal(q, k, v), mean_prefix, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 17, 1), (2, 4, 2, 33, 3), (1, 2, 2, 40, 8), (1, 6, 3, 19, 5)])
+def test_normalised_forms_match_brute_force(seed, shape):
+    B, Hq, Hkv, n, d = shape
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=seed)
+    np.testing.assert_allclose(oracle.forward(q, k, v), brute_normalised(q, k, v, False),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.causal(q, k, v), brute_normalised(q, k, v, True),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+@pytest.mark.parametrize("kind", ["random", "causal", "full", "first"])
+def test_prefix_mask_matches_brute_force(seed, kind):
+    B, H, n, d = 2, 3, 37, 6
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=seed)
+    m = li.mask(n, kind, rng=rng)
+    got = oracle.prefix_mask(q, k, v, m)
+    np.testing.assert_allclose(got, brute_prefix(q, k, v, mask2d_from_m(m)), rtol=1e-11, atol=1e-11)
+
+
+def test_prefix_mask_page_example():
+    """m = [2, 0, 1] against the page's own two-dimensional mask."""
+    g = _golden("trim_mask_example.json")
+    m = np.array(g["m"], dtype=np.int64)
+    page_mask = np.array(g["mask2d_true_means_zeroed"], dtype=bool)
+    assert np.array_equal(mask2d_from_m(m), page_mask)
+    q, k, v, _ = li.qkv(1, 2, 2, 3, 4, li.F32, seed=11)
+    np.testing.assert_allclose(oracle.prefix_mask(q, k, v, m), brute_prefix(q, k, v, page_mask),
+                               rtol=1e-12, atol=1e-12)
+    # arange(n) is the causal mask: its 2-D form keeps exactly the lower triangle.
+    assert np.array_equal(~mask2d_from_m(li.mask(5, "causal")), np.tril(np.ones((5, 5), bool)))
+
+
+def test_cross_form_identities():
+    """Causal normalised = num/den of the prefix form with m = arange(n) on
+    (phi(Q), phi(K), [V | 1]); non-causal = the same with m_i = n - 1."""
+    B, Hq, n, d = 2, 2, 29, 5
+    q, k, v, _ = li.qkv(B, Hq, Hq, n, d, li.F32, seed=4)
+    # inputs on a 2^-8 grid, so that phi(x) = relu(x) + 1 is exact in fp32
+    q, k = (np.round(x * 256) / 256 for x in (q, k))
+    q, k = q.astype(np.float32), k.astype(np.float32)
+    pad = lambda x: np.concatenate([x, np.zeros(x.shape[:-1] + (1,), np.float32)], -1)
+    fq = pad(_relu1(q).astype(np.float32))
+    fk = pad(_relu1(k).astype(np.float32))
+    v1 = np.concatenate([v, np.ones(v.shape[:-1] + (1,), np.float32)], -1)
+    for kind, ref in (("causal", oracle.causal(q, k, v)), ("full", oracle.forward(q, k, v))):
+        nd = oracle.prefix_mask(fq, fk, v1, li.mask(n, kind))
+        np.testing.assert_allclose(nd[..., :d] / nd[..., d:], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_permutation_and_prefix_invariance():
+    B, Hq, Hkv, n, d = 1, 2, 1, 50, 7
+    q, k, v, rng = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=9)
+    perm = rng.permutation(n)
+    np.testing.assert_allclose(oracle.forward(q, k[:, :, perm], v[:, :, perm]),
+                               oracle.forward(q, k, v), rtol=1e-12, atol=1e-13)
+    full = oracle.causal(q, k, v)
+    for n2 in (1, 17, 49):
+        part = oracle.causal(q[:, :, :n2].copy(), k[:, :, :n2].copy(), v[:, :, :n2].copy())
+        np.testing.assert_allclose(part, full[:, :, :n2], rtol=1e-13, atol=1e-14)
+
+
+def test_linear_in_v():
+    B, Hq, n, d = 1, 1, 40, 6
+    q, k, v1, rng = li.qkv(B, Hq, Hq, n, d, li.F32, seed=12)
+    v2 = rng.standard_normal(v1.shape, dtype=np.float32)
+    for f in (oracle.forward, oracle.causal):
+        lhs = f(q, k, (v1 + 2 * v2).astype(np.float32))
+        rhs = f(q, k, v1) + 2 * f(q, k, v2)
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-6, atol=1e-6)
+
+
+def test_d1_output_does_not_depend_on_q():
+    """With d = 1 phi(q) cancels: out_i = sum_j phi(k_j) v_j / sum_j phi(k_j)."""
+    B, H, n = 1, 1, 64
+    _, k, v, rng = li.qkv(B, H, H, n, 1, li.F32, seed=2)
+    q1 = rng.standard_normal((B, H, n, 1), dtype=np.float32)
+    q2 = 10 * rng.standard_normal((B, H, n, 1), dtype=np.float32)
+    pk = _relu1(k[0, 0, :, 0].astype(np.float64))
+    vv = v[0, 0, :, 0].astype(np.float64)
+    want_causal = np.cumsum(pk * vv) / np.cumsum(pk)
+    for q in (q1, q2):
+        np.testing.assert_allclose(oracle.forward(q, k, v)[0, 0, :, 0],
+                                   np.full(n, want_causal[-1]), rtol=1e-12)
+        np.testing.assert_allclose(oracle.causal(q, k, v)[0, 0, :, 0], want_causal, rtol=1e-12)
+
+
+def test_outputs_are_convex_combinations():
+    B, Hq, n, d = 2, 2, 120, 8
+    q, k, v, _ = li.qkv(B, Hq, Hq, n, d, li.F32, seed=21, scaled=True)
+    vf = v.astype(np.float64)
+    out = oracle.forward(q, k, v)
+    assert np.all(out <= vf.max(axis=2, keepdims=True) + 1e-12)
+    assert np.all(out >= vf.min(axis=2, keepdims=True) - 1e-12)
+    outc = oracle.causal(q, k, v)
+    assert np.all(outc <= np.maximum.accumulate(vf, axis=2) + 1e-12)
+    assert np.all(outc >= np.minimum.accumulate(vf, axis=2) - 1e-12)
+
+
+def test_gqa_equals_repeated_kv_heads():
+    B, Hq, Hkv, n, d = 2, 6, 2, 31, 4
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=8)
+    kr = np.repeat(k, Hq // Hkv, axis=1)  # head h -> kv head h // (Hq/Hkv)
+    vr = np.repeat(v, Hq // Hkv, axis=1)
+    np.testing.assert_array_equal(oracle.forward(q, k, v), oracle.forward(q, kr, vr))
+    np.testing.assert_array_equal(oracle.causal(q, k, v), oracle.causal(q, kr, vr))
+
+
+def test_bf16_inputs_are_widened_exactly():
+    q, k, v, _ = li.qkv(1, 2, 1, 23, 9, li.BF16, seed=3)
+    qf, kf, vf = (li.to_f32(x) for x in (q, k, v))
+    np.testing.assert_array_equal(oracle.forward(q, k, v), oracle.forward(qf, kf, vf))
+    np.testing.assert_array_equal(oracle.causal(q, k, v), oracle.causal(qf, kf, vf))
+    m = li.mask(23, "random", seed=1)
+    q1, qf1 = q[:, :1].copy(), qf[:, :1].copy()
+    np.testing.assert_array_equal(oracle.prefix_mask(q1, k, v, m), oracle.prefix_mask(qf1, kf, vf, m))
+
+
+def test_row_selection_matches_full_output():
+    B, Hq, Hkv, n, d = 2, 4, 2, 45, 5
+    q, k, v, rng = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=13)
+    rows = np.array([0, 7, 8, 30, 44])
+    np.testing.assert_array_equal(oracle.forward(q, k, v, rows=rows), oracle.forward(q, k, v)[:, :, rows])
+    np.testing.assert_array_equal(oracle.causal(q, k, v, rows=rows), oracle.causal(q, k, v)[:, :, rows])
+    qh, kh, vh = q[:, :2].copy(), k[:, :2].copy(), v[:, :2].copy()
+    m = li.mask(n, "random", rng=rng)
+    np.testing.assert_array_equal(oracle.prefix_mask(qh, kh, vh, m, rows=rows),
+                                  oracle.prefix_mask(qh, kh, vh, m)[:, :, rows])
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_decode_steps_continue_the_causal_pass(dtype):
+    """Causal over n tokens == causal state over the first n - T tokens, then T
+    decode steps (each adds its token before its queries read the state)."""
+    B, Hq, Hkv, n, d, T = 2, 4, 2, 24, 6, 5
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=17)
+    full, S_full, z_full = oracle.causal(q, k, v, want_state=True)
+    _, S, z = oracle.causal(None, k[:, :, :n - T].copy(), v[:, :, :n - T].copy(), want_state=True, Hq=Hq)
+    for t in range(n - T, n):
+        out = oracle.decode_step(q[:, :, t].copy(), k[:, :, t].copy(), v[:, :, t].copy(), S, z)
+        np.testing.assert_allclose(out, full[:, :, t], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S, S_full, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(z, z_full, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_step_matches_brute_force():
+    """One decode step from an empty state over a single token equals the
+    brute-force causal output of a length-1 sequence (which is V_0)."""
+    B, Hq, Hkv, d = 3, 4, 2, 5
+    q, k, v, _ = li.qkv(B, Hq, Hkv, 1, d, li.F32, seed=19)
+    S = np.zeros((B, Hkv, d, d)); z = np.zeros((B, Hkv, d))
+    out = oracle.decode_step(q[:, :, 0].copy(), k[:, :, 0].copy(), v[:, :, 0].copy(), S, z)
+    np.testing.assert_allclose(out, np.repeat(v[:, :, 0], Hq // Hkv, axis=1), rtol=1e-12)
+    np.testing.assert_allclose(z, _relu1(k[:, :, 0].astype(np.float64)), rtol=0)
+
+
+def test_bf16_rounding_helper_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3, 0.0, -0.0], dtype=np.float32)
+    bits = li.f32_to_bf16_bits(x)
+    back = li.bf16_bits_to_f32(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa -> 1.0
+    # 1 + 3*2^-8 is a tie between 1 + 2^-7 and 1 + 2^-6: even -> 1 + 2^-6
+    np.testing.assert_array_equal(back[:4], np.array([1.0, 1.0, 1.015625, -2.5], np.float32))
+    assert abs(back[4] - 3.0e-3) <= 3.0e-3 * 2 ** -8
+    assert np.array_equal(bits[5:], np.array([0x0000, 0x8000], np.uint16))
