@@ -29,9 +29,11 @@ BF16 = "bf16"
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-    return b.astype(np.uint16)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 rounding helper expects finite values")
+    b = x.view(np.uint32)
+    # finite values stay below 0xFF800000, so adding at most 0x8000 cannot wrap
+    return ((b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

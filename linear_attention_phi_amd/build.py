@@ -1,0 +1,50 @@
+"""Build liblaphi.so (the C-ABI HIP library) in-tree for gfx950.
+
+    python -m linear_attention_phi_amd.build
+
+Every HIP source is compiled with hipcc for gfx950 only, with packed-fp32
+instructions disabled on the device (-Xclang -target-feature -Xclang
+-packed-fp32-ops): the kernels use plain fp32 arithmetic and MFMA only.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "liblaphi.so")
+ARCH = "gfx950"
+
+SOURCES = ["la_api.cpp", "la_kernels.hip"]
+
+
+def command(out: str = LIB) -> list[str]:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Wall", "-Wno-unused-function",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    cmd = command(LIB + ".tmp")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 device feature and says so
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if err.strip() and verbose:
+        print(err, file=sys.stderr)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,243 @@
+// la_api.cpp -- the C ABI declared in include/la.h: argument checks,
+// workspace sizing and the choice of chunk / segment sizes.  Host-only C++:
+// every check runs before anything is enqueued, and no HIP call is made on an
+// error path (so the checks also run on a machine without a GPU).
+#include "la.h"
+
+#include <stdint.h>
+
+#include "la_internal.h"
+
+namespace la_internal {
+
+int default_chunk(int elem_bytes, int DP) {
+  return chunk_fits(elem_bytes, DP, 64) ? 64 : 32;
+}
+
+// Segments: about kTargetGroups workgroups per pass, so that the 256 CUs each
+// get several, while each workgroup still walks a run of chunks.
+static constexpr int64_t kTargetGroups = 1024;
+
+Plan make_plan(int op, int64_t B, int64_t Hkv, int64_t n, int64_t d, int elem_bytes, int chunk) {
+  (void)op;
+  Plan p;
+  p.DP = padded_dim(d);
+  p.C = chunk;
+  p.nchunks = (n + chunk - 1) / chunk;
+  const int64_t units = B * Hkv * p.nchunks;
+  int64_t G = (units + kTargetGroups - 1) / kTargetGroups;
+  if (G < 1) G = 1;
+  if (G > p.nchunks) G = p.nchunks;
+  p.G = G;
+  p.nseg = (p.nchunks + G - 1) / G;
+  (void)elem_bytes;
+  return p;
+}
+
+size_t state_bytes(const Plan& p, int64_t B, int64_t Hkv) {
+  const size_t slot = ((size_t)p.DP * p.DP + p.DP) * sizeof(float);
+  return (size_t)B * Hkv * (size_t)(p.nseg + 1) * slot;
+}
+
+size_t bucket_bytes(int64_t n, int C) {
+  const int64_t nchunks = (n + C - 1) / C;
+  return (size_t)(nchunks + 1 + n) * sizeof(int);
+}
+
+}  // namespace la_internal
+
+using namespace la_internal;
+
+namespace {
+
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+int elem_bytes(la_dtype dt) { return dt == LA_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  if (!a || !b || abytes == 0 || bbytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// Sizes shared by the three forward forms.  Returns LA_OK or an error.
+la_status check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dt) {
+  if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || n < 1 || d < 1 || d > kMaxD) return LA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return LA_ERR_SHAPE;
+  if (n >= ((int64_t)1 << 31)) return LA_ERR_SHAPE;
+  // element counts must stay well inside int64 (and byte counts inside size_t)
+  const int64_t lim = (int64_t)1 << 40;
+  if (B > lim / Hq || B * Hq > lim / n || B * Hq * n > lim / d) return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
+la_status resolve_chunk(int32_t chunk, la_dtype dt, int64_t d, int* C) {
+  const int DP = padded_dim(d);
+  const int eb = elem_bytes(dt);
+  int c = chunk == 0 ? default_chunk(eb, DP) : chunk;
+  if (c != 32 && c != 64 && c != 128) return LA_ERR_UNSUPPORTED;
+  if (!chunk_fits(eb, DP, c)) return LA_ERR_UNSUPPORTED;
+  *C = c;
+  return LA_OK;
+}
+
+size_t required_ws(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dt, int C,
+                   Plan* out_plan) {
+  (void)Hq;
+  const Plan p = make_plan(op, B, Hkv, n, d, elem_bytes(dt), C);
+  if (out_plan) *out_plan = p;
+  size_t bytes = state_bytes(p, B, Hkv);
+  if (op == LA_OP_PREFIX_MASK) bytes += bucket_bytes(n, C);
+  return bytes;
+}
+
+la_status check_grid(const Plan& p, int64_t B, int64_t Hkv) {
+  if (B * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
+la_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return LA_OK;
+  if (!ws || ws_bytes < need) return LA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LA_ERR_ALIGN;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_str(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL: return "LA_ERR_NULL: a required pointer is NULL";
+    case LA_ERR_SHAPE: return "LA_ERR_SHAPE: a size is out of range or inconsistent";
+    case LA_ERR_DTYPE: return "LA_ERR_DTYPE: unknown dtype code";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: chunk size not offered for this dtype / head dim";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+    case LA_ERR_ALIGN: return "LA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps an input";
+    case LA_ERR_LAUNCH: return "LA_ERR_LAUNCH: the HIP runtime rejected a launch";
+    default: return "unknown la_status";
+  }
+}
+
+size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dtype,
+                          int32_t chunk) {
+  if (op != LA_OP_FORWARD && op != LA_OP_CAUSAL && op != LA_OP_PREFIX_MASK) return 0;
+  if (check_sizes(B, Hq, Hkv, n, d, dtype) != LA_OK) return 0;
+  int C = 0;
+  if (op == LA_OP_FORWARD) {
+    C = default_chunk(elem_bytes(dtype), padded_dim(d));
+  } else if (resolve_chunk(chunk, dtype, d, &C) != LA_OK) {
+    return 0;
+  }
+  if (op == LA_OP_PREFIX_MASK && (Hq != Hkv || (n + C - 1) / C > kMaxBuckets)) return 0;
+  return required_ws(op, B, Hq, Hkv, n, d, dtype, C, nullptr);
+}
+
+la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                     int64_t d, la_dtype dtype, void* out, void* ws, size_t ws_bytes, void* stream) {
+  la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
+  if (st != LA_OK) return st;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  const size_t eb = elem_bytes(dtype);
+  const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb)) return LA_ERR_ALIAS;
+  const int C = default_chunk((int)eb, padded_dim(d));
+  Plan p;
+  const size_t need = required_ws(LA_OP_FORWARD, B, Hq, Hkv, n, d, dtype, C, &p);
+  if ((st = check_grid(p, B, Hkv)) != LA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
+  if (overlaps(ws, need, out, qb) || overlaps(ws, need, q, qb) || overlaps(ws, need, k, kvb) ||
+      overlaps(ws, need, v, kvb))
+    return LA_ERR_ALIAS;
+  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream};
+  return launch_forward(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_causal_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                            int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out, float* S_final,
+                            float* z_final, void* ws, size_t ws_bytes, void* stream) {
+  la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
+  if (st != LA_OK) return st;
+  if (!k || !v) return LA_ERR_NULL;
+  if ((q == nullptr) != (out == nullptr)) return LA_ERR_NULL;
+  if (!q && !S_final && !z_final) return LA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || (q && !aligned16(q)) || (out && !aligned16(out)) ||
+      (S_final && !aligned16(S_final)) || (z_final && !aligned16(z_final)))
+    return LA_ERR_ALIGN;
+  int C = 0;
+  if ((st = resolve_chunk(chunk, dtype, d, &C)) != LA_OK) return st;
+  const size_t eb = elem_bytes(dtype);
+  const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
+  const size_t sb = (size_t)(B * Hkv * d * d) * sizeof(float), zb = (size_t)(B * Hkv * d) * sizeof(float);
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb)) return LA_ERR_ALIAS;
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {qb, kvb, kvb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(S_final, sb, ins[i], inb[i]) || overlaps(z_final, zb, ins[i], inb[i])) return LA_ERR_ALIAS;
+  if (overlaps(S_final, sb, out, qb) || overlaps(z_final, zb, out, qb) || overlaps(S_final, sb, z_final, zb))
+    return LA_ERR_ALIAS;
+  Plan p;
+  const size_t need = required_ws(LA_OP_CAUSAL, B, Hq, Hkv, n, d, dtype, C, &p);
+  if ((st = check_grid(p, B, Hkv)) != LA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(ws, need, ins[i], inb[i])) return LA_ERR_ALIAS;
+  if (overlaps(ws, need, out, qb) || overlaps(ws, need, S_final, sb) || overlaps(ws, need, z_final, zb))
+    return LA_ERR_ALIAS;
+  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream};
+  return launch_causal(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, const int64_t* m, int64_t B,
+                                 int64_t H, int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  la_status st = check_sizes(B, H, H, n, d, dtype);
+  if (st != LA_OK) return st;
+  if (!q || !k || !v || !m || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(m) || !aligned16(out)) return LA_ERR_ALIGN;
+  int C = 0;
+  if ((st = resolve_chunk(chunk, dtype, d, &C)) != LA_OK) return st;
+  if ((n + C - 1) / C > kMaxBuckets) return LA_ERR_UNSUPPORTED;
+  const size_t eb = elem_bytes(dtype);
+  const size_t tb = (size_t)(B * H * n * d) * eb, mb = (size_t)n * sizeof(int64_t);
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) || overlaps(out, tb, m, mb))
+    return LA_ERR_ALIAS;
+  Plan p;
+  const size_t need = required_ws(LA_OP_PREFIX_MASK, B, H, H, n, d, dtype, C, &p);
+  if ((st = check_grid(p, B, H)) != LA_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
+  if (overlaps(ws, need, q, tb) || overlaps(ws, need, k, tb) || overlaps(ws, need, v, tb) ||
+      overlaps(ws, need, m, mb) || overlaps(ws, need, out, tb))
+    return LA_ERR_ALIAS;
+  Fwd a{q, k, v, out, B, H, H, n, d, (int)dtype, m, nullptr, nullptr, ws, stream};
+  return launch_prefix(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t d, la_dtype dtype, float* S, float* z, void* out, void* stream) {
+  la_status st = check_sizes(B, Hq, Hkv, 1, d, dtype);
+  if (st != LA_OK) return st;
+  if (B * Hkv >= kMaxGrid) return LA_ERR_SHAPE;
+  if (!q || !k || !v || !S || !z || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z) || !aligned16(out))
+    return LA_ERR_ALIGN;
+  const size_t eb = elem_bytes(dtype);
+  const size_t qb = (size_t)(B * Hq * d) * eb, kvb = (size_t)(B * Hkv * d) * eb;
+  const size_t sb = (size_t)(B * Hkv * d * d) * sizeof(float), zb = (size_t)(B * Hkv * d) * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {qb, kvb, kvb};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(out, qb, ins[i], inb[i]) || overlaps(S, sb, ins[i], inb[i]) || overlaps(z, zb, ins[i], inb[i]))
+      return LA_ERR_ALIAS;
+  if (overlaps(out, qb, S, sb) || overlaps(out, qb, z, zb) || overlaps(S, sb, z, zb)) return LA_ERR_ALIAS;
+  return launch_decode(q, k, v, B, Hq, Hkv, d, (int)dtype, S, z, out, stream) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// la_internal.h -- interface between the host-only API layer (la_api.cpp:
+// argument checks, workspace sizing) and the HIP launchers (la_kernels.hip).
+// No HIP type appears here, so the API layer builds without HIP headers.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la_internal {
+
+constexpr int kMaxD = 128;
+
+// Feature dimension padded to the 32-wide MFMA tile.
+inline int padded_dim(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
+
+// Static LDS bytes of the chunk kernel (k_out) for (element bytes, padded
+// dim, chunk): sQ and sK [C][DP+4], sKT and sVT [DP][C+4], sST [DP][DP+4],
+// sP [C][C+4] in the element type, plus z [DP] in fp32.  A (dtype, chunk)
+// pair is offered only when this fits in one CU's 160 KiB of LDS.
+constexpr size_t chunk_lds_bytes(int eb, int DP, int C) {
+  return (size_t)eb * (2 * C * (DP + 4) + 2 * DP * (C + 4) + DP * (DP + 4) + C * (C + 4)) + 4 * (size_t)DP;
+}
+constexpr size_t kLdsLimit = 160 * 1024;
+constexpr bool chunk_fits(int eb, int DP, int C) { return chunk_lds_bytes(eb, DP, C) <= kLdsLimit; }
+int default_chunk(int elem_bytes, int DP);
+
+// The prefix form sorts queries into ceil(n / C) buckets held in LDS.
+constexpr int64_t kMaxBuckets = 16383;
+
+// How a causal / prefix / non-causal pass splits each head's chunks into
+// segments (one workgroup per segment and head).
+struct Plan {
+  int DP;        // padded feature dim
+  int C;         // chunk length
+  int64_t nchunks;
+  int64_t G;     // chunks per segment
+  int64_t nseg;  // segments per head
+};
+Plan make_plan(int op, int64_t B, int64_t Hkv, int64_t n, int64_t d, int elem_bytes, int chunk);
+
+// Workspace layout (bytes) for a plan.
+size_t state_bytes(const Plan& p, int64_t B, int64_t Hkv);  // fp32 segment states
+size_t bucket_bytes(int64_t n, int C);                        // prefix-mask bucketing
+
+struct Fwd {
+  const void* q; const void* k; const void* v; void* out;
+  int64_t B, Hq, Hkv, n, d;
+  int dtype;
+  const int64_t* m;      // prefix form only
+  float* S_final; float* z_final;
+  void* ws;
+  void* stream;
+};
+
+// Each returns 0 on success, else a nonzero HIP error code.
+int launch_forward(const Fwd& a, const Plan& p);
+int launch_causal(const Fwd& a, const Plan& p);
+int launch_prefix(const Fwd& a, const Plan& p);
+int launch_decode(const void* q, const void* k, const void* v, int64_t B,
+                  int64_t Hq, int64_t Hkv, int64_t d, int dtype, float* S,
+                  float* z, void* out, void* stream);
+
+}  // namespace la_internal

@@ -1,0 +1,763 @@
+// la_kernels.hip -- gfx950 (MI355X) kernels for kernelized linear attention.
+//
+// Method (nx_f32_linear_attention.nx source: function la_phi, the
+// "accumulate KV-summary" loop and the "per-query" loop): with
+// phi(x) = relu(x) + 1,  S = sum_j phi(K_j) (x) V_j,  z = sum_j phi(K_j),
+// out_i = phi(Q_i) S / (phi(Q_i) . z).  The causal and prefix-mask forms
+// (trim-transformer 0.1.0, "Masking") restrict query i to keys 0..m_i.
+//
+// Work decomposition (per batch x key/value head, "bh"):
+//   tokens are cut into chunks of C rows; G consecutive chunks form a segment,
+//   and one 256-thread workgroup owns one segment of one head.
+//   k_state : per segment, Delta S = sum_c phi(K_c)^T V_c and Delta z on MFMA
+//             -> fp32 segment aggregate in the workspace.
+//   k_scan  : per head, exclusive prefix over the segment aggregates (fixed
+//             sequential order, so results are bit-reproducible), plus the
+//             total (non-causal S, and the causal final state).
+//   k_out   : per segment, walks its chunks in order carrying S in MFMA
+//             accumulators: out_c = phi(Q_c) S_prev + tril(phi(Q_c) phi(K_c)^T) V_c,
+//             den_c likewise, division fused in the epilogue; then
+//             S += phi(K_c)^T V_c.  The prefix form gathers the queries whose
+//             mask ends inside chunk c (a counting sort by floor(m_i / C)).
+//   k_out_nc: non-causal output: phi(Q) S_total / (phi(Q) . z_total).
+//   k_decode: one recurrent step, S += phi(k) (x) v, then out per query head.
+//
+// MFMA conventions (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2_f32
+// for fp32).  Every operand matrix lives in LDS row-major with the
+// *non-contracted* index as the row and the contracted index k contiguous.
+// For a 32x32 product block and a 16-wide k block kb, lane l (row r = l % 32,
+// half h = l / 32) reads the 8 values at k = 16kb + 4h + {0..3} and
+// 16kb + 8 + 4h + {0..3}.  A and B use this same k assignment, which is all a
+// contraction needs.  The accumulator of a block with rows m and columns n
+// holds, in lane l, column n = l % 32 and rows m = 8q + 4h + s in register
+// 4q + s; written back to LDS "transposed" (row n, four contiguous m per q),
+// it is directly readable as an operand whose k index is m.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la_internal.h"
+
+namespace {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int NT = 256;  // threads per workgroup
+constexpr int NW = 4;    // waves per workgroup
+constexpr int PAD = 4;   // LDS row padding (elements): 8-byte (bf16) / 16-byte
+                         // (fp32) fragment reads of 32 rows hit distinct banks
+
+enum Form { CAUSAL = 0, PREFIX = 1 };
+
+__device__ __forceinline__ float phi_f(float x) { return fmaxf(x, 0.0f) + 1.0f; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T cvt(float x);
+template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }
+
+// ---------------------------------------------------------------- fragments
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ void ld_frag(Frag<bf16>& f, const bf16* p) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 8);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void ld_frag(Frag<float>& f, const float* p) {
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 8);
+}
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[u], b.lo[u], acc, 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[u], b.hi[u], acc, 0, 0, 0);
+}
+
+// acc[m][n] += sum_k A[m][k] B[n][k] over NKB k-blocks of 16, with A and B
+// pointing at row 0 / column k0 of their 32-row blocks in LDS.
+template <typename T, int NKB>
+__device__ __forceinline__ void gemm_acc(f32x16& acc, const T* A, int lda, const T* B, int ldb, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const T* pa = A + r * lda + 4 * h;
+  const T* pb = B + r * ldb + 4 * h;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    Frag<T> fa, fb;
+    ld_frag(fa, pa + 16 * kb);
+    ld_frag(fb, pb + 16 * kb);
+    mma(acc, fa, fb);
+  }
+}
+
+// Write an accumulator block (rows m, columns n) to X[n][m] in LDS, rounded to T.
+__device__ __forceinline__ void st_accT(bf16* X, int ldx, const f32x16& acc, int lane) {
+  const int n = lane & 31, h = lane >> 5;
+  bf16* p = X + n * ldx + 4 * h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bf16x4 t = {(bf16)acc[4 * q], (bf16)acc[4 * q + 1], (bf16)acc[4 * q + 2], (bf16)acc[4 * q + 3]};
+    *reinterpret_cast<bf16x4*>(p + 8 * q) = t;
+  }
+}
+__device__ __forceinline__ void st_accT(float* X, int ldx, const f32x16& acc, int lane) {
+  const int n = lane & 31, h = lane >> 5;
+  float* p = X + n * ldx + 4 * h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 t = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    *reinterpret_cast<f32x4*>(p + 8 * q) = t;
+  }
+}
+
+// ---------------------------------------------------------------- tile loads
+// Load C rows x DP features of one head (base = row 0 of the head, row stride
+// d) into LDS: tm[row][col] (token-major, stride DP+PAD) and/or
+// fm[col][row] (feature-major, stride C+PAD).  Row r of the tile is global
+// row (gidx ? gidx[r] : row0 + r) and exists for r < nvalid.  Missing rows and
+// the padding features col >= d are stored as 0 -- NOT phi(0) = 1, so that
+// they add nothing to any sum.  PHI applies phi to the loaded values.
+// vec: d == DP, 16-byte pieces (base and row stride are 16-byte aligned).
+template <typename T, int DP, int C, bool PHI, bool TM, bool FM>
+__device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t row0, const int* __restrict__ gidx,
+                                          int nvalid, int d, bool vec, T* tm, T* fm, int tid) {
+  if (vec) {
+    constexpr int EPP = 16 / (int)sizeof(T);
+    constexpr int PPR = DP / EPP;
+    constexpr int NP = C * PPR;
+#pragma unroll 2
+    for (int p = tid; p < NP; p += NT) {
+      const int row = p / PPR, col = (p % PPR) * EPP;
+      union { uint4 u; T e[EPP]; } val;
+      if (row < nvalid) {
+        const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
+        val.u = *reinterpret_cast<const uint4*>(base + grow * DP + col);
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) {
+          float x = to_f(val.e[e]);
+          if (PHI) x = phi_f(x);
+          val.e[e] = cvt<T>(x);
+        }
+      } else {
+        val.u = make_uint4(0, 0, 0, 0);
+      }
+      if (TM) {
+        T* dst = tm + row * (DP + PAD) + col;
+        if (sizeof(T) == 4) {
+          *reinterpret_cast<uint4*>(dst) = val.u;
+        } else {  // rows of DP+PAD bf16 are only 8-byte aligned
+          reinterpret_cast<uint2*>(dst)[0] = make_uint2(val.u.x, val.u.y);
+          reinterpret_cast<uint2*>(dst)[1] = make_uint2(val.u.z, val.u.w);
+        }
+      }
+      if (FM) {
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) fm[(col + e) * (C + PAD) + row] = val.e[e];
+      }
+    }
+  } else {
+    for (int idx = tid; idx < C * DP; idx += NT) {
+      const int row = idx / DP, col = idx % DP;
+      float x = 0.0f;
+      if (row < nvalid && col < d) {
+        const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
+        x = to_f(base[grow * d + col]);
+        if (PHI) x = phi_f(x);
+      }
+      const T t = cvt<T>(x);
+      if (TM) tm[row * (DP + PAD) + col] = t;
+      if (FM) fm[col * (C + PAD) + row] = t;
+    }
+  }
+}
+
+// Number of 32x32 state blocks (a-block, b-block) each wave owns.
+template <int DP> struct StateBlocks {
+  static constexpr int NB = DP / 32;
+  static constexpr int TOTAL = NB * NB;
+  static constexpr int PER_WAVE = (TOTAL + NW - 1) / NW;
+};
+
+// Accumulator block <-> fp32 [DP][DP] row-major state in global memory.
+template <int DP>
+__device__ __forceinline__ void ld_state_block(f32x16& acc, const float* __restrict__ S, int ma, int nb, int lane) {
+  const int b = nb * 32 + (lane & 31), h = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = S[(ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * DP + b];
+}
+template <int DP>
+__device__ __forceinline__ void st_state_block(float* __restrict__ S, const f32x16& acc, int ma, int nb, int lane) {
+  const int b = nb * 32 + (lane & 31), h = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S[(ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * DP + b] = acc[r];
+}
+
+// Per-head slot layout of the state workspace: (nseg + 1) slots of
+// DP*DP + DP floats (S row-major [a][b], then z[a]); slot s < nseg holds the
+// aggregate of segment s (after k_scan: the exclusive prefix before segment
+// s); slot nseg holds the total.
+__host__ __device__ __forceinline__ int64_t slot_elems(int DP) { return (int64_t)DP * DP + DP; }
+
+// ------------------------------------------------------------------ k_state
+template <typename T, int DP, int C, bool PHI>
+__global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* __restrict__ v, int64_t n, int d,
+                                              bool vec, int64_t nchunks, int64_t G, int64_t nseg,
+                                              float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) T sKT[DP * (C + PAD)];
+  __shared__ __attribute__((aligned(16))) T sVT[DP * (C + PAD)];
+  using SB = StateBlocks<DP>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const T* kb = k + bh * n * d;
+  const T* vb = v + bh * n * d;
+  f32x16 accS[SB::PER_WAVE];
+#pragma unroll
+  for (int s = 0; s < SB::PER_WAVE; ++s) accS[s] = f32x16{};
+  float zrun = 0.0f;
+  const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)((n - t0) < C ? (n - t0) : C);
+    load_tile<T, DP, C, PHI, false, true>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
+    load_tile<T, DP, C, false, false, true>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SB::PER_WAVE; ++s) {
+      const int e = w + NW * s;
+      if (e < SB::TOTAL) {
+        const int ma = e / SB::NB, nb = e % SB::NB;
+        gemm_acc<T, C / 16>(accS[s], sKT + ma * 32 * (C + PAD), C + PAD, sVT + nb * 32 * (C + PAD), C + PAD, lane);
+      }
+    }
+    if (tid < DP) {
+      float sum = 0.0f;
+      for (int t = 0; t < C; ++t) sum += to_f(sKT[tid * (C + PAD) + t]);
+      zrun += sum;
+    }
+    __syncthreads();
+  }
+  float* dst = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
+#pragma unroll
+  for (int s = 0; s < SB::PER_WAVE; ++s) {
+    const int e = w + NW * s;
+    if (e < SB::TOTAL) st_state_block<DP>(dst, accS[s], e / SB::NB, e % SB::NB, lane);
+  }
+  if (tid < DP) dst[DP * DP + tid] = zrun;
+}
+
+// ------------------------------------------------------------------- k_scan
+// One thread per state element of one head: exclusive prefix over segments
+// in place, total into slot nseg, and the caller's final state if asked.
+__global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nseg, int DP, int d,
+                                             float* __restrict__ S_final, float* __restrict__ z_final) {
+  const int64_t E = slot_elems(DP);
+  const int64_t bh = blockIdx.x;
+  const int64_t e = (int64_t)blockIdx.y * NT + threadIdx.x;
+  if (e >= E) return;
+  float* base = ws + bh * (nseg + 1) * E + e;
+  float run = 0.0f;
+  for (int64_t s = 0; s < nseg; ++s) {
+    const float x = base[s * E];
+    base[s * E] = run;
+    run += x;
+  }
+  base[nseg * E] = run;
+  if (e < (int64_t)DP * DP) {
+    const int a = (int)(e / DP), b = (int)(e % DP);
+    if (S_final && a < d && b < d) S_final[bh * d * d + (int64_t)a * d + b] = run;
+  } else {
+    const int a = (int)(e - (int64_t)DP * DP);
+    if (z_final && a < d) z_final[bh * d + a] = run;
+  }
+}
+
+// -------------------------------------------------------------------- k_out
+// Causal (FORM = CAUSAL: phi, normalised; the queries of chunk c are its own
+// rows, for each of the R query heads of this key/value head) or prefix
+// (FORM = PREFIX: identity feature map, no normaliser, R = 1; the queries of
+// chunk c are the bucket perm[boff[c] .. boff[c+1]) in tiles of C).
+template <typename T, int DP, int C, int FORM>
+__global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __restrict__ k,
+                                            const T* __restrict__ v, T* __restrict__ out, int64_t n, int d,
+                                            int R, bool vec, int64_t nchunks, int64_t G, int64_t nseg,
+                                            const float* __restrict__ ws, const int* __restrict__ perm,
+                                            const int* __restrict__ boff, const int64_t* __restrict__ m) {
+  constexpr int LQ = DP + PAD;  // row stride of sQ, sK, sST
+  constexpr int LC = C + PAD;   // row stride of sKT, sVT, sP
+  constexpr int NIB = C / 32;   // 32-row query / key blocks per chunk
+  constexpr int NBB = DP / 32;  // 32-wide feature blocks
+  constexpr bool NORM = (FORM == CAUSAL);
+  __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
+  __shared__ __attribute__((aligned(16))) T sK[C * LQ];
+  __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
+  __shared__ __attribute__((aligned(16))) T sVT[DP * LC];
+  __shared__ __attribute__((aligned(16))) T sST[DP * LQ];
+  __shared__ __attribute__((aligned(16))) T sP[C * LC];
+  __shared__ float sz[DP];
+  using SB = StateBlocks<DP>;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const T* kb = k + bh * n * d;
+  const T* vb = v + bh * n * d;
+
+  // This wave's output blocks: fixed query block ib, feature blocks nb.
+  const int ib = w % NIB;
+  const int nb0 = w / NIB;
+  constexpr int NB_STEP = NW / NIB;  // NIB divides NW
+  const bool has_out = nb0 < NBB;
+
+  f32x16 accS[SB::PER_WAVE];
+  {
+    const float* src = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
+#pragma unroll
+    for (int s = 0; s < SB::PER_WAVE; ++s) {
+      const int e = w + NW * s;
+      if (e < SB::TOTAL) ld_state_block<DP>(accS[s], src, e / SB::NB, e % SB::NB, lane);
+      else accS[s] = f32x16{};
+    }
+  }
+  float zrun = 0.0f;
+  if (NORM && tid < DP) zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + tid];
+
+  const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)((n - t0) < C ? (n - t0) : C);
+    // Query groups of this chunk: R heads (causal) or bucket tiles (prefix).
+    int64_t qstart = 0;
+    int ngroups = R;
+    if (FORM == PREFIX) {
+      qstart = boff[c];
+      const int64_t cnt = boff[c + 1] - qstart;
+      ngroups = (int)((cnt + C - 1) / C);
+    }
+
+    load_tile<T, DP, C, NORM, true, true>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
+    load_tile<T, DP, C, false, false, true>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+#pragma unroll
+    for (int s = 0; s < SB::PER_WAVE; ++s) {
+      const int e = w + NW * s;
+      if (e < SB::TOTAL) {
+        const int ma = e / SB::NB, nb = e % SB::NB;
+        st_accT(sST + nb * 32 * LQ + ma * 32, LQ, accS[s], lane);  // sST[b][a] = S[a][b]
+      }
+    }
+    if (NORM && tid < DP) sz[tid] = zrun;
+
+    for (int grp = 0; grp < ngroups; ++grp) {
+      // ---- query tile of this group
+      const T* qb;
+      const int* gidx = nullptr;
+      int qcount;
+      if (FORM == CAUSAL) {
+        qb = q + (bh * R + grp) * n * d;
+        qcount = nv;
+      } else {
+        qb = q + bh * n * d;
+        const int64_t s0 = qstart + (int64_t)grp * C;
+        const int64_t rem = boff[c + 1] - s0;
+        qcount = (int)(rem < C ? rem : C);
+        gidx = perm + s0;
+      }
+      if (grp > 0) __syncthreads();  // previous group is done with sQ / sP
+      load_tile<T, DP, C, NORM, true, false>(qb, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
+      __syncthreads();
+
+      // ---- P^T blocks (key block jb, query block ib2), masked, -> sP[i][j]
+      {
+        int e = 0;
+#pragma unroll
+        for (int ib2 = 0; ib2 < NIB; ++ib2) {
+#pragma unroll
+          for (int jb = 0; jb < NIB; ++jb) {
+            if (FORM == CAUSAL && jb > ib2) continue;
+            if ((e++ % NW) != w) continue;
+            f32x16 acc = f32x16{};
+            gemm_acc<T, DP / 16>(acc, sK + jb * 32 * LQ, LQ, sQ + ib2 * 32 * LQ, LQ, lane);
+            const int i = ib2 * 32 + (lane & 31);
+            int limit;
+            if (FORM == CAUSAL) {
+              limit = i;
+            } else {
+              limit = -1;
+              if (i < qcount) {
+                int64_t mi = m[gidx[i]];
+                mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);  // same clamp as k_bucket
+                limit = (int)(mi - t0);
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = jb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+              if (j > limit) acc[r] = 0.0f;
+            }
+            st_accT(sP + ib2 * 32 * LC + jb * 32, LC, acc, lane);
+          }
+        }
+      }
+      __syncthreads();
+
+      // ---- outputs of this wave: out^T[b][i] = S^T phi(Q)^T + V^T P^T
+      if (has_out) {
+        const int i = ib * 32 + (lane & 31);
+        float den = 1.0f;
+        if (NORM) {
+          float part = 0.0f;
+          const T* qrow = sQ + i * LQ + h * (DP / 2);
+          const float* zz = sz + h * (DP / 2);
+          for (int a = 0; a < DP / 2; ++a) part += to_f(qrow[a]) * zz[a];
+          constexpr int JMAX = C;  // entries past the causal limit are zero
+          const int jend = (ib + 1) * 32 < JMAX ? (ib + 1) * 32 : JMAX;
+          const T* prow = sP + i * LC;
+          for (int j = h * (jend / 2); j < (h + 1) * (jend / 2); ++j) part += to_f(prow[j]);
+          den = part + __shfl_xor(part, 32);
+        }
+        const float inv = 1.0f / den;
+        int64_t grow = -1;
+        if (i < qcount) grow = (FORM == CAUSAL) ? t0 + i : (int64_t)gidx[i];
+        T* ob = (FORM == CAUSAL) ? out + (bh * R + grp) * n * d : out + bh * n * d;
+        for (int nb = nb0; nb < NBB; nb += NB_STEP) {
+          f32x16 acc = f32x16{};
+          gemm_acc<T, DP / 16>(acc, sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
+#pragma unroll
+          for (int jb = 0; jb < NIB; ++jb) {
+            if (FORM == CAUSAL && jb > ib) continue;
+            gemm_acc<T, 2>(acc, sVT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
+          }
+          if (grow >= 0) {
+            T* orow = ob + grow * d;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int b0 = nb * 32 + 8 * qq + 4 * h;
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                if (b0 + s < d) orow[b0 + s] = cvt<T>(NORM ? acc[4 * qq + s] * inv : acc[4 * qq + s]);
+              }
+            }
+          }
+        }
+      }
+    }
+
+    // ---- S += phi(K_c)^T V_c ;  z += column sums of phi(K_c)
+#pragma unroll
+    for (int s = 0; s < SB::PER_WAVE; ++s) {
+      const int e = w + NW * s;
+      if (e < SB::TOTAL) {
+        const int ma = e / SB::NB, nb = e % SB::NB;
+        gemm_acc<T, C / 16>(accS[s], sKT + ma * 32 * LC, LC, sVT + nb * 32 * LC, LC, lane);
+      }
+    }
+    if (NORM && tid < DP) {
+      float sum = 0.0f;
+      for (int t = 0; t < C; ++t) sum += to_f(sKT[tid * LC + t]);
+      zrun += sum;
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------- k_out_nc
+// Non-causal output: out_i = phi(Q_i) S / (phi(Q_i) . z) with the total state
+// (slot nseg of the head).  One workgroup per (head, run of G chunks of
+// queries), for each of the R query heads.
+template <typename T, int DP, int C>
+__global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __restrict__ out, int64_t n, int d, int R,
+                                               bool vec, int64_t nchunks, int64_t G, int64_t nqseg, int64_t nseg,
+                                               const float* __restrict__ ws) {
+  constexpr int LQ = DP + PAD;
+  constexpr int NIB = C / 32;
+  constexpr int NBB = DP / 32;
+  __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
+  __shared__ __attribute__((aligned(16))) T sST[DP * LQ];
+  __shared__ float sz[DP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int64_t bh = blockIdx.x / nqseg, qs = blockIdx.x % nqseg;
+  const float* tot = ws + (bh * (nseg + 1) + nseg) * slot_elems(DP);
+  for (int idx = tid; idx < DP * DP; idx += NT) {
+    const int a = idx / DP, b = idx % DP;
+    sST[b * LQ + a] = cvt<T>(tot[idx]);
+  }
+  if (tid < DP) sz[tid] = tot[DP * DP + tid];
+  const int ib = w % NIB;
+  const int nb0 = w / NIB;
+  constexpr int NB_STEP = NW / NIB;
+  const bool has_out = nb0 < NBB;
+  const int64_t c0 = qs * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)((n - t0) < C ? (n - t0) : C);
+    for (int r = 0; r < R; ++r) {
+      const T* qb = q + (bh * R + r) * n * d;
+      __syncthreads();  // sQ free (and sST / sz visible on the first pass)
+      load_tile<T, DP, C, true, true, false>(qb, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
+      __syncthreads();
+      if (has_out) {
+        const int i = ib * 32 + (lane & 31);
+        float part = 0.0f;
+        const T* qrow = sQ + i * LQ + h * (DP / 2);
+        const float* zz = sz + h * (DP / 2);
+        for (int a = 0; a < DP / 2; ++a) part += to_f(qrow[a]) * zz[a];
+        const float inv = 1.0f / (part + __shfl_xor(part, 32));
+        T* orow = (i < nv) ? out + (bh * R + r) * n * d + (t0 + i) * d : nullptr;
+        for (int nb = nb0; nb < NBB; nb += NB_STEP) {
+          f32x16 acc = f32x16{};
+          gemm_acc<T, DP / 16>(acc, sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
+          if (orow) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int b0 = nb * 32 + 8 * qq + 4 * h;
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                if (b0 + s < d) orow[b0 + s] = cvt<T>(acc[4 * qq + s] * inv);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- k_bucket
+// Counting sort of the queries by the chunk their mask ends in,
+// c(i) = floor(m_i / C): boff[c] is the first slot of bucket c in perm,
+// boff[nchunks] = n.  One workgroup; the histogram and the fill cursors live
+// in LDS (nchunks <= kMaxBuckets).  The order inside a bucket is arbitrary,
+// which changes no output: each query's row is computed on its own.
+// m_i outside [0, n-1] is clamped into that range.
+__global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks,
+                                                 int* __restrict__ boff, int* __restrict__ perm) {
+  __shared__ int cnt[la_internal::kMaxBuckets + 1];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int len = (int)nchunks + 1;
+  for (int c = tid; c < len; c += nt) cnt[c] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += nt) {
+    int64_t mi = m[i];
+    mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
+    atomicAdd(&cnt[mi / C + 1], 1);
+  }
+  __syncthreads();
+  // inclusive scan of cnt[0..nchunks] (cnt[0] == 0): contiguous per-thread
+  // ranges, then a scan of the per-thread sums
+  const int per = (len + nt - 1) / nt;
+  const int lo = tid * per, hi = (lo + per < len) ? lo + per : len;
+  int sum = 0;
+  for (int c = lo; c < hi; ++c) sum += cnt[c];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const int x = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += x;
+    __syncthreads();
+  }
+  int run = tid > 0 ? part[tid - 1] : 0;
+  for (int c = lo; c < hi; ++c) {
+    run += cnt[c];
+    cnt[c] = run;
+    boff[c] = run;
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += nt) {
+    int64_t mi = m[i];
+    mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
+    const int pos = atomicAdd(&cnt[mi / C], 1);  // cnt[c] is now bucket c's fill cursor
+    perm[pos] = (int)i;
+  }
+}
+
+// ----------------------------------------------------------------- k_decode
+// One workgroup per (batch, key/value head): S += phi(k) (x) v, z += phi(k),
+// then out_h = phi(q_h) S / (phi(q_h) . z) for the R query heads of the group.
+// Thread t owns column b = t % 128 of rows a = t / 128 + 2u (u < 64) and keeps
+// them in registers between the update and the reads.
+template <typename T>
+__global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
+                                               const T* __restrict__ v, int d, int R, float* __restrict__ S,
+                                               float* __restrict__ z, T* __restrict__ out) {
+  __shared__ float pk[la_internal::kMaxD], vv[la_internal::kMaxD], zn[la_internal::kMaxD];
+  __shared__ float pq[la_internal::kMaxD];
+  __shared__ float red[2][la_internal::kMaxD];
+  __shared__ float sden;
+  const int tid = threadIdx.x;
+  const int64_t bg = blockIdx.x;  // b * Hkv + g
+  float* Sg = S + bg * d * d;
+  float* zg = z + bg * d;
+  if (tid < d) {
+    const float pkv = phi_f(to_f(k[bg * d + tid]));
+    pk[tid] = pkv;
+    vv[tid] = to_f(v[bg * d + tid]);
+    const float znew = zg[tid] + pkv;
+    zg[tid] = znew;
+    zn[tid] = znew;
+  }
+  __syncthreads();
+  const int b = tid & 127, half = tid >> 7;
+  float s[64];
+  if (b < d) {
+    const float vb = vv[b];
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      const int a = half + 2 * u;
+      if (a < d) {
+        const float x = Sg[(int64_t)a * d + b] + pk[a] * vb;
+        Sg[(int64_t)a * d + b] = x;
+        s[u] = x;
+      } else {
+        s[u] = 0.0f;
+      }
+    }
+  }
+  for (int r = 0; r < R; ++r) {
+    const int64_t qh = bg * R + r;  // (b * Hkv + g) * R + r = b * Hq + g * R + r
+    __syncthreads();                // previous head's reads of pq / red are done
+    if (tid < d) pq[tid] = phi_f(to_f(q[qh * d + tid]));
+    __syncthreads();
+    if (tid < 64) {  // wave 0: den = phi(q) . z
+      float p = 0.0f;
+      for (int a = tid; a < d; a += 64) p += pq[a] * zn[a];
+      for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+      if (tid == 0) sden = p;
+    }
+    float num = 0.0f;
+    if (b < d) {
+#pragma unroll
+      for (int u = 0; u < 64; ++u) {
+        const int a = half + 2 * u;
+        if (a < d) num += pq[a] * s[u];
+      }
+      red[half][b] = num;
+    }
+    __syncthreads();
+    if (tid < d) out[qh * d + tid] = cvt<T>((red[0][tid] + red[1][tid]) / sden);
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+template <typename T, int DP, int C>
+int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, int form) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const bool vec = (a.d == DP);
+  const int64_t nbh = a.B * a.Hkv;
+  float* states = reinterpret_cast<float*>(a.ws);
+  const int R = (int)(a.Hq / a.Hkv);
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  T* out = reinterpret_cast<T*>(a.out);
+  int* boff = nullptr; int* perm = nullptr;
+  if (form == PREFIX) {
+    char* bw = reinterpret_cast<char*>(a.ws) + la_internal::state_bytes(p, a.B, a.Hkv);
+    boff = reinterpret_cast<int*>(bw);
+    perm = boff + (p.nchunks + 1);
+    k_bucket<<<1, 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
+  }
+  const bool phi = (form == CAUSAL);
+  if (phi)
+    k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
+  else
+    k_state<T, DP, C, false><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
+  const int64_t E = slot_elems(DP);
+  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final, a.z_final);
+  if (q && out) {
+    if (form == CAUSAL)
+      k_out<T, DP, C, CAUSAL><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
+    else
+      k_out<T, DP, C, PREFIX><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m);
+  }
+  return (int)hipGetLastError();
+}
+
+template <typename T, int DP, int C>
+int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const bool vec = (a.d == DP);
+  const int64_t nbh = a.B * a.Hkv;
+  float* states = reinterpret_cast<float*>(a.ws);
+  const int R = (int)(a.Hq / a.Hkv);
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  T* out = reinterpret_cast<T*>(a.out);
+  k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
+  const int64_t E = slot_elems(DP);
+  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr);
+  // query runs: about 1024 workgroups in total
+  int64_t Gq = (nbh * p.nchunks + 1023) / 1024;
+  if (Gq < 1) Gq = 1;
+  const int64_t nqseg = (p.nchunks + Gq - 1) / Gq;
+  k_out_nc<T, DP, C><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks, Gq, nqseg, p.nseg, states);
+  return (int)hipGetLastError();
+}
+
+// Instantiate for a (T, DP) pair and every chunk that fits in LDS.
+template <typename T, int DP>
+int dispatch_chunk(const la_internal::Fwd& a, const la_internal::Plan& p, int op) {
+  switch (p.C) {
+#define LA_CASE(CC)                                                                            \
+  case CC:                                                                                     \
+    if constexpr (la_internal::chunk_fits((int)sizeof(T), DP, CC)) {                           \
+      if (op == 0) return run_forward<T, DP, CC>(a, p);                                        \
+      return run_causal_or_prefix<T, DP, CC>(a, p, op == 1 ? CAUSAL : PREFIX);                  \
+    }                                                                                          \
+    break;
+    LA_CASE(32)
+    LA_CASE(64)
+    LA_CASE(128)
+#undef LA_CASE
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <int DP>
+int dispatch_dtype(const la_internal::Fwd& a, const la_internal::Plan& p, int op) {
+  if (a.dtype == 0) return dispatch_chunk<float, DP>(a, p, op);
+  return dispatch_chunk<bf16, DP>(a, p, op);
+}
+
+int dispatch(const la_internal::Fwd& a, const la_internal::Plan& p, int op) {
+  switch (p.DP) {
+    case 32: return dispatch_dtype<32>(a, p, op);
+    case 64: return dispatch_dtype<64>(a, p, op);
+    case 128: return dispatch_dtype<128>(a, p, op);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace
+
+namespace la_internal {
+
+int launch_forward(const Fwd& a, const Plan& p) { return dispatch(a, p, 0); }
+int launch_causal(const Fwd& a, const Plan& p) { return dispatch(a, p, 1); }
+int launch_prefix(const Fwd& a, const Plan& p) { return dispatch(a, p, 2); }
+
+int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                  int dtype, float* S, float* z, void* out, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int R = (int)(Hq / Hkv);
+  const dim3 grid((unsigned)(B * Hkv));
+  if (dtype == 0)
+    k_decode<float><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
+                                         reinterpret_cast<const float*>(v), (int)d, R, S, z,
+                                         reinterpret_cast<float*>(out));
+  else
+    k_decode<bf16><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
+                                        reinterpret_cast<const bf16*>(v), (int)d, R, S, z,
+                                        reinterpret_cast<bf16*>(out));
+  return (int)hipGetLastError();
+}
+
+}  // namespace la_internal

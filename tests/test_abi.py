@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/la.h declares, sizes workspaces, and rejects every invalid argument
+with its status code before anything is launched (the checks run on the host
+and return before the first HIP call, so fake device pointers are safe)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_phi_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, ALIGN, ALIAS = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return la.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == {"la_status_str", "la_workspace_bytes", "la_forward", "la_causal_forward",
+                          "la_prefix_mask_forward", "la_decode_step"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(la.STATUS_NAMES):
+        assert la.la_status_str(code).startswith(name)
+    assert la.la_status_str(99) == "unknown la_status"
+
+
+def test_workspace_bytes():
+    f = la.la_workspace_bytes
+    # causal bf16 B8 H8 n2048 d64: (nseg + 1) fp32 slots of (64*64 + 64) per head
+    b = f(la.LA_OP_CAUSAL, 8, 8, 8, 2048, 64, la.LA_BF16, 64)
+    assert b > 0 and b % (4 * (64 * 64 + 64)) == 0
+    assert f(la.LA_OP_CAUSAL, 8, 8, 8, 2048, 64, la.LA_BF16, 0) == b  # default chunk is 64
+    assert f(la.LA_OP_FORWARD, 2, 8, 8, 4096, 64, la.LA_F32, 0) > 0
+    # prefix form: states plus bucket offsets and the permutation
+    p = f(la.LA_OP_PREFIX_MASK, 4, 8, 8, 8192, 64, la.LA_F32, 64)
+    assert p > 4 * (8192 + 8192 // 64 + 1)
+    # invalid requests size to 0
+    assert f(7, 1, 1, 1, 16, 16, la.LA_F32, 0) == 0
+    assert f(la.LA_OP_CAUSAL, 1, 3, 2, 16, 16, la.LA_F32, 0) == 0      # Hq % Hkv
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 16, 129, la.LA_F32, 0) == 0     # d > 128
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 0, 16, la.LA_F32, 0) == 0       # n = 0
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 16, 16, 5, 0) == 0              # dtype
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 16, 16, la.LA_F32, 48) == 0     # chunk
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 16, 128, la.LA_F32, 64) == 0    # fp32 d=128 chunk 64: LDS
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 16, 128, la.LA_F32, 32) > 0
+    assert f(la.LA_OP_PREFIX_MASK, 1, 2, 1, 16, 16, la.LA_F32, 0) == 0  # prefix needs Hq == Hkv
+
+
+# Fake, 16-byte aligned "device" addresses far apart; never dereferenced.
+Q, K, V, O, WSP, M, S, Z = (0x10000000 * (i + 1) for i in range(8))
+BIG = 1 << 30
+
+
+def fwd(lib, q=Q, k=K, v=V, B=1, Hq=2, Hkv=1, n=16, d=16, dt=0, out=O, ws=WSP, wsb=BIG):
+    return lib.la_forward(q, k, v, B, Hq, Hkv, n, d, dt, out, ws, wsb, None)
+
+
+def causal(lib, q=Q, k=K, v=V, B=1, Hq=2, Hkv=1, n=16, d=16, dt=1, chunk=0, out=O, Sf=None, zf=None,
+           ws=WSP, wsb=BIG):
+    return lib.la_causal_forward(q, k, v, B, Hq, Hkv, n, d, dt, chunk, out, Sf, zf, ws, wsb, None)
+
+
+def prefix(lib, q=Q, k=K, v=V, m=M, B=1, H=1, n=16, d=16, dt=0, chunk=0, out=O, ws=WSP, wsb=BIG):
+    return lib.la_prefix_mask_forward(q, k, v, m, B, H, n, d, dt, chunk, out, ws, wsb, None)
+
+
+def decode(lib, q=Q, k=K, v=V, B=1, Hq=2, Hkv=1, d=16, dt=0, S_=S, z=Z, out=O):
+    return lib.la_decode_step(q, k, v, B, Hq, Hkv, d, dt, S_, z, out, None)
+
+
+def test_forward_rejections(lib):
+    assert fwd(lib, q=None) == NULL
+    assert fwd(lib, out=None) == NULL
+    assert fwd(lib, dt=3) == DTYPE
+    assert fwd(lib, d=0) == SHAPE
+    assert fwd(lib, d=129) == SHAPE
+    assert fwd(lib, n=0) == SHAPE
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, Hq=3, Hkv=2) == SHAPE
+    assert fwd(lib, q=Q + 8) == ALIGN
+    assert fwd(lib, out=Q + 64) == ALIAS
+    assert fwd(lib, out=K) == ALIAS
+    assert fwd(lib, wsb=16) == WS
+    assert fwd(lib, ws=None) == WS
+    assert fwd(lib, ws=WSP + 4) == ALIGN
+    assert fwd(lib, ws=V) == ALIAS
+
+
+def test_causal_rejections(lib):
+    assert causal(lib, k=None) == NULL
+    assert causal(lib, q=None) == NULL                 # q without out
+    assert causal(lib, out=None) == NULL               # out without q
+    assert causal(lib, q=None, out=None) == NULL       # state-only needs S_final or z_final
+    assert causal(lib, chunk=48) == UNSUP
+    assert causal(lib, chunk=16) == UNSUP
+    assert causal(lib, d=128, dt=0, chunk=128) == UNSUP
+    assert causal(lib, Sf=S + 4) == ALIGN
+    assert causal(lib, Sf=Q) == ALIAS
+    assert causal(lib, Sf=S, zf=S + 16) == ALIAS
+    assert causal(lib, wsb=100) == WS
+    assert causal(lib, ws=O) == ALIAS
+    assert causal(lib, n=(1 << 31)) == SHAPE
+
+
+def test_prefix_rejections(lib):
+    assert prefix(lib, m=None) == NULL
+    assert prefix(lib, m=M + 8) == ALIGN
+    assert prefix(lib, out=M) == ALIAS
+    assert prefix(lib, n=64 * 16384) == UNSUP   # too many buckets
+    assert prefix(lib, chunk=100) == UNSUP
+    assert prefix(lib, wsb=8) == WS
+
+
+def test_decode_rejections(lib):
+    assert decode(lib, S_=None) == NULL
+    assert decode(lib, z=None) == NULL
+    assert decode(lib, d=200) == SHAPE
+    assert decode(lib, Hq=3, Hkv=2) == SHAPE
+    assert decode(lib, dt=2) == DTYPE
+    assert decode(lib, out=S) == ALIAS
+    assert decode(lib, z=S + 256) == ALIAS
+    assert decode(lib, q=Q + 2) == ALIGN
+
+
+def test_binding_checks_shapes_before_calling():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 4)
+    k = torch.zeros(1, 1, 8, 4)
+    with pytest.raises(ValueError):
+        la.la_forward(q, k, torch.zeros(1, 1, 8, 5))           # v shape
+    with pytest.raises(ValueError):
+        la.la_forward(q, k.to(torch.bfloat16), k)              # dtype mismatch
+    with pytest.raises(ValueError):
+        la.la_forward(torch.zeros(1, 3, 8, 4), torch.zeros(1, 2, 8, 4), torch.zeros(1, 2, 8, 4))
+    with pytest.raises(TypeError):
+        la.la_forward(q.double(), k.double(), k.double())
+    with pytest.raises(ValueError):  # CPU tensors are refused (no host fallback)
+        la.la_forward(q, k, k)

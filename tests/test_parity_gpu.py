@@ -1,0 +1,249 @@
+"""GPU parity: the HIP kernels (through the C ABI and its binding) against
+the fp64 oracle on identical seeded inputs.
+
+Metric: the largest row-wise max-norm relative error,
+max_rows ||gpu_row - oracle_row||_inf / ||oracle_row||_inf, where a row is
+one query's d-vector in one head.  Tolerances: 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs (fp32 accumulation in both).  Element-wise relative
+error is not used: outputs near zero make it meaningless.
+"""
+import numpy as np
+import pytest
+
+import la_inputs as li
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {li.F32: 1e-4, li.BF16: 2e-2}
+
+
+def dev(x):
+    return li.to_torch(x).cuda()
+
+
+def host(t):
+    return li.to_f32(li.from_torch(t)).astype(np.float64)
+
+
+def rel_rows(g, o):
+    num = np.abs(g - o).max(axis=-1)
+    den = np.abs(o).max(axis=-1)
+    return float((num / np.maximum(den, 1e-30)).max())
+
+
+def check(g, o, dtype, what):
+    err = rel_rows(g, o)
+    print(f"{what}: row-wise rel err {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    assert err <= TOL[dtype], f"{what}: {err:.3e} > {TOL[dtype]}"
+    return err
+
+
+# --------------------------------------------------------------- hand cases
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_hand_cases(gpu, dtype):
+    """The nx page's gates through the GPU (d = 2: 30 masked feature lanes)."""
+    for which, want_nc, want_c in (
+            ("zero", [[4, 6], [4, 6]], [[2, 4], [4, 6]]),
+            ("identity", [[34 / 9, 52 / 9], [38 / 9, 56 / 9]], [[2, 4], [38 / 9, 56 / 9]])):
+        q, k, v = (li.as_dtype(x, dtype) for x in li.hand_case(which))
+        nc = host(gpu.la_forward(dev(q), dev(k), dev(v)))[0, 0]
+        ca = host(gpu.la_causal_forward(dev(q), dev(k), dev(v)))[0, 0]
+        check(nc, np.array(want_nc, float), dtype, f"gate {which} non-causal")
+        check(ca, np.array(want_c, float), dtype, f"gate {which} causal")
+    # the page's state for gate 2
+    q, k, v = (li.as_dtype(x, dtype) for x in li.hand_case("identity"))
+    _, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True)
+    np.testing.assert_allclose(S.cpu().numpy()[0, 0], [[10, 16], [14, 20]], rtol=1e-6)
+    np.testing.assert_allclose(z.cpu().numpy()[0, 0], [3, 3], rtol=1e-6)
+
+
+# ------------------------------------------------------------- small / ragged
+SMALL = [
+    # (B, Hq, Hkv, n, d, chunk)
+    (1, 1, 1, 256, 16, 0),     # the tiny config
+    (1, 1, 1, 1, 1, 32),
+    (2, 2, 1, 2, 3, 64),
+    (1, 3, 1, 63, 64, 32),
+    (1, 2, 2, 65, 64, 64),
+    (2, 4, 2, 100, 33, 64),
+    (1, 2, 1, 257, 128, 64),
+    (1, 1, 1, 300, 100, 128),
+    (1, 4, 4, 129, 64, 128),
+    (2, 8, 2, 200, 31, 32),
+]
+
+
+def _small_id(c):
+    return "B%d_Hq%d_Hkv%d_n%d_d%d_c%d" % c
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("case", SMALL, ids=_small_id)
+def test_noncausal_small(gpu, dtype, case):
+    B, Hq, Hkv, n, d, _ = case
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=0)
+    g = host(gpu.la_forward(dev(q), dev(k), dev(v)))
+    check(g, oracle.forward(q, k, v), dtype, f"forward {_small_id(case)} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("case", SMALL, ids=_small_id)
+def test_causal_small(gpu, dtype, case):
+    B, Hq, Hkv, n, d, chunk = case
+    if dtype == li.F32 and d > 64 and chunk > 32:
+        chunk = 32  # fp32 at d = 128 fits LDS only with 32-token chunks
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=1, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=chunk, want_state=True)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True)
+    check(host(out), ref, dtype, f"causal {_small_id(case)} {dtype}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-4 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
+@pytest.mark.parametrize("kind", ["random", "causal", "full", "first"])
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("case", SMALL[:8], ids=_small_id)
+def test_prefix_small(gpu, dtype, kind, case):
+    B, H, _, n, d, chunk = case
+    if dtype == li.F32 and d > 64 and chunk > 32:
+        chunk = 32
+    q, k, v, rng = li.qkv(B, H, H, n, d, dtype, seed=2, scaled=True)
+    m = li.mask(n, kind, rng=rng)
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=chunk))
+    check(g, oracle.prefix_mask(q, k, v, m), dtype, f"prefix {kind} {_small_id(case)} {dtype}")
+
+
+def test_prefix_page_mask(gpu):
+    """m = [2, 0, 1] (the trim-transformer page's example) on the GPU."""
+    q, k, v, _ = li.qkv(1, 2, 2, 3, 4, li.F32, seed=11)
+    m = np.array([2, 0, 1], dtype=np.int64)
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m)))
+    check(g, oracle.prefix_mask(q, k, v, m), li.F32, "prefix [2,0,1]")
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_chunk_size_invariance(gpu, dtype):
+    """The chunk length only changes rounding: 32, 64 and 128 agree with the oracle."""
+    q, k, v, _ = li.qkv(2, 4, 2, 777, 64, dtype, seed=5, scaled=True)
+    ref = oracle.causal(q, k, v)
+    for chunk in (32, 64, 128):
+        g = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=chunk))
+        check(g, ref, dtype, f"causal chunk {chunk}")
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_decode_continues_causal(gpu, dtype):
+    """State-only causal pass over n - T tokens, then T decode steps, equals the
+    causal pass over all n tokens (outputs and final state)."""
+    B, Hq, Hkv, n, d, T = 3, 4, 2, 150, 64, 6
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=6, scaled=True)
+    full, Sf, zf = oracle.causal(q, k, v, want_state=True)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    S, z = gpu.la_causal_forward(None, kd[:, :, :n - T].contiguous(), vd[:, :, :n - T].contiguous(), Hq=Hq)
+    for t in range(n - T, n):
+        o = gpu.la_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), S, z)
+        check(host(o), full[:, :, t], dtype, f"decode step {t}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sf, rtol=1e-4, atol=1e-4 * np.abs(Sf).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zf, rtol=1e-5)
+
+
+def test_state_only_matches_full_pass(gpu):
+    q, k, v, _ = li.qkv(2, 4, 2, 300, 64, li.BF16, seed=7, scaled=True)
+    _, S1, z1 = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True)
+    S2, z2 = gpu.la_causal_forward(None, dev(k), dev(v), Hq=4)
+    assert np.array_equal(S1.cpu().numpy(), S2.cpu().numpy())
+    assert np.array_equal(z1.cpu().numpy(), z2.cpu().numpy())
+
+
+def test_run_to_run_bitwise(gpu):
+    q, k, v, rng = li.qkv(2, 8, 8, 1000, 64, li.BF16, seed=8, scaled=True)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    bits = lambda t: li.from_torch(t)  # raw bf16 bit patterns
+    a = bits(gpu.la_causal_forward(qd, kd, vd))
+    b = bits(gpu.la_causal_forward(qd, kd, vd))
+    assert np.array_equal(a, b)
+    m = dev(li.mask(1000, "random", rng=rng))
+    a = bits(gpu.la_prefix_mask_forward(qd, kd, vd, m))
+    b = bits(gpu.la_prefix_mask_forward(qd, kd, vd, m))
+    assert np.array_equal(a, b)
+    a = bits(gpu.la_forward(qd, kd, vd))
+    b = bits(gpu.la_forward(qd, kd, vd))
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------- the workloads' sizes
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_noncausal_B2_H8_n4096_d64(gpu, dtype):
+    q, k, v, _ = li.qkv(2, 8, 8, 4096, 64, dtype, seed=0)
+    g = host(gpu.la_forward(dev(q), dev(k), dev(v)))
+    check(g, oracle.forward(q, k, v), dtype, f"non-causal B2 H8 n4096 d64 {dtype}")
+
+
+def test_causal_B8_H8_n2048_d64_bf16(gpu):
+    q, k, v, _ = li.qkv(8, 8, 8, 2048, 64, li.BF16, seed=0, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64, want_state=True)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True)
+    check(host(out), ref, li.BF16, "causal B8 H8 n2048 d64 bf16")
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
+def test_causal_uniform_keys_closed_form_full_scale(gpu):
+    """All key rows equal: out_i = mean(V_0..V_i) exactly (every key has the
+    same weight), at the causal workload's full size."""
+    B, H, n, d = 8, 8, 2048, 64
+    q, _, v, rng = li.qkv(B, H, H, n, d, li.BF16, seed=3, scaled=True)
+    row = li.as_dtype(rng.standard_normal(d, dtype=np.float32) / 8, li.BF16)
+    k = np.broadcast_to(row, (B, H, n, d)).copy()
+    g = host(gpu.la_causal_forward(dev(q), dev(k), dev(v)))
+    vf = li.to_f32(v).astype(np.float64)
+    want = np.cumsum(vf, axis=2) / np.arange(1, n + 1)[None, None, :, None]
+    check(g, want, li.BF16, "causal uniform keys")
+
+
+@pytest.mark.parametrize("kind", ["causal", "random"])
+def test_prefix_B4_H8_n8192_d64_f32(gpu, kind):
+    q, k, v, rng = li.qkv(4, 8, 8, 8192, 64, li.F32, seed=0, scaled=True)
+    m = li.mask(8192, kind, rng=rng)
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m)))
+    check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B4 H8 n8192 d64 f32")
+
+
+def test_gqa_causal_B1_Hq32_Hkv8_n65536_d128_bf16(gpu):
+    n = 65536
+    q, k, v, rng = li.qkv(1, 32, 8, n, 128, li.BF16, seed=0, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True)
+    rows = np.unique(np.concatenate([rng.choice(n, 62, replace=False), [0, 63, 64, n - 1]]))
+    ref, Sr, zr = oracle.causal(q, k, v, rows=rows, want_state=True)
+    g = host(out[:, :, rows.tolist()])
+    check(g, ref, li.BF16, "GQA causal n65536 d128 (sampled rows)")
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
+def test_decode_B128_Hq32_Hkv8_d128_256_steps(gpu):
+    """Prefill a 4096-token prefix (state-only causal pass), then 256 decode
+    steps for 128 sequences; the oracle follows 4 sampled sequences."""
+    import torch
+    B, Hq, Hkv, d, P, T = 128, 32, 8, 128, 4096, 256
+    rng = np.random.default_rng(0)
+    s = 1 / np.sqrt(d)
+    kp = li.gaussian(rng, (B, Hkv, P, d), s, li.BF16)
+    vp = li.gaussian(rng, (B, Hkv, P, d), s, li.BF16)
+    steps = [tuple(li.gaussian(rng, shp, s, li.BF16) for shp in ((B, Hq, d), (B, Hkv, d), (B, Hkv, d)))
+             for _ in range(T)]
+    S, z = gpu.la_causal_forward(None, dev(kp), dev(vp), Hq=Hq)
+    sample = np.array([0, 37, 90, 127])
+    _, Sr, zr = oracle.causal(None, kp[sample], vp[sample], want_state=True, Hq=Hq)
+    np.testing.assert_allclose(S.cpu().numpy()[sample], Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
+    worst = 0.0
+    for t, (qs, ks, vs) in enumerate(steps):
+        o = gpu.la_decode_step(dev(qs), dev(ks), dev(vs), S, z)
+        ref = oracle.decode_step(qs[sample], ks[sample], vs[sample], Sr, zr)
+        if t % 32 == 0 or t == T - 1:
+            worst = max(worst, check(host(o)[sample], ref, li.BF16, f"decode step {t}"))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(S.cpu().numpy()[sample], Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy()[sample], zr, rtol=1e-5)
