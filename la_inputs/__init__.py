@@ -55,8 +55,11 @@ def to_f32(x: np.ndarray) -> np.ndarray:
 
 
 def to_torch(x: np.ndarray):
-    """Storage-format array -> CPU torch tensor (float32 or bfloat16)."""
+    """Storage-format array -> CPU torch tensor (float32, bfloat16, or an
+    integer array such as a prefix mask, passed through unchanged)."""
     import torch
+    if x.dtype in (np.int64, np.int32):
+        return torch.from_numpy(np.ascontiguousarray(x))
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))

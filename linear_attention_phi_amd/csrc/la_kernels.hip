@@ -120,14 +120,24 @@ __device__ __forceinline__ void st_accT(float* X, int ldx, const f32x16& acc, in
 }
 
 // ---------------------------------------------------------------- tile loads
+// What a tile copy holds: not written, the raw value, phi(x) = relu(x) + 1,
+// or relu(x).
+enum Xf { XF_NONE = 0, XF_ID = 1, XF_PHI = 2, XF_RELU = 3 };
+
+template <int X> __device__ __forceinline__ float xform(float x) {
+  if (X == XF_PHI) return phi_f(x);
+  if (X == XF_RELU) return fmaxf(x, 0.0f);
+  return x;
+}
+
 // Load C rows x DP features of one head (base = row 0 of the head, row stride
-// d) into LDS: tm[row][col] (token-major, stride DP+PAD) and/or
-// fm[col][row] (feature-major, stride C+PAD).  Row r of the tile is global
-// row (gidx ? gidx[r] : row0 + r) and exists for r < nvalid.  Missing rows and
-// the padding features col >= d are stored as 0 -- NOT phi(0) = 1, so that
-// they add nothing to any sum.  PHI applies phi to the loaded values.
+// d) into LDS: tm[row][col] (token-major, stride DP+PAD) transformed by TMX,
+// and/or fm[col][row] (feature-major, stride C+PAD) transformed by FMX.  Row r
+// of the tile is global row (gidx ? gidx[r] : row0 + r) and exists for
+// r < nvalid.  Missing rows and the padding features col >= d are stored as
+// 0 -- NOT phi(0) = 1 -- so that they add nothing to any sum.
 // vec: d == DP, 16-byte pieces (base and row stride are 16-byte aligned).
-template <typename T, int DP, int C, bool PHI, bool TM, bool FM>
+template <typename T, int DP, int C, int TMX, int FMX>
 __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t row0, const int* __restrict__ gidx,
                                           int nvalid, int d, bool vec, T* tm, T* fm, int tid) {
   if (vec) {
@@ -137,47 +147,54 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t ro
 #pragma unroll 2
     for (int p = tid; p < NP; p += NT) {
       const int row = p / PPR, col = (p % PPR) * EPP;
-      union { uint4 u; T e[EPP]; } val;
+      union V { uint4 u; T e[EPP]; };
+      V raw, a, b;
+      raw.u = make_uint4(0, 0, 0, 0);
       if (row < nvalid) {
         const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
-        val.u = *reinterpret_cast<const uint4*>(base + grow * DP + col);
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) {
-          float x = to_f(val.e[e]);
-          if (PHI) x = phi_f(x);
-          val.e[e] = cvt<T>(x);
-        }
-      } else {
-        val.u = make_uint4(0, 0, 0, 0);
+        raw.u = *reinterpret_cast<const uint4*>(base + grow * DP + col);
       }
-      if (TM) {
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        const float x = to_f(raw.e[e]);
+        a.e[e] = row < nvalid ? cvt<T>(xform<TMX>(x)) : cvt<T>(0.0f);
+        b.e[e] = row < nvalid ? cvt<T>(xform<FMX>(x)) : cvt<T>(0.0f);
+      }
+      if (TMX != XF_NONE) {
         T* dst = tm + row * (DP + PAD) + col;
         if (sizeof(T) == 4) {
-          *reinterpret_cast<uint4*>(dst) = val.u;
+          *reinterpret_cast<uint4*>(dst) = a.u;
         } else {  // rows of DP+PAD bf16 are only 8-byte aligned
-          reinterpret_cast<uint2*>(dst)[0] = make_uint2(val.u.x, val.u.y);
-          reinterpret_cast<uint2*>(dst)[1] = make_uint2(val.u.z, val.u.w);
+          reinterpret_cast<uint2*>(dst)[0] = make_uint2(a.u.x, a.u.y);
+          reinterpret_cast<uint2*>(dst)[1] = make_uint2(a.u.z, a.u.w);
         }
       }
-      if (FM) {
+      if (FMX != XF_NONE) {
 #pragma unroll
-        for (int e = 0; e < EPP; ++e) fm[(col + e) * (C + PAD) + row] = val.e[e];
+        for (int e = 0; e < EPP; ++e) fm[(col + e) * (C + PAD) + row] = b.e[e];
       }
     }
   } else {
     for (int idx = tid; idx < C * DP; idx += NT) {
       const int row = idx / DP, col = idx % DP;
       float x = 0.0f;
-      if (row < nvalid && col < d) {
+      const bool ok = row < nvalid && col < d;
+      if (ok) {
         const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
         x = to_f(base[grow * d + col]);
-        if (PHI) x = phi_f(x);
       }
-      const T t = cvt<T>(x);
-      if (TM) tm[row * (DP + PAD) + col] = t;
-      if (FM) fm[col * (C + PAD) + row] = t;
+      if (TMX != XF_NONE) tm[row * (DP + PAD) + col] = cvt<T>(ok ? xform<TMX>(x) : 0.0f);
+      if (FMX != XF_NONE) fm[col * (C + PAD) + row] = cvt<T>(ok ? xform<FMX>(x) : 0.0f);
     }
   }
+}
+
+// Sum of the C entries of LDS row r (stride C+PAD), in order.
+template <typename T, int C>
+__device__ __forceinline__ float row_sum(const T* X, int r) {
+  float sum = 0.0f;
+  for (int t = 0; t < C; ++t) sum += to_f(X[r * (C + PAD) + t]);
+  return sum;
 }
 
 // Number of 32x32 state blocks (a-block, b-block) each wave owns.
@@ -201,6 +218,14 @@ __device__ __forceinline__ void st_state_block(float* __restrict__ S, const f32x
   for (int r = 0; r < 16; ++r) S[(ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * DP + b] = acc[r];
 }
 
+// acc[a][b] += add (lane's column b) for the rows a < d of block row ma.
+__device__ __forceinline__ void add_col(f32x16& acc, float add, int ma, int d, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3) < d) acc[r] += add;
+}
+
 // Per-head slot layout of the state workspace: (nseg + 1) slots of
 // DP*DP + DP floats (S row-major [a][b], then z[a]); slot s < nseg holds the
 // aggregate of segment s (after k_scan: the exclusive prefix before segment
@@ -208,12 +233,17 @@ __device__ __forceinline__ void st_state_block(float* __restrict__ S, const f32x
 __host__ __device__ __forceinline__ int64_t slot_elems(int DP) { return (int64_t)DP * DP + DP; }
 
 // ------------------------------------------------------------------ k_state
+// With PHI the state is built as phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t
+// and z = sum_t relu(K_t) + (number of keys): relu of an input value is
+// exact in the input type, so the MFMA products are exact and the state is
+// exact up to fp32 summation (rounding phi(K) to bf16 would not be).
 template <typename T, int DP, int C, bool PHI>
 __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* __restrict__ v, int64_t n, int d,
                                               bool vec, int64_t nchunks, int64_t G, int64_t nseg,
                                               float* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) T sKT[DP * (C + PAD)];
   __shared__ __attribute__((aligned(16))) T sVT[DP * (C + PAD)];
+  __shared__ float svs[DP];
   using SB = StateBlocks<DP>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
@@ -222,13 +252,13 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
   f32x16 accS[SB::PER_WAVE];
 #pragma unroll
   for (int s = 0; s < SB::PER_WAVE; ++s) accS[s] = f32x16{};
-  float zrun = 0.0f;
+  float zrun = 0.0f, vrun = 0.0f;
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
-    load_tile<T, DP, C, PHI, false, true>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
-    load_tile<T, DP, C, false, false, true>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    load_tile<T, DP, C, XF_NONE, PHI ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
+    load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
@@ -238,12 +268,20 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
         gemm_acc<T, C / 16>(accS[s], sKT + ma * 32 * (C + PAD), C + PAD, sVT + nb * 32 * (C + PAD), C + PAD, lane);
       }
     }
-    if (tid < DP) {
-      float sum = 0.0f;
-      for (int t = 0; t < C; ++t) sum += to_f(sKT[tid * (C + PAD) + t]);
-      zrun += sum;
+    if (PHI && tid < DP) {
+      zrun += row_sum<T, C>(sKT, tid) + (tid < d ? (float)nv : 0.0f);
+      vrun += row_sum<T, C>(sVT, tid);
     }
     __syncthreads();
+  }
+  if (PHI) {
+    if (tid < DP) svs[tid] = vrun;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < SB::PER_WAVE; ++s) {
+      const int e = w + NW * s;
+      if (e < SB::TOTAL) add_col(accS[s], svs[(e % SB::NB) * 32 + (lane & 31)], e / SB::NB, d, lane);
+    }
   }
   float* dst = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
 #pragma unroll
@@ -303,6 +341,7 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
   __shared__ __attribute__((aligned(16))) T sST[DP * LQ];
   __shared__ __attribute__((aligned(16))) T sP[C * LC];
   __shared__ float sz[DP];
+  __shared__ float svc[DP];  // sum of V over the chunks done so far (see k_state)
   using SB = StateBlocks<DP>;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
@@ -326,8 +365,13 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
       else accS[s] = f32x16{};
     }
   }
-  float zrun = 0.0f;
+  // The accumulators hold relu(K)^T V terms on top of the exclusive prefix;
+  // S = accS + 1 (x) vrun over the rows a < d (vrun: sum of V since the
+  // segment start).  z is carried exactly in zrun.
+  float zrun = 0.0f, vrun = 0.0f;
   if (NORM && tid < DP) zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + tid];
+  if (NORM && tid < DP) svc[tid] = 0.0f;
+  if (NORM) __syncthreads();
 
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
   for (int64_t c = c0; c < c1; ++c) {
@@ -342,14 +386,16 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
       ngroups = (int)((cnt + C - 1) / C);
     }
 
-    load_tile<T, DP, C, NORM, true, true>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
-    load_tile<T, DP, C, false, false, true>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, NORM ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
+    load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
       const int e = w + NW * s;
       if (e < SB::TOTAL) {
         const int ma = e / SB::NB, nb = e % SB::NB;
-        st_accT(sST + nb * 32 * LQ + ma * 32, LQ, accS[s], lane);  // sST[b][a] = S[a][b]
+        f32x16 cur = accS[s];
+        if (NORM) add_col(cur, svc[nb * 32 + (lane & 31)], ma, d, lane);
+        st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
       }
     }
     if (NORM && tid < DP) sz[tid] = zrun;
@@ -370,7 +416,7 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
         gidx = perm + s0;
       }
       if (grp > 0) __syncthreads();  // previous group is done with sQ / sP
-      load_tile<T, DP, C, NORM, true, false>(qb, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
+      load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, XF_NONE>(qb, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
       __syncthreads();
 
       // ---- P^T blocks (key block jb, query block ib2), masked, -> sP[i][j]
@@ -459,9 +505,9 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
       }
     }
     if (NORM && tid < DP) {
-      float sum = 0.0f;
-      for (int t = 0; t < C; ++t) sum += to_f(sKT[tid * LC + t]);
-      zrun += sum;
+      zrun += row_sum<T, C>(sKT, tid) + (tid < d ? (float)nv : 0.0f);
+      vrun += row_sum<T, C>(sVT, tid);
+      svc[tid] = vrun;  // read at the next chunk's start, after the barrier below
     }
     __syncthreads();
   }
@@ -500,7 +546,7 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
     for (int r = 0; r < R; ++r) {
       const T* qb = q + (bh * R + r) * n * d;
       __syncthreads();  // sQ free (and sST / sz visible on the first pass)
-      load_tile<T, DP, C, true, true, false>(qb, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
+      load_tile<T, DP, C, XF_PHI, XF_NONE>(qb, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
       __syncthreads();
       if (has_out) {
         const int i = ib * 32 + (lane & 31);

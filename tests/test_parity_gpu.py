@@ -32,6 +32,16 @@ def rel_rows(g, o):
     return float((num / np.maximum(den, 1e-30)).max())
 
 
+def fit_chunk(gpu, dtype, d, chunk):
+    """The requested chunk if the library offers it for this dtype and head
+    dim (it must fit one CU's LDS), else the largest smaller one."""
+    code = gpu.LA_F32 if dtype == li.F32 else gpu.LA_BF16
+    for c in [chunk] + [c for c in (128, 64, 32) if c < (chunk or 65)]:
+        if gpu.la_workspace_bytes(gpu.LA_OP_CAUSAL, 1, 1, 1, 64, d, code, c) > 0:
+            return c
+    raise AssertionError("no chunk size fits")
+
+
 def check(g, o, dtype, what):
     err = rel_rows(g, o)
     print(f"{what}: row-wise rel err {err:.3e} (tol {TOL[dtype]:.0e})", flush=True)
@@ -92,8 +102,7 @@ def test_noncausal_small(gpu, dtype, case):
 @pytest.mark.parametrize("case", SMALL, ids=_small_id)
 def test_causal_small(gpu, dtype, case):
     B, Hq, Hkv, n, d, chunk = case
-    if dtype == li.F32 and d > 64 and chunk > 32:
-        chunk = 32  # fp32 at d = 128 fits LDS only with 32-token chunks
+    chunk = fit_chunk(gpu, dtype, d, chunk)
     q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=1, scaled=True)
     out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=chunk, want_state=True)
     ref, Sr, zr = oracle.causal(q, k, v, want_state=True)
@@ -107,8 +116,7 @@ def test_causal_small(gpu, dtype, case):
 @pytest.mark.parametrize("case", SMALL[:8], ids=_small_id)
 def test_prefix_small(gpu, dtype, kind, case):
     B, H, _, n, d, chunk = case
-    if dtype == li.F32 and d > 64 and chunk > 32:
-        chunk = 32
+    chunk = fit_chunk(gpu, dtype, d, chunk)
     q, k, v, rng = li.qkv(B, H, H, n, d, dtype, seed=2, scaled=True)
     m = li.mask(n, kind, rng=rng)
     g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=chunk))
@@ -128,7 +136,11 @@ def test_chunk_size_invariance(gpu, dtype):
     """The chunk length only changes rounding: 32, 64 and 128 agree with the oracle."""
     q, k, v, _ = li.qkv(2, 4, 2, 777, 64, dtype, seed=5, scaled=True)
     ref = oracle.causal(q, k, v)
-    for chunk in (32, 64, 128):
+    code = gpu.LA_F32 if dtype == li.F32 else gpu.LA_BF16
+    chunks = [c for c in (32, 64, 128)
+              if gpu.la_workspace_bytes(gpu.LA_OP_CAUSAL, 2, 4, 2, 777, 64, code, c) > 0]
+    assert len(chunks) >= 2
+    for chunk in chunks:
         g = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=chunk))
         check(g, ref, dtype, f"causal chunk {chunk}")
 
