@@ -73,6 +73,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the benchmark, run plain device-to-device copies of 64 MiB "
+                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -90,6 +93,16 @@ def main():
     la.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # 10 rotating 64 MiB sources (640 MiB > the 256 MiB MALL); each copy
+        # moves 64 MiB in and 64 MiB out
+        src = [torch.full((64 << 20,), i, dtype=torch.uint8, device=dev) for i in range(ROTATE)]
+        dst = torch.empty_like(src[0])
+        for i in range(args.warmup + args.steps):
+            dst.copy_(src[i % ROTATE])
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": 64 << 20, "copies": args.warmup + args.steps}))
+        return
     q, k, v, _ = li.qkv(B, H, H, N, D, li.BF16, seed=0, scaled=True)
     qd, kd, vd = (li.to_torch(x).to(dev) for x in (q, k, v))
     sets = [(qd.clone(), kd.clone(), vd.clone(), torch.empty_like(qd)) for _ in range(ROTATE)]

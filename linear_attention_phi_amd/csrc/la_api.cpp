@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "la_internal.h"
 
 namespace la_internal {
@@ -31,6 +33,16 @@ Plan make_plan(int op, int64_t B, int64_t Hkv, int64_t n, int64_t d, int elem_by
   p.G = G;
   p.nseg = (p.nchunks + G - 1) / G;
   (void)elem_bytes;
+  return p;
+}
+
+Plan make_fused_plan(int64_t n) {
+  Plan p;
+  p.DP = 64;
+  p.C = 64;
+  p.nchunks = (n + 63) / 64;
+  p.G = kFusedG;
+  p.nseg = (p.nchunks + kFusedG - 1) / kFusedG;
   return p;
 }
 
@@ -91,8 +103,18 @@ size_t required_ws(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, in
   if (out_plan) *out_plan = p;
   size_t bytes = state_bytes(p, B, Hkv);
   if (op == LA_OP_PREFIX_MASK) bytes += bucket_bytes(n, C);
+  if (op == LA_OP_CAUSAL && fused_causal_applies(Hq, Hkv, n, d, (int)dt, C)) {
+    const size_t f = fused_causal_ws_bytes(B * Hkv, make_fused_plan(n).nseg);
+    if (f > bytes) bytes = f;
+  }
   return bytes;
 }
+
+// Flags of the single-launch causal kernel carry a per-call epoch; the top
+// bits 0xFFF8 make every epoch a NaN pattern, which no float state or index
+// stored in a workspace can equal.
+std::atomic<uint64_t> g_epoch{0};
+uint64_t next_epoch() { return 0xFFF8000000000000ull | (g_epoch.fetch_add(1, std::memory_order_relaxed) + 1); }
 
 la_status check_grid(const Plan& p, int64_t B, int64_t Hkv) {
   if (B * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
@@ -192,6 +214,11 @@ la_status la_causal_forward(const void* q, const void* k, const void* v, int64_t
   if (overlaps(ws, need, out, qb) || overlaps(ws, need, S_final, sb) || overlaps(ws, need, z_final, zb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream};
+  if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {
+    const Plan fp = make_fused_plan(n);
+    if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
+    return launch_causal_fused(a, fp, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
+  }
   return launch_causal(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 

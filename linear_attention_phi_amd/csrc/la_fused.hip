@@ -1,0 +1,593 @@
+// la_fused.hip -- single-launch causal kernel for bf16 inputs, d = 64,
+// chunk 64, one query head per key/value head (gfx950).
+//
+// Same mathematics as the three-launch path in la_kernels.hip (causal form:
+// out_i = phi(Q_i) S_i / (phi(Q_i) . z_i) with S_i, z_i over keys 0..i;
+// nx_f32_linear_attention.nx for phi, S, z and the read; trim-transformer
+// 0.1.0 "Masking" for the causal prefix), organised so that every input
+// byte is read from HBM once and every output byte written once:
+//
+//  phase 1  a workgroup walks the G chunks of its segment with a state S_loc
+//           that starts at zero at the segment start; per chunk it builds
+//           the un-normalised numerator
+//             num_c = phi(Q_c) S_loc + tril(phi(Q_c) phi(K_c)^T) V_c
+//           and denominator den_c in registers, then S_loc += phi(K_c)^T V_c;
+//  phase 2  it publishes its segment aggregate (S_loc, z_loc) and sums the
+//           aggregates of all earlier segments of the head (waiting on their
+//           flags): S_prev, z_prev;
+//  phase 3  out_c = (num_c + phi(Q_c) S_prev) / (den_c + phi(Q_c) . z_prev).
+//
+// Waves: wave w owns query block ib = w & 1 and feature block nb = w >> 1 of
+// the 64 x 64 output tile, and keeps S_loc[:, nb] (both 32-row blocks) in
+// MFMA accumulators, which feed the phi(Q) S products directly as A
+// operands.  P^T = phi(K) phi(Q)^T is computed per wave for its query block;
+// its accumulators are the B operand of the V^T P^T product (see
+// la_device.h), so P never goes through LDS.  phi(K)^T V is formed as
+// relu(K)^T V + 1 (x) sum_t V_t (exact products; see la_kernels.hip).
+//
+// Segments are numbered segment-major (blockIdx = seg * NH + head), so a
+// workgroup only ever waits for workgroups dispatched before it.  Flags are
+// 64-bit words holding a per-call epoch (top bits 0xFFF8: a NaN pattern, so
+// no float or index the workspace held before can equal one).  Spins are
+// bounded; exhausting the bound records an error bit instead of hanging.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace {
+
+using namespace la_dev;
+
+constexpr int FD = 64;        // head dim
+constexpr int FC = 64;        // chunk
+constexpr int LT = FD + PAD;  // token-major LDS row stride (elements)
+constexpr int LF = FC + PAD;  // feature-major LDS row stride
+constexpr int AGG_FLOATS = 4 * 64 * 16 + FD;  // published segment aggregate: 4 blocks in lane order + z
+
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int G = 4;           // chunks per group (4 waves)
+constexpr int NGRP = 2;        // groups per workgroup: a segment is G * NGRP chunks
+constexpr int FNT = NT * NGRP; // threads per workgroup
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16x2 t = {(bf16)lo, (bf16)hi};
+  return __builtin_bit_cast(uint32_t, t);
+}
+__device__ __forceinline__ float lo_f(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_f(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+// relu of two packed bf16 values: as 16-bit integers, max(x, 0) keeps every
+// value whose sign bit is clear and sends the others (including -0) to +0
+__device__ __forceinline__ uint32_t relu2(uint32_t x) {
+  const s16x2 z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, x), z));
+}
+// phi = relu + 1 of two packed bf16 values, rounded to nearest-even bf16
+__device__ __forceinline__ uint32_t phi2(uint32_t x) {
+  const uint32_t r = relu2(x);
+  return pack2(lo_f(r) + 1.0f, hi_f(r) + 1.0f);
+}
+// a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs, accumulated in fp32
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ uint32_t pair(const Frag<bf16>& f, int p) {
+  return __builtin_bit_cast(u32x4, f.v)[p];
+}
+constexpr uint32_t ONE2 = 0x3F803F80u;  // two bf16 ones
+
+// Registers holding one chunk's inputs between its global loads and its LDS
+// writes.  Thread t (of a group's 256) handles rows 2 * (t >> 3) and
+// 2 * (t >> 3) + 1, features 8 * (t & 7) .. +7, of both K and V, and the
+// 16-byte Q pieces t and t + 256 (row p >> 3, features 8 * (p & 7) .. +7).
+// Rows past the sequence end load as zero.
+struct Stage {
+  u32x4 k2[2], v2[2], qp[2];
+};
+
+// Rows past the sequence end are read as the last row (always in bounds);
+// stage_store zeroes what must be zero.
+__device__ __forceinline__ void stage_load(Stage& st, const bf16* __restrict__ qh, const bf16* __restrict__ kh,
+                                           const bf16* __restrict__ vh, int64_t t0, int nv, int tid) {
+  const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int64_t off = (t0 + (r0 + r < nv ? r0 + r : nv - 1)) * FD + c0;
+    st.k2[r] = *reinterpret_cast<const u32x4*>(kh + off);
+    st.v2[r] = *reinterpret_cast<const u32x4*>(vh + off);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int p = tid + 256 * u, row = p >> 3, col = 8 * (p & 7);
+    st.qp[u] = *reinterpret_cast<const u32x4*>(qh + (t0 + (row < nv ? row : nv - 1)) * FD + col);
+  }
+}
+
+// Two rows x 8 features -> 8 feature rows of 2 tokens (one dword each).
+__device__ __forceinline__ void store_pairs_transposed(bf16* fm, int r0, int c0, const uint32_t (&x)[2][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint32_t*>(fm + (c0 + 2 * j) * LF + r0) = (x[0][j] & 0xFFFFu) | (x[1][j] << 16);
+    *reinterpret_cast<uint32_t*>(fm + (c0 + 2 * j + 1) * LF + r0) = (x[0][j] >> 16) | (x[1][j] & 0xFFFF0000u);
+  }
+}
+
+// The LDS of one group.
+struct GroupLds {
+  bf16 sQ[G][FC * LT];     // phi(Q) of every chunk of the group (kept for the last phase)
+  bf16 sK[FC * LT];        // relu(K), token-major
+  bf16 sKT[FD * LF];       // relu(K), feature-major
+  bf16 sVT[FD * LF];       // V, feature-major
+  bf16 sST[FD * LT];       // S_prev^T in bf16 (last phase)
+  uint32_t zh[2][FD / 2];  // z so far as bf16 pairs, high part (double-buffered by chunk parity)
+  uint32_t zl[2][FD / 2];  // ... and the low part: z = zh + zl to about 2^-17
+  float szp[FD];           // z_prev in fp32 (for the final state)
+  uint32_t zph[FD / 2];    // z_prev as bf16 (high, low) pairs (last phase)
+  uint32_t zpl[FD / 2];
+  float sinv[G][FC];       // 1 / normaliser per chunk and query (last phase)
+  u32x4 sSx[4][64][2];     // running state block (ma, nb) in bf16, operand order per lane
+};
+
+// Stage -> LDS: sQ[c][i][a] = phi(Q), sK[j][a] = relu(K), sKT[a][t] = relu(K),
+// sVT[b][t] = V.  Rows t >= nv of sKT and sVT are zero (they enter sums over
+// all 64 rows); the other copies of such rows only meet masked-out entries.
+// The empty asm statement pins the use of the staged registers here, so that
+// the compiler does not move this work -- and the wait for its loads --
+// ahead of earlier chunks.
+__device__ __forceinline__ void stage_store(Stage& st, bf16* sQc, GroupLds& L, int nv, int tid) {
+  asm volatile("" : "+v"(st.k2[0]), "+v"(st.k2[1]), "+v"(st.v2[0]), "+v"(st.v2[1]), "+v"(st.qp[0]), "+v"(st.qp[1])
+               :
+               : "memory");
+  const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
+  uint32_t xk[2][4], xv[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint32_t keep = (r0 + r < nv) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xk[r][j] = relu2(st.k2[r][j]) & keep;
+      xv[r][j] = st.v2[r][j] & keep;
+    }
+    uint2* dst = reinterpret_cast<uint2*>(L.sK + (r0 + r) * LT + c0);
+    dst[0] = make_uint2(xk[r][0], xk[r][1]);
+    dst[1] = make_uint2(xk[r][2], xk[r][3]);
+  }
+  store_pairs_transposed(L.sKT, r0, c0, xk);
+  store_pairs_transposed(L.sVT, r0, c0, xv);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int p = tid + 256 * u, row = p >> 3, col = 8 * (p & 7);
+    uint2* dst = reinterpret_cast<uint2*>(sQc + row * LT + col);
+    dst[0] = make_uint2(phi2(st.qp[u][0]), phi2(st.qp[u][1]));
+    dst[1] = make_uint2(phi2(st.qp[u][2]), phi2(st.qp[u][3]));
+  }
+}
+
+// Operand fragment from accumulator registers 8 * half .. 8 * half + 7, in bf16.
+__device__ __forceinline__ Frag<bf16> acc_frag(const f32x16& acc, int half) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)acc[8 * half + e];
+  return f;
+}
+
+// One half (this lane's 32 features) of phi(Q_i) . z with z given as bf16
+// (high, low) pairs; the other half lives in lane l ^ 32.
+__device__ __forceinline__ float half_dot_pairs(const Frag<bf16> (&qf)[4], const uint32_t* zh, const uint32_t* zl, int h) {
+  float s = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int zi = 8 * kb + 2 * h + (p & 1) + 4 * (p >> 1);  // pair index of features a, a + 1
+      s = dot2(pair(qf[kb], p), zh[zi], s);
+      s = dot2(pair(qf[kb], p), zl[zi], s);
+    }
+  }
+  return s;
+}
+// Cross-workgroup data (segment aggregates) is written and read with
+// device-scope (sc1) buffer accesses, which gfx950 performs at the device
+// coherence point, so no L2 writeback or invalidate is needed.  Order: each
+// wave waits for its aggregate stores to complete (s_waitcnt vmcnt(0)) before
+// the workgroup barrier; only then does one thread store the flag (an
+// agent-scope atomic).  A reader observes the flag, passes a barrier, and only
+// then issues its sc1 aggregate loads.
+constexpr int CPOL_SC1 = 16;  // cache-policy bit of buffer instructions: device scope
+
+__device__ __forceinline__ void st_sc1(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4v x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, byte_off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ f32x4v ld_sc1(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, CPOL_SC1));
+}
+
+struct FusedArgs {
+  const bf16* q; const bf16* k; const bf16* v; bf16* out;
+  int64_t n, nchunks, nseg, NH;
+  float* agg; uint64_t* flags; uint64_t epoch;
+  float* S_final; float* z_final; uint32_t* err;
+};
+
+// Write z values held one per lane (feature a = a0 + lane index within the
+// writing lanes) into the (high, low) bf16 pair arrays: even lanes pair with
+// their right neighbour.  All 64 lanes must call it; lanes with write set and
+// an even feature store.
+__device__ __forceinline__ void store_z_pairs(uint32_t* zh, uint32_t* zl, float z, int a, bool write) {
+  const float zn = __shfl_down(z, 1);
+  if (write && (a & 1) == 0) {
+    const uint32_t hi = pack2(z, zn);
+    zh[a >> 1] = hi;
+    zl[a >> 1] = pack2(z - lo_f(hi), zn - hi_f(hi));
+  }
+}
+
+// The work of one wave of group g; IB (its query block) is a template
+// parameter so that the causal block structure and masks are resolved at
+// compile time.  Every wave of the workgroup executes the same sequence of
+// barriers.
+template <int IB>
+__device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NGRP], float* xch) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
+  const int g = w >> 2;         // group
+  const int nb = (w >> 1) & 1;  // feature block; nb == 0 waves also own the normaliser, nb == 1 waves z
+  const int tg = tid & (NT - 1);
+  GroupLds& L = LL[g];
+  const int64_t seg = blockIdx.x / A.NH, head = blockIdx.x % A.NH;
+  const bf16* qh = A.q + head * A.n * FD;
+  const bf16* kh = A.k + head * A.n * FD;
+  const bf16* vh = A.v + head * A.n * FD;
+  const int64_t c_begin = seg * (G * NGRP) + g * G;
+  const int64_t rem = A.nchunks - c_begin;
+  const int ncl = (int)(rem < 0 ? 0 : (rem < G ? rem : G));
+  const int i = IB * 32 + r;  // this lane's query row within a chunk
+
+  // loads run two chunks ahead of the chunk being computed
+  Stage st[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c < ncl) {
+      const int64_t t0 = (c_begin + c) * FC;
+      stage_load(st[c], qh, kh, vh, t0, (int)((A.n - t0) < FC ? (A.n - t0) : FC), tg);
+    }
+  }
+
+  // ---------------------------------------------------------------- phase 1
+  // S_acc: block (ma = IB, nb) of phi(K)^T V over the group's chunks so far,
+  // built as relu(K)^T V + ones^T V (exact products).  The partner wave
+  // (1 - IB, nb) holds block (1 - IB, nb); the two swap bf16 copies through
+  // LDS once per chunk for the phi(Q) S products.
+  f32x16 S_acc = f32x16{};
+  float zloc = 0.0f;  // (nb == 1) z so far for a = 32 IB + r
+  f32x16 OUT[G];
+  float den[G];
+  if (tg < FD / 2) {
+    L.zh[0][tg] = 0u;
+    L.zl[0][tg] = 0u;
+  }
+  Frag<bf16> ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones.v[e] = (bf16)1.0f;
+  // causal mask of the diagonal P^T block: element e holds key row
+  // 8 (e >> 2) + 4 h + (e & 3) of query row r
+  bool keep[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) keep[e] = 8 * (e >> 2) + 4 * h + (e & 3) <= r;
+
+#pragma unroll
+  for (int c = 0; c < G; ++c) {
+    // own state block S_loc(c) as operand fragments, also handed to the partner
+    Frag<bf16> sown[2];
+    if (c > 0 && c < ncl) {
+      sown[0] = acc_frag(S_acc, 0);
+      sown[1] = acc_frag(S_acc, 1);
+      L.sSx[IB * 2 + nb][lane][0] = __builtin_bit_cast(u32x4, sown[0].v);
+      L.sSx[IB * 2 + nb][lane][1] = __builtin_bit_cast(u32x4, sown[1].v);
+    }
+    if (c < ncl) {
+      const int64_t t0 = (c_begin + c) * FC;
+      stage_store(st[c & 1], L.sQ[c], L, (int)((A.n - t0) < FC ? (A.n - t0) : FC), tg);
+      if (c + 2 < ncl) {
+        const int64_t t2 = t0 + 2 * FC;
+        stage_load(st[c & 1], qh, kh, vh, t2, (int)((A.n - t2) < FC ? (A.n - t2) : FC), tg);
+      }
+    }
+    __syncthreads();
+    if (c < ncl) {
+      const int64_t t0 = (c_begin + c) * FC;
+      const int nv = (int)((A.n - t0) < FC ? (A.n - t0) : FC);
+      Frag<bf16> qf[4], vt[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) ld_frag(vt[kt], L.sVT + (nb * 32 + r) * LF + 16 * kt + 4 * h);
+      // sum_a phi(Q_i)[a]: P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
+      float sq = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) sq = dot2(pair(qf[kb], p), ONE2, sq);
+      sq += __shfl_xor(sq, 32);
+
+      // P^T blocks for key blocks jb <= IB; only the diagonal block is masked
+      Frag<bf16> pfr[IB + 1][2];
+      float rsum = 0.0f;
+#pragma unroll
+      for (int jb = 0; jb <= IB; ++jb) {
+        f32x16 pacc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pacc[e] = sq;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          Frag<bf16> kf;
+          ld_frag(kf, L.sK + (jb * 32 + r) * LT + 16 * kb + 4 * h);
+          mma(pacc, kf, qf[kb]);
+        }
+        if (jb == IB) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) pacc[e] = keep[e] ? pacc[e] : 0.0f;
+        }
+        pfr[jb][0] = acc_frag(pacc, 0);
+        pfr[jb][1] = acc_frag(pacc, 1);
+        if (nb == 0) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) rsum = dot2(pair(pfr[jb][1], p), ONE2, dot2(pair(pfr[jb][0], p), ONE2, rsum));
+        }
+      }
+
+      // num_c = phi(Q) S_loc + V^T P^T   (rows b of block nb, column i)
+      f32x16 o = f32x16{};
+      if (c > 0) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          Frag<bf16> sa;
+          if ((kb >> 1) == IB)
+            sa = sown[kb & 1];
+          else
+            sa.v = __builtin_bit_cast(bf16x8v, L.sSx[(1 - IB) * 2 + nb][lane][kb & 1]);
+          mma(o, sa, qf[kb]);
+        }
+      }
+#pragma unroll
+      for (int jb = 0; jb <= IB; ++jb) {
+        mma(o, vt[2 * jb], pfr[jb][0]);
+        mma(o, vt[2 * jb + 1], pfr[jb][1]);
+      }
+      OUT[c] = o;
+      if (nb == 0) {
+        const float dpart = half_dot_pairs(qf, L.zh[c & 1], L.zl[c & 1], h) + rsum;
+        den[c] = dpart + __shfl_xor(dpart, 32);
+      }
+
+      // S_loc += relu(K)^T V + ones^T V for block (IB, nb); z (nb == 1 waves)
+      float zp = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        Frag<bf16> kf;
+        ld_frag(kf, L.sKT + (IB * 32 + r) * LF + 16 * kt + 4 * h);
+        mma(S_acc, kf, vt[kt]);
+        mma(S_acc, ones, vt[kt]);
+        if (nb == 1) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) zp = dot2(pair(kf, p), ONE2, zp);
+        }
+      }
+      if (nb == 1) {
+        zloc += zp + __shfl_xor(zp, 32) + (float)nv;
+        store_z_pairs(L.zh[(c + 1) & 1], L.zl[(c + 1) & 1], zloc, IB * 32 + r, h == 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- phase 2
+  // group 0 hands its aggregate (block (IB, nb) in lane order, and z) to
+  // group 1 through LDS; group 1 publishes the segment's aggregate.
+  float* xz = xch + 4 * 64 * 16;
+  if (g == 0) {
+    f32x4v* d4 = reinterpret_cast<f32x4v*>(xch + ((IB * 2 + nb) * 64 + lane) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d4[u] = f32x4v{S_acc[4 * u], S_acc[4 * u + 1], S_acc[4 * u + 2], S_acc[4 * u + 3]};
+    if (nb == 1 && h == 0) xz[IB * 32 + r] = zloc;
+  }
+  __syncthreads();
+  f32x16 a0 = f32x16{};  // (group 1) group 0's aggregate block
+  float za0 = 0.0f;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(A.agg + head * A.nseg * AGG_FLOATS, 0, (int)(A.nseg * AGG_FLOATS * 4), 0x00020000);
+  const int blk = ((IB * 2 + nb) * 64 + lane) * 64;  // byte offset of this lane's block values in an aggregate
+  if (g == 1) {
+    const f32x4v* s4 = reinterpret_cast<const f32x4v*>(xch + ((IB * 2 + nb) * 64 + lane) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4v x = s4[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a0[4 * u + e] = x[e];
+    }
+    za0 = xz[IB * 32 + r];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      st_sc1(rs, (int)(seg * AGG_FLOATS * 4) + blk + 16 * u,
+             f32x4v{a0[4 * u] + S_acc[4 * u], a0[4 * u + 1] + S_acc[4 * u + 1],
+                    a0[4 * u + 2] + S_acc[4 * u + 2], a0[4 * u + 3] + S_acc[4 * u + 3]});
+    if (nb == 1 && h == 0)
+      __hip_atomic_store(A.agg + (head * A.nseg + seg) * AGG_FLOATS + 4 * 64 * 16 + IB * 32 + r, za0 + zloc,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's aggregate stores have completed
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(A.flags + head * A.nseg + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  if (seg > 0) {
+    if (w == 0) {
+      for (int64_t p = lane; p < seg; p += 64) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(A.flags + head * A.nseg + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != A.epoch) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > (1u << 22)) {
+            atomicOr(A.err, 1u);
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // S_prev of the segment (block (IB, nb)) and z_prev, summed over earlier
+  // segments in order, two segments' loads in flight at a time; group 1 adds
+  // group 0's aggregate.
+  f32x16 sp = f32x16{};
+  float zprev = 0.0f;
+  const bool zlane = (w & 3) == 0;  // wave 0 of each group sums z (lane = feature)
+  {
+    int64_t p = 0;
+    for (; p + 1 < seg; p += 2) {
+      f32x4v x[4], y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = ld_sc1(rs, (int)(p * AGG_FLOATS * 4) + blk + 16 * u);
+        y[u] = ld_sc1(rs, (int)((p + 1) * AGG_FLOATS * 4) + blk + 16 * u);
+      }
+      float zx = 0.0f, zy = 0.0f;
+      if (zlane) {
+        zx = __hip_atomic_load(A.agg + (head * A.nseg + p) * AGG_FLOATS + 4 * 64 * 16 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        zy = __hip_atomic_load(A.agg + (head * A.nseg + p + 1) * AGG_FLOATS + 4 * 64 * 16 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[4 * u + e] += x[u][e];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[4 * u + e] += y[u][e];
+      zprev += zx;
+      zprev += zy;
+    }
+    if (p < seg) {
+      f32x4v x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = ld_sc1(rs, (int)(p * AGG_FLOATS * 4) + blk + 16 * u);
+      float zx = 0.0f;
+      if (zlane)
+        zx = __hip_atomic_load(A.agg + (head * A.nseg + p) * AGG_FLOATS + 4 * 64 * 16 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sp[4 * u + e] += x[u][e];
+      zprev += zx;
+    }
+  }
+  if (g == 1) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sp[e] += a0[e];
+    if (zlane) zprev += xz[lane];
+  }
+  st_accT(L.sST + nb * 32 * LT + IB * 32, LT, sp, lane);  // sST[b][a] = S_prev[a][b]
+  if (zlane) {
+    L.szp[lane] = zprev;
+    store_z_pairs(L.zph, L.zpl, zprev, lane, true);
+  }
+  if (A.S_final && g == 1 && seg == A.nseg - 1) {
+    float* Sf = A.S_final + head * FD * FD;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int a = IB * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      Sf[a * FD + nb * 32 + r] = sp[e] + S_acc[e];
+    }
+  }
+  __syncthreads();
+  if (A.z_final && g == 1 && seg == A.nseg - 1 && nb == 1 && h == 0)
+    A.z_final[head * FD + IB * 32 + r] = L.szp[IB * 32 + r] + zloc;
+
+  // ---------------------------------------------------------------- phase 3
+  // waves with nb == 0 finish the normalisers and share them through LDS
+  if (nb == 0) {
+#pragma unroll
+    for (int c = 0; c < G; ++c) {
+      if (c < ncl) {
+        Frag<bf16> qf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
+        const float zq = half_dot_pairs(qf, L.zph, L.zpl, h);
+        const float zt = zq + __shfl_xor(zq, 32);  // every lane takes part in the exchange
+        if (h == 0) L.sinv[c][i] = __builtin_amdgcn_rcpf(den[c] + zt);
+      }
+    }
+  }
+  __syncthreads();
+  const bool has_prev = seg > 0 || g > 0;
+  Frag<bf16> sf[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) ld_frag(sf[kb], L.sST + (nb * 32 + r) * LT + 16 * kb + 4 * h);
+#pragma unroll
+  for (int c = 0; c < G; ++c) {
+    if (c < ncl) {
+      f32x16 o = OUT[c];
+      if (has_prev) {
+        Frag<bf16> qf[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(o, sf[kb], qf[kb]);
+      }
+      const float inv = L.sinv[c][i];
+      const int64_t row = (c_begin + c) * FC + i;
+      if (row < A.n) {
+        bf16* orow = A.out + (head * A.n + row) * FD + nb * 32 + 4 * h;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *reinterpret_cast<uint2*>(orow + 8 * qq) =
+              make_uint2(pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv), pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
+  __shared__ __attribute__((aligned(16))) GroupLds LL[NGRP];
+  // group 0's K / V tiles are free after the first phase: they carry the
+  // hand-off of group 0's aggregate (AGG_FLOATS floats) to group 1
+  float* xch = reinterpret_cast<float*>(LL[0].sK);
+  static_assert(sizeof(LL[0].sK) + sizeof(LL[0].sKT) + sizeof(LL[0].sVT) >= AGG_FLOATS * sizeof(float),
+                "hand-off area too small");
+  if (((threadIdx.x >> 6) & 1) == 0)
+    fused_wave<0>(A, LL, xch);
+  else
+    fused_wave<1>(A, LL, xch);
+}
+
+}  // namespace
+
+namespace la_internal {
+
+bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk) {
+  // n bound: one head's aggregates must stay inside a 32-bit buffer range
+  return dtype == 1 && d == FD && Hq == Hkv && chunk == FC && n <= ((int64_t)1 << 24);
+}
+
+size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {
+  return (size_t)NH * nseg * (AGG_FLOATS * sizeof(float) + sizeof(uint64_t)) + 256;
+}
+
+int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const int64_t NH = a.B * a.Hkv;
+  float* agg = reinterpret_cast<float*>(a.ws);
+  uint64_t* flags = reinterpret_cast<uint64_t*>(agg + NH * p.nseg * AGG_FLOATS);
+  uint32_t* err = reinterpret_cast<uint32_t*>(flags + NH * p.nseg);
+  static_assert(kFusedG == G * NGRP, "segment length");
+  FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
+              reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, p.nchunks, p.nseg, NH,
+              agg, flags, epoch, a.S_final, a.z_final, err};
+  k_causal_fused<<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
+  return (int)hipGetLastError();
+}
+
+}  // namespace la_internal

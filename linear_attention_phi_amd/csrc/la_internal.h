@@ -55,6 +55,13 @@ struct Fwd {
 int launch_forward(const Fwd& a, const Plan& p);
 int launch_causal(const Fwd& a, const Plan& p);
 int launch_prefix(const Fwd& a, const Plan& p);
+// Single-launch causal kernel (la_fused.hip): bf16, d = 64, chunk 64,
+// Hq == Hkv, outputs requested.  Segments hold kFusedG chunks.
+constexpr int kFusedG = 8;
+bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk);
+size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg);
+int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch);
+
 int launch_decode(const void* q, const void* k, const void* v, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t d, int dtype, float* S,
                   float* z, void* out, void* stream);

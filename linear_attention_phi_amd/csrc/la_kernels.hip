@@ -22,215 +22,17 @@
 //   k_out_nc: non-causal output: phi(Q) S_total / (phi(Q) . z_total).
 //   k_decode: one recurrent step, S += phi(k) (x) v, then out per query head.
 //
-// MFMA conventions (v_mfma_f32_32x32x16_bf16 for bf16, v_mfma_f32_32x32x2_f32
-// for fp32).  Every operand matrix lives in LDS row-major with the
-// *non-contracted* index as the row and the contracted index k contiguous.
-// For a 32x32 product block and a 16-wide k block kb, lane l (row r = l % 32,
-// half h = l / 32) reads the 8 values at k = 16kb + 4h + {0..3} and
-// 16kb + 8 + 4h + {0..3}.  A and B use this same k assignment, which is all a
-// contraction needs.  The accumulator of a block with rows m and columns n
-// holds, in lane l, column n = l % 32 and rows m = 8q + 4h + s in register
-// 4q + s; written back to LDS "transposed" (row n, four contiguous m per q),
-// it is directly readable as an operand whose k index is m.
+// MFMA operand / accumulator conventions: see la_device.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "la_device.h"
 #include "la_internal.h"
 
 namespace {
 
-typedef __bf16 bf16;
-typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace la_dev;
 
-constexpr int NT = 256;  // threads per workgroup
-constexpr int NW = 4;    // waves per workgroup
-constexpr int PAD = 4;   // LDS row padding (elements): 8-byte (bf16) / 16-byte
-                         // (fp32) fragment reads of 32 rows hit distinct banks
-
-enum Form { CAUSAL = 0, PREFIX = 1 };
-
-__device__ __forceinline__ float phi_f(float x) { return fmaxf(x, 0.0f) + 1.0f; }
-__device__ __forceinline__ float to_f(float x) { return x; }
-__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
-template <typename T> __device__ __forceinline__ T cvt(float x);
-template <> __device__ __forceinline__ float cvt<float>(float x) { return x; }
-template <> __device__ __forceinline__ bf16 cvt<bf16>(float x) { return (bf16)x; }
-
-// ---------------------------------------------------------------- fragments
-template <typename T> struct Frag;
-template <> struct Frag<bf16> { bf16x8 v; };
-template <> struct Frag<float> { f32x4 lo, hi; };
-
-__device__ __forceinline__ void ld_frag(Frag<bf16>& f, const bf16* p) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 8);
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ void ld_frag(Frag<float>& f, const float* p) {
-  f.lo = *reinterpret_cast<const f32x4*>(p);
-  f.hi = *reinterpret_cast<const f32x4*>(p + 8);
-}
-__device__ __forceinline__ void mma(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
-}
-__device__ __forceinline__ void mma(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[u], b.lo[u], acc, 0, 0, 0);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[u], b.hi[u], acc, 0, 0, 0);
-}
-
-// acc[m][n] += sum_k A[m][k] B[n][k] over NKB k-blocks of 16, with A and B
-// pointing at row 0 / column k0 of their 32-row blocks in LDS.
-template <typename T, int NKB>
-__device__ __forceinline__ void gemm_acc(f32x16& acc, const T* A, int lda, const T* B, int ldb, int lane) {
-  const int r = lane & 31, h = lane >> 5;
-  const T* pa = A + r * lda + 4 * h;
-  const T* pb = B + r * ldb + 4 * h;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    Frag<T> fa, fb;
-    ld_frag(fa, pa + 16 * kb);
-    ld_frag(fb, pb + 16 * kb);
-    mma(acc, fa, fb);
-  }
-}
-
-// Write an accumulator block (rows m, columns n) to X[n][m] in LDS, rounded to T.
-__device__ __forceinline__ void st_accT(bf16* X, int ldx, const f32x16& acc, int lane) {
-  const int n = lane & 31, h = lane >> 5;
-  bf16* p = X + n * ldx + 4 * h;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    bf16x4 t = {(bf16)acc[4 * q], (bf16)acc[4 * q + 1], (bf16)acc[4 * q + 2], (bf16)acc[4 * q + 3]};
-    *reinterpret_cast<bf16x4*>(p + 8 * q) = t;
-  }
-}
-__device__ __forceinline__ void st_accT(float* X, int ldx, const f32x16& acc, int lane) {
-  const int n = lane & 31, h = lane >> 5;
-  float* p = X + n * ldx + 4 * h;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x4 t = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-    *reinterpret_cast<f32x4*>(p + 8 * q) = t;
-  }
-}
-
-// ---------------------------------------------------------------- tile loads
-// What a tile copy holds: not written, the raw value, phi(x) = relu(x) + 1,
-// or relu(x).
-enum Xf { XF_NONE = 0, XF_ID = 1, XF_PHI = 2, XF_RELU = 3 };
-
-template <int X> __device__ __forceinline__ float xform(float x) {
-  if (X == XF_PHI) return phi_f(x);
-  if (X == XF_RELU) return fmaxf(x, 0.0f);
-  return x;
-}
-
-// Load C rows x DP features of one head (base = row 0 of the head, row stride
-// d) into LDS: tm[row][col] (token-major, stride DP+PAD) transformed by TMX,
-// and/or fm[col][row] (feature-major, stride C+PAD) transformed by FMX.  Row r
-// of the tile is global row (gidx ? gidx[r] : row0 + r) and exists for
-// r < nvalid.  Missing rows and the padding features col >= d are stored as
-// 0 -- NOT phi(0) = 1 -- so that they add nothing to any sum.
-// vec: d == DP, 16-byte pieces (base and row stride are 16-byte aligned).
-template <typename T, int DP, int C, int TMX, int FMX>
-__device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t row0, const int* __restrict__ gidx,
-                                          int nvalid, int d, bool vec, T* tm, T* fm, int tid) {
-  if (vec) {
-    constexpr int EPP = 16 / (int)sizeof(T);
-    constexpr int PPR = DP / EPP;
-    constexpr int NP = C * PPR;
-#pragma unroll 2
-    for (int p = tid; p < NP; p += NT) {
-      const int row = p / PPR, col = (p % PPR) * EPP;
-      union V { uint4 u; T e[EPP]; };
-      V raw, a, b;
-      raw.u = make_uint4(0, 0, 0, 0);
-      if (row < nvalid) {
-        const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
-        raw.u = *reinterpret_cast<const uint4*>(base + grow * DP + col);
-      }
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) {
-        const float x = to_f(raw.e[e]);
-        a.e[e] = row < nvalid ? cvt<T>(xform<TMX>(x)) : cvt<T>(0.0f);
-        b.e[e] = row < nvalid ? cvt<T>(xform<FMX>(x)) : cvt<T>(0.0f);
-      }
-      if (TMX != XF_NONE) {
-        T* dst = tm + row * (DP + PAD) + col;
-        if (sizeof(T) == 4) {
-          *reinterpret_cast<uint4*>(dst) = a.u;
-        } else {  // rows of DP+PAD bf16 are only 8-byte aligned
-          reinterpret_cast<uint2*>(dst)[0] = make_uint2(a.u.x, a.u.y);
-          reinterpret_cast<uint2*>(dst)[1] = make_uint2(a.u.z, a.u.w);
-        }
-      }
-      if (FMX != XF_NONE) {
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) fm[(col + e) * (C + PAD) + row] = b.e[e];
-      }
-    }
-  } else {
-    for (int idx = tid; idx < C * DP; idx += NT) {
-      const int row = idx / DP, col = idx % DP;
-      float x = 0.0f;
-      const bool ok = row < nvalid && col < d;
-      if (ok) {
-        const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
-        x = to_f(base[grow * d + col]);
-      }
-      if (TMX != XF_NONE) tm[row * (DP + PAD) + col] = cvt<T>(ok ? xform<TMX>(x) : 0.0f);
-      if (FMX != XF_NONE) fm[col * (C + PAD) + row] = cvt<T>(ok ? xform<FMX>(x) : 0.0f);
-    }
-  }
-}
-
-// Sum of the C entries of LDS row r (stride C+PAD), in order.
-template <typename T, int C>
-__device__ __forceinline__ float row_sum(const T* X, int r) {
-  float sum = 0.0f;
-  for (int t = 0; t < C; ++t) sum += to_f(X[r * (C + PAD) + t]);
-  return sum;
-}
-
-// Number of 32x32 state blocks (a-block, b-block) each wave owns.
-template <int DP> struct StateBlocks {
-  static constexpr int NB = DP / 32;
-  static constexpr int TOTAL = NB * NB;
-  static constexpr int PER_WAVE = (TOTAL + NW - 1) / NW;
-};
-
-// Accumulator block <-> fp32 [DP][DP] row-major state in global memory.
-template <int DP>
-__device__ __forceinline__ void ld_state_block(f32x16& acc, const float* __restrict__ S, int ma, int nb, int lane) {
-  const int b = nb * 32 + (lane & 31), h = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = S[(ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * DP + b];
-}
-template <int DP>
-__device__ __forceinline__ void st_state_block(float* __restrict__ S, const f32x16& acc, int ma, int nb, int lane) {
-  const int b = nb * 32 + (lane & 31), h = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) S[(ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * DP + b] = acc[r];
-}
-
-// acc[a][b] += add (lane's column b) for the rows a < d of block row ma.
-__device__ __forceinline__ void add_col(f32x16& acc, float add, int ma, int d, int lane) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    if (ma * 32 + 8 * (r >> 2) + 4 * h + (r & 3) < d) acc[r] += add;
-}
-
-// Per-head slot layout of the state workspace: (nseg + 1) slots of
-// DP*DP + DP floats (S row-major [a][b], then z[a]); slot s < nseg holds the
-// aggregate of segment s (after k_scan: the exclusive prefix before segment
-// s); slot nseg holds the total.
-__host__ __device__ __forceinline__ int64_t slot_elems(int DP) { return (int64_t)DP * DP + DP; }
 
 // ------------------------------------------------------------------ k_state
 // With PHI the state is built as phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t

@@ -259,3 +259,33 @@ def test_decode_B128_Hq32_Hkv8_d128_256_steps(gpu):
     torch.cuda.synchronize()
     np.testing.assert_allclose(S.cpu().numpy()[sample], Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
     np.testing.assert_allclose(z.cpu().numpy()[sample], zr, rtol=1e-5)
+
+
+# ------------------------------------------ the single-launch causal kernel
+# bf16, d = 64, chunk 64, one query head per key/value head takes the
+# single-launch path (segments of 4 chunks that wait on the aggregates of
+# earlier segments); these cases cover ragged tails, one to many segments,
+# and a deep wait chain.
+SINGLE = [(1, 1, 1), (1, 1, 63), (1, 2, 64), (2, 1, 65), (1, 3, 257), (2, 4, 1000), (1, 2, 20000)]
+
+
+@pytest.mark.parametrize("case", SINGLE, ids=lambda c: "B%d_H%d_n%d" % c)
+def test_causal_single_launch_path(gpu, case):
+    B, H, n = case
+    q, k, v, _ = li.qkv(B, H, H, n, 64, li.BF16, seed=n, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64, want_state=True)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True)
+    check(host(out), ref, li.BF16, f"single-launch causal B{B} H{H} n{n}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
+def test_single_launch_matches_three_launch_path(gpu):
+    """The same inputs through chunk 64 (single launch) and chunk 32 (three
+    launches) agree to bf16 rounding, and the workspace can be shared."""
+    q, k, v, _ = li.qkv(4, 8, 8, 3000, 64, li.BF16, seed=4, scaled=True)
+    a = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64))
+    b = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=32))
+    c = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64))
+    assert np.array_equal(a, c)
+    check(a, b, li.BF16, "single vs three launches")
