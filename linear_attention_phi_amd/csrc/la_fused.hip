@@ -529,22 +529,41 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
 #pragma unroll
   for (int c = 0; c < G; ++c) {
     if (c < ncl) {
-      f32x16 o = OUT[c];
       if (has_prev) {
         Frag<bf16> qf[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(o, sf[kb], qf[kb]);
+        for (int kb = 0; kb < 4; ++kb) mma(OUT[c], sf[kb], qf[kb]);
       }
-      const float inv = L.sinv[c][i];
-      const int64_t row = (c_begin + c) * FC + i;
-      if (row < A.n) {
-        bf16* orow = A.out + (head * A.n + row) * FD + nb * 32 + 4 * h;
+    }
+  }
+  // the output rows go through LDS (into the phi(Q) tiles, which are no
+  // longer read once every wave has passed this barrier) so that global
+  // stores cover whole 128-byte rows, 16 bytes per lane
+  __syncthreads();
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          *reinterpret_cast<uint2*>(orow + 8 * qq) =
-              make_uint2(pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv), pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+  for (int c = 0; c < G; ++c) {
+    if (c < ncl) {
+      const float inv = L.sinv[c][i];
+      const f32x16& o = OUT[c];
+      uint2* srow = reinterpret_cast<uint2*>(L.sQ[c] + i * LT + nb * 32 + 4 * h);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        srow[2 * qq] = make_uint2(pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv), pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < G; ++c) {
+    if (c < ncl) {
+      const int64_t t0 = (c_begin + c) * FC;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = tg + NT * u, row = p >> 3, col = 8 * (p & 7);
+        if (t0 + row < A.n)
+          *reinterpret_cast<u32x4*>(A.out + (head * A.n + t0 + row) * FD + col) =
+              *reinterpret_cast<const u32x4*>(L.sQ[c] + row * LT + col);
       }
     }
   }
