@@ -1,21 +1,29 @@
-"""Benchmark of the causal kernelized linear-attention forward on one MI355X.
+"""Benchmark of the kernelized linear-attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload NAME]
 
-Workload: causal normalised linear attention, phi(x) = relu(x) + 1, bf16
-inputs with fp32 state and accumulation, B=8, H=8, n=2048, d=64, chunk 64;
-Q, K, V i.i.d. N(0,1)/sqrt(d) from the seeded generator in la_inputs.  One
-step is one la_causal_forward call over the whole batch (every kernel of the
-path).  Inputs are resident in HBM before timing starts; 10 copies of the
-input/output set rotate so that the 640 MiB footprint is not served from the
-256 MiB last-level (MALL) cache.
+The default workload is causal normalised linear attention, phi(x) = relu(x)
++ 1, bf16 inputs with fp32 state and accumulation, B=8, H=8, n=2048, d=64,
+chunk 64; Q, K, V i.i.d. N(0,1)/sqrt(d) from the seeded generator in
+la_inputs.  One step is one la_causal_forward call over the whole batch (every
+kernel of the path).  The other workloads (--workload) measure the other
+forms of the method the same way: non-causal (B2 H8 n4096 d64, fp32 / bf16),
+the unnormalised prefix-mask form (B4 H8 n8192 d64 fp32, causal and random
+masks), the long-context grouped-query causal pass (B1 Hq32 Hkv8 n65536 d128
+bf16) and the recurrent decode step (B128 Hq32 Hkv8 d128, state prefilled
+from 4096 tokens; one step = one la_decode_step call).
 
-Prints one JSON line:
-  value     tokens*heads per second (B * H * n per step / step time);
-  roofline  algorithmic HBM bytes of one call (Q, K, V read once, out written
-            once: 4 * B * H * n * d * 2 bytes) / the call's average duration,
-            measured with HIP events on the stream the kernels run on,
-            against the 8 TB/s HBM3E peak;
+Inputs are resident in HBM before timing starts; where one input/output set
+is smaller than 640 MiB, several copies rotate so that the footprint is not
+served from the 256 MiB last-level (MALL) cache.  K steps run back to back
+between two HIP events recorded on the stream the kernels are launched on.
+
+Prints one JSON line per workload:
+  value     tokens*heads per second (B * Hq * n per call; B * Hq per decode step);
+  roofline  algorithmic HBM bytes of one call (inputs read once, outputs
+            written once; for decode the state read and written once) / the
+            call's average duration, against the 8 TB/s HBM3E peak, plus the
+            MFMA fraction of the algorithmic flops at the input dtype's peak;
   cpu_baseline  the fp64 oracle (test infrastructure, untuned) timed on this
             host's cores on a bounded sample of the same workload.
 """
@@ -23,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -31,48 +40,281 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-B, H, N, D, CHUNK = 8, 8, 2048, 64, 64
 HBM_PEAK_GBS = 8000.0
-ROTATE = 10
+MFMA_F32_PEAK_TFS = 157.3
+MFMA_BF16_PEAK_TFS = 2500.0
+FOOTPRINT = 640 << 20  # rotate input/output sets up to this many bytes
+
+WORKLOADS = {
+    "causal": dict(form="causal", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", chunk=64, scaled=True, steps=200),
+    "forward_f32": dict(form="forward", B=2, Hq=8, Hkv=8, n=4096, d=64, dt="f32", scaled=False, steps=200),
+    "forward_bf16": dict(form="forward", B=2, Hq=8, Hkv=8, n=4096, d=64, dt="bf16", scaled=False, steps=200),
+    "prefix_causal": dict(form="prefix", B=4, Hq=8, Hkv=8, n=8192, d=64, dt="f32", chunk=64, scaled=True,
+                          mask="causal", steps=50),
+    "prefix_random": dict(form="prefix", B=4, Hq=8, Hkv=8, n=8192, d=64, dt="f32", chunk=64, scaled=True,
+                          mask="random", steps=50),
+    "gqa_causal": dict(form="causal", B=1, Hq=32, Hkv=8, n=65536, d=128, dt="bf16", chunk=0, scaled=True, steps=20),
+    "decode": dict(form="decode", B=128, Hq=32, Hkv=8, d=128, dt="bf16", prefix=4096, scaled=True, steps=256),
+}
+
+DESCRIPTIONS = {
+    "causal": "causal normalised linear attention, phi=relu+1, bf16 in, fp32 state",
+    "forward_f32": "non-causal normalised linear attention, phi=relu+1, fp32",
+    "forward_bf16": "non-causal normalised linear attention, phi=relu+1, bf16 in, fp32 accumulation",
+    "prefix_causal": "unnormalised QK^T V with prefix mask m=arange(n), fp32",
+    "prefix_random": "unnormalised QK^T V with prefix mask m_i ~ U{0..n-1}, fp32",
+    "gqa_causal": "long-context GQA causal normalised linear attention, bf16 in, fp32 state",
+    "decode": "recurrent decode step, fp32 state prefilled from a 4096-token prefix, bf16 q/k/v",
+}
 
 
-def algorithmic_bytes(B, Hq, Hkv, n, d, elem=2):
-    return (2 * B * Hq * n * d + 2 * B * Hkv * n * d) * elem
+def elem_bytes(dt):
+    return 4 if dt == "f32" else 2
 
 
-def cpu_baseline(q, k, v, budget_s=12.0):
-    """Time the oracle on slices of the workload's batch until about budget_s
-    seconds of CPU work have been spent.  Each slice holds enough batch
-    elements for every host thread to own one (batch, head) pair."""
+def algorithmic_bytes(w):
+    """Bytes the method must move per call: inputs read once, outputs written once."""
+    e = elem_bytes(w["dt"])
+    if w["form"] == "decode":
+        B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
+        return 2 * B * Hkv * (d * d + d) * 4 + B * (2 * Hq + 2 * Hkv) * d * e
+    B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
+    extra = 8 * n if w["form"] == "prefix" else 0
+    return (2 * B * Hq * n * d + 2 * B * Hkv * n * d) * e + extra
+
+
+def algorithmic_flops(w):
+    """Multiply-add work of the chunked method at chunk C (2 flops per MAC)."""
+    if w["form"] == "decode":
+        B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
+        return 2 * (B * Hkv * d * d + B * Hq * d * d)
+    B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
+    if w["form"] == "forward":
+        return 2 * (B * Hkv * n * d * d + B * Hq * n * d * d)
+    C = w.get("chunk") or 64
+    # state build per KV head; per query head phi(Q) S_prev, the masked C x C
+    # score block and its product with V
+    return 2 * (B * Hkv * n * d * d + B * Hq * (n * d * d + 2 * n * C * d))
+
+
+def tokens_heads(w):
+    if w["form"] == "decode":
+        return w["B"] * w["Hq"]
+    return w["B"] * w["Hq"] * w["n"]
+
+
+def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
+    """Time the untuned oracle on a bounded sample of the workload: slices of
+    the batch (causal, non-causal, prefix), the first tokens of every head
+    (long context) or a few steps on the whole batch (decode), repeated until
+    about budget_s seconds of CPU work have been spent."""
+    import numpy as np
+
+    import la_inputs as li
     import oracle
 
     threads = oracle.num_threads()
-    bs = max(1, min(B, -(-threads // H)))
+    form = w["form"]
+    if form == "decode":
+        B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
+        rng = np.random.default_rng(1)
+        toks = [tuple(li.gaussian(rng, (B, h, d), 1.0 / math.sqrt(d), li.BF16) for h in (Hq, Hkv, Hkv))
+                for _ in range(4)]
+        Sd = S.astype(np.float64)
+        zd = z.astype(np.float64)
+        steps, el = 0, 0.0
+        while el < budget_s:
+            qs, ks, vs = toks[steps % 4]
+            t0 = time.perf_counter()
+            oracle.decode_step(qs, ks, vs, Sd, zd)
+            el += time.perf_counter() - t0
+            steps += 1
+        return {"value": steps * B * Hq / el, "unit": "tokens*heads/s", "cores": min(threads, B * Hkv),
+                "kind": "oracle",
+                "sample": f"{steps} decode steps on the whole batch (B={B} Hq={Hq} Hkv={Hkv} d={d}), "
+                          f"fp64 oracle, {el:.1f} s"}
+    B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
+    if form == "causal" and B * Hkv < threads:
+        # long context: the first n_s tokens of every head (the causal output of
+        # a prefix does not depend on later tokens)
+        n_s = 4096
+        qs, ks, vs = (np.ascontiguousarray(x[:, :, :n_s]) for x in (q, k, v))
+
+        def call():
+            oracle.causal(qs, ks, vs)
+
+        per = B * Hq * n_s
+        what = f"the first {n_s} tokens of all {Hq} query heads (causal, d={d})"
+        cores = min(threads, B * Hkv)
+    else:
+        bs = max(1, min(B, -(-threads // Hkv)))
+        fn = {"causal": lambda a, b_, c: oracle.causal(a, b_, c),
+              "forward": lambda a, b_, c: oracle.forward(a, b_, c),
+              "prefix": lambda a, b_, c: oracle.prefix_mask(a, b_, c, m)}[form]
+        state = {"r": 0}
+
+        def call():
+            b0 = (state["r"] * bs) % B
+            state["r"] += 1
+            fn(q[b0:b0 + bs], k[b0:b0 + bs], v[b0:b0 + bs])
+
+        per = bs * Hq * n
+        what = f"{bs}-element slices of the batch (Hq={Hq} n={n} d={d})"
+        cores = min(threads, bs * Hkv)
     t0 = time.perf_counter()
-    oracle.causal(q[:bs], k[:bs], v[:bs])
+    call()
     one = time.perf_counter() - t0
     reps = max(1, int(budget_s / max(one, 1e-3)))
     t0 = time.perf_counter()
-    for r in range(reps):
-        b = (r * bs) % B
-        oracle.causal(q[b:b + bs], k[b:b + bs], v[b:b + bs])
+    for _ in range(reps):
+        call()
     el = time.perf_counter() - t0
-    return {
-        "value": reps * bs * H * N / el,
-        "unit": "tokens*heads/s",
-        "cores": min(threads, bs * H),
-        "kind": "oracle",
-        "sample": f"{reps} calls on {bs}-element slices of the workload's batch (H={H} n={N} d={D}, "
-                  f"causal, fp64 oracle on the bf16 inputs), {el:.1f} s",
+    return {"value": reps * per / el, "unit": "tokens*heads/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} oracle calls on {what}, fp64, {el:.1f} s"}
+
+
+def run(name, args):
+    import numpy as np
+    import torch
+
+    import la_inputs as li
+    import linear_attention_phi_amd as la
+
+    w = dict(WORKLOADS[name])
+    steps = args.steps if args.steps is not None else w["steps"]
+    warmup = args.warmup
+    dev = torch.device("cuda", 0)
+    dtc = li.BF16 if w["dt"] == "bf16" else li.F32
+    ladt = la.LA_BF16 if w["dt"] == "bf16" else la.LA_F32
+    form = w["form"]
+    m = S0 = z0 = q = k = v = None
+    if form == "decode":
+        B, Hq, Hkv, d, P = w["B"], w["Hq"], w["Hkv"], w["d"], w["prefix"]
+        # state prefilled by a state-only causal pass over a 4096-token prefix
+        # (drawn one sequence at a time, K then V, to bound host memory)
+        rng = np.random.default_rng(0)
+        kp = torch.empty((B, Hkv, P, d), dtype=torch.bfloat16 if dtc == li.BF16 else torch.float32, device=dev)
+        vp = torch.empty_like(kp)
+        for b in range(B):
+            kp[b] = li.to_torch(li.gaussian(rng, (Hkv, P, d), 1.0 / math.sqrt(d), dtc)).to(dev)
+            vp[b] = li.to_torch(li.gaussian(rng, (Hkv, P, d), 1.0 / math.sqrt(d), dtc)).to(dev)
+        S0, z0 = la.la_causal_forward(None, kp, vp, chunk=0, Hq=Hq)
+        del kp, vp
+        state_bytes = (S0.numel() + z0.numel()) * 4
+        rot = max(1, min(8, -(-FOOTPRINT // state_bytes)))
+        states = [(S0.clone(), z0.clone()) for _ in range(rot)]
+        T = 8  # distinct per-step token sets (their values do not change the work)
+        toks = []
+        for _ in range(T):
+            qs, ks, vs = (li.to_torch(li.gaussian(rng, (B, h, d), 1.0 / math.sqrt(d), dtc)).to(dev)
+                          for h in (Hq, Hkv, Hkv))
+            toks.append((qs, ks, vs, torch.empty_like(qs)))
+
+        def step(i):
+            S, z = states[i % rot]
+            qs, ks, vs, o = toks[i % T]
+            la.la_decode_step(qs, ks, vs, S, z, out=o)
+    else:
+        B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
+        q, k, v, rng = li.qkv(B, Hq, Hkv, n, d, dtc, seed=0, scaled=w["scaled"])
+        md = None
+        if form == "prefix":
+            m = li.mask(n, w["mask"], rng=rng)
+            md = li.to_torch(m).to(dev)
+        qd, kd, vd = (li.to_torch(x).to(dev) for x in (q, k, v))
+        set_bytes = 2 * (qd.numel() + kd.numel()) * qd.element_size()
+        rot = max(1, min(16, -(-FOOTPRINT // set_bytes)))
+        sets = [(qd, kd, vd, torch.empty_like(qd))] + [
+            (qd.clone(), kd.clone(), vd.clone(), torch.empty_like(qd)) for _ in range(rot - 1)]
+        op = {"causal": la.LA_OP_CAUSAL, "forward": la.LA_OP_FORWARD, "prefix": la.LA_OP_PREFIX_MASK}[form]
+        chunk = w.get("chunk", 0)
+        need = la.la_workspace_bytes(op, B, Hq, Hkv, n, d, ladt, chunk)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            qq, kk, vv, oo = sets[i % rot]
+            if form == "causal":
+                la.la_causal_forward(qq, kk, vv, chunk=chunk, out=oo, ws=ws)
+            elif form == "forward":
+                la.la_forward(qq, kk, vv, out=oo, ws=ws)
+            else:
+                la.la_prefix_mask_forward(qq, kk, vv, md, chunk=chunk, out=oo, ws=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # the K steps run back to back, bracketed by two events on the stream the
+    # kernels are launched on (an event between calls would add its own gap)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+
+    nbytes = algorithmic_bytes(w)
+    flops = algorithmic_flops(w)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    single = form == "causal" and w["dt"] == "bf16" and w["d"] == 64 and w["Hq"] == w["Hkv"]
+    roof = {
+        "bound": "hbm",
+        "kernel": "k_causal_fused (the call's one launch)" if single else
+                  ("k_decode (the call's one launch)" if form == "decode" else f"la_{form} (whole call)"),
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": achieved / HBM_PEAK_GBS,
+        "traffic": None,
+        "algorithmic_bytes_per_call": nbytes,
+        "algorithmic_flops_per_call": flops,
+        "call_us_mean": ms * 1e3,
+        "rotating_sets": rot,
     }
+    tfs = flops / (ms * 1e-3) / 1e12
+    mpeak = MFMA_F32_PEAK_TFS if w["dt"] == "f32" else MFMA_BF16_PEAK_TFS
+    roof["mfma"] = {"achieved": tfs, "peak": mpeak, "unit": "TFLOP/s", "frac": tfs / mpeak}
+    if form != "decode" and flops / (mpeak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
+        roof["note"] = "the MFMA time of the algorithmic flops exceeds their HBM time: compare both fractions"
+    cfg = {"workload": DESCRIPTIONS[name], "name": name}
+    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix") if kk in w})
+    if form != "decode":
+        cfg.update({"global_batch": w["B"], "seq_len": w["n"]})
+    line = {
+        "metric": "linear-attn fwd tokens*heads/s + HBM GB/s (% peak), causal bf16 n=2048 d=64"
+                  if name == "causal" else f"linear-attn tokens*heads/s + HBM GB/s (% peak), {name}",
+        "value": tokens_heads(w) / (ms * 1e-3),
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dt"],
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        if form == "decode":
+            line["cpu_baseline"] = cpu_baseline(w, None, None, None, S=S0.cpu().numpy(), z=z0.cpu().numpy())
+        else:
+            line["cpu_baseline"] = cpu_baseline(w, q, k, v, m=m)
+    print(json.dumps(line), flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--workload", default="causal", help="one of: " + ", ".join(WORKLOADS) + ", or all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the benchmark, run plain device-to-device copies of 64 MiB "
                          "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -83,10 +325,14 @@ def main():
               "(batch x head sharding needs no communication; run one process per GPU).",
               file=sys.stderr)
         sys.exit(2)
+    names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    for nm in names:
+        if nm not in WORKLOADS:
+            print(f"unknown workload {nm!r}; choose from {', '.join(WORKLOADS)} or all", file=sys.stderr)
+            sys.exit(2)
 
     import torch
 
-    import la_inputs as li
     import linear_attention_phi_amd as la
 
     la.load()
@@ -95,72 +341,17 @@ def main():
     if args.copy_calibration:
         # 10 rotating 64 MiB sources (640 MiB > the 256 MiB MALL); each copy
         # moves 64 MiB in and 64 MiB out
-        src = [torch.full((64 << 20,), i, dtype=torch.uint8, device=dev) for i in range(ROTATE)]
+        src = [torch.full((64 << 20,), i, dtype=torch.uint8, device=dev) for i in range(10)]
         dst = torch.empty_like(src[0])
-        for i in range(args.warmup + args.steps):
-            dst.copy_(src[i % ROTATE])
+        n = args.warmup + (args.steps or 200)
+        for i in range(n):
+            dst.copy_(src[i % 10])
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_each_way": 64 << 20, "copies": args.warmup + args.steps}))
+        print(json.dumps({"copy_calibration_bytes_each_way": 64 << 20, "copies": n}))
         return
-    q, k, v, _ = li.qkv(B, H, H, N, D, li.BF16, seed=0, scaled=True)
-    qd, kd, vd = (li.to_torch(x).to(dev) for x in (q, k, v))
-    sets = [(qd.clone(), kd.clone(), vd.clone(), torch.empty_like(qd)) for _ in range(ROTATE)]
-    need = la.la_workspace_bytes(la.LA_OP_CAUSAL, B, H, H, N, D, la.LA_BF16, CHUNK)
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-
-    def step(i):
-        qq, kk, vv, oo = sets[i % ROTATE]
-        la.la_causal_forward(qq, kk, vv, chunk=CHUNK, out=oo, ws=ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # the K steps run back to back, bracketed by two events on the stream the
-    # kernels are launched on (an event between calls would add its own gap)
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-
-    nbytes = algorithmic_bytes(B, H, H, N, D)
-    achieved = nbytes / (ms * 1e-3) / 1e9
-    line = {
-        "metric": "linear-attn fwd tokens*heads/s + HBM GB/s (% peak), causal bf16 n=2048 d=64",
-        "value": B * H * N / (ms * 1e-3),
-        "unit": "tokens*heads/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "causal normalised linear attention, phi=relu+1, bf16 in, fp32 state",
-                   "B": B, "H": H, "n": N, "d": D, "chunk": CHUNK,
-                   "global_batch": B, "seq_len": N},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "la_causal_forward (whole call)",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "algorithmic_bytes_per_call": nbytes,
-            "call_us_mean": ms * 1e3,
-        },
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(q, k, v)
-    print(json.dumps(line), flush=True)
+    for nm in names:
+        run(nm, args)
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -105,10 +105,20 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
   if (e >= E) return;
   float* base = ws + bh * (nseg + 1) * E + e;
   float run = 0.0f;
-  for (int64_t s = 0; s < nseg; ++s) {
-    const float x = base[s * E];
-    base[s * E] = run;
-    run += x;
+  // segments in blocks of 16: all loads of a block are issued before its
+  // stores (which the compiler could not move past them), in a fixed order
+  constexpr int BLK = 16;
+  for (int64_t s0 = 0; s0 < nseg; s0 += BLK) {
+    float x[BLK];
+#pragma unroll
+    for (int u = 0; u < BLK; ++u) x[u] = (s0 + u < nseg) ? base[(s0 + u) * E] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < BLK; ++u) {
+      if (s0 + u < nseg) {
+        base[(s0 + u) * E] = run;
+        run += x[u];
+      }
+    }
   }
   base[nseg * E] = run;
   if (e < (int64_t)DP * DP) {
@@ -340,36 +350,60 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
   const int ib = w % NIB;
   const int nb0 = w / NIB;
   constexpr int NB_STEP = NW / NIB;
+  constexpr int NPW = (NBB + NB_STEP - 1) / NB_STEP;  // output blocks per wave
   const bool has_out = nb0 < NBB;
   const int64_t c0 = qs * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
     for (int r = 0; r < R; ++r) {
-      const T* qb = q + (bh * R + r) * n * d;
       __syncthreads();  // sQ free (and sST / sz visible on the first pass)
-      load_tile<T, DP, C, XF_PHI, XF_NONE>(qb, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
+      load_tile<T, DP, C, XF_PHI, XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
       __syncthreads();
+      const int i = ib * 32 + (lane & 31);
+      f32x16 acc[NPW];
+      float inv = 0.0f;
       if (has_out) {
-        const int i = ib * 32 + (lane & 31);
         float part = 0.0f;
         const T* qrow = sQ + i * LQ + h * (DP / 2);
         const float* zz = sz + h * (DP / 2);
         for (int a = 0; a < DP / 2; ++a) part += to_f(qrow[a]) * zz[a];
-        const float inv = 1.0f / (part + __shfl_xor(part, 32));
-        T* orow = (i < nv) ? out + (bh * R + r) * n * d + (t0 + i) * d : nullptr;
-        for (int nb = nb0; nb < NBB; nb += NB_STEP) {
-          f32x16 acc = f32x16{};
-          gemm_acc<T, DP / 16>(acc, sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
-          if (orow) {
+        inv = 1.0f / (part + __shfl_xor(part, 32));
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const int b0 = nb * 32 + 8 * qq + 4 * h;
+        for (int u = 0; u < NPW; ++u) {
+          acc[u] = f32x16{};
+          const int nb = nb0 + u * NB_STEP;
+          if (nb < NBB) gemm_acc<T, DP / 16>(acc[u], sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
+        }
+      }
+      // the tile goes out through sQ so that global stores cover whole rows
+      __syncthreads();
+      if (has_out) {
 #pragma unroll
-              for (int s = 0; s < 4; ++s)
-                if (b0 + s < d) orow[b0 + s] = cvt<T>(acc[4 * qq + s] * inv);
-            }
+        for (int u = 0; u < NPW; ++u) {
+          const int nb = nb0 + u * NB_STEP;
+          if (nb < NBB) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sQ[i * LQ + nb * 32 + 8 * (e >> 2) + 4 * h + (e & 3)] = cvt<T>(acc[u][e] * inv);
           }
+        }
+      }
+      __syncthreads();
+      T* ob = out + (bh * R + r) * n * d + t0 * d;
+      if (vec) {
+        // d == DP: rows of DP / 4 four-element pieces
+        constexpr int PPR = DP / 4;
+        for (int idx = tid; idx < nv * PPR; idx += NT) {
+          const int row = idx / PPR, col = 4 * (idx % PPR);
+          const T* src = sQ + row * LQ + col;
+          T* dst = ob + (int64_t)row * d + col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = src[e];
+        }
+      } else {
+        for (int idx = tid; idx < nv * d; idx += NT) {
+          const int row = idx / d, col = idx % d;
+          ob[(int64_t)row * d + col] = sQ[row * LQ + col];
         }
       }
     }
@@ -430,64 +464,70 @@ __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, 
 // One workgroup per (batch, key/value head): S += phi(k) (x) v, z += phi(k),
 // then out_h = phi(q_h) S / (phi(q_h) . z) for the R query heads of the group.
 // Thread t owns column b = t % 128 of rows a = t / 128 + 2u (u < 64) and keeps
-// them in registers between the update and the reads.
+// them in registers between the update and the reads.  The state goes
+// through buffer instructions bounded to this head's d x d floats: entries
+// outside the d x d square get an offset past the end, so their loads return
+// zero and their stores are dropped, and the update runs without branches
+// (a branch per element would make every store wait for the previous one).
 template <typename T>
 __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, int d, int R, float* __restrict__ S,
                                                float* __restrict__ z, T* __restrict__ out) {
-  __shared__ float pk[la_internal::kMaxD], vv[la_internal::kMaxD], zn[la_internal::kMaxD];
-  __shared__ float pq[la_internal::kMaxD];
-  __shared__ float red[2][la_internal::kMaxD];
+  constexpr int MD = la_internal::kMaxD;
+  __shared__ float pk[MD], vv[MD], zn[MD];
+  __shared__ float pq[MD];
+  __shared__ float red[2][MD];
   __shared__ float sden;
   const int tid = threadIdx.x;
   const int64_t bg = blockIdx.x;  // b * Hkv + g
   float* Sg = S + bg * d * d;
   float* zg = z + bg * d;
-  if (tid < d) {
-    const float pkv = phi_f(to_f(k[bg * d + tid]));
+  if (tid < MD) {
+    // entries past d are zero so that padded rows and columns add nothing
+    float pkv = 0.0f, vvv = 0.0f, znew = 0.0f;
+    if (tid < d) {
+      pkv = phi_f(to_f(k[bg * d + tid]));
+      vvv = to_f(v[bg * d + tid]);
+      znew = zg[tid] + pkv;
+      zg[tid] = znew;
+    }
     pk[tid] = pkv;
-    vv[tid] = to_f(v[bg * d + tid]);
-    const float znew = zg[tid] + pkv;
-    zg[tid] = znew;
+    vv[tid] = vvv;
     zn[tid] = znew;
   }
   __syncthreads();
   const int b = tid & 127, half = tid >> 7;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(Sg, 0, d * d * 4, 0x00020000);
+  constexpr int OOB = 0x7FFFFFF0;  // past num_records for every d <= 128
   float s[64];
-  if (b < d) {
-    const float vb = vv[b];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const int a = half + 2 * u;
-      if (a < d) {
-        const float x = Sg[(int64_t)a * d + b] + pk[a] * vb;
-        Sg[(int64_t)a * d + b] = x;
-        s[u] = x;
-      } else {
-        s[u] = 0.0f;
-      }
-    }
+  for (int u = 0; u < 64; ++u) {
+    const int a = half + 2 * u;
+    const int off = (a < d && b < d) ? (a * d + b) * 4 : OOB;
+    s[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+  }
+  const float vb = vv[b];
+#pragma unroll
+  for (int u = 0; u < 64; ++u) {
+    const int a = half + 2 * u;
+    const int off = (a < d && b < d) ? (a * d + b) * 4 : OOB;
+    s[u] += pk[a] * vb;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s[u]), rs, off, 0, 0);
   }
   for (int r = 0; r < R; ++r) {
     const int64_t qh = bg * R + r;  // (b * Hkv + g) * R + r = b * Hq + g * R + r
     __syncthreads();                // previous head's reads of pq / red are done
-    if (tid < d) pq[tid] = phi_f(to_f(q[qh * d + tid]));
+    if (tid < MD) pq[tid] = tid < d ? phi_f(to_f(q[qh * d + tid])) : 0.0f;
     __syncthreads();
     if (tid < 64) {  // wave 0: den = phi(q) . z
-      float p = 0.0f;
-      for (int a = tid; a < d; a += 64) p += pq[a] * zn[a];
+      float p = pq[tid] * zn[tid] + pq[tid + 64] * zn[tid + 64];
       for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
       if (tid == 0) sden = p;
     }
     float num = 0.0f;
-    if (b < d) {
 #pragma unroll
-      for (int u = 0; u < 64; ++u) {
-        const int a = half + 2 * u;
-        if (a < d) num += pq[a] * s[u];
-      }
-      red[half][b] = num;
-    }
+    for (int u = 0; u < 64; ++u) num += pq[half + 2 * u] * s[u];
+    red[half][b] = num;
     __syncthreads();
     if (tid < d) out[qh * d + tid] = cvt<T>((red[0][tid] + red[1][tid]) / sden);
   }
