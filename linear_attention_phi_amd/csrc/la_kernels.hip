@@ -26,12 +26,38 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace {
 
 using namespace la_dev;
+
+// Copy the first nrows rows of a tile held in LDS (row stride LQ elements) to
+// global rows of d elements: tile row r goes to row gidx[r] when gidx is
+// given, else to row row0 + r.  With d == DP (vec) every lane moves four
+// elements at once, so a wave writes whole rows.
+template <typename T, int DP, int LQ>
+__device__ __forceinline__ void copy_rows_out(const T* tile, int nrows, int d, bool vec, T* base,
+                                              const int* gidx, int64_t row0, int tid) {
+  if (vec) {
+    constexpr int PPR = DP / 4;
+    using V4 = typename std::conditional<sizeof(T) == 2, uint2, uint4>::type;
+    for (int idx = tid; idx < nrows * PPR; idx += NT) {
+      const int r = idx / PPR, col = 4 * (idx % PPR);
+      const int64_t g = gidx ? (int64_t)gidx[r] : row0 + r;
+      *reinterpret_cast<V4*>(base + g * d + col) = *reinterpret_cast<const V4*>(tile + r * LQ + col);
+    }
+  } else {
+    for (int idx = tid; idx < nrows * d; idx += NT) {
+      const int r = idx / d, col = idx % d;
+      const int64_t g = gidx ? (int64_t)gidx[r] : row0 + r;
+      base[g * d + col] = tile[r * LQ + col];
+    }
+  }
+}
 
 
 // ------------------------------------------------------------------ k_state
@@ -266,9 +292,11 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
       __syncthreads();
 
       // ---- outputs of this wave: out^T[b][i] = S^T phi(Q)^T + V^T P^T
+      constexpr int NPW = (NBB + NB_STEP - 1) / NB_STEP;  // output blocks per wave
+      f32x16 accO[NPW];
+      float inv = 1.0f;
+      const int i = ib * 32 + (lane & 31);
       if (has_out) {
-        const int i = ib * 32 + (lane & 31);
-        float den = 1.0f;
         if (NORM) {
           float part = 0.0f;
           const T* qrow = sQ + i * LQ + h * (DP / 2);
@@ -278,33 +306,41 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
           const int jend = (ib + 1) * 32 < JMAX ? (ib + 1) * 32 : JMAX;
           const T* prow = sP + i * LC;
           for (int j = h * (jend / 2); j < (h + 1) * (jend / 2); ++j) part += to_f(prow[j]);
-          den = part + __shfl_xor(part, 32);
+          inv = 1.0f / (part + __shfl_xor(part, 32));
         }
-        const float inv = 1.0f / den;
-        int64_t grow = -1;
-        if (i < qcount) grow = (FORM == CAUSAL) ? t0 + i : (int64_t)gidx[i];
-        T* ob = (FORM == CAUSAL) ? out + (bh * R + grp) * n * d : out + bh * n * d;
-        for (int nb = nb0; nb < NBB; nb += NB_STEP) {
-          f32x16 acc = f32x16{};
-          gemm_acc<T, DP / 16>(acc, sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
 #pragma unroll
-          for (int jb = 0; jb < NIB; ++jb) {
-            if (FORM == CAUSAL && jb > ib) continue;
-            gemm_acc<T, 2>(acc, sVT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
-          }
-          if (grow >= 0) {
-            T* orow = ob + grow * d;
+        for (int u = 0; u < NPW; ++u) {
+          const int nb = nb0 + u * NB_STEP;
+          accO[u] = f32x16{};
+          if (nb < NBB) {
+            gemm_acc<T, DP / 16>(accO[u], sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const int b0 = nb * 32 + 8 * qq + 4 * h;
-#pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                if (b0 + s < d) orow[b0 + s] = cvt<T>(NORM ? acc[4 * qq + s] * inv : acc[4 * qq + s]);
-              }
+            for (int jb = 0; jb < NIB; ++jb) {
+              if (FORM == CAUSAL && jb > ib) continue;
+              gemm_acc<T, 2>(accO[u], sVT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
             }
           }
         }
       }
+      // the tile goes out through sQ (free once every wave is past this
+      // barrier) so that global stores cover whole rows
+      __syncthreads();
+      if (has_out) {
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+          const int nb = nb0 + u * NB_STEP;
+          if (nb < NBB) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              sQ[i * LQ + nb * 32 + 8 * (e >> 2) + 4 * h + (e & 3)] = cvt<T>(NORM ? accO[u][e] * inv : accO[u][e]);
+          }
+        }
+      }
+      __syncthreads();
+      if (FORM == CAUSAL)
+        copy_rows_out<T, DP, LQ>(sQ, qcount, d, vec, out + (bh * R + grp) * n * d, nullptr, t0, tid);
+      else
+        copy_rows_out<T, DP, LQ>(sQ, qcount, d, vec, out + bh * n * d, gidx, 0, tid);
     }
 
     // ---- S += phi(K_c)^T V_c ;  z += column sums of phi(K_c)
@@ -389,23 +425,7 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
         }
       }
       __syncthreads();
-      T* ob = out + (bh * R + r) * n * d + t0 * d;
-      if (vec) {
-        // d == DP: rows of DP / 4 four-element pieces
-        constexpr int PPR = DP / 4;
-        for (int idx = tid; idx < nv * PPR; idx += NT) {
-          const int row = idx / PPR, col = 4 * (idx % PPR);
-          const T* src = sQ + row * LQ + col;
-          T* dst = ob + (int64_t)row * d + col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = src[e];
-        }
-      } else {
-        for (int idx = tid; idx < nv * d; idx += NT) {
-          const int row = idx / d, col = idx % d;
-          ob[(int64_t)row * d + col] = sQ[row * LQ + col];
-        }
-      }
+      copy_rows_out<T, DP, LQ>(sQ, nv, d, vec, out + (bh * R + r) * n * d, nullptr, t0, tid);
     }
   }
 }
