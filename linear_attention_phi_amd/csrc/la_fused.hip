@@ -17,19 +17,21 @@
 //           flags): S_prev, z_prev;
 //  phase 3  out_c = (num_c + phi(Q_c) S_prev) / (den_c + phi(Q_c) . z_prev).
 //
-// Waves: wave w owns query block ib = w & 1 and feature block nb = w >> 1 of
-// the 64 x 64 output tile, and keeps S_loc[:, nb] (both 32-row blocks) in
-// MFMA accumulators, which feed the phi(Q) S products directly as A
-// operands.  P^T = phi(K) phi(Q)^T is computed per wave for its query block;
+// Waves: each group's four waves own the four (query block ib, feature block
+// nb) quarters of the 64 x 64 output tile; wave (ib, nb) keeps state block
+// (ib, nb) of S_loc in MFMA accumulators and swaps a bf16 copy with its
+// partner (1 - ib, nb) through LDS for the phi(Q) S products.  P^T = phi(K) phi(Q)^T is computed per wave for its query block;
 // its accumulators are the B operand of the V^T P^T product (see
 // la_device.h), so P never goes through LDS.  phi(K)^T V is formed as
 // relu(K)^T V + 1 (x) sum_t V_t (exact products; see la_kernels.hip).
 //
 // Segments are numbered segment-major (blockIdx = seg * NH + head), so a
-// workgroup only ever waits for workgroups dispatched before it.  Flags are
-// 64-bit words holding a per-call epoch (top bits 0xFFF8: a NaN pattern, so
-// no float or index the workspace held before can equal one).  Spins are
-// bounded; exhausting the bound records an error bit instead of hanging.
+// workgroup only ever waits for workgroups dispatched before it.  Aggregates
+// go through memory with device-scope stores and loads (the XCDs' L2 caches
+// are not coherent with each other).  Flags are 64-bit words holding a
+// per-call epoch (top bits 0xFFF8: a NaN pattern, so no float or index the
+// workspace held before can equal one).  Spins are bounded; exhausting the
+// bound records an error bit instead of hanging.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,21 +93,25 @@ struct Stage {
   u32x4 k2[2], v2[2], qp[2];
 };
 
-// Rows past the sequence end are read as the last row (always in bounds);
-// stage_store zeroes what must be zero.
-__device__ __forceinline__ void stage_load(Stage& st, const bf16* __restrict__ qh, const bf16* __restrict__ kh,
-                                           const bf16* __restrict__ vh, int64_t t0, int nv, int tid) {
+// The three inputs of one head are read through buffer resources bounded to
+// the head's n rows: rows past the sequence end read as zero (relu(0) = 0
+// keeps such keys and values out of every sum; such queries are never
+// stored).
+struct HeadRsrc {
+  __amdgpu_buffer_rsrc_t q, k, v;
+};
+__device__ __forceinline__ void stage_load(Stage& st, const HeadRsrc& R, int t0, int tid) {
   const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int64_t off = (t0 + (r0 + r < nv ? r0 + r : nv - 1)) * FD + c0;
-    st.k2[r] = *reinterpret_cast<const u32x4*>(kh + off);
-    st.v2[r] = *reinterpret_cast<const u32x4*>(vh + off);
+    const int off = ((t0 + r0 + r) * FD + c0) * 2;
+    st.k2[r] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
+    st.v2[r] = __builtin_amdgcn_raw_buffer_load_b128(R.v, off, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int p = tid + 256 * u, row = p >> 3, col = 8 * (p & 7);
-    st.qp[u] = *reinterpret_cast<const u32x4*>(qh + (t0 + (row < nv ? row : nv - 1)) * FD + col);
+    st.qp[u] = __builtin_amdgcn_raw_buffer_load_b128(R.q, ((t0 + row) * FD + col) * 2, 0, 0);
   }
 }
 
@@ -132,34 +138,18 @@ struct GroupLds {
   uint32_t zpl[FD / 2];
   float sinv[G][FC];       // 1 / normaliser per chunk and query (last phase)
   u32x4 sSx[4][64][2];     // running state block (ma, nb) in bf16, operand order per lane
+  bf16 zero[FD];           // zeros: the rows of the z operand other than 0 and 16
 };
 
-// Stage -> LDS: sQ[c][i][a] = phi(Q), sK[j][a] = relu(K), sKT[a][t] = relu(K),
-// sVT[b][t] = V.  Rows t >= nv of sKT and sVT are zero (they enter sums over
-// all 64 rows); the other copies of such rows only meet masked-out entries.
-// The empty asm statement pins the use of the staged registers here, so that
-// the compiler does not move this work -- and the wait for its loads --
-// ahead of earlier chunks.
-__device__ __forceinline__ void stage_store(Stage& st, bf16* sQc, GroupLds& L, int nv, int tid) {
-  asm volatile("" : "+v"(st.k2[0]), "+v"(st.k2[1]), "+v"(st.v2[0]), "+v"(st.v2[1]), "+v"(st.qp[0]), "+v"(st.qp[1])
-               :
-               : "memory");
-  const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
-  uint32_t xk[2][4], xv[2][4];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const uint32_t keep = (r0 + r < nv) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xk[r][j] = relu2(st.k2[r][j]) & keep;
-      xv[r][j] = st.v2[r][j] & keep;
-    }
-    uint2* dst = reinterpret_cast<uint2*>(L.sK + (r0 + r) * LT + c0);
-    dst[0] = make_uint2(xk[r][0], xk[r][1]);
-    dst[1] = make_uint2(xk[r][2], xk[r][3]);
-  }
-  store_pairs_transposed(L.sKT, r0, c0, xk);
-  store_pairs_transposed(L.sVT, r0, c0, xv);
+// Stage -> LDS, in two parts: sQ[c][i][a] = phi(Q) (into the chunk's own
+// tile, so it can be written while the previous chunk is being computed), and
+// sK[j][a] = relu(K), sKT[a][t] = relu(K), sVT[b][t] = V (shared tiles).  Rows
+// past the sequence end arrive as zeros (stage_load).  The empty asm
+// statements pin the use of the staged registers here, so that the compiler
+// does not move this work -- and the wait for its loads -- ahead of earlier
+// chunks.
+__device__ __forceinline__ void stage_store_q(Stage& st, bf16* sQc, int tid) {
+  asm volatile("" : "+v"(st.qp[0]), "+v"(st.qp[1]) : : "memory");
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int p = tid + 256 * u, row = p >> 3, col = 8 * (p & 7);
@@ -167,6 +157,24 @@ __device__ __forceinline__ void stage_store(Stage& st, bf16* sQc, GroupLds& L, i
     dst[0] = make_uint2(phi2(st.qp[u][0]), phi2(st.qp[u][1]));
     dst[1] = make_uint2(phi2(st.qp[u][2]), phi2(st.qp[u][3]));
   }
+}
+__device__ __forceinline__ void stage_store_kv(Stage& st, GroupLds& L, int tid) {
+  asm volatile("" : "+v"(st.k2[0]), "+v"(st.k2[1]), "+v"(st.v2[0]), "+v"(st.v2[1]) : : "memory");
+  const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
+  uint32_t xk[2][4], xv[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xk[r][j] = relu2(st.k2[r][j]);
+      xv[r][j] = st.v2[r][j];
+    }
+    uint2* dst = reinterpret_cast<uint2*>(L.sK + (r0 + r) * LT + c0);
+    dst[0] = make_uint2(xk[r][0], xk[r][1]);
+    dst[1] = make_uint2(xk[r][2], xk[r][3]);
+  }
+  store_pairs_transposed(L.sKT, r0, c0, xk);
+  store_pairs_transposed(L.sVT, r0, c0, xv);
 }
 
 // Operand fragment from accumulator registers 8 * half .. 8 * half + 7, in bf16.
@@ -177,21 +185,19 @@ __device__ __forceinline__ Frag<bf16> acc_frag(const f32x16& acc, int half) {
   return f;
 }
 
-// One half (this lane's 32 features) of phi(Q_i) . z with z given as bf16
-// (high, low) pairs; the other half lives in lane l ^ 32.
-__device__ __forceinline__ float half_dot_pairs(const Frag<bf16> (&qf)[4], const uint32_t* zh, const uint32_t* zl, int h) {
-  float s = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int zi = 8 * kb + 2 * h + (p & 1) + 4 * (p >> 1);  // pair index of features a, a + 1
-      s = dot2(pair(qf[kb], p), zh[zi], s);
-      s = dot2(pair(qf[kb], p), zl[zi], s);
-    }
-  }
-  return s;
+// A operand for the phi(Q) . z products on MFMA: row 0 holds the bf16 high
+// parts of z, row 16 the low parts (z = high + low to about 2^-17), the other
+// rows zero.  Against phi(Q)^T, output rows 0 and 16 of column i then hold
+// phi(Q_i) . z_high and phi(Q_i) . z_low (accumulator registers 0 and 8 of
+// the lanes with h = 0).  zh, zl: z in feature order as bf16.
+__device__ __forceinline__ Frag<bf16> z_frag(const bf16* zh, const bf16* zl, const bf16* zero, int lane, int kb) {
+  const int m = lane & 31, h = lane >> 5;
+  const bf16* base = (m == 0) ? zh : (m == 16) ? zl : zero;
+  Frag<bf16> f;
+  ld_frag(f, base + 16 * kb + 4 * h);
+  return f;
 }
+
 // Cross-workgroup data (segment aggregates) is written and read with
 // device-scope (sc1) buffer accesses, which gfx950 performs at the device
 // coherence point, so no L2 writeback or invalidate is needed.  Order: each
@@ -199,15 +205,24 @@ __device__ __forceinline__ float half_dot_pairs(const Frag<bf16> (&qf)[4], const
 // the workgroup barrier; only then does one thread store the flag (an
 // agent-scope atomic).  A reader observes the flag, passes a barrier, and only
 // then issues its sc1 aggregate loads.
-constexpr int CPOL_SC1 = 16;  // cache-policy bit of buffer instructions: device scope
+constexpr int CPOL_SC1 = 16;  // cache-policy bit of buffer instructions: device scope (memory)
 
-__device__ __forceinline__ void st_sc1(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4v x) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, byte_off, 0, CPOL_SC1);
+template <int CPOL>
+__device__ __forceinline__ void st_buf(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4v x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, byte_off, 0, CPOL);
 }
-__device__ __forceinline__ f32x4v ld_sc1(__amdgpu_buffer_rsrc_t rs, int byte_off) {
-  return __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, CPOL_SC1));
+template <int CPOL>
+__device__ __forceinline__ void st_buf1(__amdgpu_buffer_rsrc_t rs, int byte_off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rs, byte_off, 0, CPOL);
 }
-
+template <int CPOL>
+__device__ __forceinline__ f32x4v ld_buf(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(f32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, CPOL));
+}
+template <int CPOL>
+__device__ __forceinline__ float ld_buf1(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, CPOL));
+}
 struct FusedArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* out;
   int64_t n, nchunks, nseg, NH;
@@ -235,14 +250,18 @@ __device__ __forceinline__ void store_z_pairs(uint32_t* zh, uint32_t* zl, float 
 template <int IB>
 __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NGRP], float* xch) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int g = w >> 2;         // group
-  const int nb = (w >> 1) & 1;  // feature block; nb == 0 waves also own the normaliser, nb == 1 waves z
+  const int g = w >> 2;  // group
+  // feature block; nb == 0 waves also own the normaliser, nb == 1 waves z.
+  // Group 1 takes the complementary roles, so that the two waves sharing a
+  // SIMD (w and w + 4) carry one heavy and one light share of the work.
+  const int nb = ((w >> 1) & 1) ^ g;
   const int tg = tid & (NT - 1);
   GroupLds& L = LL[g];
   const int64_t seg = blockIdx.x / A.NH, head = blockIdx.x % A.NH;
-  const bf16* qh = A.q + head * A.n * FD;
-  const bf16* kh = A.k + head * A.n * FD;
-  const bf16* vh = A.v + head * A.n * FD;
+  const int hbytes = (int)(A.n * FD * 2);  // one head's rows (n <= 2^24)
+  const HeadRsrc R{__builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + head * A.n * FD), 0, hbytes, 0x00020000),
+                   __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.k + head * A.n * FD), 0, hbytes, 0x00020000),
+                   __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.v + head * A.n * FD), 0, hbytes, 0x00020000)};
   const int64_t c_begin = seg * (G * NGRP) + g * G;
   const int64_t rem = A.nchunks - c_begin;
   const int ncl = (int)(rem < 0 ? 0 : (rem < G ? rem : G));
@@ -252,10 +271,7 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
   Stage st[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    if (c < ncl) {
-      const int64_t t0 = (c_begin + c) * FC;
-      stage_load(st[c], qh, kh, vh, t0, (int)((A.n - t0) < FC ? (A.n - t0) : FC), tg);
-    }
+    if (c < ncl) stage_load(st[c], R, (int)((c_begin + c) * FC), tg);
   }
 
   // ---------------------------------------------------------------- phase 1
@@ -271,34 +287,32 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
     L.zh[0][tg] = 0u;
     L.zl[0][tg] = 0u;
   }
-  Frag<bf16> ones;
+  Frag<bf16> ones, e0;  // all ones; ones in row 0 only (P row sums on MFMA)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ones.v[e] = (bf16)1.0f;
+  for (int e = 0; e < 8; ++e) {
+    ones.v[e] = (bf16)1.0f;
+    e0.v[e] = (bf16)(r == 0 ? 1.0f : 0.0f);
+  }
+  if (tg < FD) L.zero[tg] = (bf16)0.0f;
   // causal mask of the diagonal P^T block: element e holds key row
   // 8 (e >> 2) + 4 h + (e & 3) of query row r
   bool keep[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) keep[e] = 8 * (e >> 2) + 4 * h + (e & 3) <= r;
 
+  // chunk 0's tiles
+  if (ncl > 0) {
+    stage_store_q(st[0], L.sQ[0], tg);
+    stage_store_kv(st[0], L, tg);
+    if (2 < ncl) stage_load(st[0], R, (int)((c_begin + 2) * FC), tg);
+  }
+  __syncthreads();
+  // Per chunk c: compute c, and stage phi(Q) of chunk c + 1 into its own tile
+  // in the same interval; after a barrier, hand the state block S_loc(c + 1)
+  // to the partner wave and stage chunk c + 1's K and V.
+  Frag<bf16> sown[2];  // own state block S_loc(c) as operand fragments
 #pragma unroll
   for (int c = 0; c < G; ++c) {
-    // own state block S_loc(c) as operand fragments, also handed to the partner
-    Frag<bf16> sown[2];
-    if (c > 0 && c < ncl) {
-      sown[0] = acc_frag(S_acc, 0);
-      sown[1] = acc_frag(S_acc, 1);
-      L.sSx[IB * 2 + nb][lane][0] = __builtin_bit_cast(u32x4, sown[0].v);
-      L.sSx[IB * 2 + nb][lane][1] = __builtin_bit_cast(u32x4, sown[1].v);
-    }
-    if (c < ncl) {
-      const int64_t t0 = (c_begin + c) * FC;
-      stage_store(st[c & 1], L.sQ[c], L, (int)((A.n - t0) < FC ? (A.n - t0) : FC), tg);
-      if (c + 2 < ncl) {
-        const int64_t t2 = t0 + 2 * FC;
-        stage_load(st[c & 1], qh, kh, vh, t2, (int)((A.n - t2) < FC ? (A.n - t2) : FC), tg);
-      }
-    }
-    __syncthreads();
     if (c < ncl) {
       const int64_t t0 = (c_begin + c) * FC;
       const int nv = (int)((A.n - t0) < FC ? (A.n - t0) : FC);
@@ -307,22 +321,17 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
       for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) ld_frag(vt[kt], L.sVT + (nb * 32 + r) * LF + 16 * kt + 4 * h);
-      // sum_a phi(Q_i)[a]: P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
-      float sq = 0.0f;
+      // P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]; the second term (the
+      // same for every key row) comes from an all-ones A operand
+      f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) sq = dot2(pair(qf[kb], p), ONE2, sq);
-      sq += __shfl_xor(sq, 32);
+      for (int kb = 0; kb < 4; ++kb) mma(sacc, ones, qf[kb]);
 
       // P^T blocks for key blocks jb <= IB; only the diagonal block is masked
       Frag<bf16> pfr[IB + 1][2];
-      float rsum = 0.0f;
 #pragma unroll
       for (int jb = 0; jb <= IB; ++jb) {
-        f32x16 pacc;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) pacc[e] = sq;
+        f32x16 pacc = sacc;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           Frag<bf16> kf;
@@ -335,10 +344,6 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
         }
         pfr[jb][0] = acc_frag(pacc, 0);
         pfr[jb][1] = acc_frag(pacc, 1);
-        if (nb == 0) {
-#pragma unroll
-          for (int p = 0; p < 4; ++p) rsum = dot2(pair(pfr[jb][1], p), ONE2, dot2(pair(pfr[jb][0], p), ONE2, rsum));
-        }
       }
 
       // num_c = phi(Q) S_loc + V^T P^T   (rows b of block nb, column i)
@@ -361,8 +366,18 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
       }
       OUT[c] = o;
       if (nb == 0) {
-        const float dpart = half_dot_pairs(qf, L.zh[c & 1], L.zl[c & 1], h) + rsum;
-        den[c] = dpart + __shfl_xor(dpart, 32);
+        // den_i = sum_j P_ij + phi(Q_i) . z, both on MFMA (rows 0 and 16)
+        f32x16 dacc = f32x16{};
+#pragma unroll
+        for (int jb = 0; jb <= IB; ++jb) {
+          mma(dacc, e0, pfr[jb][0]);
+          mma(dacc, e0, pfr[jb][1]);
+        }
+        const bf16* zhc = reinterpret_cast<const bf16*>(L.zh[c & 1]);
+        const bf16* zlc = reinterpret_cast<const bf16*>(L.zl[c & 1]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(dacc, z_frag(zhc, zlc, L.zero, lane, kb), qf[kb]);
+        den[c] = dacc[0] + dacc[8];  // valid in the lanes with h == 0
       }
 
       // S_loc += relu(K)^T V + ones^T V for block (IB, nb); z (nb == 1 waves)
@@ -381,6 +396,18 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
       if (nb == 1) {
         zloc += zp + __shfl_xor(zp, 32) + (float)nv;
         store_z_pairs(L.zh[(c + 1) & 1], L.zl[(c + 1) & 1], zloc, IB * 32 + r, h == 0);
+      }
+    }
+    if (c + 1 < G) {
+      if (c + 1 < ncl) stage_store_q(st[(c + 1) & 1], L.sQ[c + 1], tg);
+      __syncthreads();
+      if (c + 1 < ncl) {
+        sown[0] = acc_frag(S_acc, 0);
+        sown[1] = acc_frag(S_acc, 1);
+        L.sSx[IB * 2 + nb][lane][0] = __builtin_bit_cast(u32x4, sown[0].v);
+        L.sSx[IB * 2 + nb][lane][1] = __builtin_bit_cast(u32x4, sown[1].v);
+        stage_store_kv(st[(c + 1) & 1], L, tg);
+        if (c + 3 < ncl) stage_load(st[(c + 1) & 1], R, (int)((c_begin + c + 3) * FC), tg);
       }
     }
     __syncthreads();
@@ -402,6 +429,9 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(A.agg + head * A.nseg * AGG_FLOATS, 0, (int)(A.nseg * AGG_FLOATS * 4), 0x00020000);
   const int blk = ((IB * 2 + nb) * 64 + lane) * 64;  // byte offset of this lane's block values in an aggregate
+  const int zoff = 4 * 64 * 16 * 4;                  // byte offset of z in an aggregate
+  const bool publish = seg + 1 < A.nseg;             // the last segment has no successor
+  uint64_t* flag = A.flags + head * A.nseg;          // this head's segment flags
   if (g == 1) {
     const f32x4v* s4 = reinterpret_cast<const f32x4v*>(xch + ((IB * 2 + nb) * 64 + lane) * 16);
 #pragma unroll
@@ -411,24 +441,26 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
       for (int e = 0; e < 4; ++e) a0[4 * u + e] = x[e];
     }
     za0 = xz[IB * 32 + r];
+    if (publish) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      st_sc1(rs, (int)(seg * AGG_FLOATS * 4) + blk + 16 * u,
-             f32x4v{a0[4 * u] + S_acc[4 * u], a0[4 * u + 1] + S_acc[4 * u + 1],
-                    a0[4 * u + 2] + S_acc[4 * u + 2], a0[4 * u + 3] + S_acc[4 * u + 3]});
-    if (nb == 1 && h == 0)
-      __hip_atomic_store(A.agg + (head * A.nseg + seg) * AGG_FLOATS + 4 * 64 * 16 + IB * 32 + r, za0 + zloc,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int u = 0; u < 4; ++u)
+        st_buf<CPOL_SC1>(rs, (int)(seg * AGG_FLOATS * 4) + blk + 16 * u,
+                         f32x4v{a0[4 * u] + S_acc[4 * u], a0[4 * u + 1] + S_acc[4 * u + 1],
+                                a0[4 * u + 2] + S_acc[4 * u + 2], a0[4 * u + 3] + S_acc[4 * u + 3]});
+      if (nb == 1 && h == 0) st_buf1<CPOL_SC1>(rs, (int)(seg * AGG_FLOATS * 4) + zoff + (IB * 32 + r) * 4, za0 + zloc);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's aggregate stores have completed
-  __syncthreads();
-  if (tid == 0) __hip_atomic_store(A.flags + head * A.nseg + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (publish) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's aggregate stores have completed
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flag + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   if (seg > 0) {
     if (w == 0) {
       for (int64_t p = lane; p < seg; p += 64) {
         uint32_t spins = 0;
-        while (__hip_atomic_load(A.flags + head * A.nseg + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != A.epoch) {
+        while (__hip_atomic_load(flag + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != A.epoch) {
           __builtin_amdgcn_s_sleep(2);
           if (++spins > (1u << 22)) {
             atomicOr(A.err, 1u);
@@ -440,48 +472,32 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
     __syncthreads();
   }
   // S_prev of the segment (block (IB, nb)) and z_prev, summed over earlier
-  // segments in order, two segments' loads in flight at a time; group 1 adds
-  // group 0's aggregate.
+  // segments in order, up to four segments' loads in flight; group 1
+  // adds group 0's aggregate.
   f32x16 sp = f32x16{};
   float zprev = 0.0f;
   const bool zlane = (w & 3) == 0;  // wave 0 of each group sums z (lane = feature)
-  {
-    int64_t p = 0;
-    for (; p + 1 < seg; p += 2) {
-      f32x4v x[4], y[4];
+  for (int64_t p = 0; p < seg; p += 4) {
+    f32x4v x[4][4];
+    float zx[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[u] = ld_sc1(rs, (int)(p * AGG_FLOATS * 4) + blk + 16 * u);
-        y[u] = ld_sc1(rs, (int)((p + 1) * AGG_FLOATS * 4) + blk + 16 * u);
+    for (int u = 0; u < 4; ++u) {
+      if (p + u < seg) {
+        const int base = (int)((p + u) * AGG_FLOATS * 4);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) x[u][q4] = ld_buf<CPOL_SC1>(rs, base + blk + 16 * q4);
+        zx[u] = zlane ? ld_buf1<CPOL_SC1>(rs, base + zoff + lane * 4) : 0.0f;
       }
-      float zx = 0.0f, zy = 0.0f;
-      if (zlane) {
-        zx = __hip_atomic_load(A.agg + (head * A.nseg + p) * AGG_FLOATS + 4 * 64 * 16 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        zy = __hip_atomic_load(A.agg + (head * A.nseg + p + 1) * AGG_FLOATS + 4 * 64 * 16 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sp[4 * u + e] += x[u][e];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sp[4 * u + e] += y[u][e];
-      zprev += zx;
-      zprev += zy;
     }
-    if (p < seg) {
-      f32x4v x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = ld_sc1(rs, (int)(p * AGG_FLOATS * 4) + blk + 16 * u);
-      float zx = 0.0f;
-      if (zlane)
-        zx = __hip_atomic_load(A.agg + (head * A.nseg + p) * AGG_FLOATS + 4 * 64 * 16 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int u = 0; u < 4; ++u) {
+      if (p + u < seg) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sp[4 * u + e] += x[u][e];
-      zprev += zx;
+          for (int e = 0; e < 4; ++e) sp[4 * q4 + e] += x[u][q4][e];
+        zprev += zx[u];
+      }
     }
   }
   if (g == 1) {
@@ -515,9 +531,12 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
         Frag<bf16> qf[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
-        const float zq = half_dot_pairs(qf, L.zph, L.zpl, h);
-        const float zt = zq + __shfl_xor(zq, 32);  // every lane takes part in the exchange
-        if (h == 0) L.sinv[c][i] = __builtin_amdgcn_rcpf(den[c] + zt);
+        f32x16 zacc = f32x16{};
+        const bf16* zph = reinterpret_cast<const bf16*>(L.zph);
+        const bf16* zpl = reinterpret_cast<const bf16*>(L.zpl);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(zacc, z_frag(zph, zpl, L.zero, lane, kb), qf[kb]);
+        if (h == 0) L.sinv[c][i] = __builtin_amdgcn_rcpf(den[c] + zacc[0] + zacc[8]);
       }
     }
   }
@@ -576,7 +595,8 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   float* xch = reinterpret_cast<float*>(LL[0].sK);
   static_assert(sizeof(LL[0].sK) + sizeof(LL[0].sKT) + sizeof(LL[0].sVT) >= AGG_FLOATS * sizeof(float),
                 "hand-off area too small");
-  if (((threadIdx.x >> 6) & 1) == 0)
+  const int w = threadIdx.x >> 6;
+  if (((w & 1) ^ (w >> 2)) == 0)  // query block; complementary in group 1
     fused_wave<0>(A, LL, xch);
   else
     fused_wave<1>(A, LL, xch);
@@ -587,8 +607,10 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 namespace la_internal {
 
 bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk) {
-  // n bound: one head's aggregates must stay inside a 32-bit buffer range
-  return dtype == 1 && d == FD && Hq == Hkv && chunk == FC && n <= ((int64_t)1 << 24);
+  // n bound: every segment sums the aggregates of all earlier segments of its
+  // head, so the look-back grows with n; longer sequences take the
+  // three-launch path, whose scan is linear in the number of segments
+  return dtype == 1 && d == FD && Hq == Hkv && chunk == FC && n <= kFusedMaxN;
 }
 
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {

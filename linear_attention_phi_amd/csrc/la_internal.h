@@ -58,6 +58,7 @@ int launch_prefix(const Fwd& a, const Plan& p);
 // Single-launch causal kernel (la_fused.hip): bf16, d = 64, chunk 64,
 // Hq == Hkv, outputs requested.  Segments hold kFusedG chunks.
 constexpr int kFusedG = 8;
+constexpr int64_t kFusedMaxN = 131072;  // up to 256 segments per head
 bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk);
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg);
 int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch);
