@@ -12,9 +12,17 @@
 
 namespace la_internal {
 
+// The default chunk is the larger of 64 and 32 whose tiles leave room for two
+// workgroups per CU (the general kernels hide load latency with the second
+// workgroup), else the larger one that fits at all.
 int default_chunk(int elem_bytes, int DP) {
+  for (int c : {64, 32})
+    if (chunk_lds_bytes(elem_bytes, DP, c) <= kLdsLimit / 2) return c;
   return chunk_fits(elem_bytes, DP, 64) ? 64 : 32;
 }
+// The non-causal form's kernels hold at most two tiles per chunk: the larger
+// chunk that fits.
+static int forward_chunk(int elem_bytes, int DP) { return chunk_fits(elem_bytes, DP, 64) ? 64 : 32; }
 
 // Segments: about kTargetGroups workgroups per pass, so that the 256 CUs each
 // get several, while each workgroup still walks a run of chunks.
@@ -153,7 +161,7 @@ size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_
   if (check_sizes(B, Hq, Hkv, n, d, dtype) != LA_OK) return 0;
   int C = 0;
   if (op == LA_OP_FORWARD) {
-    C = default_chunk(elem_bytes(dtype), padded_dim(d));
+    C = forward_chunk(elem_bytes(dtype), padded_dim(d));
   } else if (resolve_chunk(chunk, dtype, d, &C) != LA_OK) {
     return 0;
   }
@@ -170,7 +178,7 @@ la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int
   const size_t eb = elem_bytes(dtype);
   const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
   if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb)) return LA_ERR_ALIAS;
-  const int C = default_chunk((int)eb, padded_dim(d));
+  const int C = forward_chunk((int)eb, padded_dim(d));
   Plan p;
   const size_t need = required_ws(LA_OP_FORWARD, B, Hq, Hkv, n, d, dtype, C, &p);
   if ((st = check_grid(p, B, Hkv)) != LA_OK) return st;

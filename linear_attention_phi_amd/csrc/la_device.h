@@ -122,22 +122,32 @@ template <typename T, int DP, int C, int TMX, int FMX>
 __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t row0, const int* __restrict__ gidx,
                                           int nvalid, int d, bool vec, T* tm, T* fm, int tid) {
   if (vec) {
+    // every piece this thread owns is requested before any is used
     constexpr int EPP = 16 / (int)sizeof(T);
     constexpr int PPR = DP / EPP;
     constexpr int NP = C * PPR;
-#pragma unroll 2
-    for (int p = tid; p < NP; p += NT) {
+    constexpr int PER = (NP + NT - 1) / NT;
+    union V { uint4 u; T e[EPP]; };
+    V raw[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int p = tid + k * NT;
+      raw[k].u = make_uint4(0, 0, 0, 0);
       const int row = p / PPR, col = (p % PPR) * EPP;
-      union V { uint4 u; T e[EPP]; };
-      V raw, a, b;
-      raw.u = make_uint4(0, 0, 0, 0);
-      if (row < nvalid) {
+      if (p < NP && row < nvalid) {
         const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
-        raw.u = *reinterpret_cast<const uint4*>(base + grow * DP + col);
+        raw[k].u = *reinterpret_cast<const uint4*>(base + grow * DP + col);
       }
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int p = tid + k * NT;
+      if (p >= NP) break;
+      const int row = p / PPR, col = (p % PPR) * EPP;
+      V a, b;
 #pragma unroll
       for (int e = 0; e < EPP; ++e) {
-        const float x = to_f(raw.e[e]);
+        const float x = to_f(raw[k].e[e]);
         a.e[e] = row < nvalid ? cvt<T>(xform<TMX>(x)) : cvt<T>(0.0f);
         b.e[e] = row < nvalid ? cvt<T>(xform<FMX>(x)) : cvt<T>(0.0f);
       }
@@ -166,6 +176,68 @@ __device__ __forceinline__ void load_tile(const T* __restrict__ base, int64_t ro
       }
       if (TMX != XF_NONE) tm[row * (DP + PAD) + col] = cvt<T>(ok ? xform<TMX>(x) : 0.0f);
       if (FMX != XF_NONE) fm[col * (C + PAD) + row] = cvt<T>(ok ? xform<FMX>(x) : 0.0f);
+    }
+  }
+}
+
+// A tile's raw 16-byte pieces held in registers between their global loads
+// (tile_fetch) and their transform into LDS (tile_store), so that the loads
+// of the next tile can be in flight while the current one is used.  Only for
+// d == DP (whole 16-byte pieces); rows at or past nvalid are zero.
+template <typename T, int DP, int C>
+struct TileRaw {
+  static constexpr int EPP = 16 / (int)sizeof(T);
+  static constexpr int PPR = DP / EPP;
+  static constexpr int NP = C * PPR;
+  static constexpr int PER = (NP + NT - 1) / NT;
+  uint4 u[PER];
+};
+
+template <typename T, int DP, int C>
+__device__ __forceinline__ void tile_fetch(TileRaw<T, DP, C>& t, const T* __restrict__ base, int64_t row0,
+                                           const int* __restrict__ gidx, int nvalid, int tid) {
+  using TR = TileRaw<T, DP, C>;
+#pragma unroll
+  for (int k = 0; k < TR::PER; ++k) {
+    const int p = tid + k * NT;
+    const int row = p / TR::PPR, col = (p % TR::PPR) * TR::EPP;
+    t.u[k] = make_uint4(0, 0, 0, 0);
+    if (p < TR::NP && row < nvalid) {
+      const int64_t grow = gidx ? (int64_t)gidx[row] : row0 + row;
+      t.u[k] = *reinterpret_cast<const uint4*>(base + grow * DP + col);
+    }
+  }
+}
+
+template <typename T, int DP, int C, int TMX, int FMX>
+__device__ __forceinline__ void tile_store(const TileRaw<T, DP, C>& t, int nvalid, T* tm, T* fm, int tid) {
+  using TR = TileRaw<T, DP, C>;
+#pragma unroll
+  for (int k = 0; k < TR::PER; ++k) {
+    const int p = tid + k * NT;
+    if (p >= TR::NP) break;
+    const int row = p / TR::PPR, col = (p % TR::PPR) * TR::EPP;
+    union V { uint4 u; T e[TR::EPP]; };
+    V raw, a, b;
+    raw.u = t.u[k];
+#pragma unroll
+    for (int e = 0; e < TR::EPP; ++e) {
+      const float x = to_f(raw.e[e]);
+      a.e[e] = row < nvalid ? cvt<T>(xform<TMX>(x)) : cvt<T>(0.0f);
+      b.e[e] = row < nvalid ? cvt<T>(xform<FMX>(x)) : cvt<T>(0.0f);
+    }
+    if (TMX != XF_NONE) {
+      T* dst = tm + row * (DP + PAD) + col;
+      if (sizeof(T) == 4) {
+        *reinterpret_cast<uint4*>(dst) = a.u;
+      } else {  // rows of DP+PAD bf16 are only 8-byte aligned
+        reinterpret_cast<uint2*>(dst)[0] = make_uint2(a.u.x, a.u.y);
+        reinterpret_cast<uint2*>(dst)[1] = make_uint2(a.u.z, a.u.w);
+      }
+    }
+    if (FMX != XF_NONE) {
+#pragma unroll
+      for (int e = 0; e < TR::EPP; ++e) fm[(col + e) * (C + PAD) + row] = b.e[e];
     }
   }
 }

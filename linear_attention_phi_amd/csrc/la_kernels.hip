@@ -212,20 +212,72 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
   if (NORM) __syncthreads();
 
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  // Query groups of chunk c: R heads (causal) or bucket tiles (prefix).
+  auto groups_of = [&](int64_t c) -> int {
+    if (FORM == CAUSAL) return R;
+    return (int)((boff[c + 1] - boff[c] + C - 1) / C);
+  };
+  // Query tile of group grp of chunk c: base, gather indices, rows
+  struct QTile {
+    const T* base;
+    const int* gidx;
+    int rows;
+  };
+  auto qtile = [&](int64_t c, int grp) -> QTile {
+    const int64_t tc = c * C;
+    if (FORM == CAUSAL) return {q + (bh * R + grp) * n * d, nullptr, (int)((n - tc) < C ? (n - tc) : C)};
+    const int64_t s0 = boff[c] + (int64_t)grp * C;
+    const int64_t rem = boff[c + 1] - s0;
+    return {q + bh * n * d, perm + s0, (int)(rem < C ? rem : C)};
+  };
+  // With d == DP the tiles are prefetched one step ahead: the next query tile
+  // while the current group runs, and (DP <= 64, where the registers allow two
+  // workgroups per CU even so) K and V of the next chunk while the current
+  // chunk's groups run.
+  constexpr bool PF_KV = DP <= 64;
+  TileRaw<T, DP, C> rK, rV, rQ;
+  int64_t kv_c = -1, q_c = -1;  // which chunk / (chunk, group) the registers hold
+  int q_g = 0;
+  auto fetch_kv = [&](int64_t c) {
+    const int64_t tc = c * C;
+    const int nvc = (int)((n - tc) < C ? (n - tc) : C);
+    tile_fetch<T, DP, C>(rK, kb, tc, nullptr, nvc, tid);
+    tile_fetch<T, DP, C>(rV, vb, tc, nullptr, nvc, tid);
+    kv_c = c;
+  };
+  auto fetch_q_after = [&](int64_t c, int grp) {  // the group after (c, grp), if any
+    int64_t cc = c;
+    int gg = grp + 1;
+    while (cc < c1 && gg >= groups_of(cc)) {
+      ++cc;
+      gg = 0;
+    }
+    if (cc < c1) {
+      const QTile qt = qtile(cc, gg);
+      tile_fetch<T, DP, C>(rQ, qt.base, cc * C, qt.gidx, qt.rows, tid);
+      q_c = cc;
+      q_g = gg;
+    } else {
+      q_c = -1;
+    }
+  };
+  if (vec && c0 < c1) {
+    if (PF_KV) fetch_kv(c0);
+    fetch_q_after(c0, -1);
+  }
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
-    // Query groups of this chunk: R heads (causal) or bucket tiles (prefix).
-    int64_t qstart = 0;
-    int ngroups = R;
-    if (FORM == PREFIX) {
-      qstart = boff[c];
-      const int64_t cnt = boff[c + 1] - qstart;
-      ngroups = (int)((cnt + C - 1) / C);
-    }
+    const int ngroups = groups_of(c);
 
-    load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, NORM ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
-    load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    if (PF_KV && vec && kv_c == c) {
+      tile_store<T, DP, C, NORM ? XF_PHI : XF_ID, NORM ? XF_RELU : XF_ID>(rK, nv, sK, sKT, tid);
+      tile_store<T, DP, C, XF_NONE, XF_ID>(rV, nv, nullptr, sVT, tid);
+      if (c + 1 < c1) fetch_kv(c + 1);
+    } else {
+      load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, NORM ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
+      load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    }
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
       const int e = w + NW * s;
@@ -240,21 +292,16 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
 
     for (int grp = 0; grp < ngroups; ++grp) {
       // ---- query tile of this group
-      const T* qb;
-      const int* gidx = nullptr;
-      int qcount;
-      if (FORM == CAUSAL) {
-        qb = q + (bh * R + grp) * n * d;
-        qcount = nv;
-      } else {
-        qb = q + bh * n * d;
-        const int64_t s0 = qstart + (int64_t)grp * C;
-        const int64_t rem = boff[c + 1] - s0;
-        qcount = (int)(rem < C ? rem : C);
-        gidx = perm + s0;
-      }
+      const QTile qt = qtile(c, grp);
+      const int* gidx = qt.gidx;
+      const int qcount = qt.rows;
       if (grp > 0) __syncthreads();  // previous group is done with sQ / sP
-      load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, XF_NONE>(qb, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
+      if (vec && q_c == c && q_g == grp) {
+        tile_store<T, DP, C, NORM ? XF_PHI : XF_ID, XF_NONE>(rQ, qcount, sQ, nullptr, tid);
+        fetch_q_after(c, grp);
+      } else {
+        load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, XF_NONE>(qt.base, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
+      }
       __syncthreads();
 
       // ---- P^T blocks (key block jb, query block ib2), masked, -> sP[i][j]
