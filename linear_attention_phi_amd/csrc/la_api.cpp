@@ -25,17 +25,20 @@ int default_chunk(int elem_bytes, int DP) {
 static int forward_chunk(int elem_bytes, int DP) { return chunk_fits(elem_bytes, DP, 64) ? 64 : 32; }
 
 // Segments: about kTargetGroups workgroups per pass, so that the 256 CUs each
-// get several, while each workgroup still walks a run of chunks.
+// get several, while each workgroup still walks a run of chunks.  The
+// non-causal form needs only the total state, so it takes longer segments
+// (about one workgroup per CU): fewer partial states to write and sum.
 static constexpr int64_t kTargetGroups = 1024;
+static constexpr int64_t kTargetGroupsForward = 256;
 
 Plan make_plan(int op, int64_t B, int64_t Hkv, int64_t n, int64_t d, int elem_bytes, int chunk) {
-  (void)op;
   Plan p;
   p.DP = padded_dim(d);
   p.C = chunk;
   p.nchunks = (n + chunk - 1) / chunk;
   const int64_t units = B * Hkv * p.nchunks;
-  int64_t G = (units + kTargetGroups - 1) / kTargetGroups;
+  const int64_t target = op == LA_OP_FORWARD ? kTargetGroupsForward : kTargetGroups;
+  int64_t G = (units + target - 1) / target;
   if (G < 1) G = 1;
   if (G > p.nchunks) G = p.nchunks;
   p.G = G;

@@ -82,11 +82,26 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
   for (int s = 0; s < SB::PER_WAVE; ++s) accS[s] = f32x16{};
   float zrun = 0.0f, vrun = 0.0f;
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  // with d == DP the next chunk's K and V tiles load while this one is used
+  TileRaw<T, DP, C> rK, rV;
+  auto fetch = [&](int64_t c) {
+    const int64_t tc = c * C;
+    const int nvc = (int)((n - tc) < C ? (n - tc) : C);
+    tile_fetch<T, DP, C>(rK, kb, tc, nullptr, nvc, tid);
+    tile_fetch<T, DP, C>(rV, vb, tc, nullptr, nvc, tid);
+  };
+  if (vec && c0 < c1) fetch(c0);
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
-    load_tile<T, DP, C, XF_NONE, PHI ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
-    load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    if (vec) {
+      tile_store<T, DP, C, XF_NONE, PHI ? XF_RELU : XF_ID>(rK, nv, nullptr, sKT, tid);
+      tile_store<T, DP, C, XF_NONE, XF_ID>(rV, nv, nullptr, sVT, tid);
+      if (c + 1 < c1) fetch(c + 1);
+    } else {
+      load_tile<T, DP, C, XF_NONE, PHI ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
+      load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
+    }
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
@@ -436,12 +451,25 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
   constexpr int NPW = (NBB + NB_STEP - 1) / NB_STEP;  // output blocks per wave
   const bool has_out = nb0 < NBB;
   const int64_t c0 = qs * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  // with d == DP the next (chunk, head) query tile loads while this one is used
+  TileRaw<T, DP, C> rQ;
+  auto fetch = [&](int64_t c, int r) {
+    const int64_t tc = c * C;
+    tile_fetch<T, DP, C>(rQ, q + (bh * R + r) * n * d, tc, nullptr, (int)((n - tc) < C ? (n - tc) : C), tid);
+  };
+  if (vec && c0 < c1) fetch(c0, 0);
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
     for (int r = 0; r < R; ++r) {
       __syncthreads();  // sQ free (and sST / sz visible on the first pass)
-      load_tile<T, DP, C, XF_PHI, XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
+      if (vec) {
+        tile_store<T, DP, C, XF_PHI, XF_NONE>(rQ, nv, sQ, nullptr, tid);
+        if (r + 1 < R) fetch(c, r + 1);
+        else if (c + 1 < c1) fetch(c + 1, 0);
+      } else {
+        load_tile<T, DP, C, XF_PHI, XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
+      }
       __syncthreads();
       const int i = ib * 32 + (lane & 31);
       f32x16 acc[NPW];
@@ -649,8 +677,9 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   const int64_t E = slot_elems(DP);
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr);
-  // query runs: about 1024 workgroups in total
-  int64_t Gq = (nbh * p.nchunks + 1023) / 1024;
+  // query runs: about 256 workgroups in total, each walking several chunks
+  // (so that its next query tile can load while the current one is used)
+  int64_t Gq = (nbh * p.nchunks + 255) / 256;
   if (Gq < 1) Gq = 1;
   const int64_t nqseg = (p.nchunks + Gq - 1) / Gq;
   k_out_nc<T, DP, C><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks, Gq, nqseg, p.nseg, states);
