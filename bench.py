@@ -97,6 +97,43 @@ def algorithmic_flops(w):
     return 2 * (B * Hkv * n * d * d + B * Hq * (n * d * d + 2 * n * C * d))
 
 
+# Counter-based HBM traffic of the single-launch causal kernel: taken with
+# rocprofv3 (FETCH_SIZE and WRITE_SIZE passes, scaled by the same counters'
+# readings for a plain 64 MiB device copy) and recorded under profiles/
+# together with a hash of the kernel's sources; reported only while the
+# sources still hash the same (null once the kernel has changed).
+COUNTER_FILE = os.path.join(ROOT, "profiles", "k_causal_fused_causal_bf16_B8H8n2048d64_counters.md")
+COUNTER_SOURCES = ["la_fused.hip", "la_device.h", "la_internal.h"]
+
+
+def kernel_source_hash(files=COUNTER_SOURCES):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "linear_attention_phi_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch from the recorded counters, or None."""
+    try:
+        with open(COUNTER_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`").strip()
+        for key in ("source_sha256:", "hbm_bytes_per_launch:"):
+            if line.startswith(key):
+                vals[key[:-1]] = line[len(key):].strip()
+    if vals.get("source_sha256") != kernel_source_hash() or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
 def tokens_heads(w):
     if w["form"] == "decode":
         return w["B"] * w["Hq"]
@@ -267,7 +304,7 @@ def run(name, args):
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
-        "traffic": None,
+        "traffic": counter_traffic() if single and name == "causal" else None,
         "algorithmic_bytes_per_call": nbytes,
         "algorithmic_flops_per_call": flops,
         "call_us_mean": ms * 1e3,

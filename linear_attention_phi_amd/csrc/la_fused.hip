@@ -136,7 +136,7 @@ struct GroupLds {
   float szp[FD];           // z_prev in fp32 (for the final state)
   uint32_t zph[FD / 2];    // z_prev as bf16 (high, low) pairs (last phase)
   uint32_t zpl[FD / 2];
-  float sinv[G][FC];       // 1 / normaliser per chunk and query (last phase)
+  float sden[G][FC];       // local part of the normaliser per chunk and query
   u32x4 sSx[4][64][2];     // running state block (ma, nb) in bf16, operand order per lane
   bf16 zero[FD];           // zeros: the rows of the z operand other than 0 and 16
 };
@@ -282,7 +282,6 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
   f32x16 S_acc = f32x16{};
   float zloc = 0.0f;  // (nb == 1) z so far for a = 32 IB + r
   f32x16 OUT[G];
-  float den[G];
   if (tg < FD / 2) {
     L.zh[0][tg] = 0u;
     L.zl[0][tg] = 0u;
@@ -377,7 +376,7 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
         const bf16* zlc = reinterpret_cast<const bf16*>(L.zl[c & 1]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mma(dacc, z_frag(zhc, zlc, L.zero, lane, kb), qf[kb]);
-        den[c] = dacc[0] + dacc[8];  // valid in the lanes with h == 0
+        if (h == 0) L.sden[c][i] = dacc[0] + dacc[8];  // rows 0 and 16 live in the lanes with h == 0
       }
 
       // S_loc += relu(K)^T V + ones^T V for block (IB, nb); z (nb == 1 waves)
@@ -523,38 +522,32 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
     A.z_final[head * FD + IB * 32 + r] = L.szp[IB * 32 + r] + zloc;
 
   // ---------------------------------------------------------------- phase 3
-  // waves with nb == 0 finish the normalisers and share them through LDS
-  if (nb == 0) {
-#pragma unroll
-    for (int c = 0; c < G; ++c) {
-      if (c < ncl) {
-        Frag<bf16> qf[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
-        f32x16 zacc = f32x16{};
-        const bf16* zph = reinterpret_cast<const bf16*>(L.zph);
-        const bf16* zpl = reinterpret_cast<const bf16*>(L.zpl);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(zacc, z_frag(zph, zpl, L.zero, lane, kb), qf[kb]);
-        if (h == 0) L.sinv[c][i] = __builtin_amdgcn_rcpf(den[c] + zacc[0] + zacc[8]);
-      }
-    }
-  }
-  __syncthreads();
+  // Every wave adds phi(Q) S_prev to its block and divides by its queries'
+  // normalisers den_local + phi(Q) . z_prev (the second term on MFMA; its
+  // result lives in the lanes with h == 0 and is broadcast to the others).
   const bool has_prev = seg > 0 || g > 0;
   Frag<bf16> sf[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) ld_frag(sf[kb], L.sST + (nb * 32 + r) * LT + 16 * kb + 4 * h);
+  const bf16* zph = reinterpret_cast<const bf16*>(L.zph);
+  const bf16* zpl = reinterpret_cast<const bf16*>(L.zpl);
+  float inv[G];
 #pragma unroll
   for (int c = 0; c < G; ++c) {
+    inv[c] = 0.0f;
     if (c < ncl) {
-      if (has_prev) {
-        Frag<bf16> qf[4];
+      Frag<bf16> qf[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
+      for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
+      if (has_prev) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mma(OUT[c], sf[kb], qf[kb]);
       }
+      f32x16 zacc = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(zacc, z_frag(zph, zpl, L.zero, lane, kb), qf[kb]);
+      const float zq = __shfl(zacc[0] + zacc[8], r);  // from the lane with h == 0
+      inv[c] = __builtin_amdgcn_rcpf(L.sden[c][i] + zq);
     }
   }
   // the output rows go through LDS (into the phi(Q) tiles, which are no
@@ -564,12 +557,13 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
 #pragma unroll
   for (int c = 0; c < G; ++c) {
     if (c < ncl) {
-      const float inv = L.sinv[c][i];
+      const float inv_c = inv[c];
       const f32x16& o = OUT[c];
       uint2* srow = reinterpret_cast<uint2*>(L.sQ[c] + i * LT + nb * 32 + 4 * h);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        srow[2 * qq] = make_uint2(pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv), pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+        srow[2 * qq] = make_uint2(pack2(o[4 * qq] * inv_c, o[4 * qq + 1] * inv_c),
+                                  pack2(o[4 * qq + 2] * inv_c, o[4 * qq + 3] * inv_c));
     }
   }
   __syncthreads();
