@@ -512,18 +512,50 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
 // in LDS (nchunks <= kMaxBuckets).  The order inside a bucket is arbitrary,
 // which changes no output: each query's row is computed on its own.
 // m_i outside [0, n-1] is clamped into that range.
+// Add 1 for each valid lane to cnt[b] and return the counter's value before
+// this lane's unit.  When every valid lane of the wave has the same b (as
+// when m is sorted), one lane adds the wave's count and each lane takes its
+// rank among the valid lanes; otherwise each lane adds its own unit.
+__device__ __forceinline__ int bucket_take(int* cnt, int b, bool valid, int lane) {
+  const uint64_t act = __ballot(valid);
+  if (act == 0) return 0;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const int b0 = __shfl(b, leader);
+  if (__ballot(valid && b == b0) == act) {
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&cnt[b0], __popcll(act));
+    base = __shfl(base, leader);
+    return base + __popcll(act & ((1ull << lane) - 1ull));
+  }
+  return valid ? atomicAdd(&cnt[b], 1) : 0;
+}
+
 __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks,
                                                  int* __restrict__ boff, int* __restrict__ perm) {
   __shared__ int cnt[la_internal::kMaxBuckets + 1];
   __shared__ int part[1024];
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
   const int len = (int)nchunks + 1;
   for (int c = tid; c < len; c += nt) cnt[c] = 0;
   __syncthreads();
-  for (int64_t i = tid; i < n; i += nt) {
-    int64_t mi = m[i];
-    mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
-    atomicAdd(&cnt[mi / C + 1], 1);
+  // queries in blocks of PER per thread: all of a block's mask values are
+  // loaded before its counters are touched
+  constexpr int PER = 8;
+  const int64_t step = (int64_t)nt * PER;
+  for (int64_t base = 0; base < n; base += step) {
+    int bk[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int64_t i = base + tid + (int64_t)k * nt;
+      bk[k] = -1;
+      if (i < n) {
+        int64_t mi = m[i];
+        mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
+        bk[k] = (int)(mi / C);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) bucket_take(cnt, bk[k] + 1, bk[k] >= 0, lane);
   }
   __syncthreads();
   // inclusive scan of cnt[0..nchunks] (cnt[0] == 0): contiguous per-thread
@@ -547,11 +579,24 @@ __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, 
     boff[c] = run;
   }
   __syncthreads();
-  for (int64_t i = tid; i < n; i += nt) {
-    int64_t mi = m[i];
-    mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
-    const int pos = atomicAdd(&cnt[mi / C], 1);  // cnt[c] is now bucket c's fill cursor
-    perm[pos] = (int)i;
+  // cnt[c] is now bucket c's fill cursor
+  for (int64_t base = 0; base < n; base += step) {
+    int bk[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int64_t i = base + tid + (int64_t)k * nt;
+      bk[k] = -1;
+      if (i < n) {
+        int64_t mi = m[i];
+        mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
+        bk[k] = (int)(mi / C);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int pos = bucket_take(cnt, bk[k], bk[k] >= 0, lane);
+      if (bk[k] >= 0) perm[pos] = (int)(base + tid + (int64_t)k * nt);
+    }
   }
 }
 
