@@ -17,7 +17,8 @@ inline int padded_dim(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
 // sP [C][C+4] in the element type, plus two [DP] fp32 vectors.  A (dtype,
 // chunk) pair is offered only when this fits in one CU's 160 KiB of LDS.
 constexpr size_t chunk_lds_bytes(int eb, int DP, int C) {
-  return (size_t)eb * (2 * C * (DP + 4) + 2 * DP * (C + 4) + DP * (DP + 4) + C * (C + 4)) + 8 * (size_t)DP;
+  return (size_t)eb * (2 * C * (DP + 4) + 2 * DP * (C + 4) + DP * (DP + 4) + C * (C + 4) + 3 * (DP + 16) + 16) +
+         8 * (size_t)DP;
 }
 constexpr size_t kLdsLimit = 160 * 1024;
 constexpr bool chunk_fits(int eb, int DP, int C) { return chunk_lds_bytes(eb, DP, C) <= kLdsLimit; }

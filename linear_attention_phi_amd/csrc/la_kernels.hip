@@ -195,6 +195,13 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
   __shared__ __attribute__((aligned(16))) T sP[C * LC];
   __shared__ float sz[DP];
   __shared__ float svc[DP];  // sum of V over the chunks done so far (see k_state)
+  // z in the input type as a high part and the remainder (z = high + low to
+  // about 2^-17 in bf16; exact high and zero low in fp32), and a zero row:
+  // the rows of the A operand of the phi(Q) . z products
+  __shared__ __attribute__((aligned(16))) T szh[DP + 16];
+  __shared__ __attribute__((aligned(16))) T szl[DP + 16];
+  __shared__ __attribute__((aligned(16))) T szero[DP + 16];
+  __shared__ __attribute__((aligned(16))) T sones[16];
   using SB = StateBlocks<DP>;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
@@ -223,6 +230,12 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
   // segment start).  z is carried exactly in zrun.
   float zrun = 0.0f, vrun = 0.0f;
   if (NORM && tid < DP) zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + tid];
+  if (NORM && tid < 16) sones[tid] = cvt<T>(1.0f);
+  if (NORM && tid < 16) {
+    szero[DP + tid] = cvt<T>(0.0f);
+    szh[DP + tid] = cvt<T>(0.0f);
+    szl[DP + tid] = cvt<T>(0.0f);
+  }
   if (NORM && tid < DP) svc[tid] = 0.0f;
   if (NORM) __syncthreads();
 
@@ -303,7 +316,13 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
         st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
       }
     }
-    if (NORM && tid < DP) sz[tid] = zrun;
+    if (NORM && tid < DP) {
+      sz[tid] = zrun;
+      const T zh = cvt<T>(zrun);
+      szh[tid] = zh;
+      szl[tid] = cvt<T>(zrun - to_f(zh));
+      szero[tid] = cvt<T>(0.0f);
+    }
 
     for (int grp = 0; grp < ngroups; ++grp) {
       // ---- query tile of this group
@@ -360,15 +379,32 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
       const int i = ib * 32 + (lane & 31);
       if (has_out) {
         if (NORM) {
-          float part = 0.0f;
-          const T* qrow = sQ + i * LQ + h * (DP / 2);
-          const float* zz = sz + h * (DP / 2);
-          for (int a = 0; a < DP / 2; ++a) part += to_f(qrow[a]) * zz[a];
-          constexpr int JMAX = C;  // entries past the causal limit are zero
-          const int jend = (ib + 1) * 32 < JMAX ? (ib + 1) * 32 : JMAX;
-          const T* prow = sP + i * LC;
-          for (int j = h * (jend / 2); j < (h + 1) * (jend / 2); ++j) part += to_f(prow[j]);
-          inv = 1.0f / (part + __shfl_xor(part, 32));
+          // den_i = sum_j P_ij + phi(Q_i) . z on MFMA: A operand rows 0 (ones
+          // over the keys, then z high over the features) and 16 (z low);
+          // the results land in registers 0 and 8 of the lanes with h == 0
+          const int m = lane & 31;
+          Frag<T> e0;
+          ld_frag(e0, m == 0 ? sones : szero);
+          f32x16 dacc = f32x16{};
+#pragma unroll
+          for (int jb = 0; jb < NIB; ++jb) {
+            if (FORM == CAUSAL && jb > ib) continue;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              Frag<T> fb;
+              ld_frag(fb, sP + i * LC + jb * 32 + 16 * kb + 4 * h);
+              mma(dacc, e0, fb);
+            }
+          }
+          const T* zrow = (m == 0) ? szh : (m == 16) ? szl : szero;
+#pragma unroll
+          for (int kb = 0; kb < DP / 16; ++kb) {
+            Frag<T> fa, fb;
+            ld_frag(fa, zrow + 16 * kb + 4 * h);
+            ld_frag(fb, sQ + i * LQ + 16 * kb + 4 * h);
+            mma(dacc, fa, fb);
+          }
+          inv = 1.0f / __shfl(dacc[0] + dacc[8], lane & 31);
         }
 #pragma unroll
         for (int u = 0; u < NPW; ++u) {
