@@ -709,6 +709,81 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
   }
 }
 
+// Same step for a power-of-two head dim D, with 16-byte state accesses:
+// thread t owns columns 4 (t % (D/4)) .. +3 of rows t / (D/4) + (NT / (D/4)) j
+// (bounded buffer instructions again, so rows past D need no branch); the
+// per-head column sums are reduced across the threads that share columns
+// through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(NT) void k_decode4(const T* __restrict__ q, const T* __restrict__ k,
+                                                const T* __restrict__ v, int R, float* __restrict__ S,
+                                                float* __restrict__ z, T* __restrict__ out) {
+  constexpr int CG = D / 4;                   // 4-column groups per row
+  constexpr int RSTEP = NT / CG;              // row step between a thread's groups
+  constexpr int NV = (D * CG + NT - 1) / NT;  // groups per thread
+  __shared__ float pk[D], vv[D], zn[D], pq[D];
+  __shared__ __attribute__((aligned(16))) float red[RSTEP][D];
+  __shared__ float sden;
+  const int tid = threadIdx.x;
+  const int64_t bg = blockIdx.x;  // b * Hkv + g
+  float* Sg = S + bg * D * D;
+  float* zg = z + bg * D;
+  if (tid < D) {
+    const float pkv = phi_f(to_f(k[bg * D + tid]));
+    pk[tid] = pkv;
+    vv[tid] = to_f(v[bg * D + tid]);
+    const float znew = zg[tid] + pkv;
+    zg[tid] = znew;
+    zn[tid] = znew;
+  }
+  __syncthreads();
+  const int cg = tid % CG, r0 = tid / CG;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(Sg, 0, D * D * 4, 0x00020000);
+  constexpr int OOB = 0x7FFFFFF0;  // past num_records: loads give zero, stores are dropped
+  f32x4 s4[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int a = r0 + RSTEP * j;
+    const int off = a < D ? (a * D + 4 * cg) * 4 : OOB;
+    s4[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+  const f32x4 vb = {vv[4 * cg], vv[4 * cg + 1], vv[4 * cg + 2], vv[4 * cg + 3]};
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int a = r0 + RSTEP * j;
+    const float pa = a < D ? pk[a] : 0.0f;
+    const int off = a < D ? (a * D + 4 * cg) * 4 : OOB;
+    s4[j] += pa * vb;
+    typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_, s4[j]), rs, off, 0, 0);
+  }
+  for (int r = 0; r < R; ++r) {
+    const int64_t qh = bg * R + r;  // (b * Hkv + g) * R + r = b * Hq + g * R + r
+    __syncthreads();                // previous head's reads of pq / red are done
+    if (tid < D) pq[tid] = phi_f(to_f(q[qh * D + tid]));
+    __syncthreads();
+    if (tid < 64) {  // wave 0: den = phi(q) . z
+      float p = (tid < D ? pq[tid] * zn[tid] : 0.0f) + (tid + 64 < D ? pq[tid + 64] * zn[tid + 64] : 0.0f);
+      for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+      if (tid == 0) sden = p;
+    }
+    f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int a = r0 + RSTEP * j;
+      num += (a < D ? pq[a] : 0.0f) * s4[j];
+    }
+    *reinterpret_cast<f32x4*>(&red[r0][4 * cg]) = num;
+    __syncthreads();
+    if (tid < D) {
+      float acc = 0.0f;
+#pragma unroll 8
+      for (int kk = 0; kk < RSTEP; ++kk) acc += red[kk][tid];
+      out[qh * D + tid] = cvt<T>(acc / sden);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 template <typename T, int DP, int C>
 int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, int form) {
@@ -814,6 +889,26 @@ int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int R = (int)(Hq / Hkv);
   const dim3 grid((unsigned)(B * Hkv));
+#define LA_DEC4(DD)                                                                                           \
+  case DD:                                                                                                    \
+    if (dtype == 0)                                                                                           \
+      k_decode4<float, DD><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k), \
+                                                reinterpret_cast<const float*>(v), R, S, z, reinterpret_cast<float*>(out)); \
+    else                                                                                                      \
+      k_decode4<bf16, DD><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),   \
+                                               reinterpret_cast<const bf16*>(v), R, S, z, reinterpret_cast<bf16*>(out)); \
+    return (int)hipGetLastError();
+  switch (d) {
+    LA_DEC4(4)
+    LA_DEC4(8)
+    LA_DEC4(16)
+    LA_DEC4(32)
+    LA_DEC4(64)
+    LA_DEC4(128)
+    default:
+      break;
+  }
+#undef LA_DEC4
   if (dtype == 0)
     k_decode<float><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
                                          reinterpret_cast<const float*>(v), (int)d, R, S, z,

@@ -161,6 +161,23 @@ def test_decode_continues_causal(gpu, dtype):
     np.testing.assert_allclose(z.cpu().numpy(), zf, rtol=1e-5)
 
 
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("d", [1, 3, 4, 16, 33, 100, 128])
+def test_decode_head_dims(gpu, dtype, d):
+    """Decode steps over head dims that take the 16-byte path (powers of two)
+    and the scalar path (the others), continuing a causal prefix."""
+    B, Hq, Hkv, n, T = 2, 4, 2, 40, 3
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=11 + d, scaled=True)
+    full, Sf, zf = oracle.causal(q, k, v, want_state=True)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    S, z = gpu.la_causal_forward(None, kd[:, :, :n - T].contiguous(), vd[:, :, :n - T].contiguous(), Hq=Hq)
+    for t in range(n - T, n):
+        o = gpu.la_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), S, z)
+        check(host(o), full[:, :, t], dtype, f"decode d={d} step {t}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sf, rtol=1e-4, atol=1e-4 * np.abs(Sf).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zf, rtol=1e-5)
+
+
 def test_state_only_matches_full_pass(gpu):
     q, k, v, _ = li.qkv(2, 4, 2, 300, 64, li.BF16, seed=7, scaled=True)
     _, S1, z1 = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True)
