@@ -176,8 +176,15 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 // rows, for each of the R query heads of this key/value head) or prefix
 // (FORM = PREFIX: identity feature map, no normaliser, R = 1; the queries of
 // chunk c are the bucket perm[boff[c] .. boff[c+1]) in tiles of C).
+// Waves per SIMD that k_out is compiled for: two where its tiles leave room for
+// two workgroups per CU (then the registers must fit that occupancy), else one.
+template <typename T, int DP, int C>
+constexpr int k_out_waves() {
+  return la_internal::chunk_lds_bytes((int)sizeof(T), DP, C) <= la_internal::kLdsLimit / 2 ? 2 : 1;
+}
+
 template <typename T, int DP, int C, int FORM>
-__global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<T, DP, C>()))) void k_out(const T* __restrict__ q, const T* __restrict__ k,
                                             const T* __restrict__ v, T* __restrict__ out, int64_t n, int d,
                                             int R, bool vec, int64_t nchunks, int64_t G, int64_t nseg,
                                             const float* __restrict__ ws, const int* __restrict__ perm,
@@ -259,10 +266,10 @@ __global__ __launch_bounds__(NT) void k_out(const T* __restrict__ q, const T* __
     return {q + bh * n * d, perm + s0, (int)(rem < C ? rem : C)};
   };
   // With d == DP the tiles are prefetched one step ahead: the next query tile
-  // while the current group runs, and (DP <= 64, where the registers allow two
-  // workgroups per CU even so) K and V of the next chunk while the current
-  // chunk's groups run.
-  constexpr bool PF_KV = DP <= 64;
+  // while the current group runs, and K and V of the next chunk while the
+  // current chunk's groups run (the kernel is compiled for two waves per
+  // SIMD, so that two workgroups share a CU where LDS allows).
+  constexpr bool PF_KV = true;
   TileRaw<T, DP, C> rK, rV, rQ;
   int64_t kv_c = -1, q_c = -1;  // which chunk / (chunk, group) the registers hold
   int q_g = 0;
