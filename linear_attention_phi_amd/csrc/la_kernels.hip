@@ -840,9 +840,11 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   const int64_t E = slot_elems(DP);
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr);
-  // query runs: about 256 workgroups in total, each walking several chunks
-  // (so that its next query tile can load while the current one is used)
-  int64_t Gq = (nbh * p.nchunks + 255) / 256;
+  // query runs: about 1024 workgroups in total for 2-byte inputs (several per
+  // CU keep more query tiles in flight), about 256 for 4-byte inputs (longer
+  // runs, each loading its next, twice as large, tile while it computes)
+  const int64_t target = sizeof(T) == 2 ? 1024 : 256;
+  int64_t Gq = (nbh * p.nchunks + target - 1) / target;
   if (Gq < 1) Gq = 1;
   const int64_t nqseg = (p.nchunks + Gq - 1) / Gq;
   k_out_nc<T, DP, C><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks, Gq, nqseg, p.nseg, states);
