@@ -5,24 +5,30 @@
 // out_i = phi(Q_i) S_i / (phi(Q_i) . z_i) with S_i, z_i over keys 0..i;
 // nx_f32_linear_attention.nx for phi, S, z and the read; trim-transformer
 // 0.1.0 "Masking" for the causal prefix), organised so that every input
-// byte is read from HBM once and every output byte written once:
+// byte is read from HBM once and every output byte written once, with all
+// of a workgroup's loads in flight from its start:
 //
-//  phase 1  a workgroup walks the G chunks of its segment with a state S_loc
-//           that starts at zero at the segment start; per chunk it builds
-//           the un-normalised numerator
-//             num_c = phi(Q_c) S_loc + tril(phi(Q_c) phi(K_c)^T) V_c
-//           and denominator den_c in registers, then S_loc += phi(K_c)^T V_c;
-//  phase 2  it publishes its segment aggregate (S_loc, z_loc) and sums the
-//           aggregates of all earlier segments of the head (waiting on their
-//           flags): S_prev, z_prev;
-//  phase 3  out_c = (num_c + phi(Q_c) S_prev) / (den_c + phi(Q_c) . z_prev).
+//  A  a workgroup owns a segment of eight chunks; wave w owns chunk w.  It
+//     loads the chunk's Q, K and V at once, and forms, in registers, the
+//     chunk-local numerator tril(phi(Q) phi(K)^T) V and denominator, and the
+//     chunk's state dS = phi(K)^T V (fp32, written to LDS) and z;
+//  B  the eight waves scan the states of the segment (each wave a slice of
+//     rows, over the eight chunks): exclusive prefixes S_loc(c), z_loc(c) and
+//     the segment aggregate, which is published; the aggregates of all
+//     earlier segments of the head are summed (waiting on their flags):
+//     S_prev, z_prev; S_pre(c) = S_prev + S_loc(c) goes to LDS as bf16;
+//  C  every wave adds phi(Q) S_pre(c) and phi(Q) . z_pre(c), normalises and
+//     writes its chunk's rows.
 //
-// Waves: each group's four waves own the four (query block ib, feature block
-// nb) quarters of the 64 x 64 output tile; wave (ib, nb) keeps state block
-// (ib, nb) of S_loc in MFMA accumulators and swaps a bf16 copy with its
-// partner (1 - ib, nb) through LDS for the phi(Q) S products.  P^T = phi(K) phi(Q)^T is computed per wave for its query block;
-// its accumulators are the B operand of the V^T P^T product (see
-// la_device.h), so P never goes through LDS.  phi(K)^T V is formed as
+// MFMA operands (v_mfma_f32_32x32x16_bf16): products over the feature index
+// read 16 contiguous bytes per lane (k = 16 kb + 8 h + {0..7}); products
+// over the token index take the accumulator-derived order of la_device.h
+// (k = 16 kt + 4 h + {0..3}, 16 kt + 8 + 4 h + {0..3}), so P^T's accumulator
+// feeds the V^T P^T product directly, and the transposed V and relu(K)
+// operands are read from the token-major LDS tiles with ds_read_b64_tr_b16
+// (in each group of 16 lanes, lane k reads 4 elements of row k / 4 at column
+// 4 (k % 4); lane i receives element e of lane 4 e + i / 4's read at
+// position i % 4: rows r0..r0+3 of column c0 + i).  phi(K)^T V is formed as
 // relu(K)^T V + 1 (x) sum_t V_t (exact products; see la_kernels.hip).
 //
 // Segments are numbered segment-major (blockIdx = seg * NH + head), so a
@@ -42,21 +48,21 @@ namespace {
 
 using namespace la_dev;
 
-constexpr int FD = 64;        // head dim
-constexpr int FC = 64;        // chunk
-constexpr int LT = FD + PAD;  // token-major LDS row stride (elements)
-constexpr int LF = FC + PAD;  // feature-major LDS row stride
-constexpr int AGG_FLOATS = 4 * 64 * 16 + FD;  // published segment aggregate: 4 blocks in lane order + z
+constexpr int FD = 64;                    // head dim
+constexpr int FC = 64;                    // chunk
+constexpr int SEGC = 8;                   // chunks per segment = waves per workgroup
+constexpr int FNT = 64 * SEGC;            // threads per workgroup
+constexpr int RS = FD + 8;                // row stride (bf16) of the token-major tiles: 144 bytes
+constexpr int RSF = FD + 4;               // row stride (fp32) of the state tiles: 272 bytes
+constexpr int AGG_FLOATS = FD * FD + FD;  // published segment aggregate: S^T [b][a], then z
+constexpr int TILE_B = FC * RS * 2;       // bytes of one token-major bf16 tile
+constexpr int REGION_B = 2 * TILE_B;      // one wave's LDS region
 
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int G = 4;           // chunks per group (4 waves)
-constexpr int NGRP = 2;        // groups per workgroup: a segment is G * NGRP chunks
-constexpr int FNT = NT * NGRP; // threads per workgroup
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const bf16x2 t = {(bf16)lo, (bf16)hi};
@@ -84,119 +90,36 @@ __device__ __forceinline__ uint32_t pair(const Frag<bf16>& f, int p) {
 }
 constexpr uint32_t ONE2 = 0x3F803F80u;  // two bf16 ones
 
-// Registers holding one chunk's inputs between its global loads and its LDS
-// writes.  Thread t (of a group's 256) handles rows 2 * (t >> 3) and
-// 2 * (t >> 3) + 1, features 8 * (t & 7) .. +7, of both K and V, and the
-// 16-byte Q pieces t and t + 256 (row p >> 3, features 8 * (p & 7) .. +7).
-// Rows past the sequence end load as zero.
-struct Stage {
-  u32x4 k2[2], v2[2], qp[2];
-};
-
-// The three inputs of one head are read through buffer resources bounded to
-// the head's n rows: rows past the sequence end read as zero (relu(0) = 0
-// keeps such keys and values out of every sum; such queries are never
-// stored).
-struct HeadRsrc {
-  __amdgpu_buffer_rsrc_t q, k, v;
-};
-__device__ __forceinline__ void stage_load(Stage& st, const HeadRsrc& R, int t0, int tid) {
-  const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int off = ((t0 + r0 + r) * FD + c0) * 2;
-    st.k2[r] = __builtin_amdgcn_raw_buffer_load_b128(R.k, off, 0, 0);
-    st.v2[r] = __builtin_amdgcn_raw_buffer_load_b128(R.v, off, 0, 0);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int p = tid + 256 * u, row = p >> 3, col = 8 * (p & 7);
-    st.qp[u] = __builtin_amdgcn_raw_buffer_load_b128(R.q, ((t0 + row) * FD + col) * 2, 0, 0);
-  }
+// 16 contiguous bf16 bytes: an operand fragment over the feature index.
+__device__ __forceinline__ Frag<bf16> ld16(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
 }
-
-// Two rows x 8 features -> 8 feature rows of 2 tokens (one dword each).
-__device__ __forceinline__ void store_pairs_transposed(bf16* fm, int r0, int c0, const uint32_t (&x)[2][4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<uint32_t*>(fm + (c0 + 2 * j) * LF + r0) = (x[0][j] & 0xFFFFu) | (x[1][j] << 16);
-    *reinterpret_cast<uint32_t*>(fm + (c0 + 2 * j + 1) * LF + r0) = (x[0][j] >> 16) | (x[1][j] & 0xFFFF0000u);
-  }
+// Operand fragment over the token index from a token-major tile: lane l
+// (row index r = l % 32, half h = l / 32) gets column c0 + r of rows
+// t0 + 4 h + {0..3} and t0 + 8 + 4 h + {0..3}, where c0 is the 32-column
+// block; two transposed reads.
+__device__ __forceinline__ Frag<bf16> ld_tr(const bf16* tile, int t0, int c0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const bf16* p = tile + (t0 + 4 * (g >> 1) + (i >> 2)) * RS + c0 + 16 * (g & 1) + 4 * (i & 3);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * RS));
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
 }
-
-// The LDS of one group.
-struct GroupLds {
-  bf16 sQ[G][FC * LT];     // phi(Q) of every chunk of the group (kept for the last phase)
-  bf16 sK[FC * LT];        // relu(K), token-major
-  bf16 sKT[FD * LF];       // relu(K), feature-major
-  bf16 sVT[FD * LF];       // V, feature-major
-  bf16 sST[FD * LT];       // S_prev^T in bf16 (last phase)
-  uint32_t zh[2][FD / 2];  // z so far as bf16 pairs, high part (double-buffered by chunk parity)
-  uint32_t zl[2][FD / 2];  // ... and the low part: z = zh + zl to about 2^-17
-  float szp[FD];           // z_prev in fp32 (for the final state)
-  uint32_t zph[FD / 2];    // z_prev as bf16 (high, low) pairs (last phase)
-  uint32_t zpl[FD / 2];
-  float sden[G][FC];       // local part of the normaliser per chunk and query
-  u32x4 sSx[4][64][2];     // running state block (ma, nb) in bf16, operand order per lane
-  bf16 zero[FD];           // zeros: the rows of the z operand other than 0 and 16
-};
-
-// Stage -> LDS, in two parts: sQ[c][i][a] = phi(Q) (into the chunk's own
-// tile, so it can be written while the previous chunk is being computed), and
-// sK[j][a] = relu(K), sKT[a][t] = relu(K), sVT[b][t] = V (shared tiles).  Rows
-// past the sequence end arrive as zeros (stage_load).  The empty asm
-// statements pin the use of the staged registers here, so that the compiler
-// does not move this work -- and the wait for its loads -- ahead of earlier
-// chunks.
-__device__ __forceinline__ void stage_store_q(Stage& st, bf16* sQc, int tid) {
-  asm volatile("" : "+v"(st.qp[0]), "+v"(st.qp[1]) : : "memory");
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int p = tid + 256 * u, row = p >> 3, col = 8 * (p & 7);
-    uint2* dst = reinterpret_cast<uint2*>(sQc + row * LT + col);
-    dst[0] = make_uint2(phi2(st.qp[u][0]), phi2(st.qp[u][1]));
-    dst[1] = make_uint2(phi2(st.qp[u][2]), phi2(st.qp[u][3]));
-  }
-}
-__device__ __forceinline__ void stage_store_kv(Stage& st, GroupLds& L, int tid) {
-  asm volatile("" : "+v"(st.k2[0]), "+v"(st.k2[1]), "+v"(st.v2[0]), "+v"(st.v2[1]) : : "memory");
-  const int r0 = 2 * (tid >> 3), c0 = 8 * (tid & 7);
-  uint32_t xk[2][4], xv[2][4];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xk[r][j] = relu2(st.k2[r][j]);
-      xv[r][j] = st.v2[r][j];
-    }
-    uint2* dst = reinterpret_cast<uint2*>(L.sK + (r0 + r) * LT + c0);
-    dst[0] = make_uint2(xk[r][0], xk[r][1]);
-    dst[1] = make_uint2(xk[r][2], xk[r][3]);
-  }
-  store_pairs_transposed(L.sKT, r0, c0, xk);
-  store_pairs_transposed(L.sVT, r0, c0, xv);
-}
-
-// Operand fragment from accumulator registers 8 * half .. 8 * half + 7, in bf16.
+// Accumulator registers 8 half .. 8 half + 7 as an operand fragment over the
+// accumulator's row index (token order of ld_tr).
 __device__ __forceinline__ Frag<bf16> acc_frag(const f32x16& acc, int half) {
   Frag<bf16> f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = (bf16)acc[8 * half + e];
   return f;
 }
-
-// A operand for the phi(Q) . z products on MFMA: row 0 holds the bf16 high
-// parts of z, row 16 the low parts (z = high + low to about 2^-17), the other
-// rows zero.  Against phi(Q)^T, output rows 0 and 16 of column i then hold
-// phi(Q_i) . z_high and phi(Q_i) . z_low (accumulator registers 0 and 8 of
-// the lanes with h = 0).  zh, zl: z in feature order as bf16.
-__device__ __forceinline__ Frag<bf16> z_frag(const bf16* zh, const bf16* zl, const bf16* zero, int lane, int kb) {
-  const int m = lane & 31, h = lane >> 5;
-  const bf16* base = (m == 0) ? zh : (m == 16) ? zl : zero;
-  Frag<bf16> f;
-  ld_frag(f, base + 16 * kb + 4 * h);
-  return f;
-}
+// Waits for this wave's LDS operations, so that lanes read what other lanes
+// of the wave wrote (a wave's LDS accesses complete in order).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Cross-workgroup data (segment aggregates) is written and read with
 // device-scope (sc1) buffer accesses, which gfx950 performs at the device
@@ -230,230 +153,230 @@ struct FusedArgs {
   float* S_final; float* z_final; uint32_t* err;
 };
 
-// Write z values held one per lane (feature a = a0 + lane index within the
-// writing lanes) into the (high, low) bf16 pair arrays: even lanes pair with
-// their right neighbour.  All 64 lanes must call it; lanes with write set and
-// an even feature store.
-__device__ __forceinline__ void store_z_pairs(uint32_t* zh, uint32_t* zl, float z, int a, bool write) {
+// Write z values held one per lane (feature a = lane) into (high, low) bf16
+// pair arrays: even lanes pair with their right neighbour.  All 64 lanes call.
+__device__ __forceinline__ void store_z_pairs(uint32_t* zh, uint32_t* zl, float z, int a) {
   const float zn = __shfl_down(z, 1);
-  if (write && (a & 1) == 0) {
+  if ((a & 1) == 0) {
     const uint32_t hi = pack2(z, zn);
     zh[a >> 1] = hi;
     zl[a >> 1] = pack2(z - lo_f(hi), zn - hi_f(hi));
   }
 }
 
-// The work of one wave of group g; IB (its query block) is a template
-// parameter so that the causal block structure and masks are resolved at
-// compile time.  Every wave of the workgroup executes the same sequence of
-// barriers.
-template <int IB>
-__device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NGRP], float* xch) {
+// LDS: one region per wave, reused phase by phase:
+//   A: relu(K) at [0, TILE_B), V at [TILE_B, 2 TILE_B), token-major rows of
+//      RS; then the chunk's state dS^T [b][a] in fp32 rows of RSF, rows
+//      b < 32 over the V tile and b >= 32 over the K tile;
+//   C: S_pre^T [b][a] in bf16 at [0, TILE_B), the output rows at
+//      [TILE_B, 2 TILE_B).
+struct CpLds {
+  uint8_t reg[SEGC][REGION_B];
+  float zloc[SEGC][FD];        // z of each chunk (then not needed)
+  uint32_t zh[SEGC][FD / 2];   // z_pre of each chunk as bf16 (high, low) pairs
+  uint32_t zl[SEGC][FD / 2];
+  bf16 zero[FD];               // zeros: the rows of the z operand other than 0 and 16
+};
+static_assert(32 * RSF * 4 <= TILE_B, "state half-tile must fit a token-major tile");
+
+__device__ __forceinline__ float* state_row(CpLds& L, int c, int b) {
+  return reinterpret_cast<float*>(L.reg[c] + (b < 32 ? TILE_B : 0)) + (b & 31) * RSF;
+}
+
+__global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
+  __shared__ __attribute__((aligned(16))) CpLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int g = w >> 2;  // group
-  // feature block; nb == 0 waves also own the normaliser, nb == 1 waves z.
-  // Group 1 takes the complementary roles, so that the two waves sharing a
-  // SIMD (w and w + 4) carry one heavy and one light share of the work.
-  const int nb = ((w >> 1) & 1) ^ g;
-  const int tg = tid & (NT - 1);
-  GroupLds& L = LL[g];
   const int64_t seg = blockIdx.x / A.NH, head = blockIdx.x % A.NH;
   const int hbytes = (int)(A.n * FD * 2);  // one head's rows (n <= 2^24)
-  const HeadRsrc R{__builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + head * A.n * FD), 0, hbytes, 0x00020000),
-                   __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.k + head * A.n * FD), 0, hbytes, 0x00020000),
-                   __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.v + head * A.n * FD), 0, hbytes, 0x00020000)};
-  const int64_t c_begin = seg * (G * NGRP) + g * G;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + head * A.n * FD), 0, hbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.k + head * A.n * FD), 0, hbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.v + head * A.n * FD), 0, hbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(A.out + head * A.n * FD, 0, hbytes, 0x00020000);
+  const int64_t c_begin = seg * SEGC;
   const int64_t rem = A.nchunks - c_begin;
-  const int ncl = (int)(rem < 0 ? 0 : (rem < G ? rem : G));
-  const int i = IB * 32 + r;  // this lane's query row within a chunk
+  const int ncl = (int)(rem < SEGC ? rem : SEGC);  // chunks of this segment (>= 1)
+  const bool mine = w < ncl;                       // this wave owns a chunk
+  const int t0 = (int)((c_begin + w) * FC);        // its first row
+  const int nv = mine ? (int)((A.n - t0) < FC ? (A.n - t0) : FC) : 0;
+  bf16* tK = reinterpret_cast<bf16*>(L.reg[w]);
+  bf16* tV = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
+  if (tid < FD) L.zero[tid] = (bf16)0.0f;
 
-  // loads run two chunks ahead of the chunk being computed
-  Stage st[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    if (c < ncl) stage_load(st[c], R, (int)((c_begin + c) * FC), tg);
-  }
-
-  // ---------------------------------------------------------------- phase 1
-  // S_acc: block (ma = IB, nb) of phi(K)^T V over the group's chunks so far,
-  // built as relu(K)^T V + ones^T V (exact products).  The partner wave
-  // (1 - IB, nb) holds block (1 - IB, nb); the two swap bf16 copies through
-  // LDS once per chunk for the phi(Q) S products.
-  f32x16 S_acc = f32x16{};
-  float zloc = 0.0f;  // (nb == 1) z so far for a = 32 IB + r
-  f32x16 OUT[G];
-  if (tg < FD / 2) {
-    L.zh[0][tg] = 0u;
-    L.zl[0][tg] = 0u;
-  }
   Frag<bf16> ones, e0;  // all ones; ones in row 0 only (P row sums on MFMA)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     ones.v[e] = (bf16)1.0f;
     e0.v[e] = (bf16)(r == 0 ? 1.0f : 0.0f);
   }
-  if (tg < FD) L.zero[tg] = (bf16)0.0f;
-  // causal mask of the diagonal P^T block: element e holds key row
-  // 8 (e >> 2) + 4 h + (e & 3) of query row r
-  bool keep[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) keep[e] = 8 * (e >> 2) + 4 * h + (e & 3) <= r;
 
-  // chunk 0's tiles
-  if (ncl > 0) {
-    stage_store_q(st[0], L.sQ[0], tg);
-    stage_store_kv(st[0], L, tg);
-    if (2 < ncl) stage_load(st[0], R, (int)((c_begin + 2) * FC), tg);
-  }
-  __syncthreads();
-  // Per chunk c: compute c, and stage phi(Q) of chunk c + 1 into its own tile
-  // in the same interval; after a barrier, hand the state block S_loc(c + 1)
-  // to the partner wave and stage chunk c + 1's K and V.
-  Frag<bf16> sown[2];  // own state block S_loc(c) as operand fragments
+  // ------------------------------------------------------------------ A
+  // Loads: K and V as 16-byte row pieces (rows lane / 8 + 8 u), Q directly
+  // as operand fragments (query row 32 ib + r, features 16 kb + 8 h ..).
+  // Rows past the sequence end read as zero.
+  f32x16 O[2][2];     // numerator blocks (feature block nb, query block ib): rows b, column i
+  Frag<bf16> qf[2][4];  // phi(Q) fragments (query block ib, feature block kb)
+  float den[2] = {0.0f, 0.0f};  // chunk-local normaliser of query 32 ib + r (lanes with h == 0)
 #pragma unroll
-  for (int c = 0; c < G; ++c) {
-    if (c < ncl) {
-      const int64_t t0 = (c_begin + c) * FC;
-      const int nv = (int)((A.n - t0) < FC ? (A.n - t0) : FC);
-      Frag<bf16> qf[4], vt[4];
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
+    for (int ib = 0; ib < 2; ++ib) O[nb][ib] = f32x16{};
+  if (mine) {
+    u32x4 kr[8], vr[8], qr[2][4];
+    const int prow = lane >> 3, pcol = 8 * (lane & 7);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) ld_frag(vt[kt], L.sVT + (nb * 32 + r) * LF + 16 * kt + 4 * h);
-      // P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]; the second term (the
-      // same for every key row) comes from an all-ones A operand
+    for (int u = 0; u < 8; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, 0);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        qr[ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((t0 + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      u32x4 x = kr[u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = relu2(x[j]);
+      *reinterpret_cast<u32x4*>(tK + (prow + 8 * u) * RS + pcol) = x;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(tV + (prow + 8 * u) * RS + pcol) = vr[u];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4 x = qr[ib][kb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
+        qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
+      }
+    wave_lds_sync();
+
+    // V^T fragments (feature block nb, token block kt): A operand of V^T P^T,
+    // B operand of relu(K)^T V
+    Frag<bf16> vt[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) vt[nb][kt] = ld_tr(tV, 16 * kt, 32 * nb, lane);
+
+    // P^T blocks (key block jb, query block ib), jb <= ib:
+    //   P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
+    // (the second term from an all-ones A operand); only the diagonal block
+    // is masked: element e holds key row 8 (e >> 2) + 4 h + (e & 3) of query r.
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
       f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(sacc, ones, qf[kb]);
-
-      // P^T blocks for key blocks jb <= IB; only the diagonal block is masked
-      Frag<bf16> pfr[IB + 1][2];
+      for (int kb = 0; kb < 4; ++kb) mma(sacc, ones, qf[ib][kb]);
+      f32x16 dacc = f32x16{};
 #pragma unroll
-      for (int jb = 0; jb <= IB; ++jb) {
+      for (int jb = 0; jb <= ib; ++jb) {
         f32x16 pacc = sacc;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          Frag<bf16> kf;
-          ld_frag(kf, L.sK + (jb * 32 + r) * LT + 16 * kb + 4 * h);
-          mma(pacc, kf, qf[kb]);
-        }
-        if (jb == IB) {
+        for (int kb = 0; kb < 4; ++kb) mma(pacc, ld16(tK + (32 * jb + r) * RS + 16 * kb + 8 * h), qf[ib][kb]);
+        if (jb == ib) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) pacc[e] = keep[e] ? pacc[e] : 0.0f;
+          for (int e = 0; e < 16; ++e) pacc[e] = (8 * (e >> 2) + 4 * h + (e & 3) <= r) ? pacc[e] : 0.0f;
         }
-        pfr[jb][0] = acc_frag(pacc, 0);
-        pfr[jb][1] = acc_frag(pacc, 1);
+        const Frag<bf16> p0 = acc_frag(pacc, 0), p1 = acc_frag(pacc, 1);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          mma(O[nb][ib], vt[nb][2 * jb], p0);
+          mma(O[nb][ib], vt[nb][2 * jb + 1], p1);
+        }
+        // den_i = sum_j P_ij: row 0 of e0 . P^T
+        mma(dacc, e0, p0);
+        mma(dacc, e0, p1);
       }
+      den[ib] = dacc[0];
+    }
 
-      // num_c = phi(Q) S_loc + V^T P^T   (rows b of block nb, column i)
-      f32x16 o = f32x16{};
-      if (c > 0) {
+    // dS = relu(K)^T V + ones^T V, block (ab, bb): rows a, columns b; written
+    // transposed (row b, four contiguous a per q) into the state tile.  The V
+    // tile is no longer read (its fragments are in registers), so rows b < 32
+    // may overwrite it; rows b >= 32 go over the K tile once its fragments
+    // are loaded.
+    Frag<bf16> kt_[2][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          Frag<bf16> sa;
-          if ((kb >> 1) == IB)
-            sa = sown[kb & 1];
-          else
-            sa.v = __builtin_bit_cast(bf16x8v, L.sSx[(1 - IB) * 2 + nb][lane][kb & 1]);
-          mma(o, sa, qf[kb]);
-        }
-      }
+    for (int ab = 0; ab < 2; ++ab)
 #pragma unroll
-      for (int jb = 0; jb <= IB; ++jb) {
-        mma(o, vt[2 * jb], pfr[jb][0]);
-        mma(o, vt[2 * jb + 1], pfr[jb][1]);
-      }
-      OUT[c] = o;
-      if (nb == 0) {
-        // den_i = sum_j P_ij + phi(Q_i) . z, both on MFMA (rows 0 and 16)
-        f32x16 dacc = f32x16{};
+      for (int kt = 0; kt < 4; ++kt) kt_[ab][kt] = ld_tr(tK, 16 * kt, 32 * ab, lane);
+    // z of the chunk: sum_t relu(K_t)[a] + nv, for a = 32 ab + r
 #pragma unroll
-        for (int jb = 0; jb <= IB; ++jb) {
-          mma(dacc, e0, pfr[jb][0]);
-          mma(dacc, e0, pfr[jb][1]);
-        }
-        const bf16* zhc = reinterpret_cast<const bf16*>(L.zh[c & 1]);
-        const bf16* zlc = reinterpret_cast<const bf16*>(L.zl[c & 1]);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(dacc, z_frag(zhc, zlc, L.zero, lane, kb), qf[kb]);
-        if (h == 0) L.sden[c][i] = dacc[0] + dacc[8];  // rows 0 and 16 live in the lanes with h == 0
-      }
-
-      // S_loc += relu(K)^T V + ones^T V for block (IB, nb); z (nb == 1 waves)
+    for (int ab = 0; ab < 2; ++ab) {
       float zp = 0.0f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        Frag<bf16> kf;
-        ld_frag(kf, L.sKT + (IB * 32 + r) * LF + 16 * kt + 4 * h);
-        mma(S_acc, kf, vt[kt]);
-        mma(S_acc, ones, vt[kt]);
-        if (nb == 1) {
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int p = 0; p < 4; ++p) zp = dot2(pair(kf, p), ONE2, zp);
+        for (int p = 0; p < 4; ++p) zp = dot2(pair(kt_[ab][kt], p), ONE2, zp);
+      zp += __shfl_xor(zp, 32);
+      if (h == 0) L.zloc[w][32 * ab + r] = zp + (float)nv;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll
+      for (int ab = 0; ab < 2; ++ab) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          mma(acc, ones, vt[bb][kt]);
+          mma(acc, kt_[ab][kt], vt[bb][kt]);
         }
-      }
-      if (nb == 1) {
-        zloc += zp + __shfl_xor(zp, 32) + (float)nv;
-        store_z_pairs(L.zh[(c + 1) & 1], L.zl[(c + 1) & 1], zloc, IB * 32 + r, h == 0);
-      }
-    }
-    if (c + 1 < G) {
-      if (c + 1 < ncl) stage_store_q(st[(c + 1) & 1], L.sQ[c + 1], tg);
-      __syncthreads();
-      if (c + 1 < ncl) {
-        sown[0] = acc_frag(S_acc, 0);
-        sown[1] = acc_frag(S_acc, 1);
-        L.sSx[IB * 2 + nb][lane][0] = __builtin_bit_cast(u32x4, sown[0].v);
-        L.sSx[IB * 2 + nb][lane][1] = __builtin_bit_cast(u32x4, sown[1].v);
-        stage_store_kv(st[(c + 1) & 1], L, tg);
-        if (c + 3 < ncl) stage_load(st[(c + 1) & 1], R, (int)((c_begin + c + 3) * FC), tg);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- phase 2
-  // group 0 hands its aggregate (block (IB, nb) in lane order, and z) to
-  // group 1 through LDS; group 1 publishes the segment's aggregate.
-  float* xz = xch + 4 * 64 * 16;
-  if (g == 0) {
-    f32x4v* d4 = reinterpret_cast<f32x4v*>(xch + ((IB * 2 + nb) * 64 + lane) * 16);
+        float* row = state_row(L, w, 32 * bb + r) + 32 * ab + 4 * h;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) d4[u] = f32x4v{S_acc[4 * u], S_acc[4 * u + 1], S_acc[4 * u + 2], S_acc[4 * u + 3]};
-    if (nb == 1 && h == 0) xz[IB * 32 + r] = zloc;
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4v*>(row + 8 * q) = f32x4v{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      }
+    }
   }
   __syncthreads();
-  f32x16 a0 = f32x16{};  // (group 1) group 0's aggregate block
-  float za0 = 0.0f;
+
+  // ------------------------------------------------------------------ B
+  // Scan: wave w owns state rows b = 8 w + lane / 8, features a0 .. a0 + 7.
+  const int sb = 8 * w + (lane >> 3), sa = 8 * (lane & 7);
+  float pre[SEGC][8];  // exclusive prefix over the segment's chunks
+  float run[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) run[e] = 0.0f;
+  float zpre[SEGC];
+  float zrun = 0.0f;
+#pragma unroll
+  for (int c = 0; c < SEGC; ++c) {
+    if (c < ncl) {
+      const float* src = state_row(L, c, sb) + sa;
+      const f32x4v x0 = *reinterpret_cast<const f32x4v*>(src);
+      const f32x4v x1 = *reinterpret_cast<const f32x4v*>(src + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pre[c][e] = run[e];
+        run[e] += e < 4 ? x0[e] : x1[e - 4];
+      }
+      if (w == 0) {
+        zpre[c] = zrun;
+        zrun += L.zloc[c][lane];
+      }
+    }
+  }
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(A.agg + head * A.nseg * AGG_FLOATS, 0, (int)(A.nseg * AGG_FLOATS * 4), 0x00020000);
-  const int blk = ((IB * 2 + nb) * 64 + lane) * 64;  // byte offset of this lane's block values in an aggregate
-  const int zoff = 4 * 64 * 16 * 4;                  // byte offset of z in an aggregate
-  const bool publish = seg + 1 < A.nseg;             // the last segment has no successor
-  uint64_t* flag = A.flags + head * A.nseg;          // this head's segment flags
-  if (g == 1) {
-    const f32x4v* s4 = reinterpret_cast<const f32x4v*>(xch + ((IB * 2 + nb) * 64 + lane) * 16);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f32x4v x = s4[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a0[4 * u + e] = x[e];
-    }
-    za0 = xz[IB * 32 + r];
-    if (publish) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        st_buf<CPOL_SC1>(rs, (int)(seg * AGG_FLOATS * 4) + blk + 16 * u,
-                         f32x4v{a0[4 * u] + S_acc[4 * u], a0[4 * u + 1] + S_acc[4 * u + 1],
-                                a0[4 * u + 2] + S_acc[4 * u + 2], a0[4 * u + 3] + S_acc[4 * u + 3]});
-      if (nb == 1 && h == 0) st_buf1<CPOL_SC1>(rs, (int)(seg * AGG_FLOATS * 4) + zoff + (IB * 32 + r) * 4, za0 + zloc);
-    }
-  }
+  const int soff = (sb * FD + sa) * 4;   // byte offset of this lane's slice in an aggregate
+  const int zoff = FD * FD * 4;          // byte offset of z in an aggregate
+  const bool publish = seg + 1 < A.nseg;  // the last segment has no successor
+  uint64_t* flag = A.flags + head * A.nseg;
   if (publish) {
+    const int base = (int)(seg * AGG_FLOATS * 4);
+    st_buf<CPOL_SC1>(rs, base + soff, f32x4v{run[0], run[1], run[2], run[3]});
+    st_buf<CPOL_SC1>(rs, base + soff + 16, f32x4v{run[4], run[5], run[6], run[7]});
+    if (w == 0) st_buf1<CPOL_SC1>(rs, base + zoff + lane * 4, zrun);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's aggregate stores have completed
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(flag + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __syncthreads();  // also: every state tile has been read
+  if (publish && tid == 0) __hip_atomic_store(flag + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   if (seg > 0) {
     if (w == 0) {
@@ -470,130 +393,97 @@ __device__ __forceinline__ void fused_wave(const FusedArgs& A, GroupLds (&LL)[NG
     }
     __syncthreads();
   }
-  // S_prev of the segment (block (IB, nb)) and z_prev, summed over earlier
-  // segments in order, up to four segments' loads in flight; group 1
-  // adds group 0's aggregate.
-  f32x16 sp = f32x16{};
+  // S_prev and z_prev (this lane's slice), summed over earlier segments in
+  // order, up to four segments' loads in flight
+  float sp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sp[e] = 0.0f;
   float zprev = 0.0f;
-  const bool zlane = (w & 3) == 0;  // wave 0 of each group sums z (lane = feature)
   for (int64_t p = 0; p < seg; p += 4) {
-    f32x4v x[4][4];
+    f32x4v x[4][2];
     float zx[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (p + u < seg) {
         const int base = (int)((p + u) * AGG_FLOATS * 4);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) x[u][q4] = ld_buf<CPOL_SC1>(rs, base + blk + 16 * q4);
-        zx[u] = zlane ? ld_buf1<CPOL_SC1>(rs, base + zoff + lane * 4) : 0.0f;
+        x[u][0] = ld_buf<CPOL_SC1>(rs, base + soff);
+        x[u][1] = ld_buf<CPOL_SC1>(rs, base + soff + 16);
+        zx[u] = w == 0 ? ld_buf1<CPOL_SC1>(rs, base + zoff + lane * 4) : 0.0f;
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (p + u < seg) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sp[4 * q4 + e] += x[u][q4][e];
+        for (int e = 0; e < 4; ++e) {
+          sp[e] += x[u][0][e];
+          sp[e + 4] += x[u][1][e];
+        }
         zprev += zx[u];
       }
     }
   }
-  if (g == 1) {
+  // S_pre(c) = S_prev + S_loc(c) in bf16, [b][a] rows of RS, over region c
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sp[e] += a0[e];
-    if (zlane) zprev += xz[lane];
-  }
-  st_accT(L.sST + nb * 32 * LT + IB * 32, LT, sp, lane);  // sST[b][a] = S_prev[a][b]
-  if (zlane) {
-    L.szp[lane] = zprev;
-    store_z_pairs(L.zph, L.zpl, zprev, lane, true);
-  }
-  if (A.S_final && g == 1 && seg == A.nseg - 1) {
-    float* Sf = A.S_final + head * FD * FD;
+  for (int c = 0; c < SEGC; ++c) {
+    if (c < ncl) {
+      uint32_t y[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int a = IB * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-      Sf[a * FD + nb * 32 + r] = sp[e] + S_acc[e];
+      for (int j = 0; j < 4; ++j) y[j] = pack2(sp[2 * j] + pre[c][2 * j], sp[2 * j + 1] + pre[c][2 * j + 1]);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(L.reg[c]) + sb * RS + sa) = u32x4{y[0], y[1], y[2], y[3]};
+      if (w == 0) store_z_pairs(L.zh[c], L.zl[c], zprev + zpre[c], lane);
     }
   }
+  if (seg == A.nseg - 1) {
+    if (A.S_final) {
+      float* Sf = A.S_final + head * FD * FD;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Sf[(sa + e) * FD + sb] = sp[e] + run[e];
+    }
+    if (A.z_final && w == 0) A.z_final[head * FD + lane] = zprev + zrun;
+  }
   __syncthreads();
-  if (A.z_final && g == 1 && seg == A.nseg - 1 && nb == 1 && h == 0)
-    A.z_final[head * FD + IB * 32 + r] = L.szp[IB * 32 + r] + zloc;
 
-  // ---------------------------------------------------------------- phase 3
-  // Every wave adds phi(Q) S_prev to its block and divides by its queries'
-  // normalisers den_local + phi(Q) . z_prev (the second term on MFMA; its
-  // result lives in the lanes with h == 0 and is broadcast to the others).
-  const bool has_prev = seg > 0 || g > 0;
-  Frag<bf16> sf[4];
+  // ------------------------------------------------------------------ C
+  if (mine) {
+    const bf16* tS = reinterpret_cast<const bf16*>(L.reg[w]);
+    const bf16* zbase = (r == 0) ? reinterpret_cast<const bf16*>(L.zh[w])
+                                 : (r == 16) ? reinterpret_cast<const bf16*>(L.zl[w]) : L.zero;
+    float inv[2];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) ld_frag(sf[kb], L.sST + (nb * 32 + r) * LT + 16 * kb + 4 * h);
-  const bf16* zph = reinterpret_cast<const bf16*>(L.zph);
-  const bf16* zpl = reinterpret_cast<const bf16*>(L.zpl);
-  float inv[G];
+    for (int ib = 0; ib < 2; ++ib) {
+      // numerator += phi(Q) S_pre: A operand S_pre^T (rows b), over features
 #pragma unroll
-  for (int c = 0; c < G; ++c) {
-    inv[c] = 0.0f;
-    if (c < ncl) {
-      Frag<bf16> qf[4];
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) ld_frag(qf[kb], L.sQ[c] + i * LT + 16 * kb + 4 * h);
-      if (has_prev) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(OUT[c], sf[kb], qf[kb]);
-      }
+        for (int kb = 0; kb < 4; ++kb) mma(O[nb][ib], ld16(tS + (32 * nb + r) * RS + 16 * kb + 8 * h), qf[ib][kb]);
+      // den_i += phi(Q_i) . z_pre: rows 0 and 16 (high and low parts of z)
       f32x16 zacc = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(zacc, z_frag(zph, zpl, L.zero, lane, kb), qf[kb]);
-      const float zq = __shfl(zacc[0] + zacc[8], r);  // from the lane with h == 0
-      inv[c] = __builtin_amdgcn_rcpf(L.sden[c][i] + zq);
+      for (int kb = 0; kb < 4; ++kb) mma(zacc, ld16(zbase + 16 * kb + 8 * h), qf[ib][kb]);
+      inv[ib] = __builtin_amdgcn_rcpf(__shfl(den[ib] + zacc[0] + zacc[8], r));  // from the lane with h == 0
     }
-  }
-  // the output rows go through LDS (into the phi(Q) tiles, which are no
-  // longer read once every wave has passed this barrier) so that global
-  // stores cover whole 128-byte rows, 16 bytes per lane
-  __syncthreads();
+    // the output rows go through LDS so that global stores cover whole
+    // 128-byte rows, 16 bytes per lane
+    bf16* tO = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
 #pragma unroll
-  for (int c = 0; c < G; ++c) {
-    if (c < ncl) {
-      const float inv_c = inv[c];
-      const f32x16& o = OUT[c];
-      uint2* srow = reinterpret_cast<uint2*>(L.sQ[c] + i * LT + nb * 32 + 4 * h);
+    for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        srow[2 * qq] = make_uint2(pack2(o[4 * qq] * inv_c, o[4 * qq + 1] * inv_c),
-                                  pack2(o[4 * qq + 2] * inv_c, o[4 * qq + 3] * inv_c));
-    }
-  }
-  __syncthreads();
+      for (int nb = 0; nb < 2; ++nb) {
+        const f32x16& o = O[nb][ib];
+        uint2* dst = reinterpret_cast<uint2*>(tO + (32 * ib + r) * RS + 32 * nb + 4 * h);
 #pragma unroll
-  for (int c = 0; c < G; ++c) {
-    if (c < ncl) {
-      const int64_t t0 = (c_begin + c) * FC;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int p = tg + NT * u, row = p >> 3, col = 8 * (p & 7);
-        if (t0 + row < A.n)
-          *reinterpret_cast<u32x4*>(A.out + (head * A.n + t0 + row) * FD + col) =
-              *reinterpret_cast<const u32x4*>(L.sQ[c] + row * LT + col);
+        for (int q = 0; q < 4; ++q)
+          dst[2 * q] = make_uint2(pack2(o[4 * q] * inv[ib], o[4 * q + 1] * inv[ib]),
+                                  pack2(o[4 * q + 2] * inv[ib], o[4 * q + 3] * inv[ib]));
       }
-    }
+    wave_lds_sync();
+    const int prow = lane >> 3, pcol = 8 * (lane & 7);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
+                                             ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, 0);
   }
-}
-
-__global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
-  __shared__ __attribute__((aligned(16))) GroupLds LL[NGRP];
-  // group 0's K / V tiles are free after the first phase: they carry the
-  // hand-off of group 0's aggregate (AGG_FLOATS floats) to group 1
-  float* xch = reinterpret_cast<float*>(LL[0].sK);
-  static_assert(sizeof(LL[0].sK) + sizeof(LL[0].sKT) + sizeof(LL[0].sVT) >= AGG_FLOATS * sizeof(float),
-                "hand-off area too small");
-  const int w = threadIdx.x >> 6;
-  if (((w & 1) ^ (w >> 2)) == 0)  // query block; complementary in group 1
-    fused_wave<0>(A, LL, xch);
-  else
-    fused_wave<1>(A, LL, xch);
 }
 
 }  // namespace
@@ -617,7 +507,7 @@ int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch) {
   float* agg = reinterpret_cast<float*>(a.ws);
   uint64_t* flags = reinterpret_cast<uint64_t*>(agg + NH * p.nseg * AGG_FLOATS);
   uint32_t* err = reinterpret_cast<uint32_t*>(flags + NH * p.nseg);
-  static_assert(kFusedG == G * NGRP, "segment length");
+  static_assert(kFusedG == SEGC, "segment length");
   FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
               reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, p.nchunks, p.nseg, NH,
               agg, flags, epoch, a.S_final, a.z_final, err};
