@@ -11,7 +11,8 @@
 //  A  a workgroup owns a segment of eight chunks; wave w owns chunk w.  It
 //     loads the chunk's Q, K and V at once, and forms, in registers, the
 //     chunk-local numerator tril(phi(Q) phi(K)^T) V and denominator, and the
-//     chunk's state dS = phi(K)^T V (fp32, written to LDS) and z;
+//     chunk's state dS = relu(K)^T V (fp32, written to LDS), the column sums
+//     of V (its ones^T V part) and z;
 //  B  the eight waves scan the states of the segment (each wave a slice of
 //     rows, over the eight chunks): exclusive prefixes S_loc(c), z_loc(c) and
 //     the segment aggregate, which is published; the aggregates of all
@@ -112,9 +113,11 @@ __device__ __forceinline__ Frag<bf16> ld_tr(const bf16* tile, int t0, int c0, in
 // Accumulator registers 8 half .. 8 half + 7 as an operand fragment over the
 // accumulator's row index (token order of ld_tr).
 __device__ __forceinline__ Frag<bf16> acc_frag(const f32x16& acc, int half) {
-  Frag<bf16> f;
+  u32x4 u;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)acc[8 * half + e];
+  for (int j = 0; j < 4; ++j) u[j] = pack2(acc[8 * half + 2 * j], acc[8 * half + 2 * j + 1]);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, u);
   return f;
 }
 // Waits for this wave's LDS operations, so that lanes read what other lanes
@@ -129,6 +132,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // agent-scope atomic).  A reader observes the flag, passes a barrier, and only
 // then issues its sc1 aggregate loads.
 constexpr int CPOL_SC1 = 16;  // cache-policy bit of buffer instructions: device scope (memory)
+constexpr int CPOL_NT = 2;    // cache-policy bit: non-temporal (streamed through the caches)
 
 template <int CPOL>
 __device__ __forceinline__ void st_buf(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4v x) {
@@ -172,7 +176,8 @@ __device__ __forceinline__ void store_z_pairs(uint32_t* zh, uint32_t* zl, float 
 //      [TILE_B, 2 TILE_B).
 struct CpLds {
   uint8_t reg[SEGC][REGION_B];
-  float zloc[SEGC][FD];        // z of each chunk (then not needed)
+  float zloc[SEGC][FD];        // z of each chunk
+  float vsum[SEGC][FD];        // sum_t V_t of each chunk: the ones^T V part of its state, by column b
   uint32_t zh[SEGC][FD / 2];   // z_pre of each chunk as bf16 (high, low) pairs
   uint32_t zl[SEGC][FD / 2];
   bf16 zero[FD];               // zeros: the rows of the z operand other than 0 and 16
@@ -262,6 +267,18 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) vt[nb][kt] = ld_tr(tV, 16 * kt, 32 * nb, lane);
+    // column sums of V (b = 32 nb + r): the scan adds them to every row a of
+    // the chunk's state (phi(K) = relu(K) + 1)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float cs = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) cs = dot2(pair(vt[nb][kt], p), ONE2, cs);
+      cs += __shfl_xor(cs, 32);
+      if (h == 0) L.vsum[w][32 * nb + r] = cs;
+    }
 
     // P^T blocks (key block jb, query block ib), jb <= ib:
     //   P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
@@ -295,7 +312,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       den[ib] = dacc[0];
     }
 
-    // dS = relu(K)^T V + ones^T V, block (ab, bb): rows a, columns b; written
+    // dS = relu(K)^T V (+ ones^T V in the scan), block (ab, bb): rows a, columns b; written
     // transposed (row b, four contiguous a per q) into the state tile.  The V
     // tile is no longer read (its fragments are in registers), so rows b < 32
     // may overwrite it; rows b >= 32 go over the K tile once its fragments
@@ -323,10 +340,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       for (int ab = 0; ab < 2; ++ab) {
         f32x16 acc = f32x16{};
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          mma(acc, ones, vt[bb][kt]);
-          mma(acc, kt_[ab][kt], vt[bb][kt]);
-        }
+        for (int kt = 0; kt < 4; ++kt) mma(acc, kt_[ab][kt], vt[bb][kt]);
         float* row = state_row(L, w, 32 * bb + r) + 32 * ab + 4 * h;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -351,10 +365,11 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       const float* src = state_row(L, c, sb) + sa;
       const f32x4v x0 = *reinterpret_cast<const f32x4v*>(src);
       const f32x4v x1 = *reinterpret_cast<const f32x4v*>(src + 4);
+      const float cs = L.vsum[c][sb];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pre[c][e] = run[e];
-        run[e] += e < 4 ? x0[e] : x1[e - 4];
+        run[e] += (e < 4 ? x0[e] : x1[e - 4]) + cs;
       }
       if (w == 0) {
         zpre[c] = zrun;
@@ -464,7 +479,9 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       inv[ib] = __builtin_amdgcn_rcpf(__shfl(den[ib] + zacc[0] + zacc[8], r));  // from the lane with h == 0
     }
     // the output rows go through LDS so that global stores cover whole
-    // 128-byte rows, 16 bytes per lane
+    // 128-byte rows, 16 bytes per lane; the stores are non-temporal, so that
+    // they do not sit in L2 as dirty lines to be written back when the
+    // kernel ends
     bf16* tO = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -482,7 +499,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
-                                             ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, 0);
+                                             ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, CPOL_NT);
   }
 }
 
