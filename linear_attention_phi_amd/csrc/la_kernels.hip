@@ -42,19 +42,21 @@ using namespace la_dev;
 template <typename T, int DP, int LQ>
 __device__ __forceinline__ void copy_rows_out(const T* tile, int nrows, int d, bool vec, T* base,
                                               const int* gidx, int64_t row0, int tid) {
+  // non-temporal stores: the output is not read again here, and dirty L2
+  // lines would otherwise be written back when the kernel ends
   if (vec) {
     constexpr int PPR = DP / 4;
-    using V4 = typename std::conditional<sizeof(T) == 2, uint2, uint4>::type;
+    typedef uint32_t U __attribute__((ext_vector_type(sizeof(T))));  // 4 elements
     for (int idx = tid; idx < nrows * PPR; idx += NT) {
       const int r = idx / PPR, col = 4 * (idx % PPR);
       const int64_t g = gidx ? (int64_t)gidx[r] : row0 + r;
-      *reinterpret_cast<V4*>(base + g * d + col) = *reinterpret_cast<const V4*>(tile + r * LQ + col);
+      __builtin_nontemporal_store(*reinterpret_cast<const U*>(tile + r * LQ + col), reinterpret_cast<U*>(base + g * d + col));
     }
   } else {
     for (int idx = tid; idx < nrows * d; idx += NT) {
       const int r = idx / d, col = idx % d;
       const int64_t g = gidx ? (int64_t)gidx[r] : row0 + r;
-      base[g * d + col] = tile[r * LQ + col];
+      __builtin_nontemporal_store(tile[r * LQ + col], base + g * d + col);
     }
   }
 }
