@@ -280,10 +280,12 @@ def test_decode_B128_Hq32_Hkv8_d128_256_steps(gpu):
 
 # ------------------------------------------ the single-launch causal kernel
 # bf16, d = 64, chunk 64, one query head per key/value head takes the
-# single-launch path (segments of 4 chunks that wait on the aggregates of
+# single-launch path (segments of 8 chunks that wait on the aggregates of
 # earlier segments); these cases cover ragged tails, one to many segments,
-# and a deep wait chain.
-SINGLE = [(1, 1, 1), (1, 1, 63), (1, 2, 64), (2, 1, 65), (1, 3, 257), (2, 4, 1000), (1, 2, 20000)]
+# and a deep wait chain (B3 H8 n4500: more than four earlier segments, whose
+# aggregates are read in two batches).
+SINGLE = [(1, 1, 1), (1, 1, 63), (1, 2, 64), (2, 1, 65), (1, 3, 257), (2, 4, 1000), (1, 2, 20000),
+          (1, 8, 1500), (3, 8, 4500)]
 
 
 @pytest.mark.parametrize("case", SINGLE, ids=lambda c: "B%d_H%d_n%d" % c)
