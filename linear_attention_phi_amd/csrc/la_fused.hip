@@ -210,12 +210,9 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   bf16* tV = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
   if (tid < FD) L.zero[tid] = (bf16)0.0f;
 
-  Frag<bf16> ones, e0;  // all ones; ones in row 0 only (P row sums on MFMA)
+  Frag<bf16> ones;  // all ones
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    ones.v[e] = (bf16)1.0f;
-    e0.v[e] = (bf16)(r == 0 ? 1.0f : 0.0f);
-  }
+  for (int e = 0; e < 8; ++e) ones.v[e] = (bf16)1.0f;
 
   // ------------------------------------------------------------------ A
   // Loads: K and V as 16-byte row pieces (rows lane / 8 + 8 u), Q directly
@@ -223,7 +220,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   // Rows past the sequence end read as zero.
   f32x16 O[2][2];     // numerator blocks (feature block nb, query block ib): rows b, column i
   Frag<bf16> qf[2][4];  // phi(Q) fragments (query block ib, feature block kb)
-  float den[2] = {0.0f, 0.0f};  // chunk-local normaliser of query 32 ib + r (lanes with h == 0)
+  float den[2] = {0.0f, 0.0f};  // chunk-local normaliser of query 32 ib + r
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -249,24 +246,29 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(tV + (prow + 8 * u) * RS + pcol) = vr[u];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        u32x4 x = qr[ib][kb];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
-        qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
-      }
     wave_lds_sync();
 
-    // V^T fragments (feature block nb, token block kt): A operand of V^T P^T,
-    // B operand of relu(K)^T V
-    Frag<bf16> vt[2][4];
+    // Fragments: V^T (feature block nb, token block kt): A operand of V^T P^T
+    // and B operand of relu(K)^T V; relu(K)^T (feature block ab, token block
+    // kt): A operand of relu(K)^T V; relu(K) token-major (key block jb,
+    // feature block kb): A operand of P^T.  The chunk's state comes first: it
+    // needs K and V only, so it runs while Q may still be arriving; the state
+    // tile then overwrites the K and V tiles (rows b < 32 the V tile, rows
+    // b >= 32 the K tile).
+    Frag<bf16> vt[2][4], kt_[2][4], kf[2][4];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) vt[nb][kt] = ld_tr(tV, 16 * kt, 32 * nb, lane);
+#pragma unroll
+    for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) kt_[ab][kt] = ld_tr(tK, 16 * kt, 32 * ab, lane);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) kf[jb][kb] = ld16(tK + (32 * jb + r) * RS + 16 * kb + 8 * h);
+    wave_lds_sync();
     // column sums of V (b = 32 nb + r): the scan adds them to every row a of
     // the chunk's state (phi(K) = relu(K) + 1)
 #pragma unroll
@@ -279,49 +281,6 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       cs += __shfl_xor(cs, 32);
       if (h == 0) L.vsum[w][32 * nb + r] = cs;
     }
-
-    // P^T blocks (key block jb, query block ib), jb <= ib:
-    //   P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
-    // (the second term from an all-ones A operand); only the diagonal block
-    // is masked: element e holds key row 8 (e >> 2) + 4 h + (e & 3) of query r.
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(sacc, ones, qf[ib][kb]);
-      f32x16 dacc = f32x16{};
-#pragma unroll
-      for (int jb = 0; jb <= ib; ++jb) {
-        f32x16 pacc = sacc;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(pacc, ld16(tK + (32 * jb + r) * RS + 16 * kb + 8 * h), qf[ib][kb]);
-        if (jb == ib) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) pacc[e] = (8 * (e >> 2) + 4 * h + (e & 3) <= r) ? pacc[e] : 0.0f;
-        }
-        const Frag<bf16> p0 = acc_frag(pacc, 0), p1 = acc_frag(pacc, 1);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          mma(O[nb][ib], vt[nb][2 * jb], p0);
-          mma(O[nb][ib], vt[nb][2 * jb + 1], p1);
-        }
-        // den_i = sum_j P_ij: row 0 of e0 . P^T
-        mma(dacc, e0, p0);
-        mma(dacc, e0, p1);
-      }
-      den[ib] = dacc[0];
-    }
-
-    // dS = relu(K)^T V (+ ones^T V in the scan), block (ab, bb): rows a, columns b; written
-    // transposed (row b, four contiguous a per q) into the state tile.  The V
-    // tile is no longer read (its fragments are in registers), so rows b < 32
-    // may overwrite it; rows b >= 32 go over the K tile once its fragments
-    // are loaded.
-    Frag<bf16> kt_[2][4];
-#pragma unroll
-    for (int ab = 0; ab < 2; ++ab)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) kt_[ab][kt] = ld_tr(tK, 16 * kt, 32 * ab, lane);
     // z of the chunk: sum_t relu(K_t)[a] + nv, for a = 32 ab + r
 #pragma unroll
     for (int ab = 0; ab < 2; ++ab) {
@@ -333,7 +292,9 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       zp += __shfl_xor(zp, 32);
       if (h == 0) L.zloc[w][32 * ab + r] = zp + (float)nv;
     }
-    wave_lds_sync();
+    // dS = relu(K)^T V (+ ones^T V in the scan), block (ab, bb): rows a,
+    // columns b; written transposed (row b, four contiguous a per q) into
+    // the state tile
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
@@ -346,6 +307,48 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
         for (int q = 0; q < 4; ++q)
           *reinterpret_cast<f32x4v*>(row + 8 * q) = f32x4v{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
       }
+    }
+
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4 x = qr[ib][kb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
+        qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
+      }
+    // P^T blocks (key block jb, query block ib), jb <= ib:
+    //   P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
+    // (the second term from an all-ones A operand); only the diagonal block
+    // is masked: element e holds key row 8 (e >> 2) + 4 h + (e & 3) of query r.
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(sacc, ones, qf[ib][kb]);
+      float ds = 0.0f;
+#pragma unroll
+      for (int jb = 0; jb <= ib; ++jb) {
+        f32x16 pacc = sacc;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(pacc, kf[jb][kb], qf[ib][kb]);
+        if (jb == ib) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) pacc[e] = (8 * (e >> 2) + 4 * h + (e & 3) <= r) ? pacc[e] : 0.0f;
+        }
+        const Frag<bf16> p0 = acc_frag(pacc, 0), p1 = acc_frag(pacc, 1);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          mma(O[nb][ib], vt[nb][2 * jb], p0);
+          mma(O[nb][ib], vt[nb][2 * jb + 1], p1);
+        }
+        // den_i = sum_j P_ij over the rounded weights the numerator uses: this
+        // lane's 16 rows j of column i
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ds = dot2(pair(p1, j), ONE2, dot2(pair(p0, j), ONE2, ds));
+      }
+      den[ib] = ds + __shfl_xor(ds, 32);
     }
   }
   __syncthreads();
