@@ -352,9 +352,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--workload", default="causal", help="one of: " + ", ".join(WORKLOADS) + ", or all")
-    ap.add_argument("--copy-calibration", action="store_true",
+    ap.add_argument("--copy-calibration", nargs="?", const="vector", choices=["vector", "blit"], default=None,
                     help="instead of the benchmark, run plain device-to-device copies of 64 MiB "
-                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
+                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters): "
+                         "'vector' (default) an elementwise copy, 'blit' the runtime's copy kernel")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -377,14 +378,21 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         # 10 rotating 64 MiB sources (640 MiB > the 256 MiB MALL); each copy
-        # moves 64 MiB in and 64 MiB out
-        src = [torch.full((64 << 20,), i, dtype=torch.uint8, device=dev) for i in range(10)]
+        # moves 64 MiB in and 64 MiB out.  "blit": the runtime's copy kernel;
+        # "vector": an elementwise copy (x * 1) whose lanes load and store 16
+        # contiguous bytes each over whole rows, the access pattern of the
+        # kernels measured here (the counters' request-size accounting
+        # depends on the pattern)
+        src = [torch.full((16 << 20,), float(i), dtype=torch.float32, device=dev) for i in range(10)]
         dst = torch.empty_like(src[0])
         n = args.warmup + (args.steps or 200)
         for i in range(n):
-            dst.copy_(src[i % 10])
+            if args.copy_calibration == "blit":
+                dst.copy_(src[i % 10])
+            else:
+                torch.mul(src[i % 10], 1.0, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_each_way": 64 << 20, "copies": n}))
+        print(json.dumps({"copy_calibration": args.copy_calibration, "bytes_each_way": 64 << 20, "copies": n}))
         return
     for nm in names:
         run(nm, args)
