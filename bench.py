@@ -103,7 +103,7 @@ def algorithmic_flops(w):
 # together with a hash of the kernel's sources; reported only while the
 # sources still hash the same (null once the kernel has changed).
 COUNTER_FILE = os.path.join(ROOT, "profiles", "k_causal_fused_causal_bf16_B8H8n2048d64_counters.md")
-COUNTER_SOURCES = ["la_fused.hip", "la_device.h", "la_internal.h"]
+COUNTER_SOURCES = ["la_fused.hip", "la_bf16.h", "la_device.h", "la_internal.h"]
 
 
 def kernel_source_hash(files=COUNTER_SOURCES):

@@ -82,6 +82,8 @@ SMALL = [
     (1, 1, 1, 300, 100, 128),
     (1, 4, 4, 129, 64, 128),
     (2, 8, 2, 200, 31, 32),
+    (2, 4, 2, 1000, 64, 64),   # bf16 non-causal: state partials of several segments, GQA
+    (1, 2, 1, 4500, 64, 32),   # 18 segments: the reduce's batches of eight and a remainder
 ]
 
 
