@@ -9,10 +9,10 @@
 // of a workgroup's loads in flight from its start:
 //
 //  A  a workgroup owns a segment of eight chunks; wave w owns chunk w.  It
-//     loads the chunk's Q, K and V at once, and forms, in registers, the
-//     chunk-local numerator tril(phi(Q) phi(K)^T) V and denominator, and the
-//     chunk's state dS = relu(K)^T V (fp32, written to LDS), the column sums
-//     of V (its ones^T V part) and z;
+//     loads the chunk's Q, K and V at once and forms the chunk's state
+//     dS = relu(K)^T V + ones^T V (fp32, written to LDS) and z (these need K
+//     and V only), then, in registers, the chunk-local numerator
+//     tril(phi(Q) phi(K)^T) V and denominator;
 //  B  the eight waves scan the states of the segment (each wave a slice of
 //     rows, over the eight chunks): exclusive prefixes S_loc(c), z_loc(c) and
 //     the segment aggregate, which is published; the aggregates of all
@@ -75,7 +75,6 @@ struct FusedArgs {
 struct CpLds {
   uint8_t reg[SEGC][REGION_B];
   float zloc[SEGC][FD];        // z of each chunk
-  float vsum[SEGC][FD];        // sum_t V_t of each chunk: the ones^T V part of its state, by column b
   uint32_t zh[SEGC][FD / 2];   // z_pre of each chunk as bf16 (high, low) pairs
   uint32_t zl[SEGC][FD / 2];
   bf16 zero[FD];               // zeros: the rows of the z operand other than 0 and 16
@@ -167,17 +166,17 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) kf[jb][kb] = ld16(tK + (32 * jb + r) * RS + 16 * kb + 8 * h);
     wave_lds_sync();
-    // column sums of V (b = 32 nb + r): the scan adds them to every row a of
-    // the chunk's state (phi(K) = relu(K) + 1)
+    // column sums of V (b = 32 nb + r): the ones^T V part of the chunk's
+    // state (phi(K) = relu(K) + 1), added to every row a below
+    float cs[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float cs = 0.0f;
+      cs[nb] = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) cs = dot2(pair(vt[nb][kt], p), ONE2, cs);
-      cs += __shfl_xor(cs, 32);
-      if (h == 0) L.vsum[w][32 * nb + r] = cs;
+        for (int p = 0; p < 4; ++p) cs[nb] = dot2(pair(vt[nb][kt], p), ONE2, cs[nb]);
+      cs[nb] += __shfl_xor(cs[nb], 32);
     }
     // z of the chunk: sum_t relu(K_t)[a] + nv, for a = 32 ab + r
 #pragma unroll
@@ -190,9 +189,8 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       zp += __shfl_xor(zp, 32);
       if (h == 0) L.zloc[w][32 * ab + r] = zp + (float)nv;
     }
-    // dS = relu(K)^T V (+ ones^T V in the scan), block (ab, bb): rows a,
-    // columns b; written transposed (row b, four contiguous a per q) into
-    // the state tile
+    // dS = relu(K)^T V + ones^T V, block (ab, bb): rows a, columns b; written
+    // transposed (row b, four contiguous a per q) into the state tile
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
@@ -201,9 +199,11 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) mma(acc, kt_[ab][kt], vt[bb][kt]);
         float* row = state_row(L, w, 32 * bb + r) + 32 * ab + 4 * h;
+        const float c = cs[bb];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4v*>(row + 8 * q) = f32x4v{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+          *reinterpret_cast<f32x4v*>(row + 8 * q) =
+              f32x4v{acc[4 * q] + c, acc[4 * q + 1] + c, acc[4 * q + 2] + c, acc[4 * q + 3] + c};
       }
     }
 
@@ -266,11 +266,10 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       const float* src = state_row(L, c, sb) + sa;
       const f32x4v x0 = *reinterpret_cast<const f32x4v*>(src);
       const f32x4v x1 = *reinterpret_cast<const f32x4v*>(src + 4);
-      const float cs = L.vsum[c][sb];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pre[c][e] = run[e];
-        run[e] += (e < 4 ? x0[e] : x1[e - 4]) + cs;
+        run[e] += e < 4 ? x0[e] : x1[e - 4];
       }
       if (w == 0) {
         zpre[c] = zrun;
