@@ -84,6 +84,7 @@ SMALL = [
     (2, 8, 2, 200, 31, 32),
     (2, 4, 2, 1000, 64, 64),   # bf16 non-causal: state partials of several segments, GQA
     (1, 2, 1, 4500, 64, 32),   # 18 segments: the reduce's batches of eight and a remainder
+    (1, 1, 1, 1, 64, 64),      # one token at d = 64
 ]
 
 
