@@ -28,6 +28,7 @@
 
 #include <type_traits>
 
+#include "la_bf16.h"
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -468,6 +469,171 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
   }
 }
 
+// ----------------------------------------------------------------- k_out_gqa
+// Causal output for bf16 with d = 128, chunk 32 and R = 2 or 4 query heads
+// per key/value head: the R query heads of a chunk are worked on at once
+// (8 waves; head g = w / (8 / R), each of its 8 / R waves 128 R / 8 of the
+// output features), so that a chunk costs two barriers whatever R is,
+// against four per query head in k_out.  Each wave forms its
+// head's score block P^T = phi(K) phi(Q)^T itself, in registers (its
+// accumulator is the B operand of V^T P^T; la_device.h), and the row sums of
+// the rounded P for the normaliser.  The state is carried as in k_out: two of
+// the 16 32 x 32 state blocks per wave in MFMA accumulators, relu(K)^T V on
+// top of the segment's exclusive prefix, plus 1 (x) (sum of V).
+template <int R>
+__global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                 const bf16* __restrict__ v, bf16* __restrict__ out, int64_t n,
+                                                 int64_t nchunks, int64_t G, int64_t nseg,
+                                                 const float* __restrict__ ws) {
+  constexpr int DP = 128, C = 32;
+  constexpr int LQ = DP + PAD;  // row stride of sK, sQ, sO, sST
+  constexpr int LC = C + PAD;   // row stride of sKT, sVT
+  constexpr int NPH = 8 / R;    // waves per query head
+  constexpr int NBW = 4 / NPH;  // 32-wide output feature blocks per wave
+  static_assert(R == 2 || R == 4, "two or four query heads per key/value head");
+  __shared__ __attribute__((aligned(16))) bf16 sK[C * LQ];       // phi(K), token-major
+  __shared__ __attribute__((aligned(16))) bf16 sKT[DP * LC];     // relu(K), feature-major
+  __shared__ __attribute__((aligned(16))) bf16 sVT[DP * LC];     // V, feature-major
+  __shared__ __attribute__((aligned(16))) bf16 sST[DP * LQ];     // S^T in bf16
+  __shared__ __attribute__((aligned(16))) bf16 sQ[R][C * LQ];    // phi(Q) of each query head
+  __shared__ __attribute__((aligned(16))) bf16 sO[R][C * LQ];    // outputs on their way out
+  __shared__ __attribute__((aligned(16))) bf16 szh[DP];          // z as bf16 high part,
+  __shared__ __attribute__((aligned(16))) bf16 szl[DP];          // the remainder,
+  __shared__ __attribute__((aligned(16))) bf16 szero[DP];        // and zeros: the z operand's rows
+  __shared__ float svc[DP];  // sum of V over the chunks done so far
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
+  const int half = tid >> 8, ht = tid & 255;  // the two 256-thread halves share the tile loads
+  const int g = w / NPH, hf = w % NPH;
+  const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const bf16* kb = k + bh * n * DP;
+  const bf16* vb = v + bh * n * DP;
+
+  // state blocks e = w and w + 8: (row block ma, column block nb) = (e / 4, e % 4)
+  f32x16 accS[2];
+  {
+    const float* src = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) ld_state_block<DP>(accS[s], src, (w + 8 * s) / 4, (w + 8 * s) % 4, lane);
+  }
+  float zrun = 0.0f, vrun = 0.0f;
+  if (tid < DP) {
+    zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + tid];
+    svc[tid] = 0.0f;
+    szero[tid] = (bf16)0.0f;
+  }
+
+  // tiles of a chunk: K, V and the R query tiles; tile t is loaded by half t % 2
+  constexpr int NTILE = 2 + R;
+  constexpr int PERH = (NTILE + 1) / 2;  // tiles per half
+  TileRaw<bf16, DP, C> raw[PERH];
+  const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  auto tile_src = [&](int t) -> const bf16* {
+    if (t == 0) return kb;
+    if (t == 1) return vb;
+    return q + (bh * R + (t - 2)) * n * DP;
+  };
+  auto fetch = [&](int64_t c) {
+    const int64_t tc = c * C;
+    const int nvc = (int)((n - tc) < C ? (n - tc) : C);
+#pragma unroll
+    for (int u = 0; u < PERH; ++u) {
+      const int t = 2 * u + half;
+      if (t < NTILE) tile_fetch<bf16, DP, C>(raw[u], tile_src(t), tc, nullptr, nvc, ht);
+    }
+  };
+  if (c0 < c1) fetch(c0);
+  __syncthreads();
+
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)((n - t0) < C ? (n - t0) : C);
+#pragma unroll
+    for (int u = 0; u < PERH; ++u) {
+      const int t = 2 * u + half;
+      if (t == 0) tile_store<bf16, DP, C, XF_PHI, XF_RELU>(raw[u], nv, sK, sKT, ht);
+      else if (t == 1) tile_store<bf16, DP, C, XF_NONE, XF_ID>(raw[u], nv, nullptr, sVT, ht);
+      else if (t < NTILE) tile_store<bf16, DP, C, XF_PHI, XF_NONE>(raw[u], nv, sQ[t - 2], nullptr, ht);
+    }
+    if (c + 1 < c1) fetch(c + 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int e = w + 8 * s, ma = e / 4, nb = e % 4;
+      f32x16 cur = accS[s];
+      add_col(cur, svc[nb * 32 + r], ma, DP, lane);
+      st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
+    }
+    if (tid < DP) {
+      const bf16 zh = (bf16)zrun;
+      szh[tid] = zh;
+      szl[tid] = (bf16)(zrun - (float)zh);
+    }
+    __syncthreads();
+
+    // ---- head g: P^T (keys j, queries i), masked; its row sums; phi(Q) . z
+    const bf16* qg = sQ[g];
+    f32x16 pacc = f32x16{};
+    gemm_acc<bf16, DP / 16>(pacc, sK, LQ, qg, LQ, lane);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pacc[e] = (8 * (e >> 2) + 4 * h + (e & 3) <= r) ? pacc[e] : 0.0f;
+    const Frag<bf16> p0 = la_bf16::acc_frag(pacc, 0), p1 = la_bf16::acc_frag(pacc, 1);
+    float ds = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ds = la_bf16::dot2(la_bf16::pair(p1, j), la_bf16::ONE2, la_bf16::dot2(la_bf16::pair(p0, j), la_bf16::ONE2, ds));
+    ds += __shfl_xor(ds, 32);
+    f32x16 zacc = f32x16{};
+    {
+      const bf16* zrow = (r == 0) ? szh : (r == 16) ? szl : szero;
+      gemm_acc<bf16, DP / 16>(zacc, zrow - r * LQ, LQ, qg, LQ, lane);
+    }
+    const float inv = 1.0f / __shfl(ds + zacc[0] + zacc[8], r);  // from the lane with h == 0
+    // ---- this wave's output blocks: out^T[b][i] = S^T phi(Q)^T + V^T P^T
+#pragma unroll
+    for (int u = 0; u < NBW; ++u) {
+      const int nb = hf * NBW + u;
+      f32x16 o = f32x16{};
+      gemm_acc<bf16, DP / 16>(o, sST + nb * 32 * LQ, LQ, qg, LQ, lane);
+      Frag<bf16> va;
+      ld_frag(va, sVT + (nb * 32 + r) * LC + 4 * h);
+      mma(o, va, p0);
+      ld_frag(va, sVT + (nb * 32 + r) * LC + 16 + 4 * h);
+      mma(o, va, p1);
+      uint2* dst = reinterpret_cast<uint2*>(sO[g] + r * LQ + nb * 32 + 4 * h);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        dst[2 * qq] = make_uint2(la_bf16::pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv),
+                                 la_bf16::pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+    }
+
+    // ---- S += relu(K_c)^T V_c (two blocks per wave); z and the sum of V
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int e = w + 8 * s, ma = e / 4, nb = e % 4;
+      gemm_acc<bf16, C / 16>(accS[s], sKT + ma * 32 * LC, LC, sVT + nb * 32 * LC, LC, lane);
+    }
+    if (tid < DP) {
+      zrun += row_sum<bf16, C>(sKT, tid) + (float)nv;
+      vrun += row_sum<bf16, C>(sVT, tid);
+      svc[tid] = vrun;  // read at the next chunk's start (this chunk read it before the barrier above)
+    }
+    __syncthreads();
+
+    // ---- the R output tiles: whole 256-byte rows, non-temporal stores
+    constexpr int PIECES = C * (DP / 8);  // 16-byte pieces per tile
+#pragma unroll
+    for (int gg = 0; gg < R; ++gg) {
+#pragma unroll
+      for (int pp = tid; pp < PIECES; pp += 512) {
+        const int row = pp / (DP / 8), col = 8 * (pp % (DP / 8));
+        if (row < nv)
+          __builtin_nontemporal_store(*reinterpret_cast<const la_bf16::u32x4*>(sO[gg] + row * LQ + col),
+                                      reinterpret_cast<la_bf16::u32x4*>(out + ((bh * R + gg) * n + t0 + row) * DP + col));
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------- k_out_nc
 // Non-causal output: out_i = phi(Q_i) S / (phi(Q_i) . z) with the total state
 // (slot nseg of the head).  One workgroup per (head, run of G chunks of
@@ -820,6 +986,16 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   const int64_t E = slot_elems(DP);
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final, a.z_final);
   if (q && out) {
+    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
+      if (form == CAUSAL && vec && (R == 2 || R == 4)) {
+        const bf16* qq = reinterpret_cast<const bf16*>(q);
+        if (R == 2)
+          k_out_gqa<2><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, p.G, p.nseg, states);
+        else
+          k_out_gqa<4><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, p.G, p.nseg, states);
+        return (int)hipGetLastError();
+      }
+    }
     if (form == CAUSAL)
       k_out<T, DP, C, CAUSAL><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
     else

@@ -85,6 +85,8 @@ SMALL = [
     (2, 4, 2, 1000, 64, 64),   # bf16 non-causal: state partials of several segments, GQA
     (1, 2, 1, 4500, 64, 32),   # 18 segments: the reduce's batches of eight and a remainder
     (1, 1, 1, 1, 64, 64),      # one token at d = 64
+    (1, 4, 1, 300, 128, 32),   # bf16 causal: four query heads per chunk at once, ragged tail
+    (2, 4, 2, 97, 128, 0),     # ... two query heads (default chunk 32)
 ]
 
 
@@ -300,6 +302,17 @@ def test_causal_single_launch_path(gpu, case):
     check(host(out), ref, li.BF16, f"single-launch causal B{B} H{H} n{n}")
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-5 * np.abs(Sr).max())
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
+def test_gqa_output_kernel_matches_general_path(gpu):
+    """bf16, d = 128, GQA: chunk 32 (query heads of a chunk at once) and chunk
+    64 (the general output kernel) both match the oracle."""
+    q, k, v, _ = li.qkv(1, 8, 2, 1500, 128, li.BF16, seed=12, scaled=True)
+    ref = oracle.causal(q, k, v)
+    a = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=32))
+    b = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64))
+    check(a, ref, li.BF16, "GQA chunk 32")
+    check(b, ref, li.BF16, "GQA chunk 64")
 
 
 def test_single_launch_matches_three_launch_path(gpu):
