@@ -523,24 +523,25 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
     szero[tid] = (bf16)0.0f;
   }
 
-  // tiles of a chunk: K, V and the R query tiles; tile t is loaded by half t % 2
-  constexpr int NTILE = 2 + R;
-  constexpr int PERH = (NTILE + 1) / 2;  // tiles per half
-  TileRaw<bf16, DP, C> raw[PERH];
+  // Tiles of a chunk: half 0 loads K, half 1 V, as two adjacent rows x 8
+  // features per thread (so that the feature-major copies are written two
+  // tokens to a 4-byte word); query tile g goes to half g % 2.
+  constexpr int QPH = R / 2;  // query tiles per half
+  TileRaw<bf16, DP, C> raw[QPH];
+  la_bf16::u32x4 kv2[2];
+  const int pr0 = 2 * (ht >> 4), pc0 = 8 * (ht & 15);
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
-  auto tile_src = [&](int t) -> const bf16* {
-    if (t == 0) return kb;
-    if (t == 1) return vb;
-    return q + (bh * R + (t - 2)) * n * DP;
-  };
   auto fetch = [&](int64_t c) {
     const int64_t tc = c * C;
     const int nvc = (int)((n - tc) < C ? (n - tc) : C);
+    const bf16* src = half == 0 ? kb : vb;
 #pragma unroll
-    for (int u = 0; u < PERH; ++u) {
-      const int t = 2 * u + half;
-      if (t < NTILE) tile_fetch<bf16, DP, C>(raw[u], tile_src(t), tc, nullptr, nvc, ht);
-    }
+    for (int rr = 0; rr < 2; ++rr)
+      kv2[rr] = pr0 + rr < nvc ? *reinterpret_cast<const la_bf16::u32x4*>(src + (tc + pr0 + rr) * DP + pc0)
+                               : la_bf16::u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < QPH; ++u)
+      tile_fetch<bf16, DP, C>(raw[u], q + (bh * R + 2 * u + half) * n * DP, tc, nullptr, nvc, ht);
   };
   if (c0 < c1) fetch(c0);
   __syncthreads();
@@ -548,13 +549,34 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
+    {
+      // K: phi(K) token-major (zero past the sequence end), relu(K) feature-
+      // major; V: feature-major
+      uint32_t x[2][4];
 #pragma unroll
-    for (int u = 0; u < PERH; ++u) {
-      const int t = 2 * u + half;
-      if (t == 0) tile_store<bf16, DP, C, XF_PHI, XF_RELU>(raw[u], nv, sK, sKT, ht);
-      else if (t == 1) tile_store<bf16, DP, C, XF_NONE, XF_ID>(raw[u], nv, nullptr, sVT, ht);
-      else if (t < NTILE) tile_store<bf16, DP, C, XF_PHI, XF_NONE>(raw[u], nv, sQ[t - 2], nullptr, ht);
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[rr][j] = half == 0 ? la_bf16::relu2(kv2[rr][j]) : kv2[rr][j];
+      bf16* fm = half == 0 ? sKT : sVT;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint32_t*>(fm + (pc0 + 2 * j) * LC + pr0) = (x[0][j] & 0xFFFFu) | (x[1][j] << 16);
+        *reinterpret_cast<uint32_t*>(fm + (pc0 + 2 * j + 1) * LC + pr0) = (x[0][j] >> 16) | (x[1][j] & 0xFFFF0000u);
+      }
+      if (half == 0) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          uint32_t y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = pr0 + rr < nv ? la_bf16::phi2(kv2[rr][j]) : 0u;
+          uint2* dst = reinterpret_cast<uint2*>(sK + (pr0 + rr) * LQ + pc0);
+          dst[0] = make_uint2(y[0], y[1]);
+          dst[1] = make_uint2(y[2], y[3]);
+        }
+      }
     }
+#pragma unroll
+    for (int u = 0; u < QPH; ++u) tile_store<bf16, DP, C, XF_PHI, XF_NONE>(raw[u], nv, sQ[2 * u + half], nullptr, ht);
     if (c + 1 < c1) fetch(c + 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
