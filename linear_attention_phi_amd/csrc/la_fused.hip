@@ -107,10 +107,6 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   bf16* tV = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
   if (tid < FD) L.zero[tid] = (bf16)0.0f;
 
-  Frag<bf16> ones;  // all ones
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones.v[e] = (bf16)1.0f;
-
   // ------------------------------------------------------------------ A
   // Loads: K and V as 16-byte row pieces (rows lane / 8 + 8 u), Q directly
   // as operand fragments (query row 32 ib + r, features 16 kb + 8 h ..).
@@ -218,17 +214,24 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       }
     // P^T blocks (key block jb, query block ib), jb <= ib:
     //   P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
-    // (the second term from an all-ones A operand); only the diagonal block
-    // is masked: element e holds key row 8 (e >> 2) + 4 h + (e & 3) of query r.
+    // (the second term, the same for every key, is the accumulators' start
+    // value: this lane's column is query r, whose features the lane pair
+    // (h = 0, 1) holds between them); only the diagonal block is masked:
+    // element e holds key row 8 (e >> 2) + 4 h + (e & 3) of query r.
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
-      f32x16 sacc = f32x16{};
+      float qs = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(sacc, ones, qf[ib][kb]);
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) qs = dot2(pair(qf[ib][kb], p), ONE2, qs);
+      qs += __shfl_xor(qs, 32);
       float ds = 0.0f;
 #pragma unroll
       for (int jb = 0; jb <= ib; ++jb) {
-        f32x16 pacc = sacc;
+        f32x16 pacc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pacc[e] = qs;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) mma(pacc, kf[jb][kb], qf[ib][kb]);
         if (jb == ib) {
