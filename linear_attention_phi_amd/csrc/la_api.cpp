@@ -122,6 +122,10 @@ size_t required_ws(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, in
     const size_t f = forward_bf16_ws_bytes(B * Hkv, forward_bf16_nseg(n));
     if (f > bytes) bytes = f;
   }
+  if (op == LA_OP_FORWARD && forward_f32_applies(n, d, (int)dt)) {
+    const size_t f = forward_f32_ws_bytes(B * Hkv, forward_f32_nseg(n));
+    if (f > bytes) bytes = f;
+  }
   return bytes;
 }
 
@@ -197,6 +201,10 @@ la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int
   if (forward_bf16_applies(n, d, (int)dtype)) {
     if (B * Hq * forward_bf16_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_bf16(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
+  }
+  if (forward_f32_applies(n, d, (int)dtype)) {
+    if (B * Hq * forward_f32_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
+    return launch_forward_f32(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   return launch_forward(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }

@@ -67,11 +67,22 @@ int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch);
 // Non-causal path for bf16, d = 64 (la_forward_bf16.hip): state partials per
 // segment of kFwdSegChunks chunks, a reduce, then the output pass.
 constexpr int kFwdSegChunks = 4;
-constexpr int64_t kFwdMaxN = (int64_t)1 << 24;  // one head's bytes fit a 32-bit buffer offset
+// n bound: one head's rows, padded to a whole segment, stay below 2^31 bytes
+// (the range of a buffer resource's record count and offsets).
+constexpr int64_t kFwdMaxN = (int64_t)1 << 23;
 bool forward_bf16_applies(int64_t n, int64_t d, int dtype);
 int64_t forward_bf16_nseg(int64_t n);
 size_t forward_bf16_ws_bytes(int64_t NKV, int64_t nseg);
 int launch_forward_bf16(const Fwd& a);
+
+// Non-causal path for fp32, d = 64 (la_forward_f32.hip): state partials per
+// segment of kFwd32SegTokens keys, a reduce, then the output pass.
+constexpr int kFwd32SegTokens = 256;
+constexpr int64_t kFwd32MaxN = (int64_t)1 << 22;  // as kFwdMaxN, for 4-byte elements
+bool forward_f32_applies(int64_t n, int64_t d, int dtype);
+int64_t forward_f32_nseg(int64_t n);
+size_t forward_f32_ws_bytes(int64_t NKV, int64_t nseg);
+int launch_forward_f32(const Fwd& a);
 
 int launch_decode(const void* q, const void* k, const void* v, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t d, int dtype, float* S,
