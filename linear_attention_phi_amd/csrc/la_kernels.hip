@@ -138,6 +138,89 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
   if (tid < DP) dst[DP * DP + tid] = zrun;
 }
 
+// --------------------------------------------------------------- k_state_tr
+// k_state for bf16 with d = 128 and chunk 32 (the causal shape with four or
+// two query heads per key/value head): the K and V tiles stay token-major in
+// LDS (16-byte writes, two buffers, one barrier per chunk), and the operands
+// over the token index come from transposed reads (ds_read_b64_tr_b16), so
+// no feature-major copies are written.  Wave w owns state column block w
+// (all four row blocks): the column sums of V its blocks need and z of rows
+// 32 w .. are dot2 sums over fragments it reads anyway.
+constexpr int STR_RS = 128 + 16;  // tile row stride (bf16): rows 8 dwords apart mod 64 banks
+__global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t n,
+                                                 int64_t nchunks, int64_t G, int64_t nseg, float* __restrict__ ws) {
+  constexpr int DP = 128, C = 32, RS = STR_RS;
+  static_assert(NT == 256 && DP / 32 == NT / 64, "one column block per wave");
+  __shared__ __attribute__((aligned(16))) bf16 sK[2][C * RS];
+  __shared__ __attribute__((aligned(16))) bf16 sV[2][C * RS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 31, h = lane >> 5;
+  const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const bf16* kb = k + bh * n * DP;
+  const bf16* vb = v + bh * n * DP;
+  f32x16 acc[DP / 32];  // row blocks ab of column block w
+#pragma unroll
+  for (int ab = 0; ab < DP / 32; ++ab) acc[ab] = f32x16{};
+  float zrun = 0.0f, vrun = 0.0f;  // z[32 w + r] and sum_t V[t][32 w + r] (both halves)
+  const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+  // piece u of a tile: row (tid + NT u) / 16, eight features from 8 ((tid + NT u) % 16)
+  constexpr int PIECES = C * DP / 8 / NT;
+  uint4 kr[PIECES], vr[PIECES];
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * C;
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pc = tid + NT * u, row = pc >> 4, col = 8 * (pc & 15);
+      const bool ok = t0 + row < n;
+      kr[u] = ok ? *reinterpret_cast<const uint4*>(kb + (t0 + row) * DP + col) : make_uint4(0, 0, 0, 0);
+      vr[u] = ok ? *reinterpret_cast<const uint4*>(vb + (t0 + row) * DP + col) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (c0 < c1) fetch(c0);
+  int buf = 0;
+  for (int64_t c = c0; c < c1; ++c, buf ^= 1) {
+    const int nv = (int)((n - c * C) < C ? (n - c * C) : C);
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pc = tid + NT * u, row = pc >> 4, col = 8 * (pc & 15);
+      const uint4 x = kr[u];
+      *reinterpret_cast<uint4*>(sK[buf] + row * RS + col) =
+          make_uint4(la_bf16::relu2(x.x), la_bf16::relu2(x.y), la_bf16::relu2(x.z), la_bf16::relu2(x.w));
+      *reinterpret_cast<uint4*>(sV[buf] + row * RS + col) = vr[u];
+    }
+    if (c + 1 < c1) fetch(c + 1);
+    // the other buffer was last read before this barrier's predecessor, so
+    // one barrier per chunk suffices
+    __syncthreads();
+    Frag<bf16> vt[C / 16], kz[C / 16];
+#pragma unroll
+    for (int kt = 0; kt < C / 16; ++kt) {
+      vt[kt] = la_bf16::ld_tr<RS>(sV[buf], 16 * kt, 32 * w, lane);
+      kz[kt] = la_bf16::ld_tr<RS>(sK[buf], 16 * kt, 32 * w, lane);
+    }
+#pragma unroll
+    for (int ab = 0; ab < DP / 32; ++ab)
+#pragma unroll
+      for (int kt = 0; kt < C / 16; ++kt) mma(acc[ab], la_bf16::ld_tr<RS>(sK[buf], 16 * kt, 32 * ab, lane), vt[kt]);
+    float zs = 0.0f, vs = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < C / 16; ++kt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        zs = la_bf16::dot2(la_bf16::pair(kz[kt], q), la_bf16::ONE2, zs);
+        vs = la_bf16::dot2(la_bf16::pair(vt[kt], q), la_bf16::ONE2, vs);
+      }
+    zrun += zs + __shfl_xor(zs, 32) + (float)nv;  // phi(K) = relu(K) + 1 over the nv keys
+    vrun += vs + __shfl_xor(vs, 32);
+  }
+  // phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t
+#pragma unroll
+  for (int ab = 0; ab < DP / 32; ++ab) add_col(acc[ab], vrun, ab, DP, lane);
+  float* dst = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
+#pragma unroll
+  for (int ab = 0; ab < DP / 32; ++ab) st_state_block<DP>(dst, acc[ab], ab, w, lane);
+  if (h == 0) dst[DP * DP + 32 * w + r] = zrun;
+}
+
 // ------------------------------------------------------------------- k_scan
 // One thread per state element of one head: exclusive prefix over segments
 // in place, total into slot nseg, and the caller's final state if asked.
@@ -1001,7 +1084,15 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
     k_bucket<<<1, 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
   }
   const bool phi = (form == CAUSAL);
-  if (phi)
+  bool state_done = false;
+  if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
+    if (phi && vec) {
+      k_state_tr<<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
+      state_done = true;
+    }
+  }
+  if (state_done) {
+  } else if (phi)
     k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   else
     k_state<T, DP, C, false><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
