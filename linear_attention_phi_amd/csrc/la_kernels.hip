@@ -562,7 +562,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
 // accumulator is the B operand of V^T P^T; la_device.h), and the row sums of
 // the rounded P for the normaliser.  The state is carried as in k_out: two of
 // the 16 32 x 32 state blocks per wave in MFMA accumulators, relu(K)^T V on
-// top of the segment's exclusive prefix, plus 1 (x) (sum of V).
+// top of the segment's exclusive prefix, plus 1 (x) (sum of V).  relu(K) and
+// V stay token-major in LDS; their operands over the token index (V^T for
+// V^T P^T, both operands of relu(K)^T V) are transposed reads, and z and the
+// sums of V are dot2 sums over those fragments (waves 0-3: z of rows
+// 32 w .., waves 4-7: sums of V of columns 32 (w - 4) ..).
 template <int R>
 __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                  const bf16* __restrict__ v, bf16* __restrict__ out, int64_t n,
@@ -570,13 +574,13 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
                                                  const float* __restrict__ ws) {
   constexpr int DP = 128, C = 32;
   constexpr int LQ = DP + PAD;  // row stride of sK, sQ, sO, sST
-  constexpr int LC = C + PAD;   // row stride of sKT, sVT
+  constexpr int RS = STR_RS;    // row stride of sKr, sV (conflict-free transposed reads)
   constexpr int NPH = 8 / R;    // waves per query head
   constexpr int NBW = 4 / NPH;  // 32-wide output feature blocks per wave
   static_assert(R == 2 || R == 4, "two or four query heads per key/value head");
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LQ];       // phi(K), token-major
-  __shared__ __attribute__((aligned(16))) bf16 sKT[DP * LC];     // relu(K), feature-major
-  __shared__ __attribute__((aligned(16))) bf16 sVT[DP * LC];     // V, feature-major
+  __shared__ __attribute__((aligned(16))) bf16 sKr[C * RS];     // relu(K), token-major
+  __shared__ __attribute__((aligned(16))) bf16 sV[C * RS];      // V, token-major
   __shared__ __attribute__((aligned(16))) bf16 sST[DP * LQ];     // S^T in bf16
   __shared__ __attribute__((aligned(16))) bf16 sQ[R][C * LQ];    // phi(Q) of each query head
   __shared__ __attribute__((aligned(16))) bf16 sO[R][C * LQ];    // outputs on their way out
@@ -599,16 +603,15 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
 #pragma unroll
     for (int s = 0; s < 2; ++s) ld_state_block<DP>(accS[s], src, (w + 8 * s) / 4, (w + 8 * s) % 4, lane);
   }
-  float zrun = 0.0f, vrun = 0.0f;
+  float zrun = 0.0f, vrun = 0.0f;  // waves 0-3: z[32 w + r]; waves 4-7: sum of V[., 32 (w - 4) + r]
+  if (w < 4) zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + 32 * w + r];
   if (tid < DP) {
-    zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + tid];
     svc[tid] = 0.0f;
     szero[tid] = (bf16)0.0f;
   }
 
-  // Tiles of a chunk: half 0 loads K, half 1 V, as two adjacent rows x 8
-  // features per thread (so that the feature-major copies are written two
-  // tokens to a 4-byte word); query tile g goes to half g % 2.
+  // Tiles of a chunk: half 0 loads K, half 1 V, two adjacent rows x 8
+  // features per thread; query tile g goes to half g % 2.
   constexpr int QPH = R / 2;  // query tiles per half
   TileRaw<bf16, DP, C> raw[QPH];
   la_bf16::u32x4 kv2[2];
@@ -633,18 +636,17 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
     {
-      // K: phi(K) token-major (zero past the sequence end), relu(K) feature-
-      // major; V: feature-major
-      uint32_t x[2][4];
+      // K: relu(K) and phi(K) token-major (phi(K) zero past the sequence
+      // end; relu(K) and V are zero there as loaded); V: token-major
+      bf16* tm = half == 0 ? sKr : sV;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
+      for (int rr = 0; rr < 2; ++rr) {
+        la_bf16::u32x4 x = kv2[rr];
+        if (half == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[rr][j] = half == 0 ? la_bf16::relu2(kv2[rr][j]) : kv2[rr][j];
-      bf16* fm = half == 0 ? sKT : sVT;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<uint32_t*>(fm + (pc0 + 2 * j) * LC + pr0) = (x[0][j] & 0xFFFFu) | (x[1][j] << 16);
-        *reinterpret_cast<uint32_t*>(fm + (pc0 + 2 * j + 1) * LC + pr0) = (x[0][j] >> 16) | (x[1][j] & 0xFFFF0000u);
+          for (int j = 0; j < 4; ++j) x[j] = la_bf16::relu2(x[j]);
+        }
+        *reinterpret_cast<la_bf16::u32x4*>(tm + (pr0 + rr) * RS + pc0) = x;
       }
       if (half == 0) {
 #pragma unroll
@@ -668,10 +670,10 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
       add_col(cur, svc[nb * 32 + r], ma, DP, lane);
       st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
     }
-    if (tid < DP) {
+    if (w < 4 && h == 0) {
       const bf16 zh = (bf16)zrun;
-      szh[tid] = zh;
-      szl[tid] = (bf16)(zrun - (float)zh);
+      szh[32 * w + r] = zh;
+      szl[32 * w + r] = (bf16)(zrun - (float)zh);
     }
     __syncthreads();
 
@@ -699,11 +701,8 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
       const int nb = hf * NBW + u;
       f32x16 o = f32x16{};
       gemm_acc<bf16, DP / 16>(o, sST + nb * 32 * LQ, LQ, qg, LQ, lane);
-      Frag<bf16> va;
-      ld_frag(va, sVT + (nb * 32 + r) * LC + 4 * h);
-      mma(o, va, p0);
-      ld_frag(va, sVT + (nb * 32 + r) * LC + 16 + 4 * h);
-      mma(o, va, p1);
+      mma(o, la_bf16::ld_tr<RS>(sV, 0, nb * 32, lane), p0);
+      mma(o, la_bf16::ld_tr<RS>(sV, 16, nb * 32, lane), p1);
       uint2* dst = reinterpret_cast<uint2*>(sO[g] + r * LQ + nb * 32 + 4 * h);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
@@ -712,15 +711,31 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
     }
 
     // ---- S += relu(K_c)^T V_c (two blocks per wave); z and the sum of V
+    {
+      Frag<bf16> vt[C / 16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int e = w + 8 * s, ma = e / 4, nb = e % 4;
-      gemm_acc<bf16, C / 16>(accS[s], sKT + ma * 32 * LC, LC, sVT + nb * 32 * LC, LC, lane);
-    }
-    if (tid < DP) {
-      zrun += row_sum<bf16, C>(sKT, tid) + (float)nv;
-      vrun += row_sum<bf16, C>(sVT, tid);
-      svc[tid] = vrun;  // read at the next chunk's start (this chunk read it before the barrier above)
+      for (int kt = 0; kt < C / 16; ++kt) vt[kt] = la_bf16::ld_tr<RS>(sV, 16 * kt, (w % 4) * 32, lane);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ma = (w + 8 * s) / 4;  // column block w % 4
+#pragma unroll
+        for (int kt = 0; kt < C / 16; ++kt) mma(accS[s], la_bf16::ld_tr<RS>(sKr, 16 * kt, ma * 32, lane), vt[kt]);
+      }
+      // waves 0-3: z of rows 32 w ..; waves 4-7: sums of V of columns 32 (w - 4) ..
+      float cs = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < C / 16; ++kt) {
+        const Frag<bf16> f = w < 4 ? la_bf16::ld_tr<RS>(sKr, 16 * kt, w * 32, lane) : vt[kt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs = la_bf16::dot2(la_bf16::pair(f, j), la_bf16::ONE2, cs);
+      }
+      cs += __shfl_xor(cs, 32);
+      if (w < 4) {
+        zrun += cs + (float)nv;
+      } else {
+        vrun += cs;
+        if (h == 0) svc[32 * (w - 4) + r] = vrun;  // read at the next chunk's start (this chunk read it before the barrier above)
+      }
     }
     __syncthreads();
 
