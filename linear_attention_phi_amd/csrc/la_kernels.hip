@@ -861,10 +861,10 @@ __device__ __forceinline__ int bucket_take(int* cnt, int b, bool valid, int lane
   return valid ? atomicAdd(&cnt[b], 1) : 0;
 }
 
-__global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks,
-                                                 int* __restrict__ boff, int* __restrict__ perm) {
-  __shared__ int cnt[la_internal::kMaxBuckets + 1];
-  __shared__ int part[1024];
+// The sort, for one workgroup of up to 1024 threads; cnt holds nchunks + 1
+// ints and part one int per thread, both in LDS.
+__device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks, int* __restrict__ boff,
+                            int* __restrict__ perm, int* cnt, int* part) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
   const int len = (int)nchunks + 1;
   for (int c = tid; c < len; c += nt) cnt[c] = 0;
@@ -928,6 +928,134 @@ __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, 
       const int pos = bucket_take(cnt, bk[k], bk[k] >= 0, lane);
       if (bk[k] >= 0) perm[pos] = (int)(base + tid + (int64_t)k * nt);
     }
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks,
+                                                 int* __restrict__ boff, int* __restrict__ perm) {
+  __shared__ int cnt[la_internal::kMaxBuckets + 1];
+  __shared__ int part[1024];
+  bucket_sort(m, n, C, nchunks, boff, perm, cnt, part);
+}
+
+// ---------------------------------------------------------------- k_state32
+// k_state for fp32 with d = 64, on v_mfma_f32_16x16x4_f32 straight from
+// token-major rows (no LDS transposes; the scheme of la_forward_f32.hip): a
+// lane that loads 16 bytes of a row holds four consecutive features of one
+// key, and each of them is the operand of its own MFMA.  The segment's keys
+// go in 32-key blocks to the eight waves in turn; the buffer resources end
+// at the segment's last key, so rows past it read as zero.  The wave
+// results are summed in LDS in wave order and written to the segment's slot
+// (S row-major, then z).  With bucket arguments (the prefix form), block 0
+// of the same launch does k_bucket's sort (dispatched first, so that its
+// serial passes overlap the state work).  n <= kFwd32MaxN, so
+// that a head's rows stay below 2^31 bytes (the resources' record count).
+union State32Lds {
+  struct {
+    f32x4 acc[8][16][64];  // entry (4 j + j', lane l), float rr: S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']
+    f32x4 z[8][16];        // z[4 m .. 4 m + 3] of each wave
+  } s;
+  struct {
+    int cnt[la_internal::kMaxBuckets + 1];
+    int part[512];
+  } b;
+};
+
+template <bool PHI>
+__global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, const float* __restrict__ v, int64_t n,
+                                                 int64_t nchunks, int C, int64_t G, int64_t nseg,
+                                                 float* __restrict__ ws, const int64_t* __restrict__ m,
+                                                 int* __restrict__ boff, int* __restrict__ perm) {
+  constexpr int FD = 64, TW = 32, NW8 = 8;
+  __shared__ State32Lds L;
+  int64_t sb = blockIdx.x;  // state block
+  if (m) {
+    if (sb == 0) {
+      bucket_sort(m, n, C, nchunks, boff, perm, L.b.cnt, L.b.part);
+      return;
+    }
+    --sb;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
+  const int64_t bh = sb / nseg, seg = sb % nseg;
+  const int64_t k0 = seg * G * C, k1r = (seg + 1) * G * C, k1 = k1r < n ? k1r : n;
+  // resources over this head's rows [0, k1): keys past the segment read as zero
+  const int ebytes = (int)(k1 * FD * 4);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(k + bh * n * FD), 0, ebytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(v + bh * n * FD), 0, ebytes, 0x00020000);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) acc[j][jp] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 zr = f32x4{0.0f, 0.0f, 0.0f, 0.0f};  // sum of relu(K) over this lane's keys
+  int nkeys = 0;                               // keys this wave has taken
+  const int64_t nblk = (k1 - k0 + TW - 1) / TW;
+  for (int64_t blk = w; blk < nblk; blk += NW8) {
+    const int64_t t0 = k0 + blk * TW;
+    nkeys += (int)((k1 - t0) < TW ? (k1 - t0) : TW);
+    // step s: keys t0 + 4 s + kq, features 4 mm ..; loads first, in step
+    // order, then the steps (pinned so that step s waits for its own rows)
+    f32x4 kr[TW / 4], vr[TW / 4];
+#pragma unroll
+    for (int s = 0; s < TW / 4; ++s) {
+      const uint32_t off = (uint32_t)((t0 + 4 * s + kq) * FD + 4 * mm) * 4u;
+      kr[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)off, 0, 0));
+      vr[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0, 0));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int s = 0; s < TW / 4; ++s) {
+      f32x4 pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (PHI) {
+          const float x = fmaxf(kr[s][j], 0.0f);
+          zr[j] += x;
+          pk[j] = x + 1.0f;  // keys past the segment: 1, against V = 0
+        } else {
+          pk[j] = kr[s][j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp)
+          acc[j][jp] = __builtin_amdgcn_mfma_f32_16x16x4f32(pk[j], vr[s][jp], acc[j][jp], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    zr[j] += __shfl_xor(zr[j], 16);
+    zr[j] += __shfl_xor(zr[j], 32);
+    zr[j] += PHI ? (float)nkeys : 0.0f;  // the ones of phi(K), real keys only
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) L.s.acc[w][4 * j + jp][lane] = acc[j][jp];
+  if (kq == 0) L.s.z[w][mm] = zr;
+  __syncthreads();
+  // the segment's aggregate: the waves' results summed in wave order, then
+  // from accumulator order to S row-major
+  float* dst = ws + (bh * (nseg + 1) + seg) * slot_elems(FD);
+  const f32x4* la = &L.s.acc[0][0][0];
+  for (int e = tid; e < 16 * 64; e += 512) {
+    f32x4 sm = la[e];
+#pragma unroll
+    for (int u = 1; u < NW8; ++u) sm += la[u * 16 * 64 + e];
+    const int b = e >> 6, l = e & 63, j = b >> 2, jp = b & 3, m4 = l & 15, kk = l >> 4;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) dst[(16 * kk + 4 * rr + j) * FD + 4 * m4 + jp] = sm[rr];
+  }
+  if (tid < 16) {
+    f32x4 sm = L.s.z[0][tid];
+#pragma unroll
+    for (int u = 1; u < NW8; ++u) sm += L.s.z[u][tid];
+    *reinterpret_cast<f32x4*>(dst + FD * FD + 4 * tid) = sm;
   }
 }
 
@@ -1092,14 +1220,28 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   const T* v = reinterpret_cast<const T*>(a.v);
   T* out = reinterpret_cast<T*>(a.out);
   int* boff = nullptr; int* perm = nullptr;
+  bool state_done = false;
   if (form == PREFIX) {
     char* bw = reinterpret_cast<char*>(a.ws) + la_internal::state_bytes(p, a.B, a.Hkv);
     boff = reinterpret_cast<int*>(bw);
     perm = boff + (p.nchunks + 1);
-    k_bucket<<<1, 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
+    if constexpr (std::is_same<T, float>::value && DP == 64) {
+      if (vec && a.n <= la_internal::kFwd32MaxN) {  // the sort as one more workgroup of the state launch
+        k_state32<false><<<dim3((unsigned)(nbh * p.nseg + 1)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
+                                                                              states, a.m, boff, perm);
+        state_done = true;
+      }
+    }
+    if (!state_done) k_bucket<<<1, 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
   }
   const bool phi = (form == CAUSAL);
-  bool state_done = false;
+  if constexpr (std::is_same<T, float>::value && DP == 64) {
+    if (phi && vec && a.n <= la_internal::kFwd32MaxN) {
+      k_state32<true><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
+                                                                       states, nullptr, nullptr, nullptr);
+      state_done = true;
+    }
+  }
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
     if (phi && vec) {
       k_state_tr<<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
