@@ -257,6 +257,201 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
   }
 }
 
+// ----------------------------------------------------------- k_out_prefix32
+// Prefix form for fp32 with d = 64 and chunk 64 on v_mfma_f32_16x16x4_f32,
+// with no LDS transposes:
+//   out^T(bucket c) = S_prev(c)^T Q^T + V_c^T P^T,   P^T = mask(K_c Q^T),
+// where S_prev(c) is the state before chunk c (the segment's exclusive prefix
+// plus the segment's earlier chunks) and the mask keeps key j for query i iff
+// j <= m_i.  The queries of bucket c go in groups of 128, one 16-query block
+// per wave, their rows gathered through perm and staged in LDS.  Operands
+// (the contraction index k is lane / 16, the other index lane % 16):
+//   S^T  from LDS in operand order: entry (bb, tt, lane) is the float4 over
+//        jj of S[16 tt + 4 (lane / 16) + jj][16 bb + lane % 16];
+//   Q^T  the float4 of query row lane % 16 at features 16 tt + 4 (lane / 16);
+//   K    the float4 of key row 16 kb + lane % 16 at the same features;
+//   P^T  the score accumulator itself: its register rr holds key
+//        16 kb + 4 (lane / 16) + rr of query lane % 16, which is the B operand
+//        of the k-step over keys {16 kb + 4 k + rr};
+//   V^T  for that k-step, V[16 kb + 4 (lane / 16) + rr][16 bb + lane % 16],
+//        one float per lane from the V tile.
+// A lane's output accumulator holds features 16 bb + 4 (lane / 16) .. + 3 of
+// query lane % 16.  Waves 4-7 keep the state: wave w holds tiles (j, j') =
+// (w - 4, 0..3) in accumulator order (entry rr of lane l:
+// S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']), writes them in operand order
+// at the chunk's start and adds K_c^T V_c while waves 0-3 work on the
+// chunk's first query group (buckets of up to 64 queries need only waves
+// 0-3; larger ones give blocks 4-7 to waves 4-7 after their update).
+constexpr int PX_RS = 64 + 4;  // row stride (floats) of the LDS tiles
+constexpr int PX_QG = 128;     // queries per group: one 16-query block per wave
+__global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
+                                                      const float* __restrict__ v, float* __restrict__ out, int64_t n,
+                                                      int64_t nchunks, int64_t G, int64_t nseg,
+                                                      const float* __restrict__ ws, const int* __restrict__ perm,
+                                                      const int* __restrict__ boff, const int64_t* __restrict__ m) {
+  constexpr int FD = 64, C = 64, RS = PX_RS, QG = PX_QG;
+  __shared__ __attribute__((aligned(16))) float sK[C * RS];
+  __shared__ __attribute__((aligned(16))) float sV[C * RS];
+  __shared__ __attribute__((aligned(16))) float sQ[QG * RS];
+  __shared__ __attribute__((aligned(16))) float sS[16 * 64 * 4];  // S in operand order
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
+  const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  const float* qh = q + bh * n * FD;
+  const float* kh = k + bh * n * FD;
+  const float* vh = v + bh * n * FD;
+  float* oh = out + bh * n * FD;
+
+  // waves 4-7: state tiles (w - 4, 0..3), from the segment's exclusive
+  // prefix (row-major)
+  const bool owner = w >= 4;
+  const int sj = w & 3;
+  f32x4 accS[4];
+  {
+    const float* src = ws + (bh * (nseg + 1) + seg) * slot_elems(FD);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) accS[t][rr] = owner ? src[(16 * kq + 4 * rr + sj) * FD + 4 * mm + t] : 0.0f;
+  }
+  auto state_update = [&]() {  // S += K_c^T V_c on this wave's tiles
+#pragma unroll
+    for (int st = 0; st < C / 4; ++st) {
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(sK + (4 * st + kq) * RS + 4 * mm);
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(sV + (4 * st + kq) * RS + 4 * mm);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) accS[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[sj], vv[t], accS[t], 0, 0, 0);
+    }
+  };
+  const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
+
+  // next chunk's K and V rows (piece u: row (tid + 512 u) / 16, features
+  // 4 ((tid + 512 u) % 16)), and the next query group's rows
+  f32x4 kr[2], vr[2], qraw[4];
+  auto fetch_kv = [&](int64_t c) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+      const int64_t t = c * C + row;
+      kr[u] = t < n ? *reinterpret_cast<const f32x4*>(kh + t * FD + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      vr[u] = t < n ? *reinterpret_cast<const f32x4*>(vh + t * FD + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  auto groups_of = [&](int64_t c) -> int { return (int)((boff[c + 1] - boff[c] + QG - 1) / QG); };
+  auto fetch_q_after = [&](int64_t c, int grp) {  // rows of the query group after (c, grp), if any
+    int64_t cc = c;
+    int gg = grp + 1;
+    while (cc < c1 && gg >= groups_of(cc)) {
+      ++cc;
+      gg = 0;
+    }
+    if (cc >= c1) return;
+    const int64_t s0 = boff[cc] + (int64_t)QG * gg, e0 = boff[cc + 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+      qraw[u] = s0 + row < e0 ? *reinterpret_cast<const f32x4*>(qh + (int64_t)perm[s0 + row] * FD + col)
+                              : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  if (c0 < c1) {
+    fetch_kv(c0);
+    fetch_q_after(c0, -1);
+  }
+
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int ngroups = groups_of(c);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+      *reinterpret_cast<f32x4*>(sK + row * RS + col) = kr[u];
+      *reinterpret_cast<f32x4*>(sV + row * RS + col) = vr[u];
+    }
+    if (c + 1 < c1) fetch_kv(c + 1);
+    // S_prev(c) in operand order: tile entry S[16 kq + 4 rr + sj][4 mm + j']
+    // -> (bb, tt, L, jj) = (mm / 4, kq, 16 rr + 4 (mm % 4) + j', sj)
+    if (owner) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          sS[(((mm >> 2) * 4 + kq) * 64 + 16 * rr + 4 * (mm & 3) + t) * 4 + sj] = accS[t][rr];
+    }
+    __syncthreads();  // tiles and S visible
+    if (ngroups == 0 && owner) state_update();
+
+    for (int grp = 0; grp < ngroups; ++grp) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+        *reinterpret_cast<f32x4*>(sQ + row * RS + col) = qraw[u];
+      }
+      fetch_q_after(c, grp);
+      __syncthreads();  // the group's query rows visible
+      if (grp == 0 && owner) state_update();
+      const int64_t i0 = boff[c] + (int64_t)QG * grp + 16 * w;  // this wave's first query (position in perm)
+      const int64_t e0 = boff[c + 1];
+      if (i0 < e0) {
+        const bool valid = i0 + mm < e0;
+        const int qi = valid ? perm[i0 + mm] : 0;
+        int64_t mi = valid ? m[qi] : 0;
+        mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);  // same clamp as the bucket sort
+        const int limit = (int)(mi - t0);
+        f32x4 qo[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) qo[tt] = *reinterpret_cast<const f32x4*>(sQ + (16 * w + mm) * RS + 16 * tt + 4 * kq);
+        f32x4 o[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) o[bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // S_prev^T Q^T
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f32x4 so[4];
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) so[bb] = *reinterpret_cast<const f32x4*>(sS + ((bb * 4 + tt) * 64 + lane) * 4);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) o[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(so[bb][jj], qo[tt][jj], o[bb], 0, 0, 0);
+        }
+        // the four key blocks' scores (independent chains), masked, then
+        // V^T P^T over their keys
+        f32x4 sc[C / 16];
+#pragma unroll
+        for (int kb = 0; kb < C / 16; ++kb) sc[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f32x4 ko[C / 16];
+#pragma unroll
+          for (int kb = 0; kb < C / 16; ++kb) ko[kb] = *reinterpret_cast<const f32x4*>(sK + (16 * kb + mm) * RS + 16 * tt + 4 * kq);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int kb = 0; kb < C / 16; ++kb) sc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ko[kb][jj], qo[tt][jj], sc[kb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int kb = 0; kb < C / 16; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) sc[kb][rr] = (16 * kb + 4 * kq + rr <= limit) ? sc[kb][rr] : 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < C / 16; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              o[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(sV[(16 * kb + 4 * kq + rr) * RS + 16 * bb + mm], sc[kb][rr], o[bb], 0, 0, 0);
+        if (valid) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            __builtin_nontemporal_store(o[bb], reinterpret_cast<f32x4*>(oh + (int64_t)qi * FD + 16 * bb + 4 * kq));
+        }
+      }
+      __syncthreads();  // the group's rows are no longer read
+    }
+    __syncthreads();  // tiles and S are rewritten by the next chunk
+  }
+}
+
 // -------------------------------------------------------------------- k_out
 // Causal (FORM = CAUSAL: phi, normalised; the queries of chunk c are its own
 // rows, for each of the R query heads of this key/value head) or prefix
@@ -1263,6 +1458,13 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
           k_out_gqa<2><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, p.G, p.nseg, states);
         else
           k_out_gqa<4><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, p.G, p.nseg, states);
+        return (int)hipGetLastError();
+      }
+    }
+    if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
+      if (form == PREFIX && vec) {
+        k_out_prefix32<<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(q, k, v, out, a.n, p.nchunks, p.G, p.nseg,
+                                                                      states, perm, boff, a.m);
         return (int)hipGetLastError();
       }
     }

@@ -128,6 +128,23 @@ def test_prefix_small(gpu, dtype, kind, case):
     check(g, oracle.prefix_mask(q, k, v, m), dtype, f"prefix {kind} {_small_id(case)} {dtype}")
 
 
+@pytest.mark.parametrize("kind", ["random", "causal", "full"])
+@pytest.mark.parametrize("shape", [(1, 2, 1000), (2, 3, 300)], ids=lambda c: "B%d_H%d_n%d" % c)
+def test_prefix_f32_d64_query_groups(gpu, kind, shape):
+    """fp32, d = 64, chunk 64 (the 16x16x4 MFMA prefix kernel): ragged tails,
+    several segments, and with the 'full' mask a single bucket of n queries,
+    so that a chunk takes several groups of 128 queries.  Not the 'first'
+    mask at these sizes: it makes every row the single dot product q_i . k_0
+    times v_0, whose fp32 relative error is unbounded when the dot product
+    cancels (seed 5, B1 H2 n1000 has a row with sum |q_a k_a| / |q . k| of
+    about 15000, where numpy's own fp32 product is off by 1.2e-4)."""
+    B, H, n = shape
+    q, k, v, rng = li.qkv(B, H, H, n, 64, li.F32, seed=5, scaled=True)
+    m = li.mask(n, kind, rng=rng)
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=64))
+    check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B{B} H{H} n{n} d64 f32")
+
+
 def test_prefix_page_mask(gpu):
     """m = [2, 0, 1] (the trim-transformer page's example) on the GPU."""
     q, k, v, _ = li.qkv(1, 2, 2, 3, 4, li.F32, seed=11)
@@ -239,9 +256,10 @@ def test_causal_uniform_keys_closed_form_full_scale(gpu):
 
 @pytest.mark.parametrize("kind", ["causal", "random"])
 def test_prefix_B4_H8_n8192_d64_f32(gpu, kind):
+    """At chunk 64, the launch configuration the benchmark times."""
     q, k, v, rng = li.qkv(4, 8, 8, 8192, 64, li.F32, seed=0, scaled=True)
     m = li.mask(8192, kind, rng=rng)
-    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m)))
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=64))
     check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B4 H8 n8192 d64 f32")
 
 
