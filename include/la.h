@@ -116,7 +116,8 @@ la_status la_causal_forward(const void* q, const void* k, const void* v,
  * normaliser, no scale.  m is a device int64 array [n] shared by every batch
  * and head, any order, duplicates allowed; every m_i must lie in [0, n-1]
  * (not checked on the device: out-of-range values are a contract violation).
- * q, k, v, out [B][H][n][d].  chunk as for la_causal_forward. */
+ * q, k, v, out [B][H][n][d].  chunk as for la_causal_forward, except that
+ * the default for fp32 with d = 64 is 64. */
 la_status la_prefix_mask_forward(const void* q, const void* k, const void* v,
                                  const int64_t* m, int64_t B, int64_t H,
                                  int64_t n, int64_t d, la_dtype dtype,

@@ -166,6 +166,12 @@ const char* la_status_str(la_status s) {
   }
 }
 
+// The prefix form with fp32 and d = 64 defaults to chunk 64: its state and
+// output kernels (16x16x4 fp32 MFMA, no LDS transposes) exist for that chunk.
+static int32_t prefix_chunk(bool prefix, int32_t chunk, la_dtype dtype, int64_t d) {
+  return prefix && chunk == 0 && dtype == LA_F32 && d == 64 ? 64 : chunk;
+}
+
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dtype,
                           int32_t chunk) {
   if (op != LA_OP_FORWARD && op != LA_OP_CAUSAL && op != LA_OP_PREFIX_MASK) return 0;
@@ -173,7 +179,7 @@ size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_
   int C = 0;
   if (op == LA_OP_FORWARD) {
     C = forward_chunk(elem_bytes(dtype), padded_dim(d));
-  } else if (resolve_chunk(chunk, dtype, d, &C) != LA_OK) {
+  } else if (resolve_chunk(prefix_chunk(op == LA_OP_PREFIX_MASK, chunk, dtype, d), dtype, d, &C) != LA_OK) {
     return 0;
   }
   if (op == LA_OP_PREFIX_MASK && (Hq != Hkv || (n + C - 1) / C > kMaxBuckets)) return 0;
@@ -257,7 +263,7 @@ la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, co
   if (!q || !k || !v || !m || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(m) || !aligned16(out)) return LA_ERR_ALIGN;
   int C = 0;
-  if ((st = resolve_chunk(chunk, dtype, d, &C)) != LA_OK) return st;
+  if ((st = resolve_chunk(prefix_chunk(true, chunk, dtype, d), dtype, d, &C)) != LA_OK) return st;
   if ((n + C - 1) / C > kMaxBuckets) return LA_ERR_UNSUPPORTED;
   const size_t eb = elem_bytes(dtype);
   const size_t tb = (size_t)(B * H * n * d) * eb, mb = (size_t)n * sizeof(int64_t);
