@@ -78,6 +78,9 @@ struct CpLds {
   uint32_t zh[SEGC][FD / 2];   // z_pre of each chunk as bf16 (high, low) pairs
   uint32_t zl[SEGC][FD / 2];
   bf16 zero[FD];               // zeros: the rows of the z operand other than 0 and 16
+  bf16 sprev[FC * RS];         // S_prev^T [b][a] in bf16: the earlier segments' total
+  uint32_t zhp[FD / 2];        // z_prev as bf16 (high, low) pairs
+  uint32_t zlp[FD / 2];
 };
 static_assert(32 * RSF * 4 <= TILE_B, "state half-tile must fit a token-major tile");
 
@@ -296,6 +299,40 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   __syncthreads();  // also: every state tile has been read
   if (publish && tid == 0) __hip_atomic_store(flag + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+  // S_loc(c) (this segment's chunks before c) in bf16, [b][a] rows of RS,
+  // over region c, and z_loc(c) as pairs; their products with phi(Q) run
+  // while the earlier segments' aggregates are awaited.  S_loc(0) = 0.
+#pragma unroll
+  for (int c = 1; c < SEGC; ++c) {
+    if (c < ncl) {
+      uint32_t y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = pack2(pre[c][2 * j], pre[c][2 * j + 1]);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(L.reg[c]) + sb * RS + sa) = u32x4{y[0], y[1], y[2], y[3]};
+      if (w == 0) store_z_pairs(L.zh[c], L.zl[c], zpre[c], lane);
+    }
+  }
+  __syncthreads();
+  // num += phi(Q) S_loc (A operand S^T, rows b, over features); den_i +=
+  // phi(Q_i) . z via rows 0 and 16 of the z operand (high and low parts)
+  float dz[2] = {0.0f, 0.0f};  // phi(Q_i) . z terms (lanes with h == 0)
+  auto state_products = [&](const bf16* tS, const uint32_t* zh, const uint32_t* zl) {
+    const bf16* zbase = (r == 0) ? reinterpret_cast<const bf16*>(zh)
+                                 : (r == 16) ? reinterpret_cast<const bf16*>(zl) : L.zero;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(O[nb][ib], ld16(tS + (32 * nb + r) * RS + 16 * kb + 8 * h), qf[ib][kb]);
+      f32x16 zacc = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(zacc, ld16(zbase + 16 * kb + 8 * h), qf[ib][kb]);
+      dz[ib] += zacc[0] + zacc[8];
+    }
+  };
+  if (mine && w > 0) state_products(reinterpret_cast<const bf16*>(L.reg[w]), L.zh[w], L.zl[w]);
+
   if (seg > 0) {
     if (w == 0) {
       for (int64_t p = lane; p < seg; p += 64) {
@@ -341,16 +378,13 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       }
     }
   }
-  // S_pre(c) = S_prev + S_loc(c) in bf16, [b][a] rows of RS, over region c
+  // S_prev in bf16 into the shared tile, z_prev as pairs
+  if (seg > 0) {
+    uint32_t y[4];
 #pragma unroll
-  for (int c = 0; c < SEGC; ++c) {
-    if (c < ncl) {
-      uint32_t y[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = pack2(sp[2 * j] + pre[c][2 * j], sp[2 * j + 1] + pre[c][2 * j + 1]);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(L.reg[c]) + sb * RS + sa) = u32x4{y[0], y[1], y[2], y[3]};
-      if (w == 0) store_z_pairs(L.zh[c], L.zl[c], zprev + zpre[c], lane);
-    }
+    for (int j = 0; j < 4; ++j) y[j] = pack2(sp[2 * j], sp[2 * j + 1]);
+    *reinterpret_cast<u32x4*>(L.sprev + sb * RS + sa) = u32x4{y[0], y[1], y[2], y[3]};
+    if (w == 0) store_z_pairs(L.zhp, L.zlp, zprev, lane);
   }
   if (seg == A.nseg - 1) {
     if (A.S_final) {
@@ -364,23 +398,10 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 
   // ------------------------------------------------------------------ C
   if (mine) {
-    const bf16* tS = reinterpret_cast<const bf16*>(L.reg[w]);
-    const bf16* zbase = (r == 0) ? reinterpret_cast<const bf16*>(L.zh[w])
-                                 : (r == 16) ? reinterpret_cast<const bf16*>(L.zl[w]) : L.zero;
+    if (seg > 0) state_products(L.sprev, L.zhp, L.zlp);
     float inv[2];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      // numerator += phi(Q) S_pre: A operand S_pre^T (rows b), over features
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(O[nb][ib], ld16(tS + (32 * nb + r) * RS + 16 * kb + 8 * h), qf[ib][kb]);
-      // den_i += phi(Q_i) . z_pre: rows 0 and 16 (high and low parts of z)
-      f32x16 zacc = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(zacc, ld16(zbase + 16 * kb + 8 * h), qf[ib][kb]);
-      inv[ib] = __builtin_amdgcn_rcpf(__shfl(den[ib] + zacc[0] + zacc[8], r));  // from the lane with h == 0
-    }
+    for (int ib = 0; ib < 2; ++ib) inv[ib] = __builtin_amdgcn_rcpf(__shfl(den[ib] + dz[ib], r));  // from the lane with h == 0
     // the output rows go through LDS so that global stores cover whole
     // 128-byte rows, 16 bytes per lane; the stores are non-temporal, so that
     // they do not sit in L2 as dirty lines to be written back when the
