@@ -231,16 +231,15 @@ __global__ __launch_bounds__(WNT) void k_fwd_out(FwdArgs A) {
   constexpr int OOB = 0x7FFFFFF0;  // past num_records: reads as zero
   // phi(Q) (query block ib, feature block kb), S^T (feature block nb, kb) and
   // the z operand (row 0: high parts, row 16: low parts, other rows zero)
-  Frag<bf16> qf[2][4], sf[2][4], zf[4];
+  // every load is issued before phi is applied to Q (left to itself the
+  // compiler waits for each Q fragment before issuing the next)
+  u32x4 qraw[2][4];
 #pragma unroll
   for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, ((t0 + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
-      qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int kb = 0; kb < 4; ++kb)
+      qraw[ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((t0 + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
+  Frag<bf16> qf[2][4], sf[2][4], zf[4];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -252,6 +251,16 @@ __global__ __launch_bounds__(WNT) void k_fwd_out(FwdArgs A) {
   for (int kb = 0; kb < 4; ++kb)
     zf[kb].v = __builtin_bit_cast(
         bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rt, zrow < 0 ? OOB : zrow + (16 * kb + 8 * h) * 2, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4 x = qraw[ib][kb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
+      qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
+    }
 
   bf16* tO = reinterpret_cast<bf16*>(Lout[w]);
 #pragma unroll

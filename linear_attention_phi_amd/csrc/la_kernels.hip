@@ -1070,12 +1070,20 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
   const int64_t step = (int64_t)nt * PER;
   for (int64_t base = 0; base < n; base += step) {
     int bk[PER];
+    int64_t mv[PER];  // all of the block's loads first (left to itself the
+                      // compiler waits for each before issuing the next)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int64_t i = base + tid + (int64_t)k * nt;
+      mv[k] = i < n ? m[i] : -1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int64_t i = base + tid + (int64_t)k * nt;
       bk[k] = -1;
       if (i < n) {
-        int64_t mi = m[i];
+        int64_t mi = mv[k];
         mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
         bk[k] = (int)(mi / C);
       }
@@ -1108,12 +1116,20 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
   // cnt[c] is now bucket c's fill cursor
   for (int64_t base = 0; base < n; base += step) {
     int bk[PER];
+    int64_t mv[PER];  // all of the block's loads first (left to itself the
+                      // compiler waits for each before issuing the next)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int64_t i = base + tid + (int64_t)k * nt;
+      mv[k] = i < n ? m[i] : -1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int64_t i = base + tid + (int64_t)k * nt;
       bk[k] = -1;
       if (i < n) {
-        int64_t mi = m[i];
+        int64_t mi = mv[k];
         mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
         bk[k] = (int)(mi / C);
       }
