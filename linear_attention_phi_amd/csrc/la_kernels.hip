@@ -263,8 +263,8 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 //   out^T(bucket c) = S_prev(c)^T Q^T + V_c^T P^T,   P^T = mask(K_c Q^T),
 // where S_prev(c) is the state before chunk c (the segment's exclusive prefix
 // plus the segment's earlier chunks) and the mask keeps key j for query i iff
-// j <= m_i.  The queries of bucket c go in groups of 128, one 16-query block
-// per wave, their rows gathered through perm and staged in LDS.  Operands
+// j <= m_i.  The queries of bucket c go in groups of 16 NWV, one 16-query
+// block per wave, their rows gathered through perm and staged in LDS.  Operands
 // (the contraction index k is lane / 16, the other index lane % 16):
 //   S^T  from LDS in operand order: entry (bb, tt, lane) is the float4 over
 //        jj of S[16 tt + 4 (lane / 16) + jj][16 bb + lane % 16];
@@ -276,20 +276,27 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 //   V^T  for that k-step, V[16 kb + 4 (lane / 16) + rr][16 bb + lane % 16],
 //        one float per lane from the V tile.
 // A lane's output accumulator holds features 16 bb + 4 (lane / 16) .. + 3 of
-// query lane % 16.  Waves 4-7 keep the state: wave w holds tiles (j, j') =
-// (w - 4, 0..3) in accumulator order (entry rr of lane l:
+// query lane % 16.  The last four waves keep the state: the w-th of them
+// holds tiles (j, j') = (w, 0..3) in accumulator order (entry rr of lane l:
 // S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']), writes them in operand order
-// at the chunk's start and adds K_c^T V_c while waves 0-3 work on the
-// chunk's first query group (buckets of up to 64 queries need only waves
-// 0-3; larger ones give blocks 4-7 to waves 4-7 after their update).
+// at the chunk's start and adds K_c^T V_c during the chunk's first query
+// group.
 constexpr int PX_RS = 64 + 4;  // row stride (floats) of the LDS tiles
-constexpr int PX_QG = 128;     // queries per group: one 16-query block per wave
-__global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
+// NWV waves per workgroup, queries per group QG = 16 NWV (one 16-query block
+// per wave); the state is owned by waves NWV - 4 .. NWV - 1, four tiles each.
+// Four waves (68.6 KB of LDS, so that two workgroups share a CU and cover
+// each other's barriers) measured 146.9 / 179.3 us at B4 H8 n8192 (m = arange
+// / uniform) against 162.7 / 190.9 us for eight.
+constexpr int PX_NWV = 4;
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ v, float* __restrict__ out, int64_t n,
                                                       int64_t nchunks, int64_t G, int64_t nseg,
                                                       const float* __restrict__ ws, const int* __restrict__ perm,
                                                       const int* __restrict__ boff, const int64_t* __restrict__ m) {
-  constexpr int FD = 64, C = 64, RS = PX_RS, QG = PX_QG;
+  constexpr int FD = 64, C = 64, RS = PX_RS, QG = 16 * NWV, NT_ = 64 * NWV;
+  constexpr int KVP = C * FD / 4 / NT_;  // 16-byte pieces of a K or V tile per thread
+  static_assert(NWV == 4 || NWV == 8, "four or eight waves");
   __shared__ __attribute__((aligned(16))) float sK[C * RS];
   __shared__ __attribute__((aligned(16))) float sV[C * RS];
   __shared__ __attribute__((aligned(16))) float sQ[QG * RS];
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ 
 
   // waves 4-7: state tiles (w - 4, 0..3), from the segment's exclusive
   // prefix (row-major)
-  const bool owner = w >= 4;
+  const bool owner = w >= NWV - 4;
   const int sj = w & 3;
   f32x4 accS[4];
   {
@@ -324,13 +331,13 @@ __global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ 
   };
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
 
-  // next chunk's K and V rows (piece u: row (tid + 512 u) / 16, features
-  // 4 ((tid + 512 u) % 16)), and the next query group's rows
-  f32x4 kr[2], vr[2], qraw[4];
+  // next chunk's K and V rows (piece u: row (tid + NT_ u) / 16, features
+  // 4 ((tid + NT_ u) % 16)), and the next query group's rows
+  f32x4 kr[KVP], vr[KVP], qraw[4];
   auto fetch_kv = [&](int64_t c) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+    for (int u = 0; u < KVP; ++u) {
+      const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
       const int64_t t = c * C + row;
       kr[u] = t < n ? *reinterpret_cast<const f32x4*>(kh + t * FD + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       vr[u] = t < n ? *reinterpret_cast<const f32x4*>(vh + t * FD + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ 
     const int64_t s0 = boff[cc] + (int64_t)QG * gg, e0 = boff[cc + 1];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+      const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
       qraw[u] = s0 + row < e0 ? *reinterpret_cast<const f32x4*>(qh + (int64_t)perm[s0 + row] * FD + col)
                               : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -362,8 +369,8 @@ __global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ 
     const int64_t t0 = c * C;
     const int ngroups = groups_of(c);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+    for (int u = 0; u < KVP; ++u) {
+      const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
       *reinterpret_cast<f32x4*>(sK + row * RS + col) = kr[u];
       *reinterpret_cast<f32x4*>(sV + row * RS + col) = vr[u];
     }
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(512) void k_out_prefix32(const float* __restrict__ 
     for (int grp = 0; grp < ngroups; ++grp) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int pc = tid + 512 * u, row = pc >> 4, col = 4 * (pc & 15);
+        const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
         *reinterpret_cast<f32x4*>(sQ + row * RS + col) = qraw[u];
       }
       fetch_q_after(c, grp);
@@ -1479,8 +1486,8 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
     }
     if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
       if (form == PREFIX && vec) {
-        k_out_prefix32<<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(q, k, v, out, a.n, p.nchunks, p.G, p.nseg,
-                                                                      states, perm, boff, a.m);
+        k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * p.nseg)), 64 * PX_NWV, 0, st>>>(
+            q, k, v, out, a.n, p.nchunks, p.G, p.nseg, states, perm, boff, a.m);
         return (int)hipGetLastError();
       }
     }
