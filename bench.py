@@ -15,8 +15,10 @@ from 4096 tokens; one step = one la_decode_step call).
 
 Inputs are resident in HBM before timing starts; where one input/output set
 is smaller than 640 MiB, several copies rotate so that the footprint is not
-served from the 256 MiB last-level (MALL) cache.  K steps run back to back
-between two HIP events recorded on the stream the kernels are launched on.
+served from the 256 MiB last-level (MALL) cache.  W untimed steps (default
+1000, a few milliseconds to under a second of work) bring the GPU to steady
+clocks; then K steps run back to back between two HIP events recorded on the
+stream the kernels are launched on.
 
 Prints one JSON line per workload:
   value     tokens*heads per second (B * Hq * n per call; B * Hq per decode step);
@@ -198,14 +200,13 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
         per = bs * Hq * n
         what = f"{bs}-element slices of the batch (Hq={Hq} n={n} d={d})"
         cores = min(threads, bs * Hkv)
+    call()  # first-call costs (allocation, thread start) outside the timing
+    reps, el = 0, 0.0
     t0 = time.perf_counter()
-    call()
-    one = time.perf_counter() - t0
-    reps = max(1, int(budget_s / max(one, 1e-3)))
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    while el < budget_s:
         call()
-    el = time.perf_counter() - t0
+        reps += 1
+        el = time.perf_counter() - t0
     return {"value": reps * per / el, "unit": "tokens*heads/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} oracle calls on {what}, fp64, {el:.1f} s"}
 
@@ -349,7 +350,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload)")
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first (the GPU reaches steady clocks only after some "
+                         "milliseconds of work: after 10 the headline measured ~1 us slower per call)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--workload", default="causal", help="one of: " + ", ".join(WORKLOADS) + ", or all")
     ap.add_argument("--copy-calibration", nargs="?", const="vector", choices=["vector", "blit"], default=None,
