@@ -1425,6 +1425,77 @@ __global__ __launch_bounds__(NT) void k_decode4(const T* __restrict__ q, const T
   }
 }
 
+// The same step for D = 128 without LDS: wave w owns columns 32 w .. 32 w +
+// 31 of the head's state (lane l: columns 32 w + 4 (l % 8) .. + 3 of rows
+// l / 8 + 8 j, j < 16; a wave instruction covers eight whole 128-byte row
+// pieces), so phi(q) S for those columns and the normaliser reduce within
+// the wave by lane shuffles: no barrier per query head.  phi(q) of all R
+// query heads of the group is staged in LDS (R * 512 bytes, dynamic) while
+// the state loads are in flight, so no query load waits at the end.  One
+// barrier only: it publishes phi(q), and every wave has read the old z
+// before wave 0 writes the new one.
+template <typename T>
+__global__ __launch_bounds__(256) void k_decode128(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, int R, float* __restrict__ S,
+                                                   float* __restrict__ z, T* __restrict__ out) {
+  constexpr int D = 128, NJ = 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, cg = lane & 7, r0 = lane >> 3;
+  const int64_t bg = blockIdx.x;  // b * Hkv + g
+  const int col0 = 32 * w + 4 * cg;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(S + bg * D * D, 0, D * D * 4, 0x00020000);
+  f32x4 s4[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    s4[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((r0 + 8 * j) * D + col0) * 4, 0, 0));
+  float pk[NJ], zn[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    pk[j] = phi_f(to_f(k[bg * D + r0 + 8 * j]));
+    zn[j] = z[bg * D + r0 + 8 * j] + pk[j];  // z after this step's key
+  }
+  const f32x4 vb = {to_f(v[bg * D + col0]), to_f(v[bg * D + col0 + 1]), to_f(v[bg * D + col0 + 2]),
+                    to_f(v[bg * D + col0 + 3])};
+  extern __shared__ float pqs[];  // [R][D]: phi(q) of the group's query heads
+  const T* qg = q + bg * R * D;   // heads (b * Hkv + g) * R + r are contiguous
+#pragma unroll 4
+  for (int i = tid; i < R * D; i += 256) pqs[i] = phi_f(to_f(qg[i]));
+  __syncthreads();  // phi(q) staged; every wave has read the old z
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (cg == 0) z[bg * D + r0 + 8 * j] = zn[j];
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    s4[j] += pk[j] * vb;
+    typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_, s4[j]), rs, ((r0 + 8 * j) * D + col0) * 4, 0, 0);
+  }
+  for (int r = 0; r < R; ++r) {
+    const int64_t qh = bg * R + r;  // (b * Hkv + g) * R + r = b * Hq + g * R + r
+    f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float pq = pqs[r * D + r0 + 8 * j];
+      num += pq * s4[j];
+      den = fmaf(pq, zn[j], den);
+    }
+    // sum over the eight row groups (lane bits 3..5)
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] += __shfl_xor(num[e], off);
+      den += __shfl_xor(den, off);
+    }
+    if (r0 == 0) {
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[qh * D + col0 + e] = cvt<T>(num[e] * inv);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 template <typename T, int DP, int C>
 int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, int form) {
@@ -1571,8 +1642,7 @@ int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int R = (int)(Hq / Hkv);
   const dim3 grid((unsigned)(B * Hkv));
-#define LA_DEC4(DD)                                                                                           \
-  case DD:                                                                                                    \
+#define LA_DEC4_LAUNCH(DD)                                                                                    \
     if (dtype == 0)                                                                                           \
       k_decode4<float, DD><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k), \
                                                 reinterpret_cast<const float*>(v), R, S, z, reinterpret_cast<float*>(out)); \
@@ -1580,17 +1650,32 @@ int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_
       k_decode4<bf16, DD><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),   \
                                                reinterpret_cast<const bf16*>(v), R, S, z, reinterpret_cast<bf16*>(out)); \
     return (int)hipGetLastError();
+#define LA_DEC4(DD) \
+  case DD:          \
+    LA_DEC4_LAUNCH(DD)
+  constexpr int kDec128MaxR = 64;  // phi(q) staging of at most 32 KB of LDS
   switch (d) {
     LA_DEC4(4)
     LA_DEC4(8)
     LA_DEC4(16)
     LA_DEC4(32)
     LA_DEC4(64)
-    LA_DEC4(128)
+  case 128:
+    if (R > kDec128MaxR) {
+      LA_DEC4_LAUNCH(128)
+    }
+    if (dtype == 0)
+      k_decode128<float><<<grid, 256, R * 128 * 4, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
+                                              reinterpret_cast<const float*>(v), R, S, z, reinterpret_cast<float*>(out));
+    else
+      k_decode128<bf16><<<grid, 256, R * 128 * 4, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
+                                             reinterpret_cast<const bf16*>(v), R, S, z, reinterpret_cast<bf16*>(out));
+    return (int)hipGetLastError();
     default:
       break;
   }
 #undef LA_DEC4
+#undef LA_DEC4_LAUNCH
   if (dtype == 0)
     k_decode<float><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
                                          reinterpret_cast<const float*>(v), (int)d, R, S, z,

@@ -200,6 +200,24 @@ def test_decode_head_dims(gpu, dtype, d):
     np.testing.assert_allclose(z.cpu().numpy(), zf, rtol=1e-5)
 
 
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (6, 3), (64, 1), (65, 1)])
+def test_decode_d128_group_sizes(gpu, dtype, Hq, Hkv):
+    """Decode at d = 128 over query-group sizes R = Hq / Hkv: 1, 2, 64 (the
+    largest group whose phi(q) the step stages in LDS) and 65 (past it, the
+    step with per-head LDS reductions)."""
+    B, n, T, d = 2, 24, 2, 128
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=5 + Hq, scaled=True)
+    full, Sf, zf = oracle.causal(q, k, v, want_state=True)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    S, z = gpu.la_causal_forward(None, kd[:, :, :n - T].contiguous(), vd[:, :, :n - T].contiguous(), Hq=Hq)
+    for t in range(n - T, n):
+        o = gpu.la_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), S, z)
+        check(host(o), full[:, :, t], dtype, f"decode Hq={Hq} Hkv={Hkv} step {t}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sf, rtol=1e-4, atol=1e-4 * np.abs(Sf).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zf, rtol=1e-5)
+
+
 def test_state_only_matches_full_pass(gpu):
     q, k, v, _ = li.qkv(2, 4, 2, 300, 64, li.BF16, seed=7, scaled=True)
     _, S1, z1 = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True)
