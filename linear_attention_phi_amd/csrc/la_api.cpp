@@ -205,8 +205,8 @@ la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream};
   if (forward_bf16_applies(n, d, (int)dtype)) {
-    if (B * Hq * forward_bf16_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
-    return launch_forward_bf16(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
+    if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
+    return launch_forward_bf16(a, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   if (forward_f32_applies(n, d, (int)dtype)) {
     if (B * Hq * forward_f32_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;

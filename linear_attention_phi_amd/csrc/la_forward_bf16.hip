@@ -3,22 +3,35 @@
 // out_i = phi(Q_i) S / (phi(Q_i) . z) with S = sum_j phi(K_j) (x) V_j and
 // z = sum_j phi(K_j) over all n keys of the query's key/value head
 // (nx_f32_linear_attention.nx: "accumulate KV-summary" and "per-query"
-// loops; LinearTile 1.0.1, "How It Works": K^T V once, then Q).  Three
-// launches, each streaming its data once with one wave per 64-token chunk:
+// loops; LinearTile 1.0.1, "How It Works": K^T V once, then Q).  One launch
+// whose workgroups take one of three roles by their index, streaming the
+// data once with one wave per 64-token chunk:
 //
-//  k_fwd_state   a workgroup of four waves owns four chunks of one key/value
-//                head; each wave forms its chunk's relu(K)^T V on MFMA (fp32,
-//                transposed operands from LDS with ds_read_b64_tr_b16), the
-//                column sums of V and z; the workgroup sums its four chunks
-//                in LDS and writes one partial (S^T [b][a] fp32, then z);
-//  k_fwd_reduce  sums each head's partials in segment order (one 16-byte
-//                slice per thread, so the result does not depend on timing)
-//                and stores S^T as bf16 in MFMA operand order and z as bf16
-//                (high, low) pairs;
-//  k_fwd_out     one wave per chunk of queries: phi(Q) fragments straight
-//                from HBM, num = phi(Q) S and phi(Q) . z on MFMA, division,
-//                rows staged through LDS and stored whole with non-temporal
-//                stores.
+//  state    (the first NKV * nseg workgroups) a workgroup of four waves owns
+//           four chunks of one key/value head; each wave forms its chunk's
+//           relu(K)^T V on MFMA (fp32, transposed operands from LDS with
+//           ds_read_b64_tr_b16), the column sums of V and z; the workgroup
+//           sums its four chunks in LDS and publishes one partial (S^T [b][a]
+//           fp32, then z);
+//  reduce   (the next NKV * RED_BLOCKS) once a head's partials are all
+//           published, sums them in segment order (one lane slot per
+//           thread, so the result does not depend on timing) and publishes
+//           S^T as bf16 in MFMA operand order and z as bf16 (high, low) pairs;
+//  output   (the rest) one wave per two chunks of queries, so that at the
+//           common shapes the whole grid is resident at once (two
+//           workgroups per CU): its Q fragments are requested straight from
+//           HBM at once, so they stream while the state is formed; once the
+//           head's total is published, per chunk: num =
+//           phi(Q) S and phi(Q) . z on MFMA, division, rows staged through
+//           LDS and stored whole with non-temporal stores.
+//
+// A workgroup only waits for workgroups of lower index, which are
+// dispatched before it.  Published data goes through memory with
+// device-scope (sc1) stores and loads, and each publication is announced
+// by a 64-bit flag set to the call's epoch (a NaN pattern that no value the
+// workspace held before can equal) once the data stores have completed.
+// Spins are bounded; exhausting the bound records an error bit instead of
+// hanging.
 //
 // phi(K)^T V is formed as relu(K)^T V + 1 (x) sum_t V_t and z as
 // sum_t relu(K_t) + (number of keys), exactly as in the causal kernels.
@@ -34,25 +47,56 @@ namespace {
 using namespace la_dev;
 using namespace la_bf16;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int FD = 64;                     // head dim
 constexpr int FC = 64;                     // chunk
 constexpr int W = la_internal::kFwdSegChunks;  // chunks per state workgroup = waves
+constexpr int OC = 2;                      // chunks per output wave
 constexpr int WNT = 64 * W;                // threads per workgroup
 constexpr int RS = FD + 8;                 // row stride (bf16) of the token-major tiles: 144 bytes
 constexpr int RSF = FD + 4;                // row stride (fp32) of the state tiles: 272 bytes
 constexpr int TILE_B = FC * RS * 2;        // bytes of one token-major bf16 tile
 constexpr int REGION_B = 2 * TILE_B;       // one wave's LDS region (state kernel)
-constexpr int PART_FLOATS = FD * FD + FD;  // one partial: S^T [b][a], then z
-constexpr int TOT_BYTES = FD * FD * 2 + FD * 4;  // one total: S^T bf16, then z high and low pairs
+// S^T is published in MFMA operand order: fragment (nb, kb) -- rows b = 32 nb
+// + 0..31, features a = 16 kb + 0..15 -- is a block of 64 lane slots, lane
+// r + 32 h holding b = 32 nb + r, a = 16 kb + 8 h .. + 7.  A partial keeps
+// each slot's 8 floats as two 16-byte halves in separate 1 KB blocks
+// ((fragment, half) blocks of 64 lanes), the total keeps 8 bf16 per slot; so
+// every store and load instruction of a wave covers 1 KB contiguously.
+constexpr int PART_FLOATS = FD * FD + FD;  // one partial: S^T slots, then z
+constexpr int TOT_BYTES = FD * FD * 2 + FD * 4;  // one total: S^T bf16 slots, then z high and low pairs
 constexpr int RED_THREADS = 256;
-constexpr int RED_BLOCKS = (PART_FLOATS / 4 + RED_THREADS - 1) / RED_THREADS;  // blocks per head
+constexpr int RED_S_BLOCKS = FD * FD / 8 / RED_THREADS;  // reduce workgroups per head for S^T (a slot each)
+constexpr int RED_BLOCKS = RED_S_BLOCKS + 1;               // and one for z
+constexpr int RED_BATCH = 16;                              // segments' loads in flight per reduce step
 
 struct FwdArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* out;
-  int64_t n, nchunks, nseg, NKV, NQ, R;
-  float* part;    // [NKV][nseg][PART_FLOATS]
-  uint8_t* tot;   // [NKV][TOT_BYTES]
+  int64_t n, nchunks, nseg, NKV, NQ, R;  // nseg: state workgroups per head
+  float* part;      // [NKV][nseg][PART_FLOATS]
+  uint8_t* tot;     // [NKV][TOT_BYTES]
+  uint64_t* sflag;  // [NKV][nseg]: the segment's partial is published
+  uint64_t* rflag;  // [NKV][RED_BLOCKS]: the slice of the head's total is published
+  uint32_t* err;    // bit 0: a wait ran out of spins
+  uint64_t epoch;
 };
+
+// Every lane of the calling wave spins until flags[0 .. cnt) all hold the
+// call's epoch, then orders its later loads after the flags.
+__device__ __forceinline__ void wait_epoch(const uint64_t* flags, int64_t cnt, const FwdArgs& A, int lane) {
+  for (int64_t p = lane; p < cnt; p += 64) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(flags + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != A.epoch) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > (1u << 22)) {
+        atomicOr(A.err, 1u);
+        break;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 struct StateLds {
   uint8_t reg[W][REGION_B];  // relu(K), V tiles; then the chunk's state dS^T [b][a] in fp32
@@ -65,10 +109,9 @@ __device__ __forceinline__ float* state_row(StateLds& L, int c, int b) {
   return reinterpret_cast<float*>(L.reg[c] + (b < 32 ? TILE_B : 0)) + (b & 31) * RSF;
 }
 
-__global__ __launch_bounds__(WNT) void k_fwd_state(FwdArgs A) {
-  __shared__ __attribute__((aligned(16))) StateLds L;
+__device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int64_t seg = blockIdx.x / A.NKV, head = blockIdx.x % A.NKV;
+  const int64_t seg = bid / A.NKV, head = bid % A.NKV;
   const int hbytes = (int)(A.n * FD * 2);  // one head's rows (n <= 2^24)
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.k + head * A.n * FD), 0, hbytes, 0x00020000);
@@ -151,143 +194,208 @@ __global__ __launch_bounds__(WNT) void k_fwd_state(FwdArgs A) {
   }
   __syncthreads();
 
-  // The segment's partial: wave w sums rows b = 16 w + lane / 4, features
-  // a0 .. a0 + 15 over its chunks (plus the ones^T V part), wave 0 also z.
-  const int sb = 16 * w + (lane >> 2), sa = 16 * (lane & 3);
-  float run[16];
+  // The segment's partial: thread (w, lane) sums the lane slots of
+  // fragments w and w + 4 -- rows b = 32 i + r (i = 0, 1), features a = 16 w
+  // + 8 h .. + 7 -- over its chunks (plus the ones^T V part), wave 0 also z.
+  float run[2][8];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) run[e] = 0.0f;
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) run[i][e] = 0.0f;
   float zrun = 0.0f;
 #pragma unroll
   for (int c = 0; c < W; ++c) {
     if (c < ncl) {
-      const f32x4v* src = reinterpret_cast<const f32x4v*>(state_row(L, c, sb) + sa);
-      const float cs = L.vsum[c][sb];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4v x = src[j];
+      for (int i = 0; i < 2; ++i) {
+        const f32x4v* src = reinterpret_cast<const f32x4v*>(state_row(L, c, 32 * i + r) + 16 * w + 8 * h);
+        const float cs = L.vsum[c][32 * i + r];
+        const f32x4v x0 = src[0], x1 = src[1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) run[4 * j + e] += x[e] + cs;
+        for (int e = 0; e < 4; ++e) {
+          run[i][e] += x0[e] + cs;
+          run[i][4 + e] += x1[e] + cs;
+        }
       }
       zrun += L.zloc[c][lane];
     }
   }
-  // non-temporal: the partials are read once, by the next launch, and would
-  // otherwise wait in L2 as dirty lines for the write-back at the kernel's end
-  float* dst = A.part + (head * A.nseg + seg) * PART_FLOATS;
-  f32x4v* d4 = reinterpret_cast<f32x4v*>(dst + sb * FD + sa);
+  // publish: device-scope stores, completed before the barrier, then the flag
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      A.part + (head * A.nseg + seg) * PART_FLOATS, 0, PART_FLOATS * 4, 0x00020000);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_nontemporal_store(f32x4v{run[4 * j], run[4 * j + 1], run[4 * j + 2], run[4 * j + 3]}, d4 + j);
-  if (w == 0) __builtin_nontemporal_store(zrun, dst + FD * FD + lane);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      st_buf<CPOL_SC1>(rp, (((w + 4 * i) * 2 + hf) * 64 + lane) * 16,
+                       f32x4v{run[i][4 * hf], run[i][4 * hf + 1], run[i][4 * hf + 2], run[i][4 * hf + 3]});
+  if (w == 0) st_buf1<CPOL_SC1>(rp, (FD * FD + lane) * 4, zrun);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(A.sflag + head * A.nseg + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Thread t of a head's RED_BLOCKS * RED_THREADS handles floats 4 t .. 4 t + 3
 // of a partial (S^T [b][a] for 4 t < FD * FD, else z).
-__global__ __launch_bounds__(RED_THREADS) void k_fwd_reduce(FwdArgs A) {
-  const int64_t head = blockIdx.x / RED_BLOCKS;
-  const int t = (int)(blockIdx.x % RED_BLOCKS) * RED_THREADS + threadIdx.x;
-  if (4 * t >= PART_FLOATS) return;
-  const float* src = A.part + head * A.nseg * PART_FLOATS + 4 * t;
-  f32x4v s = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
-  int64_t p = 0;
-  for (; p + 8 <= A.nseg; p += 8) {
-    f32x4v x[8];
+__device__ __forceinline__ void fwd_reduce(const FwdArgs& A, int64_t bid) {
+  const int64_t head = bid / RED_BLOCKS, slice = bid % RED_BLOCKS;
+  wait_epoch(A.sflag + head * A.nseg, A.nseg, A, threadIdx.x & 63);
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      A.part + head * A.nseg * PART_FLOATS, 0, (int)(A.nseg * PART_FLOATS * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rt =
+      __builtin_amdgcn_make_buffer_rsrc(A.tot + head * TOT_BYTES, 0, TOT_BYTES, 0x00020000);
+  // past every head's partials (nseg * PART_FLOATS * 4 < 2^30 bytes): reads
+  // as zero, and adding a slot's offset cannot overflow
+  constexpr int OOB = 1 << 30;
+  static_assert((la_internal::kFwdMaxN / (FC * W) + 1) * PART_FLOATS * 4 < (1 << 30), "partials below 2^30 bytes");
+  if (slice < RED_S_BLOCKS) {
+    // lane slot t of S^T: fragment t / 64, lane t % 64; its two halves
+    const int t = (int)slice * RED_THREADS + threadIdx.x;
+    const int o0 = ((t >> 6) * 2 * 64 + (t & 63)) * 16, o1 = o0 + 64 * 16;
+    // up to RED_BATCH segments' loads in flight, summed in segment order
+    f32x4v s0 = f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
+    for (int64_t p = 0; p < A.nseg; p += RED_BATCH) {
+      f32x4v x[RED_BATCH][2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const f32x4v*>(src + (p + u) * PART_FLOATS);
+      for (int u = 0; u < RED_BATCH; ++u) {
+        const int base = p + u < A.nseg ? (int)((p + u) * PART_FLOATS * 4) : OOB;
+        x[u][0] = ld_buf<CPOL_SC1>(rp, base + o0);
+        x[u][1] = ld_buf<CPOL_SC1>(rp, base + o1);
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += x[u];
-  }
-  for (; p < A.nseg; ++p) s += *reinterpret_cast<const f32x4v*>(src + p * PART_FLOATS);
-  uint8_t* tot = A.tot + head * TOT_BYTES;
-  if (4 * t < FD * FD) {
-    *reinterpret_cast<uint2*>(tot + 8 * t) = make_uint2(pack2(s[0], s[1]), pack2(s[2], s[3]));
-  } else {
+      for (int u = 0; u < RED_BATCH; ++u) {
+        s0 += x[u][0];
+        s1 += x[u][1];
+      }
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{pack2(s0[0], s0[1]), pack2(s0[2], s0[3]), pack2(s1[0], s1[1]), pack2(s1[2], s1[3])}, rt, t * 16, 0,
+        CPOL_SC1);
+  } else if (threadIdx.x < FD / 4) {
     // z as (high, low) bf16 pairs: z = high + low to about 2^-17
-    const int a = 4 * t - FD * FD;
-    uint32_t* zh = reinterpret_cast<uint32_t*>(tot + FD * FD * 2);
-    uint32_t* zl = zh + FD / 2;
+    const int a = 4 * (int)threadIdx.x;
+    f32x4v zs = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t p = 0; p < A.nseg; p += RED_BATCH) {
+      f32x4v x[RED_BATCH];
+#pragma unroll
+      for (int u = 0; u < RED_BATCH; ++u)
+        x[u] = ld_buf<CPOL_SC1>(rp, p + u < A.nseg ? (int)(((p + u) * PART_FLOATS + FD * FD + a) * 4) : OOB);
+#pragma unroll
+      for (int u = 0; u < RED_BATCH; ++u) zs += x[u];
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t hi = pack2(s[2 * j], s[2 * j + 1]);
-      zh[a / 2 + j] = hi;
-      zl[a / 2 + j] = pack2(s[2 * j] - lo_f(hi), s[2 * j + 1] - hi_f(hi));
+      const uint32_t hi = pack2(zs[2 * j], zs[2 * j + 1]);
+      const uint32_t lo = pack2(zs[2 * j] - lo_f(hi), zs[2 * j + 1] - hi_f(hi));
+      __builtin_amdgcn_raw_buffer_store_b32(hi, rt, FD * FD * 2 + (a / 2 + j) * 4, 0, CPOL_SC1);
+      __builtin_amdgcn_raw_buffer_store_b32(lo, rt, FD * FD * 2 + FD * 2 + (a / 2 + j) * 4, 0, CPOL_SC1);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(A.rflag + head * RED_BLOCKS + slice, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(WNT) void k_fwd_out(FwdArgs A) {
-  __shared__ __attribute__((aligned(16))) uint8_t Lout[W][TILE_B];
+__device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (&Lout)[W][TILE_B]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int64_t seg = blockIdx.x / A.NQ, qh = blockIdx.x % A.NQ, kvh = qh / A.R;
-  const int64_t c = seg * W + w;
-  if (c >= A.nchunks) return;  // no barrier below: a wave without a chunk leaves
-  const int t0 = (int)(c * FC);
+  const int64_t seg = bid / A.NQ, qh = bid % A.NQ, kvh = qh / A.R;
+  const int64_t c0 = (seg * W + w) * OC;  // this wave's first chunk
+  if (c0 >= A.nchunks) return;            // no barrier below: a wave without a chunk leaves
   const int hbytes = (int)(A.n * FD * 2);
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + qh * A.n * FD), 0, hbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(A.out + qh * A.n * FD, 0, hbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(A.tot + kvh * TOT_BYTES, 0, TOT_BYTES, 0x00020000);
   constexpr int OOB = 0x7FFFFFF0;  // past num_records: reads as zero
-  // phi(Q) (query block ib, feature block kb), S^T (feature block nb, kb) and
-  // the z operand (row 0: high parts, row 16: low parts, other rows zero)
-  // every load is issued before phi is applied to Q (left to itself the
-  // compiler waits for each Q fragment before issuing the next)
-  u32x4 qraw[2][4];
+  // phi(Q) (chunk j, query block ib, feature block kb), S^T (feature block
+  // nb, kb) and the z operand (row 0: high parts, row 16: low parts, other
+  // rows zero).  Q of both chunks is requested first, before the wait for
+  // the head's total (rows past the sequence end read as zero); the total's
+  // loads are all issued before phi is applied to Q (left to itself the
+  // compiler waits for each fragment before issuing the next)
+  u32x4 qraw[OC][2][4];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
+  for (int j = 0; j < OC; ++j)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      qraw[ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((t0 + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
-  Frag<bf16> qf[2][4], sf[2][4], zf[4];
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        qraw[j][ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(
+            rq, (((int)(c0 + j) * FC + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_epoch(A.rflag + kvh * RED_BLOCKS, RED_BLOCKS, A, lane);
+  Frag<bf16> sf[2][4], zf[4];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
       sf[nb][kb].v = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rt, ((32 * nb + r) * FD + 16 * kb + 8 * h) * 2, 0, 0));
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rt, ((nb * 4 + kb) * 64 + lane) * 16, 0, CPOL_SC1));
   const int zrow = r == 0 ? FD * FD * 2 : (r == 16 ? FD * FD * 2 + FD * 2 : -1);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
     zf[kb].v = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rt, zrow < 0 ? OOB : zrow + (16 * kb + 8 * h) * 2, 0, 0));
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rt, zrow < 0 ? OOB : zrow + (16 * kb + 8 * h) * 2, 0, CPOL_SC1));
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4 x = qraw[ib][kb];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
-      qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
-    }
 
   bf16* tO = reinterpret_cast<bf16*>(Lout[w]);
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
-    f32x16 zacc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma(zacc, zf[kb], qf[ib][kb]);
-    const float inv = __builtin_amdgcn_rcpf(__shfl(zacc[0] + zacc[8], r));  // from the lane with h == 0
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      f32x16 o = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma(o, sf[nb][kb], qf[ib][kb]);
-      uint2* dst = reinterpret_cast<uint2*>(tO + (32 * ib + r) * RS + 32 * nb + 4 * h);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[2 * q] = make_uint2(pack2(o[4 * q] * inv, o[4 * q + 1] * inv), pack2(o[4 * q + 2] * inv, o[4 * q + 3] * inv));
-    }
-  }
-  wave_lds_sync();
-  // whole 128-byte rows, 16 bytes per lane; rows past the sequence end fall
-  // outside the bounded resource and are dropped
   const int prow = lane >> 3, pcol = 8 * (lane & 7);
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
-                                           ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, CPOL_NT);
+  for (int j = 0; j < OC; ++j) {
+    const int t0 = (int)(c0 + j) * FC;
+    Frag<bf16> qf[2][4];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4 x = qraw[j][ib][kb];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = phi2(x[e]);
+        qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
+      }
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      f32x16 zacc = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(zacc, zf[kb], qf[ib][kb]);
+      const float inv = __builtin_amdgcn_rcpf(__shfl(zacc[0] + zacc[8], r));  // from the lane with h == 0
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x16 o = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(o, sf[nb][kb], qf[ib][kb]);
+        uint2* dst = reinterpret_cast<uint2*>(tO + (32 * ib + r) * RS + 32 * nb + 4 * h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dst[2 * q] = make_uint2(pack2(o[4 * q] * inv, o[4 * q + 1] * inv), pack2(o[4 * q + 2] * inv, o[4 * q + 3] * inv));
+      }
+    }
+    wave_lds_sync();
+    // whole 128-byte rows, 16 bytes per lane; rows past the sequence end fall
+    // outside the bounded resource and are dropped (the wave's LDS accesses
+    // run in order, so the next chunk's tile writes follow these reads)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
+                                             ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, CPOL_NT);
+  }
+}
+
+union FwdLds {
+  StateLds state;
+  uint8_t out[W][TILE_B];
+};
+
+__global__ __launch_bounds__(WNT) void k_fwd_one(FwdArgs A) {
+  __shared__ __attribute__((aligned(16))) FwdLds L;
+  const int64_t nS = A.NKV * A.nseg, nR = A.NKV * RED_BLOCKS, b = blockIdx.x;
+  if (b < nS)
+    fwd_state(A, b, L.state);
+  else if (b < nS + nR)
+    fwd_reduce(A, b - nS);
+  else
+    fwd_out(A, b - nS - nR, L.out);
 }
 
 }  // namespace
@@ -300,22 +408,32 @@ bool forward_bf16_applies(int64_t n, int64_t d, int dtype) {
 
 int64_t forward_bf16_nseg(int64_t n) { return ((n + FC - 1) / FC + W - 1) / W; }
 
-size_t forward_bf16_ws_bytes(int64_t NKV, int64_t nseg) {
-  return (size_t)NKV * nseg * PART_FLOATS * sizeof(float) + (size_t)NKV * TOT_BYTES + 256;
+int64_t forward_bf16_grid(int64_t NKV, int64_t NQ, int64_t n) {
+  const int64_t nchunks = (n + FC - 1) / FC;
+  return NKV * forward_bf16_nseg(n) + NKV * RED_BLOCKS + NQ * ((nchunks + W * OC - 1) / (W * OC));
 }
 
-int launch_forward_bf16(const Fwd& a) {
+size_t forward_bf16_ws_bytes(int64_t NKV, int64_t nseg) {
+  return (size_t)NKV * nseg * PART_FLOATS * sizeof(float) + (size_t)NKV * TOT_BYTES +
+         (size_t)NKV * (nseg + RED_BLOCKS) * sizeof(uint64_t) + 256;
+}
+
+int launch_forward_bf16(const Fwd& a, uint64_t epoch) {
+  static_assert(RED_THREADS == WNT, "one block size for every role");
+  static_assert(RED_S_BLOCKS * RED_THREADS * 8 == FD * FD && FD / 4 <= RED_THREADS, "reduce slices");
+  static_assert(TOT_BYTES % 16 == 0 && (PART_FLOATS * 4) % 16 == 0, "workspace alignment");
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const int64_t NKV = a.B * a.Hkv, NQ = a.B * a.Hq;
   const int64_t nchunks = (a.n + FC - 1) / FC, nseg = forward_bf16_nseg(a.n);
   float* part = reinterpret_cast<float*>(a.ws);
   uint8_t* tot = reinterpret_cast<uint8_t*>(part + NKV * nseg * PART_FLOATS);
+  uint64_t* sflag = reinterpret_cast<uint64_t*>(tot + NKV * TOT_BYTES);
+  uint64_t* rflag = sflag + NKV * nseg;
+  uint32_t* err = reinterpret_cast<uint32_t*>(rflag + NKV * RED_BLOCKS);
   FwdArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
             reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, nchunks, nseg, NKV, NQ,
-            a.Hq / a.Hkv, part, tot};
-  k_fwd_state<<<dim3((unsigned)(NKV * nseg)), WNT, 0, st>>>(A);
-  k_fwd_reduce<<<dim3((unsigned)(NKV * RED_BLOCKS)), RED_THREADS, 0, st>>>(A);
-  k_fwd_out<<<dim3((unsigned)(NQ * nseg)), WNT, 0, st>>>(A);
+            a.Hq / a.Hkv, part, tot, sflag, rflag, err, epoch};
+  k_fwd_one<<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
   return (int)hipGetLastError();
 }
 

@@ -64,8 +64,9 @@ bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dty
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg);
 int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch);
 
-// Non-causal path for bf16, d = 64 (la_forward_bf16.hip): state partials per
-// segment of kFwdSegChunks chunks, a reduce, then the output pass.
+// Non-causal path for bf16, d = 64 (la_forward_bf16.hip): one launch; state
+// partials per segment of kFwdSegChunks chunks, a reduce, then the output
+// pass, ordered by flags that carry the call's epoch.
 constexpr int kFwdSegChunks = 4;
 // n bound: one head's rows, padded to a whole segment, stay below 2^31 bytes
 // (the range of a buffer resource's record count and offsets).
@@ -73,7 +74,8 @@ constexpr int64_t kFwdMaxN = (int64_t)1 << 23;
 bool forward_bf16_applies(int64_t n, int64_t d, int dtype);
 int64_t forward_bf16_nseg(int64_t n);
 size_t forward_bf16_ws_bytes(int64_t NKV, int64_t nseg);
-int launch_forward_bf16(const Fwd& a);
+int64_t forward_bf16_grid(int64_t NKV, int64_t NQ, int64_t n);
+int launch_forward_bf16(const Fwd& a, uint64_t epoch);
 
 // Non-causal path for fp32, d = 64 (la_forward_f32.hip): state partials per
 // segment of kFwd32SegTokens keys, a reduce, then the output pass.
