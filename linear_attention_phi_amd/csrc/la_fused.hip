@@ -285,14 +285,17 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   }
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(A.agg + head * A.nseg * AGG_FLOATS, 0, (int)(A.nseg * AGG_FLOATS * 4), 0x00020000);
-  const int soff = (sb * FD + sa) * 4;   // byte offset of this lane's slice in an aggregate
+  // A lane's slice of an aggregate (rows sb, features sa .. sa + 7) is kept as
+  // two 16-byte halves 1 KB apart, so that each of a wave's store and load
+  // instructions covers 1 KB contiguously
+  const int soff = (w * 128 + lane) * 16;  // byte offset of this lane's first half in an aggregate
   const int zoff = FD * FD * 4;          // byte offset of z in an aggregate
   const bool publish = seg + 1 < A.nseg;  // the last segment has no successor
   uint64_t* flag = A.flags + head * A.nseg;
   if (publish) {
     const int base = (int)(seg * AGG_FLOATS * 4);
     st_buf<CPOL_SC1>(rs, base + soff, f32x4v{run[0], run[1], run[2], run[3]});
-    st_buf<CPOL_SC1>(rs, base + soff + 16, f32x4v{run[4], run[5], run[6], run[7]});
+    st_buf<CPOL_SC1>(rs, base + soff + 1024, f32x4v{run[4], run[5], run[6], run[7]});
     if (w == 0) st_buf1<CPOL_SC1>(rs, base + zoff + lane * 4, zrun);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's aggregate stores have completed
   }
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       if (p + u < seg) {
         const int base = (int)((p + u) * AGG_FLOATS * 4);
         x[u][0] = ld_buf<CPOL_SC1>(rs, base + soff);
-        x[u][1] = ld_buf<CPOL_SC1>(rs, base + soff + 16);
+        x[u][1] = ld_buf<CPOL_SC1>(rs, base + soff + 1024);
         zx[u] = w == 0 ? ld_buf1<CPOL_SC1>(rs, base + zoff + lane * 4) : 0.0f;
       }
     }
