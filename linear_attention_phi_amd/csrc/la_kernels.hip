@@ -224,8 +224,11 @@ __global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, con
 // ------------------------------------------------------------------- k_scan
 // One thread per state element of one head: exclusive prefix over segments
 // in place, total into slot nseg, and the caller's final state if asked.
+// Only the prefixes of segments s with s % F == 0 are stored (the output
+// launch that follows starts a workgroup at every F-th segment); the total
+// always is.
 __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nseg, int DP, int d,
-                                             float* __restrict__ S_final, float* __restrict__ z_final) {
+                                             float* __restrict__ S_final, float* __restrict__ z_final, int64_t F) {
   const int64_t E = slot_elems(DP);
   const int64_t bh = blockIdx.x;
   const int64_t e = (int64_t)blockIdx.y * NT + threadIdx.x;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 #pragma unroll
     for (int u = 0; u < BLK; ++u) {
       if (s0 + u < nseg) {
-        base[(s0 + u) * E] = run;
+        if ((s0 + u) % F == 0) base[(s0 + u) * E] = run;
         run += x[u];
       }
     }
@@ -288,6 +291,12 @@ constexpr int PX_RS = 64 + 4;  // row stride (floats) of the LDS tiles
 // each other's barriers) measured 146.9 / 179.3 us at B4 H8 n8192 (m = arange
 // / uniform) against 162.7 / 190.9 us for eight.
 constexpr int PX_NWV = 4;
+// Workgroups of the GQA output launch (one per CU): each walks the chunks of
+// several state segments.
+#ifndef LA_GQA_OUT_GROUPS
+#define LA_GQA_OUT_GROUPS 256
+#endif
+constexpr int64_t kGqaOutGroups = LA_GQA_OUT_GROUPS;
 template <int NWV>
 __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ v, float* __restrict__ out, int64_t n,
@@ -769,11 +778,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
 // V^T P^T, both operands of relu(K)^T V) are transposed reads, and z and the
 // sums of V are dot2 sums over those fragments (waves 0-3: z of rows
 // 32 w .., waves 4-7: sums of V of columns 32 (w - 4) ..).
+// A workgroup walks F state segments (G chunks of the state pass each) and
+// starts from the exclusive prefix in slot F * seg of the workspace, whose
+// per-head stride is nseg_ws + 1 slots.
 template <int R>
 __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                  const bf16* __restrict__ v, bf16* __restrict__ out, int64_t n,
-                                                 int64_t nchunks, int64_t G, int64_t nseg,
-                                                 const float* __restrict__ ws) {
+                                                 int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
+                                                 int64_t nseg_ws, const float* __restrict__ ws) {
   constexpr int DP = 128, C = 32;
   constexpr int LQ = DP + PAD;  // row stride of sK, sQ, sO, sST
   constexpr int RS = STR_RS;    // row stride of sKr, sV (conflict-free transposed reads)
@@ -797,16 +809,14 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const bf16* kb = k + bh * n * DP;
   const bf16* vb = v + bh * n * DP;
+  const float* slot = ws + (bh * (nseg_ws + 1) + F * seg) * slot_elems(DP);
 
   // state blocks e = w and w + 8: (row block ma, column block nb) = (e / 4, e % 4)
   f32x16 accS[2];
-  {
-    const float* src = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) ld_state_block<DP>(accS[s], src, (w + 8 * s) / 4, (w + 8 * s) % 4, lane);
-  }
+  for (int s = 0; s < 2; ++s) ld_state_block<DP>(accS[s], slot, (w + 8 * s) / 4, (w + 8 * s) % 4, lane);
   float zrun = 0.0f, vrun = 0.0f;  // waves 0-3: z[32 w + r]; waves 4-7: sum of V[., 32 (w - 4) + r]
-  if (w < 4) zrun = ws[(bh * (nseg + 1) + seg) * slot_elems(DP) + DP * DP + 32 * w + r];
+  if (w < 4) zrun = slot[DP * DP + 32 * w + r];
   if (tid < DP) {
     svc[tid] = 0.0f;
     szero[tid] = (bf16)0.0f;
@@ -1543,15 +1553,26 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   else
     k_state<T, DP, C, false><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   const int64_t E = slot_elems(DP);
-  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final, a.z_final);
+  // the GQA output kernel: F state segments per workgroup, so that about
+  // kGqaOutGroups workgroups (one per CU) each walk a longer run of chunks
+  bool gqa_out = false;
+  if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
+    gqa_out = q && out && form == CAUSAL && vec && (R == 2 || R == 4);
+  int64_t F = gqa_out ? nbh * p.nseg / kGqaOutGroups : 1;
+  if (F < 1) F = 1;
+  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final,
+                                                                          a.z_final, F);
   if (q && out) {
     if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
-      if (form == CAUSAL && vec && (R == 2 || R == 4)) {
+      if (gqa_out) {
         const bf16* qq = reinterpret_cast<const bf16*>(q);
+        const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
         if (R == 2)
-          k_out_gqa<2><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, p.G, p.nseg, states);
+          k_out_gqa<2><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
+                                                                        p.nseg, states);
         else
-          k_out_gqa<4><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, p.G, p.nseg, states);
+          k_out_gqa<4><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
+                                                                        p.nseg, states);
         return (int)hipGetLastError();
       }
     }
@@ -1583,7 +1604,7 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   T* out = reinterpret_cast<T*>(a.out);
   k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   const int64_t E = slot_elems(DP);
-  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr);
+  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr, 1);
   // query runs: about 1024 workgroups in total for 2-byte inputs (several per
   // CU keep more query tiles in flight), about 256 for 4-byte inputs (longer
   // runs, each loading its next, twice as large, tile while it computes)
