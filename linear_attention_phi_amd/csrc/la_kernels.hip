@@ -297,11 +297,17 @@ constexpr int PX_NWV = 4;
 #define LA_GQA_OUT_GROUPS 256
 #endif
 constexpr int64_t kGqaOutGroups = LA_GQA_OUT_GROUPS;
+// Workgroups of the fp32 prefix-form output launch (two per CU).
+#ifndef LA_PREFIX_OUT_GROUPS
+#define LA_PREFIX_OUT_GROUPS 512
+#endif
+constexpr int64_t kPrefixOutGroups = LA_PREFIX_OUT_GROUPS;
 template <int NWV>
 __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ v, float* __restrict__ out, int64_t n,
-                                                      int64_t nchunks, int64_t G, int64_t nseg,
-                                                      const float* __restrict__ ws, const int* __restrict__ perm,
+                                                      int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
+                                                      int64_t nseg_ws, const float* __restrict__ ws,
+                                                      const int* __restrict__ perm,
                                                       const int* __restrict__ boff, const int64_t* __restrict__ m) {
   constexpr int FD = 64, C = 64, RS = PX_RS, QG = 16 * NWV, NT_ = 64 * NWV;
   constexpr int KVP = C * FD / 4 / NT_;  // 16-byte pieces of a K or V tile per thread
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   const int sj = w & 3;
   f32x4 accS[4];
   {
-    const float* src = ws + (bh * (nseg + 1) + seg) * slot_elems(FD);
+    const float* src = ws + (bh * (nseg_ws + 1) + F * seg) * slot_elems(FD);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1553,20 +1559,23 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   else
     k_state<T, DP, C, false><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   const int64_t E = slot_elems(DP);
-  // the GQA output kernel: F state segments per workgroup, so that about
-  // kGqaOutGroups workgroups (one per CU) each walk a longer run of chunks
-  bool gqa_out = false;
+  // the GQA and fp32 prefix output kernels: F state segments per
+  // workgroup, so that about kGqaOutGroups / kPrefixOutGroups workgroups
+  // (one / two per CU) each walk a longer run of chunks
+  bool gqa_out = false, px_out = false;
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
     gqa_out = q && out && form == CAUSAL && vec && (R == 2 || R == 4);
-  int64_t F = gqa_out ? nbh * p.nseg / kGqaOutGroups : 1;
+  if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64)
+    px_out = q && out && form == PREFIX && vec;
+  int64_t F = gqa_out ? nbh * p.nseg / kGqaOutGroups : px_out ? nbh * p.nseg / kPrefixOutGroups : 1;
   if (F < 1) F = 1;
+  const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final,
                                                                           a.z_final, F);
   if (q && out) {
     if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
       if (gqa_out) {
         const bf16* qq = reinterpret_cast<const bf16*>(q);
-        const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
         if (R == 2)
           k_out_gqa<2><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
                                                                         p.nseg, states);
@@ -1577,9 +1586,9 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
       }
     }
     if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
-      if (form == PREFIX && vec) {
-        k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * p.nseg)), 64 * PX_NWV, 0, st>>>(
-            q, k, v, out, a.n, p.nchunks, p.G, p.nseg, states, perm, boff, a.m);
+      if (px_out) {
+        k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
+            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, perm, boff, a.m);
         return (int)hipGetLastError();
       }
     }
