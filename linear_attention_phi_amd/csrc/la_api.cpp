@@ -24,11 +24,13 @@ int default_chunk(int elem_bytes, int DP) {
 // chunk that fits.
 static int forward_chunk(int elem_bytes, int DP) { return chunk_fits(elem_bytes, DP, 64) ? 64 : 32; }
 
-// Segments: about kTargetGroups workgroups per pass, so that the 256 CUs each
-// get several, while each workgroup still walks a run of chunks.  The
+// Segments: about kTargetGroups workgroups per state pass, so that the 256
+// CUs each get two, while each workgroup still walks a run of chunks and the
+// scan has few segment states to read (the output launches of the GQA and
+// prefix kernels group several segments per workgroup again).  The
 // non-causal form needs only the total state, so it takes longer segments
 // (about one workgroup per CU): fewer partial states to write and sum.
-static constexpr int64_t kTargetGroups = 1024;
+static constexpr int64_t kTargetGroups = 512;
 static constexpr int64_t kTargetGroupsForward = 256;
 
 Plan make_plan(int op, int64_t B, int64_t Hkv, int64_t n, int64_t d, int elem_bytes, int chunk) {
