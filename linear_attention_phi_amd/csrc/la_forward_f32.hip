@@ -168,14 +168,15 @@ __global__ __launch_bounds__(RED_THREADS) void k_fwd32_reduce(Fwd32Args A) {
   if (t >= PART_F / 4) return;
   const f32x4* src = reinterpret_cast<const f32x4*>(A.part + head * A.nseg * PART_F) + t;
   constexpr int STRIDE = PART_F / 4;
+  // sixteen segments' loads in flight, summed in segment order
   f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   int64_t p = 0;
-  for (; p + 8 <= A.nseg; p += 8) {
-    f32x4 x[8];
+  for (; p + 16 <= A.nseg; p += 16) {
+    f32x4 x[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = src[(p + u) * STRIDE];
+    for (int u = 0; u < 16; ++u) x[u] = src[(p + u) * STRIDE];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += x[u];
+    for (int u = 0; u < 16; ++u) s += x[u];
   }
   for (; p < A.nseg; ++p) s += src[p * STRIDE];
   float* tot = A.tot + head * PART_F;

@@ -83,7 +83,7 @@ SMALL = [
     (1, 4, 4, 129, 64, 128),
     (2, 8, 2, 200, 31, 32),
     (2, 4, 2, 1000, 64, 64),   # bf16 non-causal: state partials of several segments, GQA
-    (1, 2, 1, 4500, 64, 32),   # 18 segments: the reduce's batches of eight and a remainder
+    (1, 2, 1, 4500, 64, 32),   # 18 segments: the reduces' batches of sixteen and a remainder
     (1, 1, 1, 1, 64, 64),      # one token at d = 64
     (1, 4, 1, 300, 128, 32),   # bf16 causal: four query heads per chunk at once, ragged tail
     (2, 4, 2, 97, 128, 0),     # ... two query heads (default chunk 32)
@@ -101,6 +101,40 @@ def test_noncausal_small(gpu, dtype, case):
     q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=0)
     g = host(gpu.la_forward(dev(q), dev(k), dev(v)))
     check(g, oracle.forward(q, k, v), dtype, f"forward {_small_id(case)} {dtype}")
+
+
+@pytest.mark.parametrize("fill", ["random", "ones"])
+def test_workspace_contents_do_not_matter(gpu, fill):
+    """The kernels that hand data between workgroups (the non-causal passes,
+    the single-launch causal kernel, the prefix form's sort and state) read
+    no workspace word before this call wrote it: their flags must equal the
+    call's epoch, so a workspace holding random bytes or all-ones bytes gives
+    the same outputs as a zero-filled one."""
+    import torch
+    gen = torch.Generator(device="cpu").manual_seed(3)
+
+    def ws(op, B, Hq, Hkv, n, d, dt, chunk=0):
+        nbytes = gpu.la_workspace_bytes(op, B, Hq, Hkv, n, d, 1 if dt == li.BF16 else 0, chunk)
+        if fill == "random":
+            w = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=gen)
+        else:
+            w = torch.full((nbytes,), 255, dtype=torch.uint8)
+        return w.to("cuda")
+
+    for dtype in (li.BF16, li.F32):
+        B, Hq, Hkv, n, d = 2, 4, 2, 1000, 64
+        q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=4)
+        g = gpu.la_forward(dev(q), dev(k), dev(v), ws=ws(gpu.LA_OP_FORWARD, B, Hq, Hkv, n, d, dtype))
+        check(host(g), oracle.forward(q, k, v), dtype, f"forward {fill} workspace {dtype}")
+    B, H, n, d = 2, 2, 1000, 64
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.BF16, seed=5, scaled=True)
+    out = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64, ws=ws(gpu.LA_OP_CAUSAL, B, H, H, n, d, li.BF16, 64))
+    check(host(out), oracle.causal(q, k, v), li.BF16, f"causal {fill} workspace")
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=6, scaled=True)
+    m = li.mask(n, "random", rng=rng)
+    g = gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=64,
+                                   ws=ws(gpu.LA_OP_PREFIX_MASK, B, H, H, n, d, li.F32, 64))
+    check(host(g), oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {fill} workspace")
 
 
 @pytest.mark.parametrize("dtype", [li.F32, li.BF16])
