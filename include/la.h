@@ -38,10 +38,12 @@
  *   call only enqueues work on that stream and returns: no host
  *   synchronisation, no device allocation.
  * Workspace.  Forward calls take a device workspace of at least
- *   la_workspace_bytes(...) bytes.  It must be zero-filled before its first
- *   use with this library; every call leaves the words it synchronises on
- *   zero again, so one zero-fill at allocation suffices.  Two calls that run
- *   concurrently must not share a workspace.
+ *   la_workspace_bytes(...) bytes, owned by the caller.  Its contents before
+ *   a call do not matter (no zero-fill is needed): every word a call reads
+ *   there it wrote first, and the flags that order its workgroups must equal
+ *   a value new to that call.  One workspace may serve calls of every kind
+ *   and shape in turn (the library's workspace bytes for that shape at
+ *   least); two calls that run concurrently must not share a workspace.
  * Errors.  Every argument check runs on the host before anything is
  *   enqueued; on failure nothing is launched and a nonzero la_status is
  *   returned (0 means success, as the nx page's functions return 0).

@@ -103,8 +103,8 @@ _ws_cache: dict = {}
 
 
 def workspace(nbytes: int, device):
-    """A zero-filled device workspace of at least nbytes, cached per device.
-    The kernels leave it in a reusable state, so it is zeroed only when made."""
+    """A device workspace of at least nbytes, cached per device and shared by
+    every call on that device (its contents before a call do not matter)."""
     torch = _torch()
     key = (device.type, device.index)
     buf = _ws_cache.get(key)
