@@ -52,10 +52,10 @@ def _load():
         lib = ctypes.CDLL(LIB_PATH)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.lao_num_threads.restype = I
-        lib.lao_forward.argtypes = [P, P, P, I, I64, I64, I64, I64, I64, P, I64, P]
-        lib.lao_causal.argtypes = [P, P, P, I, I64, I64, I64, I64, I64, P, I64, P, P, P]
+        lib.lao_forward.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P]
+        lib.lao_causal.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P, P, P]
         lib.lao_prefix_mask.argtypes = [P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
-        lib.lao_decode_step.argtypes = [P, P, P, I, I64, I64, I64, I64, P, P, P]
+        lib.lao_decode_step.argtypes = [P, P, P, I, I, I64, I64, I64, I64, P, P, P]
         for f in ("lao_forward", "lao_causal", "lao_prefix_mask", "lao_decode_step"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -104,8 +104,18 @@ def _same_dtype(*codes):
     return codes[0]
 
 
-def forward(q, k, v, rows=None):
-    """Non-causal normalised linear attention; q [B,Hq,n,d], k/v [B,Hkv,n,d]."""
+_PHI = {"relu1": 0, "elu1": 1}
+
+
+def _phi(phi):
+    if phi not in _PHI:
+        raise ValueError(f"phi must be one of {sorted(_PHI)}")
+    return _PHI[phi]
+
+
+def forward(q, k, v, rows=None, phi="relu1"):
+    """Non-causal normalised linear attention; q [B,Hq,n,d], k/v [B,Hkv,n,d].
+    phi: "relu1" (relu(x) + 1) or "elu1" (ELU(x) + 1)."""
     q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
     dt = _same_dtype(cq, ck, cv)
     B, Hq, n, d = q.shape
@@ -113,12 +123,12 @@ def forward(q, k, v, rows=None):
     _check_gqa(q.shape, k.shape, v.shape)
     r, nr = _rows(rows, n)
     out = np.empty((B, Hq, nr, d), dtype=np.float64)
-    _load().lao_forward(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, n, d,
+    _load().lao_forward(_ptr(q), _ptr(k), _ptr(v), dt, _phi(phi), B, Hq, Hkv, n, d,
                         _ptr(r), nr, _ptr(out))
     return out
 
 
-def causal(q, k, v, rows=None, want_state=False, Hq=None):
+def causal(q, k, v, rows=None, want_state=False, Hq=None, phi="relu1"):
     """Causal normalised linear attention (query i sees keys 0..i).
 
     q may be None for a state-only pass (then pass Hq for the head count, or
@@ -139,7 +149,7 @@ def causal(q, k, v, rows=None, want_state=False, Hq=None):
     out = None if q is None else np.empty((B, Hq, nr, d), dtype=np.float64)
     S = np.empty((B, Hkv, d, d), dtype=np.float64) if want_state else None
     z = np.empty((B, Hkv, d), dtype=np.float64) if want_state else None
-    _load().lao_causal(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, n, d,
+    _load().lao_causal(_ptr(q), _ptr(k), _ptr(v), dt, _phi(phi), B, Hq, Hkv, n, d,
                        _ptr(r), nr, _ptr(out), _ptr(S), _ptr(z))
     if want_state:
         return out, S, z
@@ -163,7 +173,7 @@ def prefix_mask(q, k, v, m, rows=None):
     return out
 
 
-def decode_step(q, k, v, S, z):
+def decode_step(q, k, v, S, z, phi="relu1"):
     """One decode step: S [B,Hkv,d,d] and z [B,Hkv,d] (float64) update in place."""
     q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
     dt = _same_dtype(cq, ck, cv)
@@ -177,6 +187,6 @@ def decode_step(q, k, v, S, z):
             S.flags.c_contiguous and z.flags.c_contiguous):
         raise TypeError("S and z must be C-contiguous float64 arrays")
     out = np.empty((B, Hq, d), dtype=np.float64)
-    _load().lao_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, d,
+    _load().lao_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _phi(phi), B, Hq, Hkv, d,
                             _ptr(S), _ptr(z), _ptr(out))
     return out

@@ -11,6 +11,10 @@
  *    S = sum_j phi(K_j) (x) V_j and z = sum_j phi(K_j) (the "accumulate
  *    KV-summary" loop), and out_i = phi(Q_i) S / (phi(Q_i) . z) (the
  *    "per-query" loop).  S is stored [a][b] row-major, as on that page.
+ *  - "LinearTile 1.0.1" (files.pythonhosted.org), section "How It Works":
+ *    the same O = phi(Q) (phi(K)^T V) with phi(x) = ELU(x) + 1, the second
+ *    feature map offered here (ELU with alpha = 1, the page naming no other:
+ *    phi(x) = x + 1 for x > 0, exp(x) otherwise).
  *  - "trim-transformer 0.1.0" (pypi.org), section "Masking": query i attends
  *    to keys 0..m_i; a causal mask is m = arange(n).  Its kernel is
  *    Attn(Q,K,V) = Q K^T V with no feature map and no normaliser.
@@ -18,7 +22,8 @@
  *    cache token by token, linear in the number of generated tokens.
  *
  * Readings where the pages leave a step open:
- *  - no epsilon in the normaliser (phi >= 1 keeps the denominator >= 1);
+ *  - no epsilon in the normaliser (relu + 1 >= 1 keeps the denominator >= 1;
+ *    ELU + 1 > 0 keeps it positive);
  *  - causal queries see their own key (m_i = i is inclusive);
  *  - query head h uses key/value head h / (Hq / Hkv) (contiguous groups);
  *  - the decode step adds the new token to the state before reading it.
@@ -52,8 +57,12 @@ static double rd(const void* p, int dtype, int64_t idx) {
   return (double)f;
 }
 
-/* phi(x) = relu(x) + 1; -0 and every negative value map to 1. */
-static double phi(double x) { return (x > 0.0 ? x : 0.0) + 1.0; }
+/* phi(x) = relu(x) + 1 (-0 and every negative value map to 1), or
+ * phi(x) = ELU(x) + 1 = x + 1 for x > 0, exp(x) otherwise. */
+static double phi(double x, int kind) {
+  if (kind == LAO_PHI_ELU1) return x > 0.0 ? x + 1.0 : exp(x);
+  return (x > 0.0 ? x : 0.0) + 1.0;
+}
 
 /* Offset of row i of head h in a [B][H][n][d] tensor. */
 static int64_t off4(int64_t b, int64_t h, int64_t i, int64_t H, int64_t n,
@@ -62,12 +71,12 @@ static int64_t off4(int64_t b, int64_t h, int64_t i, int64_t H, int64_t n,
 }
 
 /* out_row = phi(q_row) S / (phi(q_row) . z), with q_row read from q at off. */
-static void normalised_read(const void* q, int dtype, int64_t off, int64_t d,
-                            const double* S, const double* z, double* pq,
-                            double* out_row) {
+static void normalised_read(const void* q, int dtype, int phik, int64_t off,
+                            int64_t d, const double* S, const double* z,
+                            double* pq, double* out_row) {
   double den = 0.0;
   for (int64_t a = 0; a < d; ++a) {
-    pq[a] = phi(rd(q, dtype, off + a));
+    pq[a] = phi(rd(q, dtype, off + a), phik);
     den += pq[a] * z[a];
   }
   for (int64_t c = 0; c < d; ++c) {
@@ -78,8 +87,8 @@ static void normalised_read(const void* q, int dtype, int64_t off, int64_t d,
 }
 
 void lao_forward(const void* q, const void* k, const void* v, int dtype,
-                 int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
-                 const int64_t* rows, int64_t nrows, double* out) {
+                 int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                 int64_t d, const int64_t* rows, int64_t nrows, double* out) {
   const int64_t R = Hq / Hkv;
   const int64_t nr = rows ? nrows : n;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -93,7 +102,7 @@ void lao_forward(const void* q, const void* k, const void* v, int dtype,
       for (int64_t j = 0; j < n; ++j) {
         const int64_t o = off4(b, g, j, Hkv, n, d);
         for (int64_t a = 0; a < d; ++a) {
-          pk[a] = phi(rd(k, dtype, o + a));
+          pk[a] = phi(rd(k, dtype, o + a), phik);
           z[a] += pk[a];
         }
         for (int64_t a = 0; a < d; ++a)
@@ -102,7 +111,7 @@ void lao_forward(const void* q, const void* k, const void* v, int dtype,
       }
       for (int64_t r = 0; r < nr; ++r) {
         const int64_t i = rows ? rows[r] : r;
-        normalised_read(q, dtype, off4(b, h, i, Hq, n, d), d, S, z, pk,
+        normalised_read(q, dtype, phik, off4(b, h, i, Hq, n, d), d, S, z, pk,
                         out + off4(b, h, r, Hq, nr, d));
       }
       free(S);
@@ -113,8 +122,8 @@ void lao_forward(const void* q, const void* k, const void* v, int dtype,
 }
 
 void lao_causal(const void* q, const void* k, const void* v, int dtype,
-                int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
-                const int64_t* rows, int64_t nrows, double* out,
+                int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                int64_t d, const int64_t* rows, int64_t nrows, double* out,
                 double* S_final, double* z_final) {
   const int64_t R = Hq / Hkv;
   const int64_t nr = rows ? nrows : n;
@@ -129,7 +138,7 @@ void lao_causal(const void* q, const void* k, const void* v, int dtype,
         /* Add key/value i to the running state, then let query i read it. */
         const int64_t o = off4(b, g, i, Hkv, n, d);
         for (int64_t a = 0; a < d; ++a) {
-          pk[a] = phi(rd(k, dtype, o + a));
+          pk[a] = phi(rd(k, dtype, o + a), phik);
           z[a] += pk[a];
         }
         for (int64_t a = 0; a < d; ++a)
@@ -138,8 +147,8 @@ void lao_causal(const void* q, const void* k, const void* v, int dtype,
         if (!q || !out || r >= nr) continue;
         if (rows && rows[r] != i) continue;
         for (int64_t h = g * R; h < (g + 1) * R; ++h)
-          normalised_read(q, dtype, off4(b, h, i, Hq, n, d), d, S, z, pk,
-                          out + off4(b, h, r, Hq, nr, d));
+          normalised_read(q, dtype, phik, off4(b, h, i, Hq, n, d), d, S, z,
+                          pk, out + off4(b, h, r, Hq, nr, d));
         ++r;
       }
       if (S_final) memcpy(S_final + (b * Hkv + g) * d * d, S, (size_t)(d * d) * sizeof(double));
@@ -201,7 +210,7 @@ void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
 }
 
 void lao_decode_step(const void* q, const void* k, const void* v, int dtype,
-                     int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                     int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                      double* S, double* z, double* out) {
   const int64_t R = Hq / Hkv;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -213,14 +222,14 @@ void lao_decode_step(const void* q, const void* k, const void* v, int dtype,
       const int64_t o = (b * Hkv + g) * d;
       /* The new token joins the state first; then its queries read it. */
       for (int64_t a = 0; a < d; ++a) {
-        pk[a] = phi(rd(k, dtype, o + a));
+        pk[a] = phi(rd(k, dtype, o + a), phik);
         zg[a] += pk[a];
       }
       for (int64_t a = 0; a < d; ++a)
         for (int64_t c = 0; c < d; ++c)
           Sg[a * d + c] += pk[a] * rd(v, dtype, o + c);
       for (int64_t h = g * R; h < (g + 1) * R; ++h)
-        normalised_read(q, dtype, (b * Hq + h) * d, d, Sg, zg, pk,
+        normalised_read(q, dtype, phik, (b * Hq + h) * d, d, Sg, zg, pk,
                         out + (b * Hq + h) * d);
       free(pk);
     }

@@ -8,7 +8,9 @@
  *
  * What it computes (plain definitions, fp64 accumulation):
  *   phi(x) = max(x, 0) + 1                       (nx_f32_linear_attention.nx,
- *                                                 function la_phi)
+ *                                                 function la_phi), or
+ *   phi(x) = ELU(x) + 1 (alpha = 1)              (LinearTile 1.0.1,
+ *                                                 "How It Works")
  *   S = sum_j phi(K_j) (x) V_j,  z = sum_j phi(K_j)
  *   out_i = (phi(Q_i) S) / (phi(Q_i) . z)          (same page, header comment)
  * in the non-causal form (all keys), the causal form (keys 0..i), the
@@ -33,21 +35,22 @@ extern "C" {
 #endif
 
 enum { LAO_F32 = 0, LAO_BF16 = 1 };
+enum { LAO_PHI_RELU1 = 0, LAO_PHI_ELU1 = 1 };  /* phik: the feature map */
 
 /* Number of OpenMP threads the oracle uses. */
 int lao_num_threads(void);
 
 /* Non-causal normalised form: every query sees every key. */
 void lao_forward(const void* q, const void* k, const void* v, int dtype,
-                 int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
-                 const int64_t* rows, int64_t nrows, double* out);
+                 int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                 int64_t d, const int64_t* rows, int64_t nrows, double* out);
 
 /* Causal normalised form: query i sees keys 0..i.  q/out may be NULL (state
  * only).  S_final [B][Hkv][d][d] and z_final [B][Hkv][d] (either may be NULL)
  * receive the state after the last token. */
 void lao_causal(const void* q, const void* k, const void* v, int dtype,
-                int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
-                const int64_t* rows, int64_t nrows, double* out,
+                int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                int64_t d, const int64_t* rows, int64_t nrows, double* out,
                 double* S_final, double* z_final);
 
 /* Unnormalised prefix-mask form, identity feature map: query i sees keys
@@ -62,7 +65,7 @@ void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
  * head reads the updated state.  q [B][Hq][d], k and v [B][Hkv][d],
  * out [B][Hq][d]. */
 void lao_decode_step(const void* q, const void* k, const void* v, int dtype,
-                     int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                     int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                      double* S, double* z, double* out);
 
 #ifdef __cplusplus

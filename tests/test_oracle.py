@@ -301,3 +301,88 @@ def test_bf16_rounding_helper_is_nearest_even():
     np.testing.assert_array_equal(back[:4], np.array([1.0, 1.0, 1.015625, -2.5], np.float32))
     assert abs(back[4] - 3.0e-3) <= 3.0e-3 * 2 ** -8
     assert np.array_equal(bits[5:], np.array([0x0000, 0x8000], np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# The ELU + 1 feature map (LinearTile 1.0.1, "How It Works"): phi(x) = x + 1
+# for x > 0 and exp(x) otherwise (ELU with alpha = 1).
+# ---------------------------------------------------------------------------
+def _elu1(x):
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def brute_normalised_elu1(q, k, v, causal):
+    q, k, v = (li.to_f32(x).astype(np.float64) for x in (q, k, v))
+    B, Hq, n, d = q.shape
+    R = Hq // k.shape[1]
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            w = _elu1(q[b, h]) @ _elu1(k[b, h // R]).T
+            if causal:
+                w = np.tril(w)
+            out[b, h] = (w @ v[b, h // R]) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+def test_elu1_feature_map_at_chosen_points():
+    """d = 1 (phi(q) cancels): out_i = sum_{j<=i} phi(k_j) v_j / sum_{j<=i} phi(k_j),
+    with phi written out by hand at k = 0, -1, 1, -2.5, 3 (the branches meet
+    at 0: ELU(0) + 1 = 1)."""
+    import math
+    kv = [0.0, -1.0, 1.0, -2.5, 3.0]
+    vv = [1.0, 2.0, -3.0, 4.0, 0.5]
+    phis = [1.0, math.exp(-1.0), 2.0, math.exp(-2.5), 4.0]
+    k = np.array(kv, dtype=np.float32).reshape(1, 1, 5, 1)
+    v = np.array(vv, dtype=np.float32).reshape(1, 1, 5, 1)
+    q = np.array([0.3, -2.0, 5.0, -0.1, 1.0], dtype=np.float32).reshape(1, 1, 5, 1)
+    want = [sum(p * x for p, x in zip(phis[:i + 1], vv[:i + 1])) / sum(phis[:i + 1]) for i in range(5)]
+    np.testing.assert_allclose(oracle.causal(q, k, v, phi="elu1")[0, 0, :, 0], want, rtol=1e-12)
+    np.testing.assert_allclose(oracle.forward(q, k, v, phi="elu1")[0, 0, :, 0], np.full(5, want[-1]), rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 17, 1), (2, 4, 2, 33, 3), (1, 6, 3, 19, 5)])
+def test_elu1_forms_match_brute_force(seed, shape):
+    B, Hq, Hkv, n, d = shape
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=seed)
+    np.testing.assert_allclose(oracle.forward(q, k, v, phi="elu1"), brute_normalised_elu1(q, k, v, False),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.causal(q, k, v, phi="elu1"), brute_normalised_elu1(q, k, v, True),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_elu1_equals_relu1_on_positive_inputs():
+    """For x > 0 both maps are x + 1, so strictly positive Q and K give the
+    same outputs under either; mixed signs do not."""
+    B, Hq, Hkv, n, d = 1, 2, 1, 40, 6
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=4)
+    qp, kp = np.abs(q) + 0.01, np.abs(k) + 0.01
+    for f in (oracle.forward, oracle.causal):
+        np.testing.assert_allclose(f(qp, kp, v, phi="elu1"), f(qp, kp, v), rtol=1e-12, atol=1e-12)
+        assert rel_rows(f(q, k, v, phi="elu1"), f(q, k, v)) > 1e-3
+
+
+def test_elu1_equal_keys_give_mean_of_v():
+    """Every key row equal: all weights of a query are equal whatever phi is,
+    so the non-causal output is mean(V) and the causal one the running mean."""
+    B, H, n, d = 1, 1, 30, 4
+    q, _, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=5)
+    k = np.repeat(rng.standard_normal((1, 1, 1, d), dtype=np.float32), n, axis=2)
+    vf = v.astype(np.float64)
+    np.testing.assert_allclose(oracle.forward(q, k, v, phi="elu1"),
+                               np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.causal(q, k, v, phi="elu1"),
+                               np.cumsum(vf, axis=2) / np.arange(1, n + 1)[None, None, :, None], rtol=1e-12, atol=1e-12)
+
+
+def test_elu1_decode_steps_continue_the_causal_pass():
+    B, Hq, Hkv, n, d, T = 2, 4, 2, 20, 5, 3
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=6)
+    full, Sf, zf = oracle.causal(q, k, v, want_state=True, phi="elu1")
+    _, S, z = oracle.causal(None, k[:, :, :n - T], v[:, :, :n - T], want_state=True, Hq=Hq, phi="elu1")
+    for t in range(n - T, n):
+        o = oracle.decode_step(q[:, :, t].copy(), k[:, :, t].copy(), v[:, :, t].copy(), S, z, phi="elu1")
+        np.testing.assert_allclose(o, full[:, :, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, Sf, rtol=1e-12)
+    np.testing.assert_allclose(z, zf, rtol=1e-12)
