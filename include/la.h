@@ -75,6 +75,15 @@ enum {
 typedef int32_t la_dtype;
 enum { LA_F32 = 0, LA_BF16 = 1 };
 
+/* Feature map phi of the normalised forms.  LA_PHI_RELU1: phi(x) = relu(x)
+ * + 1 (nx_f32_linear_attention.nx, function la_phi), what la_forward,
+ * la_causal_forward and la_decode_step use.  LA_PHI_ELU1: phi(x) = ELU(x) +
+ * 1 with alpha = 1, i.e. x + 1 for x > 0 and e^x otherwise (LinearTile
+ * 1.0.1, "How It Works"), taken by the *_phi entry points below; any other
+ * value gives LA_ERR_UNSUPPORTED. */
+typedef int32_t la_phi;
+enum { LA_PHI_RELU1 = 0, LA_PHI_ELU1 = 1 };
+
 /* Operation codes for la_workspace_bytes. */
 enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2 };
 
@@ -137,6 +146,28 @@ la_status la_decode_step(const void* q, const void* k, const void* v,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                          la_dtype dtype, float* S, float* z, void* out,
                          void* stream);
+
+/* The three normalised entry points with the feature map as an argument
+ * (la_phi above); with LA_PHI_RELU1 each is exactly its plain counterpart.
+ * Arguments, layouts, workspace and errors are as there: la_workspace_bytes
+ * for the plain call's op and sizes covers either map.  A state built with
+ * one map must be continued (la_decode_step_phi) with the same map.  With
+ * LA_PHI_ELU1, phi(K) and phi(Q) are rounded to the input dtype before the
+ * products (bf16 inputs: relative error about 2^-9 per weight). */
+la_status la_forward_phi(const void* q, const void* k, const void* v,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                         int64_t d, la_dtype dtype, la_phi phi, void* out,
+                         void* ws, size_t ws_bytes, void* stream);
+la_status la_causal_forward_phi(const void* q, const void* k, const void* v,
+                                int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                                int64_t d, la_dtype dtype, la_phi phi,
+                                int32_t chunk, void* out, float* S_final,
+                                float* z_final, void* ws, size_t ws_bytes,
+                                void* stream);
+la_status la_decode_step_phi(const void* q, const void* k, const void* v,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                             la_dtype dtype, la_phi phi, float* S, float* z,
+                             void* out, void* stream);
 
 #ifdef __cplusplus
 }

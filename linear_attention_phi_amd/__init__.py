@@ -11,6 +11,9 @@ Functions carry the C names:
   la_causal_forward(q, k, v, chunk=0)        causal (optionally the final state)
   la_prefix_mask_forward(q, k, v, m)         unnormalised Q K^T V, prefix mask m
   la_decode_step(q, k, v, S, z)              one recurrent step (S, z in place)
+  (la_forward, la_causal_forward and la_decode_step take phi="relu1" or
+  phi="elu1"; the latter calls la_forward_phi / la_causal_forward_phi /
+  la_decode_step_phi with LA_PHI_ELU1)
   la_workspace_bytes(op, B, Hq, Hkv, n, d, dtype, chunk)
   la_status_str(code)
 Tensors are contiguous [B, H, n, d] (q, out: H = Hq; k, v: H = Hkv) in
@@ -26,6 +29,14 @@ LIB_PATH = os.path.join(_HERE, "liblaphi.so")
 
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK = 0, 1, 2
+LA_PHI_RELU1, LA_PHI_ELU1 = 0, 1
+_PHI = {"relu1": LA_PHI_RELU1, "elu1": LA_PHI_ELU1}
+
+
+def _phi(phi):
+    if phi not in _PHI:
+        raise ValueError(f"phi must be one of {sorted(_PHI)}")
+    return _PHI[phi]
 STATUS_NAMES = ["LA_OK", "LA_ERR_NULL", "LA_ERR_SHAPE", "LA_ERR_DTYPE", "LA_ERR_UNSUPPORTED",
                 "LA_ERR_WORKSPACE", "LA_ERR_ALIGN", "LA_ERR_ALIAS", "LA_ERR_LAUNCH"]
 
@@ -55,7 +66,11 @@ def load():
         lib.la_causal_forward.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, P, P, SZ, P]
         lib.la_prefix_mask_forward.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, I32, P, P, SZ, P]
         lib.la_decode_step.argtypes = [P, P, P, I64, I64, I64, I64, I32, P, P, P, P]
-        for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step"):
+        lib.la_forward_phi.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, SZ, P]
+        lib.la_causal_forward_phi.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, I32, P, P, P, P, SZ, P]
+        lib.la_decode_step_phi.argtypes = [P, P, P, I64, I64, I64, I64, I32, I32, P, P, P, P]
+        for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
+                  "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -144,8 +159,9 @@ def _call(rc, what):
         raise LAError(rc, what)
 
 
-def la_forward(q, k, v, out=None, ws=None):
-    """Non-causal normalised linear attention; returns out (q's shape and dtype)."""
+def la_forward(q, k, v, out=None, ws=None, phi="relu1"):
+    """Non-causal normalised linear attention; returns out (q's shape and dtype).
+    phi: "relu1" (relu(x) + 1, la_forward) or "elu1" (ELU(x) + 1, la_forward_phi)."""
     torch = _torch()
     B, Hq, Hkv, n, d = _qkv(q, k, v)
     dt = _dtype_code(q)
@@ -153,14 +169,18 @@ def la_forward(q, k, v, out=None, ws=None):
     _expect(out, q.shape, q.dtype, "out")
     need = la_workspace_bytes(LA_OP_FORWARD, B, Hq, Hkv, n, d, dt, 0)
     ws = workspace(need, q.device) if ws is None else ws
-    _call(load().la_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt,
-                            _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), "la_forward")
+    if phi == "relu1":
+        _call(load().la_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt,
+                                _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), "la_forward")
+    else:
+        _call(load().la_forward_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, _phi(phi),
+                                    _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), "la_forward_phi")
     return out
 
 
 def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None, z_final=None,
-                      ws=None, Hq=None):
-    """Causal normalised linear attention.
+                      ws=None, Hq=None, phi="relu1"):
+    """Causal normalised linear attention (phi: "relu1" or "elu1", as la_forward).
 
     q may be None for a state-only pass (pass Hq, default Hkv); then the
     final state is returned.  With want_state, returns (out, S_final, z_final).
@@ -184,9 +204,15 @@ def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None
     if need == 0:
         raise LAError(4, f"la_causal_forward (chunk={chunk}, d={d}, dtype={k.dtype})")
     ws = workspace(need, k.device) if ws is None else ws
-    _call(load().la_causal_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, chunk,
-                                   _dev(out, "out"), _dev(S_final, "S_final"), _dev(z_final, "z_final"),
-                                   _dev(ws, "ws"), ws.numel(), _stream(k)), "la_causal_forward")
+    if phi == "relu1":
+        _call(load().la_causal_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, chunk,
+                                       _dev(out, "out"), _dev(S_final, "S_final"), _dev(z_final, "z_final"),
+                                       _dev(ws, "ws"), ws.numel(), _stream(k)), "la_causal_forward")
+    else:
+        _call(load().la_causal_forward_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt,
+                                           _phi(phi), chunk, _dev(out, "out"), _dev(S_final, "S_final"),
+                                           _dev(z_final, "z_final"), _dev(ws, "ws"), ws.numel(), _stream(k)),
+              "la_causal_forward_phi")
     if q is None:
         return S_final, z_final
     if want_state:
@@ -215,9 +241,10 @@ def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):
     return out
 
 
-def la_decode_step(q, k, v, S, z, out=None):
+def la_decode_step(q, k, v, S, z, out=None, phi="relu1"):
     """One decode step: q [B,Hq,d], k/v [B,Hkv,d]; S [B,Hkv,d,d], z [B,Hkv,d]
-    (float32) are updated in place.  Returns out [B,Hq,d]."""
+    (float32) are updated in place.  Returns out [B,Hq,d].  phi as la_forward
+    (the map the state was built with)."""
     torch = _torch()
     B, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -230,6 +257,11 @@ def la_decode_step(q, k, v, S, z, out=None):
     _expect(z, (B, Hkv, d), torch.float32, "z")
     out = torch.empty_like(q) if out is None else out
     _expect(out, q.shape, q.dtype, "out")
-    _call(load().la_decode_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, d, dt,
-                                _dev(S, "S"), _dev(z, "z"), _dev(out, "out"), _stream(q)), "la_decode_step")
+    if phi == "relu1":
+        _call(load().la_decode_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, d, dt,
+                                    _dev(S, "S"), _dev(z, "z"), _dev(out, "out"), _stream(q)), "la_decode_step")
+    else:
+        _call(load().la_decode_step_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, d, dt, _phi(phi),
+                                        _dev(S, "S"), _dev(z, "z"), _dev(out, "out"), _stream(q)),
+              "la_decode_step_phi")
     return out

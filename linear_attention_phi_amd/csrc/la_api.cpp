@@ -188,10 +188,11 @@ size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_
   return required_ws(op, B, Hq, Hkv, n, d, dtype, C, nullptr);
 }
 
-la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
-                     int64_t d, la_dtype dtype, void* out, void* ws, size_t ws_bytes, void* stream) {
+la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                         int64_t d, la_dtype dtype, la_phi phi, void* out, void* ws, size_t ws_bytes, void* stream) {
   la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
   if (st != LA_OK) return st;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const size_t eb = elem_bytes(dtype);
@@ -205,23 +206,30 @@ la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int
   if (overlaps(ws, need, out, qb) || overlaps(ws, need, q, qb) || overlaps(ws, need, k, kvb) ||
       overlaps(ws, need, v, kvb))
     return LA_ERR_ALIAS;
-  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream};
-  if (forward_bf16_applies(n, d, (int)dtype)) {
+  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream, (int)phi};
+  // the d = 64 kernels split phi(K) as relu(K) + 1; ELU + 1 takes the general path
+  if (phi == LA_PHI_RELU1 && forward_bf16_applies(n, d, (int)dtype)) {
     if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_bf16(a, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
-  if (forward_f32_applies(n, d, (int)dtype)) {
+  if (phi == LA_PHI_RELU1 && forward_f32_applies(n, d, (int)dtype)) {
     if (B * Hq * forward_f32_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_f32(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   return launch_forward(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 
-la_status la_causal_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
-                            int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out, float* S_final,
-                            float* z_final, void* ws, size_t ws_bytes, void* stream) {
+la_status la_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                     int64_t d, la_dtype dtype, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return la_forward_phi(q, k, v, B, Hq, Hkv, n, d, dtype, LA_PHI_RELU1, out, ws, ws_bytes, stream);
+}
+
+la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                                int64_t n, int64_t d, la_dtype dtype, la_phi phi, int32_t chunk, void* out,
+                                float* S_final, float* z_final, void* ws, size_t ws_bytes, void* stream) {
   la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
   if (st != LA_OK) return st;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
   if (!k || !v) return LA_ERR_NULL;
   if ((q == nullptr) != (out == nullptr)) return LA_ERR_NULL;
   if (!q && !S_final && !z_final) return LA_ERR_NULL;
@@ -248,13 +256,20 @@ la_status la_causal_forward(const void* q, const void* k, const void* v, int64_t
     if (overlaps(ws, need, ins[i], inb[i])) return LA_ERR_ALIAS;
   if (overlaps(ws, need, out, qb) || overlaps(ws, need, S_final, sb) || overlaps(ws, need, z_final, zb))
     return LA_ERR_ALIAS;
-  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream};
-  if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {
+  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream, (int)phi};
+  if (phi == LA_PHI_RELU1 && q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {
     const Plan fp = make_fused_plan(n);
     if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_causal_fused(a, fp, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   return launch_causal(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_causal_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                            int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out, float* S_final,
+                            float* z_final, void* ws, size_t ws_bytes, void* stream) {
+  return la_causal_forward_phi(q, k, v, B, Hq, Hkv, n, d, dtype, LA_PHI_RELU1, chunk, out, S_final, z_final, ws,
+                               ws_bytes, stream);
 }
 
 la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, const int64_t* m, int64_t B,
@@ -282,10 +297,11 @@ la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, co
   return launch_prefix(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 
-la_status la_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
-                         int64_t d, la_dtype dtype, float* S, float* z, void* out, void* stream) {
+la_status la_decode_step_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                             int64_t d, la_dtype dtype, la_phi phi, float* S, float* z, void* out, void* stream) {
   la_status st = check_sizes(B, Hq, Hkv, 1, d, dtype);
   if (st != LA_OK) return st;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
   if (B * Hkv >= kMaxGrid) return LA_ERR_SHAPE;
   if (!q || !k || !v || !S || !z || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z) || !aligned16(out))
@@ -299,7 +315,12 @@ la_status la_decode_step(const void* q, const void* k, const void* v, int64_t B,
     if (overlaps(out, qb, ins[i], inb[i]) || overlaps(S, sb, ins[i], inb[i]) || overlaps(z, zb, ins[i], inb[i]))
       return LA_ERR_ALIAS;
   if (overlaps(out, qb, S, sb) || overlaps(out, qb, z, zb) || overlaps(S, sb, z, zb)) return LA_ERR_ALIAS;
-  return launch_decode(q, k, v, B, Hq, Hkv, d, (int)dtype, S, z, out, stream) == 0 ? LA_OK : LA_ERR_LAUNCH;
+  return launch_decode(q, k, v, B, Hq, Hkv, d, (int)dtype, (int)phi, S, z, out, stream) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t d, la_dtype dtype, float* S, float* z, void* out, void* stream) {
+  return la_decode_step_phi(q, k, v, B, Hq, Hkv, d, dtype, LA_PHI_RELU1, S, z, out, stream);
 }
 
 }  // extern "C"

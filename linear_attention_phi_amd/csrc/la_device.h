@@ -34,6 +34,13 @@ constexpr int PAD = 4;   // LDS row padding (elements): 8-byte (bf16) / 16-byte
 enum Form { CAUSAL = 0, PREFIX = 1 };
 
 __device__ __forceinline__ float phi_f(float x) { return fmaxf(x, 0.0f) + 1.0f; }
+// The feature maps a call can take: the identity (the prefix form),
+// relu(x) + 1 (nx_f32_linear_attention.nx, function la_phi) and ELU(x) + 1
+// with alpha = 1 (LinearTile 1.0.1, "How It Works"): x + 1 for x > 0, e^x
+// otherwise.
+enum PhiMode { PM_ID = 0, PM_RELU1 = 1, PM_ELU1 = 2 };
+__device__ __forceinline__ float elu1_f(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
+template <int PM> __device__ __forceinline__ float phi_m(float x) { return PM == PM_ELU1 ? elu1_f(x) : phi_f(x); }
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T cvt(float x);
@@ -102,12 +109,13 @@ __device__ __forceinline__ void st_accT(float* X, int ldx, const f32x16& acc, in
 
 // ---------------------------------------------------------------- tile loads
 // What a tile copy holds: not written, the raw value, phi(x) = relu(x) + 1,
-// or relu(x).
-enum Xf { XF_NONE = 0, XF_ID = 1, XF_PHI = 2, XF_RELU = 3 };
+// relu(x), or ELU(x) + 1.
+enum Xf { XF_NONE = 0, XF_ID = 1, XF_PHI = 2, XF_RELU = 3, XF_ELU1 = 4 };
 
 template <int X> __device__ __forceinline__ float xform(float x) {
   if (X == XF_PHI) return phi_f(x);
   if (X == XF_RELU) return fmaxf(x, 0.0f);
+  if (X == XF_ELU1) return elu1_f(x);
   return x;
 }
 

@@ -50,6 +50,7 @@ struct Fwd {
   float* S_final; float* z_final;
   void* ws;
   void* stream;
+  int phi = 0;           // feature map of the normalised forms: 0 relu + 1, 1 ELU + 1
 };
 
 // Each returns 0 on success, else a nonzero HIP error code.
@@ -87,7 +88,7 @@ size_t forward_f32_ws_bytes(int64_t NKV, int64_t nseg);
 int launch_forward_f32(const Fwd& a);
 
 int launch_decode(const void* q, const void* k, const void* v, int64_t B,
-                  int64_t Hq, int64_t Hkv, int64_t d, int dtype, float* S,
-                  float* z, void* out, void* stream);
+                  int64_t Hq, int64_t Hkv, int64_t d, int dtype, int phi,
+                  float* S, float* z, void* out, void* stream);
 
 }  // namespace la_internal

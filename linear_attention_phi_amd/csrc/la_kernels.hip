@@ -64,11 +64,14 @@ __device__ __forceinline__ void copy_rows_out(const T* tile, int nrows, int d, b
 
 
 // ------------------------------------------------------------------ k_state
-// With PHI the state is built as phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t
-// and z = sum_t relu(K_t) + (number of keys): relu of an input value is
-// exact in the input type, so the MFMA products are exact and the state is
-// exact up to fp32 summation (rounding phi(K) to bf16 would not be).
-template <typename T, int DP, int C, bool PHI>
+// PM is the feature map of K.  With relu + 1 the state is built as
+// phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t and z = sum_t relu(K_t) +
+// (number of keys): relu of an input value is exact in the input type, so
+// the MFMA products are exact and the state is exact up to fp32 summation
+// (rounding phi(K) to bf16 would not be).  ELU + 1 has no such split: the
+// tile holds phi(K) in the input type.  The identity (prefix form) builds
+// K^T V and no z.
+template <typename T, int DP, int C, int PM>
 __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* __restrict__ v, int64_t n, int d,
                                               bool vec, int64_t nchunks, int64_t G, int64_t nseg,
                                               float* __restrict__ ws) {
@@ -76,6 +79,7 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
   __shared__ __attribute__((aligned(16))) T sVT[DP * (C + PAD)];
   __shared__ float svs[DP];
   using SB = StateBlocks<DP>;
+  constexpr int KX = PM == PM_RELU1 ? XF_RELU : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const T* kb = k + bh * n * d;
@@ -98,11 +102,11 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
     const int64_t t0 = c * C;
     const int nv = (int)((n - t0) < C ? (n - t0) : C);
     if (vec) {
-      tile_store<T, DP, C, XF_NONE, PHI ? XF_RELU : XF_ID>(rK, nv, nullptr, sKT, tid);
+      tile_store<T, DP, C, XF_NONE, KX>(rK, nv, nullptr, sKT, tid);
       tile_store<T, DP, C, XF_NONE, XF_ID>(rV, nv, nullptr, sVT, tid);
       if (c + 1 < c1) fetch(c + 1);
     } else {
-      load_tile<T, DP, C, XF_NONE, PHI ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
+      load_tile<T, DP, C, XF_NONE, KX>(kb, t0, nullptr, nv, d, vec, nullptr, sKT, tid);
       load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
     }
     __syncthreads();
@@ -114,13 +118,13 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
         gemm_acc<T, C / 16>(accS[s], sKT + ma * 32 * (C + PAD), C + PAD, sVT + nb * 32 * (C + PAD), C + PAD, lane);
       }
     }
-    if (PHI && tid < DP) {
-      zrun += row_sum<T, C>(sKT, tid) + (tid < d ? (float)nv : 0.0f);
-      vrun += row_sum<T, C>(sVT, tid);
+    if (PM != PM_ID && tid < DP) {
+      zrun += row_sum<T, C>(sKT, tid) + (PM == PM_RELU1 && tid < d ? (float)nv : 0.0f);
+      if (PM == PM_RELU1) vrun += row_sum<T, C>(sVT, tid);
     }
     __syncthreads();
   }
-  if (PHI) {
+  if (PM == PM_RELU1) {
     if (tid < DP) svs[tid] = vrun;
     __syncthreads();
 #pragma unroll
@@ -486,7 +490,7 @@ constexpr int k_out_waves() {
   return la_internal::chunk_lds_bytes((int)sizeof(T), DP, C) <= la_internal::kLdsLimit / 2 ? 2 : 1;
 }
 
-template <typename T, int DP, int C, int FORM>
+template <typename T, int DP, int C, int FORM, int PM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<T, DP, C>()))) void k_out(const T* __restrict__ q, const T* __restrict__ k,
                                             const T* __restrict__ v, T* __restrict__ out, int64_t n, int d,
                                             int R, bool vec, int64_t nchunks, int64_t G, int64_t nseg,
@@ -497,6 +501,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
   constexpr int NIB = C / 32;   // 32-row query / key blocks per chunk
   constexpr int NBB = DP / 32;  // 32-wide feature blocks
   constexpr bool NORM = (FORM == CAUSAL);
+  static_assert(NORM == (PM != PM_ID), "the causal form takes a feature map, the prefix form none");
+  // tiles of phi(Q) and phi(K) (scores), of the keys the state update takes
+  // (relu(K) with the relu + 1 split, below), and whether S and z carry that
+  // split (S = accS + 1 (x) sum of V, z counts the keys)
+  constexpr int QX = PM == PM_RELU1 ? XF_PHI : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
+  constexpr int KTX = PM == PM_RELU1 ? XF_RELU : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
+  constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
   __shared__ __attribute__((aligned(16))) T sK[C * LQ];
   __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
@@ -609,11 +620,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
     const int ngroups = groups_of(c);
 
     if (PF_KV && vec && kv_c == c) {
-      tile_store<T, DP, C, NORM ? XF_PHI : XF_ID, NORM ? XF_RELU : XF_ID>(rK, nv, sK, sKT, tid);
+      tile_store<T, DP, C, QX, KTX>(rK, nv, sK, sKT, tid);
       tile_store<T, DP, C, XF_NONE, XF_ID>(rV, nv, nullptr, sVT, tid);
       if (c + 1 < c1) fetch_kv(c + 1);
     } else {
-      load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, NORM ? XF_RELU : XF_ID>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
+      load_tile<T, DP, C, QX, KTX>(kb, t0, nullptr, nv, d, vec, sK, sKT, tid);
       load_tile<T, DP, C, XF_NONE, XF_ID>(vb, t0, nullptr, nv, d, vec, nullptr, sVT, tid);
     }
 #pragma unroll
@@ -622,7 +633,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
       if (e < SB::TOTAL) {
         const int ma = e / SB::NB, nb = e % SB::NB;
         f32x16 cur = accS[s];
-        if (NORM) add_col(cur, svc[nb * 32 + (lane & 31)], ma, d, lane);
+        if (SPLIT) add_col(cur, svc[nb * 32 + (lane & 31)], ma, d, lane);
         st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
       }
     }
@@ -641,10 +652,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
       const int qcount = qt.rows;
       if (grp > 0) __syncthreads();  // previous group is done with sQ / sP
       if (vec && q_c == c && q_g == grp) {
-        tile_store<T, DP, C, NORM ? XF_PHI : XF_ID, XF_NONE>(rQ, qcount, sQ, nullptr, tid);
+        tile_store<T, DP, C, QX, XF_NONE>(rQ, qcount, sQ, nullptr, tid);
         fetch_q_after(c, grp);
       } else {
-        load_tile<T, DP, C, NORM ? XF_PHI : XF_ID, XF_NONE>(qt.base, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
+        load_tile<T, DP, C, QX, XF_NONE>(qt.base, t0, gidx, qcount, d, vec, sQ, nullptr, tid);
       }
       __syncthreads();
 
@@ -761,9 +772,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
       }
     }
     if (NORM && tid < DP) {
-      zrun += row_sum<T, C>(sKT, tid) + (tid < d ? (float)nv : 0.0f);
-      vrun += row_sum<T, C>(sVT, tid);
-      svc[tid] = vrun;  // read at the next chunk's start, after the barrier below
+      zrun += row_sum<T, C>(sKT, tid) + (SPLIT && tid < d ? (float)nv : 0.0f);
+      if (SPLIT) {
+        vrun += row_sum<T, C>(sVT, tid);
+        svc[tid] = vrun;  // read at the next chunk's start, after the barrier below
+      }
     }
     __syncthreads();
   }
@@ -976,7 +989,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
 // Non-causal output: out_i = phi(Q_i) S / (phi(Q_i) . z) with the total state
 // (slot nseg of the head).  One workgroup per (head, run of G chunks of
 // queries), for each of the R query heads.
-template <typename T, int DP, int C>
+template <typename T, int DP, int C, int PM>
 __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __restrict__ out, int64_t n, int d, int R,
                                                bool vec, int64_t nchunks, int64_t G, int64_t nqseg, int64_t nseg,
                                                const float* __restrict__ ws) {
@@ -1013,11 +1026,12 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
     for (int r = 0; r < R; ++r) {
       __syncthreads();  // sQ free (and sST / sz visible on the first pass)
       if (vec) {
-        tile_store<T, DP, C, XF_PHI, XF_NONE>(rQ, nv, sQ, nullptr, tid);
+        tile_store<T, DP, C, PM == PM_ELU1 ? XF_ELU1 : XF_PHI, XF_NONE>(rQ, nv, sQ, nullptr, tid);
         if (r + 1 < R) fetch(c, r + 1);
         else if (c + 1 < c1) fetch(c + 1, 0);
       } else {
-        load_tile<T, DP, C, XF_PHI, XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ, nullptr, tid);
+        load_tile<T, DP, C, PM == PM_ELU1 ? XF_ELU1 : XF_PHI, XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ,
+                                                                  nullptr, tid);
       }
       __syncthreads();
       const int i = ib * 32 + (lane & 31);
@@ -1302,7 +1316,7 @@ __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, co
 // outside the d x d square get an offset past the end, so their loads return
 // zero and their stores are dropped, and the update runs without branches
 // (a branch per element would make every store wait for the previous one).
-template <typename T>
+template <typename T, int PM>
 __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, int d, int R, float* __restrict__ S,
                                                float* __restrict__ z, T* __restrict__ out) {
@@ -1319,7 +1333,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
     // entries past d are zero so that padded rows and columns add nothing
     float pkv = 0.0f, vvv = 0.0f, znew = 0.0f;
     if (tid < d) {
-      pkv = phi_f(to_f(k[bg * d + tid]));
+      pkv = phi_m<PM>(to_f(k[bg * d + tid]));
       vvv = to_f(v[bg * d + tid]);
       znew = zg[tid] + pkv;
       zg[tid] = znew;
@@ -1350,7 +1364,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
   for (int r = 0; r < R; ++r) {
     const int64_t qh = bg * R + r;  // (b * Hkv + g) * R + r = b * Hq + g * R + r
     __syncthreads();                // previous head's reads of pq / red are done
-    if (tid < MD) pq[tid] = tid < d ? phi_f(to_f(q[qh * d + tid])) : 0.0f;
+    if (tid < MD) pq[tid] = tid < d ? phi_m<PM>(to_f(q[qh * d + tid])) : 0.0f;
     __syncthreads();
     if (tid < 64) {  // wave 0: den = phi(q) . z
       float p = pq[tid] * zn[tid] + pq[tid + 64] * zn[tid + 64];
@@ -1371,7 +1385,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T* __restrict__ q, const T*
 // (bounded buffer instructions again, so rows past D need no branch); the
 // per-head column sums are reduced across the threads that share columns
 // through LDS.
-template <typename T, int D>
+template <typename T, int D, int PM>
 __global__ __launch_bounds__(NT) void k_decode4(const T* __restrict__ q, const T* __restrict__ k,
                                                 const T* __restrict__ v, int R, float* __restrict__ S,
                                                 float* __restrict__ z, T* __restrict__ out) {
@@ -1386,7 +1400,7 @@ __global__ __launch_bounds__(NT) void k_decode4(const T* __restrict__ q, const T
   float* Sg = S + bg * D * D;
   float* zg = z + bg * D;
   if (tid < D) {
-    const float pkv = phi_f(to_f(k[bg * D + tid]));
+    const float pkv = phi_m<PM>(to_f(k[bg * D + tid]));
     pk[tid] = pkv;
     vv[tid] = to_f(v[bg * D + tid]);
     const float znew = zg[tid] + pkv;
@@ -1417,7 +1431,7 @@ __global__ __launch_bounds__(NT) void k_decode4(const T* __restrict__ q, const T
   for (int r = 0; r < R; ++r) {
     const int64_t qh = bg * R + r;  // (b * Hkv + g) * R + r = b * Hq + g * R + r
     __syncthreads();                // previous head's reads of pq / red are done
-    if (tid < D) pq[tid] = phi_f(to_f(q[qh * D + tid]));
+    if (tid < D) pq[tid] = phi_m<PM>(to_f(q[qh * D + tid]));
     __syncthreads();
     if (tid < 64) {  // wave 0: den = phi(q) . z
       float p = (tid < D ? pq[tid] * zn[tid] : 0.0f) + (tid + 64 < D ? pq[tid + 64] * zn[tid + 64] : 0.0f);
@@ -1450,7 +1464,7 @@ __global__ __launch_bounds__(NT) void k_decode4(const T* __restrict__ q, const T
 // the state loads are in flight, so no query load waits at the end.  One
 // barrier only: it publishes phi(q), and every wave has read the old z
 // before wave 0 writes the new one.
-template <typename T>
+template <typename T, int PM>
 __global__ __launch_bounds__(256) void k_decode128(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, int R, float* __restrict__ S,
                                                    float* __restrict__ z, T* __restrict__ out) {
@@ -1466,7 +1480,7 @@ __global__ __launch_bounds__(256) void k_decode128(const T* __restrict__ q, cons
   float pk[NJ], zn[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    pk[j] = phi_f(to_f(k[bg * D + r0 + 8 * j]));
+    pk[j] = phi_m<PM>(to_f(k[bg * D + r0 + 8 * j]));
     zn[j] = z[bg * D + r0 + 8 * j] + pk[j];  // z after this step's key
   }
   const f32x4 vb = {to_f(v[bg * D + col0]), to_f(v[bg * D + col0 + 1]), to_f(v[bg * D + col0 + 2]),
@@ -1474,7 +1488,7 @@ __global__ __launch_bounds__(256) void k_decode128(const T* __restrict__ q, cons
   extern __shared__ float pqs[];  // [R][D]: phi(q) of the group's query heads
   const T* qg = q + bg * R * D;   // heads (b * Hkv + g) * R + r are contiguous
 #pragma unroll 4
-  for (int i = tid; i < R * D; i += 256) pqs[i] = phi_f(to_f(qg[i]));
+  for (int i = tid; i < R * D; i += 256) pqs[i] = phi_m<PM>(to_f(qg[i]));
   __syncthreads();  // phi(q) staged; every wave has read the old z
   if (w == 0) {
 #pragma unroll
@@ -1526,6 +1540,19 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   T* out = reinterpret_cast<T*>(a.out);
   int* boff = nullptr; int* perm = nullptr;
   bool state_done = false;
+  if (form == CAUSAL && a.phi == 1) {
+    // ELU + 1: the general state, scan and output kernels (the specialised
+    // ones split relu + 1)
+    k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
+                                                                             p.G, p.nseg, states);
+    const int64_t E = slot_elems(DP);
+    k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d,
+                                                                            a.S_final, a.z_final, 1);
+    if (q && out)
+      k_out<T, DP, C, CAUSAL, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
+          q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
+    return (int)hipGetLastError();
+  }
   if (form == PREFIX) {
     char* bw = reinterpret_cast<char*>(a.ws) + la_internal::state_bytes(p, a.B, a.Hkv);
     boff = reinterpret_cast<int*>(bw);
@@ -1555,9 +1582,9 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   }
   if (state_done) {
   } else if (phi)
-    k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
+    k_state<T, DP, C, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   else
-    k_state<T, DP, C, false><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
+    k_state<T, DP, C, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
   const int64_t E = slot_elems(DP);
   // the GQA and fp32 prefix output kernels: F state segments per
   // workgroup, so that about kGqaOutGroups / kPrefixOutGroups workgroups
@@ -1593,9 +1620,9 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
       }
     }
     if (form == CAUSAL)
-      k_out<T, DP, C, CAUSAL><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
+      k_out<T, DP, C, CAUSAL, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
     else
-      k_out<T, DP, C, PREFIX><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m);
+      k_out<T, DP, C, PREFIX, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m);
   }
   return (int)hipGetLastError();
 }
@@ -1611,7 +1638,13 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   const T* k = reinterpret_cast<const T*>(a.k);
   const T* v = reinterpret_cast<const T*>(a.v);
   T* out = reinterpret_cast<T*>(a.out);
-  k_state<T, DP, C, true><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
+  const bool elu = a.phi == 1;
+  if (elu)
+    k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
+                                                                             p.nseg, states);
+  else
+    k_state<T, DP, C, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
+                                                                              p.nseg, states);
   const int64_t E = slot_elems(DP);
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr, 1);
   // query runs: about 1024 workgroups in total for 2-byte inputs (several per
@@ -1621,7 +1654,12 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   int64_t Gq = (nbh * p.nchunks + target - 1) / target;
   if (Gq < 1) Gq = 1;
   const int64_t nqseg = (p.nchunks + Gq - 1) / Gq;
-  k_out_nc<T, DP, C><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks, Gq, nqseg, p.nseg, states);
+  if (elu)
+    k_out_nc<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks,
+                                                                             Gq, nqseg, p.nseg, states);
+  else
+    k_out_nc<T, DP, C, PM_RELU1><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks,
+                                                                              Gq, nqseg, p.nseg, states);
   return (int)hipGetLastError();
 }
 
@@ -1659,26 +1697,24 @@ int dispatch(const la_internal::Fwd& a, const la_internal::Plan& p, int op) {
   return (int)hipErrorInvalidValue;
 }
 
-}  // namespace
-
-namespace la_internal {
-
-int launch_forward(const Fwd& a, const Plan& p) { return dispatch(a, p, 0); }
-int launch_causal(const Fwd& a, const Plan& p) { return dispatch(a, p, 1); }
-int launch_prefix(const Fwd& a, const Plan& p) { return dispatch(a, p, 2); }
-
-int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
-                  int dtype, float* S, float* z, void* out, void* stream) {
+// One decode step with feature map PM, dispatched on d and the dtype.
+template <int PM>
+int launch_decode_pm(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                     int dtype, float* S, float* z, void* out, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int R = (int)(Hq / Hkv);
   const dim3 grid((unsigned)(B * Hkv));
 #define LA_DEC4_LAUNCH(DD)                                                                                    \
     if (dtype == 0)                                                                                           \
-      k_decode4<float, DD><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k), \
-                                                reinterpret_cast<const float*>(v), R, S, z, reinterpret_cast<float*>(out)); \
+      k_decode4<float, DD, PM><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q),                        \
+                                                    reinterpret_cast<const float*>(k),                        \
+                                                    reinterpret_cast<const float*>(v), R, S, z,               \
+                                                    reinterpret_cast<float*>(out));                           \
     else                                                                                                      \
-      k_decode4<bf16, DD><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),   \
-                                               reinterpret_cast<const bf16*>(v), R, S, z, reinterpret_cast<bf16*>(out)); \
+      k_decode4<bf16, DD, PM><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q),                          \
+                                                   reinterpret_cast<const bf16*>(k),                          \
+                                                   reinterpret_cast<const bf16*>(v), R, S, z,                 \
+                                                   reinterpret_cast<bf16*>(out));                             \
     return (int)hipGetLastError();
 #define LA_DEC4(DD) \
   case DD:          \
@@ -1695,11 +1731,15 @@ int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_
       LA_DEC4_LAUNCH(128)
     }
     if (dtype == 0)
-      k_decode128<float><<<grid, 256, R * 128 * 4, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
-                                              reinterpret_cast<const float*>(v), R, S, z, reinterpret_cast<float*>(out));
+      k_decode128<float, PM><<<grid, 256, R * 128 * 4, st>>>(reinterpret_cast<const float*>(q),
+                                                             reinterpret_cast<const float*>(k),
+                                                             reinterpret_cast<const float*>(v), R, S, z,
+                                                             reinterpret_cast<float*>(out));
     else
-      k_decode128<bf16><<<grid, 256, R * 128 * 4, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
-                                             reinterpret_cast<const bf16*>(v), R, S, z, reinterpret_cast<bf16*>(out));
+      k_decode128<bf16, PM><<<grid, 256, R * 128 * 4, st>>>(reinterpret_cast<const bf16*>(q),
+                                                            reinterpret_cast<const bf16*>(k),
+                                                            reinterpret_cast<const bf16*>(v), R, S, z,
+                                                            reinterpret_cast<bf16*>(out));
     return (int)hipGetLastError();
     default:
       break;
@@ -1707,14 +1747,28 @@ int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_
 #undef LA_DEC4
 #undef LA_DEC4_LAUNCH
   if (dtype == 0)
-    k_decode<float><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
-                                         reinterpret_cast<const float*>(v), (int)d, R, S, z,
-                                         reinterpret_cast<float*>(out));
+    k_decode<float, PM><<<grid, NT, 0, st>>>(reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
+                                             reinterpret_cast<const float*>(v), (int)d, R, S, z,
+                                             reinterpret_cast<float*>(out));
   else
-    k_decode<bf16><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
-                                        reinterpret_cast<const bf16*>(v), (int)d, R, S, z,
-                                        reinterpret_cast<bf16*>(out));
+    k_decode<bf16, PM><<<grid, NT, 0, st>>>(reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
+                                            reinterpret_cast<const bf16*>(v), (int)d, R, S, z,
+                                            reinterpret_cast<bf16*>(out));
   return (int)hipGetLastError();
+}
+
+}  // namespace
+
+namespace la_internal {
+
+int launch_forward(const Fwd& a, const Plan& p) { return dispatch(a, p, 0); }
+int launch_causal(const Fwd& a, const Plan& p) { return dispatch(a, p, 1); }
+int launch_prefix(const Fwd& a, const Plan& p) { return dispatch(a, p, 2); }
+
+int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
+                  int dtype, int phi, float* S, float* z, void* out, void* stream) {
+  return phi == 1 ? launch_decode_pm<PM_ELU1>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream)
+                  : launch_decode_pm<PM_RELU1>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream);
 }
 
 }  // namespace la_internal

@@ -30,7 +30,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"la_status_str", "la_workspace_bytes", "la_forward", "la_causal_forward",
-                          "la_prefix_mask_forward", "la_decode_step"}
+                          "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
+                          "la_causal_forward_phi", "la_decode_step_phi"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -83,6 +84,24 @@ def prefix(lib, q=Q, k=K, v=V, m=M, B=1, H=1, n=16, d=16, dt=0, chunk=0, out=O, 
 
 def decode(lib, q=Q, k=K, v=V, B=1, Hq=2, Hkv=1, d=16, dt=0, S_=S, z=Z, out=O):
     return lib.la_decode_step(q, k, v, B, Hq, Hkv, d, dt, S_, z, out, None)
+
+
+def test_feature_map_rejections(lib):
+    """The *_phi entry points reject an unknown feature map, and run every
+    other check of their plain counterparts (each call below fails a check,
+    so nothing is launched)."""
+    for phi in (2, -1, 7):
+        assert lib.la_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 0, phi, O, WSP, BIG, None) == UNSUP
+        assert lib.la_causal_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 1, phi, 0, O, None, None, WSP, BIG, None) == UNSUP
+        assert lib.la_decode_step_phi(Q, K, V, 1, 2, 1, 16, 0, phi, S, Z, O, None) == UNSUP
+    for phi in (la.LA_PHI_RELU1, la.LA_PHI_ELU1):
+        assert lib.la_forward_phi(None, K, V, 1, 2, 1, 16, 16, 0, phi, O, WSP, BIG, None) == NULL
+        assert lib.la_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 0, phi, K, WSP, BIG, None) == ALIAS
+        assert lib.la_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 0, phi, O, WSP, 16, None) == WS
+        assert lib.la_causal_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 1, phi, 48, O, None, None, WSP, BIG, None) == UNSUP
+        assert lib.la_causal_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 1, phi, 0, O, S + 4, None, WSP, BIG, None) == ALIGN
+        assert lib.la_decode_step_phi(Q, K, V, 1, 3, 2, 16, 0, phi, S, Z, O, None) == SHAPE
+        assert lib.la_decode_step_phi(Q, K, V, 1, 2, 1, 16, 0, phi, S, Z, S, None) == ALIAS
 
 
 def test_forward_rejections(lib):

@@ -394,3 +394,82 @@ def test_single_launch_matches_three_launch_path(gpu):
     c = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64))
     assert np.array_equal(a, c)
     check(a, b, li.BF16, "single vs three launches")
+
+
+# ---------------------------------------------------------------------------
+# The ELU + 1 feature map (la_*_phi with LA_PHI_ELU1): the general state,
+# scan and output kernels and the decode kernels, against the oracle.
+# ---------------------------------------------------------------------------
+ELU_CASES = [
+    (1, 1, 1, 256, 16, 0),
+    (2, 4, 2, 1000, 64, 64),
+    (1, 2, 2, 300, 128, 32),
+    (2, 3, 1, 129, 33, 0),
+    (1, 4, 1, 65, 100, 0),
+]
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("case", ELU_CASES, ids=_small_id)
+def test_elu1_noncausal(gpu, dtype, case):
+    B, Hq, Hkv, n, d, _ = case
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=30, scaled=True)
+    g = host(gpu.la_forward(dev(q), dev(k), dev(v), phi="elu1"))
+    check(g, oracle.forward(q, k, v, phi="elu1"), dtype, f"elu1 forward {_small_id(case)} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("case", ELU_CASES, ids=_small_id)
+def test_elu1_causal_and_state(gpu, dtype, case):
+    B, Hq, Hkv, n, d, chunk = case
+    chunk = fit_chunk(gpu, dtype, d, chunk)
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=31, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=chunk, want_state=True, phi="elu1")
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True, phi="elu1")
+    check(host(out), ref, dtype, f"elu1 causal {_small_id(case)} {dtype}")
+    tol = 1e-4 if dtype == li.F32 else 1e-2  # phi(K) rounded to the input dtype
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=tol, atol=tol * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=tol)
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_elu1_causal_chunks_bf16(gpu, chunk):
+    B, H, n, d = 1, 2, 700, 64
+    chunk = fit_chunk(gpu, li.BF16, d, chunk)
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.BF16, seed=32, scaled=True)
+    out = gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=chunk, phi="elu1")
+    check(host(out), oracle.causal(q, k, v, phi="elu1"), li.BF16, f"elu1 causal chunk {chunk}")
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("d", [16, 64, 128, 33])
+def test_elu1_decode_continues_causal(gpu, dtype, d):
+    B, Hq, Hkv, n, T = 2, 4, 2, 48, 3
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, dtype, seed=33, scaled=True)
+    full, Sf, zf = oracle.causal(q, k, v, want_state=True, phi="elu1")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    S, z = gpu.la_causal_forward(None, kd[:, :, :n - T].contiguous(), vd[:, :, :n - T].contiguous(), Hq=Hq,
+                                 phi="elu1")
+    for t in range(n - T, n):
+        o = gpu.la_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), S, z,
+                               phi="elu1")
+        check(host(o), full[:, :, t], dtype, f"elu1 decode d={d} step {t}")
+    tol = 1e-4 if dtype == li.F32 else 1e-2
+    np.testing.assert_allclose(S.cpu().numpy(), Sf, rtol=tol, atol=tol * np.abs(Sf).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zf, rtol=tol)
+
+
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_elu1_equals_relu1_on_positive_inputs(gpu, dtype):
+    """On strictly positive Q and K both maps are x + 1: the ELU path (general
+    kernels) and the relu + 1 path (the single-launch causal and the d = 64
+    non-causal kernels) agree to the arithmetic's rounding."""
+    import torch
+    B, H, n, d = 2, 2, 1000, 64
+    q, k, v, _ = li.qkv(B, H, H, n, d, dtype, seed=34, scaled=True)
+    qd, kd, vd = dev(q).abs() + 0.01, dev(k).abs() + 0.01, dev(v)
+    for f, kw in ((gpu.la_forward, {}), (gpu.la_causal_forward, {"chunk": 64})):
+        a = f(qd, kd, vd, phi="elu1", **kw).float()
+        b = f(qd, kd, vd, **kw).float()
+        err = ((a - b).abs().amax(dim=-1) / b.abs().amax(dim=-1)).max().item()
+        assert err < (1e-5 if dtype == li.F32 else 1e-2), (f.__name__, dtype, err)
