@@ -57,6 +57,11 @@ WORKLOADS = {
                           mask="random", steps=50),
     "gqa_causal": dict(form="causal", B=1, Hq=32, Hkv=8, n=65536, d=128, dt="bf16", chunk=0, scaled=True, steps=20),
     "decode": dict(form="decode", B=128, Hq=32, Hkv=8, d=128, dt="bf16", prefix=4096, scaled=True, steps=256),
+    # the ELU + 1 feature map (la_*_phi), on the general kernels
+    "causal_elu": dict(form="causal", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", chunk=64, scaled=True, steps=200,
+                       phi="elu1"),
+    "forward_elu": dict(form="forward", B=2, Hq=8, Hkv=8, n=4096, d=64, dt="bf16", scaled=False, steps=200,
+                        phi="elu1"),
 }
 
 DESCRIPTIONS = {
@@ -67,6 +72,8 @@ DESCRIPTIONS = {
     "prefix_random": "unnormalised QK^T V with prefix mask m_i ~ U{0..n-1}, fp32",
     "gqa_causal": "long-context GQA causal normalised linear attention, bf16 in, fp32 state",
     "decode": "recurrent decode step, fp32 state prefilled from a 4096-token prefix, bf16 q/k/v",
+    "causal_elu": "causal normalised linear attention, phi=ELU+1, bf16 in, fp32 state",
+    "forward_elu": "non-causal normalised linear attention, phi=ELU+1, bf16 in, fp32 accumulation",
 }
 
 
@@ -154,6 +161,7 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
 
     threads = oracle.num_threads()
     form = w["form"]
+    phi = w.get("phi", "relu1")
     if form == "decode":
         B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
         rng = np.random.default_rng(1)
@@ -180,15 +188,15 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
         qs, ks, vs = (np.ascontiguousarray(x[:, :, :n_s]) for x in (q, k, v))
 
         def call():
-            oracle.causal(qs, ks, vs)
+            oracle.causal(qs, ks, vs, phi=phi)
 
         per = B * Hq * n_s
         what = f"the first {n_s} tokens of all {Hq} query heads (causal, d={d})"
         cores = min(threads, B * Hkv)
     else:
         bs = max(1, min(B, -(-threads // Hkv)))
-        fn = {"causal": lambda a, b_, c: oracle.causal(a, b_, c),
-              "forward": lambda a, b_, c: oracle.forward(a, b_, c),
+        fn = {"causal": lambda a, b_, c: oracle.causal(a, b_, c, phi=phi),
+              "forward": lambda a, b_, c: oracle.forward(a, b_, c, phi=phi),
               "prefix": lambda a, b_, c: oracle.prefix_mask(a, b_, c, m)}[form]
         state = {"r": 0}
 
@@ -269,12 +277,14 @@ def run(name, args):
         need = la.la_workspace_bytes(op, B, Hq, Hkv, n, d, ladt, chunk)
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
+        phi = w.get("phi", "relu1")
+
         def step(i):
             qq, kk, vv, oo = sets[i % rot]
             if form == "causal":
-                la.la_causal_forward(qq, kk, vv, chunk=chunk, out=oo, ws=ws)
+                la.la_causal_forward(qq, kk, vv, chunk=chunk, out=oo, ws=ws, phi=phi)
             elif form == "forward":
-                la.la_forward(qq, kk, vv, out=oo, ws=ws)
+                la.la_forward(qq, kk, vv, out=oo, ws=ws, phi=phi)
             else:
                 la.la_prefix_mask_forward(qq, kk, vv, md, chunk=chunk, out=oo, ws=ws)
 
@@ -296,7 +306,8 @@ def run(name, args):
     nbytes = algorithmic_bytes(w)
     flops = algorithmic_flops(w)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    single = form == "causal" and w["dt"] == "bf16" and w["d"] == 64 and w["Hq"] == w["Hkv"]
+    single = (form == "causal" and w["dt"] == "bf16" and w["d"] == 64 and w["Hq"] == w["Hkv"]
+              and w.get("phi", "relu1") == "relu1")
     roof = {
         "bound": "hbm",
         "kernel": "k_causal_fused (the call's one launch)" if single else
@@ -317,7 +328,7 @@ def run(name, args):
     if form != "decode" and flops / (mpeak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
         roof["note"] = "the MFMA time of the algorithmic flops exceeds their HBM time: compare both fractions"
     cfg = {"workload": DESCRIPTIONS[name], "name": name}
-    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix") if kk in w})
+    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix", "phi") if kk in w})
     if form != "decode":
         cfg.update({"global_batch": w["B"], "seq_len": w["n"]})
     line = {

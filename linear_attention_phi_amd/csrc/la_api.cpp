@@ -207,8 +207,9 @@ la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B,
       overlaps(ws, need, v, kvb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream, (int)phi};
-  // the d = 64 kernels split phi(K) as relu(K) + 1; ELU + 1 takes the general path
-  if (phi == LA_PHI_RELU1 && forward_bf16_applies(n, d, (int)dtype)) {
+  // the fp32 d = 64 kernels split phi(K) as relu(K) + 1; with ELU + 1 fp32
+  // takes the general path
+  if (forward_bf16_applies(n, d, (int)dtype)) {  // either feature map
     if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_bf16(a, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
@@ -257,7 +258,7 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
   if (overlaps(ws, need, out, qb) || overlaps(ws, need, S_final, sb) || overlaps(ws, need, z_final, zb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream, (int)phi};
-  if (phi == LA_PHI_RELU1 && q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {
+  if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // either feature map
     const Plan fp = make_fused_plan(n);
     if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_causal_fused(a, fp, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;

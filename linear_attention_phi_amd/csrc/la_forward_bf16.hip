@@ -34,7 +34,9 @@
 // hanging.
 //
 // phi(K)^T V is formed as relu(K)^T V + 1 (x) sum_t V_t and z as
-// sum_t relu(K_t) + (number of keys), exactly as in the causal kernels.
+// sum_t relu(K_t) + (number of keys), exactly as in the causal kernels; with
+// ELU + 1 (template PM) phi(K) and phi(Q) are rounded to bf16 in the tiles
+// and fragments instead, and key rows past the end are 0, not phi(0).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,7 +111,9 @@ __device__ __forceinline__ float* state_row(StateLds& L, int c, int b) {
   return reinterpret_cast<float*>(L.reg[c] + (b < 32 ? TILE_B : 0)) + (b & 31) * RSF;
 }
 
+template <int PM>
 __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLds& L) {
+  constexpr bool SPLIT = PM == PM_RELU1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
   const int64_t seg = bid / A.NKV, head = bid % A.NKV;
   const int hbytes = (int)(A.n * FD * 2);  // one head's rows (n <= 2^24)
@@ -136,8 +140,9 @@ __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLd
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       u32x4 x = kr[u];
+      const bool real = prow + 8 * u < nv;  // ELU + 1: rows past the end hold 0, not phi(0)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = relu2(x[j]);
+      for (int j = 0; j < 4; ++j) x[j] = SPLIT ? relu2(x[j]) : (real ? elu2(x[j]) : 0u);
       *reinterpret_cast<u32x4*>(tK + (prow + 8 * u) * RS + pcol) = x;
     }
 #pragma unroll
@@ -158,12 +163,14 @@ __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLd
     // column sums of V (b = 32 nb + r) and z (a = 32 ab + r)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float cs = 0.0f;
+      float cs = 0.0f;  // (the ones part of relu + 1 only)
+      if (SPLIT) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) cs = dot2(pair(vt[nb][kt], p), ONE2, cs);
-      cs += __shfl_xor(cs, 32);
+          for (int p = 0; p < 4; ++p) cs = dot2(pair(vt[nb][kt], p), ONE2, cs);
+        cs += __shfl_xor(cs, 32);
+      }
       if (h == 0) L.vsum[w][32 * nb + r] = cs;
     }
 #pragma unroll
@@ -174,7 +181,7 @@ __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLd
 #pragma unroll
         for (int p = 0; p < 4; ++p) zp = dot2(pair(kt_[ab][kt], p), ONE2, zp);
       zp += __shfl_xor(zp, 32);
-      if (h == 0) L.zloc[w][32 * ab + r] = zp + (float)nv;
+      if (h == 0) L.zloc[w][32 * ab + r] = zp + (SPLIT ? (float)nv : 0.0f);
     }
     // dS = relu(K)^T V, block (ab, bb): rows a, columns b; written transposed
     // (row b, four contiguous a per q)
@@ -297,6 +304,7 @@ __device__ __forceinline__ void fwd_reduce(const FwdArgs& A, int64_t bid) {
     __hip_atomic_store(A.rflag + head * RED_BLOCKS + slice, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int PM>
 __device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (&Lout)[W][TILE_B]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
   const int64_t seg = bid / A.NQ, qh = bid % A.NQ, kvh = qh / A.R;
@@ -351,7 +359,7 @@ __device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (
       for (int kb = 0; kb < 4; ++kb) {
         u32x4 x = qraw[j][ib][kb];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = phi2(x[e]);
+        for (int e = 0; e < 4; ++e) x[e] = PM == PM_RELU1 ? phi2(x[e]) : elu2(x[e]);
         qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
       }
 #pragma unroll
@@ -387,15 +395,16 @@ union FwdLds {
   uint8_t out[W][TILE_B];
 };
 
+template <int PM>
 __global__ __launch_bounds__(WNT) void k_fwd_one(FwdArgs A) {
   __shared__ __attribute__((aligned(16))) FwdLds L;
   const int64_t nS = A.NKV * A.nseg, nR = A.NKV * RED_BLOCKS, b = blockIdx.x;
   if (b < nS)
-    fwd_state(A, b, L.state);
+    fwd_state<PM>(A, b, L.state);
   else if (b < nS + nR)
     fwd_reduce(A, b - nS);
   else
-    fwd_out(A, b - nS - nR, L.out);
+    fwd_out<PM>(A, b - nS - nR, L.out);
 }
 
 }  // namespace
@@ -433,7 +442,10 @@ int launch_forward_bf16(const Fwd& a, uint64_t epoch) {
   FwdArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
             reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, nchunks, nseg, NKV, NQ,
             a.Hq / a.Hkv, part, tot, sflag, rflag, err, epoch};
-  k_fwd_one<<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
+  if (a.phi == 1)
+    k_fwd_one<PM_ELU1><<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
+  else
+    k_fwd_one<PM_RELU1><<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
   return (int)hipGetLastError();
 }
 

@@ -88,7 +88,14 @@ __device__ __forceinline__ float* state_row(CpLds& L, int c, int b) {
   return reinterpret_cast<float*>(L.reg[c] + (b < 32 ? TILE_B : 0)) + (b & 31) * RSF;
 }
 
+// PM: the feature map.  relu + 1 is split as relu(K) (exact in bf16) and the
+// ones part (column sums of V, the key count in z, sum_a phi(Q_i)[a] at the
+// start of each score); ELU + 1 has no such split: phi(K) and phi(Q) are
+// rounded to bf16 in the tiles and fragments, and rows past the sequence end
+// are stored as 0, not phi(0) = 1.
+template <int PM>
 __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
+  constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) CpLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
   const int64_t seg = blockIdx.x / A.NH, head = blockIdx.x % A.NH;
@@ -136,8 +143,9 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       u32x4 x = kr[u];
+      const bool real = prow + 8 * u < nv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = relu2(x[j]);
+      for (int j = 0; j < 4; ++j) x[j] = SPLIT ? relu2(x[j]) : (real ? elu2(x[j]) : 0u);
       *reinterpret_cast<u32x4*>(tK + (prow + 8 * u) * RS + pcol) = x;
     }
 #pragma unroll
@@ -167,15 +175,16 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     wave_lds_sync();
     // column sums of V (b = 32 nb + r): the ones^T V part of the chunk's
     // state (phi(K) = relu(K) + 1), added to every row a below
-    float cs[2];
+    float cs[2] = {0.0f, 0.0f};
+    if (SPLIT) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      cs[nb] = 0.0f;
+      for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) cs[nb] = dot2(pair(vt[nb][kt], p), ONE2, cs[nb]);
-      cs[nb] += __shfl_xor(cs[nb], 32);
+          for (int p = 0; p < 4; ++p) cs[nb] = dot2(pair(vt[nb][kt], p), ONE2, cs[nb]);
+        cs[nb] += __shfl_xor(cs[nb], 32);
+      }
     }
     // z of the chunk: sum_t relu(K_t)[a] + nv, for a = 32 ab + r
 #pragma unroll
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) zp = dot2(pair(kt_[ab][kt], p), ONE2, zp);
       zp += __shfl_xor(zp, 32);
-      if (h == 0) L.zloc[w][32 * ab + r] = zp + (float)nv;
+      if (h == 0) L.zloc[w][32 * ab + r] = zp + (SPLIT ? (float)nv : 0.0f);
     }
     // dS = relu(K)^T V + ones^T V, block (ab, bb): rows a, columns b; written
     // transposed (row b, four contiguous a per q) into the state tile
@@ -212,10 +221,11 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       for (int kb = 0; kb < 4; ++kb) {
         u32x4 x = qr[ib][kb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = phi2(x[j]);
+        for (int j = 0; j < 4; ++j) x[j] = SPLIT ? phi2(x[j]) : elu2(x[j]);
         qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
       }
-    // P^T blocks (key block jb, query block ib), jb <= ib:
+    // P^T blocks (key block jb, query block ib), jb <= ib (with ELU + 1 the
+    // tile holds phi(K) and the accumulators start at 0):
     //   P_ij = phi(Q_i) . relu(K_j) + sum_a phi(Q_i)[a]
     // (the second term, the same for every key, is the accumulators' start
     // value: this lane's column is query r, whose features the lane pair
@@ -224,11 +234,13 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       float qs = 0.0f;
+      if (SPLIT) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) qs = dot2(pair(qf[ib][kb], p), ONE2, qs);
-      qs += __shfl_xor(qs, 32);
+          for (int p = 0; p < 4; ++p) qs = dot2(pair(qf[ib][kb], p), ONE2, qs);
+        qs += __shfl_xor(qs, 32);
+      }
       float ds = 0.0f;
 #pragma unroll
       for (int jb = 0; jb <= ib; ++jb) {
@@ -455,7 +467,10 @@ int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch) {
   FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
               reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, p.nchunks, p.nseg, NH,
               agg, flags, epoch, a.S_final, a.z_final, err};
-  k_causal_fused<<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
+  if (a.phi == 1)
+    k_causal_fused<PM_ELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
+  else
+    k_causal_fused<PM_RELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
   return (int)hipGetLastError();
 }
 

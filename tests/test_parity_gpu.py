@@ -401,6 +401,7 @@ def test_single_launch_matches_three_launch_path(gpu):
 # scan and output kernels and the decode kernels, against the oracle.
 # ---------------------------------------------------------------------------
 ELU_CASES = [
+    (2, 3, 3, 1500, 64, 64),   # bf16: the single-launch causal kernel, 3 segments, ragged tail
     (1, 1, 1, 256, 16, 0),
     (2, 4, 2, 1000, 64, 64),
     (1, 2, 2, 300, 128, 32),
