@@ -207,13 +207,11 @@ la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B,
       overlaps(ws, need, v, kvb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream, (int)phi};
-  // the fp32 d = 64 kernels split phi(K) as relu(K) + 1; with ELU + 1 fp32
-  // takes the general path
   if (forward_bf16_applies(n, d, (int)dtype)) {  // either feature map
     if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_bf16(a, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
-  if (phi == LA_PHI_RELU1 && forward_f32_applies(n, d, (int)dtype)) {
+  if (forward_f32_applies(n, d, (int)dtype)) {  // either feature map
     if (B * Hq * forward_f32_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_f32(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }

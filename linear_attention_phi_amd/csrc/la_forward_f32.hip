@@ -36,6 +36,7 @@
 //
 // phi(K) = relu(K) + 1 is formed in fp32; padded keys (past n) read as zero,
 // so their phi(K) = 1 meets V = 0 in S, and z counts only the n real keys.
+// With ELU + 1 (template ELU) phi(K) of a padded key is set to 0.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,6 +82,11 @@ struct St32Lds {
   f32x4 z[NW][16];        // each wave's z[4 m .. 4 m + 3]
 };
 
+// ELU selects phi = ELU + 1 (alpha = 1: x + 1 for x > 0, e^x otherwise)
+// instead of relu + 1; keys past the end then count as 0, not phi(0) = 1.
+__device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
+
+template <bool ELU>
 __global__ __launch_bounds__(WNT) void k_fwd32_state(Fwd32Args A) {
   __shared__ St32Lds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, kq = lane >> 4;
@@ -111,15 +117,21 @@ __global__ __launch_bounds__(WNT) void k_fwd32_state(Fwd32Args A) {
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int jp = 0; jp < 4; ++jp) acc[j][jp] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4 zr = f32x4{0.0f, 0.0f, 0.0f, 0.0f};  // sum of relu(K) over this lane's keys
+  f32x4 zr = f32x4{0.0f, 0.0f, 0.0f, 0.0f};  // sum of relu(K) (ELU: of phi(K)) over this lane's keys
 #pragma unroll
   for (int s = 0; s < TW / 4; ++s) {
     f32x4 pk;
+    const bool real = 4 * s + kq < nv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float x = fmaxf(kr[s][j], 0.0f);
-      zr[j] += x;
-      pk[j] = x + 1.0f;
+      if (ELU) {
+        pk[j] = real ? elu1(kr[s][j]) : 0.0f;
+        zr[j] += pk[j];
+      } else {
+        const float x = fmaxf(kr[s][j], 0.0f);
+        zr[j] += x;
+        pk[j] = x + 1.0f;
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(WNT) void k_fwd32_state(Fwd32Args A) {
   for (int j = 0; j < 4; ++j) {
     zr[j] += __shfl_xor(zr[j], 16);
     zr[j] += __shfl_xor(zr[j], 32);
-    zr[j] += (float)nv;  // the ones of phi(K) = relu(K) + 1, real keys only
+    if (!ELU) zr[j] += (float)nv;  // the ones of phi(K) = relu(K) + 1, real keys only
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -192,6 +204,7 @@ __global__ __launch_bounds__(RED_THREADS) void k_fwd32_reduce(Fwd32Args A) {
   }
 }
 
+template <bool ELU>
 __global__ __launch_bounds__(WNT) void k_fwd32_out(Fwd32Args A) {
   __shared__ __attribute__((aligned(16))) float tiles[NW][TW * RQ];  // each wave's Q rows, then its output rows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, m = lane & 15, kq = lane >> 4;
@@ -242,7 +255,7 @@ __global__ __launch_bounds__(WNT) void k_fwd32_out(Fwd32Args A) {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float x = fmaxf(qr[qb][tt][jj], 0.0f) + 1.0f;
+        const float x = ELU ? elu1(qr[qb][tt][jj]) : fmaxf(qr[qb][tt][jj], 0.0f) + 1.0f;
         den = fmaf(x, zo[tt][jj], den);
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) o[bb] = mfma4(so[bb][tt][jj], x, o[bb]);
@@ -283,9 +296,16 @@ int launch_forward_f32(const Fwd& a) {
   Fwd32Args A{reinterpret_cast<const float*>(a.q), reinterpret_cast<const float*>(a.k),
               reinterpret_cast<const float*>(a.v), reinterpret_cast<float*>(a.out), a.n, nseg, NKV, NQ,
               a.Hq / a.Hkv, part, tot};
-  k_fwd32_state<<<dim3((unsigned)(NKV * nseg)), WNT, 0, st>>>(A);
+  const bool elu = a.phi == 1;
+  if (elu)
+    k_fwd32_state<true><<<dim3((unsigned)(NKV * nseg)), WNT, 0, st>>>(A);
+  else
+    k_fwd32_state<false><<<dim3((unsigned)(NKV * nseg)), WNT, 0, st>>>(A);
   k_fwd32_reduce<<<dim3((unsigned)(NKV * RED_BLOCKS)), RED_THREADS, 0, st>>>(A);
-  k_fwd32_out<<<dim3((unsigned)(NQ * nseg)), WNT, 0, st>>>(A);
+  if (elu)
+    k_fwd32_out<true><<<dim3((unsigned)(NQ * nseg)), WNT, 0, st>>>(A);
+  else
+    k_fwd32_out<false><<<dim3((unsigned)(NQ * nseg)), WNT, 0, st>>>(A);
   return (int)hipGetLastError();
 }
 
