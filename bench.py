@@ -106,16 +106,24 @@ def algorithmic_flops(w):
     return 2 * (B * Hkv * n * d * d + B * Hq * (n * d * d + 2 * n * C * d))
 
 
-# Counter-based HBM traffic of the single-launch causal kernel: taken with
-# rocprofv3 (FETCH_SIZE and WRITE_SIZE passes, scaled by the same counters'
-# readings for a plain 64 MiB device copy) and recorded under profiles/
-# together with a hash of the kernel's sources; reported only while the
-# sources still hash the same (null once the kernel has changed).
-COUNTER_FILE = os.path.join(ROOT, "profiles", "k_causal_fused_causal_bf16_B8H8n2048d64_counters.md")
-COUNTER_SOURCES = ["la_fused.hip", "la_bf16.h", "la_device.h", "la_internal.h"]
+# Counter-based HBM traffic of the workloads whose call is one launch: taken
+# with rocprofv3 (FETCH_SIZE and WRITE_SIZE passes, scaled by the same
+# counters' readings for a plain 64 MiB device copy) and recorded under
+# profiles/ together with a hash of the kernel's sources; reported only while
+# the sources still hash the same (null once the kernel has changed).
+COUNTERS = {
+    "causal": ("k_causal_fused_causal_bf16_B8H8n2048d64_counters.md",
+               ["la_fused.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
+    "forward_bf16": ("k_fwd_one_forward_bf16_B2H8n4096d64_counters.md",
+                     ["la_forward_bf16.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
+    "decode": ("k_decode128_decode_B128Hq32Hkv8d128_counters.md",
+               ["la_kernels.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
+}
+SINGLE_LAUNCH = {"causal": "k_causal_fused", "forward_bf16": "k_fwd_one", "decode": "k_decode128",
+                 "causal_elu": "k_causal_fused", "forward_elu": "k_fwd_one"}
 
 
-def kernel_source_hash(files=COUNTER_SOURCES):
+def kernel_source_hash(files):
     import hashlib
 
     h = hashlib.sha256()
@@ -125,10 +133,13 @@ def kernel_source_hash(files=COUNTER_SOURCES):
     return h.hexdigest()
 
 
-def counter_traffic():
-    """HBM bytes per launch from the recorded counters, or None."""
+def counter_traffic(name):
+    """HBM bytes per launch of workload name from the recorded counters, or None."""
+    if name not in COUNTERS:
+        return None
+    fname, sources = COUNTERS[name]
     try:
-        with open(COUNTER_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", fname)) as fh:
             text = fh.read()
     except OSError:
         return None
@@ -138,7 +149,7 @@ def counter_traffic():
         for key in ("source_sha256:", "hbm_bytes_per_launch:"):
             if line.startswith(key):
                 vals[key[:-1]] = line[len(key):].strip()
-    if vals.get("source_sha256") != kernel_source_hash() or "hbm_bytes_per_launch" not in vals:
+    if vals.get("source_sha256") != kernel_source_hash(sources) or "hbm_bytes_per_launch" not in vals:
         return None
     return float(vals["hbm_bytes_per_launch"])
 
@@ -306,17 +317,15 @@ def run(name, args):
     nbytes = algorithmic_bytes(w)
     flops = algorithmic_flops(w)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    single = (form == "causal" and w["dt"] == "bf16" and w["d"] == 64 and w["Hq"] == w["Hkv"]
-              and w.get("phi", "relu1") == "relu1")
+    single = SINGLE_LAUNCH.get(name)
     roof = {
         "bound": "hbm",
-        "kernel": "k_causal_fused (the call's one launch)" if single else
-                  ("k_decode (the call's one launch)" if form == "decode" else f"la_{form} (whole call)"),
+        "kernel": f"{single} (the call's one launch)" if single else f"la_{form} (whole call)",
         "achieved": achieved,
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": achieved / HBM_PEAK_GBS,
-        "traffic": counter_traffic() if single and name == "causal" else None,
+        "traffic": counter_traffic(name),
         "algorithmic_bytes_per_call": nbytes,
         "algorithmic_flops_per_call": flops,
         "call_us_mean": ms * 1e3,
