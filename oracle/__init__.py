@@ -54,7 +54,7 @@ def _load():
         lib.lao_num_threads.restype = I
         lib.lao_forward.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P]
         lib.lao_causal.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P, P, P]
-        lib.lao_prefix_mask.argtypes = [P, P, P, I, P, I64, I64, I64, I64, P, I64, P]
+        lib.lao_prefix_mask.argtypes = [P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
         lib.lao_decode_step.argtypes = [P, P, P, I, I, I64, I64, I64, I64, P, P, P]
         for f in ("lao_forward", "lao_causal", "lao_prefix_mask", "lao_decode_step"):
             getattr(lib, f).restype = None
@@ -157,19 +157,21 @@ def causal(q, k, v, rows=None, want_state=False, Hq=None, phi="relu1"):
 
 
 def prefix_mask(q, k, v, m, rows=None):
-    """Unnormalised Q K^T V with prefix mask m (query i sees keys 0..m[i])."""
+    """Unnormalised Q K^T V with prefix mask m: query i of batch b sees keys
+    0..m[i] (m of shape (n,), shared by the batches) or 0..m[b, i] (m of
+    shape (B, n), one mask per batch)."""
     q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
     dt = _same_dtype(cq, ck, cv)
     B, H, n, d = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("prefix_mask needs q, k and v of one shape [B,H,n,d]")
     m = np.ascontiguousarray(np.asarray(m, dtype=np.int64))
-    if m.shape != (n,) or (n and (m.min() < 0 or m.max() >= n)):
-        raise ValueError("m must have shape (n,) with values in [0, n)")
+    if m.shape not in ((n,), (B, n)) or (n and (m.min() < 0 or m.max() >= n)):
+        raise ValueError("m must have shape (n,) or (B, n) with values in [0, n)")
     r, nr = _rows(rows, n)
     out = np.empty((B, H, nr, d), dtype=np.float64)
-    _load().lao_prefix_mask(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(m), B, H, n, d,
-                            _ptr(r), nr, _ptr(out))
+    _load().lao_prefix_mask(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(m), 0 if m.ndim == 1 else n,
+                            B, H, n, d, _ptr(r), nr, _ptr(out))
     return out
 
 

@@ -161,23 +161,22 @@ void lao_causal(const void* q, const void* k, const void* v, int dtype,
 }
 
 void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
-                     const int64_t* m, int64_t B, int64_t H, int64_t n,
-                     int64_t d, const int64_t* rows, int64_t nrows,
+                     const int64_t* m, int64_t m_bstride, int64_t B, int64_t H,
+                     int64_t n, int64_t d, const int64_t* rows, int64_t nrows,
                      double* out) {
   const int64_t nr = rows ? nrows : n;
-  /* Lists L_t = {selected rows r : m[row r] == t}, as a counting sort. */
-  int64_t* start = (int64_t*)calloc((size_t)(n + 1), sizeof(int64_t));
-  int64_t* list = (int64_t*)malloc((size_t)(nr > 0 ? nr : 1) * sizeof(int64_t));
-  for (int64_t r = 0; r < nr; ++r) start[m[rows ? rows[r] : r] + 1] += 1;
-  for (int64_t t = 0; t < n; ++t) start[t + 1] += start[t];
-  int64_t* fill = (int64_t*)malloc((size_t)(n + 1) * sizeof(int64_t));
-  memcpy(fill, start, (size_t)(n + 1) * sizeof(int64_t));
-  for (int64_t r = 0; r < nr; ++r) list[fill[m[rows ? rows[r] : r]]++] = r;
-  free(fill);
-
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t h = 0; h < H; ++h) {
+      const int64_t* mb = m + b * m_bstride; /* this batch's mask */
+      /* Lists L_t = {selected rows r : mb[row r] == t}, as a counting sort. */
+      int64_t* start = (int64_t*)calloc((size_t)(n + 1), sizeof(int64_t));
+      int64_t* list = (int64_t*)malloc((size_t)(nr > 0 ? nr : 1) * sizeof(int64_t));
+      int64_t* fill = (int64_t*)malloc((size_t)(n + 1) * sizeof(int64_t));
+      for (int64_t r = 0; r < nr; ++r) start[mb[rows ? rows[r] : r] + 1] += 1;
+      for (int64_t t = 0; t < n; ++t) start[t + 1] += start[t];
+      memcpy(fill, start, (size_t)(n + 1) * sizeof(int64_t));
+      for (int64_t r = 0; r < nr; ++r) list[fill[mb[rows ? rows[r] : r]]++] = r;
       double* P = (double*)calloc((size_t)(d * d), sizeof(double));
       double* kt = (double*)malloc((size_t)d * sizeof(double));
       for (int64_t t = 0; t < n; ++t) {
@@ -203,10 +202,11 @@ void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
       }
       free(P);
       free(kt);
+      free(start);
+      free(list);
+      free(fill);
     }
   }
-  free(start);
-  free(list);
 }
 
 void lao_decode_step(const void* q, const void* k, const void* v, int dtype,

@@ -53,11 +53,13 @@ void lao_causal(const void* q, const void* k, const void* v, int dtype,
                 int64_t d, const int64_t* rows, int64_t nrows, double* out,
                 double* S_final, double* z_final);
 
-/* Unnormalised prefix-mask form, identity feature map: query i sees keys
- * 0..m[i]; m is shared by every batch and head, each m[i] in [0, n). */
+/* Unnormalised prefix-mask form, identity feature map: query i of batch b
+ * sees keys 0..m[b * m_bstride + i], each in [0, n); m_bstride = 0 shares one
+ * mask [n] among the batches, m_bstride = n gives each its own ([B][n]).
+ * Every head of a batch uses that batch's mask. */
 void lao_prefix_mask(const void* q, const void* k, const void* v, int dtype,
-                     const int64_t* m, int64_t B, int64_t H, int64_t n,
-                     int64_t d, const int64_t* rows, int64_t nrows,
+                     const int64_t* m, int64_t m_bstride, int64_t B, int64_t H,
+                     int64_t n, int64_t d, const int64_t* rows, int64_t nrows,
                      double* out);
 
 /* One recurrent decode step.  S [B][Hkv][d][d] and z [B][Hkv][d] are

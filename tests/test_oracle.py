@@ -386,3 +386,25 @@ def test_elu1_decode_steps_continue_the_causal_pass():
         np.testing.assert_allclose(o, full[:, :, t], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(S, Sf, rtol=1e-12)
     np.testing.assert_allclose(z, zf, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Per-batch prefix masks m [B, n]: batch b's queries use row b.
+# ---------------------------------------------------------------------------
+def test_prefix_mask_per_batch_matches_brute_force():
+    B, H, n, d = 3, 2, 23, 3
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=40)
+    m = np.stack([li.mask(n, kind, rng=rng) for kind in ("random", "causal", "first")])
+    out = oracle.prefix_mask(q, k, v, m)
+    for b in range(B):
+        want = brute_prefix(q[b:b + 1], k[b:b + 1], v[b:b + 1], mask2d_from_m(m[b]))
+        np.testing.assert_allclose(out[b:b + 1], want, rtol=1e-12, atol=1e-12)
+    # rows differ, so the outputs differ from the shared-mask form with row 0
+    assert not np.allclose(out, oracle.prefix_mask(q, k, v, m[0]))
+
+
+def test_prefix_mask_per_batch_equal_rows_is_shared():
+    B, H, n, d = 2, 3, 31, 4
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=41)
+    m = li.mask(n, "random", rng=rng)
+    np.testing.assert_array_equal(oracle.prefix_mask(q, k, v, np.tile(m, (B, 1))), oracle.prefix_mask(q, k, v, m))
