@@ -55,6 +55,8 @@ WORKLOADS = {
                           mask="causal", steps=50),
     "prefix_random": dict(form="prefix", B=4, Hq=8, Hkv=8, n=8192, d=64, dt="f32", chunk=64, scaled=True,
                           mask="random", steps=50),
+    "prefix_random_batched": dict(form="prefix", B=4, Hq=8, Hkv=8, n=8192, d=64, dt="f32", chunk=64, scaled=True,
+                                  mask="random", batched=True, steps=50),
     "gqa_causal": dict(form="causal", B=1, Hq=32, Hkv=8, n=65536, d=128, dt="bf16", chunk=0, scaled=True, steps=20),
     "decode": dict(form="decode", B=128, Hq=32, Hkv=8, d=128, dt="bf16", prefix=4096, scaled=True, steps=256),
     # the ELU + 1 feature map (la_*_phi), on the general kernels
@@ -70,6 +72,7 @@ DESCRIPTIONS = {
     "forward_bf16": "non-causal normalised linear attention, phi=relu+1, bf16 in, fp32 accumulation",
     "prefix_causal": "unnormalised QK^T V with prefix mask m=arange(n), fp32",
     "prefix_random": "unnormalised QK^T V with prefix mask m_i ~ U{0..n-1}, fp32",
+    "prefix_random_batched": "unnormalised QK^T V with a prefix mask per batch, m[b, i] ~ U{0..n-1}, fp32",
     "gqa_causal": "long-context GQA causal normalised linear attention, bf16 in, fp32 state",
     "decode": "recurrent decode step, fp32 state prefilled from a 4096-token prefix, bf16 q/k/v",
     "causal_elu": "causal normalised linear attention, phi=ELU+1, bf16 in, fp32 state",
@@ -88,7 +91,7 @@ def algorithmic_bytes(w):
         B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
         return 2 * B * Hkv * (d * d + d) * 4 + B * (2 * Hq + 2 * Hkv) * d * e
     B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
-    extra = 8 * n if w["form"] == "prefix" else 0
+    extra = 8 * n * (w["B"] if w.get("batched") else 1) if w["form"] == "prefix" else 0
     return (2 * B * Hq * n * d + 2 * B * Hkv * n * d) * e + extra
 
 
@@ -208,13 +211,16 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
         bs = max(1, min(B, -(-threads // Hkv)))
         fn = {"causal": lambda a, b_, c: oracle.causal(a, b_, c, phi=phi),
               "forward": lambda a, b_, c: oracle.forward(a, b_, c, phi=phi),
-              "prefix": lambda a, b_, c: oracle.prefix_mask(a, b_, c, m)}[form]
+              "prefix": None}[form]
         state = {"r": 0}
 
         def call():
             b0 = (state["r"] * bs) % B
             state["r"] += 1
-            fn(q[b0:b0 + bs], k[b0:b0 + bs], v[b0:b0 + bs])
+            if form == "prefix":  # the batches' own mask rows when there is one per batch
+                oracle.prefix_mask(q[b0:b0 + bs], k[b0:b0 + bs], v[b0:b0 + bs], m if m.ndim == 1 else m[b0:b0 + bs])
+            else:
+                fn(q[b0:b0 + bs], k[b0:b0 + bs], v[b0:b0 + bs])
 
         per = bs * Hq * n
         what = f"{bs}-element slices of the batch (Hq={Hq} n={n} d={d})"
@@ -276,14 +282,18 @@ def run(name, args):
         q, k, v, rng = li.qkv(B, Hq, Hkv, n, d, dtc, seed=0, scaled=w["scaled"])
         md = None
         if form == "prefix":
-            m = li.mask(n, w["mask"], rng=rng)
+            if w.get("batched"):
+                m = np.stack([li.mask(n, w["mask"], rng=rng) for _ in range(B)])
+            else:
+                m = li.mask(n, w["mask"], rng=rng)
             md = li.to_torch(m).to(dev)
         qd, kd, vd = (li.to_torch(x).to(dev) for x in (q, k, v))
         set_bytes = 2 * (qd.numel() + kd.numel()) * qd.element_size()
         rot = max(1, min(16, -(-FOOTPRINT // set_bytes)))
         sets = [(qd, kd, vd, torch.empty_like(qd))] + [
             (qd.clone(), kd.clone(), vd.clone(), torch.empty_like(qd)) for _ in range(rot - 1)]
-        op = {"causal": la.LA_OP_CAUSAL, "forward": la.LA_OP_FORWARD, "prefix": la.LA_OP_PREFIX_MASK}[form]
+        op = {"causal": la.LA_OP_CAUSAL, "forward": la.LA_OP_FORWARD,
+              "prefix": la.LA_OP_PREFIX_MASK_BATCHED if w.get("batched") else la.LA_OP_PREFIX_MASK}[form]
         chunk = w.get("chunk", 0)
         need = la.la_workspace_bytes(op, B, Hq, Hkv, n, d, ladt, chunk)
         ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
@@ -337,7 +347,8 @@ def run(name, args):
     if form != "decode" and flops / (mpeak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
         roof["note"] = "the MFMA time of the algorithmic flops exceeds their HBM time: compare both fractions"
     cfg = {"workload": DESCRIPTIONS[name], "name": name}
-    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix", "phi") if kk in w})
+    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix", "phi", "batched")
+                if kk in w})
     if form != "decode":
         cfg.update({"global_batch": w["B"], "seq_len": w["n"]})
     line = {

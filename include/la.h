@@ -85,14 +85,15 @@ typedef int32_t la_phi;
 enum { LA_PHI_RELU1 = 0, LA_PHI_ELU1 = 1 };
 
 /* Operation codes for la_workspace_bytes. */
-enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2 };
+enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2, LA_OP_PREFIX_MASK_BATCHED = 3 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* la_status_str(la_status s);
 
 /* Workspace bytes needed by la_forward (op LA_OP_FORWARD), la_causal_forward
- * (LA_OP_CAUSAL) or la_prefix_mask_forward (LA_OP_PREFIX_MASK, pass Hq = Hkv
- * = H) for these sizes.  Returns 0 if the arguments are invalid. */
+ * (LA_OP_CAUSAL), la_prefix_mask_forward (LA_OP_PREFIX_MASK, pass Hq = Hkv
+ * = H) or la_prefix_mask_forward_batched (LA_OP_PREFIX_MASK_BATCHED, the
+ * same) for these sizes.  Returns 0 if the arguments are invalid. */
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv,
                           int64_t n, int64_t d, la_dtype dtype, int32_t chunk);
 
@@ -134,6 +135,19 @@ la_status la_prefix_mask_forward(const void* q, const void* k, const void* v,
                                  int64_t n, int64_t d, la_dtype dtype,
                                  int32_t chunk, void* out, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* The same form with one mask per batch: m is a device int64 array [B][n]
+ * and query i of batch b (every head) sees keys 0..m[b][i] (the masks of
+ * the trim-transformer page, "Masking", one per sequence).  Each row has the
+ * contract of la_prefix_mask_forward's m; the workspace is
+ * la_workspace_bytes(LA_OP_PREFIX_MASK_BATCHED, ...) (a bucket sort per
+ * batch).  Everything else as la_prefix_mask_forward. */
+la_status la_prefix_mask_forward_batched(const void* q, const void* k,
+                                         const void* v, const int64_t* m,
+                                         int64_t B, int64_t H, int64_t n,
+                                         int64_t d, la_dtype dtype,
+                                         int32_t chunk, void* out, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /* One recurrent decode step (trim-transformer 0.1.0, "Key-value caching":
  * use and update the cache in one call).  For every (b, kv head g):

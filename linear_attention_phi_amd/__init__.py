@@ -9,7 +9,8 @@ call fails, an exception is raised.
 Functions carry the C names:
   la_forward(q, k, v)                        non-causal
   la_causal_forward(q, k, v, chunk=0)        causal (optionally the final state)
-  la_prefix_mask_forward(q, k, v, m)         unnormalised Q K^T V, prefix mask m
+  la_prefix_mask_forward(q, k, v, m)         unnormalised Q K^T V, prefix mask m [n]
+                                             (or [B, n]: la_prefix_mask_forward_batched)
   la_decode_step(q, k, v, S, z)              one recurrent step (S, z in place)
   (la_forward, la_causal_forward and la_decode_step take phi="relu1" or
   phi="elu1"; the latter calls la_forward_phi / la_causal_forward_phi /
@@ -28,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblaphi.so")
 
 LA_F32, LA_BF16 = 0, 1
-LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK = 0, 1, 2
+LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK, LA_OP_PREFIX_MASK_BATCHED = 0, 1, 2, 3
 LA_PHI_RELU1, LA_PHI_ELU1 = 0, 1
 _PHI = {"relu1": LA_PHI_RELU1, "elu1": LA_PHI_ELU1}
 
@@ -65,12 +66,13 @@ def load():
         lib.la_forward.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, P, P, SZ, P]
         lib.la_causal_forward.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, P, P, SZ, P]
         lib.la_prefix_mask_forward.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, I32, P, P, SZ, P]
+        lib.la_prefix_mask_forward_batched.argtypes = [P, P, P, P, I64, I64, I64, I64, I32, I32, P, P, SZ, P]
         lib.la_decode_step.argtypes = [P, P, P, I64, I64, I64, I64, I32, P, P, P, P]
         lib.la_forward_phi.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, SZ, P]
         lib.la_causal_forward_phi.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, I32, P, P, P, P, SZ, P]
         lib.la_decode_step_phi.argtypes = [P, P, P, I64, I64, I64, I64, I32, I32, P, P, P, P]
         for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
-                  "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi"):
+                  "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -221,23 +223,26 @@ def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None
 
 
 def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):
-    """Unnormalised Q K^T V where query i sees keys 0..m[i] (m: int64 [n] on the GPU)."""
+    """Unnormalised Q K^T V where query i sees keys 0..m[i] (m: int64 [n] on the
+    GPU, shared by the batches), or query i of batch b keys 0..m[b, i] (m:
+    int64 [B, n], la_prefix_mask_forward_batched)."""
     torch = _torch()
     B, H, Hkv, n, d = _qkv(q, k, v)
     if Hkv != H:
         raise ValueError("the prefix-mask form needs as many key/value heads as query heads")
     dt = _dtype_code(q)
-    if m.dtype != torch.int64 or tuple(m.shape) != (n,):
-        raise ValueError("m must be an int64 tensor of shape (n,)")
+    if m.dtype != torch.int64 or tuple(m.shape) not in ((n,), (B, n)) or not m.is_contiguous():
+        raise ValueError("m must be a contiguous int64 tensor of shape (n,) or (B, n)")
+    batched = m.dim() == 2
     out = torch.empty_like(q) if out is None else out
     _expect(out, q.shape, q.dtype, "out")
-    need = la_workspace_bytes(LA_OP_PREFIX_MASK, B, H, H, n, d, dt, chunk)
+    need = la_workspace_bytes(LA_OP_PREFIX_MASK_BATCHED if batched else LA_OP_PREFIX_MASK, B, H, H, n, d, dt, chunk)
     if need == 0:
         raise LAError(4, f"la_prefix_mask_forward (chunk={chunk}, n={n}, d={d}, dtype={q.dtype})")
     ws = workspace(need, q.device) if ws is None else ws
-    _call(load().la_prefix_mask_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(m, "m"), B, H, n, d,
-                                        dt, chunk, _dev(out, "out"), _dev(ws, "ws"), ws.numel(),
-                                        _stream(q)), "la_prefix_mask_forward")
+    fn = "la_prefix_mask_forward_batched" if batched else "la_prefix_mask_forward"
+    _call(getattr(load(), fn)(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(m, "m"), B, H, n, d,
+                              dt, chunk, _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), fn)
     return out
 
 

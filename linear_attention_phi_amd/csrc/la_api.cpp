@@ -116,6 +116,7 @@ size_t required_ws(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, in
   if (out_plan) *out_plan = p;
   size_t bytes = state_bytes(p, B, Hkv);
   if (op == LA_OP_PREFIX_MASK) bytes += bucket_bytes(n, C);
+  if (op == LA_OP_PREFIX_MASK_BATCHED) bytes += (size_t)B * bucket_bytes(n, C);  // one sort per batch
   if (op == LA_OP_CAUSAL && fused_causal_applies(Hq, Hkv, n, d, (int)dt, C)) {
     const size_t f = fused_causal_ws_bytes(B * Hkv, make_fused_plan(n).nseg);
     if (f > bytes) bytes = f;
@@ -176,15 +177,17 @@ static int32_t prefix_chunk(bool prefix, int32_t chunk, la_dtype dtype, int64_t 
 
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dtype,
                           int32_t chunk) {
-  if (op != LA_OP_FORWARD && op != LA_OP_CAUSAL && op != LA_OP_PREFIX_MASK) return 0;
+  if (op != LA_OP_FORWARD && op != LA_OP_CAUSAL && op != LA_OP_PREFIX_MASK && op != LA_OP_PREFIX_MASK_BATCHED)
+    return 0;
+  const bool prefix = op == LA_OP_PREFIX_MASK || op == LA_OP_PREFIX_MASK_BATCHED;
   if (check_sizes(B, Hq, Hkv, n, d, dtype) != LA_OK) return 0;
   int C = 0;
   if (op == LA_OP_FORWARD) {
     C = forward_chunk(elem_bytes(dtype), padded_dim(d));
-  } else if (resolve_chunk(prefix_chunk(op == LA_OP_PREFIX_MASK, chunk, dtype, d), dtype, d, &C) != LA_OK) {
+  } else if (resolve_chunk(prefix_chunk(prefix, chunk, dtype, d), dtype, d, &C) != LA_OK) {
     return 0;
   }
-  if (op == LA_OP_PREFIX_MASK && (Hq != Hkv || (n + C - 1) / C > kMaxBuckets)) return 0;
+  if (prefix && (Hq != Hkv || (n + C - 1) / C > kMaxBuckets)) return 0;
   return required_ws(op, B, Hq, Hkv, n, d, dtype, C, nullptr);
 }
 
@@ -271,9 +274,11 @@ la_status la_causal_forward(const void* q, const void* k, const void* v, int64_t
                                ws_bytes, stream);
 }
 
-la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, const int64_t* m, int64_t B,
-                                 int64_t H, int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out,
-                                 void* ws, size_t ws_bytes, void* stream) {
+// The prefix form with one shared mask (batched = false: m [n]) or one mask
+// per batch (batched: m [B][n]).
+static la_status prefix_impl(const void* q, const void* k, const void* v, const int64_t* m, bool batched,
+                             int64_t B, int64_t H, int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out,
+                             void* ws, size_t ws_bytes, void* stream) {
   la_status st = check_sizes(B, H, H, n, d, dtype);
   if (st != LA_OK) return st;
   if (!q || !k || !v || !m || !out) return LA_ERR_NULL;
@@ -282,18 +287,30 @@ la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, co
   if ((st = resolve_chunk(prefix_chunk(true, chunk, dtype, d), dtype, d, &C)) != LA_OK) return st;
   if ((n + C - 1) / C > kMaxBuckets) return LA_ERR_UNSUPPORTED;
   const size_t eb = elem_bytes(dtype);
-  const size_t tb = (size_t)(B * H * n * d) * eb, mb = (size_t)n * sizeof(int64_t);
+  const size_t tb = (size_t)(B * H * n * d) * eb, mb = (size_t)(batched ? B : 1) * n * sizeof(int64_t);
   if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) || overlaps(out, tb, m, mb))
     return LA_ERR_ALIAS;
   Plan p;
-  const size_t need = required_ws(LA_OP_PREFIX_MASK, B, H, H, n, d, dtype, C, &p);
+  const size_t need = required_ws(batched ? LA_OP_PREFIX_MASK_BATCHED : LA_OP_PREFIX_MASK, B, H, H, n, d, dtype, C, &p);
   if ((st = check_grid(p, B, H)) != LA_OK) return st;
   if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
   if (overlaps(ws, need, q, tb) || overlaps(ws, need, k, tb) || overlaps(ws, need, v, tb) ||
       overlaps(ws, need, m, mb) || overlaps(ws, need, out, tb))
     return LA_ERR_ALIAS;
-  Fwd a{q, k, v, out, B, H, H, n, d, (int)dtype, m, nullptr, nullptr, ws, stream};
+  Fwd a{q, k, v, out, B, H, H, n, d, (int)dtype, m, nullptr, nullptr, ws, stream, 0, batched ? B : 1};
   return launch_prefix(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_prefix_mask_forward(const void* q, const void* k, const void* v, const int64_t* m, int64_t B,
+                                 int64_t H, int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  return prefix_impl(q, k, v, m, false, B, H, n, d, dtype, chunk, out, ws, ws_bytes, stream);
+}
+
+la_status la_prefix_mask_forward_batched(const void* q, const void* k, const void* v, const int64_t* m, int64_t B,
+                                         int64_t H, int64_t n, int64_t d, la_dtype dtype, int32_t chunk, void* out,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  return prefix_impl(q, k, v, m, true, B, H, n, d, dtype, chunk, out, ws, ws_bytes, stream);
 }
 
 la_status la_decode_step_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,

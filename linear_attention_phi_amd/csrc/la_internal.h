@@ -51,6 +51,7 @@ struct Fwd {
   void* ws;
   void* stream;
   int phi = 0;           // feature map of the normalised forms: 0 relu + 1, 1 ELU + 1
+  int64_t nmask = 1;     // prefix form: masks in m (1: shared [n]; B: one per batch, [B][n])
 };
 
 // Each returns 0 on success, else a nonzero HIP error code.

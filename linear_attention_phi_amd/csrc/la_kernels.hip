@@ -312,7 +312,8 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
                                                       int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
                                                       int64_t nseg_ws, const float* __restrict__ ws,
                                                       const int* __restrict__ perm,
-                                                      const int* __restrict__ boff, const int64_t* __restrict__ m) {
+                                                      const int* __restrict__ boff, const int64_t* __restrict__ m,
+                                                      int64_t H, int64_t nmask) {
   constexpr int FD = 64, C = 64, RS = PX_RS, QG = 16 * NWV, NT_ = 64 * NWV;
   constexpr int KVP = C * FD / 4 / NT_;  // 16-byte pieces of a K or V tile per thread
   static_assert(NWV == 4 || NWV == 8, "four or eight waves");
@@ -322,6 +323,12 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   __shared__ __attribute__((aligned(16))) float sS[16 * 64 * 4];  // S in operand order
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  {  // this batch's mask, buckets and permutation (one per batch, or one shared)
+    const int64_t mb = nmask > 1 ? bh / H : 0;
+    perm += mb * n;
+    boff += mb * (nchunks + 1);
+    m += mb * n;
+  }
   const float* qh = q + bh * n * FD;
   const float* kh = k + bh * n * FD;
   const float* vh = v + bh * n * FD;
@@ -495,7 +502,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
                                             const T* __restrict__ v, T* __restrict__ out, int64_t n, int d,
                                             int R, bool vec, int64_t nchunks, int64_t G, int64_t nseg,
                                             const float* __restrict__ ws, const int* __restrict__ perm,
-                                            const int* __restrict__ boff, const int64_t* __restrict__ m) {
+                                            const int* __restrict__ boff, const int64_t* __restrict__ m,
+                                            int64_t H, int64_t nmask) {
   constexpr int LQ = DP + PAD;  // row stride of sQ, sK, sST
   constexpr int LC = C + PAD;   // row stride of sKT, sVT, sP
   constexpr int NIB = C / 32;   // 32-row query / key blocks per chunk
@@ -527,6 +535,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+  if (FORM == PREFIX) {  // this batch's mask, buckets and permutation (one per batch, or one shared)
+    const int64_t mb = nmask > 1 ? bh / H : 0;
+    perm += mb * n;
+    boff += mb * (nchunks + 1);
+    m += mb * n;
+  }
   const T* kb = k + bh * n * d;
   const T* vb = v + bh * n * d;
 
@@ -1179,8 +1193,13 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
   }
 }
 
+// Workgroup b sorts mask b (m [nmask][n] into boff [nmask][nchunks + 1] and
+// perm [nmask][n]).
 __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks,
                                                  int* __restrict__ boff, int* __restrict__ perm) {
+  m += blockIdx.x * n;
+  boff += blockIdx.x * (nchunks + 1);
+  perm += blockIdx.x * n;
   __shared__ int cnt[la_internal::kMaxBuckets + 1];
   __shared__ int part[1024];
   bucket_sort(m, n, C, nchunks, boff, perm, cnt, part);
@@ -1213,16 +1232,16 @@ template <bool PHI>
 __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, const float* __restrict__ v, int64_t n,
                                                  int64_t nchunks, int C, int64_t G, int64_t nseg,
                                                  float* __restrict__ ws, const int64_t* __restrict__ m,
-                                                 int* __restrict__ boff, int* __restrict__ perm) {
+                                                 int* __restrict__ boff, int* __restrict__ perm, int64_t nmask) {
   constexpr int FD = 64, TW = 32, NW8 = 8;
   __shared__ State32Lds L;
   int64_t sb = blockIdx.x;  // state block
   if (m) {
-    if (sb == 0) {
-      bucket_sort(m, n, C, nchunks, boff, perm, L.b.cnt, L.b.part);
+    if (sb < nmask) {  // blocks 0 .. nmask - 1 sort the masks
+      bucket_sort(m + sb * n, n, C, nchunks, boff + sb * (nchunks + 1), perm + sb * n, L.b.cnt, L.b.part);
       return;
     }
-    --sb;
+    sb -= nmask;
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
   const int64_t bh = sb / nseg, seg = sb % nseg;
@@ -1550,27 +1569,28 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
                                                                             a.S_final, a.z_final, 1);
     if (q && out)
       k_out<T, DP, C, CAUSAL, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
-          q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
+          q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
     return (int)hipGetLastError();
   }
   if (form == PREFIX) {
     char* bw = reinterpret_cast<char*>(a.ws) + la_internal::state_bytes(p, a.B, a.Hkv);
-    boff = reinterpret_cast<int*>(bw);
-    perm = boff + (p.nchunks + 1);
+    boff = reinterpret_cast<int*>(bw);                // [nmask][nchunks + 1]
+    perm = boff + a.nmask * (p.nchunks + 1);          // [nmask][n]
     if constexpr (std::is_same<T, float>::value && DP == 64) {
       if (vec && a.n <= la_internal::kFwd32MaxN) {  // the sort as one more workgroup of the state launch
-        k_state32<false><<<dim3((unsigned)(nbh * p.nseg + 1)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
-                                                                              states, a.m, boff, perm);
+        k_state32<false><<<dim3((unsigned)(nbh * p.nseg + a.nmask)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G,
+                                                                                    p.nseg, states, a.m, boff, perm,
+                                                                                    a.nmask);
         state_done = true;
       }
     }
-    if (!state_done) k_bucket<<<1, 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
+    if (!state_done) k_bucket<<<dim3((unsigned)a.nmask), 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
   }
   const bool phi = (form == CAUSAL);
   if constexpr (std::is_same<T, float>::value && DP == 64) {
     if (phi && vec && a.n <= la_internal::kFwd32MaxN) {
       k_state32<true><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
-                                                                       states, nullptr, nullptr, nullptr);
+                                                                       states, nullptr, nullptr, nullptr, 1);
       state_done = true;
     }
   }
@@ -1615,14 +1635,14 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
     if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
       if (px_out) {
         k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
-            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, perm, boff, a.m);
+            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
         return (int)hipGetLastError();
       }
     }
     if (form == CAUSAL)
-      k_out<T, DP, C, CAUSAL, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr);
+      k_out<T, DP, C, CAUSAL, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
     else
-      k_out<T, DP, C, PREFIX, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m);
+      k_out<T, DP, C, PREFIX, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
   }
   return (int)hipGetLastError();
 }

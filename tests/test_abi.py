@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"la_status_str", "la_workspace_bytes", "la_forward", "la_causal_forward",
                           "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
-                          "la_causal_forward_phi", "la_decode_step_phi"}
+                          "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -136,6 +136,23 @@ def test_causal_rejections(lib):
     assert causal(lib, wsb=100) == WS
     assert causal(lib, ws=O) == ALIAS
     assert causal(lib, n=(1 << 31)) == SHAPE
+
+
+def test_batched_prefix_workspace_and_rejections(lib):
+    """A sort per batch: the workspace grows by B - 1 bucket arrays; the
+    checks are those of the shared-mask form, the mask spanning B rows."""
+    f = la.la_workspace_bytes
+    one = f(la.LA_OP_PREFIX_MASK, 4, 8, 8, 8192, 64, la.LA_F32, 64)
+    four = f(la.LA_OP_PREFIX_MASK_BATCHED, 4, 8, 8, 8192, 64, la.LA_F32, 64)
+    assert four - one == 3 * 4 * (8192 // 64 + 1 + 8192)
+    assert f(la.LA_OP_PREFIX_MASK_BATCHED, 1, 2, 1, 16, 16, la.LA_F32, 0) == 0
+    call = lib.la_prefix_mask_forward_batched
+    assert call(Q, K, V, None, 2, 1, 16, 16, 0, 0, O, WSP, BIG, None) == NULL
+    assert call(Q, K, V, M + 8, 2, 1, 16, 16, 0, 0, O, WSP, BIG, None) == ALIGN
+    assert call(Q, K, V, M, 2, 1, 16, 16, 0, 100, O, WSP, BIG, None) == UNSUP
+    assert call(Q, K, V, M, 2, 1, 16, 16, 0, 0, O, WSP, 8, None) == WS
+    # out overlapping the second batch's mask row
+    assert call(Q, K, V, M, 2, 1, 16, 16, 0, 0, M + 16 * 8, WSP, BIG, None) == ALIAS
 
 
 def test_prefix_rejections(lib):

@@ -474,3 +474,22 @@ def test_elu1_equals_relu1_on_positive_inputs(gpu, dtype):
         b = f(qd, kd, vd, **kw).float()
         err = ((a - b).abs().amax(dim=-1) / b.abs().amax(dim=-1)).max().item()
         assert err < (1e-5 if dtype == li.F32 else 1e-2), (f.__name__, dtype, err)
+
+
+# ---------------------------------------------------------------------------
+# Per-batch prefix masks (la_prefix_mask_forward_batched, m [B, n]).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("case,kinds", [
+    ((3, 2, 1000, 64, 64), ("random", "causal", "full")),     # fp32: the chunk-64 state / output kernels
+    ((2, 3, 300, 64, 0), ("causal", "random")),
+    ((4, 1, 130, 33, 0), ("first", "random", "full", "causal")),
+    ((2, 2, 257, 128, 32), ("random", "first")),
+], ids=["B3H2n1000d64c64", "B2H3n300d64", "B4H1n130d33", "B2H2n257d128c32"])
+def test_prefix_per_batch_masks(gpu, dtype, case, kinds):
+    B, H, n, d, chunk = case
+    chunk = fit_chunk(gpu, dtype, d, chunk) if chunk else 0
+    q, k, v, rng = li.qkv(B, H, H, n, d, dtype, seed=50, scaled=True)
+    m = np.stack([li.mask(n, kinds[b], rng=rng) for b in range(B)])
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=chunk))
+    check(g, oracle.prefix_mask(q, k, v, m), dtype, f"prefix per-batch {case} {kinds} {dtype}")
