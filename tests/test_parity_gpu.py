@@ -493,3 +493,40 @@ def test_prefix_per_batch_masks(gpu, dtype, case, kinds):
     m = np.stack([li.mask(n, kinds[b], rng=rng) for b in range(B)])
     g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=chunk))
     check(g, oracle.prefix_mask(q, k, v, m), dtype, f"prefix per-batch {case} {kinds} {dtype}")
+
+
+# ---------------------------------------------------------------------------
+# The specialised paths at their size limits.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [131072, 131072 + 100])
+def test_causal_at_the_single_launch_limit(gpu, n):
+    """131072 tokens (256 segments per head) is the longest sequence the
+    single-launch causal kernel takes; 100 more go to the general path.
+    Sampled rows (the first, around segment boundaries, the last) against the
+    oracle."""
+    B, H, d = 1, 2, 64
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.BF16, seed=60, scaled=True)
+    rows = np.array(sorted({0, 1, 511, 512, 513, 65535, 65536, n - 2, n - 1}), dtype=np.int64)
+    g = host(gpu.la_causal_forward(dev(q), dev(k), dev(v), chunk=64))[:, :, rows]
+    check(g, oracle.causal(q, k, v, rows=rows), li.BF16, f"causal n={n} sampled rows")
+
+
+@pytest.mark.parametrize("dtype,n", [(li.BF16, 1 << 23), (li.F32, 1 << 22)])
+def test_noncausal_at_the_single_path_limit(gpu, dtype, n):
+    """The longest sequence of the d = 64 non-causal kernels (2^23 tokens for
+    bf16, 2^22 for fp32), checked by a property that holds at any size: with
+    every key row equal, every output row is the mean of V.  Inputs drawn on
+    the GPU from a seeded generator (1 GiB per tensor)."""
+    import torch
+    d = 64
+    tdt = torch.bfloat16 if dtype == li.BF16 else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(61)
+    q = torch.randn((1, 1, n, d), generator=gen, device="cuda").div_(8).to(tdt)
+    v = torch.randn((1, 1, n, d), generator=gen, device="cuda").to(tdt)
+    row = torch.randn((1, 1, 1, d), generator=gen, device="cuda").div_(8).to(tdt)
+    k = row.expand(1, 1, n, d).contiguous()
+    out = gpu.la_forward(q, k, v)
+    want = v.double().mean(dim=2, keepdim=True)
+    err = ((out.double() - want).abs().amax(dim=-1) / want.abs().amax(dim=-1)).max().item()
+    print(f"non-causal n={n} {dtype}: row-wise rel err {err:.3e}", flush=True)
+    assert err < TOL[dtype], err
