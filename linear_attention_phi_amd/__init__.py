@@ -164,6 +164,7 @@ def _call(rc, what):
 def la_forward(q, k, v, out=None, ws=None, phi="relu1"):
     """Non-causal normalised linear attention; returns out (q's shape and dtype).
     phi: "relu1" (relu(x) + 1, la_forward) or "elu1" (ELU(x) + 1, la_forward_phi)."""
+    phi_code = _phi(phi)
     torch = _torch()
     B, Hq, Hkv, n, d = _qkv(q, k, v)
     dt = _dtype_code(q)
@@ -175,7 +176,7 @@ def la_forward(q, k, v, out=None, ws=None, phi="relu1"):
         _call(load().la_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt,
                                 _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), "la_forward")
     else:
-        _call(load().la_forward_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, _phi(phi),
+        _call(load().la_forward_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, phi_code,
                                     _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), "la_forward_phi")
     return out
 
@@ -187,6 +188,7 @@ def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None
     q may be None for a state-only pass (pass Hq, default Hkv); then the
     final state is returned.  With want_state, returns (out, S_final, z_final).
     """
+    phi_code = _phi(phi)
     torch = _torch()
     B, Hq_, Hkv, n, d = _qkv(q, k, v)
     dt = _dtype_code(k)
@@ -212,7 +214,7 @@ def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None
                                        _dev(ws, "ws"), ws.numel(), _stream(k)), "la_causal_forward")
     else:
         _call(load().la_causal_forward_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt,
-                                           _phi(phi), chunk, _dev(out, "out"), _dev(S_final, "S_final"),
+                                           phi_code, chunk, _dev(out, "out"), _dev(S_final, "S_final"),
                                            _dev(z_final, "z_final"), _dev(ws, "ws"), ws.numel(), _stream(k)),
               "la_causal_forward_phi")
     if q is None:
@@ -250,6 +252,7 @@ def la_decode_step(q, k, v, S, z, out=None, phi="relu1"):
     """One decode step: q [B,Hq,d], k/v [B,Hkv,d]; S [B,Hkv,d,d], z [B,Hkv,d]
     (float32) are updated in place.  Returns out [B,Hq,d].  phi as la_forward
     (the map the state was built with)."""
+    phi_code = _phi(phi)
     torch = _torch()
     B, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -266,7 +269,7 @@ def la_decode_step(q, k, v, S, z, out=None, phi="relu1"):
         _call(load().la_decode_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, d, dt,
                                     _dev(S, "S"), _dev(z, "z"), _dev(out, "out"), _stream(q)), "la_decode_step")
     else:
-        _call(load().la_decode_step_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, d, dt, _phi(phi),
+        _call(load().la_decode_step_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, d, dt, phi_code,
                                         _dev(S, "S"), _dev(z, "z"), _dev(out, "out"), _stream(q)),
               "la_decode_step_phi")
     return out

@@ -189,3 +189,13 @@ def test_binding_checks_shapes_before_calling():
         la.la_forward(q.double(), k.double(), k.double())
     with pytest.raises(ValueError):  # CPU tensors are refused (no host fallback)
         la.la_forward(q, k, k)
+    with pytest.raises(ValueError, match="phi"):  # an unknown feature map, before anything else
+        la.la_forward(q, k, k, phi="softmax")
+    with pytest.raises(ValueError, match="phi"):
+        la.la_causal_forward(q, k, k, phi="elu")
+    with pytest.raises(ValueError, match="phi"):
+        la.la_decode_step(q[:, :, 0], k[:, :, 0], k[:, :, 0], torch.zeros(1, 1, 4, 4), torch.zeros(1, 1, 4),
+                          phi="")
+    q4 = torch.zeros(2, 1, 8, 4)
+    with pytest.raises(ValueError, match="m must"):  # a mask neither [n] nor [B, n]
+        la.la_prefix_mask_forward(q4, q4, q4, torch.zeros(3, 8, dtype=torch.int64))
