@@ -64,6 +64,8 @@ WORKLOADS = {
                        phi="elu1"),
     "forward_elu": dict(form="forward", B=2, Hq=8, Hkv=8, n=4096, d=64, dt="bf16", scaled=False, steps=200,
                         phi="elu1"),
+    "gqa_elu": dict(form="causal", B=1, Hq=32, Hkv=8, n=65536, d=128, dt="bf16", chunk=0, scaled=True, steps=20,
+                    phi="elu1"),
 }
 
 DESCRIPTIONS = {
@@ -77,6 +79,7 @@ DESCRIPTIONS = {
     "decode": "recurrent decode step, fp32 state prefilled from a 4096-token prefix, bf16 q/k/v",
     "causal_elu": "causal normalised linear attention, phi=ELU+1, bf16 in, fp32 state",
     "forward_elu": "non-causal normalised linear attention, phi=ELU+1, bf16 in, fp32 accumulation",
+    "gqa_elu": "long-context GQA causal normalised linear attention, phi=ELU+1, bf16 in, fp32 state",
 }
 
 

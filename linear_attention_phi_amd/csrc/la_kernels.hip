@@ -151,9 +151,13 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
 // (all four row blocks): the column sums of V its blocks need and z of rows
 // 32 w .. are dot2 sums over fragments it reads anyway.
 constexpr int STR_RS = 128 + 16;  // tile row stride (bf16): rows 8 dwords apart mod 64 banks
+// PM: relu + 1 (relu(K) in the tiles, the ones part added at the end) or
+// ELU + 1 (phi(K) in the tiles, rows past the end 0).
+template <int PM>
 __global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, const bf16* __restrict__ v, int64_t n,
                                                  int64_t nchunks, int64_t G, int64_t nseg, float* __restrict__ ws) {
   constexpr int DP = 128, C = 32, RS = STR_RS;
+  constexpr bool SPLIT = PM == PM_RELU1;
   static_assert(NT == 256 && DP / 32 == NT / 64, "one column block per wave");
   __shared__ __attribute__((aligned(16))) bf16 sK[2][C * RS];
   __shared__ __attribute__((aligned(16))) bf16 sV[2][C * RS];
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, con
     for (int u = 0; u < PIECES; ++u) {
       const int pc = tid + NT * u, row = pc >> 4, col = 8 * (pc & 15);
       const uint4 x = kr[u];
-      *reinterpret_cast<uint4*>(sK[buf] + row * RS + col) =
-          make_uint4(la_bf16::relu2(x.x), la_bf16::relu2(x.y), la_bf16::relu2(x.z), la_bf16::relu2(x.w));
+      auto fk = [&](uint32_t y) { return SPLIT ? la_bf16::relu2(y) : (row < nv ? la_bf16::elu2(y) : 0u); };
+      *reinterpret_cast<uint4*>(sK[buf] + row * RS + col) = make_uint4(fk(x.x), fk(x.y), fk(x.z), fk(x.w));
       *reinterpret_cast<uint4*>(sV[buf] + row * RS + col) = vr[u];
     }
     if (c + 1 < c1) fetch(c + 1);
@@ -213,12 +217,14 @@ __global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, con
         zs = la_bf16::dot2(la_bf16::pair(kz[kt], q), la_bf16::ONE2, zs);
         vs = la_bf16::dot2(la_bf16::pair(vt[kt], q), la_bf16::ONE2, vs);
       }
-    zrun += zs + __shfl_xor(zs, 32) + (float)nv;  // phi(K) = relu(K) + 1 over the nv keys
+    zrun += zs + __shfl_xor(zs, 32) + (SPLIT ? (float)nv : 0.0f);  // relu + 1: the ones over the nv keys
     vrun += vs + __shfl_xor(vs, 32);
   }
-  // phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t
+  // relu + 1: phi(K)^T V = relu(K)^T V + 1 (x) sum_t V_t
+  if (SPLIT) {
 #pragma unroll
-  for (int ab = 0; ab < DP / 32; ++ab) add_col(acc[ab], vrun, ab, DP, lane);
+    for (int ab = 0; ab < DP / 32; ++ab) add_col(acc[ab], vrun, ab, DP, lane);
+  }
   float* dst = ws + (bh * (nseg + 1) + seg) * slot_elems(DP);
 #pragma unroll
   for (int ab = 0; ab < DP / 32; ++ab) st_state_block<DP>(dst, acc[ab], ab, w, lane);
@@ -814,7 +820,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
 // A workgroup walks F state segments (G chunks of the state pass each) and
 // starts from the exclusive prefix in slot F * seg of the workspace, whose
 // per-head stride is nseg_ws + 1 slots.
-template <int R>
+template <int R, int PM>
 __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                  const bf16* __restrict__ v, bf16* __restrict__ out, int64_t n,
                                                  int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
@@ -825,6 +831,8 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
   constexpr int NPH = 8 / R;    // waves per query head
   constexpr int NBW = 4 / NPH;  // 32-wide output feature blocks per wave
   static_assert(R == 2 || R == 4, "two or four query heads per key/value head");
+  // relu + 1 split as in k_state_tr; ELU + 1: phi(K), phi(Q) in the tiles
+  constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LQ];       // phi(K), token-major
   __shared__ __attribute__((aligned(16))) bf16 sKr[C * RS];     // relu(K), token-major
   __shared__ __attribute__((aligned(16))) bf16 sV[C * RS];      // V, token-major
@@ -889,7 +897,8 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
         la_bf16::u32x4 x = kv2[rr];
         if (half == 0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) x[j] = la_bf16::relu2(x[j]);
+          for (int j = 0; j < 4; ++j)
+            x[j] = SPLIT ? la_bf16::relu2(x[j]) : (pr0 + rr < nv ? la_bf16::elu2(x[j]) : 0u);
         }
         *reinterpret_cast<la_bf16::u32x4*>(tm + (pr0 + rr) * RS + pc0) = x;
       }
@@ -898,7 +907,8 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
         for (int rr = 0; rr < 2; ++rr) {
           uint32_t y[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = pr0 + rr < nv ? la_bf16::phi2(kv2[rr][j]) : 0u;
+          for (int j = 0; j < 4; ++j)
+            y[j] = pr0 + rr < nv ? (SPLIT ? la_bf16::phi2(kv2[rr][j]) : la_bf16::elu2(kv2[rr][j])) : 0u;
           uint2* dst = reinterpret_cast<uint2*>(sK + (pr0 + rr) * LQ + pc0);
           dst[0] = make_uint2(y[0], y[1]);
           dst[1] = make_uint2(y[2], y[3]);
@@ -906,13 +916,14 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
       }
     }
 #pragma unroll
-    for (int u = 0; u < QPH; ++u) tile_store<bf16, DP, C, XF_PHI, XF_NONE>(raw[u], nv, sQ[2 * u + half], nullptr, ht);
+    for (int u = 0; u < QPH; ++u)
+      tile_store<bf16, DP, C, SPLIT ? XF_PHI : XF_ELU1, XF_NONE>(raw[u], nv, sQ[2 * u + half], nullptr, ht);
     if (c + 1 < c1) fetch(c + 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int e = w + 8 * s, ma = e / 4, nb = e % 4;
       f32x16 cur = accS[s];
-      add_col(cur, svc[nb * 32 + r], ma, DP, lane);
+      if (SPLIT) add_col(cur, svc[nb * 32 + r], ma, DP, lane);
       st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
     }
     if (w < 4 && h == 0) {
@@ -976,7 +987,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
       }
       cs += __shfl_xor(cs, 32);
       if (w < 4) {
-        zrun += cs + (float)nv;
+        zrun += cs + (SPLIT ? (float)nv : 0.0f);
       } else {
         vrun += cs;
         if (h == 0) svc[32 * (w - 4) + r] = vrun;  // read at the next chunk's start (this chunk read it before the barrier above)
@@ -1560,16 +1571,39 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   int* boff = nullptr; int* perm = nullptr;
   bool state_done = false;
   if (form == CAUSAL && a.phi == 1) {
-    // ELU + 1: the general state, scan and output kernels (the specialised
-    // ones split relu + 1)
-    k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
-                                                                             p.G, p.nseg, states);
+    // ELU + 1: the bf16 d = 128 chunk-32 (GQA) state and output kernels, else
+    // the general ones (the fp32 d = 64 state kernel splits relu + 1 only)
+    bool tr = false;
+    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
+    const bool gq = tr && q && out && (R == 2 || R == 4);
+    if (tr) {
+      if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
+        k_state_tr<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
+    } else {
+      k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
+                                                                               p.G, p.nseg, states);
+    }
+    int64_t F = gq ? nbh * p.nseg / kGqaOutGroups : 1;
+    if (F < 1) F = 1;
     const int64_t E = slot_elems(DP);
     k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d,
-                                                                            a.S_final, a.z_final, 1);
-    if (q && out)
-      k_out<T, DP, C, CAUSAL, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
-          q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
+                                                                            a.S_final, a.z_final, F);
+    if (!(q && out)) return (int)hipGetLastError();
+    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
+      if (gq) {
+        const bf16* qq = reinterpret_cast<const bf16*>(q);
+        const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
+        if (R == 2)
+          k_out_gqa<2, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO,
+                                                                                 nseg_o, F, p.nseg, states);
+        else
+          k_out_gqa<4, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO,
+                                                                                 nseg_o, F, p.nseg, states);
+        return (int)hipGetLastError();
+      }
+    }
+    k_out<T, DP, C, CAUSAL, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
+        q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
     return (int)hipGetLastError();
   }
   if (form == PREFIX) {
@@ -1596,7 +1630,7 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   }
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
     if (phi && vec) {
-      k_state_tr<<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
+      k_state_tr<PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
       state_done = true;
     }
   }
@@ -1624,10 +1658,10 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
       if (gqa_out) {
         const bf16* qq = reinterpret_cast<const bf16*>(q);
         if (R == 2)
-          k_out_gqa<2><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
+          k_out_gqa<2, PM_RELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
                                                                         p.nseg, states);
         else
-          k_out_gqa<4><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
+          k_out_gqa<4, PM_RELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
                                                                         p.nseg, states);
         return (int)hipGetLastError();
       }

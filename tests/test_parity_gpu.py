@@ -427,6 +427,8 @@ def test_single_launch_matches_three_launch_path(gpu):
 # ---------------------------------------------------------------------------
 ELU_CASES = [
     (2, 3, 3, 1500, 64, 64),   # bf16: the single-launch causal kernel, 3 segments, ragged tail
+    (1, 4, 1, 700, 128, 32),   # bf16: the GQA state and output kernels, four query heads per KV head
+    (2, 4, 2, 333, 128, 0),    # ... two per KV head (default chunk 32)
     (1, 1, 1, 256, 16, 0),
     (2, 4, 2, 1000, 64, 64),
     (1, 2, 2, 300, 128, 32),
