@@ -1239,7 +1239,9 @@ union State32Lds {
   } b;
 };
 
-template <bool PHI>
+// PM: the identity (prefix form), relu + 1 (split) or ELU + 1 (keys past the
+// segment contribute 0, not phi(0) = 1).
+template <int PM>
 __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, const float* __restrict__ v, int64_t n,
                                                  int64_t nchunks, int C, int64_t G, int64_t nseg,
                                                  float* __restrict__ ws, const int64_t* __restrict__ m,
@@ -1287,12 +1289,16 @@ __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, co
 #pragma unroll
     for (int s = 0; s < TW / 4; ++s) {
       f32x4 pk;
+      const bool real = t0 + 4 * s + kq < k1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (PHI) {
+        if (PM == PM_RELU1) {
           const float x = fmaxf(kr[s][j], 0.0f);
           zr[j] += x;
           pk[j] = x + 1.0f;  // keys past the segment: 1, against V = 0
+        } else if (PM == PM_ELU1) {
+          pk[j] = real ? elu1_f(kr[s][j]) : 0.0f;
+          zr[j] += pk[j];
         } else {
           pk[j] = kr[s][j];
         }
@@ -1309,7 +1315,7 @@ __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, co
   for (int j = 0; j < 4; ++j) {
     zr[j] += __shfl_xor(zr[j], 16);
     zr[j] += __shfl_xor(zr[j], 32);
-    zr[j] += PHI ? (float)nkeys : 0.0f;  // the ones of phi(K), real keys only
+    zr[j] += PM == PM_RELU1 ? (float)nkeys : 0.0f;  // the ones of phi(K), real keys only
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -1571,14 +1577,19 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   int* boff = nullptr; int* perm = nullptr;
   bool state_done = false;
   if (form == CAUSAL && a.phi == 1) {
-    // ELU + 1: the bf16 d = 128 chunk-32 (GQA) state and output kernels, else
-    // the general ones (the fp32 d = 64 state kernel splits relu + 1 only)
-    bool tr = false;
+    // ELU + 1: the bf16 d = 128 chunk-32 (GQA) state and output kernels, the
+    // fp32 d = 64 state kernel, else the general ones
+    bool tr = false, s32 = false;
     if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
+    if constexpr (std::is_same<T, float>::value && DP == 64) s32 = vec && a.n <= la_internal::kFwd32MaxN;
     const bool gq = tr && q && out && (R == 2 || R == 4);
     if (tr) {
       if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
         k_state_tr<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
+    } else if (s32) {
+      if constexpr (std::is_same<T, float>::value && DP == 64)
+        k_state32<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
+                                                                           states, nullptr, nullptr, nullptr, 1);
     } else {
       k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
                                                                                p.G, p.nseg, states);
@@ -1612,7 +1623,7 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
     perm = boff + a.nmask * (p.nchunks + 1);          // [nmask][n]
     if constexpr (std::is_same<T, float>::value && DP == 64) {
       if (vec && a.n <= la_internal::kFwd32MaxN) {  // the sort as one more workgroup of the state launch
-        k_state32<false><<<dim3((unsigned)(nbh * p.nseg + a.nmask)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G,
+        k_state32<PM_ID><<<dim3((unsigned)(nbh * p.nseg + a.nmask)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G,
                                                                                     p.nseg, states, a.m, boff, perm,
                                                                                     a.nmask);
         state_done = true;
@@ -1623,7 +1634,7 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   const bool phi = (form == CAUSAL);
   if constexpr (std::is_same<T, float>::value && DP == 64) {
     if (phi && vec && a.n <= la_internal::kFwd32MaxN) {
-      k_state32<true><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
+      k_state32<PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
                                                                        states, nullptr, nullptr, nullptr, 1);
       state_done = true;
     }
