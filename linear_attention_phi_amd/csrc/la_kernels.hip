@@ -280,7 +280,8 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 // block per wave, their rows gathered through perm and staged in LDS.  Operands
 // (the contraction index k is lane / 16, the other index lane % 16):
 //   S^T  from LDS in operand order: entry (bb, tt, lane) is the float4 over
-//        jj of S[16 tt + 4 (lane / 16) + jj][16 bb + lane % 16];
+//        jj of S[16 tt + 4 (lane / 16) + jj][16 bb + lane % 16], kept in
+//        slot lane ^ (4 bb + tt) of block 4 bb + tt;
 //   Q^T  the float4 of query row lane % 16 at features 16 tt + 4 (lane / 16);
 //   K    the float4 of key row 16 kb + lane % 16 at the same features;
 //   P^T  the score accumulator itself: its register rr holds key
@@ -408,13 +409,20 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
     }
     if (c + 1 < c1) fetch_kv(c + 1);
     // S_prev(c) in operand order: tile entry S[16 kq + 4 rr + sj][4 mm + j']
-    // -> (bb, tt, L, jj) = (mm / 4, kq, 16 rr + 4 (mm % 4) + j', sj)
+    // -> (bb, tt, L, jj) = (mm / 4, kq, 16 rr + 4 (mm % 4) + j', sj).  Entry
+    // L of block bb * 4 + tt sits in float4 slot L ^ (bb * 4 + tt) of the
+    // block: unswizzled, the 64 lanes of one of these scalar stores differ
+    // only in L % 16 = 4 (mm % 4) + j' and reach 4 banks (16-way); the XOR
+    // with the block index spreads them over 16, the most a store that fills
+    // one float component (jj = sj) can reach.  Readers take whole float4s
+    // and stay conflict-free.
     if (owner) {
+      const int blk = (mm >> 2) * 4 + kq;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          sS[(((mm >> 2) * 4 + kq) * 64 + 16 * rr + 4 * (mm & 3) + t) * 4 + sj] = accS[t][rr];
+          sS[(blk * 64 + ((16 * rr + 4 * (mm & 3) + t) ^ blk)) * 4 + sj] = accS[t][rr];
     }
     __syncthreads();  // tiles and S visible
     if (ngroups == 0 && owner) state_update();
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
         for (int tt = 0; tt < 4; ++tt) {
           f32x4 so[4];
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb) so[bb] = *reinterpret_cast<const f32x4*>(sS + ((bb * 4 + tt) * 64 + lane) * 4);
+          for (int bb = 0; bb < 4; ++bb) so[bb] = *reinterpret_cast<const f32x4*>(sS + ((bb * 4 + tt) * 64 + (lane ^ (bb * 4 + tt))) * 4);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
