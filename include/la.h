@@ -111,8 +111,8 @@ la_status la_forward(const void* q, const void* k, const void* v, int64_t B,
  * phi(Q) phi(K)^T V term, across chunks an exclusive prefix of the chunk
  * states.  chunk: 32, 64 or 128 where the tiles fit in LDS, or 0 for the
  * default (64, or 32 where that lets two workgroups share a compute unit:
- * bf16 with d > 64, fp32 with d > 32); the result does not depend on it
- * beyond rounding.
+ * bf16 with d > 64, fp32 with d > 32, except fp32 with d = 64 and Hq = Hkv,
+ * which takes 64); the result does not depend on it beyond rounding.
  * S_final [B][Hkv][d][d] and z_final [B][Hkv][d] (fp32, device; either may
  * be NULL) receive the state after the last token -- the hand-off to
  * la_decode_step.  q and out may both be NULL for a state-only pass (then

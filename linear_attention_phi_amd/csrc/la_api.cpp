@@ -169,10 +169,11 @@ const char* la_status_str(la_status s) {
   }
 }
 
-// The prefix form with fp32 and d = 64 defaults to chunk 64: its state and
-// output kernels (16x16x4 fp32 MFMA, no LDS transposes) exist for that chunk.
-static int32_t prefix_chunk(bool prefix, int32_t chunk, la_dtype dtype, int64_t d) {
-  return prefix && chunk == 0 && dtype == LA_F32 && d == 64 ? 64 : chunk;
+// The prefix form, and the causal form with one query head per key/value
+// head, default to chunk 64 for fp32 with d = 64: their state and output
+// kernels (16x16x4 fp32 MFMA, no LDS transposes) exist for that chunk.
+static int32_t prefix_chunk(bool take, int32_t chunk, la_dtype dtype, int64_t d) {
+  return take && chunk == 0 && dtype == LA_F32 && d == 64 ? 64 : chunk;
 }
 
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dtype,
@@ -184,7 +185,7 @@ size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_
   int C = 0;
   if (op == LA_OP_FORWARD) {
     C = forward_chunk(elem_bytes(dtype), padded_dim(d));
-  } else if (resolve_chunk(prefix_chunk(prefix, chunk, dtype, d), dtype, d, &C) != LA_OK) {
+  } else if (resolve_chunk(prefix_chunk(prefix || Hq == Hkv, chunk, dtype, d), dtype, d, &C) != LA_OK) {
     return 0;
   }
   if (prefix && (Hq != Hkv || (n + C - 1) / C > kMaxBuckets)) return 0;
@@ -239,7 +240,7 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
       (S_final && !aligned16(S_final)) || (z_final && !aligned16(z_final)))
     return LA_ERR_ALIGN;
   int C = 0;
-  if ((st = resolve_chunk(chunk, dtype, d, &C)) != LA_OK) return st;
+  if ((st = resolve_chunk(prefix_chunk(Hq == Hkv, chunk, dtype, d), dtype, d, &C)) != LA_OK) return st;
   const size_t eb = elem_bytes(dtype);
   const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
   const size_t sb = (size_t)(B * Hkv * d * d) * sizeof(float), zb = (size_t)(B * Hkv * d) * sizeof(float);

@@ -295,6 +295,13 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 // S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']), writes them in operand order
 // at the chunk's start and adds K_c^T V_c during the chunk's first query
 // group.
+// With CS (the causal normalised form, feature map PM) the buckets are the
+// chunks themselves (query i of chunk c = row c C + i, m_i = i, no sort), Q
+// rows and K tiles take phi as they are staged (key rows past n stay 0), and
+// z rides along with S: wave 0 keeps z_prev(c) (from the prefix slot, plus
+// the column sums of the segment's earlier phi(K) tiles) and publishes it in
+// LDS beside S; the denominator phi(Q_i) . z_prev + the masked score row sum
+// divides each output row.
 constexpr int PX_RS = 64 + 4;  // row stride (floats) of the LDS tiles
 // NWV waves per workgroup, queries per group QG = 16 NWV (one 16-query block
 // per wave); the state is owned by waves NWV - 4 .. NWV - 1, four tiles each.
@@ -313,7 +320,7 @@ constexpr int64_t kGqaOutGroups = LA_GQA_OUT_GROUPS;
 #define LA_PREFIX_OUT_GROUPS 512
 #endif
 constexpr int64_t kPrefixOutGroups = LA_PREFIX_OUT_GROUPS;
-template <int NWV>
+template <int NWV, bool CS = false, int PM = PM_ID>
 __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ v, float* __restrict__ out, int64_t n,
                                                       int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
@@ -328,14 +335,29 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   __shared__ __attribute__((aligned(16))) float sV[C * RS];
   __shared__ __attribute__((aligned(16))) float sQ[QG * RS];
   __shared__ __attribute__((aligned(16))) float sS[16 * 64 * 4];  // S in operand order
+  __shared__ __attribute__((aligned(16))) float sz[FD];            // z_prev (CS)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-  {  // this batch's mask, buckets and permutation (one per batch, or one shared)
+  if constexpr (!CS) {  // this batch's mask, buckets and permutation (one per batch, or one shared)
     const int64_t mb = nmask > 1 ? bh / H : 0;
     perm += mb * n;
     boff += mb * (nchunks + 1);
     m += mb * n;
   }
+  // bucket c's first position, and the query row at a position
+  auto bo = [&](int64_t c) -> int64_t {
+    if constexpr (CS) return c * C < n ? c * C : n;
+    else return boff[c];
+  };
+  auto qrow = [&](int64_t i) -> int64_t {
+    if constexpr (CS) return i;
+    else return perm[i];
+  };
+  auto phi4 = [&](f32x4 x) -> f32x4 {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = phi_m<PM>(x[j]);
+    return x;
+  };
   const float* qh = q + bh * n * FD;
   const float* kh = k + bh * n * FD;
   const float* vh = v + bh * n * FD;
@@ -353,6 +375,8 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) accS[t][rr] = owner ? src[(16 * kq + 4 * rr + sj) * FD + 4 * mm + t] : 0.0f;
   }
+  float zacc = 0.0f;  // CS: z_prev of feature tid (wave 0)
+  if (CS && tid < FD) zacc = ws[(bh * (nseg_ws + 1) + F * seg) * slot_elems(FD) + FD * FD + tid];
   auto state_update = [&]() {  // S += K_c^T V_c on this wave's tiles
 #pragma unroll
     for (int st = 0; st < C / 4; ++st) {
@@ -376,7 +400,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
       vr[u] = t < n ? *reinterpret_cast<const f32x4*>(vh + t * FD + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   };
-  auto groups_of = [&](int64_t c) -> int { return (int)((boff[c + 1] - boff[c] + QG - 1) / QG); };
+  auto groups_of = [&](int64_t c) -> int { return (int)((bo(c + 1) - bo(c) + QG - 1) / QG); };
   auto fetch_q_after = [&](int64_t c, int grp) {  // rows of the query group after (c, grp), if any
     int64_t cc = c;
     int gg = grp + 1;
@@ -385,12 +409,13 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
       gg = 0;
     }
     if (cc >= c1) return;
-    const int64_t s0 = boff[cc] + (int64_t)QG * gg, e0 = boff[cc + 1];
+    const int64_t s0 = bo(cc) + (int64_t)QG * gg, e0 = bo(cc + 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
-      qraw[u] = s0 + row < e0 ? *reinterpret_cast<const f32x4*>(qh + (int64_t)perm[s0 + row] * FD + col)
+      qraw[u] = s0 + row < e0 ? *reinterpret_cast<const f32x4*>(qh + qrow(s0 + row) * FD + col)
                               : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (CS && s0 + row < e0) qraw[u] = phi4(qraw[u]);
     }
   };
   if (c0 < c1) {
@@ -404,9 +429,12 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
 #pragma unroll
     for (int u = 0; u < KVP; ++u) {
       const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
-      *reinterpret_cast<f32x4*>(sK + row * RS + col) = kr[u];
+      f32x4 kk = kr[u];
+      if (CS) kk = t0 + row < n ? phi4(kk) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      *reinterpret_cast<f32x4*>(sK + row * RS + col) = kk;
       *reinterpret_cast<f32x4*>(sV + row * RS + col) = vr[u];
     }
+    if (CS && tid < FD) sz[tid] = zacc;
     if (c + 1 < c1) fetch_kv(c + 1);
     // S_prev(c) in operand order: tile entry S[16 kq + 4 rr + sj][4 mm + j']
     // -> (bb, tt, L, jj) = (mm / 4, kq, 16 rr + 4 (mm % 4) + j', sj).  Entry
@@ -436,13 +464,18 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
       fetch_q_after(c, grp);
       __syncthreads();  // the group's query rows visible
       if (grp == 0 && owner) state_update();
-      const int64_t i0 = boff[c] + (int64_t)QG * grp + 16 * w;  // this wave's first query (position in perm)
-      const int64_t e0 = boff[c + 1];
+      const int64_t i0 = bo(c) + (int64_t)QG * grp + 16 * w;  // this wave's first query (position in perm)
+      const int64_t e0 = bo(c + 1);
       if (i0 < e0) {
         const bool valid = i0 + mm < e0;
-        const int qi = valid ? perm[i0 + mm] : 0;
-        int64_t mi = valid ? m[qi] : 0;
-        mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);  // same clamp as the bucket sort
+        const int qi = valid ? (int)qrow(i0 + mm) : 0;
+        int64_t mi;
+        if constexpr (CS) {
+          mi = qi;
+        } else {
+          mi = valid ? m[qi] : 0;
+          mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);  // same clamp as the bucket sort
+        }
         const int limit = (int)(mi - t0);
         f32x4 qo[4];
 #pragma unroll
@@ -487,6 +520,26 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
               o[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(sV[(16 * kb + 4 * kq + rr) * RS + 16 * bb + mm], sc[kb][rr], o[bb], 0, 0, 0);
+        if constexpr (CS) {  // denominator of query mm: phi(Q) . z_prev + its masked scores
+          float dn = 0.0f;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 zz = *reinterpret_cast<const f32x4*>(sz + 16 * tt + 4 * kq);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dn += qo[tt][jj] * zz[jj];
+          }
+#pragma unroll
+          for (int kb = 0; kb < C / 16; ++kb)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) dn += sc[kb][rr];
+          dn += __shfl_xor(dn, 16);
+          dn += __shfl_xor(dn, 32);
+          const float rd = 1.0f / dn;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) o[bb][jj] *= rd;
+        }
         if (valid) {
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb)
@@ -494,6 +547,10 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
         }
       }
       __syncthreads();  // the group's rows are no longer read
+    }
+    if (CS && tid < FD) {  // z_prev(c + 1): add this chunk's phi(K) column sums (rows past n are 0)
+#pragma unroll 8
+      for (int r = 0; r < C; ++r) zacc += sK[r * RS + tid];
     }
     __syncthreads();  // tiles and S are rewritten by the next chunk
   }
@@ -1591,6 +1648,8 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
     if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
     if constexpr (std::is_same<T, float>::value && DP == 64) s32 = vec && a.n <= la_internal::kFwd32MaxN;
     const bool gq = tr && q && out && (R == 2 || R == 4);
+    bool px = false;  // the fp32 d = 64 chunk-64 output kernel
+    if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) px = vec && q && out && R == 1;
     if (tr) {
       if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
         k_state_tr<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
@@ -1602,7 +1661,7 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
       k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
                                                                                p.G, p.nseg, states);
     }
-    int64_t F = gq ? nbh * p.nseg / kGqaOutGroups : 1;
+    int64_t F = gq ? nbh * p.nseg / kGqaOutGroups : px ? nbh * p.nseg / kPrefixOutGroups : 1;
     if (F < 1) F = 1;
     const int64_t E = slot_elems(DP);
     k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d,
@@ -1618,6 +1677,14 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
         else
           k_out_gqa<4, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO,
                                                                                  nseg_o, F, p.nseg, states);
+        return (int)hipGetLastError();
+      }
+    }
+    if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
+      if (px) {
+        const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
+        k_out_prefix32<PX_NWV, true, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
+            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
         return (int)hipGetLastError();
       }
     }
@@ -1666,7 +1733,7 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
     gqa_out = q && out && form == CAUSAL && vec && (R == 2 || R == 4);
   if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64)
-    px_out = q && out && form == PREFIX && vec;
+    px_out = q && out && vec && (form == PREFIX || (form == CAUSAL && R == 1));
   int64_t F = gqa_out ? nbh * p.nseg / kGqaOutGroups : px_out ? nbh * p.nseg / kPrefixOutGroups : 1;
   if (F < 1) F = 1;
   const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
@@ -1686,9 +1753,14 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
       }
     }
     if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
-      if (px_out) {
+      if (px_out && form == PREFIX) {
         k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
             q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
+        return (int)hipGetLastError();
+      }
+      if (px_out) {
+        k_out_prefix32<PX_NWV, true, PM_RELU1><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
+            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
         return (int)hipGetLastError();
       }
     }

@@ -179,6 +179,40 @@ def test_prefix_f32_d64_query_groups(gpu, kind, shape):
     check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B{B} H{H} n{n} d64 f32")
 
 
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("shape", [(1, 2, 1000), (2, 3, 300), (1, 1, 64), (1, 1, 5)], ids=lambda c: "B%d_H%d_n%d" % c)
+def test_causal_f32_d64_chunk64_output_kernel(gpu, phi, shape):
+    """fp32, d = 64, one query head per KV head: the default chunk 64 runs the
+    16x16x4 MFMA output kernel with the chunks as buckets, phi applied as the
+    rows are staged and z carried beside S.  Ragged tails, several segments,
+    a single chunk, a partial single chunk; the final state as well."""
+    B, H, n = shape
+    q, k, v, _ = li.qkv(B, H, H, n, 64, li.F32, seed=9, scaled=True)
+    assert gpu.la_workspace_bytes(gpu.LA_OP_CAUSAL, B, H, H, n, 64, gpu.LA_F32, 0) == \
+        gpu.la_workspace_bytes(gpu.LA_OP_CAUSAL, B, H, H, n, 64, gpu.LA_F32, 64)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True, phi=phi)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True, phi=phi)
+    check(host(out), ref, li.F32, f"causal f32 d64 {phi} B{B} H{H} n{n}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-4 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
+def test_causal_f32_d64_full_scale_sampled(gpu):
+    """The same kernel at B4 H8 n8192 (512 output workgroups, two state
+    segments each): sampled rows against the oracle's closed form per row."""
+    B, H, n, d = 4, 8, 8192, 64
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.F32, seed=13, scaled=True)
+    g = host(gpu.la_causal_forward(dev(q), dev(k), dev(v)))
+    rng = np.random.default_rng(3)
+    for b, h, i in zip(rng.integers(0, B, 12), rng.integers(0, H, 12), list(rng.integers(0, n, 10)) + [0, n - 1]):
+        pk = np.maximum(k[b, h, : i + 1].astype(np.float64), 0) + 1
+        pq = np.maximum(q[b, h, i].astype(np.float64), 0) + 1
+        sc = pk @ pq
+        ref = (sc @ v[b, h, : i + 1].astype(np.float64)) / sc.sum()
+        err = np.abs(g[b, h, i] - ref).max() / np.abs(ref).max()
+        assert err <= 1e-4, (b, h, i, err)
+
+
 def test_prefix_page_mask(gpu):
     """m = [2, 0, 1] (the trim-transformer page's example) on the GPU."""
     q, k, v, _ = li.qkv(1, 2, 2, 3, 4, li.F32, seed=11)
