@@ -38,16 +38,26 @@
  *   call only enqueues work on that stream and returns: no host
  *   synchronisation, no device allocation.
  * Workspace.  Forward calls take a device workspace of at least
- *   la_workspace_bytes(...) bytes, owned by the caller.  Its contents before
- *   a call do not matter (no zero-fill is needed): every word a call reads
- *   there it wrote first, and the flags that order its workgroups must equal
- *   a value new to that call.  One workspace may serve calls of every kind
- *   and shape in turn (the library's workspace bytes for that shape at
- *   least); two calls that run concurrently must not share a workspace.
+ *   la_workspace_bytes(...) bytes, owned by the caller.  Its first 256 bytes
+ *   are a control block that must hold zeros before the first call that
+ *   uses the workspace (la_workspace_init, or any zero-fill of the buffer);
+ *   calls keep it valid from then on.  The rest may hold anything before a
+ *   call: every word a call reads there it wrote first, and the flags that
+ *   order a call's workgroups carry an epoch that the control block makes
+ *   new for every call -- also for every replay of a call captured into a
+ *   HIP graph.  One workspace may serve calls of every kind and shape in turn
+ *   (with the bytes the largest of them needs); calls that may overlap in time
+ *   (on different streams) must not share a workspace.
  * Errors.  Every argument check runs on the host before anything is
  *   enqueued; on failure nothing is launched and a nonzero la_status is
  *   returned (0 means success, as the nx page's functions return 0).
- *   A launch failure returns LA_ERR_LAUNCH.
+ *   A launch failure returns LA_ERR_LAUNCH.  What only the device can see --
+ *   a bounded wait between workgroups that gave up (the outputs of that call
+ *   are then wrong), a prefix-mask value outside [0, n - 1] -- is recorded in
+ *   the workspace's control block and returned by la_workspace_status.
+ * Graphs.  Every call only launches kernels (no allocation, no memset, no
+ *   host synchronisation), so it may be captured into a HIP graph; replays
+ *   then run on the workspace captured with it, in stream order.
  */
 #ifndef LA_H
 #define LA_H
@@ -69,7 +79,10 @@ enum {
   LA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   LA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
   LA_ERR_ALIAS = 7,       /* out overlaps an input */
-  LA_ERR_LAUNCH = 8       /* the HIP runtime rejected a launch */
+  LA_ERR_LAUNCH = 8,      /* the HIP runtime rejected a launch */
+  LA_ERR_TIMEOUT = 9,     /* (la_workspace_status) a bounded wait gave up */
+  LA_ERR_RANGE = 10,      /* (la_workspace_status) a mask value out of range */
+  LA_ERR_DEVICE = 11      /* (la_workspace_status) a HIP copy or sync failed */
 };
 
 typedef int32_t la_dtype;
@@ -97,8 +110,28 @@ const char* la_status_str(la_status s);
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv,
                           int64_t n, int64_t d, la_dtype dtype, int32_t chunk);
 
-/* Non-causal normalised linear attention (nx_f32_linear_attention.nx: the
- * KV-summary loop over all keys, then the per-query read and division).
+/* Control block of a workspace (its first 256 bytes).
+ * la_workspace_init: enqueue on `stream` a kernel that zeroes it (needed
+ *   once for a new workspace that was not zero-filled).
+ * la_workspace_status: wait for `stream` to finish (host synchronisation),
+ *   then return the errors recorded since the last status call and clear
+ *   them: LA_ERR_TIMEOUT if a bounded wait between workgroups gave up in some
+ *   call (its outputs are wrong), else LA_ERR_RANGE if a prefix-mask value
+ *   lay outside [0, n - 1], else LA_OK.  LA_ERR_DEVICE if the HIP runtime
+ *   failed to synchronise or copy.
+ * la_workspace_set_wait: diagnostics for testing failure handling.  limit is
+ *   the number of polls after which a wait gives up (0: the default, about
+ *   2^22 polls); skew is added to the epoch the waits expect, so with skew
+ *   != 0 no wait can succeed and every one gives up after `limit` polls,
+ *   while every kernel still runs to its end.  (0, 0) restores the default.
+ * Each returns LA_ERR_NULL, LA_ERR_WORKSPACE (ws_bytes < 256) or LA_ERR_ALIGN
+ * for a bad workspace and launches nothing then. */
+la_status la_workspace_init(void* ws, size_t ws_bytes, void* stream);
+la_status la_workspace_status(void* ws, size_t ws_bytes, void* stream);
+la_status la_workspace_set_wait(void* ws, size_t ws_bytes, uint32_t limit, uint32_t skew, void* stream);
+
+/* Non-causal normalised linear attention (nx_f32_linear_attention.nx: S, z
+ * over all keys, then every query's normalised read).
  *   q [B][Hq][n][d], k, v [B][Hkv][n][d] -> out [B][Hq][n][d]. */
 la_status la_forward(const void* q, const void* k, const void* v, int64_t B,
                      int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
@@ -126,8 +159,12 @@ la_status la_causal_forward(const void* q, const void* k, const void* v,
 /* Unnormalised prefix-mask form Attn(Q,K,V) = Q K^T V (trim-transformer
  * 0.1.0): out_i = sum_{j <= m_i} (Q_i . K_j) V_j, no feature map, no
  * normaliser, no scale.  m is a device int64 array [n] shared by every batch
- * and head, any order, duplicates allowed; every m_i must lie in [0, n-1]
- * (not checked on the device: out-of-range values are a contract violation).
+ * and head, any order, duplicates allowed; every m_i must lie in [0, n-1].
+ * A value outside that range is a contract violation: the device clamps it
+ * into range (so that no access leaves the buffers; the outputs of such rows
+ * are then not the form's) and records it in the workspace's control block,
+ * which la_workspace_status reports as LA_ERR_RANGE (the Python binding
+ * checks this after every call when LA_DEBUG_CHECKS=1).
  * q, k, v, out [B][H][n][d].  chunk as for la_causal_forward, except that
  * the default for fp32 with d = 64 is 64. */
 la_status la_prefix_mask_forward(const void* q, const void* k, const void* v,

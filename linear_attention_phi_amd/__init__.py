@@ -16,9 +16,20 @@ Functions carry the C names:
   phi="elu1"; the latter calls la_forward_phi / la_causal_forward_phi /
   la_decode_step_phi with LA_PHI_ELU1)
   la_workspace_bytes(op, B, Hq, Hkv, n, d, dtype, chunk)
+  la_workspace_init(ws) / la_workspace_status(ws) / la_workspace_set_wait(ws, limit, skew)
   la_status_str(code)
 Tensors are contiguous [B, H, n, d] (q, out: H = Hq; k, v: H = Hkv) in
 float32 or bfloat16 on one GPU; states are float32.
+
+Workspaces: unless a call is given ws=, it uses one cached per (device,
+stream), so calls on different streams never share one (calls on one stream
+run in order).  A cached workspace starts zero-filled, as the control block
+in its first 256 bytes must.  Under HIP graph capture a call must be given
+ws= (a workspace allocated and zero-filled before the capture), because a
+workspace allocated during capture would be re-zeroed by every replay.
+With the environment variable LA_DEBUG_CHECKS=1, every forward call
+synchronises its stream afterwards and raises LAError for the errors only the
+device sees (a bounded wait that gave up, a mask value out of range).
 """
 from __future__ import annotations
 
@@ -39,7 +50,10 @@ def _phi(phi):
         raise ValueError(f"phi must be one of {sorted(_PHI)}")
     return _PHI[phi]
 STATUS_NAMES = ["LA_OK", "LA_ERR_NULL", "LA_ERR_SHAPE", "LA_ERR_DTYPE", "LA_ERR_UNSUPPORTED",
-                "LA_ERR_WORKSPACE", "LA_ERR_ALIGN", "LA_ERR_ALIAS", "LA_ERR_LAUNCH"]
+                "LA_ERR_WORKSPACE", "LA_ERR_ALIGN", "LA_ERR_ALIAS", "LA_ERR_LAUNCH", "LA_ERR_TIMEOUT",
+                "LA_ERR_RANGE", "LA_ERR_DEVICE"]
+LA_ERR_TIMEOUT, LA_ERR_RANGE = 9, 10
+CTL_BYTES = 256  # the workspace's control block
 
 _lib = None
 
@@ -71,8 +85,13 @@ def load():
         lib.la_forward_phi.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, SZ, P]
         lib.la_causal_forward_phi.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, I32, P, P, P, P, SZ, P]
         lib.la_decode_step_phi.argtypes = [P, P, P, I64, I64, I64, I64, I32, I32, P, P, P, P]
+        U32 = ctypes.c_uint32
+        lib.la_workspace_init.argtypes = [P, SZ, P]
+        lib.la_workspace_status.argtypes = [P, SZ, P]
+        lib.la_workspace_set_wait.argtypes = [P, SZ, U32, U32, P]
         for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
-                  "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched"):
+                  "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
+                  "la_workspace_init", "la_workspace_status", "la_workspace_set_wait"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -120,15 +139,54 @@ _ws_cache: dict = {}
 
 
 def workspace(nbytes: int, device):
-    """A device workspace of at least nbytes, cached per device and shared by
-    every call on that device (its contents before a call do not matter)."""
+    """A device workspace of at least nbytes, cached per (device, current
+    stream) and shared by the calls on that stream, which run in order.  It is
+    allocated zero-filled on that stream (the control block must start at
+    zero) and only ever used there.  Raises under graph capture if no cached
+    workspace is large enough (pass ws= then)."""
     torch = _torch()
-    key = (device.type, device.index)
+    if device.type != "cuda":
+        raise ValueError("inputs must be GPU tensors (there is no host path)")
+    stream = torch.cuda.current_stream(device)
+    key = (device.index, stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("a linear-attention call under graph capture needs ws= (a workspace "
+                               "allocated and zero-filled before the capture)")
+        buf = torch.zeros(max(nbytes, CTL_BYTES), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
+
+
+def new_workspace(nbytes: int, device):
+    """A zero-filled workspace of at least nbytes for the caller to keep (for
+    graph capture, or calls on several streams at once)."""
+    torch = _torch()
+    return torch.zeros(max(int(nbytes), CTL_BYTES), dtype=torch.uint8, device=device)
+
+
+def la_workspace_init(ws):
+    """Zero the control block of ws on the current stream."""
+    _call(load().la_workspace_init(_dev(ws, "ws"), ws.numel(), _stream(ws)), "la_workspace_init")
+
+
+def la_workspace_status(ws) -> int:
+    """Synchronise the current stream, then return (and clear) the status the
+    device recorded in ws since the last check: 0, LA_ERR_TIMEOUT or LA_ERR_RANGE."""
+    return int(load().la_workspace_status(_dev(ws, "ws"), ws.numel(), _stream(ws)))
+
+
+def la_workspace_set_wait(ws, limit=0, skew=0):
+    """Diagnostics: polls before a bounded wait gives up (0: default) and a skew
+    added to the epoch the waits expect (non-zero: every wait gives up)."""
+    _call(load().la_workspace_set_wait(_dev(ws, "ws"), ws.numel(), int(limit), int(skew), _stream(ws)),
+          "la_workspace_set_wait")
+
+
+def _debug_check(ws, what):
+    if os.environ.get("LA_DEBUG_CHECKS") == "1" and not _torch().cuda.is_current_stream_capturing():
+        _call(la_workspace_status(ws), what)
 
 
 def _expect(t, shape, dtype, name):
@@ -178,6 +236,7 @@ def la_forward(q, k, v, out=None, ws=None, phi="relu1"):
     else:
         _call(load().la_forward_phi(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, phi_code,
                                     _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), "la_forward_phi")
+    _debug_check(ws, "la_forward")
     return out
 
 
@@ -217,6 +276,7 @@ def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None
                                            phi_code, chunk, _dev(out, "out"), _dev(S_final, "S_final"),
                                            _dev(z_final, "z_final"), _dev(ws, "ws"), ws.numel(), _stream(k)),
               "la_causal_forward_phi")
+    _debug_check(ws, "la_causal_forward")
     if q is None:
         return S_final, z_final
     if want_state:
@@ -245,6 +305,7 @@ def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):
     fn = "la_prefix_mask_forward_batched" if batched else "la_prefix_mask_forward"
     _call(getattr(load(), fn)(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(m, "m"), B, H, n, d,
                               dt, chunk, _dev(out, "out"), _dev(ws, "ws"), ws.numel(), _stream(q)), fn)
+    _debug_check(ws, fn)
     return out
 
 

@@ -18,30 +18,60 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblaphi.so")
 ARCH = "gfx950"
 
-SOURCES = ["la_api.cpp", "la_kernels.hip", "la_fused.hip", "la_forward_bf16.hip", "la_forward_f32.hip"]
+SOURCES = ["la_api.cpp", "la_control.hip", "la_kernels.hip", "la_fused.hip", "la_forward_bf16.hip", "la_forward_f32.hip"]
+
+
+def _flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _hipcc() -> str:
+    return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def command(out: str = LIB) -> list[str]:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-function",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+    """One hipcc line that compiles and links every source (for reference)."""
+    return [_hipcc(), *_flags(), "-shared", *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+
+
+# hipcc's host pass does not know the packed-fp32 device feature and says so
+_NOISE = "'-packed-fp32-ops' is not a recognized feature"
+
+
+def _run(cmd: list[str]) -> str:
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{err}")
+    return err
 
 
 def build(verbose: bool = False) -> str:
-    cmd = command(LIB + ".tmp")
+    """Compile every source to an object (in parallel, under _build/), then
+    link liblaphi.so; the library is replaced only once the link succeeds."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        jobs.append(([_hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj], obj))
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 device feature and says so
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+        for cmd, _ in jobs:
+            print(" ".join(cmd), flush=True)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        errs = list(ex.map(lambda j: _run(j[0]), jobs))
+    link = [_hipcc(), f"--offload-arch={ARCH}", "-shared", *[o for _, o in jobs], "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(link), flush=True)
+    errs.append(_run(link))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e, file=sys.stderr)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

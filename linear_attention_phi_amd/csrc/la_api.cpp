@@ -6,8 +6,6 @@
 
 #include <stdint.h>
 
-#include <atomic>
-
 #include "la_internal.h"
 
 namespace la_internal {
@@ -129,14 +127,14 @@ size_t required_ws(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, in
     const size_t f = forward_f32_ws_bytes(B * Hkv, forward_f32_nseg(n));
     if (f > bytes) bytes = f;
   }
-  return bytes;
+  return kCtlBytes + bytes;  // the control block, then the data regions
 }
 
-// Flags of the single-launch causal kernel carry a per-call epoch; the top
-// bits 0xFFF8 make every epoch a NaN pattern, which no float state or index
-// stored in a workspace can equal.
-std::atomic<uint64_t> g_epoch{0};
-uint64_t next_epoch() { return 0xFFF8000000000000ull | (g_epoch.fetch_add(1, std::memory_order_relaxed) + 1); }
+// The launchers see the data regions (past the control block) and the block.
+void attach_ws(Fwd& a, void* ws) {
+  a.ctl = reinterpret_cast<Ctl*>(ws);
+  a.ws = reinterpret_cast<char*>(ws) + kCtlBytes;
+}
 
 la_status check_grid(const Plan& p, int64_t B, int64_t Hkv) {
   if (B * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
@@ -165,6 +163,9 @@ const char* la_status_str(la_status s) {
     case LA_ERR_ALIGN: return "LA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case LA_ERR_ALIAS: return "LA_ERR_ALIAS: an output overlaps an input";
     case LA_ERR_LAUNCH: return "LA_ERR_LAUNCH: the HIP runtime rejected a launch";
+    case LA_ERR_TIMEOUT: return "LA_ERR_TIMEOUT: a bounded wait between workgroups gave up (outputs are wrong)";
+    case LA_ERR_RANGE: return "LA_ERR_RANGE: a prefix-mask value lay outside [0, n - 1]";
+    case LA_ERR_DEVICE: return "LA_ERR_DEVICE: a HIP call failed while reading or writing the control block";
     default: return "unknown la_status";
   }
 }
@@ -211,9 +212,10 @@ la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B,
       overlaps(ws, need, v, kvb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream, (int)phi};
+  attach_ws(a, ws);
   if (forward_bf16_applies(n, d, (int)dtype)) {  // either feature map
     if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
-    return launch_forward_bf16(a, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
+    return launch_forward_bf16(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   if (forward_f32_applies(n, d, (int)dtype)) {  // either feature map
     if (B * Hq * forward_f32_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
@@ -260,10 +262,11 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
   if (overlaps(ws, need, out, qb) || overlaps(ws, need, S_final, sb) || overlaps(ws, need, z_final, zb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream, (int)phi};
+  attach_ws(a, ws);
   if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // either feature map
     const Plan fp = make_fused_plan(n);
     if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
-    return launch_causal_fused(a, fp, next_epoch()) == 0 ? LA_OK : LA_ERR_LAUNCH;
+    return launch_causal_fused(a, fp) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   return launch_causal(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
@@ -299,6 +302,7 @@ static la_status prefix_impl(const void* q, const void* k, const void* v, const 
       overlaps(ws, need, m, mb) || overlaps(ws, need, out, tb))
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, H, H, n, d, (int)dtype, m, nullptr, nullptr, ws, stream, 0, batched ? B : 1};
+  attach_ws(a, ws);
   return launch_prefix(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 

@@ -2,8 +2,8 @@
 //
 // out_i = phi(Q_i) S / (phi(Q_i) . z) with S = sum_j phi(K_j) (x) V_j and
 // z = sum_j phi(K_j) over all n keys of the query's key/value head
-// (nx_f32_linear_attention.nx: "accumulate KV-summary" and "per-query"
-// loops; LinearTile 1.0.1, "How It Works": K^T V once, then Q).  One launch
+// (nx_f32_linear_attention.nx source, header comment: S and z over all
+// keys, then each query's normalised read; LinearTile 1.0.1, "How It Works": K^T V once, then Q).  One launch
 // whose workgroups take one of three roles by their index, streaming the
 // data once with one wave per 64-token chunk:
 //
@@ -28,9 +28,11 @@
 // A workgroup only waits for workgroups of lower index, which are
 // dispatched before it.  Published data goes through memory with
 // device-scope (sc1) stores and loads, and each publication is announced
-// by a 64-bit flag set to the call's epoch (a NaN pattern that no value the
-// workspace held before can equal) once the data stores have completed.
-// Spins are bounded; exhausting the bound records an error bit instead of
+// by a 64-bit flag set to the call's epoch (taken from the workspace's
+// control block, la_ctl.h: a NaN pattern that no value the workspace held
+// before can equal, new for every call and every replay of a captured
+// launch) once the data stores have completed.  Spins are bounded;
+// exhausting the bound records an error bit in the control block instead of
 // hanging.
 //
 // phi(K)^T V is formed as relu(K)^T V + 1 (x) sum_t V_t and z as
@@ -41,6 +43,7 @@
 #include <stdint.h>
 
 #include "la_bf16.h"
+#include "la_ctl.h"
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -80,19 +83,41 @@ struct FwdArgs {
   uint8_t* tot;     // [NKV][TOT_BYTES]
   uint64_t* sflag;  // [NKV][nseg]: the segment's partial is published
   uint64_t* rflag;  // [NKV][RED_BLOCKS]: the slice of the head's total is published
-  uint32_t* err;    // bit 0: a wait ran out of spins
-  uint64_t epoch;
+  la_internal::Ctl* ctl;
+  uint64_t host_epoch;  // the call's epoch, or 0: take it from the control block
 };
+
+// The call's epoch as the workgroup sees it (in LDS, written by thread 0).
+struct EpochLds {
+  uint64_t epoch, expect;  // flags are set to epoch; waits compare with expect
+  uint32_t limit;          // polls before a wait gives up
+};
+
+// Thread 0 takes the call's epoch from the control words it loaded and counts
+// the workgroup in; returns the counter's old value (for ctl_leave).
+__device__ __forceinline__ uint32_t take_epoch(const FwdArgs& A, const la_ctl::CtlView& cv, EpochLds& E) {
+  E.epoch = A.host_epoch ? A.host_epoch : la_ctl::epoch_of(cv.gen);
+  E.expect = E.epoch + cv.skew;
+  E.limit = la_ctl::wait_limit(cv);
+  return A.host_epoch ? 0u : la_ctl::ctl_arrive(A.ctl, cv);
+}
+// The thread that took the epoch, after its last use of it.
+__device__ __forceinline__ void leave_epoch(const FwdArgs& A, uint32_t arrived, const EpochLds& E) {
+  if (!A.host_epoch) la_ctl::ctl_leave(A.ctl, arrived, E.epoch);
+}
 
 // Every lane of the calling wave spins until flags[0 .. cnt) all hold the
 // call's epoch, then orders its later loads after the flags.
-__device__ __forceinline__ void wait_epoch(const uint64_t* flags, int64_t cnt, const FwdArgs& A, int lane) {
+__device__ __forceinline__ void wait_epoch(const uint64_t* flags, int64_t cnt, const FwdArgs& A, const EpochLds& E,
+                                           int lane) {
+  const uint64_t expect = E.expect;
+  const uint32_t limit = E.limit;
   for (int64_t p = lane; p < cnt; p += 64) {
     uint32_t spins = 0;
-    while (__hip_atomic_load(flags + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != A.epoch) {
+    while (__hip_atomic_load(flags + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != expect) {
       __builtin_amdgcn_s_sleep(2);
-      if (++spins > (1u << 22)) {
-        atomicOr(A.err, 1u);
+      if (++spins >= limit) {
+        la_ctl::ctl_fail(A.ctl, la_internal::kErrWait);
         break;
       }
     }
@@ -112,9 +137,11 @@ __device__ __forceinline__ float* state_row(StateLds& L, int c, int b) {
 }
 
 template <int PM>
-__device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLds& L) {
+__device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLds& L, EpochLds& E) {
   constexpr bool SPLIT = PM == PM_RELU1;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
+  la_ctl::CtlView cv{};
+  if (w == 0) cv = la_ctl::ctl_load(A.ctl);  // used once this wave's loads are in
   const int64_t seg = bid / A.NKV, head = bid % A.NKV;
   const int hbytes = (int)(A.n * FD * 2);  // one head's rows (n <= 2^24)
   const __amdgpu_buffer_rsrc_t rk =
@@ -199,6 +226,8 @@ __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLd
       }
     }
   }
+  uint32_t arrived = 0;
+  if (tid == 0) arrived = take_epoch(A, cv, E);
   __syncthreads();
 
   // The segment's partial: thread (w, lane) sums the lane slots of
@@ -239,14 +268,20 @@ __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLd
   if (w == 0) st_buf1<CPOL_SC1>(rp, (FD * FD + lane) * 4, zrun);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(A.sflag + head * A.nseg + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(A.sflag + head * A.nseg + seg, E.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    leave_epoch(A, arrived, E);
+  }
 }
 
 // Thread t of a head's RED_BLOCKS * RED_THREADS handles floats 4 t .. 4 t + 3
 // of a partial (S^T [b][a] for 4 t < FD * FD, else z).
-__device__ __forceinline__ void fwd_reduce(const FwdArgs& A, int64_t bid) {
+__device__ __forceinline__ void fwd_reduce(const FwdArgs& A, int64_t bid, EpochLds& E) {
   const int64_t head = bid / RED_BLOCKS, slice = bid % RED_BLOCKS;
-  wait_epoch(A.sflag + head * A.nseg, A.nseg, A, threadIdx.x & 63);
+  uint32_t arrived = 0;
+  if (threadIdx.x == 0) arrived = take_epoch(A, la_ctl::ctl_load(A.ctl), E);
+  __syncthreads();
+  wait_epoch(A.sflag + head * A.nseg, A.nseg, A, E, threadIdx.x & 63);
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
       A.part + head * A.nseg * PART_FLOATS, 0, (int)(A.nseg * PART_FLOATS * 4), 0x00020000);
   const __amdgpu_buffer_rsrc_t rt =
@@ -300,16 +335,23 @@ __device__ __forceinline__ void fwd_reduce(const FwdArgs& A, int64_t bid) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(A.rflag + head * RED_BLOCKS + slice, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(A.rflag + head * RED_BLOCKS + slice, E.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    leave_epoch(A, arrived, E);
+  }
 }
 
 template <int PM>
-__device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (&Lout)[W][TILE_B]) {
+__device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (&Lout)[W][TILE_B], EpochLds& E) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
   const int64_t seg = bid / A.NQ, qh = bid % A.NQ, kvh = qh / A.R;
-  const int64_t c0 = (seg * W + w) * OC;  // this wave's first chunk
-  if (c0 >= A.nchunks) return;            // no barrier below: a wave without a chunk leaves
+  const int64_t c0 = (seg * W + w) * OC;  // this wave's first chunk (wave 0 always has one)
+  la_ctl::CtlView cv{};
+  if (w == 0) cv = la_ctl::ctl_load(A.ctl);
+  if (c0 >= A.nchunks) {  // a wave without a chunk leaves after the epoch barrier
+    __syncthreads();
+    return;
+  }
   const int hbytes = (int)(A.n * FD * 2);
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + qh * A.n * FD), 0, hbytes, 0x00020000);
@@ -332,7 +374,10 @@ __device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (
         qraw[j][ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(
             rq, (((int)(c0 + j) * FC + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  wait_epoch(A.rflag + kvh * RED_BLOCKS, RED_BLOCKS, A, lane);
+  uint32_t arrived = 0;
+  if (tid == 0) arrived = take_epoch(A, cv, E);
+  __syncthreads();
+  wait_epoch(A.rflag + kvh * RED_BLOCKS, RED_BLOCKS, A, E, lane);
   Frag<bf16> sf[2][4], zf[4];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
@@ -388,6 +433,7 @@ __device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (
       __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
                                              ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, CPOL_NT);
   }
+  if (tid == 0) leave_epoch(A, arrived, E);
 }
 
 union FwdLds {
@@ -398,13 +444,14 @@ union FwdLds {
 template <int PM>
 __global__ __launch_bounds__(WNT) void k_fwd_one(FwdArgs A) {
   __shared__ __attribute__((aligned(16))) FwdLds L;
+  __shared__ EpochLds E;
   const int64_t nS = A.NKV * A.nseg, nR = A.NKV * RED_BLOCKS, b = blockIdx.x;
   if (b < nS)
-    fwd_state<PM>(A, b, L.state);
+    fwd_state<PM>(A, b, L.state, E);
   else if (b < nS + nR)
-    fwd_reduce(A, b - nS);
+    fwd_reduce(A, b - nS, E);
   else
-    fwd_out<PM>(A, b - nS - nR, L.out);
+    fwd_out<PM>(A, b - nS - nR, L.out, E);
 }
 
 }  // namespace
@@ -424,10 +471,10 @@ int64_t forward_bf16_grid(int64_t NKV, int64_t NQ, int64_t n) {
 
 size_t forward_bf16_ws_bytes(int64_t NKV, int64_t nseg) {
   return (size_t)NKV * nseg * PART_FLOATS * sizeof(float) + (size_t)NKV * TOT_BYTES +
-         (size_t)NKV * (nseg + RED_BLOCKS) * sizeof(uint64_t) + 256;
+         (size_t)NKV * (nseg + RED_BLOCKS) * sizeof(uint64_t);
 }
 
-int launch_forward_bf16(const Fwd& a, uint64_t epoch) {
+int launch_forward_bf16(const Fwd& a) {
   static_assert(RED_THREADS == WNT, "one block size for every role");
   static_assert(RED_S_BLOCKS * RED_THREADS * 8 == FD * FD && FD / 4 <= RED_THREADS, "reduce slices");
   static_assert(TOT_BYTES % 16 == 0 && (PART_FLOATS * 4) % 16 == 0, "workspace alignment");
@@ -438,10 +485,9 @@ int launch_forward_bf16(const Fwd& a, uint64_t epoch) {
   uint8_t* tot = reinterpret_cast<uint8_t*>(part + NKV * nseg * PART_FLOATS);
   uint64_t* sflag = reinterpret_cast<uint64_t*>(tot + NKV * TOT_BYTES);
   uint64_t* rflag = sflag + NKV * nseg;
-  uint32_t* err = reinterpret_cast<uint32_t*>(rflag + NKV * RED_BLOCKS);
   FwdArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
             reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, nchunks, nseg, NKV, NQ,
-            a.Hq / a.Hkv, part, tot, sflag, rflag, err, epoch};
+            a.Hq / a.Hkv, part, tot, sflag, rflag, a.ctl, launch_epoch(a.stream)};
   if (a.phi == 1)
     k_fwd_one<PM_ELU1><<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
   else

@@ -2,8 +2,8 @@
 //
 // out_i = phi(Q_i) S / (phi(Q_i) . z) with S = sum_j phi(K_j) (x) V_j and
 // z = sum_j phi(K_j) over all n keys of the query's key/value head
-// (nx_f32_linear_attention.nx: "accumulate KV-summary" and "per-query"
-// loops; LinearTile 1.0.1, "How It Works": K^T V once, then Q).
+// (nx_f32_linear_attention.nx source, header comment: S and z over all
+// keys, then each query's normalised read; LinearTile 1.0.1, "How It Works": K^T V once, then Q).
 //
 // The products run on v_mfma_f32_16x16x4_f32, whose operands put the
 // contraction index k on lane / 16 and the other index on lane % 16.  A

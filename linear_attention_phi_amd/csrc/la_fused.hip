@@ -33,14 +33,16 @@
 // Segments are numbered segment-major (blockIdx = seg * NH + head), so a
 // workgroup only ever waits for workgroups dispatched before it.  Aggregates
 // go through memory with device-scope stores and loads (the XCDs' L2 caches
-// are not coherent with each other).  Flags are 64-bit words holding a
-// per-call epoch (top bits 0xFFF8: a NaN pattern, so no float or index the
-// workspace held before can equal one).  Spins are bounded; exhausting the
-// bound records an error bit instead of hanging.
+// are not coherent with each other).  Flags are 64-bit words holding the
+// call's epoch, taken from the workspace's control block (la_ctl.h), so that
+// replays of a captured launch are ordered as well.  Spins are bounded;
+// exhausting the bound records an error bit in the control block (read by
+// la_workspace_status) instead of hanging.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "la_bf16.h"
+#include "la_ctl.h"
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -62,8 +64,9 @@ constexpr int REGION_B = 2 * TILE_B;      // one wave's LDS region
 struct FusedArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* out;
   int64_t n, nchunks, nseg, NH;
-  float* agg; uint64_t* flags; uint64_t epoch;
-  float* S_final; float* z_final; uint32_t* err;
+  float* agg; uint64_t* flags;
+  float* S_final; float* z_final; la_internal::Ctl* ctl;
+  uint64_t host_epoch;  // the call's epoch, or 0: take it from the control block
 };
 
 // LDS: one region per wave, reused phase by phase:
@@ -81,6 +84,8 @@ struct CpLds {
   bf16 sprev[FC * RS];         // S_prev^T [b][a] in bf16: the earlier segments' total
   uint32_t zhp[FD / 2];        // z_prev as bf16 (high, low) pairs
   uint32_t zlp[FD / 2];
+  uint64_t epoch, expect;      // the call's epoch; what the waits compare flags with
+  uint32_t limit;              // polls before a wait gives up
 };
 static_assert(32 * RSF * 4 <= TILE_B, "state half-tile must fit a token-major tile");
 
@@ -116,6 +121,9 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   bf16* tK = reinterpret_cast<bf16*>(L.reg[w]);
   bf16* tV = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
   if (tid < FD) L.zero[tid] = (bf16)0.0f;
+  // the control words are requested first; wave 0 uses them after its loads
+  la_ctl::CtlView cv{};
+  if (w == 0) cv = la_ctl::ctl_load(A.ctl);
 
   // ------------------------------------------------------------------ A
   // Loads: K and V as 16-byte row pieces (rows lane / 8 + 8 u), Q directly
@@ -267,6 +275,14 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       den[ib] = ds + __shfl_xor(ds, 32);
     }
   }
+  // the call's epoch, and this workgroup counted in (its loads are all in)
+  uint32_t arrived = 0;
+  if (tid == 0) {
+    L.epoch = A.host_epoch ? A.host_epoch : la_ctl::epoch_of(cv.gen);
+    L.expect = L.epoch + cv.skew;
+    L.limit = la_ctl::wait_limit(cv);
+    if (!A.host_epoch) arrived = la_ctl::ctl_arrive(A.ctl, cv);
+  }
   __syncthreads();
 
   // ------------------------------------------------------------------ B
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's aggregate stores have completed
   }
   __syncthreads();  // also: every state tile has been read
-  if (publish && tid == 0) __hip_atomic_store(flag + seg, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (publish && tid == 0) __hip_atomic_store(flag + seg, L.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // S_loc(c) (this segment's chunks before c) in bf16, [b][a] rows of RS,
   // over region c, and z_loc(c) as pairs; their products with phi(Q) run
@@ -350,12 +366,14 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 
   if (seg > 0) {
     if (w == 0) {
+      const uint64_t expect = L.expect;
+      const uint32_t limit = L.limit;
       for (int64_t p = lane; p < seg; p += 64) {
         uint32_t spins = 0;
-        while (__hip_atomic_load(flag + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != A.epoch) {
+        while (__hip_atomic_load(flag + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != expect) {
           __builtin_amdgcn_s_sleep(2);
-          if (++spins > (1u << 22)) {
-            atomicOr(A.err, 1u);
+          if (++spins >= limit) {
+            la_ctl::ctl_fail(A.ctl, la_internal::kErrWait);
             break;
           }
         }
@@ -440,6 +458,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
                                              ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, CPOL_NT);
   }
+  if (tid == 0 && !A.host_epoch) la_ctl::ctl_leave(A.ctl, arrived, L.epoch);
 }
 
 }  // namespace
@@ -454,19 +473,18 @@ bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dty
 }
 
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {
-  return (size_t)NH * nseg * (AGG_FLOATS * sizeof(float) + sizeof(uint64_t)) + 256;
+  return (size_t)NH * nseg * (AGG_FLOATS * sizeof(float) + sizeof(uint64_t));
 }
 
-int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch) {
+int launch_causal_fused(const Fwd& a, const Plan& p) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const int64_t NH = a.B * a.Hkv;
   float* agg = reinterpret_cast<float*>(a.ws);
   uint64_t* flags = reinterpret_cast<uint64_t*>(agg + NH * p.nseg * AGG_FLOATS);
-  uint32_t* err = reinterpret_cast<uint32_t*>(flags + NH * p.nseg);
   static_assert(kFusedG == SEGC, "segment length");
   FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
               reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, p.nchunks, p.nseg, NH,
-              agg, flags, epoch, a.S_final, a.z_final, err};
+              agg, flags, a.S_final, a.z_final, a.ctl, launch_epoch(a.stream)};
   if (a.phi == 1)
     k_causal_fused<PM_ELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
   else

@@ -9,6 +9,35 @@ namespace la_internal {
 
 constexpr int kMaxD = 128;
 
+// Control block: the first kCtlBytes of every workspace (the data regions
+// follow it).  It must hold zeros before the first call that uses the
+// workspace; every call leaves it valid for the next one on the same stream.
+//   gen         epoch of the last call whose workgroups were ordered by
+//               flags; a call's flags carry the next epoch, so that flags a
+//               previous call (or a replay of the same captured launch) left
+//               behind never match
+//   arrive      workgroups of the running call that have taken their epoch;
+//               the last one stores the new gen and resets it to 0
+//   err         sticky error bits, read and cleared by la_workspace_status
+//   wait_limit  polls before a bounded wait gives up (0: kDefaultWaitLimit)
+//   wait_skew   added to the epoch that waits expect: 0, except when a test
+//               makes every wait give up on purpose
+constexpr size_t kCtlBytes = 256;
+struct Ctl {
+  uint64_t gen;
+  uint32_t arrive;
+  uint32_t err;
+  uint32_t wait_limit;
+  uint32_t wait_skew;
+};
+constexpr uint32_t kErrWait = 1;   // a bounded wait gave up
+constexpr uint32_t kErrRange = 2;  // a prefix-mask value lay outside [0, n - 1]
+constexpr uint32_t kDefaultWaitLimit = 1u << 22;
+// The epoch a launch on this stream passes to its kernel: a new host epoch
+// (top bits 0xFFF8) if the stream is not capturing, 0 if it is (the kernel
+// then takes its epoch from the control block; la_ctl.h).
+uint64_t launch_epoch(void* stream);
+
 // Feature dimension padded to the 32-wide MFMA tile.
 inline int padded_dim(int64_t d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
 
@@ -52,6 +81,7 @@ struct Fwd {
   void* stream;
   int phi = 0;           // feature map of the normalised forms: 0 relu + 1, 1 ELU + 1
   int64_t nmask = 1;     // prefix form: masks in m (1: shared [n]; B: one per batch, [B][n])
+  Ctl* ctl = nullptr;    // the workspace's control block (ws points past it)
 };
 
 // Each returns 0 on success, else a nonzero HIP error code.
@@ -64,11 +94,11 @@ constexpr int kFusedG = 8;
 constexpr int64_t kFusedMaxN = 131072;  // up to 256 segments per head
 bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk);
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg);
-int launch_causal_fused(const Fwd& a, const Plan& p, uint64_t epoch);
+int launch_causal_fused(const Fwd& a, const Plan& p);
 
 // Non-causal path for bf16, d = 64 (la_forward_bf16.hip): one launch; state
 // partials per segment of kFwdSegChunks chunks, a reduce, then the output
-// pass, ordered by flags that carry the call's epoch.
+// pass, ordered by flags that carry the call's epoch (from the control block).
 constexpr int kFwdSegChunks = 4;
 // n bound: one head's rows, padded to a whole segment, stay below 2^31 bytes
 // (the range of a buffer resource's record count and offsets).
@@ -77,7 +107,7 @@ bool forward_bf16_applies(int64_t n, int64_t d, int dtype);
 int64_t forward_bf16_nseg(int64_t n);
 size_t forward_bf16_ws_bytes(int64_t NKV, int64_t nseg);
 int64_t forward_bf16_grid(int64_t NKV, int64_t NQ, int64_t n);
-int launch_forward_bf16(const Fwd& a, uint64_t epoch);
+int launch_forward_bf16(const Fwd& a);
 
 // Non-causal path for fp32, d = 64 (la_forward_f32.hip): state partials per
 // segment of kFwd32SegTokens keys, a reduce, then the output pass.

@@ -1,7 +1,7 @@
 // la_kernels.hip -- gfx950 (MI355X) kernels for kernelized linear attention.
 //
-// Method (nx_f32_linear_attention.nx source: function la_phi, the
-// "accumulate KV-summary" loop and the "per-query" loop): with
+// Method (nx_f32_linear_attention.nx source, header comment: the feature
+// map, the key/value summary and the normalised read): with
 // phi(x) = relu(x) + 1,  S = sum_j phi(K_j) (x) V_j,  z = sum_j phi(K_j),
 // out_i = phi(Q_i) S / (phi(Q_i) . z).  The causal and prefix-mask forms
 // (trim-transformer 0.1.0, "Masking") restrict query i to keys 0..m_i.
@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "la_bf16.h"
+#include "la_ctl.h"
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -1184,10 +1185,14 @@ __device__ __forceinline__ int bucket_take(int* cnt, int b, bool valid, int lane
 }
 
 // The sort, for one workgroup of up to 1024 threads; cnt holds nchunks + 1
-// ints and part one int per thread, both in LDS.
+// ints and part one int per thread, both in LDS.  A mask value outside
+// [0, n - 1] breaks the form's contract: it is clamped into range (so that
+// every access stays inside the buffers) and recorded in the control
+// block's error word, which la_workspace_status reports.
 __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks, int* __restrict__ boff,
-                            int* __restrict__ perm, int* cnt, int* part) {
+                            int* __restrict__ perm, int* cnt, int* part, la_internal::Ctl* ctl) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+  bool bad = false;
   const int len = (int)nchunks + 1;
   for (int c = tid; c < len; c += nt) cnt[c] = 0;
   __syncthreads();
@@ -1211,6 +1216,7 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
       bk[k] = -1;
       if (i < n) {
         int64_t mi = mv[k];
+        bad |= mi < 0 || mi >= n;
         mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
         bk[k] = (int)(mi / C);
       }
@@ -1218,6 +1224,7 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
 #pragma unroll
     for (int k = 0; k < PER; ++k) bucket_take(cnt, bk[k] + 1, bk[k] >= 0, lane);
   }
+  if (__ballot(bad) != 0 && lane == 0) la_ctl::ctl_fail(ctl, la_internal::kErrRange);
   __syncthreads();
   // inclusive scan of cnt[0..nchunks] (cnt[0] == 0): contiguous per-thread
   // ranges, then a scan of the per-thread sums
@@ -1272,13 +1279,14 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
 // Workgroup b sorts mask b (m [nmask][n] into boff [nmask][nchunks + 1] and
 // perm [nmask][n]).
 __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks,
-                                                 int* __restrict__ boff, int* __restrict__ perm) {
+                                                 int* __restrict__ boff, int* __restrict__ perm,
+                                                 la_internal::Ctl* ctl) {
   m += blockIdx.x * n;
   boff += blockIdx.x * (nchunks + 1);
   perm += blockIdx.x * n;
   __shared__ int cnt[la_internal::kMaxBuckets + 1];
   __shared__ int part[1024];
-  bucket_sort(m, n, C, nchunks, boff, perm, cnt, part);
+  bucket_sort(m, n, C, nchunks, boff, perm, cnt, part, ctl);
 }
 
 // ---------------------------------------------------------------- k_state32
@@ -1310,13 +1318,14 @@ template <int PM>
 __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, const float* __restrict__ v, int64_t n,
                                                  int64_t nchunks, int C, int64_t G, int64_t nseg,
                                                  float* __restrict__ ws, const int64_t* __restrict__ m,
-                                                 int* __restrict__ boff, int* __restrict__ perm, int64_t nmask) {
+                                                 int* __restrict__ boff, int* __restrict__ perm, int64_t nmask,
+                                                 la_internal::Ctl* ctl) {
   constexpr int FD = 64, TW = 32, NW8 = 8;
   __shared__ State32Lds L;
   int64_t sb = blockIdx.x;  // state block
   if (m) {
     if (sb < nmask) {  // blocks 0 .. nmask - 1 sort the masks
-      bucket_sort(m + sb * n, n, C, nchunks, boff + sb * (nchunks + 1), perm + sb * n, L.b.cnt, L.b.part);
+      bucket_sort(m + sb * n, n, C, nchunks, boff + sb * (nchunks + 1), perm + sb * n, L.b.cnt, L.b.part, ctl);
       return;
     }
     sb -= nmask;
@@ -1656,7 +1665,7 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
     } else if (s32) {
       if constexpr (std::is_same<T, float>::value && DP == 64)
         k_state32<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
-                                                                           states, nullptr, nullptr, nullptr, 1);
+                                                                           states, nullptr, nullptr, nullptr, 1, nullptr);
     } else {
       k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
                                                                                p.G, p.nseg, states);
@@ -1700,17 +1709,17 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
       if (vec && a.n <= la_internal::kFwd32MaxN) {  // the sort as one more workgroup of the state launch
         k_state32<PM_ID><<<dim3((unsigned)(nbh * p.nseg + a.nmask)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G,
                                                                                     p.nseg, states, a.m, boff, perm,
-                                                                                    a.nmask);
+                                                                                    a.nmask, a.ctl);
         state_done = true;
       }
     }
-    if (!state_done) k_bucket<<<dim3((unsigned)a.nmask), 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm);
+    if (!state_done) k_bucket<<<dim3((unsigned)a.nmask), 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm, a.ctl);
   }
   const bool phi = (form == CAUSAL);
   if constexpr (std::is_same<T, float>::value && DP == 64) {
     if (phi && vec && a.n <= la_internal::kFwd32MaxN) {
       k_state32<PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
-                                                                       states, nullptr, nullptr, nullptr, 1);
+                                                                       states, nullptr, nullptr, nullptr, 1, nullptr);
       state_done = true;
     }
   }

@@ -6,11 +6,11 @@
  * beyond the definitions below.  It shares no code with the HIP library.
  *
  * Sources (web pages this follows):
- *  - "nx_f32_linear_attention.nx source" (nishifamily.com): the feature map
- *    phi(x) = relu(x) + 1 (function la_phi), the key/value summary
- *    S = sum_j phi(K_j) (x) V_j and z = sum_j phi(K_j) (the "accumulate
- *    KV-summary" loop), and out_i = phi(Q_i) S / (phi(Q_i) . z) (the
- *    "per-query" loop).  S is stored [a][b] row-major, as on that page.
+ *  - "nx_f32_linear_attention.nx source" (nishifamily.com), its header
+ *    comment: the feature map phi(x) = relu(x) + 1, the key/value summary
+ *    S = sum_j phi(K_j) (x) V_j (d x d) and z = sum_j phi(K_j), and the read
+ *    out_i = phi(Q_i) S / (phi(Q_i) . z).  Each entry of S and z below is its
+ *    own sum over the keys, written as the definition states it.
  *  - "LinearTile 1.0.1" (files.pythonhosted.org), section "How It Works":
  *    the same O = phi(Q) (phi(K)^T V) with phi(x) = ELU(x) + 1, the second
  *    feature map offered here (ELU with alpha = 1, the page naming no other:
@@ -95,28 +95,31 @@ void lao_forward(const void* q, const void* k, const void* v, int dtype,
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t h = 0; h < Hq; ++h) {
       const int64_t g = h / R;
-      double* S = (double*)calloc((size_t)(d * d), sizeof(double));
-      double* z = (double*)calloc((size_t)d, sizeof(double));
-      double* pk = (double*)malloc((size_t)d * sizeof(double));
-      /* S = sum_j phi(K_j) (x) V_j, z = sum_j phi(K_j), over all n keys. */
-      for (int64_t j = 0; j < n; ++j) {
-        const int64_t o = off4(b, g, j, Hkv, n, d);
-        for (int64_t a = 0; a < d; ++a) {
-          pk[a] = phi(rd(k, dtype, o + a), phik);
-          z[a] += pk[a];
+      double* S = (double*)malloc((size_t)(d * d) * sizeof(double));
+      double* z = (double*)malloc((size_t)d * sizeof(double));
+      double* pq = (double*)malloc((size_t)d * sizeof(double));
+      const int64_t o = off4(b, g, 0, Hkv, n, d); /* key/value row 0 */
+      /* z[a] = sum over all n keys of phi(K_j[a]);
+       * S[a][c] = sum over all n keys of phi(K_j[a]) * V_j[c]. */
+      for (int64_t a = 0; a < d; ++a) {
+        double za = 0.0;
+        for (int64_t j = 0; j < n; ++j) za += phi(rd(k, dtype, o + j * d + a), phik);
+        z[a] = za;
+        for (int64_t c = 0; c < d; ++c) {
+          double sac = 0.0;
+          for (int64_t j = 0; j < n; ++j)
+            sac += phi(rd(k, dtype, o + j * d + a), phik) * rd(v, dtype, o + j * d + c);
+          S[a * d + c] = sac;
         }
-        for (int64_t a = 0; a < d; ++a)
-          for (int64_t c = 0; c < d; ++c)
-            S[a * d + c] += pk[a] * rd(v, dtype, o + c);
       }
       for (int64_t r = 0; r < nr; ++r) {
         const int64_t i = rows ? rows[r] : r;
-        normalised_read(q, dtype, phik, off4(b, h, i, Hq, n, d), d, S, z, pk,
+        normalised_read(q, dtype, phik, off4(b, h, i, Hq, n, d), d, S, z, pq,
                         out + off4(b, h, r, Hq, nr, d));
       }
       free(S);
       free(z);
-      free(pk);
+      free(pq);
     }
   }
 }

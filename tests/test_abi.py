@@ -31,7 +31,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert set(names) == {"la_status_str", "la_workspace_bytes", "la_forward", "la_causal_forward",
                           "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
-                          "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched"}
+                          "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
+                          "la_workspace_init", "la_workspace_status", "la_workspace_set_wait"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -40,13 +41,39 @@ def test_status_strings(lib):
     for code, name in enumerate(la.STATUS_NAMES):
         assert la.la_status_str(code).startswith(name)
     assert la.la_status_str(99) == "unknown la_status"
+    # the device-side statuses la_workspace_status returns
+    assert la.la_status_str(9).startswith("LA_ERR_TIMEOUT")
+    assert la.la_status_str(10).startswith("LA_ERR_RANGE")
+    assert la.la_status_str(11).startswith("LA_ERR_DEVICE")
+    assert (la.LA_ERR_TIMEOUT, la.LA_ERR_RANGE) == (9, 10)
+
+
+def test_control_block_calls_reject_bad_workspaces(lib):
+    """la_workspace_init / _status / _set_wait check the workspace on the host
+    and return before any HIP call when it is NULL, smaller than the 256-byte
+    control block or misaligned."""
+    for ws, nbytes, want in ((None, 4096, NULL), (WSP, 255, WS), (WSP, 0, WS), (WSP + 8, 4096, ALIGN)):
+        assert lib.la_workspace_init(ws, nbytes, None) == want
+        assert lib.la_workspace_status(ws, nbytes, None) == want
+        assert lib.la_workspace_set_wait(ws, nbytes, 64, 1, None) == want
+
+
+def test_workspace_bytes_include_the_control_block(lib):
+    """Every forward workspace holds the 256-byte control block before its
+    data regions: the causal general path's size is that block plus (nseg + 1)
+    fp32 state slots per head."""
+    f = la.la_workspace_bytes
+    # fp32 d = 32 causal, B1 H1 n64 chunk 32: two one-chunk segments -> 3 slots of 32*32 + 32 floats
+    assert f(la.LA_OP_CAUSAL, 1, 1, 1, 64, 32, la.LA_F32, 32) == 256 + 3 * 4 * (32 * 32 + 32)
+    for op in (la.LA_OP_FORWARD, la.LA_OP_CAUSAL, la.LA_OP_PREFIX_MASK):
+        assert f(op, 1, 1, 1, 1, 1, la.LA_F32, 0) > 256
 
 
 def test_workspace_bytes():
     f = la.la_workspace_bytes
     # causal bf16 B8 H8 n2048 d64: (nseg + 1) fp32 slots of (64*64 + 64) per head
     b = f(la.LA_OP_CAUSAL, 8, 8, 8, 2048, 64, la.LA_BF16, 64)
-    assert b > 0 and b % (4 * (64 * 64 + 64)) == 0
+    assert b > 256 and (b - 256) % (4 * (64 * 64 + 64)) == 0
     assert f(la.LA_OP_CAUSAL, 8, 8, 8, 2048, 64, la.LA_BF16, 0) == b  # default chunk is 64
     assert f(la.LA_OP_FORWARD, 2, 8, 8, 4096, 64, la.LA_F32, 0) > 0
     # prefix form: states plus bucket offsets and the permutation

@@ -105,11 +105,12 @@ def test_noncausal_small(gpu, dtype, case):
 
 @pytest.mark.parametrize("fill", ["random", "ones"])
 def test_workspace_contents_do_not_matter(gpu, fill):
-    """The kernels that hand data between workgroups (the non-causal passes,
-    the single-launch causal kernel, the prefix form's sort and state) read
-    no workspace word before this call wrote it: their flags must equal the
-    call's epoch, so a workspace holding random bytes or all-ones bytes gives
-    the same outputs as a zero-filled one."""
+    """Past the control block (zeroed by la_workspace_init), the kernels that
+    hand data between workgroups (the non-causal passes, the single-launch
+    causal kernel, the prefix form's sort and state) read no workspace word
+    before this call wrote it: their flags must equal the call's epoch, so a
+    workspace holding random bytes or all-ones bytes gives the same outputs
+    as a zero-filled one."""
     import torch
     gen = torch.Generator(device="cpu").manual_seed(3)
 
@@ -119,7 +120,9 @@ def test_workspace_contents_do_not_matter(gpu, fill):
             w = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=gen)
         else:
             w = torch.full((nbytes,), 255, dtype=torch.uint8)
-        return w.to("cuda")
+        w = w.to("cuda")
+        gpu.la_workspace_init(w)
+        return w
 
     for dtype in (li.BF16, li.F32):
         B, Hq, Hkv, n, d = 2, 4, 2, 1000, 64
