@@ -156,6 +156,23 @@ la_status la_causal_forward(const void* q, const void* k, const void* v,
                             void* out, float* S_final, float* z_final,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* la_causal_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same results
+ * (the same kernels).  Its workspace is a static 64 MiB device array per GPU,
+ * held until the process ends; sizes whose la_workspace_bytes(LA_OP_CAUSAL,
+ * ...) exceed it return LA_ERR_WORKSPACE and launch nothing (the causal
+ * workload B8 H8 n2048 d64 needs about 4.3 MB).  It calls no allocator.
+ * Every call on a GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (on different streams) race on it.  The errors that
+ * la_workspace_status reports for a caller's workspace are recorded in the
+ * array and cannot be read back. */
+la_status la_causal_forward_noalloc(const void* q, const void* k, const void* v,
+                                    int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t n, int64_t d, la_dtype dtype,
+                                    int32_t chunk, void* out, float* S_final,
+                                    float* z_final, void* stream);
+
 /* Unnormalised prefix-mask form Attn(Q,K,V) = Q K^T V (trim-transformer
  * 0.1.0): out_i = sum_{j <= m_i} (Q_i . K_j) V_j, no feature map, no
  * normaliser, no scale.  m is a device int64 array [n] shared by every batch

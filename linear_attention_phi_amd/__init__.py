@@ -89,9 +89,11 @@ def load():
         lib.la_workspace_init.argtypes = [P, SZ, P]
         lib.la_workspace_status.argtypes = [P, SZ, P]
         lib.la_workspace_set_wait.argtypes = [P, SZ, U32, U32, P]
+        lib.la_causal_forward_noalloc.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, P, P]
         for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
                   "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
-                  "la_workspace_init", "la_workspace_status", "la_workspace_set_wait"):
+                  "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
+                  "la_causal_forward_noalloc"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -282,6 +284,26 @@ def la_causal_forward(q, k, v, chunk=0, out=None, want_state=False, S_final=None
     if want_state:
         return out, S_final, z_final
     return out
+
+
+def la_causal_forward_noalloc(q, k, v, chunk=0, out=None, want_state=False):
+    """la_causal_forward (relu + 1) through la_causal_forward_noalloc, whose
+    workspace is the library's static per-GPU array: no workspace is
+    allocated.  out (and the final state, with want_state) are allocated here
+    unless given."""
+    torch = _torch()
+    B, Hq, Hkv, n, d = _qkv(q, k, v)
+    dt = _dtype_code(q)
+    out = torch.empty_like(q) if out is None else out
+    _expect(out, q.shape, q.dtype, "out")
+    S_final = z_final = None
+    if want_state:
+        S_final = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=k.device)
+        z_final = torch.empty((B, Hkv, d), dtype=torch.float32, device=k.device)
+    _call(load().la_causal_forward_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, chunk,
+                                           _dev(out, "out"), _dev(S_final, "S_final"), _dev(z_final, "z_final"),
+                                           _stream(q)), "la_causal_forward_noalloc")
+    return (out, S_final, z_final) if want_state else out
 
 
 def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):

@@ -32,7 +32,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"la_status_str", "la_workspace_bytes", "la_forward", "la_causal_forward",
                           "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
                           "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
-                          "la_workspace_init", "la_workspace_status", "la_workspace_set_wait"}
+                          "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
+                          "la_causal_forward_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -226,3 +227,22 @@ def test_binding_checks_shapes_before_calling():
     q4 = torch.zeros(2, 1, 8, 4)
     with pytest.raises(ValueError, match="m must"):  # a mask neither [n] nor [B, n]
         la.la_prefix_mask_forward(q4, q4, q4, torch.zeros(3, 8, dtype=torch.int64))
+
+
+def test_noalloc_rejections(lib):
+    """la_causal_forward_noalloc checks its arguments as la_causal_forward does,
+    and refuses a size whose workspace exceeds its 64 MiB static array, all
+    before any HIP call."""
+    f = lambda **kw: lib.la_causal_forward_noalloc(*[kw.get(x, dflt) for x, dflt in (
+        ("q", Q), ("k", K), ("v", V), ("B", 1), ("Hq", 2), ("Hkv", 1), ("n", 16), ("d", 16), ("dt", 1),
+        ("chunk", 0), ("out", O), ("Sf", None), ("zf", None))], None)
+    assert f(q=None) == NULL
+    assert f(Hq=3, Hkv=2) == SHAPE
+    assert f(dt=7) == DTYPE
+    assert f(chunk=48) == UNSUP
+    assert f(q=Q + 8) == ALIGN
+    assert f(out=K) == ALIAS
+    # B16 H64 n4096 d128 fp32: 1024 heads of two 66 KB state slots, more than 64 MiB
+    assert la.la_workspace_bytes(la.LA_OP_CAUSAL, 16, 64, 64, 4096, 128, la.LA_F32, 0) > 64 << 20
+    far = [(i + 1) << 40 for i in range(4)]  # fake addresses 1 TiB apart: the 2 GiB tensors do not overlap
+    assert f(q=far[0], k=far[1], v=far[2], out=far[3], B=16, Hq=64, Hkv=64, n=4096, d=128, dt=0) == WS
