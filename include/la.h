@@ -92,10 +92,16 @@ enum { LA_F32 = 0, LA_BF16 = 1 };
  * + 1 (nx_f32_linear_attention.nx, function la_phi), what la_forward,
  * la_causal_forward and la_decode_step use.  LA_PHI_ELU1: phi(x) = ELU(x) +
  * 1 with alpha = 1, i.e. x + 1 for x > 0 and e^x otherwise (LinearTile
- * 1.0.1, "How It Works"), taken by the *_phi entry points below; any other
- * value gives LA_ERR_UNSUPPORTED. */
+ * 1.0.1, "How It Works").  LA_PHI_FEATURES: a feature map of the caller's
+ * choice (LinearTile 1.0.1, "Features": phi replaceable at will), applied by
+ * the caller: q and k (and the decode step's q and k) already hold phi(Q)
+ * and phi(K), which must be positive (every denominator phi(Q_i) . z_i must
+ * be > 0; nothing checks this), and the library computes
+ * out_i = phi(Q_i) S_i / (phi(Q_i) . z_i) with S, z summed over phi(K) as
+ * given.  Taken by the *_phi entry points below; any other value gives
+ * LA_ERR_UNSUPPORTED. */
 typedef int32_t la_phi;
-enum { LA_PHI_RELU1 = 0, LA_PHI_ELU1 = 1 };
+enum { LA_PHI_RELU1 = 0, LA_PHI_ELU1 = 1, LA_PHI_FEATURES = 2 };
 
 /* Operation codes for la_workspace_bytes. */
 enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2, LA_OP_PREFIX_MASK_BATCHED = 3 };
@@ -202,6 +208,20 @@ la_status la_prefix_mask_forward_batched(const void* q, const void* k,
                                          int64_t d, la_dtype dtype,
                                          int32_t chunk, void* out, void* ws,
                                          size_t ws_bytes, void* stream);
+
+/* Sliding-window causal normalised linear attention (LinearTile 1.0.1,
+ * "Features": sliding-window attention, local context): query i sees the
+ * `window` keys j with i - window < j <= i (keys 0..i while i < window):
+ *     out_i = phi(Q_i) (S_i - S_{i-window}) / (phi(Q_i) . (z_i - z_{i-window})),
+ * S_t, z_t the causal sums over keys 0..t (zero for t < 0).  window >= 1
+ * (LA_ERR_SHAPE otherwise); window >= n is the causal form.  phi as for
+ * la_causal_forward_phi.  q, out [B][Hq][n][d]; k, v [B][Hkv][n][d].  Needs
+ * no workspace.  Offered where the kernel's tiles fit in LDS: bf16 with any
+ * d <= 128, fp32 with d <= 64 (LA_ERR_UNSUPPORTED for fp32 with d > 64). */
+la_status la_window_forward(const void* q, const void* k, const void* v,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                            int64_t d, la_dtype dtype, la_phi phi,
+                            int64_t window, void* out, void* stream);
 
 /* One recurrent decode step (trim-transformer 0.1.0, "Key-value caching":
  * use and update the cache in one call).  For every (b, kv head g):

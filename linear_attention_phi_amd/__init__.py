@@ -12,9 +12,13 @@ Functions carry the C names:
   la_prefix_mask_forward(q, k, v, m)         unnormalised Q K^T V, prefix mask m [n]
                                              (or [B, n]: la_prefix_mask_forward_batched)
   la_decode_step(q, k, v, S, z)              one recurrent step (S, z in place)
-  (la_forward, la_causal_forward and la_decode_step take phi="relu1" or
-  phi="elu1"; the latter calls la_forward_phi / la_causal_forward_phi /
-  la_decode_step_phi with LA_PHI_ELU1)
+  la_window_forward(q, k, v, window)         sliding window: keys i - window < j <= i
+  la_causal_forward_noalloc(q, k, v)         la_causal_forward on the static scratch
+  (la_forward, la_causal_forward and la_decode_step take phi="relu1",
+  phi="elu1" or phi="features" -- q and k then hold phi(Q) and phi(K) of a
+  positive map the caller applied; the last two call la_forward_phi /
+  la_causal_forward_phi / la_decode_step_phi with LA_PHI_ELU1 or
+  LA_PHI_FEATURES)
   la_workspace_bytes(op, B, Hq, Hkv, n, d, dtype, chunk)
   la_workspace_init(ws) / la_workspace_status(ws) / la_workspace_set_wait(ws, limit, skew)
   la_status_str(code)
@@ -41,8 +45,8 @@ LIB_PATH = os.path.join(_HERE, "liblaphi.so")
 
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK, LA_OP_PREFIX_MASK_BATCHED = 0, 1, 2, 3
-LA_PHI_RELU1, LA_PHI_ELU1 = 0, 1
-_PHI = {"relu1": LA_PHI_RELU1, "elu1": LA_PHI_ELU1}
+LA_PHI_RELU1, LA_PHI_ELU1, LA_PHI_FEATURES = 0, 1, 2
+_PHI = {"relu1": LA_PHI_RELU1, "elu1": LA_PHI_ELU1, "features": LA_PHI_FEATURES}
 
 
 def _phi(phi):
@@ -90,10 +94,11 @@ def load():
         lib.la_workspace_status.argtypes = [P, SZ, P]
         lib.la_workspace_set_wait.argtypes = [P, SZ, U32, U32, P]
         lib.la_causal_forward_noalloc.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, P, P]
+        lib.la_window_forward.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, I64, P, P]
         for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
                   "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
                   "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
-                  "la_causal_forward_noalloc"):
+                  "la_causal_forward_noalloc", "la_window_forward"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -304,6 +309,20 @@ def la_causal_forward_noalloc(q, k, v, chunk=0, out=None, want_state=False):
                                            _dev(out, "out"), _dev(S_final, "S_final"), _dev(z_final, "z_final"),
                                            _stream(q)), "la_causal_forward_noalloc")
     return (out, S_final, z_final) if want_state else out
+
+
+def la_window_forward(q, k, v, window, out=None, phi="relu1"):
+    """Sliding-window causal normalised linear attention: query i sees keys
+    max(0, i - window + 1) .. i.  phi as la_forward.  No workspace."""
+    phi_code = _phi(phi)
+    torch = _torch()
+    B, Hq, Hkv, n, d = _qkv(q, k, v)
+    dt = _dtype_code(q)
+    out = torch.empty_like(q) if out is None else out
+    _expect(out, q.shape, q.dtype, "out")
+    _call(load().la_window_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, phi_code,
+                                   int(window), _dev(out, "out"), _stream(q)), "la_window_forward")
+    return out
 
 
 def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):

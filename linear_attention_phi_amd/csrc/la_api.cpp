@@ -197,7 +197,7 @@ la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B,
                          int64_t d, la_dtype dtype, la_phi phi, void* out, void* ws, size_t ws_bytes, void* stream) {
   la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
   if (st != LA_OK) return st;
-  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1 && phi != LA_PHI_FEATURES) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const size_t eb = elem_bytes(dtype);
@@ -213,11 +213,11 @@ la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B,
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream, (int)phi};
   attach_ws(a, ws);
-  if (forward_bf16_applies(n, d, (int)dtype)) {  // either feature map
+  if (phi != LA_PHI_FEATURES && forward_bf16_applies(n, d, (int)dtype)) {  // relu + 1 or ELU + 1
     if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_bf16(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
-  if (forward_f32_applies(n, d, (int)dtype)) {  // either feature map
+  if (phi != LA_PHI_FEATURES && forward_f32_applies(n, d, (int)dtype)) {  // relu + 1 or ELU + 1
     if (B * Hq * forward_f32_nseg(n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_f32(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
@@ -234,7 +234,7 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
                                 float* S_final, float* z_final, void* ws, size_t ws_bytes, void* stream) {
   la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
   if (st != LA_OK) return st;
-  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1 && phi != LA_PHI_FEATURES) return LA_ERR_UNSUPPORTED;
   if (!k || !v) return LA_ERR_NULL;
   if ((q == nullptr) != (out == nullptr)) return LA_ERR_NULL;
   if (!q && !S_final && !z_final) return LA_ERR_NULL;
@@ -263,7 +263,7 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream, (int)phi};
   attach_ws(a, ws);
-  if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // either feature map
+  if (q && phi != LA_PHI_FEATURES && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // relu + 1 or ELU + 1
     const Plan fp = make_fused_plan(n);
     if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_causal_fused(a, fp) == 0 ? LA_OK : LA_ERR_LAUNCH;
@@ -318,11 +318,31 @@ la_status la_prefix_mask_forward_batched(const void* q, const void* k, const voi
   return prefix_impl(q, k, v, m, true, B, H, n, d, dtype, chunk, out, ws, ws_bytes, stream);
 }
 
+la_status la_window_forward(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
+                            int64_t n, int64_t d, la_dtype dtype, la_phi phi, int64_t window, void* out,
+                            void* stream) {
+  la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
+  if (st != LA_OK) return st;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1 && phi != LA_PHI_FEATURES) return LA_ERR_UNSUPPORTED;
+  if (window < 1) return LA_ERR_SHAPE;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
+  const size_t eb = elem_bytes(dtype);
+  const int C = window_chunk((int)eb, padded_dim(d));
+  if (C == 0) return LA_ERR_UNSUPPORTED;
+  const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb)) return LA_ERR_ALIAS;
+  if (B * Hkv * ((n + C - 1) / C) >= kMaxGrid) return LA_ERR_SHAPE;
+  if (window > n) window = n;  // the whole causal prefix
+  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, nullptr, stream, (int)phi};
+  return launch_window(a, window) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
 la_status la_decode_step_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,
                              int64_t d, la_dtype dtype, la_phi phi, float* S, float* z, void* out, void* stream) {
   la_status st = check_sizes(B, Hq, Hkv, 1, d, dtype);
   if (st != LA_OK) return st;
-  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1 && phi != LA_PHI_FEATURES) return LA_ERR_UNSUPPORTED;
   if (B * Hkv >= kMaxGrid) return LA_ERR_SHAPE;
   if (!q || !k || !v || !S || !z || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z) || !aligned16(out))

@@ -35,15 +35,20 @@ enum Form { CAUSAL = 0, PREFIX = 1 };
 
 __device__ __forceinline__ float phi_f(float x) { return fmaxf(x, 0.0f) + 1.0f; }
 // The feature maps a call can take: the identity (the prefix form),
-// relu(x) + 1 (nx_f32_linear_attention.nx, function la_phi) and ELU(x) + 1
+// relu(x) + 1 (nx_f32_linear_attention.nx, function la_phi), ELU(x) + 1
 // with alpha = 1 (LinearTile 1.0.1, "How It Works"): x + 1 for x > 0, e^x
-// otherwise.
-enum PhiMode { PM_ID = 0, PM_RELU1 = 1, PM_ELU1 = 2 };
+// otherwise, and caller-applied features (PM_FEAT: Q and K already hold
+// phi(Q) and phi(K) for a positive map of the caller's choice, LinearTile
+// 1.0.1, "Features": a replaceable phi): the normalised forms with the
+// identity on Q and K, z summed over K as given.
+enum PhiMode { PM_ID = 0, PM_RELU1 = 1, PM_ELU1 = 2, PM_FEAT = 3 };
 // e^x as the hardware exp2 of x log2(e): a few fp32 ulp for the arguments
 // here (x <= 0), far inside every tolerance, and several times cheaper than
 // the correctly rounded expf in the tile transforms
 __device__ __forceinline__ float elu1_f(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
-template <int PM> __device__ __forceinline__ float phi_m(float x) { return PM == PM_ELU1 ? elu1_f(x) : phi_f(x); }
+template <int PM> __device__ __forceinline__ float phi_m(float x) {
+  return PM == PM_ELU1 ? elu1_f(x) : PM == PM_FEAT ? x : phi_f(x);
+}
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T cvt(float x);
@@ -114,6 +119,15 @@ __device__ __forceinline__ void st_accT(float* X, int ldx, const f32x16& acc, in
 // What a tile copy holds: not written, the raw value, phi(x) = relu(x) + 1,
 // relu(x), or ELU(x) + 1.
 enum Xf { XF_NONE = 0, XF_ID = 1, XF_PHI = 2, XF_RELU = 3, XF_ELU1 = 4 };
+
+// The tile transforms of a feature map: on Q (phi), and on the keys of the
+// state (relu(K) with the relu + 1 split, phi(K) otherwise)
+template <int PM> constexpr int q_xform() {
+  return PM == PM_RELU1 ? XF_PHI : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
+}
+template <int PM> constexpr int k_xform() {
+  return PM == PM_RELU1 ? XF_RELU : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
+}
 
 template <int X> __device__ __forceinline__ float xform(float x) {
   if (X == XF_PHI) return phi_f(x);

@@ -118,6 +118,12 @@ int64_t forward_f32_nseg(int64_t n);
 size_t forward_f32_ws_bytes(int64_t NKV, int64_t nseg);
 int launch_forward_f32(const Fwd& a);
 
+// Sliding-window causal form (la_window.hip): no workspace.  window_chunk
+// is the chunk its kernel takes for (element bytes, padded dim), 0 if none
+// fits in LDS.
+int window_chunk(int elem_bytes, int DP);
+int launch_window(const Fwd& a, int64_t window);
+
 int launch_decode(const void* q, const void* k, const void* v, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t d, int dtype, int phi,
                   float* S, float* z, void* out, void* stream);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
   __shared__ __attribute__((aligned(16))) T sVT[DP * (C + PAD)];
   __shared__ float svs[DP];
   using SB = StateBlocks<DP>;
-  constexpr int KX = PM == PM_RELU1 ? XF_RELU : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
+  constexpr int KX = k_xform<PM>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const T* kb = k + bh * n * d;
@@ -585,8 +585,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
   // tiles of phi(Q) and phi(K) (scores), of the keys the state update takes
   // (relu(K) with the relu + 1 split, below), and whether S and z carry that
   // split (S = accS + 1 (x) sum of V, z counts the keys)
-  constexpr int QX = PM == PM_RELU1 ? XF_PHI : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
-  constexpr int KTX = PM == PM_RELU1 ? XF_RELU : PM == PM_ELU1 ? XF_ELU1 : XF_ID;
+  constexpr int QX = q_xform<PM>();
+  constexpr int KTX = k_xform<PM>();
   constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
   __shared__ __attribute__((aligned(16))) T sK[C * LQ];
@@ -1117,11 +1117,11 @@ __global__ __launch_bounds__(NT) void k_out_nc(const T* __restrict__ q, T* __res
     for (int r = 0; r < R; ++r) {
       __syncthreads();  // sQ free (and sST / sz visible on the first pass)
       if (vec) {
-        tile_store<T, DP, C, PM == PM_ELU1 ? XF_ELU1 : XF_PHI, XF_NONE>(rQ, nv, sQ, nullptr, tid);
+        tile_store<T, DP, C, q_xform<PM>(), XF_NONE>(rQ, nv, sQ, nullptr, tid);
         if (r + 1 < R) fetch(c, r + 1);
         else if (c + 1 < c1) fetch(c + 1, 0);
       } else {
-        load_tile<T, DP, C, PM == PM_ELU1 ? XF_ELU1 : XF_PHI, XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ,
+        load_tile<T, DP, C, q_xform<PM>(), XF_NONE>(q + (bh * R + r) * n * d, t0, nullptr, nv, d, vec, sQ,
                                                                   nullptr, tid);
       }
       __syncthreads();
@@ -1650,6 +1650,18 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   T* out = reinterpret_cast<T*>(a.out);
   int* boff = nullptr; int* perm = nullptr;
   bool state_done = false;
+  if (form == CAUSAL && a.phi == 2) {
+    // caller-applied features: the general state, scan and output kernels
+    k_state<T, DP, C, PM_FEAT><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
+                                                                             p.G, p.nseg, states);
+    const int64_t E = slot_elems(DP);
+    k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d,
+                                                                            a.S_final, a.z_final, 1);
+    if (!(q && out)) return (int)hipGetLastError();
+    k_out<T, DP, C, CAUSAL, PM_FEAT><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
+        q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
+    return (int)hipGetLastError();
+  }
   if (form == CAUSAL && a.phi == 1) {
     // ELU + 1: the bf16 d = 128 chunk-32 (GQA) state and output kernels, the
     // fp32 d = 64 state kernel, else the general ones
@@ -1792,8 +1804,11 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   const T* k = reinterpret_cast<const T*>(a.k);
   const T* v = reinterpret_cast<const T*>(a.v);
   T* out = reinterpret_cast<T*>(a.out);
-  const bool elu = a.phi == 1;
-  if (elu)
+  const bool elu = a.phi == 1, feat = a.phi == 2;
+  if (feat)
+    k_state<T, DP, C, PM_FEAT><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
+                                                                             p.nseg, states);
+  else if (elu)
     k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
                                                                              p.nseg, states);
   else
@@ -1808,7 +1823,10 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   int64_t Gq = (nbh * p.nchunks + target - 1) / target;
   if (Gq < 1) Gq = 1;
   const int64_t nqseg = (p.nchunks + Gq - 1) / Gq;
-  if (elu)
+  if (feat)
+    k_out_nc<T, DP, C, PM_FEAT><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks,
+                                                                             Gq, nqseg, p.nseg, states);
+  else if (elu)
     k_out_nc<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * nqseg)), NT, 0, st>>>(q, out, a.n, (int)a.d, R, vec, p.nchunks,
                                                                              Gq, nqseg, p.nseg, states);
   else
@@ -1921,6 +1939,7 @@ int launch_prefix(const Fwd& a, const Plan& p) { return dispatch(a, p, 2); }
 
 int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                   int dtype, int phi, float* S, float* z, void* out, void* stream) {
+  if (phi == 2) return launch_decode_pm<PM_FEAT>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream);
   return phi == 1 ? launch_decode_pm<PM_ELU1>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream)
                   : launch_decode_pm<PM_RELU1>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream);
 }

@@ -55,9 +55,12 @@ def _load():
         lib.lao_forward.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P]
         lib.lao_causal.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P, P, P]
         lib.lao_prefix_mask.argtypes = [P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
+        lib.lao_window.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, I64, P, I64, P]
+        lib.lao_window.restype = None
         lib.lao_decode_step.argtypes = [P, P, P, I, I, I64, I64, I64, I64, P, P, P]
         for f in ("lao_forward", "lao_causal", "lao_prefix_mask", "lao_decode_step"):
             getattr(lib, f).restype = None
+
         _lib = lib
     return _lib
 
@@ -67,12 +70,14 @@ def num_threads() -> int:
 
 
 def _inp(x):
-    """Return (contiguous array, dtype code) for an fp32 or bf16-bits input."""
+    """Return (contiguous array, dtype code) for an fp32, bf16-bits or fp64 input."""
     if x is None:
         return None, F32
     x = np.ascontiguousarray(x)
     if x.dtype == np.float32:
         return x, F32
+    if x.dtype == np.float64:
+        return x, 2
     if x.dtype == np.uint16:
         return x, BF16
     raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {x.dtype}")
@@ -104,18 +109,41 @@ def _same_dtype(*codes):
     return codes[0]
 
 
-_PHI = {"relu1": 0, "elu1": 1}
+_PHI = {"relu1": 0, "elu1": 1, "features": 2}
+F64 = 2
 
 
 def _phi(phi):
+    """Feature-map code: "relu1", "elu1" or "features" (q and k hold phi(Q)
+    and phi(K) already)."""
     if phi not in _PHI:
-        raise ValueError(f"phi must be one of {sorted(_PHI)}")
+        raise ValueError(f"phi must be one of {sorted(_PHI)} or a function")
     return _PHI[phi]
+
+
+def _mapped(x, phi):
+    """A test's own feature map (a numpy function, applied elementwise)
+    evaluated in fp64 on the stored values, as fp64 "features"."""
+    if x is None:
+        return None
+    xf = (x.astype(np.uint32) << 16).view(np.float32) if x.dtype == np.uint16 else x
+    return np.ascontiguousarray(phi(np.asarray(xf, dtype=np.float64)), dtype=np.float64)
+
+
+def _with_map(q, k, v, phi):
+    """(q, k, v, phi) with a callable phi applied here in fp64 to q and k (then
+    "features"; v widened to fp64 too, so that the three share a dtype)."""
+    if callable(phi):
+        return _mapped(q, phi), _mapped(k, phi), _mapped(v, lambda x: x), "features"
+    return q, k, v, phi
 
 
 def forward(q, k, v, rows=None, phi="relu1"):
     """Non-causal normalised linear attention; q [B,Hq,n,d], k/v [B,Hkv,n,d].
-    phi: "relu1" (relu(x) + 1) or "elu1" (ELU(x) + 1)."""
+    phi: "relu1" (relu(x) + 1), "elu1" (ELU(x) + 1), "features" (q and k hold
+    phi(Q), phi(K) already) or a numpy function applied elementwise in fp64
+    (a map of the caller's choice)."""
+    q, k, v, phi = _with_map(q, k, v, phi)
     q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
     dt = _same_dtype(cq, ck, cv)
     B, Hq, n, d = q.shape
@@ -135,6 +163,7 @@ def causal(q, k, v, rows=None, want_state=False, Hq=None, phi="relu1"):
     it defaults to Hkv).  With want_state the final (S [B,Hkv,d,d],
     z [B,Hkv,d]) are returned as well.
     """
+    q, k, v, phi = _with_map(q, k, v, phi)
     k, ck = _inp(k); v, cv = _inp(v)
     B, Hkv, n, d = k.shape
     if q is not None:
@@ -153,6 +182,24 @@ def causal(q, k, v, rows=None, want_state=False, Hq=None, phi="relu1"):
                        _ptr(r), nr, _ptr(out), _ptr(S), _ptr(z))
     if want_state:
         return out, S, z
+    return out
+
+
+def window(q, k, v, w, rows=None, phi="relu1"):
+    """Sliding-window normalised linear attention: query i sees keys
+    max(0, i - w + 1) .. i.  q [B,Hq,n,d], k/v [B,Hkv,n,d]; phi as forward."""
+    q, k, v, phi = _with_map(q, k, v, phi)
+    q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
+    dt = _same_dtype(cq, ck, cv)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    _check_gqa(q.shape, k.shape, v.shape)
+    if int(w) < 1:
+        raise ValueError("the window must hold at least one key")
+    r, nr = _rows(rows, n)
+    out = np.empty((B, Hq, nr, d), dtype=np.float64)
+    code = _phi(phi)
+    _load().lao_window(_ptr(q), _ptr(k), _ptr(v), dt, code, B, Hq, Hkv, n, d, int(w), _ptr(r), nr, _ptr(out))
     return out
 
 
@@ -177,6 +224,7 @@ def prefix_mask(q, k, v, m, rows=None):
 
 def decode_step(q, k, v, S, z, phi="relu1"):
     """One decode step: S [B,Hkv,d,d] and z [B,Hkv,d] (float64) update in place."""
+    q, k, v, phi = _with_map(q, k, v, phi)
     q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v)
     dt = _same_dtype(cq, ck, cv)
     B, Hq, d = q.shape

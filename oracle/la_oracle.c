@@ -14,12 +14,17 @@
  *  - "LinearTile 1.0.1" (files.pythonhosted.org), section "How It Works":
  *    the same O = phi(Q) (phi(K)^T V) with phi(x) = ELU(x) + 1, the second
  *    feature map offered here (ELU with alpha = 1, the page naming no other:
- *    phi(x) = x + 1 for x > 0, exp(x) otherwise).
+ *    phi(x) = x + 1 for x > 0, exp(x) otherwise); section "Features": phi
+ *    may be replaced at will -- any positive map, applied to q and k
+ *    beforehand (LAO_PHI_FEATURES; the Python wrapper evaluates a test's map
+ *    in fp64 and passes the results as fp64 inputs).
  *  - "trim-transformer 0.1.0" (pypi.org), section "Masking": query i attends
  *    to keys 0..m_i; a causal mask is m = arange(n).  Its kernel is
  *    Attn(Q,K,V) = Q K^T V with no feature map and no normaliser.
  *  - same page, section "Key-value caching": generation reuses and updates a
  *    cache token by token, linear in the number of generated tokens.
+ *  - "LinearTile 1.0.1", section "Features": sliding-window attention (local
+ *    context): query i sees only the last `window` keys, i - window < j <= i.
  *
  * Readings where the pages leave a step open:
  *  - no epsilon in the normaliser (relu + 1 >= 1 keeps the denominator >= 1;
@@ -51,6 +56,7 @@ int lao_num_threads(void) {
 /* Read element idx of an input array, widening fp32 or bf16 bits to fp64. */
 static double rd(const void* p, int dtype, int64_t idx) {
   if (dtype == LAO_F32) return (double)((const float*)p)[idx];
+  if (dtype == LAO_F64) return ((const double*)p)[idx];
   uint32_t bits = ((uint32_t)((const uint16_t*)p)[idx]) << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -58,9 +64,11 @@ static double rd(const void* p, int dtype, int64_t idx) {
 }
 
 /* phi(x) = relu(x) + 1 (-0 and every negative value map to 1), or
- * phi(x) = ELU(x) + 1 = x + 1 for x > 0, exp(x) otherwise. */
+ * phi(x) = ELU(x) + 1 = x + 1 for x > 0, exp(x) otherwise, or the identity
+ * (features mapped beforehand). */
 static double phi(double x, int kind) {
   if (kind == LAO_PHI_ELU1) return x > 0.0 ? x + 1.0 : exp(x);
+  if (kind == LAO_PHI_FEATURES) return x;
   return (x > 0.0 ? x : 0.0) + 1.0;
 }
 
@@ -98,17 +106,18 @@ void lao_forward(const void* q, const void* k, const void* v, int dtype,
       double* S = (double*)malloc((size_t)(d * d) * sizeof(double));
       double* z = (double*)malloc((size_t)d * sizeof(double));
       double* pq = (double*)malloc((size_t)d * sizeof(double));
+      double* pk = (double*)malloc((size_t)(n * d) * sizeof(double));
       const int64_t o = off4(b, g, 0, Hkv, n, d); /* key/value row 0 */
+      for (int64_t e = 0; e < n * d; ++e) pk[e] = phi(rd(k, dtype, o + e), phik);
       /* z[a] = sum over all n keys of phi(K_j[a]);
        * S[a][c] = sum over all n keys of phi(K_j[a]) * V_j[c]. */
       for (int64_t a = 0; a < d; ++a) {
         double za = 0.0;
-        for (int64_t j = 0; j < n; ++j) za += phi(rd(k, dtype, o + j * d + a), phik);
+        for (int64_t j = 0; j < n; ++j) za += pk[j * d + a];
         z[a] = za;
         for (int64_t c = 0; c < d; ++c) {
           double sac = 0.0;
-          for (int64_t j = 0; j < n; ++j)
-            sac += phi(rd(k, dtype, o + j * d + a), phik) * rd(v, dtype, o + j * d + c);
+          for (int64_t j = 0; j < n; ++j) sac += pk[j * d + a] * rd(v, dtype, o + j * d + c);
           S[a * d + c] = sac;
         }
       }
@@ -120,6 +129,7 @@ void lao_forward(const void* q, const void* k, const void* v, int dtype,
       free(S);
       free(z);
       free(pq);
+      free(pk);
     }
   }
 }
@@ -158,6 +168,43 @@ void lao_causal(const void* q, const void* k, const void* v, int dtype,
       if (z_final) memcpy(z_final + (b * Hkv + g) * d, z, (size_t)d * sizeof(double));
       free(S);
       free(z);
+      free(pk);
+    }
+  }
+}
+
+void lao_window(const void* q, const void* k, const void* v, int dtype,
+                int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                int64_t d, int64_t window, const int64_t* rows, int64_t nrows,
+                double* out) {
+  const int64_t R = Hq / Hkv;
+  const int64_t nr = rows ? nrows : n;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t g = h / R;
+      double* pq = (double*)malloc((size_t)d * sizeof(double));
+      double* pk = (double*)malloc((size_t)(n * d) * sizeof(double));
+      for (int64_t e = 0; e < n * d; ++e) pk[e] = phi(rd(k, dtype, off4(b, g, 0, Hkv, n, d) + e), phik);
+      for (int64_t r = 0; r < nr; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        const int64_t lo = i - window + 1 > 0 ? i - window + 1 : 0;
+        const int64_t oq = off4(b, h, i, Hq, n, d);
+        for (int64_t a = 0; a < d; ++a) pq[a] = phi(rd(q, dtype, oq + a), phik);
+        double* dst = out + off4(b, h, r, Hq, nr, d);
+        for (int64_t c = 0; c < d; ++c) dst[c] = 0.0;
+        double den = 0.0;
+        /* the weight of key j is phi(Q_i) . phi(K_j); keys lo..i only */
+        for (int64_t j = lo; j <= i; ++j) {
+          const int64_t ok = off4(b, g, j, Hkv, n, d);
+          double wij = 0.0;
+          for (int64_t a = 0; a < d; ++a) wij += pq[a] * pk[j * d + a];
+          den += wij;
+          for (int64_t c = 0; c < d; ++c) dst[c] += wij * rd(v, dtype, ok + c);
+        }
+        for (int64_t c = 0; c < d; ++c) dst[c] /= den;
+      }
+      free(pq);
       free(pk);
     }
   }

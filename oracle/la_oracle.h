@@ -10,7 +10,9 @@
  *   phi(x) = max(x, 0) + 1                       (nx_f32_linear_attention.nx,
  *                                                 function la_phi), or
  *   phi(x) = ELU(x) + 1 (alpha = 1)              (LinearTile 1.0.1,
- *                                                 "How It Works")
+ *                                                 "How It Works"), or
+ *   any positive phi the caller gives             (LinearTile 1.0.1,
+ *                                                 "Features": phi replaceable)
  *   S = sum_j phi(K_j) (x) V_j,  z = sum_j phi(K_j)
  *   out_i = (phi(Q_i) S) / (phi(Q_i) . z)          (same page, header comment)
  * in the non-causal form (all keys), the causal form (keys 0..i), the
@@ -20,7 +22,8 @@
  *
  * Layouts: q [B][Hq][n][d], k and v [B][Hkv][n][d], row-major, d fastest.
  * Query head h reads key/value head h / (Hq / Hkv).  Inputs are fp32
- * (dtype LAO_F32) or raw bf16 bit patterns (LAO_BF16), widened exactly.
+ * (dtype LAO_F32), raw bf16 bit patterns (LAO_BF16), widened exactly, or
+ * fp64 (LAO_F64).
  *
  * Row selection: `rows` (ascending, each in [0, n)) picks which query rows
  * are produced; out is then [B][Hq][nrows][d].  rows == NULL means all rows
@@ -34,8 +37,12 @@
 extern "C" {
 #endif
 
-enum { LAO_F32 = 0, LAO_BF16 = 1 };
-enum { LAO_PHI_RELU1 = 0, LAO_PHI_ELU1 = 1 };  /* phik: the feature map */
+enum { LAO_F32 = 0, LAO_BF16 = 1, LAO_F64 = 2 };
+/* phik: the feature map.  LAO_PHI_FEATURES: the identity on q and k (they
+ * hold a positive map applied beforehand -- by a caller, or by the Python
+ * wrapper, which evaluates a test's own map in fp64 and passes the results
+ * as LAO_F64 inputs). */
+enum { LAO_PHI_RELU1 = 0, LAO_PHI_ELU1 = 1, LAO_PHI_FEATURES = 2 };
 
 /* Number of OpenMP threads the oracle uses. */
 int lao_num_threads(void);
@@ -52,6 +59,15 @@ void lao_causal(const void* q, const void* k, const void* v, int dtype,
                 int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
                 int64_t d, const int64_t* rows, int64_t nrows, double* out,
                 double* S_final, double* z_final);
+
+/* Sliding-window normalised form: query i sees keys max(0, i - window + 1)
+ * .. i (window >= 1).  Written as the pairwise weights themselves:
+ * out_i = sum_j (phi(Q_i) . phi(K_j)) V_j / sum_j phi(Q_i) . phi(K_j) over
+ * those keys (no state). */
+void lao_window(const void* q, const void* k, const void* v, int dtype,
+                int phik, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                int64_t d, int64_t window, const int64_t* rows, int64_t nrows,
+                double* out);
 
 /* Unnormalised prefix-mask form, identity feature map: query i of batch b
  * sees keys 0..m[b * m_bstride + i], each in [0, n); m_bstride = 0 shares one

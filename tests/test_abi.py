@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
                           "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
                           "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
-                          "la_causal_forward_noalloc"}
+                          "la_causal_forward_noalloc", "la_window_forward"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -118,11 +118,11 @@ def test_feature_map_rejections(lib):
     """The *_phi entry points reject an unknown feature map, and run every
     other check of their plain counterparts (each call below fails a check,
     so nothing is launched)."""
-    for phi in (2, -1, 7):
+    for phi in (3, -1, 7):
         assert lib.la_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 0, phi, O, WSP, BIG, None) == UNSUP
         assert lib.la_causal_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 1, phi, 0, O, None, None, WSP, BIG, None) == UNSUP
         assert lib.la_decode_step_phi(Q, K, V, 1, 2, 1, 16, 0, phi, S, Z, O, None) == UNSUP
-    for phi in (la.LA_PHI_RELU1, la.LA_PHI_ELU1):
+    for phi in (la.LA_PHI_RELU1, la.LA_PHI_ELU1, la.LA_PHI_FEATURES):
         assert lib.la_forward_phi(None, K, V, 1, 2, 1, 16, 16, 0, phi, O, WSP, BIG, None) == NULL
         assert lib.la_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 0, phi, K, WSP, BIG, None) == ALIAS
         assert lib.la_forward_phi(Q, K, V, 1, 2, 1, 16, 16, 0, phi, O, WSP, 16, None) == WS
@@ -246,3 +246,20 @@ def test_noalloc_rejections(lib):
     assert la.la_workspace_bytes(la.LA_OP_CAUSAL, 16, 64, 64, 4096, 128, la.LA_F32, 0) > 64 << 20
     far = [(i + 1) << 40 for i in range(4)]  # fake addresses 1 TiB apart: the 2 GiB tensors do not overlap
     assert f(q=far[0], k=far[1], v=far[2], out=far[3], B=16, Hq=64, Hkv=64, n=4096, d=128, dt=0) == WS
+
+
+def test_window_rejections(lib):
+    """la_window_forward: every check on the host, nothing launched."""
+    f = lambda **kw: lib.la_window_forward(*[kw.get(x, dflt) for x, dflt in (
+        ("q", Q), ("k", K), ("v", V), ("B", 1), ("Hq", 2), ("Hkv", 1), ("n", 16), ("d", 16), ("dt", 1),
+        ("phi", 0), ("w", 4), ("out", O))], None)
+    assert f(q=None) == NULL
+    assert f(out=None) == NULL
+    assert f(w=0) == SHAPE
+    assert f(w=-3) == SHAPE
+    assert f(Hq=3, Hkv=2) == SHAPE
+    assert f(dt=9) == DTYPE
+    assert f(phi=5) == UNSUP
+    assert f(dt=0, d=128) == UNSUP        # fp32 with d > 64: the tiles do not fit in LDS
+    assert f(k=K + 4) == ALIGN
+    assert f(out=V) == ALIAS

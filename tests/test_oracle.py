@@ -408,3 +408,171 @@ def test_prefix_mask_per_batch_equal_rows_is_shared():
     q, k, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=41)
     m = li.mask(n, "random", rng=rng)
     np.testing.assert_array_equal(oracle.prefix_mask(q, k, v, np.tile(m, (B, 1))), oracle.prefix_mask(q, k, v, m))
+
+
+# ---------------------------------------------------------------------------
+# A feature map of the caller's choice (LinearTile 1.0.1, "Features": phi
+# replaceable at will): given to the oracle as an fp64 function, or applied
+# to q and k beforehand ("features").  Pinned by what holds for every
+# positive map: equal keys give the mean of V, d = 1 does not depend on Q,
+# the pairwise brute force with that map's weights.
+# ---------------------------------------------------------------------------
+def _softplus(x):
+    return np.log1p(np.exp(x))
+
+
+def _sq1(x):  # 1 + x^2: exact in fp32 on a 2^-4 grid of small values
+    return 1.0 + x * x
+
+
+def brute_normalised_fn(q, k, v, causal, fn):
+    q, k, v = (li.to_f32(x).astype(np.float64) for x in (q, k, v))
+    B, Hq, n, d = q.shape
+    R = Hq // k.shape[1]
+    out = np.empty_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // R
+            w = fn(q[b, h]) @ fn(k[b, g]).T
+            if causal:
+                w = np.tril(w)
+            out[b, h] = (w @ v[b, g]) / w.sum(axis=1, keepdims=True)
+    return out
+
+
+@pytest.mark.parametrize("fn", [_softplus, np.exp, _sq1], ids=["softplus", "exp", "sq1"])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 17, 1), (2, 4, 2, 23, 3), (1, 2, 2, 19, 6)])
+def test_callback_feature_map_matches_brute_force(fn, shape):
+    B, Hq, Hkv, n, d = shape
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=5, scaled=True)
+    assert rel_rows(oracle.forward(q, k, v, phi=fn), brute_normalised_fn(q, k, v, False, fn)) < 1e-12
+    assert rel_rows(oracle.causal(q, k, v, phi=fn), brute_normalised_fn(q, k, v, True, fn)) < 1e-12
+
+
+def test_callback_relu1_equals_the_built_in_map():
+    q, k, v, _ = li.qkv(2, 4, 2, 40, 8, li.F32, seed=6)
+    assert np.array_equal(oracle.forward(q, k, v, phi=_relu1), oracle.forward(q, k, v))
+    assert np.array_equal(oracle.causal(q, k, v, phi=_relu1), oracle.causal(q, k, v))
+
+
+@pytest.mark.parametrize("fn", [_softplus, np.exp], ids=["softplus", "exp"])
+def test_callback_equal_keys_give_mean_of_v(fn):
+    """Every key row equal: every key has the same weight phi(Q_i) . phi(k)
+    whatever the positive map, so the outputs are the (running) mean of V."""
+    B, H, n, d = 1, 2, 30, 4
+    q, _, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=7)
+    k = np.broadcast_to(rng.standard_normal(d, dtype=np.float32), (B, H, n, d)).copy()
+    vf = v.astype(np.float64)
+    nc = oracle.forward(q, k, v, phi=fn)
+    assert np.allclose(nc, np.broadcast_to(vf.mean(axis=2, keepdims=True), nc.shape), rtol=1e-12, atol=1e-12)
+    run = np.cumsum(vf, axis=2) / np.arange(1, n + 1)[None, None, :, None]
+    assert np.allclose(oracle.causal(q, k, v, phi=fn), run, rtol=1e-12, atol=1e-12)
+
+
+def test_callback_d1_output_does_not_depend_on_q():
+    """d = 1: phi(q_i) cancels between numerator and denominator."""
+    q1, k, v, _ = li.qkv(1, 1, 1, 25, 1, li.F32, seed=8)
+    q2 = (q1 * 3.0 + 1.0).astype(np.float32)
+    a = oracle.causal(q1, k, v, phi=_softplus)
+    b = oracle.causal(q2, k, v, phi=_softplus)
+    assert np.allclose(a, b, rtol=1e-13, atol=0)
+    pk = _softplus(k[0, 0, :, 0].astype(np.float64))
+    want = np.cumsum(pk * v[0, 0, :, 0]) / np.cumsum(pk)
+    assert np.allclose(a[0, 0, :, 0], want, rtol=1e-13)
+
+
+def test_features_mode_equals_the_map_applied_by_the_oracle():
+    """q and k mapped beforehand ("features") give what the oracle gives
+    applying the same map itself (1 + x^2 on a 2^-4 grid is exact in fp32),
+    in every normalised form and the decode step."""
+    B, Hq, Hkv, n, d = 2, 4, 2, 21, 5
+    rng = np.random.default_rng(9)
+    grid = lambda shape: (rng.integers(-24, 25, size=shape) / 16.0).astype(np.float32)
+    q, k, v = grid((B, Hq, n, d)), grid((B, Hkv, n, d)), grid((B, Hkv, n, d))
+    fq, fk = _sq1(q).astype(np.float32), _sq1(k).astype(np.float32)
+    assert np.array_equal(oracle.forward(fq, fk, v, phi="features"), oracle.forward(q, k, v, phi=_sq1))
+    o1, S1, z1 = oracle.causal(fq, fk, v, phi="features", want_state=True)
+    o2, S2, z2 = oracle.causal(q, k, v, phi=_sq1, want_state=True)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2) and np.array_equal(z1, z2)
+    qs, ks, vs = grid((B, Hq, d)), grid((B, Hkv, d)), grid((B, Hkv, d))
+    S1c, z1c = S1.copy(), z1.copy()
+    a = oracle.decode_step(_sq1(qs).astype(np.float32), _sq1(ks).astype(np.float32), vs, S1, z1, phi="features")
+    b = oracle.decode_step(qs, ks, vs, S1c, z1c, phi=_sq1)
+    assert np.array_equal(a, b) and np.array_equal(S1, S1c)
+
+
+def test_callback_decode_steps_continue_the_causal_pass():
+    B, Hq, Hkv, n, d, T = 2, 4, 2, 30, 6, 5
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.F32, seed=10, scaled=True)
+    full = oracle.causal(q, k, v, phi=_softplus)
+    _, S, z = oracle.causal(q[:, :, : n - T], k[:, :, : n - T], v[:, :, : n - T], want_state=True, phi=_softplus)
+    for t in range(n - T, n):
+        o = oracle.decode_step(q[:, :, t].copy(), k[:, :, t].copy(), v[:, :, t].copy(), S, z, phi=_softplus)
+        assert rel_rows(o, full[:, :, t]) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Sliding window (LinearTile 1.0.1, "Features"): query i sees keys
+# i - w < j <= i.  Pinned by its special cases: w = 1 returns V_i, w >= i + 1
+# is the causal form (the oracle's state recurrence, a different
+# computation), equal keys give the window mean of V, d = 1 does not depend
+# on Q, and keys outside a query's window do not move its output.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+def test_window_of_one_returns_v(dtype):
+    q, k, v, _ = li.qkv(2, 4, 2, 37, 5, dtype, seed=20)
+    got = oracle.window(q, k, v, 1)
+    want = np.repeat(li.to_f32(v).astype(np.float64), 2, axis=1)
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+def test_window_covering_the_prefix_is_the_causal_form(phi):
+    q, k, v, _ = li.qkv(2, 4, 2, 41, 6, li.F32, seed=21, scaled=True)
+    for w in (41, 50, 1000):
+        assert rel_rows(oracle.window(q, k, v, w, phi=phi), oracle.causal(q, k, v, phi=phi)) < 1e-12
+    # rows i < w see the whole prefix
+    got = oracle.window(q, k, v, 10, phi=phi)
+    assert rel_rows(got[:, :, :10], oracle.causal(q, k, v, phi=phi)[:, :, :10]) < 1e-12
+
+
+def test_window_equal_keys_give_the_window_mean():
+    B, H, n, d, w = 1, 2, 50, 4, 7
+    q, _, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=22)
+    k = np.broadcast_to(rng.standard_normal(d, dtype=np.float32), (B, H, n, d)).copy()
+    vf = v.astype(np.float64)
+    want = np.stack([vf[:, :, max(0, i - w + 1): i + 1].mean(axis=2) for i in range(n)], axis=2)
+    assert np.allclose(oracle.window(q, k, v, w), want, rtol=1e-12, atol=1e-12)
+
+
+def test_window_d1_output_does_not_depend_on_q():
+    q1, k, v, _ = li.qkv(1, 1, 1, 30, 1, li.F32, seed=23)
+    q2 = (q1 * -2.0 + 0.5).astype(np.float32)
+    w = 6
+    a, b = oracle.window(q1, k, v, w), oracle.window(q2, k, v, w)
+    assert np.allclose(a, b, rtol=1e-13, atol=0)
+    pk = _relu1(k[0, 0, :, 0].astype(np.float64))
+    vv = v[0, 0, :, 0].astype(np.float64)
+    want = [(pk[max(0, i - w + 1): i + 1] * vv[max(0, i - w + 1): i + 1]).sum() / pk[max(0, i - w + 1): i + 1].sum()
+            for i in range(30)]
+    assert np.allclose(a[0, 0, :, 0], want, rtol=1e-13)
+
+
+def test_window_ignores_keys_outside_it():
+    """Changing key/value i - w (just outside query i's window) leaves out_i
+    unchanged and moves out_{i-1} (whose window holds it)."""
+    B, H, n, d, w = 1, 1, 40, 4, 9
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.F32, seed=24)
+    i = 25
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 0, i - w] += 1.0
+    v2[0, 0, i - w] -= 3.0
+    a, b = oracle.window(q, k, v, w), oracle.window(q, k2, v2, w)
+    assert np.array_equal(a[0, 0, i], b[0, 0, i])
+    assert not np.allclose(a[0, 0, i - 1], b[0, 0, i - 1])
+
+
+def test_window_gqa_equals_repeated_kv_heads():
+    q, k, v, _ = li.qkv(2, 6, 2, 23, 3, li.F32, seed=25)
+    rep = lambda x: np.repeat(x, 3, axis=1)
+    assert np.array_equal(oracle.window(q, k, v, 5), oracle.window(q, rep(k), rep(v), 5))
