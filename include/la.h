@@ -104,7 +104,8 @@ typedef int32_t la_phi;
 enum { LA_PHI_RELU1 = 0, LA_PHI_ELU1 = 1, LA_PHI_FEATURES = 2 };
 
 /* Operation codes for la_workspace_bytes. */
-enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2, LA_OP_PREFIX_MASK_BATCHED = 3 };
+enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2, LA_OP_PREFIX_MASK_BATCHED = 3,
+       LA_OP_SEQS = 4 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* la_status_str(la_status s);
@@ -222,6 +223,47 @@ la_status la_window_forward(const void* q, const void* k, const void* v,
                             int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
                             int64_t d, la_dtype dtype, la_phi phi,
                             int64_t window, void* out, void* stream);
+
+/* The causal (window = 0) or sliding-window (window >= 1) normalised form
+ * over a table of sequences of any layout (LinearTile 1.0.1, "Features":
+ * variable sequence length with no padding waste; the [batch, seq, dim]
+ * inputs of trim-transformer 0.1.0's quickstart).  Sequence s, key/value head
+ * g, query head h, token t of that sequence:
+ *   K, V row at k + s*kv_strides[0] + (start(s) + t)*kv_strides[2] + g*kv_strides[1]
+ *   Q, out row at q + s*q_strides[0] + (start(s) + t)*q_strides[2] + h*q_strides[1]
+ * (strides in elements; the d features of a row are contiguous), where
+ *   - cu_seqlens == NULL: nseq sequences of max_len tokens each, start(s) = 0
+ *     (e.g. [B, n, H, d] with strides {n*H*d, d, H*d}; [B, H, n, d] with
+ *     {H*n*d, n*d, d});
+ *   - cu_seqlens != NULL: a DEVICE int64 array [nseq + 1], cu[0] = 0,
+ *     nondecreasing, cu[nseq] <= total: sequence s is the packed token rows
+ *     cu[s] .. cu[s+1] - 1 (start(s) = cu[s]) of buffers holding `total` rows
+ *     (e.g. [total, H, d] with strides {0, d, H*d}); strides[0] must be 0 and
+ *     every length at most max_len.  An inconsistent table is checked on
+ *     the device: a sequence s with cu[s - 1] > cu[s] (s > 0), cu[s] > cu[s+1],
+ *     cu[0] < 0, cu[s+1] > total or a length above max_len is left untouched
+ *     (its out rows keep their contents) and LA_ERR_RANGE is recorded for
+ *     la_workspace_status.
+ * Query head h reads key/value head h / (Hq / Hkv).  phi as
+ * la_causal_forward_phi.  window = 0: the causal form; S_final
+ * [nseq][Hkv][d][d] and z_final [nseq][Hkv][d] (either may be NULL) receive
+ * each sequence's final state (q = out = NULL: state only).  window >= 1:
+ * query t sees keys t - window < j <= t of its sequence (S_final, z_final
+ * must be NULL).  ws: la_workspace_bytes(LA_OP_SEQS, nseq, Hq, Hkv, max_len,
+ * d, dtype, 0) bytes (covers both forms).  Offered where the kernels' tiles
+ * fit in LDS: the causal form for every d <= 128, the window form for bf16
+ * and for fp32 with d <= 64 (LA_ERR_UNSUPPORTED otherwise).  Errors as
+ * elsewhere; LA_ERR_SHAPE for negative strides, heads of a row that overlap,
+ * or a nonzero strides[0] with cu_seqlens. */
+la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
+                                    const int64_t* cu_seqlens, int64_t nseq,
+                                    int64_t max_len, int64_t total, int64_t Hq,
+                                    int64_t Hkv, int64_t d,
+                                    const int64_t* q_strides,
+                                    const int64_t* kv_strides, la_dtype dtype,
+                                    la_phi phi, int64_t window, void* out,
+                                    float* S_final, float* z_final, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* One recurrent decode step (trim-transformer 0.1.0, "Key-value caching":
  * use and update the cache in one call).  For every (b, kv head g):

@@ -44,7 +44,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblaphi.so")
 
 LA_F32, LA_BF16 = 0, 1
-LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK, LA_OP_PREFIX_MASK_BATCHED = 0, 1, 2, 3
+LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK, LA_OP_PREFIX_MASK_BATCHED, LA_OP_SEQS = 0, 1, 2, 3, 4
 LA_PHI_RELU1, LA_PHI_ELU1, LA_PHI_FEATURES = 0, 1, 2
 _PHI = {"relu1": LA_PHI_RELU1, "elu1": LA_PHI_ELU1, "features": LA_PHI_FEATURES}
 
@@ -95,10 +95,12 @@ def load():
         lib.la_workspace_set_wait.argtypes = [P, SZ, U32, U32, P]
         lib.la_causal_forward_noalloc.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, P, P]
         lib.la_window_forward.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, I64, P, P]
+        lib.la_causal_forward_strided.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, I32, I32, I64,
+                                                  P, P, P, P, SZ, P]
         for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
                   "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
                   "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
-                  "la_causal_forward_noalloc", "la_window_forward"):
+                  "la_causal_forward_noalloc", "la_window_forward", "la_causal_forward_strided"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -134,6 +136,13 @@ def _dev(t, name):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_any(t):
+    """A GPU tensor's data pointer, whatever its strides (the caller passes them)."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -323,6 +332,83 @@ def la_window_forward(q, k, v, window, out=None, phi="relu1"):
     _call(load().la_window_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, n, d, dt, phi_code,
                                    int(window), _dev(out, "out"), _stream(q)), "la_window_forward")
     return out
+
+
+def la_causal_forward_strided(q, k, v, cu_seqlens=None, max_len=None, window=0, out=None, want_state=False,
+                              ws=None, phi="relu1", Hq=None):
+    """The causal (window=0) or sliding-window form over sequences of any layout.
+
+    cu_seqlens None: q [B, Hq, n, d], k, v [B, Hkv, n, d] as views with any
+    strides (the last one 1), e.g. x.view(B, n, H, d).transpose(1, 2) for a
+    [batch, seq, H, d] buffer.  cu_seqlens given (int64 [nseq + 1] on the
+    GPU): packed q [total, Hq, d], k, v [total, Hkv, d] (any strides, the last
+    one 1); sequence s is rows cu[s] .. cu[s+1] - 1; max_len bounds the lengths
+    (computed from cu_seqlens, with a host synchronisation, when None).  out
+    takes q's layout (allocated like q unless given).  q may be None for a
+    state-only causal pass (pass Hq).  With want_state (causal form) returns
+    (out, S_final [nseq, Hkv, d, d], z_final [nseq, Hkv, d])."""
+    phi_code = _phi(phi)
+    torch = _torch()
+    packed = cu_seqlens is not None
+    dims = 3 if packed else 4
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t is None:
+            continue
+        if t.dim() != dims or t.stride(-1) != 1 or not t.is_cuda:
+            raise ValueError(f"{name} must be a {dims}-D GPU tensor whose last dimension is contiguous")
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape and dtype")
+    if packed:
+        total, Hkv, d = k.shape
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+            raise ValueError("cu_seqlens must be a contiguous int64 vector [nseq + 1]")
+        nseq = cu_seqlens.numel() - 1
+        if max_len is None:
+            max_len = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if nseq > 0 else 0
+        kvs = (0, k.stride(1), k.stride(0))
+        seq_dim, head_dim = None, 1
+    else:
+        nseq, Hkv, max_len, d = k.shape
+        total = nseq * max_len
+        kvs = (k.stride(0), k.stride(1), k.stride(2))
+    if v.stride() != k.stride():
+        raise ValueError("k and v must share strides")
+    if q is not None:
+        Hq = q.shape[1]
+        if q.dtype != k.dtype or (packed and tuple(q.shape) != (total, Hq, d)) or (
+                not packed and tuple(q.shape) != (nseq, Hq, max_len, d)):
+            raise ValueError("q must match k's sizes (with its own head count) and dtype")
+        out = torch.empty_like(q) if out is None else out
+        if out.shape != q.shape or out.stride() != q.stride() or out.dtype != q.dtype:
+            raise ValueError("out must have q's shape, strides and dtype")
+        qs = (0, q.stride(1), q.stride(0)) if packed else (q.stride(0), q.stride(1), q.stride(2))
+    else:
+        Hq = Hq or Hkv
+        want_state = True
+        qs = (0, d, Hq * d) if packed else (Hq * max_len * d, max_len * d, d)
+    if Hq % Hkv:
+        raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
+    dt = _dtype_code(k)
+    S_final = z_final = None
+    if want_state:
+        if window:
+            raise ValueError("the window form hands on no state")
+        S_final = torch.empty((nseq, Hkv, d, d), dtype=torch.float32, device=k.device)
+        z_final = torch.empty((nseq, Hkv, d), dtype=torch.float32, device=k.device)
+    need = la_workspace_bytes(LA_OP_SEQS, max(nseq, 1), Hq, Hkv, max(max_len, 1), d, dt, 0)
+    ws = workspace(need, k.device) if ws is None else ws
+    qa = (ctypes.c_int64 * 3)(*qs)
+    ka = (ctypes.c_int64 * 3)(*kvs)
+    _call(load().la_causal_forward_strided(_dev_any(q) if q is not None else None, _dev_any(k), _dev_any(v),
+                                           _dev(cu_seqlens, "cu_seqlens") if packed else None, nseq, max_len,
+                                           total, Hq, Hkv, d, qa, ka, dt, phi_code, int(window),
+                                           _dev_any(out) if out is not None else None, _dev(S_final, "S_final"),
+                                           _dev(z_final, "z_final"), _dev(ws, "ws"), ws.numel(), _stream(k)),
+          "la_causal_forward_strided")
+    _debug_check(ws, "la_causal_forward_strided")
+    if q is None:
+        return S_final, z_final
+    return (out, S_final, z_final) if want_state else out
 
 
 def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):

@@ -179,6 +179,17 @@ static int32_t prefix_chunk(bool take, int32_t chunk, la_dtype dtype, int64_t d)
 
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dtype,
                           int32_t chunk) {
+  if (op == LA_OP_SEQS) {  // la_causal_forward_strided: B sequences of length at most n
+    if (check_sizes(B, Hq, Hkv, n, d, dtype) != LA_OK) return 0;
+    const int C = seq_chunk(elem_bytes(dtype), padded_dim(d), false);
+    if (C == 0) return 0;
+    SeqCall a{};
+    a.S.n = n;
+    a.nseq = B;
+    a.Hkv = Hkv;
+    a.d = d;
+    return kCtlBytes + state_bytes(seq_plan(a, C), B, Hkv);
+  }
   if (op != LA_OP_FORWARD && op != LA_OP_CAUSAL && op != LA_OP_PREFIX_MASK && op != LA_OP_PREFIX_MASK_BATCHED)
     return 0;
   const bool prefix = op == LA_OP_PREFIX_MASK || op == LA_OP_PREFIX_MASK_BATCHED;
@@ -328,14 +339,93 @@ la_status la_window_forward(const void* q, const void* k, const void* v, int64_t
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return LA_ERR_ALIGN;
   const size_t eb = elem_bytes(dtype);
-  const int C = window_chunk((int)eb, padded_dim(d));
+  const int C = seq_chunk((int)eb, padded_dim(d), true);
   if (C == 0) return LA_ERR_UNSUPPORTED;
   const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
   if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kvb) || overlaps(out, qb, v, kvb)) return LA_ERR_ALIAS;
-  if (B * Hkv * ((n + C - 1) / C) >= kMaxGrid) return LA_ERR_SHAPE;
   if (window > n) window = n;  // the whole causal prefix
-  Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, nullptr, stream, (int)phi};
-  return launch_window(a, window) == 0 ? LA_OK : LA_ERR_LAUNCH;
+  // contiguous [B, H, n, d] as a table of B sequences of length n
+  SeqCall a{q, k, v, out, Seqs{Hq * n * d, n * d, d, Hkv * n * d, n * d, d, nullptr, n, B * n},
+            B, Hq, Hkv, d, (int)dtype, (int)phi, window, d == padded_dim(d) && d * (int64_t)eb >= 16,
+            nullptr, nullptr, nullptr, nullptr, stream};
+  const Plan p = seq_plan(a, C);
+  if (B * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
+  return launch_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+// Bytes spanned by one tensor of a sequence table: the largest element offset
+// plus one row (0 if a stride is negative or the span overflows).
+static size_t table_span(int64_t nseq, int64_t H, int64_t n, int64_t d, const int64_t* st, bool packed,
+                         int64_t total, size_t eb) {
+  if (st[0] < 0 || st[1] < 0 || st[2] < 0) return 0;
+  const int64_t lim = (int64_t)1 << 50;
+  if (st[0] > lim / (nseq + 1) || st[1] > lim / (H + 1) || st[2] > lim / (total + n + 1)) return 0;
+  const int64_t rows = packed ? total : n;
+  if (rows == 0) return 0;
+  const int64_t last = (packed ? 0 : (nseq - 1) * st[0]) + (H - 1) * st[1] + (rows - 1) * st[2];
+  return (size_t)(last + d) * eb;
+}
+
+la_status la_causal_forward_strided(const void* q, const void* k, const void* v, const int64_t* cu_seqlens,
+                                    int64_t nseq, int64_t max_len, int64_t total, int64_t Hq, int64_t Hkv, int64_t d,
+                                    const int64_t* q_strides, const int64_t* kv_strides, la_dtype dtype, la_phi phi,
+                                    int64_t window, void* out, float* S_final, float* z_final, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  const bool packed = cu_seqlens != nullptr;
+  la_status st = check_sizes(nseq, Hq, Hkv, max_len, d, dtype);
+  if (st != LA_OK) return st;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1 && phi != LA_PHI_FEATURES) return LA_ERR_UNSUPPORTED;
+  if (!q_strides || !kv_strides) return LA_ERR_NULL;
+  if (window < 0) return LA_ERR_SHAPE;
+  if (packed && (total < 0 || total >= ((int64_t)1 << 40) || q_strides[0] != 0 || kv_strides[0] != 0))
+    return LA_ERR_SHAPE;
+  if (!packed) total = nseq * max_len;
+  if (window > max_len) window = max_len;  // the whole causal prefix of the longest sequence
+  if (!k || !v) return LA_ERR_NULL;
+  if ((q == nullptr) != (out == nullptr)) return LA_ERR_NULL;
+  if (!q && (window > 0 || (!S_final && !z_final))) return LA_ERR_NULL;
+  if (window > 0 && (S_final || z_final)) return LA_ERR_UNSUPPORTED;  // a window has no running state to hand on
+  if (!aligned16(k) || !aligned16(v) || (q && !aligned16(q)) || (out && !aligned16(out)) ||
+      (S_final && !aligned16(S_final)) || (z_final && !aligned16(z_final)) || (packed && !aligned16(cu_seqlens)))
+    return LA_ERR_ALIGN;
+  const size_t eb = elem_bytes(dtype);
+  const int DP = padded_dim(d);
+  const int C = seq_chunk((int)eb, DP, window > 0);
+  if (C == 0) return LA_ERR_UNSUPPORTED;
+  const size_t qspan = table_span(nseq, Hq, max_len, d, q_strides, packed, total, eb);
+  const size_t kvspan = table_span(nseq, Hkv, max_len, d, kv_strides, packed, total, eb);
+  if (kvspan == 0 || (q && qspan == 0)) return LA_ERR_SHAPE;
+  if (q_strides[1] < d && Hq > 1) return LA_ERR_SHAPE;   // heads of one row must not overlap
+  if (kv_strides[1] < d && Hkv > 1) return LA_ERR_SHAPE;
+  const size_t sb = (size_t)(nseq * Hkv * d * d) * sizeof(float), zb = (size_t)(nseq * Hkv * d) * sizeof(float);
+  if (overlaps(out, qspan, q, qspan) || overlaps(out, qspan, k, kvspan) || overlaps(out, qspan, v, kvspan))
+    return LA_ERR_ALIAS;
+  const void* ins[3] = {q, k, v};
+  const size_t inb[3] = {qspan, kvspan, kvspan};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(S_final, sb, ins[i], inb[i]) || overlaps(z_final, zb, ins[i], inb[i])) return LA_ERR_ALIAS;
+  if (overlaps(S_final, sb, out, qspan) || overlaps(z_final, zb, out, qspan) || overlaps(S_final, sb, z_final, zb))
+    return LA_ERR_ALIAS;
+  // 16-byte row pieces when every row and every row start is 16-byte aligned
+  const int64_t align_el = 16 / (int64_t)eb;
+  bool vec = d == DP && d >= align_el;
+  for (int i = 0; i < 3; ++i) vec = vec && q_strides[i] % align_el == 0 && kv_strides[i] % align_el == 0;
+  SeqCall a{q, k, v, out,
+            Seqs{q_strides[0], q_strides[1], q_strides[2], kv_strides[0], kv_strides[1], kv_strides[2], cu_seqlens,
+                 max_len, total},
+            nseq, Hq, Hkv, d, (int)dtype, (int)phi, window, vec, S_final, z_final, nullptr, nullptr, stream};
+  const Plan p = seq_plan(a, C);
+  if (nseq * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
+  const size_t need = kCtlBytes + (window > 0 ? 0 : state_bytes(p, nseq, Hkv));
+  if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(ws, need, ins[i], inb[i])) return LA_ERR_ALIAS;
+  if (overlaps(ws, need, out, qspan) || overlaps(ws, need, S_final, sb) || overlaps(ws, need, z_final, zb) ||
+      overlaps(ws, need, cu_seqlens, (size_t)(nseq + 1) * sizeof(int64_t)))
+    return LA_ERR_ALIAS;
+  a.ctl = reinterpret_cast<Ctl*>(ws);
+  a.ws = reinterpret_cast<char*>(ws) + kCtlBytes;
+  return launch_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 
 la_status la_decode_step_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,

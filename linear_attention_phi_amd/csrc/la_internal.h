@@ -118,11 +118,38 @@ int64_t forward_f32_nseg(int64_t n);
 size_t forward_f32_ws_bytes(int64_t NKV, int64_t nseg);
 int launch_forward_f32(const Fwd& a);
 
-// Sliding-window causal form (la_window.hip): no workspace.  window_chunk
-// is the chunk its kernel takes for (element bytes, padded dim), 0 if none
-// fits in LDS.
-int window_chunk(int elem_bytes, int DP);
-int launch_window(const Fwd& a, int64_t window);
+// A table of sequences (la_window.hip): per sequence s, key/value head g and
+// query head h, row t of K and V at k + s kb + start(s) kt + g kh + t kt and
+// of Q and out at q + s qb + start(s) qt + h qh + t qt (element strides);
+// start(s) = cu[s] for packed sequences (cu [nseq + 1] on the device, every
+// length at most n, every token below total), else 0 with every length n.
+struct Seqs {
+  int64_t qb, qh, qt, kb, kh, kt;
+  const int64_t* cu;
+  int64_t n, total;
+};
+// The causal (window = 0) or sliding-window (window >= 1) form over such a
+// table: k_wstate + k_scan + k_window, or k_window alone.
+struct SeqCall {
+  const void* q; const void* k; const void* v; void* out;  // q, out NULL: state only (causal)
+  Seqs S;
+  int64_t nseq, Hq, Hkv, d;
+  int dtype, phi;
+  int64_t window;
+  bool vec;              // 16-byte rows: d a power of two >= 8, strides and bases 16-byte aligned
+  float* S_final; float* z_final;
+  void* ws;              // causal form: (nseg + 1) state slots per (sequence, KV head)
+  Ctl* ctl;              // may be NULL (no packed table to check)
+  void* stream;
+};
+// The chunk of the sequence kernels for (element bytes, padded dim, form), 0
+// if their tiles do not fit in LDS; the segment plan of a call.
+int seq_chunk(int elem_bytes, int DP, bool window);
+Plan seq_plan(const SeqCall& a, int C);
+int launch_seq(const SeqCall& a);
+// k_scan over (nseg + 1) slots per unit, F = 1 (la_kernels.hip).
+int launch_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S_final, float* z_final,
+                void* stream);
 
 int launch_decode(const void* q, const void* k, const void* v, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t d, int dtype, int phi,

@@ -1937,6 +1937,14 @@ int launch_forward(const Fwd& a, const Plan& p) { return dispatch(a, p, 0); }
 int launch_causal(const Fwd& a, const Plan& p) { return dispatch(a, p, 1); }
 int launch_prefix(const Fwd& a, const Plan& p) { return dispatch(a, p, 2); }
 
+int launch_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S_final, float* z_final,
+                void* stream) {
+  const int64_t E = slot_elems(DP);
+  k_scan<<<dim3((unsigned)nunits, (unsigned)((E + NT - 1) / NT)), NT, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      ws, nseg, DP, d, S_final, z_final, 1);
+  return (int)hipGetLastError();
+}
+
 int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                   int dtype, int phi, float* S, float* z, void* out, void* stream) {
   if (phi == 2) return launch_decode_pm<PM_FEAT>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream);

@@ -30,23 +30,41 @@
 // heads of the group the masked scores, num and den on MFMA (la_device.h
 // conventions), division in the epilogue, rows staged through LDS.  No
 // workspace: the state never leaves the workgroup.
+//
+// The same kernel with WIN = false is the causal form (w covers every
+// earlier key): W starts from the exclusive prefix of the segment's first
+// chunk (k_wstate's segment states, scanned by k_scan), there is no trailing
+// tile, and W gains each chunk's state.  Both take their rows through a
+// sequence table (Seqs): per sequence s, key/value head g and query head h,
+// row t of K and V at k + s kb + start(s) kt + g kh + t kt and of Q and out at
+// q + s qb + start(s) qt + h qh + t qt, where start(s) = cu[s] for packed
+// sequences of different lengths (varlen: cu[s] .. cu[s + 1] - 1 are the
+// tokens of sequence s, nothing padded) and 0 for a fixed length n.  Contiguous
+// [B, H, n, d] (BHND), [B, n, H, d] (BNHD, as trim-transformer's
+// [batch, seq, dim] quickstart) and packed [tokens, H, d] are all strides of
+// this table.  A sequence whose entries of cu fall outside [0, total] or
+// decrease (cu[s - 1] <= cu[s] <= cu[s + 1] must hold), or whose length
+// exceeds the maximum the call states, is left empty and the fault is
+// recorded in the control block (la_workspace_status: LA_ERR_RANGE).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "la_ctl.h"
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace {
 
 using namespace la_dev;
+using la_internal::Seqs;
 
-// Copy ROWS rows x DP features of one head (row stride d, row0 first) into
+// Copy ROWS rows x DP features (row stride ld elements, row0 first) into
 // LDS: tm[row * ldt + col] transformed by TMX and/or fm[col * ldf + row]
 // transformed by FMX.  Rows at or past nvalid and features at or past d are
-// stored as 0 (not phi(0)).  vec: d == DP, 16-byte pieces.
+// stored as 0 (not phi(0)).  vec: d == DP and 16-byte rows, 16-byte pieces.
 template <typename T, int DP, int ROWS, int TMX, int FMX>
-__device__ __forceinline__ void stage(const T* __restrict__ base, int64_t row0, int nvalid, int d, bool vec, T* tm,
-                                      int ldt, T* fm, int ldf, int tid) {
+__device__ __forceinline__ void stage(const T* __restrict__ base, int64_t ld, int64_t row0, int nvalid, int d,
+                                      bool vec, T* tm, int ldt, T* fm, int ldf, int tid) {
   if (vec) {
     constexpr int EPP = 16 / (int)sizeof(T);
     constexpr int PPR = DP / EPP;
@@ -59,7 +77,7 @@ __device__ __forceinline__ void stage(const T* __restrict__ base, int64_t row0, 
       const int p = tid + k * NT;
       const int row = p / PPR, col = (p % PPR) * EPP;
       raw[k].u = make_uint4(0, 0, 0, 0);
-      if (p < NP && row < nvalid) raw[k].u = *reinterpret_cast<const uint4*>(base + (row0 + row) * DP + col);
+      if (p < NP && row < nvalid) raw[k].u = *reinterpret_cast<const uint4*>(base + (row0 + row) * ld + col);
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -87,7 +105,7 @@ __device__ __forceinline__ void stage(const T* __restrict__ base, int64_t row0, 
     for (int idx = tid; idx < ROWS * DP; idx += NT) {
       const int row = idx / DP, col = idx % DP;
       const bool ok = row < nvalid && col < d;
-      const float x = ok ? to_f(base[(row0 + row) * d + col]) : 0.0f;
+      const float x = ok ? to_f(base[(row0 + row) * ld + col]) : 0.0f;
       if (TMX != XF_NONE) tm[row * ldt + col] = cvt<T>(ok ? xform<TMX>(x) : 0.0f);
       if (FMX != XF_NONE) fm[col * ldf + row] = cvt<T>(ok ? xform<FMX>(x) : 0.0f);
     }
@@ -101,49 +119,46 @@ __device__ __forceinline__ int chunk_rows(int64_t x, int C, int64_t n) {
   return r <= 0 ? 0 : (r < C ? (int)r : C);
 }
 
-template <typename T, int DP, int C, int PM>
-__global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T* __restrict__ k,
-                                               const T* __restrict__ v, T* __restrict__ out, int64_t n, int d, int R,
-                                               int64_t nchunks, int64_t G, int64_t nseg, int64_t nfull, int wlen,
-                                               int delta) {
-  constexpr int LQ = DP + PAD;      // token-major rows (Q, K, trailing K, W^T)
-  constexpr int LC = C + PAD;       // feature-major rows of the leading chunk, scores
-  constexpr int LC2 = 2 * C + PAD;  // feature-major rows of the trailing tile, its scores
-  constexpr int NIB = C / 32;       // 32-row query / key blocks of a chunk
-  constexpr int NTB = 2 * NIB;      // key blocks of the trailing tile
-  constexpr int NBB = DP / 32;
-  constexpr int PX = q_xform<PM>();  // phi on Q and on every K tile (no relu split here)
-  static_assert(PM != PM_ID, "normalised form");
-  __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
-  __shared__ __attribute__((aligned(16))) T sK[C * LQ];
-  __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
-  __shared__ __attribute__((aligned(16))) T sVT[DP * LC];
-  __shared__ __attribute__((aligned(16))) T sKtr[2 * C * LQ];
-  __shared__ __attribute__((aligned(16))) T sKTtr[DP * LC2];
-  __shared__ __attribute__((aligned(16))) T sVTtr[DP * LC2];
-  __shared__ __attribute__((aligned(16))) T sST[DP * LQ];
-  __shared__ __attribute__((aligned(16))) T sP[C * LC];
-  __shared__ __attribute__((aligned(16))) T sPtr[C * LC2];
-  // z of the window as a high part and the remainder in T, a zero row and a
-  // ones row: the A operand rows of the denominator products
-  __shared__ __attribute__((aligned(16))) T szh[DP + 16];
-  __shared__ __attribute__((aligned(16))) T szl[DP + 16];
-  __shared__ __attribute__((aligned(16))) T szero[DP + 16];
-  __shared__ __attribute__((aligned(16))) T sones[16];
+// Sequence s of the table: its first token and its length (0, with the
+// error recorded, if the table is inconsistent).
+struct SeqSpan {
+  int64_t start, len;
+};
+__device__ __forceinline__ SeqSpan seq_span(const Seqs& S, int64_t s, la_internal::Ctl* ctl, bool report) {
+  if (!S.cu) return {0, S.n};
+  const int64_t a = S.cu[s], b = S.cu[s + 1], prev = s > 0 ? S.cu[s - 1] : 0;
+  if (a < prev || b < a || b > S.total || b - a > S.n) {  // (cu[0] itself must be >= 0)
+    if (report) la_ctl::ctl_fail(ctl, la_internal::kErrRange);
+    return {0, 0};
+  }
+  return {a, b - a};
+}
+
+struct WinArgs {
+  const void* q; const void* k; const void* v; void* out;
+  Seqs S;
+  int d, R;
+  int64_t Hkv, G, nseg;  // segments of G chunks; nseg per (sequence, KV head) in the grid
+  int64_t nfull;         // window form: chunks inside every window of a query chunk (see above)
+  int wlen, delta;       // window form: w, and the trailing tile's mask offset
+  bool vec;              // 16-byte row pieces
+  float* states;         // causal form: (nseg + 1) slots per (sequence, KV head), scanned
+  la_internal::Ctl* ctl;
+};
+
+// The window state W (fp32 accumulators of the la_device.h layout, plus z of
+// thread tid < DP) and its updates from feature-major phi(K) and V tiles.
+template <typename T, int DP, int C>
+struct WinState {
   using SB = StateBlocks<DP>;
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
-  const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
-  const bool vec = d == DP;
-  const T* kb = k + bh * n * d;
-  const T* vb = v + bh * n * d;
-  const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
-
-  f32x16 accW[SB::PER_WAVE];
+  f32x16 acc[SB::PER_WAVE];
+  float z = 0.0f;
+  __device__ __forceinline__ void clear() {
 #pragma unroll
-  for (int s = 0; s < SB::PER_WAVE; ++s) accW[s] = f32x16{};
-  float zW = 0.0f;  // z of the window, feature tid (tid < DP)
-  auto add_state = [&](const T* KT, int ldk, const T* VT, int ldv, bool sub) {
+    for (int s = 0; s < SB::PER_WAVE; ++s) acc[s] = f32x16{};
+    z = 0.0f;
+  }
+  __device__ __forceinline__ void add(const T* KT, int ldk, const T* VT, int ldv, bool sub, int w, int lane, int tid) {
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
       const int e = w + NW * s;
@@ -153,28 +168,126 @@ __global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T*
           f32x16 t = f32x16{};
           gemm_acc<T, C / 16>(t, KT + ma * 32 * ldk, ldk, VT + nb * 32 * ldv, ldv, lane);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) accW[s][r] -= t[r];
+          for (int r = 0; r < 16; ++r) acc[s][r] -= t[r];
         } else {
-          gemm_acc<T, C / 16>(accW[s], KT + ma * 32 * ldk, ldk, VT + nb * 32 * ldv, ldv, lane);
+          gemm_acc<T, C / 16>(acc[s], KT + ma * 32 * ldk, ldk, VT + nb * 32 * ldv, ldv, lane);
         }
       }
     }
     if (tid < DP) {
       float zs = 0.0f;
       for (int t = 0; t < C; ++t) zs += to_f(KT[tid * ldk + t]);
-      zW += sub ? -zs : zs;
+      z += sub ? -zs : zs;
     }
-  };
+  }
+};
 
-  // ---- warm-up: W = states of chunks c0 - nfull - 1 .. c0 - 1 (the first
-  // step subtracts chunk c0 - nfull - 1 again); none while nfull = 0
-  for (int64_t x = (c0 - nfull - 1 > 0 ? c0 - nfull - 1 : 0); nfull > 0 && x < c0; ++x) {
-    const int nvx = chunk_rows(x, C, n);
-    stage<T, DP, C, XF_NONE, PX>(kb, x * C, nvx, d, vec, nullptr, 0, sKT, LC, tid);
-    stage<T, DP, C, XF_NONE, XF_ID>(vb, x * C, nvx, d, vec, nullptr, 0, sVT, LC, tid);
+// ------------------------------------------------------------------ k_wstate
+// Causal form's state pass: the segment's chunk states summed (S row-major,
+// then z: the slot layout of k_scan), zeros for segments past a sequence's
+// end.
+template <typename T, int DP, int C, int PM>
+__global__ __launch_bounds__(NT) void k_wstate(WinArgs A) {
+  constexpr int LC = C + PAD;
+  constexpr int PX = q_xform<PM>();
+  __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
+  __shared__ __attribute__((aligned(16))) T sVT[DP * LC];
+  using SB = StateBlocks<DP>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t u = blockIdx.x / A.nseg, seg = blockIdx.x % A.nseg;
+  const int64_t sq = u / A.Hkv, g = u % A.Hkv;
+  const SeqSpan sp = seq_span(A.S, sq, A.ctl, seg == 0 && tid == 0);
+  const T* kb = reinterpret_cast<const T*>(A.k) + sq * A.S.kb + sp.start * A.S.kt + g * A.S.kh;
+  const T* vb = reinterpret_cast<const T*>(A.v) + sq * A.S.kb + sp.start * A.S.kt + g * A.S.kh;
+  const int64_t nch = (sp.len + C - 1) / C;
+  const int64_t c0 = seg * A.G, c1 = (c0 + A.G < nch) ? c0 + A.G : nch;
+  WinState<T, DP, C> W;
+  W.clear();
+  for (int64_t c = c0; c < c1; ++c) {
+    const int nv = chunk_rows(c, C, sp.len);
+    stage<T, DP, C, XF_NONE, PX>(kb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sKT, LC, tid);
+    stage<T, DP, C, XF_NONE, XF_ID>(vb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sVT, LC, tid);
     __syncthreads();
-    add_state(sKT, LC, sVT, LC, false);
+    W.add(sKT, LC, sVT, LC, false, w, lane, tid);
     __syncthreads();
+  }
+  float* dst = A.states + (u * (A.nseg + 1) + seg) * slot_elems(DP);
+#pragma unroll
+  for (int s = 0; s < SB::PER_WAVE; ++s) {
+    const int e = w + NW * s;
+    if (e < SB::TOTAL) st_state_block<DP>(dst, W.acc[s], e / SB::NB, e % SB::NB, lane);
+  }
+  if (tid < DP) dst[DP * DP + tid] = W.z;
+}
+
+// ------------------------------------------------------------------ k_window
+template <typename T, int DP, int C, int PM, bool WIN>
+__global__ __launch_bounds__(NT) void k_window(WinArgs A) {
+  constexpr int LQ = DP + PAD;      // token-major rows (Q, K, trailing K, W^T)
+  constexpr int LC = C + PAD;       // feature-major rows of the leading chunk, scores
+  constexpr int LC2 = 2 * C + PAD;  // feature-major rows of the trailing tile, its scores
+  constexpr int NIB = C / 32;       // 32-row query / key blocks of a chunk
+  constexpr int NTB = WIN ? 2 * NIB : 0;  // key blocks of the trailing tile
+  constexpr int NBB = DP / 32;
+  constexpr int PX = q_xform<PM>();  // phi on Q and on every K tile (no relu split here)
+  static_assert(PM != PM_ID, "normalised form");
+  // the trailing tile exists in the window form only
+  constexpr int TR_K = WIN ? 2 * C * LQ : 8, TR_T = WIN ? DP * LC2 : 8, TR_P = WIN ? C * LC2 : 8;
+  __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
+  __shared__ __attribute__((aligned(16))) T sK[C * LQ];
+  __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
+  __shared__ __attribute__((aligned(16))) T sVT[DP * LC];
+  __shared__ __attribute__((aligned(16))) T sKtr[TR_K];
+  __shared__ __attribute__((aligned(16))) T sKTtr[TR_T];
+  __shared__ __attribute__((aligned(16))) T sVTtr[TR_T];
+  __shared__ __attribute__((aligned(16))) T sST[DP * LQ];
+  __shared__ __attribute__((aligned(16))) T sP[C * LC];
+  __shared__ __attribute__((aligned(16))) T sPtr[TR_P];
+  // z of the window as a high part and the remainder in T, a zero row and a
+  // ones row: the A operand rows of the denominator products
+  __shared__ __attribute__((aligned(16))) T szh[DP + 16];
+  __shared__ __attribute__((aligned(16))) T szl[DP + 16];
+  __shared__ __attribute__((aligned(16))) T szero[DP + 16];
+  __shared__ __attribute__((aligned(16))) T sones[16];
+  using SB = StateBlocks<DP>;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int64_t u = blockIdx.x / A.nseg, seg = blockIdx.x % A.nseg;
+  const int64_t sq = u / A.Hkv, g = u % A.Hkv;
+  const SeqSpan sp = seq_span(A.S, sq, A.ctl, seg == 0 && tid == 0);
+  const int64_t n = sp.len, nchunks = (n + C - 1) / C;
+  const int64_t c0 = seg * A.G, c1 = (c0 + A.G < nchunks) ? c0 + A.G : nchunks;
+  if (c0 >= c1) return;  // past this sequence's end: nothing to do, and no barrier below is skipped by half the group
+  const int d = A.d, R = A.R;
+  const bool vec = A.vec;
+  const int64_t kt = A.S.kt, qt = A.S.qt;
+  const T* kb = reinterpret_cast<const T*>(A.k) + sq * A.S.kb + sp.start * kt + g * A.S.kh;
+  const T* vb = reinterpret_cast<const T*>(A.v) + sq * A.S.kb + sp.start * kt + g * A.S.kh;
+  const int64_t nfull = A.nfull;
+
+  WinState<T, DP, C> W;
+  if (WIN) {
+    // warm-up: W = states of chunks c0 - nfull - 1 .. c0 - 1 (the first step
+    // subtracts chunk c0 - nfull - 1 again); none while nfull = 0
+    W.clear();
+    for (int64_t x = (c0 - nfull - 1 > 0 ? c0 - nfull - 1 : 0); nfull > 0 && x < c0; ++x) {
+      const int nvx = chunk_rows(x, C, n);
+      stage<T, DP, C, XF_NONE, PX>(kb, kt, x * C, nvx, d, vec, nullptr, 0, sKT, LC, tid);
+      stage<T, DP, C, XF_NONE, XF_ID>(vb, kt, x * C, nvx, d, vec, nullptr, 0, sVT, LC, tid);
+      __syncthreads();
+      W.add(sKT, LC, sVT, LC, false, w, lane, tid);
+      __syncthreads();
+    }
+  } else {
+    // the exclusive prefix before chunk c0 (the scanned segment state)
+    const float* src = A.states + (u * (A.nseg + 1) + seg) * slot_elems(DP);
+#pragma unroll
+    for (int s = 0; s < SB::PER_WAVE; ++s) {
+      const int e = w + NW * s;
+      if (e < SB::TOTAL) ld_state_block<DP>(W.acc[s], src, e / SB::NB, e % SB::NB, lane);
+      else W.acc[s] = f32x16{};
+    }
+    W.z = tid < DP ? src[DP * DP + tid] : 0.0f;
   }
   if (tid < 16) {
     sones[tid] = cvt<T>(1.0f);
@@ -189,41 +302,44 @@ __global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T*
   const bool has_out = nb0 < NBB;
 
   for (int64_t c = c0; c < c1; ++c) {
-    const int64_t t0 = c * C, ce = c - nfull;  // the first chunk inside every window
+    const int64_t t0 = c * C, ce = c - nfull;  // window form: the first chunk inside every window
     const int nv = chunk_rows(c, C, n);
     // leading chunk: phi(K) token- and feature-major, V feature-major;
-    // trailing tile: chunks e - 2 and e - 1 (phi(K) both ways, V feature-major)
-    stage<T, DP, C, PX, PX>(kb, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
-    stage<T, DP, C, XF_NONE, XF_ID>(vb, t0, nv, d, vec, nullptr, 0, sVT, LC, tid);
+    // trailing tile: chunks ce - 2 and ce - 1 (phi(K) both ways, V feature-major)
+    stage<T, DP, C, PX, PX>(kb, kt, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
+    stage<T, DP, C, XF_NONE, XF_ID>(vb, kt, t0, nv, d, vec, nullptr, 0, sVT, LC, tid);
+    if (WIN) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int64_t x = ce - 2 + half;
-      const int nvx = chunk_rows(x, C, n);
-      const int64_t r0 = x < 0 ? 0 : x * C;
-      stage<T, DP, C, PX, PX>(kb, r0, nvx, d, vec, sKtr + half * C * LQ, LQ, sKTtr + half * C, LC2, tid);
-      stage<T, DP, C, XF_NONE, XF_ID>(vb, r0, nvx, d, vec, nullptr, 0, sVTtr + half * C, LC2, tid);
-    }
-    if (nfull > 0) {  // W loses chunk e - 1, which has left the chunks inside every window
-      __syncthreads();
-      add_state(sKTtr + C, LC2, sVTtr + C, LC2, true);
+      for (int half = 0; half < 2; ++half) {
+        const int64_t x = ce - 2 + half;
+        const int nvx = chunk_rows(x, C, n);
+        const int64_t r0 = x < 0 ? 0 : x * C;
+        stage<T, DP, C, PX, PX>(kb, kt, r0, nvx, d, vec, sKtr + half * C * LQ, LQ, sKTtr + half * C, LC2, tid);
+        stage<T, DP, C, XF_NONE, XF_ID>(vb, kt, r0, nvx, d, vec, nullptr, 0, sVTtr + half * C, LC2, tid);
+      }
+      if (nfull > 0) {  // W loses chunk ce - 1, which has left the chunks inside every window
+        __syncthreads();
+        W.add(sKTtr + C, LC2, sVTtr + C, LC2, true, w, lane, tid);
+      }
     }
     // W^T (sST[b][a] = W[a][b]) and z of the window in T
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
       const int e = w + NW * s;
-      if (e < SB::TOTAL) st_accT(sST + (e % SB::NB) * 32 * LQ + (e / SB::NB) * 32, LQ, accW[s], lane);
+      if (e < SB::TOTAL) st_accT(sST + (e % SB::NB) * 32 * LQ + (e / SB::NB) * 32, LQ, W.acc[s], lane);
     }
     if (tid < DP) {
-      const T zh = cvt<T>(zW);
+      const T zh = cvt<T>(W.z);
       szh[tid] = zh;
-      szl[tid] = cvt<T>(zW - to_f(zh));
+      szl[tid] = cvt<T>(W.z - to_f(zh));
       szero[tid] = cvt<T>(0.0f);
     }
 
     for (int r = 0; r < R; ++r) {
-      const T* qh = q + (bh * R + r) * n * d;
+      const int64_t hq = g * R + r;
+      const T* qh = reinterpret_cast<const T*>(A.q) + sq * A.S.qb + sp.start * qt + hq * A.S.qh;
       __syncthreads();  // the tiles above are written; the previous head is done with sQ, sP, sPtr
-      stage<T, DP, C, PX, XF_NONE>(qh, t0, nv, d, vec, sQ, LQ, nullptr, 0, tid);
+      stage<T, DP, C, PX, XF_NONE>(qh, qt, t0, nv, d, vec, sQ, LQ, nullptr, 0, tid);
       __syncthreads();
 
       // ---- scores: chunk c (keys i - w < j <= i) into sP[i][j]; the trailing
@@ -241,7 +357,8 @@ __global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T*
             const int kb2 = lead ? jb : jb - NIB;
             gemm_acc<T, DP / 16>(acc, (lead ? sK : sKtr) + kb2 * 32 * LQ, LQ, sQ + ib2 * 32 * LQ, LQ, lane);
             const int i = ib2 * 32 + (lane & 31);
-            const int lo = lead ? i - wlen + 1 : i + delta, hi = lead ? i : 2 * C;  // kept key offsets
+            const int lo = lead ? (WIN ? i - A.wlen + 1 : 0) : i + A.delta;  // kept key offsets: lo .. hi
+            const int hi = lead ? i : 2 * C;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
               const int j = kb2 * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
@@ -292,17 +409,17 @@ __global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T*
         }
         inv = 1.0f / __shfl(dacc[0] + dacc[8], lane & 31);
 #pragma unroll
-        for (int u = 0; u < NPW; ++u) {
-          const int nb = nb0 + u * NB_STEP;
-          accO[u] = f32x16{};
+        for (int uu = 0; uu < NPW; ++uu) {
+          const int nb = nb0 + uu * NB_STEP;
+          accO[uu] = f32x16{};
           if (nb < NBB) {
-            gemm_acc<T, DP / 16>(accO[u], sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
+            gemm_acc<T, DP / 16>(accO[uu], sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
 #pragma unroll
             for (int jb = 0; jb <= ib; ++jb)
-              gemm_acc<T, 2>(accO[u], sVT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
+              gemm_acc<T, 2>(accO[uu], sVT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
-              gemm_acc<T, 2>(accO[u], sVTtr + nb * 32 * LC2 + tb * 32, LC2, sPtr + ib * 32 * LC2 + tb * 32, LC2,
+              gemm_acc<T, 2>(accO[uu], sVTtr + nb * 32 * LC2 + tb * 32, LC2, sPtr + ib * 32 * LC2 + tb * 32, LC2,
                              lane);
           }
         }
@@ -310,17 +427,17 @@ __global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T*
       __syncthreads();  // every wave is past its reads of sQ: the rows go out through it
       if (has_out) {
 #pragma unroll
-        for (int u = 0; u < NPW; ++u) {
-          const int nb = nb0 + u * NB_STEP;
+        for (int uu = 0; uu < NPW; ++uu) {
+          const int nb = nb0 + uu * NB_STEP;
           if (nb < NBB) {
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-              sQ[i * LQ + nb * 32 + 8 * (e >> 2) + 4 * h + (e & 3)] = cvt<T>(accO[u][e] * inv);
+              sQ[i * LQ + nb * 32 + 8 * (e >> 2) + 4 * h + (e & 3)] = cvt<T>(accO[uu][e] * inv);
           }
         }
       }
       __syncthreads();
-      T* ob = out + (bh * R + r) * n * d;
+      T* ob = reinterpret_cast<T*>(A.out) + sq * A.S.qb + sp.start * qt + hq * A.S.qh;
       if (vec) {
         constexpr int EPP = 8 / (int)sizeof(T);  // 8-byte pieces (LDS rows are 8-byte aligned)
         constexpr int PPR = DP / EPP;
@@ -328,54 +445,60 @@ __global__ __launch_bounds__(NT) void k_window(const T* __restrict__ q, const T*
         for (int idx = tid; idx < nv * PPR; idx += NT) {
           const int rr = idx / PPR, col = EPP * (idx % PPR);
           __builtin_nontemporal_store(*reinterpret_cast<const U*>(sQ + rr * LQ + col),
-                                      reinterpret_cast<U*>(ob + (t0 + rr) * d + col));
+                                      reinterpret_cast<U*>(ob + (t0 + rr) * qt + col));
         }
       } else {
         for (int idx = tid; idx < nv * d; idx += NT) {
           const int rr = idx / d, col = idx % d;
-          ob[(t0 + rr) * d + col] = sQ[rr * LQ + col];
+          ob[(t0 + rr) * qt + col] = sQ[rr * LQ + col];
         }
       }
     }
 
-    // ---- W += dS(c)
-    if (nfull > 0) add_state(sKT, LC, sVT, LC, false);
+    // ---- W += dS(c) (the causal form always; the window form once chunks
+    // lie inside every window)
+    if (!WIN || nfull > 0) W.add(sKT, LC, sVT, LC, false, w, lane, tid);
     __syncthreads();
   }
 }
 
-// LDS bytes of k_window<T, DP, C>: must fit one CU's 160 KiB.
-constexpr size_t window_lds(int eb, int DP, int C) {
+// LDS bytes of k_window<T, DP, C, .., WIN>: must fit one CU's 160 KiB.
+constexpr size_t window_lds(int eb, int DP, int C, bool win) {
   const size_t LQ = DP + PAD, LC = C + PAD, LC2 = 2 * C + PAD;
-  return (size_t)eb * (2 * C * LQ + 2 * DP * LC + 2 * C * LQ + 2 * DP * LC2 + DP * LQ + C * LC + C * LC2 +
-                       3 * (DP + 16) + 16);
+  const size_t tr = win ? 2 * C * LQ + 2 * DP * LC2 + C * LC2 : 24;
+  return (size_t)eb * (2 * C * LQ + 2 * DP * LC + tr + DP * LQ + C * LC + 3 * (DP + 16) + 16);
 }
 
-template <typename T, int DP, int C>
-int run_window(const la_internal::Fwd& a, int64_t window) {
+template <typename T, int DP, int C, bool WIN>
+int run_window(const la_internal::SeqCall& a) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  const int64_t nbh = a.B * a.Hkv, nchunks = (a.n + C - 1) / C;
-  const int64_t nfull = window / C > 1 ? window / C - 1 : 0;
-  const int delta = (int)((nfull + 2) * C - window + 1);
-  // segments of at least nfull chunks (the warm-up is then about as long as
-  // the walk), about 512 workgroups where the sequence allows more
-  int64_t G = (nbh * nchunks + 511) / 512;
-  if (G < nfull) G = nfull;
-  if (G < 1) G = 1;
-  if (G > nchunks) G = nchunks;
-  const int64_t nseg = (nchunks + G - 1) / G;
-  const int R = (int)(a.Hq / a.Hkv);
-  const T* q = reinterpret_cast<const T*>(a.q);
-  const T* k = reinterpret_cast<const T*>(a.k);
-  const T* v = reinterpret_cast<const T*>(a.v);
-  T* out = reinterpret_cast<T*>(a.out);
-  const dim3 grid((unsigned)(nbh * nseg));
+  const la_internal::Plan p = la_internal::seq_plan(a, C);
+  WinArgs A{a.q, a.k, a.v, a.out, a.S, (int)a.d, (int)(a.Hq / a.Hkv), a.Hkv, p.G, p.nseg, 0, 0, 0,
+            a.vec, reinterpret_cast<float*>(a.ws), a.ctl};
+  if (WIN) {
+    A.nfull = a.window / C > 1 ? a.window / C - 1 : 0;
+    A.wlen = (int)a.window;
+    A.delta = (int)((A.nfull + 2) * C - a.window + 1);
+  }
+  const dim3 grid((unsigned)(a.nseq * a.Hkv * p.nseg));
+  if (!WIN) {  // the causal form: segment states, their exclusive prefix, then the walk
+    if (a.phi == 1)
+      k_wstate<T, DP, C, PM_ELU1><<<grid, NT, 0, st>>>(A);
+    else if (a.phi == 2)
+      k_wstate<T, DP, C, PM_FEAT><<<grid, NT, 0, st>>>(A);
+    else
+      k_wstate<T, DP, C, PM_RELU1><<<grid, NT, 0, st>>>(A);
+    const int e = la_internal::launch_scan(A.states, a.nseq * a.Hkv, p.nseg, DP, (int)a.d, a.S_final, a.z_final,
+                                           a.stream);
+    if (e != 0) return e;
+    if (!a.out) return (int)hipGetLastError();
+  }
   if (a.phi == 1)
-    k_window<T, DP, C, PM_ELU1><<<grid, NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, nchunks, G, nseg, nfull, (int)window, delta);
+    k_window<T, DP, C, PM_ELU1, WIN><<<grid, NT, 0, st>>>(A);
   else if (a.phi == 2)
-    k_window<T, DP, C, PM_FEAT><<<grid, NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, nchunks, G, nseg, nfull, (int)window, delta);
+    k_window<T, DP, C, PM_FEAT, WIN><<<grid, NT, 0, st>>>(A);
   else
-    k_window<T, DP, C, PM_RELU1><<<grid, NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, nchunks, G, nseg, nfull, (int)window, delta);
+    k_window<T, DP, C, PM_RELU1, WIN><<<grid, NT, 0, st>>>(A);
   return (int)hipGetLastError();
 }
 
@@ -383,28 +506,54 @@ int run_window(const la_internal::Fwd& a, int64_t window) {
 
 namespace la_internal {
 
-int window_chunk(int elem_bytes, int DP) {
+int seq_chunk(int elem_bytes, int DP, bool window) {
   for (int c : {64, 32})
-    if (window_lds(elem_bytes, DP, c) <= kLdsLimit) return c;
+    if (window_lds(elem_bytes, DP, c, window) <= kLdsLimit) return c;
   return 0;
 }
 
-int launch_window(const Fwd& a, int64_t window) {
+Plan seq_plan(const SeqCall& a, int C) {
+  Plan p;
+  p.DP = padded_dim(a.d);
+  p.C = C;
+  p.nchunks = (a.S.n + C - 1) / C;  // of the longest sequence
+  const int64_t nfull = a.window > 0 && a.window / C > 1 ? a.window / C - 1 : 0;
+  // about 512 workgroups; in the window form segments of at least nfull
+  // chunks (the warm-up is then about as long as the walk)
+  int64_t G = (a.nseq * a.Hkv * p.nchunks + 511) / 512;
+  if (G < nfull) G = nfull;
+  if (G < 1) G = 1;
+  if (G > p.nchunks) G = p.nchunks;
+  p.G = G;
+  p.nseg = (p.nchunks + G - 1) / G;
+  return p;
+}
+
+int launch_seq(const SeqCall& a) {
   const int DP = padded_dim(a.d);
-  const int C = window_chunk(a.dtype == 0 ? 4 : 2, DP);
-#define LA_WIN(TT, DD, CC)                                                                  \
-  if (DP == DD && C == CC) {                                                                \
-    if constexpr (window_lds((int)sizeof(TT), DD, CC) <= kLdsLimit) return run_window<TT, DD, CC>(a, window); \
+  const bool win = a.window > 0;
+  const int C = seq_chunk(a.dtype == 0 ? 4 : 2, DP, win);
+#define LA_SEQ(TT, DD, CC, WW)                                                                     \
+  if (DP == DD && C == CC && win == WW) {                                                         \
+    if constexpr (window_lds((int)sizeof(TT), DD, CC, WW) <= kLdsLimit) return run_window<TT, DD, CC, WW>(a); \
   }
   if (a.dtype == 0) {
-    LA_WIN(float, 32, 64)
-    LA_WIN(float, 64, 32)
+    LA_SEQ(float, 32, 64, true)
+    LA_SEQ(float, 64, 32, true)
+    LA_SEQ(float, 32, 64, false)
+    LA_SEQ(float, 64, 64, false)
+    LA_SEQ(float, 64, 32, false)
+    LA_SEQ(float, 128, 32, false)
   } else {
-    LA_WIN(bf16, 32, 64)
-    LA_WIN(bf16, 64, 64)
-    LA_WIN(bf16, 128, 32)
+    LA_SEQ(bf16, 32, 64, true)
+    LA_SEQ(bf16, 64, 64, true)
+    LA_SEQ(bf16, 128, 32, true)
+    LA_SEQ(bf16, 32, 64, false)
+    LA_SEQ(bf16, 64, 64, false)
+    LA_SEQ(bf16, 128, 64, false)
+    LA_SEQ(bf16, 128, 32, false)
   }
-#undef LA_WIN
+#undef LA_SEQ
   return (int)hipErrorInvalidValue;
 }
 

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
                           "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
                           "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
-                          "la_causal_forward_noalloc", "la_window_forward"}
+                          "la_causal_forward_noalloc", "la_window_forward", "la_causal_forward_strided"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -263,3 +263,37 @@ def test_window_rejections(lib):
     assert f(dt=0, d=128) == UNSUP        # fp32 with d > 64: the tiles do not fit in LDS
     assert f(k=K + 4) == ALIGN
     assert f(out=V) == ALIAS
+
+
+def test_strided_rejections(lib):
+    """la_causal_forward_strided: every check on the host, nothing launched."""
+    I3 = ctypes.c_int64 * 3
+    B, H, n, d = 2, 2, 64, 16
+    bnhd = I3(n * H * d, d, H * d)  # [B, n, H, d]
+
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, cu=None, nseq=B, max_len=n, total=0, Hq=H, Hkv=H, d=d, qs=bnhd, ks=bnhd, dt=1,
+                 phi=0, w=0, out=O, Sf=None, zf=None, ws=WSP, wsb=BIG)
+        a.update(kw)
+        return lib.la_causal_forward_strided(a["q"], a["k"], a["v"], a["cu"], a["nseq"], a["max_len"], a["total"],
+                                             a["Hq"], a["Hkv"], a["d"], a["qs"], a["ks"], a["dt"], a["phi"], a["w"],
+                                             a["out"], a["Sf"], a["zf"], a["ws"], a["wsb"], None)
+    assert f(k=None) == NULL
+    assert f(qs=None) == NULL
+    assert f(q=None) == NULL                      # q without out
+    assert f(q=None, out=None) == NULL            # state only needs S_final or z_final
+    assert f(q=None, out=None, w=5, Sf=S) == NULL or f(q=None, out=None, w=5, Sf=S) == UNSUP
+    assert f(w=-1) == SHAPE
+    assert f(w=4, Sf=S) == UNSUP                   # a window hands on no state
+    assert f(qs=I3(n * H * d, d, -H * d)) == SHAPE  # negative stride
+    assert f(qs=I3(n * H * d, 4, H * d)) == SHAPE   # heads of a row overlap
+    assert f(cu=M) == SHAPE                       # packed with a nonzero sequence stride
+    assert f(cu=M, qs=I3(0, d, H * d), ks=I3(0, d, H * d), total=-1) == SHAPE
+    assert f(cu=M + 8, qs=I3(0, d, H * d), ks=I3(0, d, H * d), total=100) == ALIGN
+    assert f(dt=0, d=128, w=3, qs=I3(n * H * 128, 128, H * 128), ks=I3(n * H * 128, 128, H * 128)) == UNSUP
+    assert f(out=K) == ALIAS
+    assert f(wsb=100) == WS
+    assert f(phi=7) == UNSUP
+    need = la.la_workspace_bytes(la.LA_OP_SEQS, B, H, H, n, d, la.LA_BF16, 0)
+    assert need > 256
+    assert f(wsb=need - 1) == WS
