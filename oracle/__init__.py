@@ -57,6 +57,8 @@ def _load():
         lib.lao_prefix_mask.argtypes = [P, P, P, I, P, I64, I64, I64, I64, I64, P, I64, P]
         lib.lao_window.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, I64, P, I64, P]
         lib.lao_window.restype = None
+        lib.lao_causal_backward.argtypes = [P, P, P, P, I, I, I64, I64, I64, I64, I64, P, P, P]
+        lib.lao_causal_backward.restype = None
         lib.lao_decode_step.argtypes = [P, P, P, I, I, I64, I64, I64, I64, P, P, P]
         for f in ("lao_forward", "lao_causal", "lao_prefix_mask", "lao_decode_step"):
             getattr(lib, f).restype = None
@@ -201,6 +203,25 @@ def window(q, k, v, w, rows=None, phi="relu1"):
     code = _phi(phi)
     _load().lao_window(_ptr(q), _ptr(k), _ptr(v), dt, code, B, Hq, Hkv, n, d, int(w), _ptr(r), nr, _ptr(out))
     return out
+
+
+def causal_backward(q, k, v, dout, phi="relu1"):
+    """Gradients (dq [B,Hq,n,d], dk, dv [B,Hkv,n,d], fp64) of the loss
+    sum(dout * out) of the causal normalised form.  phi: "relu1", "elu1" or
+    "features" (gradients with respect to the features themselves)."""
+    q, cq = _inp(q); k, ck = _inp(k); v, cv = _inp(v); dout, co = _inp(dout)
+    dt = _same_dtype(cq, ck, cv, co)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    _check_gqa(q.shape, k.shape, v.shape)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    _load().lao_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, _phi(phi), B, Hq, Hkv, n, d,
+                                _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv
 
 
 def prefix_mask(q, k, v, m, rows=None):

@@ -25,6 +25,10 @@
  *    cache token by token, linear in the number of generated tokens.
  *  - "LinearTile 1.0.1", section "Features": sliding-window attention (local
  *    context): query i sees only the last `window` keys, i - window < j <= i.
+ *  - "LinearTile 1.0.1", sections "Project Structure" and "Run Tests": a
+ *    backward kernel (core/kernels/backward.py) and its test: the gradients
+ *    of the causal form, differentiated here term by term from the pairwise
+ *    weights.
  *
  * Readings where the pages leave a step open:
  *  - no epsilon in the normaliser (relu + 1 >= 1 keeps the denominator >= 1;
@@ -206,6 +210,80 @@ void lao_window(const void* q, const void* k, const void* v, int dtype,
       }
       free(pq);
       free(pk);
+    }
+  }
+}
+
+/* phi'(x): relu + 1 -> 1 for x > 0 else 0; ELU + 1 -> 1 for x > 0 else e^x;
+ * features given directly -> 1. */
+static double dphi(double x, int kind) {
+  if (kind == LAO_PHI_FEATURES) return 1.0;
+  if (kind == LAO_PHI_ELU1) return x > 0.0 ? 1.0 : exp(x);
+  return x > 0.0 ? 1.0 : 0.0;
+}
+
+void lao_causal_backward(const void* q, const void* k, const void* v,
+                         const void* dout, int dtype, int phik, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
+                         double* dq, double* dk, double* dv) {
+  const int64_t R = Hq / Hkv;
+  if (dk) memset(dk, 0, (size_t)(B * Hkv * n * d) * sizeof(double));
+  if (dv) memset(dv, 0, (size_t)(B * Hkv * n * d) * sizeof(double));
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t g = 0; g < Hkv; ++g) {
+      double* pk = (double*)malloc((size_t)(n * d) * sizeof(double));
+      double* pq = (double*)malloc((size_t)(n * d) * sizeof(double));
+      double* D = (double*)malloc((size_t)n * sizeof(double));
+      double* o = (double*)malloc((size_t)(n * d) * sizeof(double));
+      double* gw = (double*)malloc((size_t)n * sizeof(double)); /* dL/dw_ij for one i */
+      const int64_t okv = off4(b, g, 0, Hkv, n, d);
+      for (int64_t e = 0; e < n * d; ++e) pk[e] = phi(rd(k, dtype, okv + e), phik);
+      for (int64_t h = g * R; h < (g + 1) * R; ++h) {
+        const int64_t oq = off4(b, h, 0, Hq, n, d);
+        for (int64_t e = 0; e < n * d; ++e) pq[e] = phi(rd(q, dtype, oq + e), phik);
+        /* the forward: D_i and out_i from the pairwise weights */
+        for (int64_t i = 0; i < n; ++i) {
+          double Di = 0.0;
+          for (int64_t c = 0; c < d; ++c) o[i * d + c] = 0.0;
+          for (int64_t j = 0; j <= i; ++j) {
+            double w = 0.0;
+            for (int64_t a = 0; a < d; ++a) w += pq[i * d + a] * pk[j * d + a];
+            Di += w;
+            for (int64_t c = 0; c < d; ++c) o[i * d + c] += w * rd(v, dtype, okv + j * d + c);
+          }
+          D[i] = Di;
+          for (int64_t c = 0; c < d; ++c) o[i * d + c] /= Di;
+        }
+        /* the gradients, query by query */
+        for (int64_t i = 0; i < n; ++i) {
+          double* dqi = dq ? dq + oq + i * d : NULL;
+          if (dqi)
+            for (int64_t a = 0; a < d; ++a) dqi[a] = 0.0;
+          for (int64_t j = 0; j <= i; ++j) {
+            double w = 0.0, gv = 0.0;
+            for (int64_t a = 0; a < d; ++a) w += pq[i * d + a] * pk[j * d + a];
+            for (int64_t c = 0; c < d; ++c)
+              gv += rd(dout, dtype, oq + i * d + c) * (rd(v, dtype, okv + j * d + c) - o[i * d + c]);
+            gw[j] = gv / D[i];
+            if (dqi)
+              for (int64_t a = 0; a < d; ++a) dqi[a] += gw[j] * pk[j * d + a];
+            if (dk)
+              for (int64_t a = 0; a < d; ++a) dk[okv + j * d + a] += gw[j] * pq[i * d + a];
+            if (dv)
+              for (int64_t c = 0; c < d; ++c) dv[okv + j * d + c] += w * rd(dout, dtype, oq + i * d + c) / D[i];
+          }
+          if (dqi)
+            for (int64_t a = 0; a < d; ++a) dqi[a] *= dphi(rd(q, dtype, oq + i * d + a), phik);
+        }
+      }
+      if (dk)
+        for (int64_t e = 0; e < n * d; ++e) dk[okv + e] *= dphi(rd(k, dtype, okv + e), phik);
+      free(pk);
+      free(pq);
+      free(D);
+      free(o);
+      free(gw);
     }
   }
 }

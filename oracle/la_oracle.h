@@ -69,6 +69,25 @@ void lao_window(const void* q, const void* k, const void* v, int dtype,
                 int64_t d, int64_t window, const int64_t* rows, int64_t nrows,
                 double* out);
 
+/* Gradients of the causal normalised form (the training step's backward;
+ * LinearTile 1.0.1, "Project Structure" / "Run Tests": a backward kernel and
+ * its test) for the loss L = sum_i dout_i . out_i: with weights
+ * w_ij = phi(Q_i) . phi(K_j) and D_i = sum_{j<=i} w_ij,
+ *   dV_j      = sum_{i>=j} w_ij dout_i / D_i
+ *   dL/dw_ij  = dout_i . (V_j - out_i) / D_i                 (j <= i)
+ *   dQ_i      = phi'(Q_i) * sum_{j<=i} dL/dw_ij phi(K_j)
+ *   dK_j      = phi'(K_j) * sum_{i>=j} dL/dw_ij phi(Q_i)
+ * summed over the query heads of a key/value head for dK, dV.  phi' of
+ * relu + 1 is 1 for x > 0 and 0 otherwise (0 at x = 0); of ELU + 1 it is 1 for
+ * x > 0 and e^x otherwise; with LAO_PHI_FEATURES the gradients are with
+ * respect to the features themselves.  Pairwise O(n^2 d) sums: the
+ * definition differentiated term by term, no state.  dq [B][Hq][n][d], dk,
+ * dv [B][Hkv][n][d]; any may be NULL. */
+void lao_causal_backward(const void* q, const void* k, const void* v,
+                         const void* dout, int dtype, int phik, int64_t B,
+                         int64_t Hq, int64_t Hkv, int64_t n, int64_t d,
+                         double* dq, double* dk, double* dv);
+
 /* Unnormalised prefix-mask form, identity feature map: query i of batch b
  * sees keys 0..m[b * m_bstride + i], each in [0, n); m_bstride = 0 shares one
  * mask [n] among the batches, m_bstride = n gives each its own ([B][n]).

@@ -576,3 +576,87 @@ def test_window_gqa_equals_repeated_kv_heads():
     q, k, v, _ = li.qkv(2, 6, 2, 23, 3, li.F32, seed=25)
     rep = lambda x: np.repeat(x, 3, axis=1)
     assert np.array_equal(oracle.window(q, k, v, 5), oracle.window(q, rep(k), rep(v), 5))
+
+
+# ---------------------------------------------------------------------------
+# Gradients of the causal form (LinearTile 1.0.1, "Project Structure" /
+# "Run Tests": backward).  Pinned by central finite differences of the
+# forward oracle in fp64, by float64 autograd through a plain torch
+# transcription of the forward, and by special cases: d = 1 (the output does
+# not depend on Q, so dQ = 0), dV does not depend on V, features mode equals
+# relu + 1 where phi' = 1, GQA = repeated heads with dK, dV summed.
+# ---------------------------------------------------------------------------
+def _away_from_zero(rng, shape, lo=0.05):
+    x = rng.standard_normal(size=shape)
+    return np.where(np.abs(x) < lo, np.sign(x + 1e-12) * lo, x)  # no element at relu's kink
+
+
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 6, 3), (1, 2, 1, 5, 2), (2, 2, 2, 4, 4)])
+def test_backward_matches_finite_differences(phi, shape):
+    B, Hq, Hkv, n, d = shape
+    rng = np.random.default_rng(40)
+    q = _away_from_zero(rng, (B, Hq, n, d))
+    k = _away_from_zero(rng, (B, Hkv, n, d))
+    v = rng.standard_normal((B, Hkv, n, d))
+    dout = rng.standard_normal((B, Hq, n, d))
+    dq, dk, dv = oracle.causal_backward(q, k, v, dout, phi=phi)
+    loss = lambda q_, k_, v_: float((oracle.causal(q_, k_, v_, phi=phi) * dout).sum())
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = loss(q, k, v)
+            x[idx] = x0 - eps
+            lm = loss(q, k, v)
+            x[idx] = x0
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert np.allclose(g, fd, rtol=1e-6, atol=1e-8), np.abs(g - fd).max()
+
+
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+def test_backward_matches_float64_autograd(phi):
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, n, d = 2, 4, 2, 37, 8
+    rng = np.random.default_rng(41)
+    q, k, v, dout = (rng.standard_normal(s) for s in ((B, Hq, n, d), (B, Hkv, n, d), (B, Hkv, n, d), (B, Hq, n, d)))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    f = (lambda x: torch.relu(x) + 1) if phi == "relu1" else (lambda x: torch.nn.functional.elu(x) + 1)
+    R = Hq // Hkv
+    kk, vv = tk.repeat_interleave(R, dim=1), tv.repeat_interleave(R, dim=1)
+    w = torch.tril(f(tq) @ f(kk).transpose(-1, -2))
+    out = (w @ vv) / w.sum(-1, keepdim=True)
+    (out * torch.tensor(dout)).sum().backward()
+    dq, dk, dv = oracle.causal_backward(q, k, v, dout, phi=phi)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.allclose(mine, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_special_cases():
+    rng = np.random.default_rng(42)
+    B, Hq, Hkv, n = 1, 2, 1, 20
+    # d = 1: phi(q) cancels in the output, so dQ = 0 exactly
+    q, k, v, dout = (rng.standard_normal(s) for s in ((B, Hq, n, 1), (B, Hkv, n, 1), (B, Hkv, n, 1), (B, Hq, n, 1)))
+    dq, _, _ = oracle.causal_backward(q, k, v, dout)
+    assert np.abs(dq).max() < 1e-12
+    # dV does not depend on V
+    d = 5
+    q, k, v, v2, dout = (rng.standard_normal(s) for s in ((B, Hq, n, d), (B, Hkv, n, d), (B, Hkv, n, d),
+                                                          (B, Hkv, n, d), (B, Hq, n, d)))
+    assert np.allclose(oracle.causal_backward(q, k, v, dout)[2], oracle.causal_backward(q, k, v2, dout)[2],
+                       rtol=1e-13, atol=1e-14)
+    # features mode on phi(x) = x + 1 (x > 0) equals relu + 1 on x (phi' = 1 there)
+    qp, kp = np.abs(q) + 0.1, np.abs(k) + 0.1
+    a = oracle.causal_backward(qp, kp, v, dout)
+    b = oracle.causal_backward(qp + 1.0, kp + 1.0, v, dout, phi="features")
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=1e-12, atol=1e-13)
+    # GQA: repeated key/value heads, dK and dV summed over the repeats
+    rep = lambda x: np.repeat(x, 2, axis=1)
+    g1 = oracle.causal_backward(q, k, v, dout)
+    g2 = oracle.causal_backward(q, rep(k), rep(v), dout)
+    assert np.allclose(g1[0], g2[0], rtol=1e-13, atol=1e-14)
+    for i in (1, 2):
+        assert np.allclose(g1[i], g2[i].reshape(B, Hkv, 2, n, d).sum(axis=2), rtol=1e-12, atol=1e-13)
