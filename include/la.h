@@ -105,7 +105,7 @@ enum { LA_PHI_RELU1 = 0, LA_PHI_ELU1 = 1, LA_PHI_FEATURES = 2 };
 
 /* Operation codes for la_workspace_bytes. */
 enum { LA_OP_FORWARD = 0, LA_OP_CAUSAL = 1, LA_OP_PREFIX_MASK = 2, LA_OP_PREFIX_MASK_BATCHED = 3,
-       LA_OP_SEQS = 4 };
+       LA_OP_SEQS = 4, LA_OP_CAUSAL_BACKWARD = 5 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* la_status_str(la_status s);
@@ -264,6 +264,29 @@ la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
                                     la_phi phi, int64_t window, void* out,
                                     float* S_final, float* z_final, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/* Gradients of the causal normalised form (LinearTile 1.0.1, "Project
+ * Structure" and "Run Tests": the backward kernel of the training step) for
+ * the loss L = sum_i dout_i . out_i, out as la_causal_forward_phi computes
+ * it from q, k, v (recomputed here: nothing of the forward pass is kept):
+ *   dq = dL/dq [B][Hq][n][d], dk = dL/dk and dv = dL/dv [B][Hkv][n][d], in
+ *   dtype (dk and dv summed over the query heads of each key/value head).
+ * With g_i = dout_i / den_i and beta_i = -(dout_i . out_i) / den_i:
+ *   dphi(Q_i) = S_i g_i + beta_i z_i, dphi(K_j) = U_j V_j + u_j,
+ *   dV_j = U_j^T phi(K_j), U_j = sum_{i>=j} phi(Q_i) g_i^T, u_j = sum_{i>=j}
+ *   beta_i phi(Q_i); dq = dphi(Q) * phi'(q), dk = dphi(K) * phi'(k), with
+ *   phi'(x) = 1 for x > 0 and 0 (relu + 1) or e^x (ELU + 1) otherwise, and
+ *   1 for LA_PHI_FEATURES (gradients with respect to the features given).
+ * phi is the map of the forward; ws: la_workspace_bytes(
+ * LA_OP_CAUSAL_BACKWARD, B, Hq, Hkv, n, d, dtype, 0) bytes.  Offered for
+ * d <= 64 (LA_ERR_UNSUPPORTED otherwise).  The gradient buffers must not
+ * overlap each other or the inputs. */
+la_status la_causal_backward(const void* q, const void* k, const void* v,
+                             const void* dout, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t n, int64_t d,
+                             la_dtype dtype, la_phi phi, void* dq, void* dk,
+                             void* dv, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* One recurrent decode step (trim-transformer 0.1.0, "Key-value caching":
  * use and update the cache in one call).  For every (b, kv head g):

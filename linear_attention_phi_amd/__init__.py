@@ -14,6 +14,8 @@ Functions carry the C names:
   la_decode_step(q, k, v, S, z)              one recurrent step (S, z in place)
   la_window_forward(q, k, v, window)         sliding window: keys i - window < j <= i
   la_causal_forward_noalloc(q, k, v)         la_causal_forward on the static scratch
+  la_causal_forward_strided(q, k, v, ...)    causal / window form on strided or packed sequences
+  la_causal_backward(q, k, v, dout)          gradients of the causal form
   (la_forward, la_causal_forward and la_decode_step take phi="relu1",
   phi="elu1" or phi="features" -- q and k then hold phi(Q) and phi(K) of a
   positive map the caller applied; the last two call la_forward_phi /
@@ -45,6 +47,7 @@ LIB_PATH = os.path.join(_HERE, "liblaphi.so")
 
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK, LA_OP_PREFIX_MASK_BATCHED, LA_OP_SEQS = 0, 1, 2, 3, 4
+LA_OP_CAUSAL_BACKWARD = 5
 LA_PHI_RELU1, LA_PHI_ELU1, LA_PHI_FEATURES = 0, 1, 2
 _PHI = {"relu1": LA_PHI_RELU1, "elu1": LA_PHI_ELU1, "features": LA_PHI_FEATURES}
 
@@ -97,10 +100,12 @@ def load():
         lib.la_window_forward.argtypes = [P, P, P, I64, I64, I64, I64, I64, I32, I32, I64, P, P]
         lib.la_causal_forward_strided.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, I32, I32, I64,
                                                   P, P, P, P, SZ, P]
+        lib.la_causal_backward.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I32, I32, P, P, P, P, SZ, P]
         for f in ("la_forward", "la_causal_forward", "la_prefix_mask_forward", "la_decode_step",
                   "la_forward_phi", "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
                   "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
-                  "la_causal_forward_noalloc", "la_window_forward", "la_causal_forward_strided"):
+                  "la_causal_forward_noalloc", "la_window_forward", "la_causal_forward_strided",
+                  "la_causal_backward"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -409,6 +414,26 @@ def la_causal_forward_strided(q, k, v, cu_seqlens=None, max_len=None, window=0, 
     if q is None:
         return S_final, z_final
     return (out, S_final, z_final) if want_state else out
+
+
+def la_causal_backward(q, k, v, dout, ws=None, phi="relu1"):
+    """Gradients (dq, dk, dv) of sum(dout * la_causal_forward(q, k, v, phi=phi));
+    the forward is recomputed.  Contiguous [B, H, n, d] tensors, d <= 64."""
+    phi_code = _phi(phi)
+    torch = _torch()
+    B, Hq, Hkv, n, d = _qkv(q, k, v)
+    _expect(dout, q.shape, q.dtype, "dout")
+    dt = _dtype_code(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = la_workspace_bytes(LA_OP_CAUSAL_BACKWARD, B, Hq, Hkv, n, d, dt, 0)
+    if need == 0:
+        raise LAError(4, f"la_causal_backward (d={d}, dtype={q.dtype})")
+    ws = workspace(need, q.device) if ws is None else ws
+    _call(load().la_causal_backward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(dout, "dout"), B, Hq, Hkv, n, d,
+                                    dt, phi_code, _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _dev(ws, "ws"),
+                                    ws.numel(), _stream(q)), "la_causal_backward")
+    _debug_check(ws, "la_causal_backward")
+    return dq, dk, dv
 
 
 def la_prefix_mask_forward(q, k, v, m, chunk=0, out=None, ws=None):

@@ -179,6 +179,13 @@ static int32_t prefix_chunk(bool take, int32_t chunk, la_dtype dtype, int64_t d)
 
 size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, int64_t d, la_dtype dtype,
                           int32_t chunk) {
+  if (op == LA_OP_CAUSAL_BACKWARD) {
+    if (check_sizes(B, Hq, Hkv, n, d, dtype) != LA_OK) return 0;
+    BwdCall a{};
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.d = d; a.dtype = (int)dtype;
+    const size_t b = backward_ws_bytes(a);
+    return b ? kCtlBytes + b : 0;
+  }
   if (op == LA_OP_SEQS) {  // la_causal_forward_strided: B sequences of length at most n
     if (check_sizes(B, Hq, Hkv, n, d, dtype) != LA_OK) return 0;
     const int C = seq_chunk(elem_bytes(dtype), padded_dim(d), false);
@@ -426,6 +433,42 @@ la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
   a.ctl = reinterpret_cast<Ctl*>(ws);
   a.ws = reinterpret_cast<char*>(ws) + kCtlBytes;
   return launch_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_causal_backward(const void* q, const void* k, const void* v, const void* dout, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t n, int64_t d, la_dtype dtype, la_phi phi, void* dq, void* dk,
+                             void* dv, void* ws, size_t ws_bytes, void* stream) {
+  la_status st = check_sizes(B, Hq, Hkv, n, d, dtype);
+  if (st != LA_OK) return st;
+  if (phi != LA_PHI_RELU1 && phi != LA_PHI_ELU1 && phi != LA_PHI_FEATURES) return LA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return LA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return LA_ERR_ALIGN;
+  const size_t eb = elem_bytes(dtype);
+  if (backward_chunk((int)eb, padded_dim(d)) == 0) return LA_ERR_UNSUPPORTED;
+  const size_t qb = (size_t)(B * Hq * n * d) * eb, kvb = (size_t)(B * Hkv * n * d) * eb;
+  const void* ins[4] = {q, k, v, dout};
+  const size_t inb[4] = {qb, kvb, kvb, qb};
+  const void* outs[3] = {dq, dk, dv};
+  const size_t outb[3] = {qb, kvb, kvb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[o], outb[o], ins[i], inb[i])) return LA_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], outb[o], outs[o2], outb[o2])) return LA_ERR_ALIAS;
+  }
+  BwdCall a{q, k, v, dout, dq, dk, dv, B, Hq, Hkv, n, d, (int)dtype, (int)phi, nullptr, stream};
+  const size_t need = kCtlBytes + backward_ws_bytes(a);
+  const int C = backward_chunk((int)eb, padded_dim(d));
+  if (B * Hkv * seq_plan(backward_seqcall(a), C).nseg >= kMaxGrid) return LA_ERR_SHAPE;
+  if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(ws, need, ins[i], inb[i])) return LA_ERR_ALIAS;
+  for (int o = 0; o < 3; ++o)
+    if (overlaps(ws, need, outs[o], outb[o])) return LA_ERR_ALIAS;
+  a.ws = reinterpret_cast<char*>(ws) + kCtlBytes;
+  return launch_backward(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 
 la_status la_decode_step_phi(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv,

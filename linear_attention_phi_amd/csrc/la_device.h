@@ -267,6 +267,80 @@ __device__ __forceinline__ void tile_store(const TileRaw<T, DP, C>& t, int nvali
   }
 }
 
+// Copy ROWS rows x DP features of T (row stride ld elements, row0 first)
+// into LDS tiles of TT: tm[row * ldt + col] transformed by TMX and/or
+// fm[col * ldf + row] transformed by FMX.  Rows at or past nvalid and
+// features at or past d are stored as 0 (not phi(0)).  vec: d == DP and
+// 16-byte rows, 16-byte pieces.  TT may be wider than T (bf16 rows widened
+// exactly into fp32 tiles).
+template <typename T, typename TT, int DP, int ROWS, int TMX, int FMX>
+__device__ __forceinline__ void stage(const T* __restrict__ base, int64_t ld, int64_t row0, int nvalid, int d,
+                                      bool vec, TT* tm, int ldt, TT* fm, int ldf, int tid) {
+  if (vec) {
+    constexpr int EPP = 16 / (int)sizeof(T);
+    constexpr int PPR = DP / EPP;
+    constexpr int NP = ROWS * PPR;
+    constexpr int PER = (NP + NT - 1) / NT;
+    constexpr int PIECES = EPP * (int)sizeof(TT) / 8;  // 8-byte stores per row piece of the tile
+    union V { uint4 u; T e[EPP]; };
+    union W { uint2 u[PIECES]; TT e[EPP]; };
+    V raw[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {  // every load first
+      const int p = tid + k * NT;
+      const int row = p / PPR, col = (p % PPR) * EPP;
+      raw[k].u = make_uint4(0, 0, 0, 0);
+      if (p < NP && row < nvalid) raw[k].u = *reinterpret_cast<const uint4*>(base + (row0 + row) * ld + col);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int p = tid + k * NT;
+      if (p >= NP) break;
+      const int row = p / PPR, col = (p % PPR) * EPP;
+      W a, b;
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) {
+        const float x = to_f(raw[k].e[e]);
+        a.e[e] = row < nvalid ? cvt<TT>(xform<TMX>(x)) : cvt<TT>(0.0f);
+        b.e[e] = row < nvalid ? cvt<TT>(xform<FMX>(x)) : cvt<TT>(0.0f);
+      }
+      if (TMX != XF_NONE) {
+        uint2* dst = reinterpret_cast<uint2*>(tm + row * ldt + col);  // rows of ldt elements are 8-byte aligned
+#pragma unroll
+        for (int q = 0; q < PIECES; ++q) dst[q] = a.u[q];
+      }
+      if (FMX != XF_NONE) {
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) fm[(col + e) * ldf + row] = b.e[e];
+      }
+    }
+  } else {
+    for (int idx = tid; idx < ROWS * DP; idx += NT) {
+      const int row = idx / DP, col = idx % DP;
+      const bool ok = row < nvalid && col < d;
+      const float x = ok ? to_f(base[(row0 + row) * ld + col]) : 0.0f;
+      if (TMX != XF_NONE) tm[row * ldt + col] = cvt<TT>(ok ? xform<TMX>(x) : 0.0f);
+      if (FMX != XF_NONE) fm[col * ldf + row] = cvt<TT>(ok ? xform<FMX>(x) : 0.0f);
+    }
+  }
+}
+
+// Rows of chunk x of a sequence of n tokens (0 for x < 0 or past the end).
+__device__ __forceinline__ int chunk_rows(int64_t x, int C, int64_t n) {
+  if (x < 0) return 0;
+  const int64_t r = n - x * C;
+  return r <= 0 ? 0 : (r < C ? (int)r : C);
+}
+
+// Write an accumulator block (rows m, columns n) to X[m][n] in LDS, rounded
+// to T (not transposed: 16 element stores per lane).
+template <typename T>
+__device__ __forceinline__ void st_acc(T* X, int ldx, const f32x16& acc, int lane) {
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) X[(8 * (r >> 2) + 4 * h + (r & 3)) * ldx + n] = cvt<T>(acc[r]);
+}
+
 // Sum of the C entries of LDS row r (stride C+PAD), in order.
 template <typename T, int C>
 __device__ __forceinline__ float row_sum(const T* X, int r) {

@@ -147,6 +147,23 @@ struct SeqCall {
 int seq_chunk(int elem_bytes, int DP, bool window);
 Plan seq_plan(const SeqCall& a, int C);
 int launch_seq(const SeqCall& a);
+// The causal form's state pass and scan alone, for chunk C (bf16 or fp32,
+// d <= 64): a.ws receives the exclusive prefix slots of seq_plan(a, C).
+int launch_seq_prefix(const SeqCall& a, int C);
+// Gradients of the causal form (la_backward.hip): contiguous [B, H, n, d],
+// d <= 64.  backward_chunk is 0 where the tiles do not fit in LDS.
+struct BwdCall {
+  const void* q; const void* k; const void* v; const void* dout;
+  void* dq; void* dk; void* dv;
+  int64_t B, Hq, Hkv, n, d;
+  int dtype, phi;
+  void* ws;  // the data regions past the control block
+  void* stream;
+};
+int backward_chunk(int elem_bytes, int DP);
+SeqCall backward_seqcall(const BwdCall& a);
+size_t backward_ws_bytes(const BwdCall& a);
+int launch_backward(const BwdCall& a);
 // k_scan over (nseg + 1) slots per unit, F = 1 (la_kernels.hip).
 int launch_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S_final, float* z_final,
                 void* stream);

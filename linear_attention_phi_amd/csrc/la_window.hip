@@ -58,67 +58,6 @@ namespace {
 using namespace la_dev;
 using la_internal::Seqs;
 
-// Copy ROWS rows x DP features (row stride ld elements, row0 first) into
-// LDS: tm[row * ldt + col] transformed by TMX and/or fm[col * ldf + row]
-// transformed by FMX.  Rows at or past nvalid and features at or past d are
-// stored as 0 (not phi(0)).  vec: d == DP and 16-byte rows, 16-byte pieces.
-template <typename T, int DP, int ROWS, int TMX, int FMX>
-__device__ __forceinline__ void stage(const T* __restrict__ base, int64_t ld, int64_t row0, int nvalid, int d,
-                                      bool vec, T* tm, int ldt, T* fm, int ldf, int tid) {
-  if (vec) {
-    constexpr int EPP = 16 / (int)sizeof(T);
-    constexpr int PPR = DP / EPP;
-    constexpr int NP = ROWS * PPR;
-    constexpr int PER = (NP + NT - 1) / NT;
-    union V { uint4 u; T e[EPP]; };
-    V raw[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {  // every load first
-      const int p = tid + k * NT;
-      const int row = p / PPR, col = (p % PPR) * EPP;
-      raw[k].u = make_uint4(0, 0, 0, 0);
-      if (p < NP && row < nvalid) raw[k].u = *reinterpret_cast<const uint4*>(base + (row0 + row) * ld + col);
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int p = tid + k * NT;
-      if (p >= NP) break;
-      const int row = p / PPR, col = (p % PPR) * EPP;
-      V a, b;
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) {
-        const float x = to_f(raw[k].e[e]);
-        a.e[e] = row < nvalid ? cvt<T>(xform<TMX>(x)) : cvt<T>(0.0f);
-        b.e[e] = row < nvalid ? cvt<T>(xform<FMX>(x)) : cvt<T>(0.0f);
-      }
-      if (TMX != XF_NONE) {
-        T* dst = tm + row * ldt + col;  // rows of ldt elements are 8-byte aligned
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(a.u.x, a.u.y);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(a.u.z, a.u.w);
-      }
-      if (FMX != XF_NONE) {
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) fm[(col + e) * ldf + row] = b.e[e];
-      }
-    }
-  } else {
-    for (int idx = tid; idx < ROWS * DP; idx += NT) {
-      const int row = idx / DP, col = idx % DP;
-      const bool ok = row < nvalid && col < d;
-      const float x = ok ? to_f(base[(row0 + row) * ld + col]) : 0.0f;
-      if (TMX != XF_NONE) tm[row * ldt + col] = cvt<T>(ok ? xform<TMX>(x) : 0.0f);
-      if (FMX != XF_NONE) fm[col * ldf + row] = cvt<T>(ok ? xform<FMX>(x) : 0.0f);
-    }
-  }
-}
-
-// Rows of chunk x of a sequence of n tokens (0 for x < 0 or past the end).
-__device__ __forceinline__ int chunk_rows(int64_t x, int C, int64_t n) {
-  if (x < 0) return 0;
-  const int64_t r = n - x * C;
-  return r <= 0 ? 0 : (r < C ? (int)r : C);
-}
-
 // Sequence s of the table: its first token and its length (0, with the
 // error recorded, if the table is inconsistent).
 struct SeqSpan {
@@ -186,12 +125,13 @@ struct WinState {
 // Causal form's state pass: the segment's chunk states summed (S row-major,
 // then z: the slot layout of k_scan), zeros for segments past a sequence's
 // end.
-template <typename T, int DP, int C, int PM>
+// TT: the tile type (T, or fp32 for the backward's fp32 prefixes of bf16 rows).
+template <typename T, int DP, int C, int PM, typename TT = T>
 __global__ __launch_bounds__(NT) void k_wstate(WinArgs A) {
   constexpr int LC = C + PAD;
   constexpr int PX = q_xform<PM>();
-  __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
-  __shared__ __attribute__((aligned(16))) T sVT[DP * LC];
+  __shared__ __attribute__((aligned(16))) TT sKT[DP * LC];
+  __shared__ __attribute__((aligned(16))) TT sVT[DP * LC];
   using SB = StateBlocks<DP>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t u = blockIdx.x / A.nseg, seg = blockIdx.x % A.nseg;
@@ -201,12 +141,12 @@ __global__ __launch_bounds__(NT) void k_wstate(WinArgs A) {
   const T* vb = reinterpret_cast<const T*>(A.v) + sq * A.S.kb + sp.start * A.S.kt + g * A.S.kh;
   const int64_t nch = (sp.len + C - 1) / C;
   const int64_t c0 = seg * A.G, c1 = (c0 + A.G < nch) ? c0 + A.G : nch;
-  WinState<T, DP, C> W;
+  WinState<TT, DP, C> W;
   W.clear();
   for (int64_t c = c0; c < c1; ++c) {
     const int nv = chunk_rows(c, C, sp.len);
-    stage<T, DP, C, XF_NONE, PX>(kb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sKT, LC, tid);
-    stage<T, DP, C, XF_NONE, XF_ID>(vb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sVT, LC, tid);
+    stage<T, TT, DP, C, XF_NONE, PX>(kb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sKT, LC, tid);
+    stage<T, TT, DP, C, XF_NONE, XF_ID>(vb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sVT, LC, tid);
     __syncthreads();
     W.add(sKT, LC, sVT, LC, false, w, lane, tid);
     __syncthreads();
@@ -272,8 +212,8 @@ __global__ __launch_bounds__(NT) void k_window(WinArgs A) {
     W.clear();
     for (int64_t x = (c0 - nfull - 1 > 0 ? c0 - nfull - 1 : 0); nfull > 0 && x < c0; ++x) {
       const int nvx = chunk_rows(x, C, n);
-      stage<T, DP, C, XF_NONE, PX>(kb, kt, x * C, nvx, d, vec, nullptr, 0, sKT, LC, tid);
-      stage<T, DP, C, XF_NONE, XF_ID>(vb, kt, x * C, nvx, d, vec, nullptr, 0, sVT, LC, tid);
+      stage<T, T, DP, C, XF_NONE, PX>(kb, kt, x * C, nvx, d, vec, nullptr, 0, sKT, LC, tid);
+      stage<T, T, DP, C, XF_NONE, XF_ID>(vb, kt, x * C, nvx, d, vec, nullptr, 0, sVT, LC, tid);
       __syncthreads();
       W.add(sKT, LC, sVT, LC, false, w, lane, tid);
       __syncthreads();
@@ -306,16 +246,16 @@ __global__ __launch_bounds__(NT) void k_window(WinArgs A) {
     const int nv = chunk_rows(c, C, n);
     // leading chunk: phi(K) token- and feature-major, V feature-major;
     // trailing tile: chunks ce - 2 and ce - 1 (phi(K) both ways, V feature-major)
-    stage<T, DP, C, PX, PX>(kb, kt, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
-    stage<T, DP, C, XF_NONE, XF_ID>(vb, kt, t0, nv, d, vec, nullptr, 0, sVT, LC, tid);
+    stage<T, T, DP, C, PX, PX>(kb, kt, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
+    stage<T, T, DP, C, XF_NONE, XF_ID>(vb, kt, t0, nv, d, vec, nullptr, 0, sVT, LC, tid);
     if (WIN) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int64_t x = ce - 2 + half;
         const int nvx = chunk_rows(x, C, n);
         const int64_t r0 = x < 0 ? 0 : x * C;
-        stage<T, DP, C, PX, PX>(kb, kt, r0, nvx, d, vec, sKtr + half * C * LQ, LQ, sKTtr + half * C, LC2, tid);
-        stage<T, DP, C, XF_NONE, XF_ID>(vb, kt, r0, nvx, d, vec, nullptr, 0, sVTtr + half * C, LC2, tid);
+        stage<T, T, DP, C, PX, PX>(kb, kt, r0, nvx, d, vec, sKtr + half * C * LQ, LQ, sKTtr + half * C, LC2, tid);
+        stage<T, T, DP, C, XF_NONE, XF_ID>(vb, kt, r0, nvx, d, vec, nullptr, 0, sVTtr + half * C, LC2, tid);
       }
       if (nfull > 0) {  // W loses chunk ce - 1, which has left the chunks inside every window
         __syncthreads();
@@ -339,7 +279,7 @@ __global__ __launch_bounds__(NT) void k_window(WinArgs A) {
       const int64_t hq = g * R + r;
       const T* qh = reinterpret_cast<const T*>(A.q) + sq * A.S.qb + sp.start * qt + hq * A.S.qh;
       __syncthreads();  // the tiles above are written; the previous head is done with sQ, sP, sPtr
-      stage<T, DP, C, PX, XF_NONE>(qh, qt, t0, nv, d, vec, sQ, LQ, nullptr, 0, tid);
+      stage<T, T, DP, C, PX, XF_NONE>(qh, qt, t0, nv, d, vec, sQ, LQ, nullptr, 0, tid);
       __syncthreads();
 
       // ---- scores: chunk c (keys i - w < j <= i) into sP[i][j]; the trailing
@@ -527,6 +467,40 @@ Plan seq_plan(const SeqCall& a, int C) {
   p.G = G;
   p.nseg = (p.nchunks + G - 1) / G;
   return p;
+}
+
+// The causal state pass and scan alone for chunk C (the backward's first
+// pass, on fp32 tiles whatever the input type): a.ws receives the exclusive
+// prefix slots of seq_plan(a, C).
+template <typename T, int DP, int C>
+int run_seq_prefix(const SeqCall& a) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const Plan p = seq_plan(a, C);
+  WinArgs A{a.q, a.k, a.v, a.out, a.S, (int)a.d, (int)(a.Hq / a.Hkv), a.Hkv, p.G, p.nseg, 0, 0, 0,
+            a.vec, reinterpret_cast<float*>(a.ws), a.ctl};
+  const dim3 grid((unsigned)(a.nseq * a.Hkv * p.nseg));
+  if (a.phi == 1)
+    k_wstate<T, DP, C, PM_ELU1, float><<<grid, NT, 0, st>>>(A);
+  else if (a.phi == 2)
+    k_wstate<T, DP, C, PM_FEAT, float><<<grid, NT, 0, st>>>(A);
+  else
+    k_wstate<T, DP, C, PM_RELU1, float><<<grid, NT, 0, st>>>(A);
+  return launch_scan(A.states, a.nseq * a.Hkv, p.nseg, DP, (int)a.d, nullptr, nullptr, a.stream);
+}
+
+int launch_seq_prefix(const SeqCall& a, int C) {
+  const int DP = padded_dim(a.d);
+#define LA_PFX(TT, DD, CC) \
+  if (DP == DD && C == CC) return run_seq_prefix<TT, DD, CC>(a);
+  if (a.dtype == 0) {
+    LA_PFX(float, 32, 64)
+    LA_PFX(float, 64, 32)
+  } else {
+    LA_PFX(bf16, 32, 64)
+    LA_PFX(bf16, 64, 32)
+  }
+#undef LA_PFX
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_seq(const SeqCall& a) {

@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "la_prefix_mask_forward", "la_decode_step", "la_forward_phi",
                           "la_causal_forward_phi", "la_decode_step_phi", "la_prefix_mask_forward_batched",
                           "la_workspace_init", "la_workspace_status", "la_workspace_set_wait",
-                          "la_causal_forward_noalloc", "la_window_forward", "la_causal_forward_strided"}
+                          "la_causal_forward_noalloc", "la_window_forward", "la_causal_forward_strided",
+                          "la_causal_backward"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -297,3 +298,26 @@ def test_strided_rejections(lib):
     need = la.la_workspace_bytes(la.LA_OP_SEQS, B, H, H, n, d, la.LA_BF16, 0)
     assert need > 256
     assert f(wsb=need - 1) == WS
+
+
+def test_backward_rejections(lib):
+    """la_causal_backward: every check on the host, nothing launched."""
+    DQ, DK, DV, DO = (0x10000000 * (i + 20) for i in range(4))
+
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, do=DO, B=1, Hq=2, Hkv=1, n=16, d=16, dt=1, phi=0, dq=DQ, dk=DK, dv=DV, ws=WSP,
+                 wsb=BIG)
+        a.update(kw)
+        return lib.la_causal_backward(a["q"], a["k"], a["v"], a["do"], a["B"], a["Hq"], a["Hkv"], a["n"], a["d"],
+                                      a["dt"], a["phi"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+    assert f(do=None) == NULL
+    assert f(dv=None) == NULL
+    assert f(d=128) == UNSUP          # d > 64
+    assert f(phi=4) == UNSUP
+    assert f(Hq=3, Hkv=2) == SHAPE
+    assert f(dq=Q) == ALIAS
+    assert f(dk=DV) == ALIAS
+    assert f(dk=K + 8) == ALIGN
+    assert f(wsb=64) == WS
+    assert la.la_workspace_bytes(la.LA_OP_CAUSAL_BACKWARD, 8, 8, 8, 2048, 64, la.LA_BF16, 0) > 256
+    assert la.la_workspace_bytes(la.LA_OP_CAUSAL_BACKWARD, 1, 1, 1, 16, 128, la.LA_BF16, 0) == 0
