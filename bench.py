@@ -66,6 +66,14 @@ WORKLOADS = {
                         phi="elu1"),
     "gqa_elu": dict(form="causal", B=1, Hq=32, Hkv=8, n=65536, d=128, dt="bf16", chunk=0, scaled=True, steps=20,
                     phi="elu1"),
+    # the next rows: sliding window, strided and packed sequences, a feature
+    # map of the caller's choice, the backward
+    "window": dict(form="window", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", window=512, scaled=True, steps=200),
+    "causal_bnhd": dict(form="strided", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", scaled=True, steps=200),
+    "varlen": dict(form="varlen", B=16, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", scaled=True, steps=200),
+    "causal_features": dict(form="causal", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", chunk=64, scaled=True,
+                            steps=200, phi="features"),
+    "backward": dict(form="backward", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", scaled=True, steps=50),
 }
 
 DESCRIPTIONS = {
@@ -80,7 +88,22 @@ DESCRIPTIONS = {
     "causal_elu": "causal normalised linear attention, phi=ELU+1, bf16 in, fp32 state",
     "forward_elu": "non-causal normalised linear attention, phi=ELU+1, bf16 in, fp32 accumulation",
     "gqa_elu": "long-context GQA causal normalised linear attention, phi=ELU+1, bf16 in, fp32 state",
+    "window": "sliding-window (512 keys) causal normalised linear attention, phi=relu+1, bf16 in, fp32 state",
+    "causal_bnhd": "causal normalised linear attention on [batch, seq, heads, d] rows (strided), bf16",
+    "varlen": "causal normalised linear attention on 16 packed sequences of 128..2048 tokens (cu_seqlens), bf16",
+    "causal_features": "causal normalised linear attention on caller-applied features (softplus), bf16",
+    "backward": "gradients dQ, dK, dV of the causal form (phi=relu+1), bf16 in, fp32 products",
 }
+
+# The packed-sequence workload's lengths: 16 sequences drawn uniformly from
+# 128 .. 2048 tokens (seed 0); the pages give no length mix.
+VARLEN_SEED = 0
+
+
+def varlen_lengths(w):
+    import numpy as np
+
+    return np.random.default_rng(VARLEN_SEED).integers(128, w["n"] + 1, size=w["B"])
 
 
 def elem_bytes(dt):
@@ -90,6 +113,12 @@ def elem_bytes(dt):
 def algorithmic_bytes(w):
     """Bytes the method must move per call: inputs read once, outputs written once."""
     e = elem_bytes(w["dt"])
+    if w["form"] == "varlen":
+        T = int(varlen_lengths(w).sum())
+        return (2 * w["Hq"] + 2 * w["Hkv"]) * T * w["d"] * e + 8 * (w["B"] + 1)
+    if w["form"] == "backward":  # q, k, v, dO read; dq, dk, dv written
+        B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
+        return (3 * B * Hq * n * d + 4 * B * Hkv * n * d) * e
     if w["form"] == "decode":
         B, Hq, Hkv, d = w["B"], w["Hq"], w["Hkv"], w["d"]
         return 2 * B * Hkv * (d * d + d) * 4 + B * (2 * Hq + 2 * Hkv) * d * e
@@ -106,6 +135,13 @@ def algorithmic_flops(w):
     B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
     if w["form"] == "forward":
         return 2 * (B * Hkv * n * d * d + B * Hq * n * d * d)
+    if w["form"] == "backward":
+        # per token and head, at chunk C = 32 (the backward's fp32 tiles): six
+        # d x d state products (phi(q) S, S g, U v, U^T phi(k), dS, dU) and six
+        # C-long intra-chunk ones (P, P V, A, A phi(K), A^T phi(Q), P^T G)
+        return 2 * B * Hq * n * 6 * (d * d + 32 * d)
+    if w["form"] == "varlen":
+        n = int(varlen_lengths(w).sum()) // B  # mean length: the products scale with the tokens
     C = w.get("chunk") or 64
     # state build per KV head; per query head phi(Q) S_prev, the masked C x C
     # score block and its product with V
@@ -163,6 +199,8 @@ def counter_traffic(name):
 def tokens_heads(w):
     if w["form"] == "decode":
         return w["B"] * w["Hq"]
+    if w["form"] == "varlen":
+        return int(varlen_lengths(w).sum()) * w["Hq"]
     return w["B"] * w["Hq"] * w["n"]
 
 
@@ -210,9 +248,22 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
         per = B * Hq * n_s
         what = f"the first {n_s} tokens of all {Hq} query heads (causal, d={d})"
         cores = min(threads, B * Hkv)
+    elif form == "backward":
+        bs = 1
+        do = li.gaussian(np.random.default_rng(5), q.shape, None, li.BF16 if q.dtype == np.uint16 else li.F32)
+
+        def call():
+            oracle.causal_backward(q[:1], k[:1], v[:1], do[:1])
+
+        per = Hq * n
+        what = f"1-element slices of the batch (Hq={Hq} n={n} d={d}, pairwise O(n^2) gradients)"
+        cores = min(threads, Hkv)
     else:
         bs = max(1, min(B, -(-threads // Hkv)))
         fn = {"causal": lambda a, b_, c: oracle.causal(a, b_, c, phi=phi),
+              "strided": lambda a, b_, c: oracle.causal(a, b_, c, phi=phi),
+              "varlen": lambda a, b_, c: oracle.causal(a, b_, c, phi=phi),
+              "window": lambda a, b_, c: oracle.window(a, b_, c, w["window"], phi=phi),
               "forward": lambda a, b_, c: oracle.forward(a, b_, c, phi=phi),
               "prefix": None}[form]
         state = {"r": 0}
@@ -280,9 +331,55 @@ def run(name, args):
             S, z = states[i % rot]
             qs, ks, vs, o = toks[i % T]
             la.la_decode_step(qs, ks, vs, S, z, out=o)
+    elif form in ("window", "strided", "varlen", "backward"):
+        B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
+        tdt = torch.bfloat16 if dtc == li.BF16 else torch.float32
+        if form == "varlen":
+            lens = varlen_lengths(w)
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+            T = int(cu[-1])
+            q, k, v, rng = li.qkv(1, Hq, Hkv, T, d, dtc, seed=0, scaled=w["scaled"])
+            cud = torch.from_numpy(cu).to(dev)
+            # packed [T, H, d] rows
+            pk = lambda x: li.to_torch(np.ascontiguousarray(x[0].transpose(1, 0, 2))).to(dev)
+            first = (pk(q), pk(k), pk(v))
+        else:
+            q, k, v, rng = li.qkv(B, Hq, Hkv, n, d, dtc, seed=0, scaled=w["scaled"])
+            if form == "strided":  # [B, n, H, d] buffers, viewed as [B, H, n, d]
+                bn = lambda x: li.to_torch(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).to(dev).transpose(1, 2)
+                first = (bn(q), bn(k), bn(v))
+            else:
+                first = tuple(li.to_torch(x).to(dev) for x in (q, k, v))
+        set_bytes = 2 * (first[0].numel() + first[1].numel()) * first[0].element_size()
+        rot = max(1, min(16, -(-FOOTPRINT // set_bytes)))
+        sets = [first] + [tuple(x.clone() for x in first) for _ in range(rot - 1)]
+        if form == "strided":  # clone() of a transposed view keeps its strides
+            assert all(x.stride() == first[0].stride() for x in sets[-1][:1])
+        outs = [torch.empty_like(s_[0]) for s_ in sets]
+        if form == "backward":
+            dos = [li.to_torch(li.gaussian(rng, (B, Hq, n, d), None, dtc)).to(dev) for _ in range(rot)]
+            need = la.la_workspace_bytes(la.LA_OP_CAUSAL_BACKWARD, B, Hq, Hkv, n, d, ladt, 0)
+        else:
+            need = la.la_workspace_bytes(la.LA_OP_SEQS, B, Hq, Hkv, n, d, ladt, 0)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        phi = w.get("phi", "relu1")
+
+        def step(i):
+            qq, kk, vv = sets[i % rot]
+            if form == "window":
+                la.la_window_forward(qq, kk, vv, w["window"], out=outs[i % rot], phi=phi)
+            elif form == "strided":
+                la.la_causal_forward_strided(qq, kk, vv, out=outs[i % rot], ws=ws, phi=phi)
+            elif form == "varlen":
+                la.la_causal_forward_strided(qq, kk, vv, cu_seqlens=cud, max_len=n, out=outs[i % rot], ws=ws, phi=phi)
+            else:
+                la.la_causal_backward(qq, kk, vv, dos[i % rot], ws=ws, phi=phi)
     else:
         B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
         q, k, v, rng = li.qkv(B, Hq, Hkv, n, d, dtc, seed=0, scaled=w["scaled"])
+        if w.get("phi") == "features":  # the caller's map (softplus) applied beforehand, in fp32
+            sp = lambda x: li.as_dtype(np.log1p(np.exp(li.to_f32(x))).astype(np.float32), dtc)
+            q, k = sp(q), sp(k)
         md = None
         if form == "prefix":
             if w.get("batched"):
@@ -320,6 +417,10 @@ def run(name, args):
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # a spin kernel ahead of the start event keeps the GPU busy while the host
+    # enqueues the first calls, so that no host launch gap falls inside the
+    # bracket (the K calls then run back to back on the device)
+    torch.cuda._sleep(2_000_000)
     e0.record(stream)
     for i in range(steps):
         step(warmup + i)
@@ -345,13 +446,16 @@ def run(name, args):
         "rotating_sets": rot,
     }
     tfs = flops / (ms * 1e-3) / 1e12
-    mpeak = MFMA_F32_PEAK_TFS if w["dt"] == "f32" else MFMA_BF16_PEAK_TFS
+    # the backward's products are fp32 MFMA for either input type
+    mpeak = MFMA_F32_PEAK_TFS if w["dt"] == "f32" or form == "backward" else MFMA_BF16_PEAK_TFS
     roof["mfma"] = {"achieved": tfs, "peak": mpeak, "unit": "TFLOP/s", "frac": tfs / mpeak}
     if form != "decode" and flops / (mpeak * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
         roof["note"] = "the MFMA time of the algorithmic flops exceeds their HBM time: compare both fractions"
     cfg = {"workload": DESCRIPTIONS[name], "name": name}
-    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix", "phi", "batched")
-                if kk in w})
+    cfg.update({kk: w[kk] for kk in ("B", "Hq", "Hkv", "n", "d", "chunk", "mask", "prefix", "phi", "batched",
+                                     "window") if kk in w})
+    if form == "varlen":
+        cfg["lengths"] = [int(x) for x in varlen_lengths(w)]
     if form != "decode":
         cfg.update({"global_batch": w["B"], "seq_len": w["n"]})
     line = {
@@ -375,6 +479,8 @@ def run(name, args):
     if not args.no_cpu:
         if form == "decode":
             line["cpu_baseline"] = cpu_baseline(w, None, None, None, S=S0.cpu().numpy(), z=z0.cpu().numpy())
+        elif form == "varlen":
+            line["cpu_baseline"] = None  # per-sequence oracle calls: see the causal workload
         else:
             line["cpu_baseline"] = cpu_baseline(w, q, k, v, m=m)
     print(json.dumps(line), flush=True)

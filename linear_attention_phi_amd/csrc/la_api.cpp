@@ -231,7 +231,7 @@ la_status la_forward_phi(const void* q, const void* k, const void* v, int64_t B,
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, nullptr, nullptr, ws, stream, (int)phi};
   attach_ws(a, ws);
-  if (phi != LA_PHI_FEATURES && forward_bf16_applies(n, d, (int)dtype)) {  // relu + 1 or ELU + 1
+  if (forward_bf16_applies(n, d, (int)dtype)) {  // every feature map
     if (forward_bf16_grid(B * Hkv, B * Hq, n) >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_forward_bf16(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
@@ -281,7 +281,7 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
     return LA_ERR_ALIAS;
   Fwd a{q, k, v, out, B, Hq, Hkv, n, d, (int)dtype, nullptr, S_final, z_final, ws, stream, (int)phi};
   attach_ws(a, ws);
-  if (q && phi != LA_PHI_FEATURES && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // relu + 1 or ELU + 1
+  if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // every feature map
     const Plan fp = make_fused_plan(n);
     if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_causal_fused(a, fp) == 0 ? LA_OK : LA_ERR_LAUNCH;

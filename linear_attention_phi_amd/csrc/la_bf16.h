@@ -47,6 +47,9 @@ __device__ __forceinline__ uint32_t phi2(uint32_t x) {
 // x log2(e), a few ulp of fp32 below the bf16 rounding)
 __device__ __forceinline__ float elu1f(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
 __device__ __forceinline__ uint32_t elu2(uint32_t x) { return pack2(elu1f(lo_f(x)), elu1f(hi_f(x))); }
+// The non-split feature map of two packed bf16 values: ELU + 1, or the
+// identity for caller-applied features
+template <int PM> __device__ __forceinline__ uint32_t map2(uint32_t x) { return PM == PM_FEAT ? x : elu2(x); }
 // a.lo * b.lo + a.hi * b.hi + c for packed bf16 pairs, accumulated in fp32
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);

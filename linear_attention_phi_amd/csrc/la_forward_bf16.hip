@@ -169,7 +169,7 @@ __device__ __forceinline__ void fwd_state(const FwdArgs& A, int64_t bid, StateLd
       u32x4 x = kr[u];
       const bool real = prow + 8 * u < nv;  // ELU + 1: rows past the end hold 0, not phi(0)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = SPLIT ? relu2(x[j]) : (real ? elu2(x[j]) : 0u);
+      for (int j = 0; j < 4; ++j) x[j] = SPLIT ? relu2(x[j]) : (real ? map2<PM>(x[j]) : 0u);
       *reinterpret_cast<u32x4*>(tK + (prow + 8 * u) * RS + pcol) = x;
     }
 #pragma unroll
@@ -404,7 +404,7 @@ __device__ __forceinline__ void fwd_out(const FwdArgs& A, int64_t bid, uint8_t (
       for (int kb = 0; kb < 4; ++kb) {
         u32x4 x = qraw[j][ib][kb];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = PM == PM_RELU1 ? phi2(x[e]) : elu2(x[e]);
+        for (int e = 0; e < 4; ++e) x[e] = PM == PM_RELU1 ? phi2(x[e]) : map2<PM>(x[e]);
         qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
       }
 #pragma unroll
@@ -488,7 +488,9 @@ int launch_forward_bf16(const Fwd& a) {
   FwdArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
             reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, nchunks, nseg, NKV, NQ,
             a.Hq / a.Hkv, part, tot, sflag, rflag, a.ctl, launch_epoch(a.stream)};
-  if (a.phi == 1)
+  if (a.phi == 2)
+    k_fwd_one<PM_FEAT><<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
+  else if (a.phi == 1)
     k_fwd_one<PM_ELU1><<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);
   else
     k_fwd_one<PM_RELU1><<<dim3((unsigned)forward_bf16_grid(NKV, NQ, a.n)), WNT, 0, st>>>(A);

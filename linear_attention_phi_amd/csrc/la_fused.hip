@@ -97,7 +97,8 @@ __device__ __forceinline__ float* state_row(CpLds& L, int c, int b) {
 // ones part (column sums of V, the key count in z, sum_a phi(Q_i)[a] at the
 // start of each score); ELU + 1 has no such split: phi(K) and phi(Q) are
 // rounded to bf16 in the tiles and fragments, and rows past the sequence end
-// are stored as 0, not phi(0) = 1.
+// are stored as 0, not phi(0) = 1.  Caller-applied features (PM_FEAT) go
+// through the same path with the identity.
 template <int PM>
 __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   constexpr bool SPLIT = PM == PM_RELU1;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       u32x4 x = kr[u];
       const bool real = prow + 8 * u < nv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = SPLIT ? relu2(x[j]) : (real ? elu2(x[j]) : 0u);
+      for (int j = 0; j < 4; ++j) x[j] = SPLIT ? relu2(x[j]) : (real ? map2<PM>(x[j]) : 0u);
       *reinterpret_cast<u32x4*>(tK + (prow + 8 * u) * RS + pcol) = x;
     }
 #pragma unroll
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
       for (int kb = 0; kb < 4; ++kb) {
         u32x4 x = qr[ib][kb];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = SPLIT ? phi2(x[j]) : elu2(x[j]);
+        for (int j = 0; j < 4; ++j) x[j] = SPLIT ? phi2(x[j]) : map2<PM>(x[j]);
         qf[ib][kb].v = __builtin_bit_cast(bf16x8, x);
       }
     // P^T blocks (key block jb, query block ib), jb <= ib (with ELU + 1 the
@@ -485,7 +486,9 @@ int launch_causal_fused(const Fwd& a, const Plan& p) {
   FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
               reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, p.nchunks, p.nseg, NH,
               agg, flags, a.S_final, a.z_final, a.ctl, launch_epoch(a.stream)};
-  if (a.phi == 1)
+  if (a.phi == 2)
+    k_causal_fused<PM_FEAT><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
+  else if (a.phi == 1)
     k_causal_fused<PM_ELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
   else
     k_causal_fused<PM_RELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);

@@ -51,7 +51,7 @@ def features(x, fn, dtype):
     return li.as_dtype(fn(li.to_f32(x)).astype(np.float32), dtype)
 
 
-CASES = [(2, 4, 2, 300, 64), (1, 2, 2, 1000, 32), (1, 2, 1, 257, 128), (1, 1, 1, 5, 3)]
+CASES = [(2, 4, 2, 300, 64), (2, 3, 3, 700, 64), (1, 2, 2, 1000, 32), (1, 2, 1, 257, 128), (1, 1, 1, 5, 3)]
 
 
 @pytest.mark.parametrize("mapname", sorted(MAPS))
