@@ -195,7 +195,13 @@ size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_
     a.nseq = B;
     a.Hkv = Hkv;
     a.d = d;
-    return kCtlBytes + state_bytes(seq_plan(a, C), B, Hkv);
+    // the general kernels' segment states, or the single-launch kernel's
+    // aggregates where the strides may let it run
+    const size_t general = state_bytes(seq_plan(a, C), B, Hkv);
+    const size_t fused = dtype == LA_BF16 && Hq == Hkv && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, 64)
+                             ? fused_seq_ws_bytes(a)
+                             : 0;
+    return kCtlBytes + (general > fused ? general : fused);
   }
   if (op != LA_OP_FORWARD && op != LA_OP_CAUSAL && op != LA_OP_PREFIX_MASK && op != LA_OP_PREFIX_MASK_BATCHED)
     return 0;
@@ -423,7 +429,9 @@ la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
             nseq, Hq, Hkv, d, (int)dtype, (int)phi, window, vec, S_final, z_final, nullptr, nullptr, stream};
   const Plan p = seq_plan(a, C);
   if (nseq * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
-  const size_t need = kCtlBytes + (window > 0 ? 0 : state_bytes(p, nseq, Hkv));
+  const bool fused = fused_seq_applies(a);
+  if (fused && nseq * Hkv * ((max_len + kFusedG * 64 - 1) / (kFusedG * 64)) >= kMaxGrid) return LA_ERR_SHAPE;
+  const size_t need = kCtlBytes + (fused ? fused_seq_ws_bytes(a) : window > 0 ? 0 : state_bytes(p, nseq, Hkv));
   if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
   for (int i = 0; i < 3; ++i)
     if (overlaps(ws, need, ins[i], inb[i])) return LA_ERR_ALIAS;
@@ -432,6 +440,7 @@ la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
     return LA_ERR_ALIAS;
   a.ctl = reinterpret_cast<Ctl*>(ws);
   a.ws = reinterpret_cast<char*>(ws) + kCtlBytes;
+  if (fused) return launch_causal_fused_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
   return launch_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 

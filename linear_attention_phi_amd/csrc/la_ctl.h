@@ -57,11 +57,11 @@ __device__ __forceinline__ uint32_t ctl_arrive(Ctl* c, const CtlView& v) {
   asm volatile("" ::"v"(v.gen) : "memory");
   return __hip_atomic_fetch_add(&c->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// The last workgroup to arrive stores the new generation and resets the
-// counter (called by the thread that arrived, after its last use of the
-// epoch).
+// The last workgroup of the grid (of every dimension) to arrive stores the
+// new generation and resets the counter (called by the thread that arrived,
+// after its last use of the epoch).
 __device__ __forceinline__ void ctl_leave(Ctl* c, uint32_t old, uint64_t epoch) {
-  if (old == gridDim.x - 1) {
+  if (old == gridDim.x * gridDim.y * gridDim.z - 1) {
     __hip_atomic_store(&c->arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&c->gen, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

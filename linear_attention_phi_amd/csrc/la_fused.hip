@@ -30,8 +30,9 @@
 // (la_bf16.h).  phi(K)^T V is formed as
 // relu(K)^T V + 1 (x) sum_t V_t (exact products; see la_kernels.hip).
 //
-// Segments are numbered segment-major (blockIdx = seg * NH + head), so a
-// workgroup only ever waits for workgroups dispatched before it.  Aggregates
+// Segments are numbered segment-major (grid x = head, y = segment; x varies
+// fastest in dispatch order), so a workgroup only ever waits for workgroups
+// dispatched before it.  Aggregates
 // go through memory with device-scope stores and loads (the XCDs' L2 caches
 // are not coherent with each other).  Flags are 64-bit words holding the
 // call's epoch, taken from the workspace's control block (la_ctl.h), so that
@@ -61,9 +62,15 @@ constexpr int AGG_FLOATS = FD * FD + FD;  // published segment aggregate: S^T [b
 constexpr int TILE_B = FC * RS * 2;       // bytes of one token-major bf16 tile
 constexpr int REGION_B = 2 * TILE_B;      // one wave's LDS region
 
+// Rows come through a sequence table: row t of head h of sequence s at
+// q + s qb + start(s) qt + h qh + t qt (K and V with kb, kt, kh; out with the
+// q strides), start(s) = cu[s] for packed sequences of different lengths and
+// 0 for one length n.  "head" below is u = s H + h.
 struct FusedArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* out;
-  int64_t n, nchunks, nseg, NH;
+  int64_t n, nchunks, nseg, NH;  // n, nchunks, nseg: of the longest sequence; NH = sequences x heads
+  int64_t H, qb, qh, qt, kb, kh, kt;
+  const int64_t* cu; int64_t total;  // cu NULL: every sequence holds n tokens
   float* agg; uint64_t* flags;
   float* S_final; float* z_final; la_internal::Ctl* ctl;
   uint64_t host_epoch;  // the call's epoch, or 0: take it from the control block
@@ -99,32 +106,81 @@ __device__ __forceinline__ float* state_row(CpLds& L, int c, int b) {
 // rounded to bf16 in the tiles and fragments, and rows past the sequence end
 // are stored as 0, not phi(0) = 1.  Caller-applied features (PM_FEAT) go
 // through the same path with the identity.
-template <int PM>
+//
+// SEQ: rows through the sequence table (runtime strides, cu); without it the
+// rows are contiguous [B, H, n, d] (compile-time strides: the address
+// arithmetic of the loads and stores folds into immediate offsets).
+template <int PM, bool SEQ>
 __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) CpLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int64_t seg = blockIdx.x / A.NH, head = blockIdx.x % A.NH;
-  const int hbytes = (int)(A.n * FD * 2);  // one head's rows (n <= 2^24)
-  const __amdgpu_buffer_rsrc_t rq =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + head * A.n * FD), 0, hbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.k + head * A.n * FD), 0, hbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.v + head * A.n * FD), 0, hbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(A.out + head * A.n * FD, 0, hbytes, 0x00020000);
-  const int64_t c_begin = seg * SEGC;
-  const int64_t rem = A.nchunks - c_begin;
-  const int ncl = (int)(rem < SEGC ? rem : SEGC);  // chunks of this segment (>= 1)
-  const bool mine = w < ncl;                       // this wave owns a chunk
-  const int t0 = (int)((c_begin + w) * FC);        // its first row
-  const int nv = mine ? (int)((A.n - t0) < FC ? (A.n - t0) : FC) : 0;
-  bf16* tK = reinterpret_cast<bf16*>(L.reg[w]);
-  bf16* tV = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
-  if (tid < FD) L.zero[tid] = (bf16)0.0f;
+  // grid (heads of every sequence, segments): x varies fastest, so the
+  // dispatch order is segment-major
+  const int64_t seg = blockIdx.y, head = blockIdx.x;
   // the control words are requested first; wave 0 uses them after its loads
   la_ctl::CtlView cv{};
   if (w == 0) cv = la_ctl::ctl_load(A.ctl);
+  // this sequence's rows: start and length (an inconsistent table entry
+  // leaves the sequence empty and is recorded once, by its first segment)
+  int64_t start = 0, len = A.n;
+  if (SEQ && A.cu) {
+    const int64_t sq = blockIdx.x / (uint32_t)A.H;
+    const int64_t a = A.cu[sq], b = A.cu[sq + 1], prev = sq > 0 ? A.cu[sq - 1] : 0;
+    if (a < prev || b < a || b > A.total || b - a > A.n) {
+      if (seg == 0 && tid == 0) la_ctl::ctl_fail(A.ctl, la_internal::kErrRange);
+      start = 0;
+      len = 0;
+    } else {
+      start = a;
+      len = b - a;
+    }
+  }
+  const int64_t nch = (len + FC - 1) / FC, nseg_s = (nch + SEGC - 1) / SEGC;
+  if (SEQ && seg >= nseg_s) {  // past this sequence's end (the grid covers the longest)
+    if (seg == 0 && len == 0) {  // an empty sequence's final state is zero
+      if (A.S_final)
+        for (int e = tid; e < FD * FD; e += FNT) A.S_final[head * FD * FD + e] = 0.0f;
+      if (A.z_final && tid < FD) A.z_final[head * FD + tid] = 0.0f;
+    }
+    if (tid == 0 && !A.host_epoch) {
+      const uint32_t arrived = la_ctl::ctl_arrive(A.ctl, cv);
+      la_ctl::ctl_leave(A.ctl, arrived, la_ctl::epoch_of(cv.gen));
+    }
+    return;
+  }
+  // buffer resources bounded to the sequence's rows of this head (rows past
+  // its end read as zero and are not written; the caller keeps row strides
+  // >= 64 elements and every offset below 2^31 bytes)
+  int qbytes = (int)(A.n * FD * 2), kbytes = qbytes;
+  int64_t qoff = head * A.n * FD, koff = qoff;
+  int qs = FD * 2, ks = FD * 2;  // row strides in bytes
+  if (SEQ) {
+    const uint32_t sq32 = blockIdx.x / (uint32_t)A.H;
+    const int64_t sq = sq32, hh = blockIdx.x - sq32 * (uint32_t)A.H;
+    qbytes = (int)(((len - 1) * A.qt + FD) * 2);
+    kbytes = (int)(((len - 1) * A.kt + FD) * 2);
+    qoff = sq * A.qb + start * A.qt + hh * A.qh;
+    koff = sq * A.kb + start * A.kt + hh * A.kh;
+    qs = (int)A.qt * 2;
+    ks = (int)A.kt * 2;
+  }
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.q + qoff), 0, qbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.k + koff), 0, kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(A.v + koff), 0, kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(A.out + qoff, 0, qbytes, 0x00020000);
+  const int64_t c_begin = seg * SEGC;
+  const int64_t rem = nch - c_begin;
+  const int ncl = (int)(rem < SEGC ? rem : SEGC);  // chunks of this segment (>= 1)
+  const bool mine = w < ncl;                       // this wave owns a chunk
+  const int t0 = (int)((c_begin + w) * FC);        // its first row
+  const int nv = mine ? (int)((len - t0) < FC ? (len - t0) : FC) : 0;
+  bf16* tK = reinterpret_cast<bf16*>(L.reg[w]);
+  bf16* tV = reinterpret_cast<bf16*>(L.reg[w] + TILE_B);
+  if (tid < FD) L.zero[tid] = (bf16)0.0f;
 
   // ------------------------------------------------------------------ A
   // Loads: K and V as 16-byte row pieces (rows lane / 8 + 8 u), Q directly
@@ -141,14 +197,14 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     u32x4 kr[8], vr[8], qr[2][4];
     const int prow = lane >> 3, pcol = 8 * (lane & 7);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, 0);
+    for (int u = 0; u < 8; ++u) kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (t0 + prow + 8 * u) * ks + pcol * 2, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, 0);
+    for (int u = 0; u < 8; ++u) vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, (t0 + prow + 8 * u) * ks + pcol * 2, 0, 0);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        qr[ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, ((t0 + 32 * ib + r) * FD + 16 * kb + 8 * h) * 2, 0, 0);
+        qr[ib][kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, (t0 + 32 * ib + r) * qs + (16 * kb + 8 * h) * 2, 0, 0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       u32x4 x = kr[u];
@@ -319,7 +375,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   // instructions covers 1 KB contiguously
   const int soff = (w * 128 + lane) * 16;  // byte offset of this lane's first half in an aggregate
   const int zoff = FD * FD * 4;          // byte offset of z in an aggregate
-  const bool publish = seg + 1 < A.nseg;  // the last segment has no successor
+  const bool publish = seg + 1 < nseg_s;  // the last segment has no successor
   uint64_t* flag = A.flags + head * A.nseg;
   if (publish) {
     const int base = (int)(seg * AGG_FLOATS * 4);
@@ -420,7 +476,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     *reinterpret_cast<u32x4*>(L.sprev + sb * RS + sa) = u32x4{y[0], y[1], y[2], y[3]};
     if (w == 0) store_z_pairs(L.zhp, L.zlp, zprev, lane);
   }
-  if (seg == A.nseg - 1) {
+  if (seg == nseg_s - 1) {
     if (A.S_final) {
       float* Sf = A.S_final + head * FD * FD;
 #pragma unroll
@@ -457,7 +513,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(tO + (prow + 8 * u) * RS + pcol), ro,
-                                             ((t0 + prow + 8 * u) * FD + pcol) * 2, 0, CPOL_NT);
+                                             (t0 + prow + 8 * u) * qs + pcol * 2, 0, CPOL_NT);
   }
   if (tid == 0 && !A.host_epoch) la_ctl::ctl_leave(A.ctl, arrived, L.epoch);
 }
@@ -477,22 +533,49 @@ size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {
   return (size_t)NH * nseg * (AGG_FLOATS * sizeof(float) + sizeof(uint64_t));
 }
 
-int launch_causal_fused(const Fwd& a, const Plan& p) {
-  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
-  const int64_t NH = a.B * a.Hkv;
-  float* agg = reinterpret_cast<float*>(a.ws);
-  uint64_t* flags = reinterpret_cast<uint64_t*>(agg + NH * p.nseg * AGG_FLOATS);
+bool fused_seq_applies(const SeqCall& a) {
+  const int64_t rs = a.S.qt > a.S.kt ? a.S.qt : a.S.kt;
+  return a.q && a.window == 0 && a.vec && a.S.qt >= FD && a.S.kt >= FD && a.Hq == a.Hkv &&
+         fused_causal_applies(a.Hq, a.Hkv, a.S.n, a.d, a.dtype, FC) && (a.S.n + FC) * rs * 2 < ((int64_t)1 << 31);
+}
+
+template <bool SEQ>
+static int launch_fused(FusedArgs& A, int phi, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   static_assert(kFusedG == SEGC, "segment length");
-  FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
-              reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.n, p.nchunks, p.nseg, NH,
-              agg, flags, a.S_final, a.z_final, a.ctl, launch_epoch(a.stream)};
-  if (a.phi == 2)
-    k_causal_fused<PM_FEAT><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
-  else if (a.phi == 1)
-    k_causal_fused<PM_ELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
+  const dim3 grid((unsigned)A.NH, (unsigned)A.nseg);
+  A.flags = reinterpret_cast<uint64_t*>(A.agg + A.NH * A.nseg * AGG_FLOATS);
+  A.host_epoch = launch_epoch(stream);
+  if (phi == 2)
+    k_causal_fused<PM_FEAT, SEQ><<<grid, FNT, 0, st>>>(A);
+  else if (phi == 1)
+    k_causal_fused<PM_ELU1, SEQ><<<grid, FNT, 0, st>>>(A);
   else
-    k_causal_fused<PM_RELU1><<<dim3((unsigned)(NH * p.nseg)), FNT, 0, st>>>(A);
+    k_causal_fused<PM_RELU1, SEQ><<<grid, FNT, 0, st>>>(A);
   return (int)hipGetLastError();
+}
+
+int launch_causal_fused(const Fwd& a, const Plan& p) {
+  const int64_t H = a.Hkv, n = a.n;
+  FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
+              reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), n, p.nchunks, p.nseg, a.B * H,
+              H, H * n * FD, n * FD, FD, H * n * FD, n * FD, FD, nullptr, a.B * n,
+              reinterpret_cast<float*>(a.ws), nullptr, a.S_final, a.z_final, a.ctl, 0};
+  return launch_fused<false>(A, a.phi, a.stream);
+}
+
+int launch_causal_fused_seq(const SeqCall& a) {
+  const int64_t nchunks = (a.S.n + FC - 1) / FC;
+  FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
+              reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.S.n, nchunks,
+              (nchunks + SEGC - 1) / SEGC, a.nseq * a.Hkv, a.Hkv, a.S.qb, a.S.qh, a.S.qt, a.S.kb, a.S.kh, a.S.kt,
+              a.S.cu, a.S.total, reinterpret_cast<float*>(a.ws), nullptr, a.S_final, a.z_final, a.ctl, 0};
+  return launch_fused<true>(A, a.phi, a.stream);
+}
+
+size_t fused_seq_ws_bytes(const SeqCall& a) {
+  const int64_t nchunks = (a.S.n + FC - 1) / FC;
+  return fused_causal_ws_bytes(a.nseq * a.Hkv, (nchunks + SEGC - 1) / SEGC);
 }
 
 }  // namespace la_internal

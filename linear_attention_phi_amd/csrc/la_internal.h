@@ -150,6 +150,13 @@ int launch_seq(const SeqCall& a);
 // The causal form's state pass and scan alone, for chunk C (bf16 or fp32,
 // d <= 64): a.ws receives the exclusive prefix slots of seq_plan(a, C).
 int launch_seq_prefix(const SeqCall& a, int C);
+// The causal form over a sequence table on the single-launch kernel
+// (la_fused.hip): bf16, d = 64, Hq == Hkv, outputs requested, 16-byte rows
+// with row strides of at least 64 elements, offsets below 2^31 bytes.  Its
+// workspace (past the control block): the fused kernel's aggregates and flags.
+bool fused_seq_applies(const SeqCall& a);
+size_t fused_seq_ws_bytes(const SeqCall& a);
+int launch_causal_fused_seq(const SeqCall& a);
 // Gradients of the causal form (la_backward.hip): contiguous [B, H, n, d],
 // d <= 64.  backward_chunk is 0 where the tiles do not fit in LDS.
 struct BwdCall {

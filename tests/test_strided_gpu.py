@@ -105,11 +105,12 @@ def test_packed_sequences(gpu, dtype, d, window, phi):
         check(g[a:b].transpose(1, 0, 2)[None], ref, dtype, f"packed seq {s} (length {L}) {phi} window {window}")
 
 
-def test_packed_sequences_bad_table_is_reported(gpu):
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2)])
+def test_packed_sequences_bad_table_is_reported(gpu, Hq, Hkv):
     """A decreasing cu_seqlens entry: that sequence is left alone, the rest are
-    right, and la_workspace_status reports LA_ERR_RANGE."""
+    right, and la_workspace_status reports LA_ERR_RANGE (Hq == Hkv: the
+    single-launch kernel; Hq > Hkv: the general kernels)."""
     import torch
-    Hq = Hkv = 2
     d = 64
     lengths = [100, 200, 50]
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
@@ -144,3 +145,87 @@ def test_bnhd_B8_n2048_H8_d64_bf16(gpu):
     ge = host(gpu.la_causal_forward_strided(bnhd(q), bnhd(ke), bnhd(v)).contiguous())
     want = np.cumsum(li.to_f32(v).astype(np.float64), axis=2) / np.arange(1, n + 1)[None, None, :, None]
     check(ge, want, li.BF16, "BNHD equal keys, every row")
+
+
+def softplus(x):
+    return np.log1p(np.exp(x))
+
+
+# Hq == Hkv, bf16, d = 64: the single-launch causal kernel takes the table.
+# Lengths over several 512-token segments, ragged tails, empty sequences.
+LONG_LENGTHS = [1, 600, 0, 513, 64, 1100, 7, 2100, 512]
+
+
+@pytest.mark.parametrize("phi", ["relu1", "elu1", "softplus"])
+def test_packed_sequences_multi_segment(gpu, phi):
+    """Packed [total, H, d] sequences of 0 .. 2100 tokens (up to five
+    segments of the single-launch kernel, whose look-back stays inside each
+    sequence): every sequence against the oracle on that sequence alone, its
+    final state, and zero state for the empty one.  softplus: features the
+    caller applies (phi="features")."""
+    import torch
+    H, d = 3, 64
+    cu = np.concatenate([[0], np.cumsum(LONG_LENGTHS)]).astype(np.int64)
+    total = int(cu[-1])
+    q, k, v, _ = li.qkv(1, H, H, total, d, li.BF16, seed=340, scaled=True)
+    if phi == "softplus":
+        fq = li.as_dtype(softplus(li.to_f32(q)).astype(np.float32), li.BF16)
+        fk = li.as_dtype(softplus(li.to_f32(k)).astype(np.float32), li.BF16)
+        call_phi, ref_phi = "features", softplus
+    else:
+        fq, fk, call_phi, ref_phi = q, k, phi, phi
+    pk = lambda x: dev(np.ascontiguousarray(x[0].transpose(1, 0, 2)))
+    cud = torch.from_numpy(cu).cuda()
+    out, S, z = gpu.la_causal_forward_strided(pk(fq), pk(fk), pk(v), cu_seqlens=cud, want_state=True, phi=call_phi)
+    g = host(out)
+    S, z = S.cpu().numpy(), z.cpu().numpy()
+    for s, L in enumerate(LONG_LENGTHS):
+        if L == 0:
+            assert not S[s].any() and not z[s].any(), "an empty sequence's state must be zero"
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda x: np.ascontiguousarray(x[:, :, a:b])
+        ref, Sr, zr = oracle.causal(sl(q), sl(k), sl(v), want_state=True, phi=ref_phi)
+        np.testing.assert_allclose(z[s], zr[0], rtol=1e-2)
+        np.testing.assert_allclose(S[s], Sr[0], rtol=1e-2, atol=1e-2 * np.abs(Sr).max())
+        check(g[a:b].transpose(1, 0, 2)[None], ref, li.BF16, f"packed seq {s} (length {L}) {phi}")
+
+
+def test_fused_qkv_buffer_layout(gpu):
+    """q, k, v as slices of one [B, n, 3, H, d] projection buffer (token
+    stride 3 H d) and out a slice of another: B2 n1500 H4 d64 bf16, every row
+    and the final state against the oracle."""
+    import torch
+    B, H, n, d = 2, 4, 1500, 64
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.BF16, seed=350, scaled=True)
+    buf = np.stack([x.transpose(0, 2, 1, 3) for x in (q, k, v)], axis=2)  # [B, n, 3, H, d]
+    bd = dev(np.ascontiguousarray(buf))
+    views = [bd[:, :, i].transpose(1, 2) for i in range(3)]  # [B, H, n, d] views
+    ob = torch.zeros_like(bd)
+    out = ob[:, :, 0].transpose(1, 2)
+    assert out.stride() == (n * 3 * H * d, d, 3 * H * d, 1)
+    _, S, z = gpu.la_causal_forward_strided(*views, out=out, want_state=True)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True)
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-2, atol=1e-2 * np.abs(Sr).max())
+    check(host(out.contiguous()), ref, li.BF16, "fused QKV buffer B2 n1500 H4 d64")
+    assert not host(ob[:, :, 1:].contiguous()).any(), "nothing may be written outside out's rows"
+
+
+def test_unaligned_token_stride_takes_general_path(gpu):
+    """Rows of 68 elements (136 bytes, not a multiple of 16): the table goes
+    to the general kernels; same result as the oracle."""
+    B, H, n, d = 1, 2, 700, 64
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.BF16, seed=360, scaled=True)
+
+    def padded(x):  # [B, H, n, d] stored as [B, n, H, 68]
+        p = np.zeros((B, n, H, 68), dtype=x.dtype)
+        p[..., :d] = x.transpose(0, 2, 1, 3)
+        return dev(p)[..., :d].transpose(1, 2)
+
+    qd, kd, vd = padded(q), padded(k), padded(v)
+    import torch
+    ob = torch.zeros((B, n, H, 68), dtype=torch.bfloat16, device="cuda")
+    out = ob[..., :d].transpose(1, 2)
+    gpu.la_causal_forward_strided(qd, kd, vd, out=out)
+    check(host(out.contiguous()), oracle.causal(q, k, v), li.BF16, "token stride 136 bytes")
