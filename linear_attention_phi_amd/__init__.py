@@ -43,7 +43,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblaphi.so")
+# LA_LIBRARY names another build of the same library to load instead (the
+# host-sanitizer build the CPU tests make); by default the in-tree one.
+LIB_PATH = os.environ.get("LA_LIBRARY") or os.path.join(_HERE, "liblaphi.so")
 
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FORWARD, LA_OP_CAUSAL, LA_OP_PREFIX_MASK, LA_OP_PREFIX_MASK_BATCHED, LA_OP_SEQS = 0, 1, 2, 3, 4

@@ -76,5 +76,56 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host sanitizers for the CPU tests: AddressSanitizer and UndefinedBehavior-
+# Sanitizer on the host code only (each flag behind -Xarch_host; the device
+# code is compiled as usual), against the shared ASan runtime, so that a
+# Python process that preloads that runtime can load the library.
+SAN_DIR = os.path.join(HERE, "_build", "san")
+SAN_LIB = os.path.join(SAN_DIR, "liblaphi_san.so")
+_SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+              "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-shared-libasan"]
+
+
+def _sources_mtime() -> float:
+    files = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "la.h")]
+    return max(os.path.getmtime(f) for f in files)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build the library with host sanitizers into _build/san (reused while it
+    is newer than every source); returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    if os.path.exists(SAN_LIB) and os.path.getmtime(SAN_LIB) > _sources_mtime():
+        return SAN_LIB
+    os.makedirs(SAN_DIR, exist_ok=True)
+    flags = [f for f in _flags() if f != "-O3"] + ["-O1", "-g", *_SAN_FLAGS]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        jobs.append(([_hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        errs = list(ex.map(lambda j: _run(j[0]), jobs))
+    link = [_hipcc(), f"--offload-arch={ARCH}", "-shared", *_SAN_FLAGS, *[o for _, o in jobs], "-o",
+            SAN_LIB + ".tmp"]
+    errs.append(_run(link))
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e, file=sys.stderr)
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
+def asan_runtime() -> str | None:
+    """The shared ASan runtime of the compiler that builds the library."""
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(_hipcc()))),
+                                         "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -267,40 +267,59 @@ __device__ __forceinline__ void tile_store(const TileRaw<T, DP, C>& t, int nvali
   }
 }
 
-// Copy ROWS rows x DP features of T (row stride ld elements, row0 first)
-// into LDS tiles of TT: tm[row * ldt + col] transformed by TMX and/or
-// fm[col * ldf + row] transformed by FMX.  Rows at or past nvalid and
-// features at or past d are stored as 0 (not phi(0)).  vec: d == DP and
-// 16-byte rows, 16-byte pieces.  TT may be wider than T (bf16 rows widened
-// exactly into fp32 tiles).
+// The 16-byte row pieces of one ROWS x DP tile that thread tid owns, held
+// in registers between stage_load (the requests) and stage_put (the LDS
+// writes), so that a walk can request the next chunk's rows before it works
+// on the current one.
+template <typename T, int DP, int ROWS>
+struct StageRegs {
+  static constexpr int EPP = 16 / (int)sizeof(T);
+  static constexpr int PPR = DP / EPP;
+  static constexpr int NP = ROWS * PPR;
+  static constexpr int PER = (NP + NT - 1) / NT;
+  uint4 u[PER];
+};
+
+// Request the tile's rows row0 .. row0 + nvalid - 1 (16-byte pieces; rows
+// past nvalid read as zero).  Without vec nothing is requested here: the
+// element path of stage_put loads as it writes.
+template <typename T, int DP, int ROWS>
+__device__ __forceinline__ void stage_load(StageRegs<T, DP, ROWS>& R, const T* __restrict__ base, int64_t ld,
+                                           int64_t row0, int nvalid, bool vec, int tid) {
+  using SR = StageRegs<T, DP, ROWS>;
+  if (!vec) return;
+#pragma unroll
+  for (int k = 0; k < SR::PER; ++k) {
+    const int p = tid + k * NT;
+    const int row = p / SR::PPR, col = (p % SR::PPR) * SR::EPP;
+    R.u[k] = make_uint4(0, 0, 0, 0);
+    if (p < SR::NP && row < nvalid) R.u[k] = *reinterpret_cast<const uint4*>(base + (row0 + row) * ld + col);
+  }
+}
+
+// Write the tile requested by stage_load (same arguments) into LDS, as stage
+// (below) describes.
 template <typename T, typename TT, int DP, int ROWS, int TMX, int FMX>
-__device__ __forceinline__ void stage(const T* __restrict__ base, int64_t ld, int64_t row0, int nvalid, int d,
-                                      bool vec, TT* tm, int ldt, TT* fm, int ldf, int tid) {
+__device__ __forceinline__ void stage_put(const StageRegs<T, DP, ROWS>& R, const T* __restrict__ base, int64_t ld,
+                                          int64_t row0, int nvalid, int d, bool vec, TT* tm, int ldt, TT* fm,
+                                          int ldf, int tid) {
+  using SR = StageRegs<T, DP, ROWS>;
   if (vec) {
-    constexpr int EPP = 16 / (int)sizeof(T);
-    constexpr int PPR = DP / EPP;
-    constexpr int NP = ROWS * PPR;
-    constexpr int PER = (NP + NT - 1) / NT;
+    constexpr int EPP = SR::EPP, PPR = SR::PPR, NP = SR::NP;
     constexpr int PIECES = EPP * (int)sizeof(TT) / 8;  // 8-byte stores per row piece of the tile
     union V { uint4 u; T e[EPP]; };
     union W { uint2 u[PIECES]; TT e[EPP]; };
-    V raw[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {  // every load first
-      const int p = tid + k * NT;
-      const int row = p / PPR, col = (p % PPR) * EPP;
-      raw[k].u = make_uint4(0, 0, 0, 0);
-      if (p < NP && row < nvalid) raw[k].u = *reinterpret_cast<const uint4*>(base + (row0 + row) * ld + col);
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
+    for (int k = 0; k < SR::PER; ++k) {
       const int p = tid + k * NT;
       if (p >= NP) break;
       const int row = p / PPR, col = (p % PPR) * EPP;
+      V raw;
+      raw.u = R.u[k];
       W a, b;
 #pragma unroll
       for (int e = 0; e < EPP; ++e) {
-        const float x = to_f(raw[k].e[e]);
+        const float x = to_f(raw.e[e]);
         a.e[e] = row < nvalid ? cvt<TT>(xform<TMX>(x)) : cvt<TT>(0.0f);
         b.e[e] = row < nvalid ? cvt<TT>(xform<FMX>(x)) : cvt<TT>(0.0f);
       }
@@ -323,6 +342,20 @@ __device__ __forceinline__ void stage(const T* __restrict__ base, int64_t ld, in
       if (FMX != XF_NONE) fm[col * ldf + row] = cvt<TT>(ok ? xform<FMX>(x) : 0.0f);
     }
   }
+}
+
+// Copy ROWS rows x DP features of T (row stride ld elements, row0 first)
+// into LDS tiles of TT: tm[row * ldt + col] transformed by TMX and/or
+// fm[col * ldf + row] transformed by FMX.  Rows at or past nvalid and
+// features at or past d are stored as 0 (not phi(0)).  vec: d == DP and
+// 16-byte rows, 16-byte pieces.  TT may be wider than T (bf16 rows widened
+// exactly into fp32 tiles).
+template <typename T, typename TT, int DP, int ROWS, int TMX, int FMX>
+__device__ __forceinline__ void stage(const T* __restrict__ base, int64_t ld, int64_t row0, int nvalid, int d,
+                                      bool vec, TT* tm, int ldt, TT* fm, int ldf, int tid) {
+  StageRegs<T, DP, ROWS> R;
+  stage_load<T, DP, ROWS>(R, base, ld, row0, nvalid, vec, tid);
+  stage_put<T, TT, DP, ROWS, TMX, FMX>(R, base, ld, row0, nvalid, d, vec, tm, ldt, fm, ldf, tid);
 }
 
 // Rows of chunk x of a sequence of n tokens (0 for x < 0 or past the end).

@@ -143,10 +143,21 @@ __global__ __launch_bounds__(NT) void k_wstate(WinArgs A) {
   const int64_t c0 = seg * A.G, c1 = (c0 + A.G < nch) ? c0 + A.G : nch;
   WinState<TT, DP, C> W;
   W.clear();
+  // chunk c + 1's rows are requested before chunk c's state is added
+  StageRegs<T, DP, C> rK, rV;
+  if (c0 < c1) {
+    stage_load<T, DP, C>(rK, kb, A.S.kt, c0 * C, chunk_rows(c0, C, sp.len), A.vec, tid);
+    stage_load<T, DP, C>(rV, vb, A.S.kt, c0 * C, chunk_rows(c0, C, sp.len), A.vec, tid);
+  }
   for (int64_t c = c0; c < c1; ++c) {
     const int nv = chunk_rows(c, C, sp.len);
-    stage<T, TT, DP, C, XF_NONE, PX>(kb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sKT, LC, tid);
-    stage<T, TT, DP, C, XF_NONE, XF_ID>(vb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sVT, LC, tid);
+    stage_put<T, TT, DP, C, XF_NONE, PX>(rK, kb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sKT, LC, tid);
+    stage_put<T, TT, DP, C, XF_NONE, XF_ID>(rV, vb, A.S.kt, c * C, nv, A.d, A.vec, nullptr, 0, sVT, LC, tid);
+    if (c + 1 < c1) {
+      const int nn = chunk_rows(c + 1, C, sp.len);
+      stage_load<T, DP, C>(rK, kb, A.S.kt, (c + 1) * C, nn, A.vec, tid);
+      stage_load<T, DP, C>(rV, vb, A.S.kt, (c + 1) * C, nn, A.vec, tid);
+    }
     __syncthreads();
     W.add(sKT, LC, sVT, LC, false, w, lane, tid);
     __syncthreads();
@@ -205,20 +216,63 @@ __global__ __launch_bounds__(NT) void k_window(WinArgs A) {
   const T* vb = reinterpret_cast<const T*>(A.v) + sq * A.S.kb + sp.start * kt + g * A.S.kh;
   const int64_t nfull = A.nfull;
 
+  // Rows are requested one step ahead: while a step works from LDS, the
+  // next step's leading chunk, trailing tile and first query head (or the
+  // step's next query head) are in flight in registers.
+  using RT = StageRegs<T, DP, C>;
+  RT rK, rV, rKt[2], rVt[2], rQ;
+  const T* qbase = reinterpret_cast<const T*>(A.q) + sq * A.S.qb + sp.start * qt;
+  auto load_step = [&](int64_t c) {
+    const int nvl = chunk_rows(c, C, n);
+    stage_load<T, DP, C>(rK, kb, kt, c * C, nvl, vec, tid);
+    stage_load<T, DP, C>(rV, vb, kt, c * C, nvl, vec, tid);
+    if (WIN) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int64_t x = c - nfull - 2 + half;
+        const int nvx = chunk_rows(x, C, n);
+        const int64_t r0 = x < 0 ? 0 : x * C;
+        stage_load<T, DP, C>(rKt[half], kb, kt, r0, nvx, vec, tid);
+        stage_load<T, DP, C>(rVt[half], vb, kt, r0, nvx, vec, tid);
+      }
+    }
+  };
+  auto load_q = [&](int64_t c, int r) {
+    stage_load<T, DP, C>(rQ, qbase + (g * R + r) * A.S.qh, qt, c * C, chunk_rows(c, C, n), vec, tid);
+  };
+
   WinState<T, DP, C> W;
   if (WIN) {
     // warm-up: W = states of chunks c0 - nfull - 1 .. c0 - 1 (the first step
     // subtracts chunk c0 - nfull - 1 again); none while nfull = 0
     W.clear();
-    for (int64_t x = (c0 - nfull - 1 > 0 ? c0 - nfull - 1 : 0); nfull > 0 && x < c0; ++x) {
+    const int64_t x0 = c0 - nfull - 1 > 0 ? c0 - nfull - 1 : 0;
+    if (nfull > 0 && x0 < c0) {
+      stage_load<T, DP, C>(rK, kb, kt, x0 * C, chunk_rows(x0, C, n), vec, tid);
+      stage_load<T, DP, C>(rV, vb, kt, x0 * C, chunk_rows(x0, C, n), vec, tid);
+    }
+    for (int64_t x = x0; nfull > 0 && x < c0; ++x) {
       const int nvx = chunk_rows(x, C, n);
-      stage<T, T, DP, C, XF_NONE, PX>(kb, kt, x * C, nvx, d, vec, nullptr, 0, sKT, LC, tid);
-      stage<T, T, DP, C, XF_NONE, XF_ID>(vb, kt, x * C, nvx, d, vec, nullptr, 0, sVT, LC, tid);
+      stage_put<T, T, DP, C, XF_NONE, PX>(rK, kb, kt, x * C, nvx, d, vec, nullptr, 0, sKT, LC, tid);
+      stage_put<T, T, DP, C, XF_NONE, XF_ID>(rV, vb, kt, x * C, nvx, d, vec, nullptr, 0, sVT, LC, tid);
+      if (x + 1 < c0) {
+        stage_load<T, DP, C>(rK, kb, kt, (x + 1) * C, chunk_rows(x + 1, C, n), vec, tid);
+        stage_load<T, DP, C>(rV, vb, kt, (x + 1) * C, chunk_rows(x + 1, C, n), vec, tid);
+      } else {
+        load_step(c0);
+        load_q(c0, 0);
+      }
       __syncthreads();
       W.add(sKT, LC, sVT, LC, false, w, lane, tid);
       __syncthreads();
     }
+    if (!(nfull > 0 && x0 < c0)) {
+      load_step(c0);
+      load_q(c0, 0);
+    }
   } else {
+    load_step(c0);
+    load_q(c0, 0);
     // the exclusive prefix before chunk c0 (the scanned segment state)
     const float* src = A.states + (u * (A.nseg + 1) + seg) * slot_elems(DP);
 #pragma unroll
@@ -246,17 +300,22 @@ __global__ __launch_bounds__(NT) void k_window(WinArgs A) {
     const int nv = chunk_rows(c, C, n);
     // leading chunk: phi(K) token- and feature-major, V feature-major;
     // trailing tile: chunks ce - 2 and ce - 1 (phi(K) both ways, V feature-major)
-    stage<T, T, DP, C, PX, PX>(kb, kt, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
-    stage<T, T, DP, C, XF_NONE, XF_ID>(vb, kt, t0, nv, d, vec, nullptr, 0, sVT, LC, tid);
+    stage_put<T, T, DP, C, PX, PX>(rK, kb, kt, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
+    stage_put<T, T, DP, C, XF_NONE, XF_ID>(rV, vb, kt, t0, nv, d, vec, nullptr, 0, sVT, LC, tid);
     if (WIN) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int64_t x = ce - 2 + half;
         const int nvx = chunk_rows(x, C, n);
         const int64_t r0 = x < 0 ? 0 : x * C;
-        stage<T, T, DP, C, PX, PX>(kb, kt, r0, nvx, d, vec, sKtr + half * C * LQ, LQ, sKTtr + half * C, LC2, tid);
-        stage<T, T, DP, C, XF_NONE, XF_ID>(vb, kt, r0, nvx, d, vec, nullptr, 0, sVTtr + half * C, LC2, tid);
+        stage_put<T, T, DP, C, PX, PX>(rKt[half], kb, kt, r0, nvx, d, vec, sKtr + half * C * LQ, LQ,
+                                       sKTtr + half * C, LC2, tid);
+        stage_put<T, T, DP, C, XF_NONE, XF_ID>(rVt[half], vb, kt, r0, nvx, d, vec, nullptr, 0, sVTtr + half * C,
+                                               LC2, tid);
       }
+    }
+    if (c + 1 < c1) load_step(c + 1);
+    if (WIN) {
       if (nfull > 0) {  // W loses chunk ce - 1, which has left the chunks inside every window
         __syncthreads();
         W.add(sKTtr + C, LC2, sVTtr + C, LC2, true, w, lane, tid);
@@ -277,9 +336,13 @@ __global__ __launch_bounds__(NT) void k_window(WinArgs A) {
 
     for (int r = 0; r < R; ++r) {
       const int64_t hq = g * R + r;
-      const T* qh = reinterpret_cast<const T*>(A.q) + sq * A.S.qb + sp.start * qt + hq * A.S.qh;
+      const T* qh = qbase + hq * A.S.qh;
       __syncthreads();  // the tiles above are written; the previous head is done with sQ, sP, sPtr
-      stage<T, T, DP, C, PX, XF_NONE>(qh, qt, t0, nv, d, vec, sQ, LQ, nullptr, 0, tid);
+      stage_put<T, T, DP, C, PX, XF_NONE>(rQ, qh, qt, t0, nv, d, vec, sQ, LQ, nullptr, 0, tid);
+      if (r + 1 < R)
+        load_q(c, r + 1);
+      else if (c + 1 < c1)
+        load_q(c + 1, 0);
       __syncthreads();
 
       // ---- scores: chunk c (keys i - w < j <= i) into sP[i][j]; the trailing

@@ -25,10 +25,25 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "la_oracle.c")
 LIB_PATH = os.path.join(_HERE, "liblaoracle.so")
+# LAO_LIBRARY names another build of la_oracle.c to load as it is (the
+# host-sanitizer build the CPU tests make); by default the in-tree one,
+# rebuilt when older than its source.
+_OVERRIDE = os.environ.get("LAO_LIBRARY")
 
 F32, BF16 = 0, 1
 
 _lib = None
+
+
+def build_sanitized(out: str) -> str:
+    """Compile la_oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    (clang, shared ASan runtime, no OpenMP) into out, for the CPU tests that
+    run the oracle's pins under the sanitizers."""
+    clang = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+    cmd = [clang, "-O1", "-g", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-shared-libasan", _SRC, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 def build(verbose: bool = False) -> str:
@@ -46,10 +61,13 @@ def build(verbose: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH) or (
-                os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
-            build()
-        lib = ctypes.CDLL(LIB_PATH)
+        if _OVERRIDE:
+            lib = ctypes.CDLL(_OVERRIDE)
+        else:
+            if not os.path.exists(LIB_PATH) or (
+                    os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
+                build()
+            lib = ctypes.CDLL(LIB_PATH)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.lao_num_threads.restype = I
         lib.lao_forward.argtypes = [P, P, P, I, I, I64, I64, I64, I64, I64, P, I64, P]
