@@ -162,7 +162,8 @@ COUNTERS = {
                ["la_kernels.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
 }
 SINGLE_LAUNCH = {"causal": "k_causal_fused", "forward_bf16": "k_fwd_one", "decode": "k_decode128",
-                 "causal_elu": "k_causal_fused", "forward_elu": "k_fwd_one"}
+                 "causal_elu": "k_causal_fused", "forward_elu": "k_fwd_one", "causal_features": "k_causal_fused",
+                 "causal_bnhd": "k_causal_fused", "varlen": "k_causal_fused", "window": "k_window_fused"}
 
 
 def kernel_source_hash(files):

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblaphi.so")
 ARCH = "gfx950"
 
-SOURCES = ["la_api.cpp", "la_control.hip", "la_noalloc.hip", "la_kernels.hip", "la_fused.hip", "la_forward_bf16.hip", "la_forward_f32.hip", "la_window.hip", "la_backward.hip"]
+SOURCES = ["la_api.cpp", "la_control.hip", "la_noalloc.hip", "la_kernels.hip", "la_fused.hip", "la_forward_bf16.hip", "la_forward_f32.hip", "la_window.hip", "la_window_fused.hip", "la_backward.hip"]
 
 
 def _flags() -> list[str]:

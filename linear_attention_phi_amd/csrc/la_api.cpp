@@ -361,6 +361,7 @@ la_status la_window_forward(const void* q, const void* k, const void* v, int64_t
   SeqCall a{q, k, v, out, Seqs{Hq * n * d, n * d, d, Hkv * n * d, n * d, d, nullptr, n, B * n},
             B, Hq, Hkv, d, (int)dtype, (int)phi, window, d == padded_dim(d) && d * (int64_t)eb >= 16,
             nullptr, nullptr, nullptr, nullptr, stream};
+  if (window_fused_applies(a)) return launch_window_fused(a, false) == 0 ? LA_OK : LA_ERR_LAUNCH;
   const Plan p = seq_plan(a, C);
   if (B * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
   return launch_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
@@ -441,6 +442,7 @@ la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
   a.ctl = reinterpret_cast<Ctl*>(ws);
   a.ws = reinterpret_cast<char*>(ws) + kCtlBytes;
   if (fused) return launch_causal_fused_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
+  if (window_fused_applies(a)) return launch_window_fused(a, true) == 0 ? LA_OK : LA_ERR_LAUNCH;
   return launch_seq(a) == 0 ? LA_OK : LA_ERR_LAUNCH;
 }
 

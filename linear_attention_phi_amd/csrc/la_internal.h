@@ -157,6 +157,12 @@ int launch_seq_prefix(const SeqCall& a, int C);
 bool fused_seq_applies(const SeqCall& a);
 size_t fused_seq_ws_bytes(const SeqCall& a);
 int launch_causal_fused_seq(const SeqCall& a);
+// The sliding-window form on the single-launch kernel (la_window_fused.hip):
+// bf16, d = 64, Hq == Hkv, windows shorter than 576 tokens, the row
+// conditions of fused_seq_applies; no workspace (a.ctl may be NULL).  table:
+// rows through the sequence table, else contiguous [B, H, n, d].
+bool window_fused_applies(const SeqCall& a);
+int launch_window_fused(const SeqCall& a, bool table);
 // Gradients of the causal form (la_backward.hip): contiguous [B, H, n, d],
 // d <= 64.  backward_chunk is 0 where the tiles do not fit in LDS.
 struct BwdCall {

@@ -1189,6 +1189,7 @@ __device__ __forceinline__ int bucket_take(int* cnt, int b, bool valid, int lane
 // [0, n - 1] breaks the form's contract: it is clamped into range (so that
 // every access stays inside the buffers) and recorded in the control
 // block's error word, which la_workspace_status reports.
+template <int PER>
 __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64_t n, int C, int64_t nchunks, int* __restrict__ boff,
                             int* __restrict__ perm, int* cnt, int* part, la_internal::Ctl* ctl) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
@@ -1197,12 +1198,14 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
   for (int c = tid; c < len; c += nt) cnt[c] = 0;
   __syncthreads();
   // queries in blocks of PER per thread: all of a block's mask values are
-  // loaded before its counters are touched
-  constexpr int PER = 8;
+  // requested before its counters are touched.  When one block covers the
+  // whole mask (n <= PER x threads) the bucket of each query stays in
+  // registers for the scatter pass, so the mask is read once.
   const int64_t step = (int64_t)nt * PER;
-  for (int64_t base = 0; base < n; base += step) {
-    int bk[PER];
-    int64_t mv[PER];  // all of the block's loads first (left to itself the
+  const bool one_block = n <= step;
+  int bk[PER];
+  auto buckets = [&](int64_t base, bool count) {
+    int64_t mv[PER];  // every load of the block first (left to itself the
                       // compiler waits for each before issuing the next)
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -1216,11 +1219,14 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
       bk[k] = -1;
       if (i < n) {
         int64_t mi = mv[k];
-        bad |= mi < 0 || mi >= n;
+        if (count) bad |= mi < 0 || mi >= n;
         mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
         bk[k] = (int)(mi / C);
       }
     }
+  };
+  for (int64_t base = 0; base < n; base += step) {
+    buckets(base, true);
 #pragma unroll
     for (int k = 0; k < PER; ++k) bucket_take(cnt, bk[k] + 1, bk[k] >= 0, lane);
   }
@@ -1249,25 +1255,7 @@ __device__ __forceinline__ void bucket_sort(const int64_t* __restrict__ m, int64
   __syncthreads();
   // cnt[c] is now bucket c's fill cursor
   for (int64_t base = 0; base < n; base += step) {
-    int bk[PER];
-    int64_t mv[PER];  // all of the block's loads first (left to itself the
-                      // compiler waits for each before issuing the next)
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int64_t i = base + tid + (int64_t)k * nt;
-      mv[k] = i < n ? m[i] : -1;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int64_t i = base + tid + (int64_t)k * nt;
-      bk[k] = -1;
-      if (i < n) {
-        int64_t mi = mv[k];
-        mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);
-        bk[k] = (int)(mi / C);
-      }
-    }
+    if (!one_block) buckets(base, false);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int pos = bucket_take(cnt, bk[k], bk[k] >= 0, lane);
@@ -1286,7 +1274,7 @@ __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, 
   perm += blockIdx.x * n;
   __shared__ int cnt[la_internal::kMaxBuckets + 1];
   __shared__ int part[1024];
-  bucket_sort(m, n, C, nchunks, boff, perm, cnt, part, ctl);
+  bucket_sort<8>(m, n, C, nchunks, boff, perm, cnt, part, ctl);  // 1024 threads
 }
 
 // ---------------------------------------------------------------- k_state32
@@ -1325,7 +1313,7 @@ __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, co
   int64_t sb = blockIdx.x;  // state block
   if (m) {
     if (sb < nmask) {  // blocks 0 .. nmask - 1 sort the masks
-      bucket_sort(m + sb * n, n, C, nchunks, boff + sb * (nchunks + 1), perm + sb * n, L.b.cnt, L.b.part, ctl);
+      bucket_sort<16>(m + sb * n, n, C, nchunks, boff + sb * (nchunks + 1), perm + sb * n, L.b.cnt, L.b.part, ctl);
       return;
     }
     sb -= nmask;

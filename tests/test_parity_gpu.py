@@ -182,6 +182,30 @@ def test_prefix_f32_d64_query_groups(gpu, kind, shape):
     check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B{B} H{H} n{n} d64 f32")
 
 
+@pytest.mark.parametrize("dtype", [li.F32, li.BF16])
+@pytest.mark.parametrize("kind", ["random", "causal"])
+@pytest.mark.parametrize("batched", [False, True])
+def test_prefix_sort_over_several_blocks(gpu, dtype, kind, batched):
+    """n = 20000 queries: more than one block of the bucket sort (8192 mask
+    values per pass in the fp32 state launch's sort blocks and in the sort
+    launch of the other kernels), so the scatter pass reloads the mask block
+    by block.  Sampled rows of every batch against the oracle."""
+    B, H, n = (2, 1, 20000) if batched else (1, 2, 20000)
+    q, k, v, rng = li.qkv(B, H, H, n, 64, dtype, seed=11, scaled=True)
+    if batched:
+        m = np.stack([li.mask(n, kind, rng=rng) for _ in range(B)])
+        g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m)))
+    else:
+        m = li.mask(n, kind, rng=rng)
+        g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m)))
+    rows = np.unique(np.concatenate([rng.choice(n, 150, replace=False), [0, 8191, 8192, n - 1]]))
+    for b in range(B):
+        mb = m[b] if batched else m
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1])
+        ref = oracle.prefix_mask(sl(q), sl(k), sl(v), mb, rows=rows)
+        check(g[b:b + 1, :, rows], ref, dtype, f"prefix {dtype} {kind} n{n} batch {b} (sampled rows)")
+
+
 @pytest.mark.parametrize("phi", ["relu1", "elu1"])
 @pytest.mark.parametrize("shape", [(1, 2, 1000), (2, 3, 300), (1, 1, 64), (1, 1, 5)], ids=lambda c: "B%d_H%d_n%d" % c)
 def test_causal_f32_d64_chunk64_output_kernel(gpu, phi, shape):

@@ -229,3 +229,33 @@ def test_unaligned_token_stride_takes_general_path(gpu):
     out = ob[..., :d].transpose(1, 2)
     gpu.la_causal_forward_strided(qd, kd, vd, out=out)
     check(host(out.contiguous()), oracle.causal(q, k, v), li.BF16, "token stride 136 bytes")
+
+
+@pytest.mark.parametrize("w", [50, 64, 300, 512])
+def test_packed_window_single_launch(gpu, w):
+    """The sliding window over packed sequences of 0 .. 2100 tokens with one
+    query head per key/value head (the single-launch window kernel through
+    the table): every sequence against the oracle on that sequence alone."""
+    import torch
+    H, d = 3, 64
+    cu = np.concatenate([[0], np.cumsum(LONG_LENGTHS)]).astype(np.int64)
+    total = int(cu[-1])
+    q, k, v, _ = li.qkv(1, H, H, total, d, li.BF16, seed=370 + w, scaled=True)
+    pk = lambda x: dev(np.ascontiguousarray(x[0].transpose(1, 0, 2)))
+    out = gpu.la_causal_forward_strided(pk(q), pk(k), pk(v), cu_seqlens=torch.from_numpy(cu).cuda(), window=w)
+    g = host(out)
+    for s, L in enumerate(LONG_LENGTHS):
+        if L == 0:
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        sl = lambda x: np.ascontiguousarray(x[:, :, a:b])
+        check(g[a:b].transpose(1, 0, 2)[None], oracle.window(sl(q), sl(k), sl(v), w), li.BF16,
+              f"packed window w={w} seq {s} (length {L})")
+
+
+def test_bnhd_window_single_launch(gpu):
+    """[B, n, H, d] rows with a 200-token window, H = Hkv = 4, n = 1300."""
+    B, H, n, d, w = 2, 4, 1300, 64, 200
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.BF16, seed=380, scaled=True)
+    out = gpu.la_causal_forward_strided(bnhd(q), bnhd(k), bnhd(v), window=w)
+    check(host(out.contiguous()), oracle.window(q, k, v, w), li.BF16, "BNHD window w200")

@@ -89,3 +89,36 @@ def test_window_B8_H8_n2048_d64_bf16_w512(gpu):
     lo = np.maximum(np.arange(n) - w + 1, 0)
     want = (c[:, :, np.arange(n) + 1] - c[:, :, lo]) / (np.arange(n) + 1 - lo)[None, None, :, None]
     check(ge, want, li.BF16, "window equal keys, every row")
+
+
+# One query head per key/value head, bf16, d = 64: the single-launch window
+# kernel (w < 576: up to seven chunks of halo).  Windows around every chunk
+# boundary it treats differently: w < 64 (leading band only), multiples of
+# 64 (one trailing chunk), w = 64 k + 1 .. 64 k + 63 (two trailing chunks).
+FUSED_WINDOWS = [1, 2, 31, 63, 64, 65, 100, 127, 128, 129, 191, 192, 200, 300, 447, 448, 449, 511, 512, 513, 575]
+
+
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("w", FUSED_WINDOWS)
+def test_window_single_launch(gpu, phi, w):
+    """B2 H3 n1500 (three segments of eight chunks, the last ragged): every
+    row against the oracle."""
+    B, H, n, d = 2, 3, 1500, 64
+    q, k, v, _ = li.qkv(B, H, H, n, d, li.BF16, seed=220 + w, scaled=True)
+    g = gpu.la_window_forward(dev(q), dev(k), dev(v), w, phi=phi)
+    check(host(g), oracle.window(q, k, v, w, phi=phi), li.BF16, f"window (single launch) {phi} w={w}")
+
+
+def test_window_single_launch_equal_keys_every_row(gpu):
+    """Equal keys make every weight equal: out_i is the mean of V over the
+    window, a closed form that the halo and own parts must both respect
+    (n = 4000, w = 383: two trailing chunks, five halo chunks)."""
+    B, H, n, d, w = 1, 4, 4000, 64, 383
+    q, k, v, rng = li.qkv(B, H, H, n, d, li.BF16, seed=230, scaled=True)
+    row = li.as_dtype(rng.standard_normal(d, dtype=np.float32) / 8, li.BF16)
+    ke = np.ascontiguousarray(np.broadcast_to(row, (B, H, n, d)))
+    g = host(gpu.la_window_forward(dev(q), dev(ke), dev(v), w))
+    c = np.cumsum(np.concatenate([np.zeros((B, H, 1, d)), li.to_f32(v).astype(np.float64)], axis=2), axis=2)
+    lo = np.maximum(np.arange(n) - w + 1, 0)
+    want = (c[:, :, np.arange(n) + 1] - c[:, :, lo]) / (np.arange(n) + 1 - lo)[None, None, :, None]
+    check(g, want, li.BF16, "window w383 equal keys, every row")
