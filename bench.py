@@ -74,6 +74,8 @@ WORKLOADS = {
     "causal_features": dict(form="causal", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", chunk=64, scaled=True,
                             steps=200, phi="features"),
     "backward": dict(form="backward", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", scaled=True, steps=50),
+    # grouped query heads at d = 64 (four per key/value head) on the single-launch kernel
+    "gqa_d64": dict(form="causal", B=4, Hq=16, Hkv=4, n=2048, d=64, dt="bf16", chunk=64, scaled=True, steps=200),
 }
 
 DESCRIPTIONS = {
@@ -93,6 +95,7 @@ DESCRIPTIONS = {
     "varlen": "causal normalised linear attention on 16 packed sequences of 128..2048 tokens (cu_seqlens), bf16",
     "causal_features": "causal normalised linear attention on caller-applied features (softplus), bf16",
     "backward": "gradients dQ, dK, dV of the causal form (phi=relu+1), bf16 in, fp32 products",
+    "gqa_d64": "causal normalised linear attention, four query heads per key/value head, d 64, bf16",
 }
 
 # The packed-sequence workload's lengths: 16 sequences drawn uniformly from
@@ -163,7 +166,8 @@ COUNTERS = {
 }
 SINGLE_LAUNCH = {"causal": "k_causal_fused", "forward_bf16": "k_fwd_one", "decode": "k_decode128",
                  "causal_elu": "k_causal_fused", "forward_elu": "k_fwd_one", "causal_features": "k_causal_fused",
-                 "causal_bnhd": "k_causal_fused", "varlen": "k_causal_fused", "window": "k_window_fused"}
+                 "causal_bnhd": "k_causal_fused", "varlen": "k_causal_fused", "window": "k_window_fused",
+                 "gqa_d64": "k_causal_fused"}
 
 
 def kernel_source_hash(files):

@@ -116,7 +116,7 @@ size_t required_ws(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_t n, in
   if (op == LA_OP_PREFIX_MASK) bytes += bucket_bytes(n, C);
   if (op == LA_OP_PREFIX_MASK_BATCHED) bytes += (size_t)B * bucket_bytes(n, C);  // one sort per batch
   if (op == LA_OP_CAUSAL && fused_causal_applies(Hq, Hkv, n, d, (int)dt, C)) {
-    const size_t f = fused_causal_ws_bytes(B * Hkv, make_fused_plan(n).nseg);
+    const size_t f = fused_causal_ws_bytes(B * Hq, make_fused_plan(n).nseg);  // one set per query head
     if (f > bytes) bytes = f;
   }
   if (op == LA_OP_FORWARD && forward_bf16_applies(n, d, (int)dt)) {
@@ -193,12 +193,13 @@ size_t la_workspace_bytes(int32_t op, int64_t B, int64_t Hq, int64_t Hkv, int64_
     SeqCall a{};
     a.S.n = n;
     a.nseq = B;
+    a.Hq = Hq;
     a.Hkv = Hkv;
     a.d = d;
     // the general kernels' segment states, or the single-launch kernel's
     // aggregates where the strides may let it run
     const size_t general = state_bytes(seq_plan(a, C), B, Hkv);
-    const size_t fused = dtype == LA_BF16 && Hq == Hkv && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, 64)
+    const size_t fused = dtype == LA_BF16 && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, 64)
                              ? fused_seq_ws_bytes(a)
                              : 0;
     return kCtlBytes + (general > fused ? general : fused);
@@ -289,7 +290,7 @@ la_status la_causal_forward_phi(const void* q, const void* k, const void* v, int
   attach_ws(a, ws);
   if (q && fused_causal_applies(Hq, Hkv, n, d, (int)dtype, C)) {  // every feature map
     const Plan fp = make_fused_plan(n);
-    if (B * Hkv * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
+    if (B * Hq * fp.nseg >= kMaxGrid) return LA_ERR_SHAPE;
     return launch_causal_fused(a, fp) == 0 ? LA_OK : LA_ERR_LAUNCH;
   }
   return launch_causal(a, p) == 0 ? LA_OK : LA_ERR_LAUNCH;
@@ -431,7 +432,7 @@ la_status la_causal_forward_strided(const void* q, const void* k, const void* v,
   const Plan p = seq_plan(a, C);
   if (nseq * Hkv * p.nseg >= kMaxGrid) return LA_ERR_SHAPE;
   const bool fused = fused_seq_applies(a);
-  if (fused && nseq * Hkv * ((max_len + kFusedG * 64 - 1) / (kFusedG * 64)) >= kMaxGrid) return LA_ERR_SHAPE;
+  if (fused && nseq * Hq * ((max_len + kFusedG * 64 - 1) / (kFusedG * 64)) >= kMaxGrid) return LA_ERR_SHAPE;
   const size_t need = kCtlBytes + (fused ? fused_seq_ws_bytes(a) : window > 0 ? 0 : state_bytes(p, nseq, Hkv));
   if ((st = check_ws(ws, ws_bytes, need)) != LA_OK) return st;
   for (int i = 0; i < 3; ++i)

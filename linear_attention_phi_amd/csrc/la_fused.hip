@@ -1,5 +1,5 @@
 // la_fused.hip -- single-launch causal kernel for bf16 inputs, d = 64,
-// chunk 64, one query head per key/value head (gfx950).
+// chunk 64, up to kFusedMaxR query heads per key/value head (gfx950).
 //
 // Same mathematics as the three-launch path in la_kernels.hip (causal form:
 // out_i = phi(Q_i) S_i / (phi(Q_i) . z_i) with S_i, z_i over keys 0..i;
@@ -62,14 +62,21 @@ constexpr int AGG_FLOATS = FD * FD + FD;  // published segment aggregate: S^T [b
 constexpr int TILE_B = FC * RS * 2;       // bytes of one token-major bf16 tile
 constexpr int REGION_B = 2 * TILE_B;      // one wave's LDS region
 
-// Rows come through a sequence table: row t of head h of sequence s at
-// q + s qb + start(s) qt + h qh + t qt (K and V with kb, kt, kh; out with the
-// q strides), start(s) = cu[s] for packed sequences of different lengths and
-// 0 for one length n.  "head" below is u = s H + h.
+// Rows come through a sequence table: row t of query head h of sequence s at
+// q + s qb + start(s) qt + h qh + t qt, of its key/value head h / R at
+// k + s kb + start(s) kt + (h / R) kh + t kt (out with the q strides),
+// start(s) = cu[s] for packed sequences of different lengths and 0 for one
+// length n.  "head" below is the query head u = s H + h.  With R > 1 query
+// heads per key/value head every query head runs as a head of its own (its
+// own segment states, aggregates and flags, the key/value head's rows read
+// by each); xcd: the R heads of a group are dispatched eight apart, so that
+// they run on one XCD (workgroups go to the eight XCDs in turn) and read
+// their K and V rows through its L2.
 struct FusedArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* out;
-  int64_t n, nchunks, nseg, NH;  // n, nchunks, nseg: of the longest sequence; NH = sequences x heads
-  int64_t H, qb, qh, qt, kb, kh, kt;
+  int64_t n, nchunks, nseg, NH;  // n, nchunks, nseg: of the longest sequence; NH = sequences x query heads
+  int64_t H, qb, qh, qt, kb, kh, kt;  // H: query heads per sequence
+  int R, xcd;                          // query heads per key/value head; dispatch order (above)
   const int64_t* cu; int64_t total;  // cu NULL: every sequence holds n tokens
   float* agg; uint64_t* flags;
   float* S_final; float* z_final; la_internal::Ctl* ctl;
@@ -110,14 +117,24 @@ __device__ __forceinline__ float* state_row(CpLds& L, int c, int b) {
 // SEQ: rows through the sequence table (runtime strides, cu); without it the
 // rows are contiguous [B, H, n, d] (compile-time strides: the address
 // arithmetic of the loads and stores folds into immediate offsets).
-template <int PM, bool SEQ>
+// GQA: several query heads per key/value head (R > 1, the dispatch order
+// above); without it every head is its own key/value head.
+template <int PM, bool SEQ, bool GQA>
 __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) CpLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
   // grid (heads of every sequence, segments): x varies fastest, so the
   // dispatch order is segment-major
-  const int64_t seg = blockIdx.y, head = blockIdx.x;
+  const int64_t seg = blockIdx.y;
+  uint32_t head32 = blockIdx.x;
+  if (GQA && A.xcd) {  // dispatch index -> (group, member): groups of eight take 8 R consecutive indices
+    const uint32_t blk = blockIdx.x / (8u * A.R), rem = blockIdx.x - blk * 8u * A.R;
+    head32 = (blk * 8u + (rem & 7u)) * A.R + (rem >> 3);
+  }
+  const int64_t head = head32;                        // the query head
+  const uint32_t member = GQA ? head32 % (uint32_t)A.R : 0u;
+  const int64_t kvhead = GQA ? head32 / (uint32_t)A.R : head32;
   // the control words are requested first; wave 0 uses them after its loads
   la_ctl::CtlView cv{};
   if (w == 0) cv = la_ctl::ctl_load(A.ctl);
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   // leaves the sequence empty and is recorded once, by its first segment)
   int64_t start = 0, len = A.n;
   if (SEQ && A.cu) {
-    const int64_t sq = blockIdx.x / (uint32_t)A.H;
+    const int64_t sq = head32 / (uint32_t)A.H;
     const int64_t a = A.cu[sq], b = A.cu[sq + 1], prev = sq > 0 ? A.cu[sq - 1] : 0;
     if (a < prev || b < a || b > A.total || b - a > A.n) {
       if (seg == 0 && tid == 0) la_ctl::ctl_fail(A.ctl, la_internal::kErrRange);
@@ -138,10 +155,10 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   }
   const int64_t nch = (len + FC - 1) / FC, nseg_s = (nch + SEGC - 1) / SEGC;
   if (SEQ && seg >= nseg_s) {  // past this sequence's end (the grid covers the longest)
-    if (seg == 0 && len == 0) {  // an empty sequence's final state is zero
+    if (seg == 0 && len == 0 && member == 0) {  // an empty sequence's final state is zero
       if (A.S_final)
-        for (int e = tid; e < FD * FD; e += FNT) A.S_final[head * FD * FD + e] = 0.0f;
-      if (A.z_final && tid < FD) A.z_final[head * FD + tid] = 0.0f;
+        for (int e = tid; e < FD * FD; e += FNT) A.S_final[kvhead * FD * FD + e] = 0.0f;
+      if (A.z_final && tid < FD) A.z_final[kvhead * FD + tid] = 0.0f;
     }
     if (tid == 0 && !A.host_epoch) {
       const uint32_t arrived = la_ctl::ctl_arrive(A.ctl, cv);
@@ -153,15 +170,15 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
   // its end read as zero and are not written; the caller keeps row strides
   // >= 64 elements and every offset below 2^31 bytes)
   int qbytes = (int)(A.n * FD * 2), kbytes = qbytes;
-  int64_t qoff = head * A.n * FD, koff = qoff;
+  int64_t qoff = head * A.n * FD, koff = kvhead * A.n * FD;
   int qs = FD * 2, ks = FD * 2;  // row strides in bytes
   if (SEQ) {
-    const uint32_t sq32 = blockIdx.x / (uint32_t)A.H;
-    const int64_t sq = sq32, hh = blockIdx.x - sq32 * (uint32_t)A.H;
+    const uint32_t sq32 = head32 / (uint32_t)A.H;
+    const int64_t sq = sq32, hh = head32 - sq32 * (uint32_t)A.H;
     qbytes = (int)(((len - 1) * A.qt + FD) * 2);
     kbytes = (int)(((len - 1) * A.kt + FD) * 2);
     qoff = sq * A.qb + start * A.qt + hh * A.qh;
-    koff = sq * A.kb + start * A.kt + hh * A.kh;
+    koff = sq * A.kb + start * A.kt + (GQA ? hh / A.R : hh) * A.kh;
     qs = (int)A.qt * 2;
     ks = (int)A.kt * 2;
   }
@@ -476,13 +493,13 @@ __global__ __launch_bounds__(FNT, 1) void k_causal_fused(FusedArgs A) {
     *reinterpret_cast<u32x4*>(L.sprev + sb * RS + sa) = u32x4{y[0], y[1], y[2], y[3]};
     if (w == 0) store_z_pairs(L.zhp, L.zlp, zprev, lane);
   }
-  if (seg == nseg_s - 1) {
+  if (seg == nseg_s - 1 && member == 0) {  // the group's first member writes the final state
     if (A.S_final) {
-      float* Sf = A.S_final + head * FD * FD;
+      float* Sf = A.S_final + kvhead * FD * FD;
 #pragma unroll
       for (int e = 0; e < 8; ++e) Sf[(sa + e) * FD + sb] = sp[e] + run[e];
     }
-    if (A.z_final && w == 0) A.z_final[head * FD + lane] = zprev + zrun;
+    if (A.z_final && w == 0) A.z_final[kvhead * FD + lane] = zprev + zrun;
   }
   __syncthreads();
 
@@ -525,8 +542,9 @@ namespace la_internal {
 bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk) {
   // n bound: every segment sums the aggregates of all earlier segments of its
   // head, so the look-back grows with n; longer sequences take the
-  // three-launch path, whose scan is linear in the number of segments
-  return dtype == 1 && d == FD && Hq == Hkv && chunk == FC && n <= kFusedMaxN;
+  // three-launch path, whose scan is linear in the number of segments.  R
+  // bound: each query head reads its key/value head's rows again
+  return dtype == 1 && d == FD && Hq % Hkv == 0 && Hq / Hkv <= kFusedMaxR && chunk == FC && n <= kFusedMaxN;
 }
 
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {
@@ -535,47 +553,63 @@ size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {
 
 bool fused_seq_applies(const SeqCall& a) {
   const int64_t rs = a.S.qt > a.S.kt ? a.S.qt : a.S.kt;
-  return a.q && a.window == 0 && a.vec && a.S.qt >= FD && a.S.kt >= FD && a.Hq == a.Hkv &&
+  return a.q && a.window == 0 && a.vec && a.S.qt >= FD && a.S.kt >= FD &&
          fused_causal_applies(a.Hq, a.Hkv, a.S.n, a.d, a.dtype, FC) && (a.S.n + FC) * rs * 2 < ((int64_t)1 << 31);
+}
+
+template <bool SEQ, bool GQA>
+static void launch_fused_pm(const FusedArgs& A, int phi, hipStream_t st) {
+  const dim3 grid((unsigned)A.NH, (unsigned)A.nseg);
+  if (phi == 2)
+    k_causal_fused<PM_FEAT, SEQ, GQA><<<grid, FNT, 0, st>>>(A);
+  else if (phi == 1)
+    k_causal_fused<PM_ELU1, SEQ, GQA><<<grid, FNT, 0, st>>>(A);
+  else
+    k_causal_fused<PM_RELU1, SEQ, GQA><<<grid, FNT, 0, st>>>(A);
 }
 
 template <bool SEQ>
 static int launch_fused(FusedArgs& A, int phi, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   static_assert(kFusedG == SEGC, "segment length");
-  const dim3 grid((unsigned)A.NH, (unsigned)A.nseg);
   A.flags = reinterpret_cast<uint64_t*>(A.agg + A.NH * A.nseg * AGG_FLOATS);
   A.host_epoch = launch_epoch(stream);
-  if (phi == 2)
-    k_causal_fused<PM_FEAT, SEQ><<<grid, FNT, 0, st>>>(A);
-  else if (phi == 1)
-    k_causal_fused<PM_ELU1, SEQ><<<grid, FNT, 0, st>>>(A);
+  // the GQA instantiation only where needed: the kernel's schedule is
+  // sensitive to the extra index arithmetic (0.8 us on the B8 H8 n2048 call)
+  if (A.R > 1)
+    launch_fused_pm<SEQ, true>(A, phi, st);
   else
-    k_causal_fused<PM_RELU1, SEQ><<<grid, FNT, 0, st>>>(A);
+    launch_fused_pm<SEQ, false>(A, phi, st);
   return (int)hipGetLastError();
 }
 
+// The XCD-aware dispatch order needs whole blocks of eight groups.
+static int xcd_order(int64_t groups, int R) { return R > 1 && groups % 8 == 0; }
+
 int launch_causal_fused(const Fwd& a, const Plan& p) {
-  const int64_t H = a.Hkv, n = a.n;
+  const int64_t n = a.n;
+  const int R = (int)(a.Hq / a.Hkv);
   FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
-              reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), n, p.nchunks, p.nseg, a.B * H,
-              H, H * n * FD, n * FD, FD, H * n * FD, n * FD, FD, nullptr, a.B * n,
-              reinterpret_cast<float*>(a.ws), nullptr, a.S_final, a.z_final, a.ctl, 0};
+              reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), n, p.nchunks, p.nseg,
+              a.B * a.Hq, a.Hq, a.Hq * n * FD, n * FD, FD, a.Hkv * n * FD, n * FD, FD, R, xcd_order(a.B * a.Hkv, R),
+              nullptr, a.B * n, reinterpret_cast<float*>(a.ws), nullptr, a.S_final, a.z_final, a.ctl, 0};
   return launch_fused<false>(A, a.phi, a.stream);
 }
 
 int launch_causal_fused_seq(const SeqCall& a) {
   const int64_t nchunks = (a.S.n + FC - 1) / FC;
+  const int R = (int)(a.Hq / a.Hkv);
   FusedArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
               reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.S.n, nchunks,
-              (nchunks + SEGC - 1) / SEGC, a.nseq * a.Hkv, a.Hkv, a.S.qb, a.S.qh, a.S.qt, a.S.kb, a.S.kh, a.S.kt,
-              a.S.cu, a.S.total, reinterpret_cast<float*>(a.ws), nullptr, a.S_final, a.z_final, a.ctl, 0};
+              (nchunks + SEGC - 1) / SEGC, a.nseq * a.Hq, a.Hq, a.S.qb, a.S.qh, a.S.qt, a.S.kb, a.S.kh, a.S.kt,
+              R, xcd_order(a.nseq * a.Hkv, R), a.S.cu, a.S.total, reinterpret_cast<float*>(a.ws), nullptr,
+              a.S_final, a.z_final, a.ctl, 0};
   return launch_fused<true>(A, a.phi, a.stream);
 }
 
 size_t fused_seq_ws_bytes(const SeqCall& a) {
   const int64_t nchunks = (a.S.n + FC - 1) / FC;
-  return fused_causal_ws_bytes(a.nseq * a.Hkv, (nchunks + SEGC - 1) / SEGC);
+  return fused_causal_ws_bytes(a.nseq * a.Hq, (nchunks + SEGC - 1) / SEGC);
 }
 
 }  // namespace la_internal

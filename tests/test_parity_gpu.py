@@ -182,6 +182,24 @@ def test_prefix_f32_d64_query_groups(gpu, kind, shape):
     check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B{B} H{H} n{n} d64 f32")
 
 
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("shape", [(1, 4, 2, 1500), (2, 8, 2, 700), (4, 16, 2, 600), (1, 64, 8, 300), (3, 6, 3, 513)],
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_n%d" % c)
+def test_causal_gqa_single_launch(gpu, phi, shape):
+    """bf16, d = 64, several query heads per key/value head (2 to 8): the
+    single-launch causal kernel with each query head on its own segment
+    chain (B4 Hq16 Hkv2 and B1 Hq64 Hkv8 hold whole blocks of eight groups:
+    the XCD-grouped dispatch order).  Every row, and the final state of
+    every key/value head."""
+    B, Hq, Hkv, n = shape
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, 64, li.BF16, seed=13, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True, phi=phi)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True, phi=phi)
+    check(host(out), ref, li.BF16, f"causal GQA {phi} B{B} Hq{Hq} Hkv{Hkv} n{n}")
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-2, atol=1e-2 * np.abs(Sr).max())
+
+
 @pytest.mark.parametrize("dtype", [li.F32, li.BF16])
 @pytest.mark.parametrize("kind", ["random", "causal"])
 @pytest.mark.parametrize("batched", [False, True])
