@@ -159,7 +159,8 @@ bool fused_seq_applies(const SeqCall& a);
 size_t fused_seq_ws_bytes(const SeqCall& a);
 int launch_causal_fused_seq(const SeqCall& a);
 // The sliding-window form on the single-launch kernel (la_window_fused.hip):
-// bf16, d = 64, Hq == Hkv, windows shorter than 576 tokens, the row
+// bf16, d = 64, up to kFusedMaxR query heads per key/value head, windows
+// shorter than 576 tokens, the row
 // conditions of fused_seq_applies; no workspace (a.ctl may be NULL).  table:
 // rows through the sequence table, else contiguous [B, H, n, d].
 bool window_fused_applies(const SeqCall& a);

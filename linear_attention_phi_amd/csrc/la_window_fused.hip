@@ -1,6 +1,6 @@
 // la_window_fused.hip -- single-launch sliding-window kernel for bf16 inputs,
-// d = 64, chunk 64, one query head per key/value head, windows w < 576
-// (gfx950).
+// d = 64, chunk 64, up to eight query heads per key/value head, windows
+// w < 576 (gfx950).
 //
 // LinearTile 1.0.1, "Features" (sliding-window attention, local context),
 // with the normalised read of nx_f32_linear_attention.nx: query i sees the
@@ -59,10 +59,15 @@ constexpr int TILE_B = FC * RS * 2;       // bytes of one token-major bf16 tile
 constexpr int REGION_B = 2 * TILE_B;      // one wave's LDS region
 constexpr int kMaxNfull = SEGC - 1;       // halo chunks a segment can hold
 
+// Heads: as in la_fused.hip, query head u = s H + h (H query heads per
+// sequence) reads key/value head h / R; with R > 1 each query head
+// recomputes its group's chunk states, and the group's heads are dispatched
+// eight apart (xcd) so that they share K and V through one XCD's L2.
 struct WfArgs {
   const bf16* q; const bf16* k; const bf16* v; bf16* out;
-  int64_t n, nseg, NH;  // n, nseg: of the longest sequence; NH = sequences x heads
+  int64_t n, nseg, NH;  // n, nseg: of the longest sequence; NH = sequences x query heads
   int64_t H, qb, qh, qt, kb, kh, kt;
+  int R, xcd;
   const int64_t* cu; int64_t total;  // cu NULL: every sequence holds n tokens
   int nfull, delta, wlen;            // the window's decomposition (header)
   la_internal::Ctl* ctl;             // NULL: nothing to report
@@ -84,15 +89,22 @@ __device__ __forceinline__ float* state_row(WfLds& L, int c, int b) {
   return reinterpret_cast<float*>(L.reg[c] + (b < 32 ? TILE_B : 0)) + (b & 31) * RSF;
 }
 
-template <int PM, bool SEQ>
+template <int PM, bool SEQ, bool GQA>
 __global__ __launch_bounds__(FNT, 1) void k_window_fused(WfArgs A) {
   constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) WfLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int64_t seg = blockIdx.y, head = blockIdx.x;
+  const int64_t seg = blockIdx.y;
+  uint32_t head32 = blockIdx.x;
+  if (GQA && A.xcd) {  // dispatch index -> (group, member): groups of eight take 8 R consecutive indices
+    const uint32_t blk = blockIdx.x / (8u * A.R), rem = blockIdx.x - blk * 8u * A.R;
+    head32 = (blk * 8u + (rem & 7u)) * A.R + (rem >> 3);
+  }
+  const int64_t head = head32;
+  const int64_t kvhead = GQA ? head32 / (uint32_t)A.R : head32;
   int64_t start = 0, len = A.n;
   if (SEQ && A.cu) {
-    const int64_t sq = blockIdx.x / (uint32_t)A.H;
+    const int64_t sq = head32 / (uint32_t)A.H;
     const int64_t a = A.cu[sq], b = A.cu[sq + 1], prev = sq > 0 ? A.cu[sq - 1] : 0;
     if (a < prev || b < a || b > A.total || b - a > A.n) {
       if (seg == 0 && tid == 0 && A.ctl) la_ctl::ctl_fail(A.ctl, la_internal::kErrRange);
@@ -105,15 +117,15 @@ __global__ __launch_bounds__(FNT, 1) void k_window_fused(WfArgs A) {
   const int64_t nch = (len + FC - 1) / FC;
   if (SEQ && seg * SEGC >= nch) return;  // past this sequence's end (the grid covers the longest)
   int qbytes = (int)(A.n * FD * 2), kbytes = qbytes;
-  int64_t qoff = head * A.n * FD, koff = qoff;
+  int64_t qoff = head * A.n * FD, koff = kvhead * A.n * FD;
   int qs = FD * 2, ks = FD * 2;  // row strides in bytes
   if (SEQ) {
-    const uint32_t sq32 = blockIdx.x / (uint32_t)A.H;
-    const int64_t sq = sq32, hh = blockIdx.x - sq32 * (uint32_t)A.H;
+    const uint32_t sq32 = head32 / (uint32_t)A.H;
+    const int64_t sq = sq32, hh = head32 - sq32 * (uint32_t)A.H;
     qbytes = (int)(((len - 1) * A.qt + FD) * 2);
     kbytes = (int)(((len - 1) * A.kt + FD) * 2);
     qoff = sq * A.qb + start * A.qt + hh * A.qh;
-    koff = sq * A.kb + start * A.kt + hh * A.kh;
+    koff = sq * A.kb + start * A.kt + (GQA ? hh / A.R : hh) * A.kh;
     qs = (int)A.qt * 2;
     ks = (int)A.kt * 2;
   }
@@ -502,16 +514,24 @@ __global__ __launch_bounds__(FNT, 1) void k_window_fused(WfArgs A) {
   }
 }
 
+template <bool SEQ, bool GQA>
+void launch_pm(const WfArgs& A, int phi, hipStream_t st) {
+  const dim3 grid((unsigned)A.NH, (unsigned)A.nseg);
+  if (phi == 2)
+    k_window_fused<PM_FEAT, SEQ, GQA><<<grid, FNT, 0, st>>>(A);
+  else if (phi == 1)
+    k_window_fused<PM_ELU1, SEQ, GQA><<<grid, FNT, 0, st>>>(A);
+  else
+    k_window_fused<PM_RELU1, SEQ, GQA><<<grid, FNT, 0, st>>>(A);
+}
+
 template <bool SEQ>
 int launch(WfArgs& A, int phi, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)A.NH, (unsigned)A.nseg);
-  if (phi == 2)
-    k_window_fused<PM_FEAT, SEQ><<<grid, FNT, 0, st>>>(A);
-  else if (phi == 1)
-    k_window_fused<PM_ELU1, SEQ><<<grid, FNT, 0, st>>>(A);
+  if (A.R > 1)
+    launch_pm<SEQ, true>(A, phi, st);
   else
-    k_window_fused<PM_RELU1, SEQ><<<grid, FNT, 0, st>>>(A);
+    launch_pm<SEQ, false>(A, phi, st);
   return (int)hipGetLastError();
 }
 
@@ -528,15 +548,18 @@ namespace la_internal {
 bool window_fused_applies(const SeqCall& a) {
   const int64_t rs = a.S.qt > a.S.kt ? a.S.qt : a.S.kt;
   const int64_t nfull = a.window / FC > 1 ? a.window / FC - 1 : 0;
-  return a.q && a.window >= 1 && nfull <= kMaxNfull && a.dtype == 1 && a.d == FD && a.Hq == a.Hkv && a.vec &&
+  return a.q && a.window >= 1 && nfull <= kMaxNfull && a.dtype == 1 && a.d == FD && a.Hq % a.Hkv == 0 &&
+         a.Hq / a.Hkv <= kFusedMaxR && a.vec &&
          a.S.qt >= FD && a.S.kt >= FD && (a.S.n + FC) * rs * 2 < ((int64_t)1 << 31);
 }
 
 int launch_window_fused(const SeqCall& a, bool table) {
   const int64_t nchunks = (a.S.n + FC - 1) / FC;
+  const int R = (int)(a.Hq / a.Hkv);
   WfArgs A{reinterpret_cast<const bf16*>(a.q), reinterpret_cast<const bf16*>(a.k),
            reinterpret_cast<const bf16*>(a.v), reinterpret_cast<bf16*>(a.out), a.S.n, (nchunks + SEGC - 1) / SEGC,
-           a.nseq * a.Hkv, a.Hkv, a.S.qb, a.S.qh, a.S.qt, a.S.kb, a.S.kh, a.S.kt, a.S.cu, a.S.total, 0, 0, 0, a.ctl};
+           a.nseq * a.Hq, a.Hq, a.S.qb, a.S.qh, a.S.qt, a.S.kb, a.S.kh, a.S.kt, R,
+           R > 1 && (a.nseq * a.Hkv) % 8 == 0, a.S.cu, a.S.total, 0, 0, 0, a.ctl};
   decompose(A, a.window);
   return table ? launch<true>(A, a.phi, a.stream) : launch<false>(A, a.phi, a.stream);
 }

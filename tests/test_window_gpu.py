@@ -122,3 +122,16 @@ def test_window_single_launch_equal_keys_every_row(gpu):
     lo = np.maximum(np.arange(n) - w + 1, 0)
     want = (c[:, :, np.arange(n) + 1] - c[:, :, lo]) / (np.arange(n) + 1 - lo)[None, None, :, None]
     check(g, want, li.BF16, "window w383 equal keys, every row")
+
+
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("shape", [(2, 16, 4, 1100, 300), (1, 6, 2, 900, 512), (1, 64, 8, 700, 64)],
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_n%d_w%d" % c)
+def test_window_single_launch_gqa(gpu, phi, shape):
+    """Grouped query heads on the single-launch window kernel (two to eight
+    per key/value head; B2 Hq16 Hkv4 and B1 Hq64 Hkv8 take the XCD-grouped
+    dispatch order): every row against the oracle."""
+    B, Hq, Hkv, n, w = shape
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, 64, li.BF16, seed=240 + w, scaled=True)
+    g = gpu.la_window_forward(dev(q), dev(k), dev(v), w, phi=phi)
+    check(host(g), oracle.window(q, k, v, w, phi=phi), li.BF16, f"window GQA {phi} {shape}")
