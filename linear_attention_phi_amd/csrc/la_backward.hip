@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   // token-major: phi(Q), phi(K), V, dO then G; feature-major: the same four
   __shared__ __attribute__((aligned(16))) T sQ[C * LQ];
   __shared__ __attribute__((aligned(16))) T sK[C * LQ];
-  __shared__ __attribute__((aligned(16))) T sV[C * LQ];
+  __shared__ __attribute__((aligned(16))) T sV[GRAD ? C * LQ : 8];  // token-major V: the gradients only
   __shared__ __attribute__((aligned(16))) T sG[C * LQ];
   __shared__ __attribute__((aligned(16))) T sQT[DP * LC];
   __shared__ __attribute__((aligned(16))) T sKT[DP * LC];
@@ -122,18 +122,22 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   __shared__ __attribute__((aligned(16))) T sGT[DP * LC];
   // S^T (rows b, k = a) and, for the gradients, S, U (rows a, k = b) and U^T
   __shared__ __attribute__((aligned(16))) T sST[DP * LQ];
-  __shared__ __attribute__((aligned(16))) T sS[GRAD ? DP * LQ : 8];
-  __shared__ __attribute__((aligned(16))) T sU[GRAD ? DP * LQ : 8];
-  __shared__ __attribute__((aligned(16))) T sUT[GRAD ? DP * LQ : 8];
-  // P[i][j], then A[i][j]; P^T and A^T ([j][i])
-  __shared__ __attribute__((aligned(16))) T sP[C * LC];
-  __shared__ __attribute__((aligned(16))) T sPT[GRAD ? C * LC : 8];
-  __shared__ __attribute__((aligned(16))) T sAT[GRAD ? C * LC : 8];
+  __shared__ __attribute__((aligned(16))) T sS[GRAD ? DP * LQ : 1];
+  __shared__ __attribute__((aligned(16))) T sU[GRAD ? DP * LQ : 1];
+  __shared__ __attribute__((aligned(16))) T sUT[GRAD ? DP * LQ : 1];
+  // P[i][j], then A[i][j]; P^T and A^T ([j][i]).  The U pass keeps P over
+  // G^T's tile (P is read before G^T is written, and a barrier separates
+  // them), so that its LDS leaves room for two workgroups per CU.
+  constexpr bool P_OVER_GT = !GRAD && C <= DP;  // P fits G^T's tile
+  __shared__ __attribute__((aligned(16))) T sPg[P_OVER_GT ? 1 : C * LC];
+  __shared__ __attribute__((aligned(16))) T sPT[GRAD ? C * LC : 1];
+  __shared__ __attribute__((aligned(16))) T sAT[GRAD ? C * LC : 1];
   __shared__ __attribute__((aligned(16))) T szh[DP + 16];
   __shared__ __attribute__((aligned(16))) T szl[DP + 16];
   __shared__ __attribute__((aligned(16))) T szero[DP + 16];
   __shared__ __attribute__((aligned(16))) T sones[16];
   __shared__ float sz[DP], su[DP], sinv[C], sbeta[C], spart[NBB][C];
+  T* const sP = P_OVER_GT ? sGT : sPg;
   using SB = StateBlocks<DP>;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
@@ -181,12 +185,31 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   const bool has_out = nb0 < NBB;
   const int i = ib * 32 + (lane & 31);  // this lane's query row (num, dQ) or key row (dK, dV)
 
+  // Rows are requested one step ahead: the next chunk's K and V while this
+  // chunk's are in use, the next query head's (or the next chunk's first)
+  // Q and dO rows while this head's are.
+  StageRegs<TI, DP, C> rK, rV, rQ, rO;
+  auto load_q = [&](int64_t c, int r) {
+    const int64_t hq = u * R + r;
+    const int nvl = chunk_rows(c, C, n);
+    stage_load<TI, DP, C>(rQ, reinterpret_cast<const TI*>(A.q) + hq * n * d, d, c * C, nvl, vec, tid);
+    stage_load<TI, DP, C>(rO, reinterpret_cast<const TI*>(A.dout) + hq * n * d, d, c * C, nvl, vec, tid);
+  };
+  stage_load<TI, DP, C>(rK, kb, d, c0 * C, chunk_rows(c0, C, n), vec, tid);
+  stage_load<TI, DP, C>(rV, vb, d, c0 * C, chunk_rows(c0, C, n), vec, tid);
+  load_q(c0, 0);
+
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = chunk_rows(c, C, n);
     __syncthreads();  // the previous chunk is done with every tile
-    stage<TI, T, DP, C, PX, PX>(kb, d, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
-    stage<TI, T, DP, C, XF_ID, XF_ID>(vb, d, t0, nv, d, vec, sV, LQ, sVT, LC, tid);
+    stage_put<TI, T, DP, C, PX, PX>(rK, kb, d, t0, nv, d, vec, sK, LQ, sKT, LC, tid);
+    stage_put<TI, T, DP, C, GRAD ? XF_ID : XF_NONE, XF_ID>(rV, vb, d, t0, nv, d, vec, GRAD ? sV : nullptr, LQ,
+                                                        sVT, LC, tid);
+    if (c + 1 < c1) {
+      stage_load<TI, DP, C>(rK, kb, d, (c + 1) * C, chunk_rows(c + 1, C, n), vec, tid);
+      stage_load<TI, DP, C>(rV, vb, d, (c + 1) * C, chunk_rows(c + 1, C, n), vec, tid);
+    }
 #pragma unroll
     for (int s = 0; s < SB::PER_WAVE; ++s) {
       const int e = w + NW * s;
@@ -215,8 +238,12 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       const TI* qh = reinterpret_cast<const TI*>(A.q) + hq * n * d;
       const TI* oh = reinterpret_cast<const TI*>(A.dout) + hq * n * d;
       __syncthreads();  // the previous head is done with sQ, sG, sP and the rest
-      stage<TI, T, DP, C, PX, PX>(qh, d, t0, nv, d, vec, sQ, LQ, sQT, LC, tid);
-      stage<TI, T, DP, C, XF_ID, XF_NONE>(oh, d, t0, nv, d, vec, sG, LQ, nullptr, 0, tid);
+      stage_put<TI, T, DP, C, PX, PX>(rQ, qh, d, t0, nv, d, vec, sQ, LQ, sQT, LC, tid);
+      stage_put<TI, T, DP, C, XF_ID, XF_NONE>(rO, oh, d, t0, nv, d, vec, sG, LQ, nullptr, 0, tid);
+      if (r + 1 < R)
+        load_q(c, r + 1);
+      else if (c + 1 < c1)
+        load_q(c + 1, 0);
       __syncthreads();
 
       // ---- P^T blocks (key block jb, query block ib2), masked j <= i: sP[i][j]
