@@ -156,13 +156,18 @@ def algorithmic_flops(w):
 # counters' readings for a plain 64 MiB device copy) and recorded under
 # profiles/ together with a hash of the kernel's sources; reported only while
 # the sources still hash the same (null once the kernel has changed).
+_FUSED_SRC = ["la_fused.hip", "la_bf16.h", "la_ctl.h", "la_device.h", "la_internal.h"]
 COUNTERS = {
-    "causal": ("k_causal_fused_causal_bf16_B8H8n2048d64_counters.md",
-               ["la_fused.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
+    "causal": ("k_causal_fused_causal_bf16_B8H8n2048d64_counters.md", _FUSED_SRC),
+    "causal_bnhd": ("k_causal_fused_causal_bnhd_bf16_B8n2048H8d64_counters.md", _FUSED_SRC),
+    "varlen": ("k_causal_fused_varlen_bf16_16seqs_128to2048_H8d64_counters.md", _FUSED_SRC),
+    "gqa_d64": ("k_causal_fused_gqa_d64_bf16_B4Hq16Hkv4n2048d64_counters.md", _FUSED_SRC),
+    "window": ("k_window_fused_window_bf16_B8H8n2048d64_w512_counters.md",
+               ["la_window_fused.hip", "la_bf16.h", "la_ctl.h", "la_device.h", "la_internal.h"]),
     "forward_bf16": ("k_fwd_one_forward_bf16_B2H8n4096d64_counters.md",
-                     ["la_forward_bf16.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
+                     ["la_forward_bf16.hip", "la_bf16.h", "la_ctl.h", "la_device.h", "la_internal.h"]),
     "decode": ("k_decode128_decode_B128Hq32Hkv8d128_counters.md",
-               ["la_kernels.hip", "la_bf16.h", "la_device.h", "la_internal.h"]),
+               ["la_kernels.hip", "la_bf16.h", "la_ctl.h", "la_device.h", "la_internal.h"]),
 }
 SINGLE_LAUNCH = {"causal": "k_causal_fused", "forward_bf16": "k_fwd_one", "decode": "k_decode128",
                  "causal_elu": "k_causal_fused", "forward_elu": "k_fwd_one", "causal_features": "k_causal_fused",
