@@ -192,7 +192,7 @@ __global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, con
     for (int u = 0; u < PIECES; ++u) {
       const int pc = tid + NT * u, row = pc >> 4, col = 8 * (pc & 15);
       const uint4 x = kr[u];
-      auto fk = [&](uint32_t y) { return SPLIT ? la_bf16::relu2(y) : (row < nv ? la_bf16::elu2(y) : 0u); };
+      auto fk = [&](uint32_t y) { return SPLIT ? la_bf16::relu2(y) : (row < nv ? la_bf16::map2<PM>(y) : 0u); };
       *reinterpret_cast<uint4*>(sK[buf] + row * RS + col) = make_uint4(fk(x.x), fk(x.y), fk(x.z), fk(x.w));
       *reinterpret_cast<uint4*>(sV[buf] + row * RS + col) = vr[u];
     }
@@ -964,7 +964,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
         if (half == 0) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            x[j] = SPLIT ? la_bf16::relu2(x[j]) : (pr0 + rr < nv ? la_bf16::elu2(x[j]) : 0u);
+            x[j] = SPLIT ? la_bf16::relu2(x[j]) : (pr0 + rr < nv ? la_bf16::map2<PM>(x[j]) : 0u);
         }
         *reinterpret_cast<la_bf16::u32x4*>(tm + (pr0 + rr) * RS + pc0) = x;
       }
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
           uint32_t y[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            y[j] = pr0 + rr < nv ? (SPLIT ? la_bf16::phi2(kv2[rr][j]) : la_bf16::elu2(kv2[rr][j])) : 0u;
+            y[j] = pr0 + rr < nv ? (SPLIT ? la_bf16::phi2(kv2[rr][j]) : la_bf16::map2<PM>(kv2[rr][j])) : 0u;
           uint2* dst = reinterpret_cast<uint2*>(sK + (pr0 + rr) * LQ + pc0);
           dst[0] = make_uint2(y[0], y[1]);
           dst[1] = make_uint2(y[2], y[3]);
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
     }
 #pragma unroll
     for (int u = 0; u < QPH; ++u)
-      tile_store<bf16, DP, C, SPLIT ? XF_PHI : XF_ELU1, XF_NONE>(raw[u], nv, sQ[2 * u + half], nullptr, ht);
+      tile_store<bf16, DP, C, q_xform<PM>(), XF_NONE>(raw[u], nv, sQ[2 * u + half], nullptr, ht);
     if (c + 1 < c1) fetch(c + 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -1358,8 +1358,8 @@ __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, co
           const float x = fmaxf(kr[s][j], 0.0f);
           zr[j] += x;
           pk[j] = x + 1.0f;  // keys past the segment: 1, against V = 0
-        } else if (PM == PM_ELU1) {
-          pk[j] = real ? elu1_f(kr[s][j]) : 0.0f;
+        } else if (PM == PM_ELU1 || PM == PM_FEAT) {  // phi(K) as it is, 0 past the segment
+          pk[j] = real ? (PM == PM_ELU1 ? elu1_f(kr[s][j]) : kr[s][j]) : 0.0f;
           zr[j] += pk[j];
         } else {
           pk[j] = kr[s][j];
@@ -1625,8 +1625,16 @@ __global__ __launch_bounds__(256) void k_decode128(const T* __restrict__ q, cons
 }
 
 // ------------------------------------------------------------------ dispatch
-template <typename T, int DP, int C>
-int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, int form) {
+// The causal form on the general kernels, for feature map PM: the state pass
+// (k_state_tr for bf16 d = 128 chunk 32, k_state32 for fp32 d = 64, else
+// k_state), the scan, then the output pass (k_out_gqa for two or four query
+// heads per key/value head at bf16 d = 128 chunk 32; k_out_prefix32 with
+// the chunks as buckets for fp32 d = 64 chunk 64 and one query head per
+// key/value head; else k_out).  The specialised kernels walk F state
+// segments per workgroup, so that about kGqaOutGroups / kPrefixOutGroups
+// workgroups (one / two per CU) each walk a longer run of chunks.
+template <typename T, int DP, int C, int PM>
+int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
   hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
   const bool vec = (a.d == DP);
   const int64_t nbh = a.B * a.Hkv;
@@ -1636,149 +1644,109 @@ int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, 
   const T* k = reinterpret_cast<const T*>(a.k);
   const T* v = reinterpret_cast<const T*>(a.v);
   T* out = reinterpret_cast<T*>(a.out);
-  int* boff = nullptr; int* perm = nullptr;
-  bool state_done = false;
-  if (form == CAUSAL && a.phi == 2) {
-    // caller-applied features: the general state, scan and output kernels
-    k_state<T, DP, C, PM_FEAT><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
-                                                                             p.G, p.nseg, states);
-    const int64_t E = slot_elems(DP);
-    k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d,
-                                                                            a.S_final, a.z_final, 1);
-    if (!(q && out)) return (int)hipGetLastError();
-    k_out<T, DP, C, CAUSAL, PM_FEAT><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
-        q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
-    return (int)hipGetLastError();
+  bool tr = false, s32 = false, px = false;
+  if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
+  if constexpr (std::is_same<T, float>::value && DP == 64) s32 = vec && a.n <= la_internal::kFwd32MaxN;
+  if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) px = vec && q && out && R == 1;
+  const bool gq = tr && q && out && (R == 2 || R == 4);
+  if (tr) {
+    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
+      k_state_tr<PM><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
+  } else if (s32) {
+    if constexpr (std::is_same<T, float>::value && DP == 64)
+      k_state32<PM><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg, states,
+                                                                    nullptr, nullptr, nullptr, 1, nullptr);
+  } else {
+    k_state<T, DP, C, PM><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
+                                                                         p.nseg, states);
   }
-  if (form == CAUSAL && a.phi == 1) {
-    // ELU + 1: the bf16 d = 128 chunk-32 (GQA) state and output kernels, the
-    // fp32 d = 64 state kernel, else the general ones
-    bool tr = false, s32 = false;
-    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
-    if constexpr (std::is_same<T, float>::value && DP == 64) s32 = vec && a.n <= la_internal::kFwd32MaxN;
-    const bool gq = tr && q && out && (R == 2 || R == 4);
-    bool px = false;  // the fp32 d = 64 chunk-64 output kernel
-    if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) px = vec && q && out && R == 1;
-    if (tr) {
-      if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
-        k_state_tr<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
-    } else if (s32) {
-      if constexpr (std::is_same<T, float>::value && DP == 64)
-        k_state32<PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
-                                                                           states, nullptr, nullptr, nullptr, 1, nullptr);
-    } else {
-      k_state<T, DP, C, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
-                                                                               p.G, p.nseg, states);
-    }
-    int64_t F = gq ? nbh * p.nseg / kGqaOutGroups : px ? nbh * p.nseg / kPrefixOutGroups : 1;
-    if (F < 1) F = 1;
-    const int64_t E = slot_elems(DP);
-    k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d,
-                                                                            a.S_final, a.z_final, F);
-    if (!(q && out)) return (int)hipGetLastError();
-    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
-      if (gq) {
-        const bf16* qq = reinterpret_cast<const bf16*>(q);
-        const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
-        if (R == 2)
-          k_out_gqa<2, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO,
-                                                                                 nseg_o, F, p.nseg, states);
-        else
-          k_out_gqa<4, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO,
-                                                                                 nseg_o, F, p.nseg, states);
-        return (int)hipGetLastError();
-      }
-    }
-    if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
-      if (px) {
-        const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
-        k_out_prefix32<PX_NWV, true, PM_ELU1><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
-            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
-        return (int)hipGetLastError();
-      }
-    }
-    k_out<T, DP, C, CAUSAL, PM_ELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
-        q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
-    return (int)hipGetLastError();
-  }
-  if (form == PREFIX) {
-    char* bw = reinterpret_cast<char*>(a.ws) + la_internal::state_bytes(p, a.B, a.Hkv);
-    boff = reinterpret_cast<int*>(bw);                // [nmask][nchunks + 1]
-    perm = boff + a.nmask * (p.nchunks + 1);          // [nmask][n]
-    if constexpr (std::is_same<T, float>::value && DP == 64) {
-      if (vec && a.n <= la_internal::kFwd32MaxN) {  // the sort as one more workgroup of the state launch
-        k_state32<PM_ID><<<dim3((unsigned)(nbh * p.nseg + a.nmask)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G,
-                                                                                    p.nseg, states, a.m, boff, perm,
-                                                                                    a.nmask, a.ctl);
-        state_done = true;
-      }
-    }
-    if (!state_done) k_bucket<<<dim3((unsigned)a.nmask), 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm, a.ctl);
-  }
-  const bool phi = (form == CAUSAL);
-  if constexpr (std::is_same<T, float>::value && DP == 64) {
-    if (phi && vec && a.n <= la_internal::kFwd32MaxN) {
-      k_state32<PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G, p.nseg,
-                                                                       states, nullptr, nullptr, nullptr, 1, nullptr);
-      state_done = true;
-    }
-  }
-  if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
-    if (phi && vec) {
-      k_state_tr<PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
-      state_done = true;
-    }
-  }
-  if (state_done) {
-  } else if (phi)
-    k_state<T, DP, C, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
-  else
-    k_state<T, DP, C, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G, p.nseg, states);
-  const int64_t E = slot_elems(DP);
-  // the GQA and fp32 prefix output kernels: F state segments per
-  // workgroup, so that about kGqaOutGroups / kPrefixOutGroups workgroups
-  // (one / two per CU) each walk a longer run of chunks
-  bool gqa_out = false, px_out = false;
-  if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
-    gqa_out = q && out && form == CAUSAL && vec && (R == 2 || R == 4);
-  if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64)
-    px_out = q && out && vec && (form == PREFIX || (form == CAUSAL && R == 1));
-  int64_t F = gqa_out ? nbh * p.nseg / kGqaOutGroups : px_out ? nbh * p.nseg / kPrefixOutGroups : 1;
+  int64_t F = gq ? nbh * p.nseg / kGqaOutGroups : px ? nbh * p.nseg / kPrefixOutGroups : 1;
   if (F < 1) F = 1;
-  const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
+  const int64_t E = slot_elems(DP);
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final,
                                                                           a.z_final, F);
-  if (q && out) {
-    if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
-      if (gqa_out) {
-        const bf16* qq = reinterpret_cast<const bf16*>(q);
-        if (R == 2)
-          k_out_gqa<2, PM_RELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
-                                                                        p.nseg, states);
-        else
-          k_out_gqa<4, PM_RELU1><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o, F,
-                                                                        p.nseg, states);
-        return (int)hipGetLastError();
-      }
+  if (!(q && out)) return (int)hipGetLastError();
+  const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
+  if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
+    if (gq) {
+      const bf16* qq = reinterpret_cast<const bf16*>(q);
+      if (R == 2)
+        k_out_gqa<2, PM><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
+                                                                         F, p.nseg, states);
+      else
+        k_out_gqa<4, PM><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
+                                                                         F, p.nseg, states);
+      return (int)hipGetLastError();
     }
-    if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
-      if (px_out && form == PREFIX) {
-        k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
-            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
-        return (int)hipGetLastError();
-      }
-      if (px_out) {
-        k_out_prefix32<PX_NWV, true, PM_RELU1><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
-            q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
-        return (int)hipGetLastError();
-      }
-    }
-    if (form == CAUSAL)
-      k_out<T, DP, C, CAUSAL, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
-    else
-      k_out<T, DP, C, PREFIX, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
   }
+  if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
+    if (px) {
+      k_out_prefix32<PX_NWV, true, PM><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
+          q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
+      return (int)hipGetLastError();
+    }
+  }
+  k_out<T, DP, C, CAUSAL, PM><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
+      q, k, v, out, a.n, (int)a.d, R, vec, p.nchunks, p.G, p.nseg, states, nullptr, nullptr, nullptr, a.Hq, 1);
   return (int)hipGetLastError();
+}
+
+// The prefix-mask form (no feature map): the bucket sort (for fp32 d = 64 as
+// extra workgroups of the k_state32 launch), the state pass, the scan, then
+// k_out_prefix32 (fp32 d = 64 chunk 64) or k_out.
+template <typename T, int DP, int C>
+int run_prefix(const la_internal::Fwd& a, const la_internal::Plan& p) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(a.stream);
+  const bool vec = (a.d == DP);
+  const int64_t nbh = a.B * a.Hkv;
+  float* states = reinterpret_cast<float*>(a.ws);
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  T* out = reinterpret_cast<T*>(a.out);
+  char* bw = reinterpret_cast<char*>(a.ws) + la_internal::state_bytes(p, a.B, a.Hkv);
+  int* boff = reinterpret_cast<int*>(bw);   // [nmask][nchunks + 1]
+  int* perm = boff + a.nmask * (p.nchunks + 1);  // [nmask][n]
+  bool state_done = false;
+  if constexpr (std::is_same<T, float>::value && DP == 64) {
+    if (vec && a.n <= la_internal::kFwd32MaxN) {  // the sort as one more workgroup of the state launch
+      k_state32<PM_ID><<<dim3((unsigned)(nbh * p.nseg + a.nmask)), 512, 0, st>>>(k, v, a.n, p.nchunks, C, p.G,
+                                                                                  p.nseg, states, a.m, boff, perm,
+                                                                                  a.nmask, a.ctl);
+      state_done = true;
+    }
+  }
+  if (!state_done) {
+    k_bucket<<<dim3((unsigned)a.nmask), 1024, 0, st>>>(a.m, a.n, C, p.nchunks, boff, perm, a.ctl);
+    k_state<T, DP, C, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks,
+                                                                            p.G, p.nseg, states);
+  }
+  bool px = false;
+  if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) px = vec;
+  int64_t F = px ? nbh * p.nseg / kPrefixOutGroups : 1;
+  if (F < 1) F = 1;
+  const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
+  const int64_t E = slot_elems(DP);
+  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr,
+                                                                          nullptr, F);
+  if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
+    if (px) {
+      k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
+          q, k, v, out, a.n, p.nchunks, GO, nseg_o, F, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
+      return (int)hipGetLastError();
+    }
+  }
+  k_out<T, DP, C, PREFIX, PM_ID><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(
+      q, k, v, out, a.n, (int)a.d, 1, vec, p.nchunks, p.G, p.nseg, states, perm, boff, a.m, a.Hq, a.nmask);
+  return (int)hipGetLastError();
+}
+
+template <typename T, int DP, int C>
+int run_causal_or_prefix(const la_internal::Fwd& a, const la_internal::Plan& p, int form) {
+  if (form == PREFIX) return run_prefix<T, DP, C>(a, p);
+  if (a.phi == 2) return run_causal<T, DP, C, PM_FEAT>(a, p);
+  if (a.phi == 1) return run_causal<T, DP, C, PM_ELU1>(a, p);
+  return run_causal<T, DP, C, PM_RELU1>(a, p);
 }
 
 template <typename T, int DP, int C>
