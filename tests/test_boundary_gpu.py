@@ -96,6 +96,84 @@ def test_graph_capture_replays_with_new_inputs(gpu, form):
         assert gpu.la_workspace_status(ws_eager) == 0
 
 
+@pytest.mark.parametrize("form", ["packed_sequences", "gqa_B4_Hq16_Hkv4_n1500"])
+def test_graph_capture_single_launch_variants(gpu, form):
+    """Graph replays of the single-launch causal kernel's other variants:
+    packed sequences (lengths 0 .. 1800, so that many workgroups of the grid
+    find their sequence ended and only count themselves in to the control
+    block) and grouped query heads (the XCD-grouped dispatch order).  Four
+    replays with new inputs copied into the static buffers, each against the
+    oracle and the eager call on the same inputs, bit for bit."""
+    import torch
+    packed = form == "packed_sequences"
+    if packed:
+        lengths = [700, 0, 1800, 65, 1, 512, 1025]
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        total, H, d = int(cu[-1]), 2, 64
+        cud = torch.from_numpy(cu).cuda()
+        ws = new_ws(gpu, gpu.LA_OP_SEQS, len(lengths), H, H, max(lengths), d, gpu.LA_BF16)
+        ws_eager = new_ws(gpu, gpu.LA_OP_SEQS, len(lengths), H, H, max(lengths), d, gpu.LA_BF16)
+        shapes = [(total, H, d)] * 3
+
+        def call(q, k, v, o, w):
+            return gpu.la_causal_forward_strided(q, k, v, cu_seqlens=cud, max_len=max(lengths), out=o, ws=w)
+
+        def inputs(seed):
+            q, k, v, _ = li.qkv(1, H, H, total, d, li.BF16, seed=seed, scaled=True)
+            return [np.ascontiguousarray(x[0].transpose(1, 0, 2)) for x in (q, k, v)], (q, k, v)
+
+        def reference(qkv):
+            q, k, v = qkv
+            outs = np.zeros((total, H, d))
+            for s_, L in enumerate(lengths):
+                if L:
+                    a, b = int(cu[s_]), int(cu[s_ + 1])
+                    sl = lambda x: np.ascontiguousarray(x[:, :, a:b])
+                    outs[a:b] = oracle.causal(sl(q), sl(k), sl(v))[0].transpose(1, 0, 2)
+            return outs
+    else:
+        B, Hq, Hkv, n, d = 4, 16, 4, 1500, 64
+        ws = new_ws(gpu, gpu.LA_OP_CAUSAL, B, Hq, Hkv, n, d, gpu.LA_BF16, 64)
+        ws_eager = new_ws(gpu, gpu.LA_OP_CAUSAL, B, Hq, Hkv, n, d, gpu.LA_BF16, 64)
+        shapes = [(B, Hq, n, d), (B, Hkv, n, d), (B, Hkv, n, d)]
+
+        def call(q, k, v, o, w):
+            return gpu.la_causal_forward(q, k, v, chunk=64, out=o, ws=w)
+
+        def inputs(seed):
+            q, k, v, _ = li.qkv(B, Hq, Hkv, n, d, li.BF16, seed=seed, scaled=True)
+            return [q, k, v], (q, k, v)
+
+        def reference(qkv):
+            return oracle.causal(*qkv)
+    qs, ks, vs = (torch.empty(sh, dtype=torch.bfloat16, device="cuda") for sh in shapes)
+    out = torch.empty_like(qs)
+    (q0, k0, v0), _ = inputs(50)
+    qs.copy_(dev(q0)); ks.copy_(dev(k0)); vs.copy_(dev(v0))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        call(qs, ks, vs, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(qs, ks, vs, out, ws)
+    for rep in range(4):
+        (q, k, v), raw = inputs(51 + rep)
+        qs.copy_(dev(q)); ks.copy_(dev(k)); vs.copy_(dev(v))
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = li.from_torch(out)
+        check(li.to_f32(got).astype(np.float64), reference(raw), li.BF16, f"{form} replay {rep}")
+        eager = li.from_torch(call(qs, ks, vs, torch.zeros_like(qs), ws_eager))
+        assert np.array_equal(got, eager), f"replay {rep} differs from the eager call"
+        call(qs, ks, vs, torch.empty_like(qs), ws)
+        assert gpu.la_workspace_status(ws) == 0
+        assert gpu.la_workspace_status(ws_eager) == 0
+
+
 # ------------------------------------------------------------------ streams
 def test_calls_on_other_streams(gpu):
     """Calls issued on two non-default streams at once, each with the
