@@ -542,9 +542,14 @@ namespace la_internal {
 bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk) {
   // n bound: every segment sums the aggregates of all earlier segments of its
   // head, so the look-back grows with n; longer sequences take the
-  // three-launch path, whose scan is linear in the number of segments.  R
-  // bound: each query head reads its key/value head's rows again
-  return dtype == 1 && d == FD && Hq % Hkv == 0 && Hq / Hkv <= kFusedMaxR && chunk == FC && n <= kFusedMaxN;
+  // three-launch path, whose scan is linear in the number of segments.  With
+  // grouped query heads each query head runs its own look-back, so the bound
+  // is lower (B1 Hq32 Hkv8 d64, interleaved timing: 58.0 against 81.2 us at
+  // n = 16384, 147 against 141 us at B2 Hq16 Hkv4 n = 32768, 375 against
+  // 260 us at B1 Hq32 Hkv8 n = 65536, single launch against three).  R
+  // bound: each query head reads its key/value head's rows again.
+  const int64_t nmax = Hq == Hkv ? kFusedMaxN : kFusedMaxNGqa;
+  return dtype == 1 && d == FD && Hq % Hkv == 0 && Hq / Hkv <= kFusedMaxR && chunk == FC && n <= nmax;
 }
 
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg) {

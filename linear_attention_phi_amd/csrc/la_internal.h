@@ -93,6 +93,7 @@ int launch_prefix(const Fwd& a, const Plan& p);
 constexpr int kFusedG = 8;
 constexpr int64_t kFusedMaxN = 131072;  // up to 256 segments per head
 constexpr int64_t kFusedMaxR = 8;       // query heads per key/value head
+constexpr int64_t kFusedMaxNGqa = 16384;  // n bound with grouped query heads (each runs its own look-back)
 bool fused_causal_applies(int64_t Hq, int64_t Hkv, int64_t n, int64_t d, int dtype, int chunk);
 size_t fused_causal_ws_bytes(int64_t NH, int64_t nseg);
 int launch_causal_fused(const Fwd& a, const Plan& p);
