@@ -183,6 +183,13 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   constexpr int NB_STEP = NW / NIB;
   constexpr int NPW = (NBB + NB_STEP - 1) / NB_STEP;  // output blocks per wave
   const bool has_out = nb0 < NBB;
+  // With one 32-row block per chunk and two 32-feature blocks (d = 64,
+  // C = 32) the output blocks occupy two of the four waves; the gradient
+  // pass then gives dphi(K) and dV to the other two (wave 2 + nb owns
+  // feature block nb), so that all four work after A is formed.
+  constexpr bool SPLIT_KV = GRAD && NIB == 1 && NBB == 2 && NW == 4;
+  const bool kv_out = SPLIT_KV ? w >= 2 : has_out;  // this wave holds dphi(K) and dV blocks
+  const int kv_nb0 = SPLIT_KV ? w - 2 : nb0;
   const int i = ib * 32 + (lane & 31);  // this lane's query row (num, dQ) or key row (dK, dV)
 
   // Rows are requested one step ahead: the next chunk's K and V while this
@@ -377,6 +384,14 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
 #pragma unroll
             for (int jb = 0; jb <= ib; ++jb)
               gemm_acc<T, 2>(accQ[uu], sKT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
+          }
+        }
+      }
+      if (kv_out) {
+#pragma unroll
+        for (int uu = 0; uu < NPW; ++uu) {
+          const int nb = kv_nb0 + uu * NB_STEP;
+          if (nb < NBB) {
 #pragma unroll
             for (int ib2 = ib; ib2 < NIB; ++ib2) {
               gemm_acc<T, 2>(accK[uu], sQT + nb * 32 * LC + ib2 * 32, LC, sAT + ib * 32 * LC + ib2 * 32, LC, lane);
@@ -433,10 +448,10 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       }
       if (tid < DP) su[tid] = urun[0];
       __syncthreads();
-      if (has_out) {
+      if (kv_out) {
 #pragma unroll
         for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = nb0 + uu * NB_STEP;
+          const int nb = kv_nb0 + uu * NB_STEP;
           if (nb < NBB) {
             gemm_acc<T, DP / 16>(accK[uu], sU + nb * 32 * LQ, LQ, sV + ib * 32 * LQ, LQ, lane);
             gemm_acc<T, DP / 16>(accV[uu], sUT + nb * 32 * LQ, LQ, sK + ib * 32 * LQ, LQ, lane);
@@ -444,10 +459,10 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
         }
       }
       __syncthreads();  // sQ and sG are free: dK and dV rows go out through them
-      if (has_out) {
+      if (kv_out) {
 #pragma unroll
         for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = nb0 + uu * NB_STEP;
+          const int nb = kv_nb0 + uu * NB_STEP;
           if (nb < NBB) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
