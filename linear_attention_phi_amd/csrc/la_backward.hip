@@ -25,7 +25,8 @@
 // again with S_pre carried forward from its prefix and U_after carried from
 // its suffix (each chunk's phi(Q)^T G leaves it), writing dQ, dK and dV.
 // Nothing is written per chunk to memory but the gradients.  Every product
-// is on fp32 MFMA (v_mfma_f32_32x32x2_f32, la_device.h conventions; the
+// is on fp32 MFMA (v_mfma_f32_32x32x2_f32 with la_device.h conventions, the
+// masked scores P and A on v_mfma_f32_16x16x4f32 over all four waves; the
 // feature map without the relu + 1 split), bf16 rows widened exactly as
 // they are staged: with relu + 1 every weight phi(Q_i) . phi(K_j) is close
 // to d, so out_i is close to the mean of V and dphi(Q) = S g + beta z is a
@@ -68,7 +69,7 @@ template <int PM> __device__ __forceinline__ float dphi(float x) {
 // LDS bytes of k_bwd<T, DP, C, .., MODE_GRAD> (the larger mode).
 constexpr size_t bwd_lds(int eb, int DP, int C) {
   const size_t LQ = DP + PAD, LC = C + PAD;
-  return (size_t)eb * (4 * C * LQ + 4 * DP * LC + 4 * DP * LQ + 3 * C * LC + 3 * (DP + 16) + 16) +
+  return (size_t)eb * (4 * C * LQ + 4 * DP * LC + 4 * DP * LQ + 3 * C * LC) +
          4 * (size_t)(2 * DP + 2 * C + (DP / 32) * C);
 }
 
@@ -103,6 +104,52 @@ __device__ __forceinline__ void rows_out(const TT* tile, int LQ, int nv, int d, 
   }
 }
 
+// Masked C x C scores on v_mfma_f32_16x16x4f32 (contraction index k = lane
+// / 16, the other index lane % 16; accumulator entry rr of lane l is row
+// 4 (l / 16) + rr, column l % 16), one 16 x 16 sub-block (key block kj,
+// query block qi) per wave in turn, so that all four waves share the work:
+//   acc[j][i] = sum_a X[j][a] Y[i][a] + add_i  for j <= i, else 0,
+// stored to Z[i][j] (a 16-byte store per lane) and, with ZT, to ZT[j][i].
+// X and Y are token-major (row stride LQ, DP features), Z and ZT have row
+// stride LC.  A lane reads the four features 16 f + 4 (l / 16) .. + 3 of its
+// rows with one 16-byte read and feeds them to four k-steps (feature
+// 16 f + 4 (l / 16) + jj is the k index l / 16 of step (f, jj) in both
+// operands).  Sub-blocks above the diagonal are only written where the
+// 32-wide products read them (inside a diagonal 32 x 32 block), as zeros.
+template <int DP, int C>
+__device__ __forceinline__ void scores16(const float* X, const float* Y, int LQ, const float* add, float* Z,
+                                         float* ZT, int LC, int w, int lane) {
+  constexpr int NB16 = C / 16;
+  const int m = lane & 15, kq = lane >> 4;
+  int e = 0;
+#pragma unroll
+  for (int qi = 0; qi < NB16; ++qi)
+#pragma unroll
+    for (int kj = 0; kj < NB16; ++kj) {
+      if (kj > qi && (kj >> 1) != (qi >> 1)) continue;  // never read
+      if ((e++ % NW) != w) continue;
+      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (kj <= qi) {
+#pragma unroll
+        for (int f = 0; f < DP / 16; ++f) {
+          const f32x4 xa = *reinterpret_cast<const f32x4*>(X + (16 * kj + m) * LQ + 16 * f + 4 * kq);
+          const f32x4 yb = *reinterpret_cast<const f32x4*>(Y + (16 * qi + m) * LQ + 16 * f + 4 * kq);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[jj], yb[jj], acc, 0, 0, 0);
+        }
+        const int iq = 16 * qi + m;
+        const float ad = add ? add[iq] : 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[rr] = 16 * kj + 4 * kq + rr > iq ? 0.0f : acc[rr] + ad;
+      }
+      *reinterpret_cast<f32x4*>(Z + (16 * qi + m) * LC + 16 * kj + 4 * kq) = acc;
+      if (ZT) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ZT[(16 * kj + 4 * kq + rr) * LC + 16 * qi + m] = acc[rr];
+      }
+    }
+}
+
 template <typename TI, int DP, int C, int PM, int MODE>
 __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   using T = float;  // every tile and product in fp32, whatever the input type (see above)
@@ -132,11 +179,8 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   __shared__ __attribute__((aligned(16))) T sPg[P_OVER_GT ? 1 : C * LC];
   __shared__ __attribute__((aligned(16))) T sPT[GRAD ? C * LC : 1];
   __shared__ __attribute__((aligned(16))) T sAT[GRAD ? C * LC : 1];
-  __shared__ __attribute__((aligned(16))) T szh[DP + 16];
-  __shared__ __attribute__((aligned(16))) T szl[DP + 16];
-  __shared__ __attribute__((aligned(16))) T szero[DP + 16];
-  __shared__ __attribute__((aligned(16))) T sones[16];
-  __shared__ float sz[DP], su[DP], sinv[C], sbeta[C], spart[NBB][C];
+  __shared__ __attribute__((aligned(16))) float sz[DP];
+  __shared__ float su[DP], sinv[C], sbeta[C], spart[NBB][C];
   T* const sP = P_OVER_GT ? sGT : sPg;
   using SB = StateBlocks<DP>;
 
@@ -171,12 +215,6 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       zrun = fs[DP * DP + tid];
       if (GRAD) urun[0] = us[DP * DP + tid];
     }
-  }
-  if (tid < 16) {
-    sones[tid] = cvt<T>(1.0f);
-    szero[DP + tid] = cvt<T>(0.0f);
-    szh[DP + tid] = cvt<T>(0.0f);
-    szl[DP + tid] = cvt<T>(0.0f);
   }
 
   const int ib = w % NIB, nb0 = w / NIB;
@@ -226,13 +264,7 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
         if (GRAD) st_acc(sS + ma * 32 * LQ + nb * 32, LQ, accS[s], lane);
       }
     }
-    if (tid < DP) {
-      sz[tid] = zrun;
-      const T zh = cvt<T>(zrun);
-      szh[tid] = zh;
-      szl[tid] = cvt<T>(zrun - to_f(zh));
-      szero[tid] = cvt<T>(0.0f);
-    }
+    if (tid < DP) sz[tid] = zrun;
     f32x16 accK[NPW], accV[NPW];  // dphi(K)^T [a][j] and dV^T [b][j] blocks (key block ib)
 #pragma unroll
     for (int uu = 0; uu < NPW; ++uu) {
@@ -253,50 +285,29 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
         load_q(c + 1, 0);
       __syncthreads();
 
-      // ---- P^T blocks (key block jb, query block ib2), masked j <= i: sP[i][j]
-      // (and sPT[j][i])
-      {
-        int e = 0;
-#pragma unroll
-        for (int ib2 = 0; ib2 < NIB; ++ib2)
-#pragma unroll
-          for (int jb = 0; jb <= ib2; ++jb) {
-            if ((e++ % NW) != w) continue;
-            f32x16 acc = f32x16{};
-            gemm_acc<T, DP / 16>(acc, sK + jb * 32 * LQ, LQ, sQ + ib2 * 32 * LQ, LQ, lane);
-            const int qi = ib2 * 32 + (lane & 31);
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-              if (jb * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3) > qi) acc[rr] = 0.0f;
-            st_accT(sP + ib2 * 32 * LC + jb * 32, LC, acc, lane);
-            if (GRAD) st_acc(sPT + jb * 32 * LC + ib2 * 32, LC, acc, lane);
-          }
-      }
+      // ---- P = M * (phi(Q) phi(K)^T): sP[i][j] (and sPT[j][i])
+      scores16<DP, C>(sK, sQ, LQ, nullptr, sP, GRAD ? sPT : nullptr, LC, w, lane);
       __syncthreads();
 
       // ---- o^T = (S^T phi(Q)^T + V^T P^T) / den; partial dots dO . o for beta
       if (has_out) {
-        const int mrow = lane & 31;
-        Frag<T> e0;
-        ld_frag(e0, mrow == 0 ? sones : szero);
-        f32x16 dacc = f32x16{};
+        // den_i = phi(Q_i) . z_pre + sum_j P[i][j] (P is 0 past the diagonal):
+        // each half of the wave sums half of the features and keys
+        float dpart = 0.0f;
 #pragma unroll
-        for (int jb = 0; jb <= ib; ++jb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            Frag<T> fb;
-            ld_frag(fb, sP + i * LC + jb * 32 + 16 * kk + 4 * h);
-            mma(dacc, e0, fb);
-          }
-        const T* zrow = (mrow == 0) ? szh : (mrow == 16) ? szl : szero;
-#pragma unroll
-        for (int kk = 0; kk < DP / 16; ++kk) {
-          Frag<T> fa, fb;
-          ld_frag(fa, zrow + 16 * kk + 4 * h);
-          ld_frag(fb, sQ + i * LQ + 16 * kk + 4 * h);
-          mma(dacc, fa, fb);
+        for (int a = 0; a < DP / 2; a += 4) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(sQ + i * LQ + h * (DP / 2) + a);
+          const f32x4 zv = *reinterpret_cast<const f32x4*>(sz + h * (DP / 2) + a);
+          dpart += qv[0] * zv[0] + qv[1] * zv[1] + qv[2] * zv[2] + qv[3] * zv[3];
         }
-        const float den = __shfl(dacc[0] + dacc[8], lane & 31);
+        for (int jb = 0; jb <= ib; ++jb) {
+#pragma unroll
+          for (int t = 0; t < 16; t += 4) {
+            const f32x4 pv = *reinterpret_cast<const f32x4*>(sP + i * LC + jb * 32 + 16 * h + t);
+            dpart += pv[0] + pv[1] + pv[2] + pv[3];
+          }
+        }
+        const float den = dpart + __shfl_xor(dpart, 32);
         const float inv = i < nv ? 1.0f / den : 0.0f;  // rows past the end: no gradient
 #pragma unroll
         for (int uu = 0; uu < NPW; ++uu) {
@@ -349,26 +360,9 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
         continue;
       }
 
-      // ---- A = M * (G V^T + beta 1^T): blocks acc[j][i] -> sP[i][j] (P is no
-      // longer needed there) and sAT[j][i]
-      {
-        int e = 0;
-#pragma unroll
-        for (int ib2 = 0; ib2 < NIB; ++ib2)
-#pragma unroll
-          for (int jb = 0; jb <= ib2; ++jb) {
-            if ((e++ % NW) != w) continue;
-            f32x16 acc = f32x16{};
-            gemm_acc<T, DP / 16>(acc, sV + jb * 32 * LQ, LQ, sG + ib2 * 32 * LQ, LQ, lane);
-            const int qi = ib2 * 32 + (lane & 31);
-            const float bq = sbeta[qi];
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-              acc[rr] = jb * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3) > qi ? 0.0f : acc[rr] + bq;
-            st_accT(sP + ib2 * 32 * LC + jb * 32, LC, acc, lane);
-            st_acc(sAT + jb * 32 * LC + ib2 * 32, LC, acc, lane);
-          }
-      }
+      // ---- A = M * (G V^T + beta 1^T): sP[i][j] (P is no longer needed
+      // there) and sAT[j][i]
+      scores16<DP, C>(sV, sG, LQ, sbeta, sP, sAT, LC, w, lane);
       __syncthreads();
 
       // ---- dphi(Q)^T [a][i] = S G^T + phi(K)^T A^T + z beta^T (staged in sQ),
