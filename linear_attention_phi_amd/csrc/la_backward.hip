@@ -25,9 +25,11 @@
 // again with S_pre carried forward from its prefix and U_after carried from
 // its suffix (each chunk's phi(Q)^T G leaves it), writing dQ, dK and dV.
 // Nothing is written per chunk to memory but the gradients.  Every product
-// is on fp32 MFMA (v_mfma_f32_32x32x2_f32 with la_device.h conventions, the
-// masked scores P and A on v_mfma_f32_16x16x4f32 over all four waves; the
-// feature map without the relu + 1 split), bf16 rows widened exactly as
+// is on fp32 MFMA: the d x d states S and U in 32 x 32 blocks
+// (v_mfma_f32_32x32x2_f32, la_device.h conventions), everything shaped like
+// the chunk's rows (the masked scores P and A, the numerator, dQ, dK, dV) in
+// 16 x 16 sub-blocks (v_mfma_f32_16x16x4f32) dealt out evenly to the four
+// waves; the feature map without the relu + 1 split; bf16 rows widened exactly as
 // they are staged: with relu + 1 every weight phi(Q_i) . phi(K_j) is close
 // to d, so out_i is close to the mean of V and dphi(Q) = S g + beta z is a
 // small difference of two large terms -- operands rounded to bf16 would
@@ -70,7 +72,7 @@ template <int PM> __device__ __forceinline__ float dphi(float x) {
 constexpr size_t bwd_lds(int eb, int DP, int C) {
   const size_t LQ = DP + PAD, LC = C + PAD;
   return (size_t)eb * (4 * C * LQ + 4 * DP * LC + 4 * DP * LQ + 3 * C * LC) +
-         4 * (size_t)(2 * DP + 2 * C + (DP / 32) * C);
+         4 * (size_t)(2 * DP + 2 * C + (DP / 16) * C);
 }
 
 // Copy a C x DP tile staged in LDS (row stride LQ) to rows t0 .. t0 + nv - 1
@@ -104,17 +106,33 @@ __device__ __forceinline__ void rows_out(const TT* tile, int LQ, int nv, int d, 
   }
 }
 
-// Masked C x C scores on v_mfma_f32_16x16x4f32 (contraction index k = lane
-// / 16, the other index lane % 16; accumulator entry rr of lane l is row
-// 4 (l / 16) + rr, column l % 16), one 16 x 16 sub-block (key block kj,
-// query block qi) per wave in turn, so that all four waves share the work:
+// acc += sum_k X[r][k] Y[c][k] over the 16-wide k-blocks kb0 .. kb1 - 1 on
+// v_mfma_f32_16x16x4f32 (contraction index k = lane / 16, the other index
+// lane % 16), X and Y pointing at the first of 16 rows each (row strides ldx,
+// ldy): accumulator entry rr of lane l is X-row 4 (l / 16) + rr, Y-row
+// l % 16.  A lane reads the four entries 16 f + 4 (l / 16) .. + 3 of its rows
+// with one 16-byte read and feeds them to four k-steps (entry
+// 16 f + 4 (l / 16) + jj is the k index l / 16 of step (f, jj) in both
+// operands).
+__device__ __forceinline__ void mm16(f32x4& acc, const float* X, int ldx, const float* Y, int ldy, int kb0, int kb1,
+                                     int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  const float* px = X + m * ldx + 4 * kq;
+  const float* py = Y + m * ldy + 4 * kq;
+  for (int f = kb0; f < kb1; ++f) {
+    const f32x4 xa = *reinterpret_cast<const f32x4*>(px + 16 * f);
+    const f32x4 yb = *reinterpret_cast<const f32x4*>(py + 16 * f);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[jj], yb[jj], acc, 0, 0, 0);
+  }
+}
+
+// Masked C x C scores, one 16 x 16 sub-block (key block kj, query block qi)
+// per wave in turn, so that all four waves share the work:
 //   acc[j][i] = sum_a X[j][a] Y[i][a] + add_i  for j <= i, else 0,
 // stored to Z[i][j] (a 16-byte store per lane) and, with ZT, to ZT[j][i].
 // X and Y are token-major (row stride LQ, DP features), Z and ZT have row
-// stride LC.  A lane reads the four features 16 f + 4 (l / 16) .. + 3 of its
-// rows with one 16-byte read and feeds them to four k-steps (feature
-// 16 f + 4 (l / 16) + jj is the k index l / 16 of step (f, jj) in both
-// operands).  Sub-blocks above the diagonal are only written where the
+// stride LC.  Sub-blocks above the diagonal are only written where the
 // 32-wide products read them (inside a diagonal 32 x 32 block), as zeros.
 template <int DP, int C>
 __device__ __forceinline__ void scores16(const float* X, const float* Y, int LQ, const float* add, float* Z,
@@ -130,13 +148,7 @@ __device__ __forceinline__ void scores16(const float* X, const float* Y, int LQ,
       if ((e++ % NW) != w) continue;
       f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if (kj <= qi) {
-#pragma unroll
-        for (int f = 0; f < DP / 16; ++f) {
-          const f32x4 xa = *reinterpret_cast<const f32x4*>(X + (16 * kj + m) * LQ + 16 * f + 4 * kq);
-          const f32x4 yb = *reinterpret_cast<const f32x4*>(Y + (16 * qi + m) * LQ + 16 * f + 4 * kq);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[jj], yb[jj], acc, 0, 0, 0);
-        }
+        mm16(acc, X + 16 * kj * LQ, LQ, Y + 16 * qi * LQ, LQ, 0, DP / 16, lane);
         const int iq = 16 * qi + m;
         const float ad = add ? add[iq] : 0.0f;
 #pragma unroll
@@ -154,7 +166,6 @@ template <typename TI, int DP, int C, int PM, int MODE>
 __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   using T = float;  // every tile and product in fp32, whatever the input type (see above)
   constexpr int LQ = DP + PAD, LC = C + PAD;
-  constexpr int NIB = C / 32, NBB = DP / 32;
   constexpr int PX = q_xform<PM>();
   constexpr bool GRAD = MODE == MODE_GRAD;
   static_assert(PM != PM_ID, "normalised form");
@@ -180,11 +191,12 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
   __shared__ __attribute__((aligned(16))) T sPT[GRAD ? C * LC : 1];
   __shared__ __attribute__((aligned(16))) T sAT[GRAD ? C * LC : 1];
   __shared__ __attribute__((aligned(16))) float sz[DP];
-  __shared__ float su[DP], sinv[C], sbeta[C], spart[NBB][C];
+  __shared__ __attribute__((aligned(16))) float su[DP];
+  __shared__ float sinv[C], sbeta[C], spart[DP / 16][C];
   T* const sP = P_OVER_GT ? sGT : sPg;
   using SB = StateBlocks<DP>;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t u = blockIdx.x / A.nseg, seg = blockIdx.x % A.nseg;
   const int64_t n = A.n, nchunks = (n + C - 1) / C;
   const int64_t c0 = seg * A.G, c1 = (c0 + A.G < nchunks) ? c0 + A.G : nchunks;
@@ -217,18 +229,13 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
     }
   }
 
-  const int ib = w % NIB, nb0 = w / NIB;
-  constexpr int NB_STEP = NW / NIB;
-  constexpr int NPW = (NBB + NB_STEP - 1) / NB_STEP;  // output blocks per wave
-  const bool has_out = nb0 < NBB;
-  // With one 32-row block per chunk and two 32-feature blocks (d = 64,
-  // C = 32) the output blocks occupy two of the four waves; the gradient
-  // pass then gives dphi(K) and dV to the other two (wave 2 + nb owns
-  // feature block nb), so that all four work after A is formed.
-  constexpr bool SPLIT_KV = GRAD && NIB == 1 && NBB == 2 && NW == 4;
-  const bool kv_out = SPLIT_KV ? w >= 2 : has_out;  // this wave holds dphi(K) and dV blocks
-  const int kv_nb0 = SPLIT_KV ? w - 2 : nb0;
-  const int i = ib * 32 + (lane & 31);  // this lane's query row (num, dQ) or key row (dK, dV)
+  // The output-shaped products go in 16 x 16 sub-blocks (query or key block
+  // qb of 16 rows, feature block fb of 16), NSB per wave: sub-block
+  // e = w + NW s is (e / NFB, e % NFB), so that each wave keeps one feature
+  // block and the waves' shares of every product are equal.
+  constexpr int NQB = C / 16, NFB = DP / 16, NSB = NQB * NFB / NW;
+  static_assert(NQB * NFB % NW == 0, "whole sub-blocks per wave");
+  const int m16 = lane & 15, kq = lane >> 4;
 
   // Rows are requested one step ahead: the next chunk's K and V while this
   // chunk's are in use, the next query head's (or the next chunk's first)
@@ -265,11 +272,13 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       }
     }
     if (tid < DP) sz[tid] = zrun;
-    f32x16 accK[NPW], accV[NPW];  // dphi(K)^T [a][j] and dV^T [b][j] blocks (key block ib)
+    // dphi(K)^T[a][j] and dV^T[b][j] sub-blocks (key block e / NFB, feature
+    // block e % NFB), summed over the query heads
+    f32x4 accK[NSB], accV[NSB];
 #pragma unroll
-    for (int uu = 0; uu < NPW; ++uu) {
-      accK[uu] = f32x16{};
-      accV[uu] = f32x16{};
+    for (int sb = 0; sb < NSB; ++sb) {
+      accK[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      accV[sb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
     for (int r = 0; r < R; ++r) {
@@ -289,52 +298,56 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       scores16<DP, C>(sK, sQ, LQ, nullptr, sP, GRAD ? sPT : nullptr, LC, w, lane);
       __syncthreads();
 
-      // ---- o^T = (S^T phi(Q)^T + V^T P^T) / den; partial dots dO . o for beta
-      if (has_out) {
-        // den_i = phi(Q_i) . z_pre + sum_j P[i][j] (P is 0 past the diagonal):
-        // each half of the wave sums half of the features and keys
-        float dpart = 0.0f;
+      // ---- 1 / den_i with den_i = phi(Q_i) . z_pre + sum_j P[i][j] (TPQ
+      // threads per query, each summing a share of the features and of the
+      // keys of the written 32-blocks of P's row), and the numerator blocks
+      // o^T[b][i] = sum_a S^T[b][a] phi(Q)[i][a] + sum_j V^T[b][j] P[i][j]
+      // (keys j < 16 (qb + 1): P is 0 past the diagonal) with their partial
+      // dots dO . o per feature block (scaled by 1 / den_i^2 in beta)
+      {
+        constexpr int TPQ = NT / C, FPT = DP / TPQ, KPT = C / TPQ;
+        static_assert(FPT % 4 == 0 && KPT % 4 == 0, "16-byte shares");
+        const int qi = tid / TPQ, pp = tid % TPQ, jlim = 32 * (qi / 32 + 1);
+        float dd = 0.0f;
 #pragma unroll
-        for (int a = 0; a < DP / 2; a += 4) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(sQ + i * LQ + h * (DP / 2) + a);
-          const f32x4 zv = *reinterpret_cast<const f32x4*>(sz + h * (DP / 2) + a);
-          dpart += qv[0] * zv[0] + qv[1] * zv[1] + qv[2] * zv[2] + qv[3] * zv[3];
+        for (int a = pp * FPT; a < (pp + 1) * FPT; a += 4) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(sQ + qi * LQ + a);
+          const f32x4 zv = *reinterpret_cast<const f32x4*>(sz + a);
+          dd += qv[0] * zv[0] + qv[1] * zv[1] + qv[2] * zv[2] + qv[3] * zv[3];
         }
-        for (int jb = 0; jb <= ib; ++jb) {
 #pragma unroll
-          for (int t = 0; t < 16; t += 4) {
-            const f32x4 pv = *reinterpret_cast<const f32x4*>(sP + i * LC + jb * 32 + 16 * h + t);
-            dpart += pv[0] + pv[1] + pv[2] + pv[3];
+        for (int jj = pp * KPT; jj < (pp + 1) * KPT; jj += 4) {
+          if (jj < jlim) {
+            const f32x4 pv = *reinterpret_cast<const f32x4*>(sP + qi * LC + jj);
+            dd += pv[0] + pv[1] + pv[2] + pv[3];
           }
         }
-        const float den = dpart + __shfl_xor(dpart, 32);
-        const float inv = i < nv ? 1.0f / den : 0.0f;  // rows past the end: no gradient
 #pragma unroll
-        for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = nb0 + uu * NB_STEP;
-          if (nb < NBB) {
-            f32x16 o = f32x16{};
-            gemm_acc<T, DP / 16>(o, sST + nb * 32 * LQ, LQ, sQ + ib * 32 * LQ, LQ, lane);
+        for (int off = 1; off < TPQ; off <<= 1) dd += __shfl_xor(dd, off);
+        if (pp == 0) sinv[qi] = qi < nv ? 1.0f / dd : 0.0f;  // rows past the end: no gradient
+      }
 #pragma unroll
-            for (int jb = 0; jb <= ib; ++jb)
-              gemm_acc<T, 2>(o, sVT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
-            float part = 0.0f;  // sum over this lane's 16 features b of dO[i][b] o[b][i]
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-              part += to_f(sG[i * LQ + nb * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3)]) * o[rr] * inv;
-            part += __shfl_xor(part, 32);
-            if (h == 0) spart[nb][i] = part;
-          }
-        }
-        if (nb0 == 0 && h == 0) sinv[i] = inv;
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int e = w + NW * sb, qb = e / NFB, fb = e % NFB;
+        f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        mm16(o, sST + 16 * fb * LQ, LQ, sQ + 16 * qb * LQ, LQ, 0, NFB, lane);
+        mm16(o, sVT + 16 * fb * LC, LC, sP + 16 * qb * LC, LC, 0, qb + 1, lane);
+        const int qi = 16 * qb + m16;  // o[rr]: feature 16 fb + 4 kq + rr of query qi
+        const f32x4 g = *reinterpret_cast<const f32x4*>(sG + qi * LQ + 16 * fb + 4 * kq);
+        float part = g[0] * o[0] + g[1] * o[1] + g[2] * o[2] + g[3] * o[3];
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (kq == 0) spart[fb][qi] = part;
       }
       __syncthreads();
-      // beta_i = -inv_i (dO_i . o_i); G = dO * inv (token- and feature-major)
+      // beta_i = -inv_i (dO_i . o_i) = -inv_i^2 (dO_i . num_i); G = dO * inv
+      // (token- and feature-major)
       if (tid < C) {
         float dot = 0.0f;
 #pragma unroll
-        for (int nb = 0; nb < NBB; ++nb) dot += spart[nb][tid];
-        sbeta[tid] = -sinv[tid] * dot;
+        for (int fb = 0; fb < NFB; ++fb) dot += spart[fb][tid];
+        const float iv = sinv[tid];
+        sbeta[tid] = -(iv * iv) * dot;
       }
       for (int idx = tid; idx < C * DP; idx += NT) {
         const int qi = idx / DP, b = idx % DP;
@@ -365,49 +378,22 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       scores16<DP, C>(sV, sG, LQ, sbeta, sP, sAT, LC, w, lane);
       __syncthreads();
 
-      // ---- dphi(Q)^T [a][i] = S G^T + phi(K)^T A^T + z beta^T (staged in sQ),
-      // dphi(K)^T += phi(Q)^T A, dV^T += G^T P (key block ib)
-      f32x16 accQ[NPW];
-      if (has_out) {
+      // ---- dphi(Q)^T[a][i] = sum_b S[a][b] G[i][b] + sum_j K^T[a][j] A[i][j]
+      // (+ z_a beta_i, then staged in sQ: nothing reads phi(Q) token-major
+      // any more), dphi(K)^T[a][j] += sum_i Q^T[a][i] A^T[j][i] and
+      // dV^T[b][j] += sum_i G^T[b][i] P^T[j][i] over the queries i >= 16 jb
 #pragma unroll
-        for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = nb0 + uu * NB_STEP;
-          accQ[uu] = f32x16{};
-          if (nb < NBB) {
-            gemm_acc<T, DP / 16>(accQ[uu], sS + nb * 32 * LQ, LQ, sG + ib * 32 * LQ, LQ, lane);
-#pragma unroll
-            for (int jb = 0; jb <= ib; ++jb)
-              gemm_acc<T, 2>(accQ[uu], sKT + nb * 32 * LC + jb * 32, LC, sP + ib * 32 * LC + jb * 32, LC, lane);
-          }
-        }
-      }
-      if (kv_out) {
-#pragma unroll
-        for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = kv_nb0 + uu * NB_STEP;
-          if (nb < NBB) {
-#pragma unroll
-            for (int ib2 = ib; ib2 < NIB; ++ib2) {
-              gemm_acc<T, 2>(accK[uu], sQT + nb * 32 * LC + ib2 * 32, LC, sAT + ib * 32 * LC + ib2 * 32, LC, lane);
-              gemm_acc<T, 2>(accV[uu], sGT + nb * 32 * LC + ib2 * 32, LC, sPT + ib * 32 * LC + ib2 * 32, LC, lane);
-            }
-          }
-        }
-      }
-      __syncthreads();  // sQ is free: dQ rows go out through it
-      if (has_out) {
-        const float bq = sbeta[i];
-#pragma unroll
-        for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = nb0 + uu * NB_STEP;
-          if (nb < NBB) {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-              const int a = nb * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-              sQ[i * LQ + a] = cvt<T>(accQ[uu][rr] + sz[a] * bq);
-            }
-          }
-        }
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int e = w + NW * sb, qb = e / NFB, fb = e % NFB;
+        f32x4 aq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        mm16(aq, sS + 16 * fb * LQ, LQ, sG + 16 * qb * LQ, LQ, 0, NFB, lane);
+        mm16(aq, sKT + 16 * fb * LC, LC, sP + 16 * qb * LC, LC, 0, qb + 1, lane);
+        mm16(accK[sb], sQT + 16 * fb * LC, LC, sAT + 16 * qb * LC, LC, qb, NQB, lane);
+        mm16(accV[sb], sGT + 16 * fb * LC, LC, sPT + 16 * qb * LC, LC, qb, NQB, lane);
+        const int qi = 16 * qb + m16, a0 = 16 * fb + 4 * kq;
+        const float bq = sbeta[qi];
+        const f32x4 zv = *reinterpret_cast<const f32x4*>(sz + a0);
+        *reinterpret_cast<f32x4*>(sQ + qi * LQ + a0) = aq + zv * bq;
       }
       // ---- U -= phi(Q)^T G, u -= phi(Q)^T beta: the states after chunk c
 #pragma unroll
@@ -442,30 +428,20 @@ __global__ __launch_bounds__(NT) void k_bwd(BwdArgs A) {
       }
       if (tid < DP) su[tid] = urun[0];
       __syncthreads();
-      if (kv_out) {
 #pragma unroll
-        for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = kv_nb0 + uu * NB_STEP;
-          if (nb < NBB) {
-            gemm_acc<T, DP / 16>(accK[uu], sU + nb * 32 * LQ, LQ, sV + ib * 32 * LQ, LQ, lane);
-            gemm_acc<T, DP / 16>(accV[uu], sUT + nb * 32 * LQ, LQ, sK + ib * 32 * LQ, LQ, lane);
-          }
-        }
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int e = w + NW * sb, jb = e / NFB, fb = e % NFB;
+        mm16(accK[sb], sU + 16 * fb * LQ, LQ, sV + 16 * jb * LQ, LQ, 0, NFB, lane);
+        mm16(accV[sb], sUT + 16 * fb * LQ, LQ, sK + 16 * jb * LQ, LQ, 0, NFB, lane);
       }
       __syncthreads();  // sQ and sG are free: dK and dV rows go out through them
-      if (kv_out) {
 #pragma unroll
-        for (int uu = 0; uu < NPW; ++uu) {
-          const int nb = kv_nb0 + uu * NB_STEP;
-          if (nb < NBB) {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-              const int a = nb * 32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-              sQ[i * LQ + a] = cvt<T>(accK[uu][rr] + su[a]);
-              sG[i * LQ + a] = cvt<T>(accV[uu][rr]);
-            }
-          }
-        }
+      for (int sb = 0; sb < NSB; ++sb) {
+        const int e = w + NW * sb, jb = e / NFB, fb = e % NFB;
+        const int kj = 16 * jb + m16, a0 = 16 * fb + 4 * kq;
+        const f32x4 uv = *reinterpret_cast<const f32x4*>(su + a0);
+        *reinterpret_cast<f32x4*>(sQ + kj * LQ + a0) = accK[sb] + uv;
+        *reinterpret_cast<f32x4*>(sG + kj * LQ + a0) = accV[sb];
       }
       __syncthreads();
       rows_out<TI, T, DP, PM>(sQ, LQ, nv, d, vec, reinterpret_cast<TI*>(A.dk) + u * n * d, kb, t0, tid);
