@@ -501,7 +501,17 @@ int run_backward(const la_internal::BwdCall& a) {
   const la_internal::SeqCall sc = la_internal::backward_seqcall(a);
   const la_internal::Plan p = la_internal::seq_plan(sc, C);
   const int64_t units = a.B * a.Hkv;
-  int e = la_internal::launch_seq_prefix(sc, C);  // forward prefix slots at a.ws
+  // forward prefix slots at a.ws: bf16 with relu + 1 or caller-applied
+  // features on the bf16-MFMA state pass (exact products), otherwise on fp32
+  // tiles
+  int e = a.dtype != 0 ? la_internal::launch_state_bf16_exact(a.k, a.v, units, a.n, (int)a.d, a.phi, C, p.nchunks,
+                                                               p.G, p.nseg, reinterpret_cast<float*>(a.ws), a.stream)
+                       : -1;
+  if (e == -1)
+    e = la_internal::launch_seq_prefix(sc, C);
+  else if (e == 0)
+    e = la_internal::launch_scan(reinterpret_cast<float*>(a.ws), units, p.nseg, DP, (int)a.d, nullptr, nullptr,
+                                 a.stream);
   if (e != 0) return e;
   float* fstates = reinterpret_cast<float*>(a.ws);
   float* ustates = fstates + units * (p.nseg + 1) * slot_elems(DP);

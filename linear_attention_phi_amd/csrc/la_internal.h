@@ -183,6 +183,13 @@ int launch_backward(const BwdCall& a);
 // k_scan over (nseg + 1) slots per unit, F = 1 (la_kernels.hip).
 int launch_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S_final, float* z_final,
                 void* stream);
+// The causal form's segment states on bf16 MFMA (k_state, la_kernels.hip)
+// for contiguous bf16 [units, n, d] rows with d = 64 and chunk 32, where they
+// are exact up to fp32 summation (relu + 1 through its split, or
+// caller-applied features): ws receives one slot per segment of G chunks.
+// Returns -1 (nothing launched) for any other case.
+int launch_state_bf16_exact(const void* k, const void* v, int64_t units, int64_t n, int d, int phi, int C,
+                            int64_t nchunks, int64_t G, int64_t nseg, float* ws, void* stream);
 
 int launch_decode(const void* q, const void* k, const void* v, int64_t B,
                   int64_t Hq, int64_t Hkv, int64_t d, int dtype, int phi,

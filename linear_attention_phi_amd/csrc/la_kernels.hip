@@ -1901,6 +1901,20 @@ int launch_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S
   return (int)hipGetLastError();
 }
 
+int launch_state_bf16_exact(const void* k, const void* v, int64_t units, int64_t n, int d, int phi, int C,
+                            int64_t nchunks, int64_t G, int64_t nseg, float* ws, void* stream) {
+  if (d != 64 || C != 32 || phi == 1) return -1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bf16* kk = reinterpret_cast<const bf16*>(k);
+  const bf16* vv = reinterpret_cast<const bf16*>(v);
+  const dim3 grid((unsigned)(units * nseg));
+  if (phi == 2)
+    k_state<bf16, 64, 32, PM_FEAT><<<grid, NT, 0, st>>>(kk, vv, n, d, true, nchunks, G, nseg, ws);
+  else
+    k_state<bf16, 64, 32, PM_RELU1><<<grid, NT, 0, st>>>(kk, vv, n, d, true, nchunks, G, nseg, ws);
+  return (int)hipGetLastError();
+}
+
 int launch_decode(const void* q, const void* k, const void* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t d,
                   int dtype, int phi, float* S, float* z, void* out, void* stream) {
   if (phi == 2) return launch_decode_pm<PM_FEAT>(q, k, v, B, Hq, Hkv, d, dtype, S, z, out, stream);
