@@ -282,7 +282,8 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 // (the contraction index k is lane / 16, the other index lane % 16):
 //   S^T  from LDS in operand order: entry (bb, tt, lane) is the float4 over
 //        jj of S[16 tt + 4 (lane / 16) + jj][16 bb + lane % 16], kept in
-//        slot lane ^ (4 bb + tt) of block 4 bb + tt;
+//        slot lane ^ (4 bb + tt) of block 4 bb + tt (one 16-byte read per
+//        lane, 1 KB per wave, no bank conflicts);
 //   Q^T  the float4 of query row lane % 16 at features 16 tt + 4 (lane / 16);
 //   K    the float4 of key row 16 kb + lane % 16 at the same features;
 //   P^T  the score accumulator itself: its register rr holds key
@@ -292,10 +293,19 @@ __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nse
 //        one float per lane from the V tile.
 // A lane's output accumulator holds features 16 bb + 4 (lane / 16) .. + 3 of
 // query lane % 16.  The last four waves keep the state: the w-th of them
-// holds tiles (j, j') = (w, 0..3) in accumulator order (entry rr of lane l:
-// S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']), writes them in operand order
-// at the chunk's start and adds K_c^T V_c during the chunk's first query
-// group.
+// holds the blocks (tt, bb) = (w, 0..3) with entry rr of lane l =
+// S[16 w + 4 (l / 16) + rr][16 bb + l % 16] -- exactly the readers' float4 of
+// block (bb, tt), so it goes to LDS with one 16-byte store per block at the
+// chunk's start -- and adds K_c^T V_c during the chunk's first query group
+// (A = K^T with rows a, B = V with columns b, one float of each per lane and
+// k-step, key 16 (st / 4) + 4 (l / 16) + st % 4 at step st).
+// The state's operand-order stores are whole float4s (with the state held
+// the other way round they were 16 scalar stores per wave and chunk, 8-way
+// bank-conflicted on gfx950: 147.7 / 177.1 against 150.0 / 178.2 us per call
+// at B4 H8 n8192, m = arange / uniform); the state update's scalar reads
+// (rows four apart) and the V reads are conflict-free at the 68-float row
+// stride.  (A 72-float stride for the K and Q tiles, whose 16-byte operand
+// reads it makes conflict-free, measured no faster: 150.4 / 177.5 us.)
 // With CS (the causal normalised form, feature map PM) the buckets are the
 // chunks themselves (query i of chunk c = row c C + i, m_i = i, no sort), Q
 // rows and K tiles take phi as they are staged (key rows past n stay 0), and
@@ -329,12 +339,13 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
                                                       const int* __restrict__ perm,
                                                       const int* __restrict__ boff, const int64_t* __restrict__ m,
                                                       int64_t H, int64_t nmask) {
-  constexpr int FD = 64, C = 64, RS = PX_RS, QG = 16 * NWV, NT_ = 64 * NWV;
+  constexpr int FD = 64, C = 64, QG = 16 * NWV, NT_ = 64 * NWV;
   constexpr int KVP = C * FD / 4 / NT_;  // 16-byte pieces of a K or V tile per thread
   static_assert(NWV == 4 || NWV == 8, "four or eight waves");
-  __shared__ __attribute__((aligned(16))) float sK[C * RS];
-  __shared__ __attribute__((aligned(16))) float sV[C * RS];
-  __shared__ __attribute__((aligned(16))) float sQ[QG * RS];
+  constexpr int RK = PX_RS, RV = PX_RS;
+  __shared__ __attribute__((aligned(16))) float sK[C * RK];
+  __shared__ __attribute__((aligned(16))) float sV[C * RV];
+  __shared__ __attribute__((aligned(16))) float sQ[QG * RK];
   __shared__ __attribute__((aligned(16))) float sS[16 * 64 * 4];  // S in operand order
   __shared__ __attribute__((aligned(16))) float sz[FD];            // z_prev (CS)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
@@ -364,27 +375,28 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   const float* vh = v + bh * n * FD;
   float* oh = out + bh * n * FD;
 
-  // waves 4-7: state tiles (w - 4, 0..3), from the segment's exclusive
-  // prefix (row-major)
+  // the last four waves: state blocks (tt, bb) = (sj, 0..3), from the
+  // segment's exclusive prefix (row-major)
   const bool owner = w >= NWV - 4;
   const int sj = w & 3;
   f32x4 accS[4];
   {
     const float* src = ws + (bh * (nseg_ws + 1) + F * seg) * slot_elems(FD);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) accS[t][rr] = owner ? src[(16 * kq + 4 * rr + sj) * FD + 4 * mm + t] : 0.0f;
+      for (int rr = 0; rr < 4; ++rr) accS[bb][rr] = owner ? src[(16 * sj + 4 * kq + rr) * FD + 16 * bb + mm] : 0.0f;
   }
   float zacc = 0.0f;  // CS: z_prev of feature tid (wave 0)
   if (CS && tid < FD) zacc = ws[(bh * (nseg_ws + 1) + F * seg) * slot_elems(FD) + FD * FD + tid];
-  auto state_update = [&]() {  // S += K_c^T V_c on this wave's tiles
+  auto state_update = [&]() {  // S += K_c^T V_c on this wave's blocks
 #pragma unroll
     for (int st = 0; st < C / 4; ++st) {
-      const f32x4 kv = *reinterpret_cast<const f32x4*>(sK + (4 * st + kq) * RS + 4 * mm);
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(sV + (4 * st + kq) * RS + 4 * mm);
+      const int key = 16 * (st >> 2) + 4 * kq + (st & 3);
+      const float ka = sK[key * RK + 16 * sj + mm];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) accS[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[sj], vv[t], accS[t], 0, 0, 0);
+      for (int bb = 0; bb < 4; ++bb)
+        accS[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka, sV[key * RV + 16 * bb + mm], accS[bb], 0, 0, 0);
     }
   };
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
@@ -432,26 +444,18 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
       const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
       f32x4 kk = kr[u];
       if (CS) kk = t0 + row < n ? phi4(kk) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      *reinterpret_cast<f32x4*>(sK + row * RS + col) = kk;
-      *reinterpret_cast<f32x4*>(sV + row * RS + col) = vr[u];
+      *reinterpret_cast<f32x4*>(sK + row * RK + col) = kk;
+      *reinterpret_cast<f32x4*>(sV + row * RV + col) = vr[u];
     }
     if (CS && tid < FD) sz[tid] = zacc;
     if (c + 1 < c1) fetch_kv(c + 1);
-    // S_prev(c) in operand order: tile entry S[16 kq + 4 rr + sj][4 mm + j']
-    // -> (bb, tt, L, jj) = (mm / 4, kq, 16 rr + 4 (mm % 4) + j', sj).  Entry
-    // L of block bb * 4 + tt sits in float4 slot L ^ (bb * 4 + tt) of the
-    // block: unswizzled, the 64 lanes of one of these scalar stores differ
-    // only in L % 16 = 4 (mm % 4) + j' and reach 4 banks (16-way); the XOR
-    // with the block index spreads them over 16, the most a store that fills
-    // one float component (jj = sj) can reach.  Readers take whole float4s
-    // and stay conflict-free.
+    // S_prev(c) in operand order: block (bb, tt = sj) entry lane is accS[bb]
     if (owner) {
-      const int blk = (mm >> 2) * 4 + kq;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          sS[(blk * 64 + ((16 * rr + 4 * (mm & 3) + t) ^ blk)) * 4 + sj] = accS[t][rr];
+      for (int bb = 0; bb < 4; ++bb) {
+        const int blk = bb * 4 + sj;
+        *reinterpret_cast<f32x4*>(sS + (blk * 64 + (lane ^ blk)) * 4) = accS[bb];
+      }
     }
     __syncthreads();  // tiles and S visible
     if (ngroups == 0 && owner) state_update();
@@ -460,7 +464,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
-        *reinterpret_cast<f32x4*>(sQ + row * RS + col) = qraw[u];
+        *reinterpret_cast<f32x4*>(sQ + row * RK + col) = qraw[u];
       }
       fetch_q_after(c, grp);
       __syncthreads();  // the group's query rows visible
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
         const int limit = (int)(mi - t0);
         f32x4 qo[4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) qo[tt] = *reinterpret_cast<const f32x4*>(sQ + (16 * w + mm) * RS + 16 * tt + 4 * kq);
+        for (int tt = 0; tt < 4; ++tt) qo[tt] = *reinterpret_cast<const f32x4*>(sQ + (16 * w + mm) * RK + 16 * tt + 4 * kq);
         f32x4 o[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) o[bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
         for (int tt = 0; tt < 4; ++tt) {
           f32x4 ko[C / 16];
 #pragma unroll
-          for (int kb = 0; kb < C / 16; ++kb) ko[kb] = *reinterpret_cast<const f32x4*>(sK + (16 * kb + mm) * RS + 16 * tt + 4 * kq);
+          for (int kb = 0; kb < C / 16; ++kb) ko[kb] = *reinterpret_cast<const f32x4*>(sK + (16 * kb + mm) * RK + 16 * tt + 4 * kq);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
           for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
-              o[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(sV[(16 * kb + 4 * kq + rr) * RS + 16 * bb + mm], sc[kb][rr], o[bb], 0, 0, 0);
+              o[bb] = __builtin_amdgcn_mfma_f32_16x16x4f32(sV[(16 * kb + 4 * kq + rr) * RV + 16 * bb + mm], sc[kb][rr], o[bb], 0, 0, 0);
         if constexpr (CS) {  // denominator of query mm: phi(Q) . z_prev + its masked scores
           float dn = 0.0f;
 #pragma unroll
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
     }
     if (CS && tid < FD) {  // z_prev(c + 1): add this chunk's phi(K) column sums (rows past n are 0)
 #pragma unroll 8
-      for (int r = 0; r < C; ++r) zacc += sK[r * RS + tid];
+      for (int r = 0; r < C; ++r) zacc += sK[r * RK + tid];
     }
     __syncthreads();  // tiles and S are rewritten by the next chunk
   }
