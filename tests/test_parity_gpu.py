@@ -242,9 +242,26 @@ def test_causal_f32_d64_chunk64_output_kernel(gpu, phi, shape):
     np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
 
 
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("shape", [(1, 1, 65536), (1, 2, 40000)], ids=lambda c: "B%d_H%d_n%d" % c)
+def test_causal_f32_d64_chunk64_walks_several_chunks(gpu, phi, shape):
+    """Shapes where each output workgroup walks several chunks (two at
+    B1 H1 n65536, three at B1 H2 n40000), so that S and z are carried from
+    chunk to chunk inside the workgroup: every row against the oracle, both
+    feature maps, and the final state."""
+    B, H, n = shape
+    q, k, v, _ = li.qkv(B, H, H, n, 64, li.F32, seed=23, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True, phi=phi)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True, phi=phi)
+    check(host(out), ref, li.F32, f"causal f32 d64 {phi} B{B} H{H} n{n}")
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-4, atol=1e-4 * np.abs(Sr).max())
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-5)
+
+
 def test_causal_f32_d64_full_scale_sampled(gpu):
-    """The same kernel at B4 H8 n8192 (512 output workgroups, two state
-    segments each): sampled rows against the oracle's closed form per row."""
+    """The same kernel at B4 H8 n8192 (512 output workgroups, each walking
+    one state segment of eight chunks): sampled rows against the oracle's
+    closed form per row."""
     B, H, n, d = 4, 8, 8192, 64
     q, k, v, _ = li.qkv(B, H, H, n, d, li.F32, seed=13, scaled=True)
     g = host(gpu.la_causal_forward(dev(q), dev(k), dev(v)))
