@@ -873,34 +873,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
 }
 
 // ----------------------------------------------------------------- k_out_gqa
-// Causal output for bf16 with d = 128, chunk 32 and R = 2 or 4 query heads
+// Causal output for bf16 with d = 128, chunk 32 and R = 1, 2 or 4 query heads
 // per key/value head: the R query heads of a chunk are worked on at once
-// (8 waves; head g = w / (8 / R), each of its 8 / R waves 128 R / 8 of the
-// output features), so that a chunk costs two barriers whatever R is,
-// against four per query head in k_out.  Each wave forms its
+// (NWV = 8 waves for R = 2, 4, four for R = 1; head g = w / (NWV / R), each
+// of its NWV / R waves 32 of the output features at R = 1 and 4 * 32 R / NWV
+// otherwise), so that a chunk costs two barriers whatever R is, against four
+// per query head in k_out.  Each wave forms its
 // head's score block P^T = phi(K) phi(Q)^T itself, in registers (its
 // accumulator is the B operand of V^T P^T; la_device.h), and the row sums of
 // the rounded P for the normaliser.  The state is carried as in k_out: two of
-// the 16 32 x 32 state blocks per wave in MFMA accumulators, relu(K)^T V on
-// top of the segment's exclusive prefix, plus 1 (x) (sum of V).  relu(K) and
-// V stay token-major in LDS; their operands over the token index (V^T for
-// V^T P^T, both operands of relu(K)^T V) are transposed reads, and z and the
-// sums of V are dot2 sums over those fragments (waves 0-3: z of rows
-// 32 w .., waves 4-7: sums of V of columns 32 (w - 4) ..).
+// the 16 32 x 32 state blocks per wave in MFMA accumulators (four with four
+// waves), relu(K)^T V on top of the segment's exclusive prefix, plus
+// 1 (x) (sum of V).  relu(K) and V stay token-major in LDS; their operands
+// over the token index (V^T for V^T P^T, both operands of relu(K)^T V) are
+// transposed reads, and z and the sums of V are dot2 sums over those
+// fragments (eight waves: waves 0-3 z of rows 32 w .., waves 4-7 sums of V of
+// columns 32 (w - 4) ..; four waves: wave w both, for 32 w ..).
 // A workgroup walks F state segments (G chunks of the state pass each) and
 // starts from the exclusive prefix in slot F * seg of the workspace, whose
 // per-head stride is nseg_ws + 1 slots.
+template <int R> constexpr int gqa_waves() { return R == 1 ? 4 : 8; }
 template <int R, int PM>
-__global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, const bf16* __restrict__ k,
+// (two waves per SIMD: one eight-wave workgroup or two four-wave ones per CU)
+__global__ __launch_bounds__(64 * gqa_waves<R>()) __attribute__((amdgpu_waves_per_eu(2))) void k_out_gqa(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                  const bf16* __restrict__ v, bf16* __restrict__ out, int64_t n,
                                                  int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
                                                  int64_t nseg_ws, const float* __restrict__ ws) {
   constexpr int DP = 128, C = 32;
   constexpr int LQ = DP + PAD;  // row stride of sK, sQ, sO, sST
   constexpr int RS = STR_RS;    // row stride of sKr, sV (conflict-free transposed reads)
-  constexpr int NPH = 8 / R;    // waves per query head
-  constexpr int NBW = 4 / NPH;  // 32-wide output feature blocks per wave
-  static_assert(R == 2 || R == 4, "two or four query heads per key/value head");
+  constexpr int NWV = gqa_waves<R>(), NT_ = 64 * NWV;
+  constexpr int NPH = NWV / R;   // waves per query head
+  constexpr int NBW = 4 / NPH;   // 32-wide output feature blocks per wave
+  constexpr int NH = NWV / 4;    // 256-thread halves sharing the tile loads
+  constexpr int NSW = 16 / NWV;  // state blocks per wave
+  static_assert(R == 1 || R == 2 || R == 4, "one, two or four query heads per key/value head");
   // relu + 1 split as in k_state_tr; ELU + 1: phi(K), phi(Q) in the tiles
   constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LQ];       // phi(K), token-major
@@ -915,29 +922,31 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
   __shared__ float svc[DP];  // sum of V over the chunks done so far
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, r = lane & 31;
-  const int half = tid >> 8, ht = tid & 255;  // the two 256-thread halves share the tile loads
+  const int half = tid >> 8, ht = tid & 255;  // the 256-thread halves share the tile loads
   const int g = w / NPH, hf = w % NPH;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   const bf16* kb = k + bh * n * DP;
   const bf16* vb = v + bh * n * DP;
   const float* slot = ws + (bh * (nseg_ws + 1) + F * seg) * slot_elems(DP);
 
-  // state blocks e = w and w + 8: (row block ma, column block nb) = (e / 4, e % 4)
-  f32x16 accS[2];
+  // state blocks e = w + NWV s: (row block ma, column block nb) = (e / 4, e % 4)
+  f32x16 accS[NSW];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) ld_state_block<DP>(accS[s], slot, (w + 8 * s) / 4, (w + 8 * s) % 4, lane);
-  float zrun = 0.0f, vrun = 0.0f;  // waves 0-3: z[32 w + r]; waves 4-7: sum of V[., 32 (w - 4) + r]
+  for (int s = 0; s < NSW; ++s) ld_state_block<DP>(accS[s], slot, (w + NWV * s) / 4, (w + NWV * s) % 4, lane);
+  // waves 0-3: z[32 w + r]; the sum of V[., 32 (w - 4) + r] on waves 4-7 (8
+  // waves), of V[., 32 w + r] beside z (4 waves)
+  float zrun = 0.0f, vrun = 0.0f;
   if (w < 4) zrun = slot[DP * DP + 32 * w + r];
   if (tid < DP) {
     svc[tid] = 0.0f;
     szero[tid] = (bf16)0.0f;
   }
 
-  // Tiles of a chunk: half 0 loads K, half 1 V, two adjacent rows x 8
-  // features per thread; query tile g goes to half g % 2.
-  constexpr int QPH = R / 2;  // query tiles per half
+  // Tiles of a chunk: half 0 loads K, half 1 V (one half: both), two adjacent
+  // rows x 8 features per thread; query tile g goes to half g % NH.
+  constexpr int QPH = R / NH;  // query tiles per half
   TileRaw<bf16, DP, C> raw[QPH];
-  la_bf16::u32x4 kv2[2];
+  la_bf16::u32x4 kv2[2], vv2[2];
   const int pr0 = 2 * (ht >> 4), pc0 = 8 * (ht & 15);
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
   auto fetch = [&](int64_t c) {
@@ -948,9 +957,15 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
     for (int rr = 0; rr < 2; ++rr)
       kv2[rr] = pr0 + rr < nvc ? *reinterpret_cast<const la_bf16::u32x4*>(src + (tc + pr0 + rr) * DP + pc0)
                                : la_bf16::u32x4{0u, 0u, 0u, 0u};
+    if constexpr (NH == 1) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        vv2[rr] = pr0 + rr < nvc ? *reinterpret_cast<const la_bf16::u32x4*>(vb + (tc + pr0 + rr) * DP + pc0)
+                                 : la_bf16::u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int u = 0; u < QPH; ++u)
-      tile_fetch<bf16, DP, C>(raw[u], q + (bh * R + 2 * u + half) * n * DP, tc, nullptr, nvc, ht);
+      tile_fetch<bf16, DP, C>(raw[u], q + (bh * R + NH * u + half) * n * DP, tc, nullptr, nvc, ht);
   };
   if (c0 < c1) fetch(c0);
   __syncthreads();
@@ -971,6 +986,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
             x[j] = SPLIT ? la_bf16::relu2(x[j]) : (pr0 + rr < nv ? la_bf16::map2<PM>(x[j]) : 0u);
         }
         *reinterpret_cast<la_bf16::u32x4*>(tm + (pr0 + rr) * RS + pc0) = x;
+        if constexpr (NH == 1) *reinterpret_cast<la_bf16::u32x4*>(sV + (pr0 + rr) * RS + pc0) = vv2[rr];
       }
       if (half == 0) {
 #pragma unroll
@@ -987,11 +1003,11 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
     }
 #pragma unroll
     for (int u = 0; u < QPH; ++u)
-      tile_store<bf16, DP, C, q_xform<PM>(), XF_NONE>(raw[u], nv, sQ[2 * u + half], nullptr, ht);
+      tile_store<bf16, DP, C, q_xform<PM>(), XF_NONE>(raw[u], nv, sQ[NH * u + half], nullptr, ht);
     if (c + 1 < c1) fetch(c + 1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int e = w + 8 * s, ma = e / 4, nb = e % 4;
+    for (int s = 0; s < NSW; ++s) {
+      const int e = w + NWV * s, ma = e / 4, nb = e % 4;
       f32x16 cur = accS[s];
       if (SPLIT) add_col(cur, svc[nb * 32 + r], ma, DP, lane);
       st_accT(sST + nb * 32 * LQ + ma * 32, LQ, cur, lane);  // sST[b][a] = S[a][b]
@@ -1042,21 +1058,31 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
 #pragma unroll
       for (int kt = 0; kt < C / 16; ++kt) vt[kt] = la_bf16::ld_tr<RS>(sV, 16 * kt, (w % 4) * 32, lane);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int ma = (w + 8 * s) / 4;  // column block w % 4
+      for (int s = 0; s < NSW; ++s) {
+        const int ma = (w + NWV * s) / 4;  // column block w % 4
 #pragma unroll
         for (int kt = 0; kt < C / 16; ++kt) mma(accS[s], la_bf16::ld_tr<RS>(sKr, 16 * kt, ma * 32, lane), vt[kt]);
       }
-      // waves 0-3: z of rows 32 w ..; waves 4-7: sums of V of columns 32 (w - 4) ..
-      float cs = 0.0f;
+      // waves 0-3: z of rows 32 w ..; the sums of V of columns 32 (w - 4) ..
+      // on waves 4-7, of columns 32 w .. beside z with four waves
+      float cs = 0.0f, csv = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < C / 16; ++kt) {
         const Frag<bf16> f = w < 4 ? la_bf16::ld_tr<RS>(sKr, 16 * kt, w * 32, lane) : vt[kt];
 #pragma unroll
         for (int j = 0; j < 4; ++j) cs = la_bf16::dot2(la_bf16::pair(f, j), la_bf16::ONE2, cs);
+        if constexpr (NWV == 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) csv = la_bf16::dot2(la_bf16::pair(vt[kt], j), la_bf16::ONE2, csv);
+        }
       }
       cs += __shfl_xor(cs, 32);
-      if (w < 4) {
+      if constexpr (NWV == 4) {
+        csv += __shfl_xor(csv, 32);
+        zrun += cs + (SPLIT ? (float)nv : 0.0f);
+        vrun += csv;
+        if (h == 0) svc[32 * w + r] = vrun;  // read at the next chunk's start (this chunk read it before the barrier above)
+      } else if (w < 4) {
         zrun += cs + (SPLIT ? (float)nv : 0.0f);
       } else {
         vrun += cs;
@@ -1070,7 +1096,7 @@ __global__ __launch_bounds__(512) void k_out_gqa(const bf16* __restrict__ q, con
 #pragma unroll
     for (int gg = 0; gg < R; ++gg) {
 #pragma unroll
-      for (int pp = tid; pp < PIECES; pp += 512) {
+      for (int pp = tid; pp < PIECES; pp += NT_) {
         const int row = pp / (DP / 8), col = 8 * (pp % (DP / 8));
         if (row < nv)
           __builtin_nontemporal_store(*reinterpret_cast<const la_bf16::u32x4*>(sO[gg] + row * LQ + col),
@@ -1652,7 +1678,7 @@ int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
   if constexpr (std::is_same<T, float>::value && DP == 64) s32 = vec && a.n <= la_internal::kFwd32MaxN;
   if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) px = vec && q && out && R == 1;
-  const bool gq = tr && q && out && (R == 2 || R == 4);
+  const bool gq = tr && q && out && (R == 1 || R == 2 || R == 4);
   if (tr) {
     if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
       k_state_tr<PM><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
@@ -1664,7 +1690,10 @@ int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
     k_state<T, DP, C, PM><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
                                                                          p.nseg, states);
   }
-  int64_t F = gq ? nbh * p.nseg / kGqaOutGroups : px ? nbh * p.nseg / kPrefixOutGroups : 1;
+  // output workgroups per CU: one of the eight-wave GQA kernel, two of the
+  // four-wave one (R = 1) and of the prefix-form kernel
+  int64_t F = gq ? nbh * p.nseg / (R == 1 ? 2 * kGqaOutGroups : kGqaOutGroups)
+                 : px ? nbh * p.nseg / kPrefixOutGroups : 1;
   if (F < 1) F = 1;
   const int64_t E = slot_elems(DP);
   k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final,
@@ -1674,7 +1703,10 @@ int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
     if (gq) {
       const bf16* qq = reinterpret_cast<const bf16*>(q);
-      if (R == 2)
+      if (R == 1)
+        k_out_gqa<1, PM><<<dim3((unsigned)(nbh * nseg_o)), 256, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
+                                                                         F, p.nseg, states);
+      else if (R == 2)
         k_out_gqa<2, PM><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
                                                                          F, p.nseg, states);
       else

@@ -506,6 +506,22 @@ def test_gqa_output_kernel_matches_general_path(gpu):
     check(b, ref, li.BF16, "GQA chunk 64")
 
 
+@pytest.mark.parametrize("phi", ["relu1", "elu1"])
+@pytest.mark.parametrize("shape", [(1, 1, 100), (2, 3, 1000), (1, 2, 20000)], ids=lambda c: "B%d_H%d_n%d" % c)
+def test_causal_mha_d128_output_kernel(gpu, phi, shape):
+    """bf16, d = 128, one query head per key/value head: the four-wave
+    variant of the grouped-heads output kernel (chunk 32, a ragged tail, one
+    to several chunks per workgroup); every row against the oracle, and the
+    final state."""
+    B, H, n = shape
+    q, k, v, _ = li.qkv(B, H, H, n, 128, li.BF16, seed=31, scaled=True)
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True, phi=phi)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True, phi=phi)
+    check(host(out), ref, li.BF16, f"causal MHA d128 {phi} B{B} H{H} n{n}")
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-2, atol=1e-2 * np.abs(Sr).max())
+
+
 def test_single_launch_matches_three_launch_path(gpu):
     """The same inputs through chunk 64 (single launch) and chunk 32 (three
     launches) agree to bf16 rounding, and the workspace can be shared."""
