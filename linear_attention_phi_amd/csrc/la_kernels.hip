@@ -873,12 +873,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(k_out_waves<
 }
 
 // ----------------------------------------------------------------- k_out_gqa
-// Causal output for bf16 with d = 128, chunk 32 and R = 1, 2 or 4 query heads
-// per key/value head: the R query heads of a chunk are worked on at once
-// (NWV = 8 waves for R = 2, 4, four for R = 1; head g = w / (NWV / R), each
-// of its NWV / R waves 32 of the output features at R = 1 and 4 * 32 R / NWV
-// otherwise), so that a chunk costs two barriers whatever R is, against four
-// per query head in k_out.  Each wave forms its
+// Causal output for bf16 with d = 128, chunk 32 and R = 1, 2, 4 or 8 query
+// heads per key/value head: the R query heads of a chunk are worked on at
+// once (NWV = 8 waves for R >= 2, four for R = 1; head g = w / (NWV / R),
+// each of its NWV / R waves 4 / (NWV / R) of the four 32-wide output feature
+// blocks), so that a chunk costs two barriers whatever R is (three at R = 8,
+// whose output tiles reuse the query tiles: each head has one wave, which
+// forms all its output blocks before writing them over its phi(Q) tile),
+// against four per query head in k_out.  Each wave forms its
 // head's score block P^T = phi(K) phi(Q)^T itself, in registers (its
 // accumulator is the B operand of V^T P^T; la_device.h), and the row sums of
 // the rounded P for the normaliser.  The state is carried as in k_out: two of
@@ -907,7 +909,8 @@ __global__ __launch_bounds__(64 * gqa_waves<R>()) __attribute__((amdgpu_waves_pe
   constexpr int NBW = 4 / NPH;   // 32-wide output feature blocks per wave
   constexpr int NH = NWV / 4;    // 256-thread halves sharing the tile loads
   constexpr int NSW = 16 / NWV;  // state blocks per wave
-  static_assert(R == 1 || R == 2 || R == 4, "one, two or four query heads per key/value head");
+  static_assert(R == 1 || R == 2 || R == 4 || R == 8, "one, two, four or eight query heads per key/value head");
+  constexpr bool OQ = R == 8;  // output tiles over the query tiles
   // relu + 1 split as in k_state_tr; ELU + 1: phi(K), phi(Q) in the tiles
   constexpr bool SPLIT = PM == PM_RELU1;
   __shared__ __attribute__((aligned(16))) bf16 sK[C * LQ];       // phi(K), token-major
@@ -915,7 +918,7 @@ __global__ __launch_bounds__(64 * gqa_waves<R>()) __attribute__((amdgpu_waves_pe
   __shared__ __attribute__((aligned(16))) bf16 sV[C * RS];      // V, token-major
   __shared__ __attribute__((aligned(16))) bf16 sST[DP * LQ];     // S^T in bf16
   __shared__ __attribute__((aligned(16))) bf16 sQ[R][C * LQ];    // phi(Q) of each query head
-  __shared__ __attribute__((aligned(16))) bf16 sO[R][C * LQ];    // outputs on their way out
+  __shared__ __attribute__((aligned(16))) bf16 sO[OQ ? 1 : R][C * LQ];  // outputs on their way out (R = 8: in sQ)
   __shared__ __attribute__((aligned(16))) bf16 szh[DP];          // z as bf16 high part,
   __shared__ __attribute__((aligned(16))) bf16 szl[DP];          // the remainder,
   __shared__ __attribute__((aligned(16))) bf16 szero[DP];        // and zeros: the z operand's rows
@@ -1038,18 +1041,40 @@ __global__ __launch_bounds__(64 * gqa_waves<R>()) __attribute__((amdgpu_waves_pe
     }
     const float inv = 1.0f / __shfl(ds + zacc[0] + zacc[8], r);  // from the lane with h == 0
     // ---- this wave's output blocks: out^T[b][i] = S^T phi(Q)^T + V^T P^T
+    // (at R = 8 all four are formed before any is written over phi(Q))
+    if constexpr (OQ) {
+      f32x16 o[NBW];
 #pragma unroll
-    for (int u = 0; u < NBW; ++u) {
-      const int nb = hf * NBW + u;
-      f32x16 o = f32x16{};
-      gemm_acc<bf16, DP / 16>(o, sST + nb * 32 * LQ, LQ, qg, LQ, lane);
-      mma(o, la_bf16::ld_tr<RS>(sV, 0, nb * 32, lane), p0);
-      mma(o, la_bf16::ld_tr<RS>(sV, 16, nb * 32, lane), p1);
-      uint2* dst = reinterpret_cast<uint2*>(sO[g] + r * LQ + nb * 32 + 4 * h);
+      for (int u = 0; u < NBW; ++u) {
+        const int nb = hf * NBW + u;
+        o[u] = f32x16{};
+        gemm_acc<bf16, DP / 16>(o[u], sST + nb * 32 * LQ, LQ, qg, LQ, lane);
+        mma(o[u], la_bf16::ld_tr<RS>(sV, 0, nb * 32, lane), p0);
+        mma(o[u], la_bf16::ld_tr<RS>(sV, 16, nb * 32, lane), p1);
+      }
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        dst[2 * qq] = make_uint2(la_bf16::pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv),
-                                 la_bf16::pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+      for (int u = 0; u < NBW; ++u) {
+        const int nb = hf * NBW + u;
+        uint2* dst = reinterpret_cast<uint2*>(sQ[g] + r * LQ + nb * 32 + 4 * h);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          dst[2 * qq] = make_uint2(la_bf16::pack2(o[u][4 * qq] * inv, o[u][4 * qq + 1] * inv),
+                                   la_bf16::pack2(o[u][4 * qq + 2] * inv, o[u][4 * qq + 3] * inv));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NBW; ++u) {
+        const int nb = hf * NBW + u;
+        f32x16 o = f32x16{};
+        gemm_acc<bf16, DP / 16>(o, sST + nb * 32 * LQ, LQ, qg, LQ, lane);
+        mma(o, la_bf16::ld_tr<RS>(sV, 0, nb * 32, lane), p0);
+        mma(o, la_bf16::ld_tr<RS>(sV, 16, nb * 32, lane), p1);
+        uint2* dst = reinterpret_cast<uint2*>(sO[g] + r * LQ + nb * 32 + 4 * h);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          dst[2 * qq] = make_uint2(la_bf16::pack2(o[4 * qq] * inv, o[4 * qq + 1] * inv),
+                                   la_bf16::pack2(o[4 * qq + 2] * inv, o[4 * qq + 3] * inv));
+      }
     }
 
     // ---- S += relu(K_c)^T V_c (two blocks per wave); z and the sum of V
@@ -1093,14 +1118,28 @@ __global__ __launch_bounds__(64 * gqa_waves<R>()) __attribute__((amdgpu_waves_pe
 
     // ---- the R output tiles: whole 256-byte rows, non-temporal stores
     constexpr int PIECES = C * (DP / 8);  // 16-byte pieces per tile
+    if constexpr (OQ) {
 #pragma unroll
-    for (int gg = 0; gg < R; ++gg) {
+      for (int gg = 0; gg < R; ++gg) {
 #pragma unroll
-      for (int pp = tid; pp < PIECES; pp += NT_) {
-        const int row = pp / (DP / 8), col = 8 * (pp % (DP / 8));
-        if (row < nv)
-          __builtin_nontemporal_store(*reinterpret_cast<const la_bf16::u32x4*>(sO[gg] + row * LQ + col),
-                                      reinterpret_cast<la_bf16::u32x4*>(out + ((bh * R + gg) * n + t0 + row) * DP + col));
+        for (int pp = tid; pp < PIECES; pp += NT_) {
+          const int row = pp / (DP / 8), col = 8 * (pp % (DP / 8));
+          if (row < nv)
+            __builtin_nontemporal_store(*reinterpret_cast<const la_bf16::u32x4*>(sQ[gg] + row * LQ + col),
+                                        reinterpret_cast<la_bf16::u32x4*>(out + ((bh * R + gg) * n + t0 + row) * DP + col));
+        }
+      }
+      __syncthreads();  // the output tiles are read before the next chunk's query tiles overwrite them
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < R; ++gg) {
+#pragma unroll
+        for (int pp = tid; pp < PIECES; pp += NT_) {
+          const int row = pp / (DP / 8), col = 8 * (pp % (DP / 8));
+          if (row < nv)
+            __builtin_nontemporal_store(*reinterpret_cast<const la_bf16::u32x4*>(sO[gg] + row * LQ + col),
+                                        reinterpret_cast<la_bf16::u32x4*>(out + ((bh * R + gg) * n + t0 + row) * DP + col));
+        }
       }
     }
   }
@@ -1678,7 +1717,7 @@ int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) tr = vec;
   if constexpr (std::is_same<T, float>::value && DP == 64) s32 = vec && a.n <= la_internal::kFwd32MaxN;
   if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) px = vec && q && out && R == 1;
-  const bool gq = tr && q && out && (R == 1 || R == 2 || R == 4);
+  const bool gq = tr && q && out && (R == 1 || R == 2 || R == 4 || R == 8);
   if (tr) {
     if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32)
       k_state_tr<PM><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, p.nchunks, p.G, p.nseg, states);
@@ -1709,8 +1748,11 @@ int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
       else if (R == 2)
         k_out_gqa<2, PM><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
                                                                          F, p.nseg, states);
-      else
+      else if (R == 4)
         k_out_gqa<4, PM><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
+                                                                         F, p.nseg, states);
+      else
+        k_out_gqa<8, PM><<<dim3((unsigned)(nbh * nseg_o)), 512, 0, st>>>(qq, k, v, out, a.n, p.nchunks, GO, nseg_o,
                                                                          F, p.nseg, states);
       return (int)hipGetLastError();
     }

@@ -522,6 +522,26 @@ def test_causal_mha_d128_output_kernel(gpu, phi, shape):
     np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-2, atol=1e-2 * np.abs(Sr).max())
 
 
+@pytest.mark.parametrize("phi", ["relu1", "elu1", "features"])
+@pytest.mark.parametrize("shape", [(1, 8, 1, 300), (2, 16, 2, 1000), (1, 16, 2, 12000)],
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_n%d" % c)
+def test_causal_gqa_r8_d128_output_kernel(gpu, phi, shape):
+    """bf16, d = 128, eight query heads per key/value head: the grouped-heads
+    output kernel with one wave per query head, its output tiles over the
+    query tiles; every row against the oracle, and the final state.  With
+    caller-applied features the inputs are softplus of Gaussian rows."""
+    B, Hq, Hkv, n = shape
+    q, k, v, _ = li.qkv(B, Hq, Hkv, n, 128, li.BF16, seed=37, scaled=True)
+    if phi == "features":
+        sp = lambda x: np.log1p(np.exp(x))
+        q, k = (li.as_dtype(sp(li.to_f32(x)).astype(np.float32), li.BF16) for x in (q, k))
+    out, S, z = gpu.la_causal_forward(dev(q), dev(k), dev(v), want_state=True, phi=phi)
+    ref, Sr, zr = oracle.causal(q, k, v, want_state=True, phi=phi)
+    check(host(out), ref, li.BF16, f"causal GQA R8 d128 {phi} B{B} Hq{Hq} Hkv{Hkv} n{n}")
+    np.testing.assert_allclose(z.cpu().numpy(), zr, rtol=1e-2)
+    np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-2, atol=1e-2 * np.abs(Sr).max())
+
+
 def test_single_launch_matches_three_launch_path(gpu):
     """The same inputs through chunk 64 (single launch) and chunk 32 (three
     launches) agree to bf16 rounding, and the workspace can be shared."""
