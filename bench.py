@@ -76,6 +76,10 @@ WORKLOADS = {
     "backward": dict(form="backward", B=8, Hq=8, Hkv=8, n=2048, d=64, dt="bf16", scaled=True, steps=50),
     # grouped query heads at d = 64 (four per key/value head) on the single-launch kernel
     "gqa_d64": dict(form="causal", B=4, Hq=16, Hkv=4, n=2048, d=64, dt="bf16", chunk=64, scaled=True, steps=200),
+    # d = 128 with one and with eight query heads per key/value head
+    "mha_d128": dict(form="causal", B=8, Hq=8, Hkv=8, n=2048, d=128, dt="bf16", chunk=0, scaled=True, steps=100),
+    "gqa_r8_d128": dict(form="causal", B=2, Hq=32, Hkv=4, n=8192, d=128, dt="bf16", chunk=0, scaled=True,
+                        steps=100),
 }
 
 DESCRIPTIONS = {
@@ -96,6 +100,8 @@ DESCRIPTIONS = {
     "causal_features": "causal normalised linear attention on caller-applied features (softplus), bf16",
     "backward": "gradients dQ, dK, dV of the causal form (phi=relu+1), bf16 in, fp32 products",
     "gqa_d64": "causal normalised linear attention, four query heads per key/value head, d 64, bf16",
+    "mha_d128": "causal normalised linear attention, one query head per key/value head, d 128, bf16",
+    "gqa_r8_d128": "causal normalised linear attention, eight query heads per key/value head, d 128, bf16",
 }
 
 # The packed-sequence workload's lengths: 16 sequences drawn uniformly from
