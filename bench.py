@@ -220,6 +220,18 @@ def tokens_heads(w):
     return w["B"] * w["Hq"] * w["n"]
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
     """Time the untuned oracle on a bounded sample of the workload: slices of
     the batch (causal, non-causal, prefix), the first tokens of every head
@@ -250,7 +262,7 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
         return {"value": steps * B * Hq / el, "unit": "tokens*heads/s", "cores": min(threads, B * Hkv),
                 "kind": "oracle",
                 "sample": f"{steps} decode steps on the whole batch (B={B} Hq={Hq} Hkv={Hkv} d={d}), "
-                          f"fp64 oracle, {el:.1f} s"}
+                          f"fp64 oracle, {el:.1f} s", "cpu": cpu_model()}
     B, Hq, Hkv, n, d = w["B"], w["Hq"], w["Hkv"], w["n"], w["d"]
     if form == "causal" and B * Hkv < threads:
         # long context: the first n_s tokens of every head (the causal output of
@@ -303,7 +315,7 @@ def cpu_baseline(w, q, k, v, m=None, S=None, z=None, budget_s=12.0):
         reps += 1
         el = time.perf_counter() - t0
     return {"value": reps * per / el, "unit": "tokens*heads/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} oracle calls on {what}, fp64, {el:.1f} s"}
+            "sample": f"{reps} oracle calls on {what}, fp64, {el:.1f} s", "cpu": cpu_model()}
 
 
 def run(name, args):
@@ -444,6 +456,23 @@ def run(name, args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
 
+    # the per-call distribution, from a separate run with an event pair around
+    # every call (the events add their own gaps, so it is not the headline)
+    ndist = min(steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ndist)]
+    torch.cuda._sleep(2_000_000)
+    for i, (ea, eb) in enumerate(evs):
+        ea.record(stream)
+        step(warmup + steps + i)
+        eb.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(ea.elapsed_time(eb) * 1e3 for ea, eb in evs)
+
+    def pct(p):
+        return per_call[min(len(per_call) - 1, int(round(p * (len(per_call) - 1))))]
+
+    dist = {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9), "calls": ndist, "unit": "us"}
+
     nbytes = algorithmic_bytes(w)
     flops = algorithmic_flops(w)
     achieved = nbytes / (ms * 1e-3) / 1e9
@@ -490,6 +519,7 @@ def run(name, args):
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,
+        "per_call_us": dist,
         "cpu_baseline": None,
     }
     if not args.no_cpu:
