@@ -151,7 +151,12 @@ __global__ __launch_bounds__(NT) void k_state(const T* __restrict__ k, const T* 
 // no feature-major copies are written.  Wave w owns state column block w
 // (all four row blocks): the column sums of V its blocks need and z of rows
 // 32 w .. are dot2 sums over fragments it reads anyway.
-constexpr int STR_RS = 128 + 16;  // tile row stride (bf16): rows 8 dwords apart mod 64 banks
+// Tile row stride (bf16): 80 dwords, so that the four rows and two 16-column
+// halves a half-wave of ds_read_b64_tr_b16 touches fall in eight distinct
+// 8-bank groups (rows 16 banks apart).  At 72 dwords (rows 8 banks apart) a
+// row's second half shares banks with the next row's first: an LDS probe
+// of the read measured 4.0 cycles per instruction against 2.0.
+constexpr int STR_RS = 128 + 32;
 // PM: relu + 1 (relu(K) in the tiles, the ones part added at the end) or
 // ELU + 1 (phi(K) in the tiles, rows past the end 0).
 template <int PM>
