@@ -353,6 +353,8 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   __shared__ __attribute__((aligned(16))) float sQ[QG * RK];
   __shared__ __attribute__((aligned(16))) float sS[16 * 64 * 4];  // S in operand order
   __shared__ __attribute__((aligned(16))) float sz[FD];            // z_prev (CS)
+  __shared__ int sI[QG];  // the group's query rows
+  __shared__ int sM[QG];  // and their mask values, clamped into [0, n - 1]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   if constexpr (!CS) {  // this batch's mask, buckets and permutation (one per batch, or one shared)
@@ -362,9 +364,12 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
     m += mb * n;
   }
   // bucket c's first position, and the query row at a position
+  // (boff is read through the constant address space: the same value for
+  // every lane, so it comes in by scalar loads, which wait on a counter of
+  // their own instead of on every vector load and store in flight)
   auto bo = [&](int64_t c) -> int64_t {
     if constexpr (CS) return c * C < n ? c * C : n;
-    else return boff[c];
+    else return ((const __attribute__((address_space(4))) int*)boff)[c];
   };
   auto qrow = [&](int64_t i) -> int64_t {
     if constexpr (CS) return i;
@@ -407,8 +412,13 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   const int64_t c0 = seg * G, c1 = (c0 + G < nchunks) ? c0 + G : nchunks;
 
   // next chunk's K and V rows (piece u: row (tid + NT_ u) / 16, features
-  // 4 ((tid + NT_ u) % 16)), and the next query group's rows
+  // 4 ((tid + NT_ u) % 16)), and the next query group's rows with their
+  // query indexes and mask values
   f32x4 kr[KVP], vr[KVP], qraw[4];
+  int qix[4];       // query row of piece u's group row
+  int64_t mraw[4];  // its mask value (prefix form)
+  int pn[4];        // perm entries of the group after the one being fetched
+  int qok = 0;      // bit u: piece u's row is a query of the fetched group
   auto fetch_kv = [&](int64_t c) {
 #pragma unroll
     for (int u = 0; u < KVP; ++u) {
@@ -419,28 +429,99 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
     }
   };
   auto groups_of = [&](int64_t c) -> int { return (int)((bo(c + 1) - bo(c) + QG - 1) / QG); };
-  auto fetch_q_after = [&](int64_t c, int grp) {  // rows of the query group after (c, grp), if any
-    int64_t cc = c;
-    int gg = grp + 1;
+  auto after = [&](int64_t& cc, int& gg) {  // the query group after (cc, gg); cc == c1 past the last
+    ++gg;
     while (cc < c1 && gg >= groups_of(cc)) {
       ++cc;
       gg = 0;
     }
-    if (cc >= c1) return;
-    const int64_t s0 = bo(cc) + (int64_t)QG * gg, e0 = bo(cc + 1);
+  };
+  // perm entries of group (cc, gg)'s rows.  They are requested one group
+  // ahead of the rows they index: a gather that waited for its own perm
+  // entries would wait for every load and store in flight (loads and
+  // stores share one counter on this GPU), and with them for the next
+  // chunk's K and V tiles (measured: 148 / 185 against 136 / 164 us per
+  // call at fp32 B4 H8 n8192, m = arange / uniform, with no perm reads).
+  // Rows past the group's end take its last entry (a group holds at least
+  // one query): an unconditional load, whose value nothing reads before the
+  // next wait (a choice between the loaded value and a constant would be
+  // made, and waited for, at once); those rows are masked where used.
+  // Past the walk's last group the loads take entry 0 (never used), so
+  // that the registers are loaded on every path: a path without the loads
+  // would have the compiler move the loaded values at the join, and wait.
+  auto fetch_perm = [&](int64_t cc, int gg) {
+    int64_t s0 = 0, e0 = 1;
+    if (cc < c1) {
+      s0 = bo(cc) + (int64_t)QG * gg;
+      e0 = bo(cc + 1);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = (tid + NT_ * u) >> 4;
+      pn[u] = (int)qrow(s0 + row < e0 ? s0 + row : e0 - 1);
+    }
+  };
+  auto fetch_q_after = [&](int64_t c, int grp) {  // rows of the query group after (c, grp), if any
+    int64_t cc = c;
+    int gg = grp;
+    after(cc, gg);
+    int64_t s0 = 0, e0 = 0;  // past the last group every row is masked (the same code path, as above)
+    if (cc < c1) {
+      s0 = bo(cc) + (int64_t)QG * gg;
+      e0 = bo(cc + 1);
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
-      qraw[u] = s0 + row < e0 ? *reinterpret_cast<const f32x4*>(qh + qrow(s0 + row) * FD + col)
-                              : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (CS && s0 + row < e0) qraw[u] = phi4(qraw[u]);
+      const bool ok = s0 + row < e0;
+      qix[u] = pn[u];
+      qraw[u] = ok ? *reinterpret_cast<const f32x4*>(qh + (int64_t)pn[u] * FD + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      qok = ok ? (qok | (1 << u)) : (qok & ~(1 << u));
+      if constexpr (!CS) mraw[u] = ok ? m[pn[u]] : 0;
     }
+    after(cc, gg);
+    fetch_perm(cc, gg);
   };
   if (c0 < c1) {
     fetch_kv(c0);
+    int64_t cc = c0;
+    int gg = -1;
+    after(cc, gg);
+    fetch_perm(cc, gg);
     fetch_q_after(c0, -1);
   }
+  // Everything requested so far has arrived before the walk starts.  Left
+  // out, the state registers' first loads would still count as pending at
+  // every chunk's S store, whose wait would then also take in the next
+  // chunk's K and V rows requested just before it.
+  __builtin_amdgcn_s_waitcnt(0);
 
+  // the fetched query group's rows into sQ, their query rows and mask
+  // values into sI and sM
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
+      // (phi is applied here, not as the rows arrive: using a loaded value
+      // waits for it)
+      *reinterpret_cast<f32x4*>(sQ + row * RK + col) = (CS && ((qok >> u) & 1)) ? phi4(qraw[u]) : qraw[u];
+      if (col == 0) {
+        sI[row] = qix[u];
+        int64_t mi = qix[u];
+        if constexpr (!CS) {
+          mi = mraw[u];
+          mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);  // same clamp as the bucket sort
+        }
+        sM[row] = (int)mi;
+      }
+    }
+  };
+
+  // Every wait for fetched data (staging into LDS) is a wait for all loads
+  // and stores in flight, so each chunk and query group stages what it needs
+  // before it requests the next one's rows: the chunk's K and V tiles and
+  // its first group's queries together, then the next chunk's tiles and the
+  // next group's rows go out.
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int ngroups = groups_of(c);
@@ -462,30 +543,22 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
         *reinterpret_cast<f32x4*>(sS + (blk * 64 + (lane ^ blk)) * 4) = accS[bb];
       }
     }
-    __syncthreads();  // tiles and S visible
+    __syncthreads();  // tiles, S and the first group's rows visible
     if (ngroups == 0 && owner) state_update();
 
     for (int grp = 0; grp < ngroups; ++grp) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pc = tid + NT_ * u, row = pc >> 4, col = 4 * (pc & 15);
-        *reinterpret_cast<f32x4*>(sQ + row * RK + col) = qraw[u];
+      {
+        stage_q();
+        fetch_q_after(c, grp);
+        __syncthreads();  // the group's query rows visible
       }
-      fetch_q_after(c, grp);
-      __syncthreads();  // the group's query rows visible
       if (grp == 0 && owner) state_update();
       const int64_t i0 = bo(c) + (int64_t)QG * grp + 16 * w;  // this wave's first query (position in perm)
       const int64_t e0 = bo(c + 1);
       if (i0 < e0) {
         const bool valid = i0 + mm < e0;
-        const int qi = valid ? (int)qrow(i0 + mm) : 0;
-        int64_t mi;
-        if constexpr (CS) {
-          mi = qi;
-        } else {
-          mi = valid ? m[qi] : 0;
-          mi = mi < 0 ? 0 : (mi >= n ? n - 1 : mi);  // same clamp as the bucket sort
-        }
+        const int qi = valid ? sI[16 * w + mm] : 0;
+        const int64_t mi = valid ? sM[16 * w + mm] : 0;
         const int limit = (int)(mi - t0);
         f32x4 qo[4];
 #pragma unroll
