@@ -337,7 +337,7 @@ constexpr int64_t kGqaOutGroups = LA_GQA_OUT_GROUPS;
 #endif
 constexpr int64_t kPrefixOutGroups = LA_PREFIX_OUT_GROUPS;
 template <int NWV, bool CS = false, int PM = PM_ID>
-__global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) void k_out_prefix32(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ v, float* __restrict__ out, int64_t n,
                                                       int64_t nchunks, int64_t G, int64_t nseg, int64_t F,
                                                       int64_t nseg_ws, const float* __restrict__ ws,
@@ -355,6 +355,7 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
   __shared__ __attribute__((aligned(16))) float sz[FD];            // z_prev (CS)
   __shared__ int sI[QG];  // the group's query rows
   __shared__ int sM[QG];  // and their mask values, clamped into [0, n - 1]
+  __shared__ __attribute__((aligned(16))) float sP[2 * 4 * 64 * 4];  // shared score blocks (partial groups)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, mm = lane & 15, kq = lane >> 4;
   const int64_t bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
   if constexpr (!CS) {  // this batch's mask, buckets and permutation (one per batch, or one shared)
@@ -553,9 +554,60 @@ __global__ __launch_bounds__(64 * NWV) void k_out_prefix32(const float* __restri
         __syncthreads();  // the group's query rows visible
       }
       if (grp == 0 && owner) state_update();
-      const int64_t i0 = bo(c) + (int64_t)QG * grp + 16 * w;  // this wave's first query (position in perm)
+      const int64_t g0 = bo(c) + (int64_t)QG * grp;  // the group's first position in perm
+      const int64_t i0 = g0 + 16 * w;                 // this wave's first query
       const int64_t e0 = bo(c + 1);
-      if (i0 < e0) {
+      // the group's 16-query blocks; fewer than one per wave (the last group
+      // of a bucket, as a rule) and the waves share the blocks instead
+      const int nbk = (int)(((e0 - g0 < QG ? e0 - g0 : QG) + 15) / 16);
+      if (!CS && nbk < NWV) {
+        // Block by block: wave w forms the masked scores of key block w
+        // and leaves them in sP (its accumulator as the lane's float4), then
+        // forms output features 16 w .. 16 w + 15 of the block's queries
+        // from S and all four key blocks' scores: 48 MFMAs per wave and
+        // block instead of 192 on one wave while the others wait.  sP has
+        // two buffers: a wave writes block qb + 2's scores only after every
+        // wave has passed block qb + 1's barrier, that is, after its reads
+        // of block qb's.
+        static_assert(NWV == 4, "one key block and one feature block per wave");
+        for (int qb = 0; qb < nbk; ++qb) {
+          const int row = 16 * qb + mm;
+          const bool valid = g0 + row < e0;
+          const int limit = valid ? (int)(sM[row] - t0) : -1;
+          f32x4 qo[4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) qo[tt] = *reinterpret_cast<const f32x4*>(sQ + row * RK + 16 * tt + 4 * kq);
+          f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 ko = *reinterpret_cast<const f32x4*>(sK + (16 * w + mm) * RK + 16 * tt + 4 * kq);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(ko[jj], qo[tt][jj], sc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) sc[rr] = (16 * w + 4 * kq + rr <= limit) ? sc[rr] : 0.0f;
+          f32x4* pb = reinterpret_cast<f32x4*>(sP) + (qb & 1) * 4 * 64;
+          pb[w * 64 + lane] = sc;
+          f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {  // S^T Q^T for this wave's features
+            const int blk = w * 4 + tt;
+            const f32x4 so = *reinterpret_cast<const f32x4*>(sS + (blk * 64 + (lane ^ blk)) * 4);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) o = __builtin_amdgcn_mfma_f32_16x16x4f32(so[jj], qo[tt][jj], o, 0, 0, 0);
+          }
+          __syncthreads();  // the block's four score blocks in sP
+#pragma unroll
+          for (int kb = 0; kb < C / 16; ++kb) {  // V^T P^T over the chunk's keys
+            const f32x4 p = pb[kb * 64 + lane];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              o = __builtin_amdgcn_mfma_f32_16x16x4f32(sV[(16 * kb + 4 * kq + rr) * RV + 16 * w + mm], p[rr], o, 0, 0, 0);
+          }
+          if (valid)
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(oh + (int64_t)sI[row] * FD + 16 * w + 4 * kq));
+        }
+      } else if (i0 < e0) {
         const bool valid = i0 + mm < e0;
         const int qi = valid ? sI[16 * w + mm] : 0;
         const int64_t mi = valid ? sM[16 * w + mm] : 0;
