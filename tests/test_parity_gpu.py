@@ -182,6 +182,23 @@ def test_prefix_f32_d64_query_groups(gpu, kind, shape):
     check(g, oracle.prefix_mask(q, k, v, m), li.F32, f"prefix {kind} B{B} H{H} n{n} d64 f32")
 
 
+def test_prefix_f32_d64_bucket_sizes_every_row(gpu):
+    """fp32, d = 64, chunk 64, a mask built for its bucket sizes (queries per
+    chunk of keys): empty buckets, single queries, whole and partial 16-query
+    blocks, groups of one to three blocks (which the four waves share block by
+    block) and of four, and buckets of several groups ending in each of those.
+    Every row of two batches and two heads against the oracle."""
+    sizes = [5, 16, 21, 37, 48, 64, 70, 96, 130, 3, 0, 50, 200, 100, 90, 94]
+    n, C = 64 * len(sizes), 64
+    assert sum(sizes) == n
+    rng = np.random.default_rng(21)
+    m = np.concatenate([rng.integers(C * c, C * c + C, size=cnt) for c, cnt in enumerate(sizes)]).astype(np.int64)
+    m = m[rng.permutation(n)]  # which query lands in which bucket: arbitrary
+    q, k, v, _ = li.qkv(2, 2, 2, n, 64, li.F32, seed=22, scaled=True)
+    g = host(gpu.la_prefix_mask_forward(dev(q), dev(k), dev(v), dev(m), chunk=64))
+    check(g, oracle.prefix_mask(q, k, v, m), li.F32, "prefix f32 d64, chosen bucket sizes")
+
+
 @pytest.mark.parametrize("phi", ["relu1", "elu1"])
 @pytest.mark.parametrize("shape", [(1, 4, 2, 1500), (2, 8, 2, 700), (4, 16, 2, 600), (1, 64, 8, 300), (3, 6, 3, 513)],
                          ids=lambda c: "B%d_Hq%d_Hkv%d_n%d" % c)
