@@ -681,7 +681,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             __builtin_nontemporal_store(o[bb], reinterpret_cast<f32x4*>(oh + (int64_t)qi * FD + 16 * bb + 4 * kq));
         }
       }
-      __syncthreads();  // the group's rows are no longer read
+      // the group's rows are no longer read (after a chunk's last group the
+      // barrier at the chunk's end serves)
+      if (grp + 1 < ngroups) __syncthreads();
     }
     if (CS && tid < FD) {  // z_prev(c + 1): add this chunk's phi(K) column sums (rows past n are 0)
 #pragma unroll 8
