@@ -1492,7 +1492,7 @@ __global__ __launch_bounds__(1024) void k_bucket(const int64_t* __restrict__ m, 
 // that a head's rows stay below 2^31 bytes (the resources' record count).
 union State32Lds {
   struct {
-    f32x4 acc[8][16][64];  // entry (4 j + j', lane l), float rr: S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']
+    f32x4 acc[4][16][64];  // entry (4 j + j', lane l), float rr: S[16 (l / 16) + 4 rr + j][4 (l % 16) + j']
     f32x4 z[8][16];        // z[4 m .. 4 m + 3] of each wave
   } s;
   struct {
@@ -1504,12 +1504,12 @@ union State32Lds {
 // PM: the identity (prefix form), relu + 1 (split) or ELU + 1 (keys past the
 // segment contribute 0, not phi(0) = 1).
 template <int PM>
-__global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, const float* __restrict__ v, int64_t n,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_state32(const float* __restrict__ k, const float* __restrict__ v, int64_t n,
                                                  int64_t nchunks, int C, int64_t G, int64_t nseg,
                                                  float* __restrict__ ws, const int64_t* __restrict__ m,
                                                  int* __restrict__ boff, int* __restrict__ perm, int64_t nmask,
                                                  la_internal::Ctl* ctl) {
-  constexpr int FD = 64, TW = 32, NW8 = 8;
+  constexpr int FD = 64, TW = 16, NW8 = 8;
   __shared__ State32Lds L;
   int64_t sb = blockIdx.x;  // state block
   if (m) {
@@ -1580,20 +1580,38 @@ __global__ __launch_bounds__(512) void k_state32(const float* __restrict__ k, co
     zr[j] += __shfl_xor(zr[j], 32);
     zr[j] += PM == PM_RELU1 ? (float)nkeys : 0.0f;  // the ones of phi(K), real keys only
   }
+  // the segment's aggregate: waves 4-7 hand their results to waves 0-3
+  // (w + 4 into w), whose sums are then added in wave order, and taken from
+  // accumulator order to S row-major (64 KB of LDS, so that two workgroups
+  // share a CU)
+  if (w >= 4) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int jp = 0; jp < 4; ++jp) L.s.acc[w][4 * j + jp][lane] = acc[j][jp];
+      for (int jp = 0; jp < 4; ++jp) L.s.acc[w - 4][4 * j + jp][lane] = acc[j][jp];
+  }
   if (kq == 0) L.s.z[w][mm] = zr;
   __syncthreads();
-  // the segment's aggregate: the waves' results summed in wave order, then
-  // from accumulator order to S row-major
+  if (w < 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) acc[j][jp] += L.s.acc[w][4 * j + jp][lane];
+  }
+  __syncthreads();
+  if (w < 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) L.s.acc[w][4 * j + jp][lane] = acc[j][jp];
+  }
+  __syncthreads();
   float* dst = ws + (bh * (nseg + 1) + seg) * slot_elems(FD);
   const f32x4* la = &L.s.acc[0][0][0];
   for (int e = tid; e < 16 * 64; e += 512) {
     f32x4 sm = la[e];
 #pragma unroll
-    for (int u = 1; u < NW8; ++u) sm += la[u * 16 * 64 + e];
+    for (int u = 1; u < 4; ++u) sm += la[u * 16 * 64 + e];
     const int b = e >> 6, l = e & 63, j = b >> 2, jp = b & 3, m4 = l & 15, kk = l >> 4;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) dst[(16 * kk + 4 * rr + j) * FD + 4 * m4 + jp] = sm[rr];
