@@ -243,36 +243,66 @@ __global__ __launch_bounds__(NT) void k_state_tr(const bf16* __restrict__ k, con
 // Only the prefixes of segments s with s % F == 0 are stored (the output
 // launch that follows starts a workgroup at every F-th segment); the total
 // always is.
+// V consecutive state elements per thread (V = 1 or 4; with 4, 16-byte loads
+// and stores: a quarter of the threads and instructions; the slot size
+// DP (DP + 1) is a multiple of four and the workspace and its slots are
+// 16-byte aligned).  Each element is summed in segment order either way.
+template <int V>
 __global__ __launch_bounds__(NT) void k_scan(float* __restrict__ ws, int64_t nseg, int DP, int d,
                                              float* __restrict__ S_final, float* __restrict__ z_final, int64_t F) {
-  const int64_t E = slot_elems(DP);
+  using vec = typename std::conditional<V == 4, f32x4, float>::type;
+  const int64_t E = slot_elems(DP), EV = E / V;
   const int64_t bh = blockIdx.x;
-  const int64_t e = (int64_t)blockIdx.y * NT + threadIdx.x;
-  if (e >= E) return;
-  float* base = ws + bh * (nseg + 1) * E + e;
-  float run = 0.0f;
+  const int64_t ev = (int64_t)blockIdx.y * NT + threadIdx.x;
+  if (ev >= EV) return;
+  vec* base = reinterpret_cast<vec*>(ws + bh * (nseg + 1) * E) + ev;
+  vec run = vec{};
   // segments in blocks of 16: all loads of a block are issued before its
   // stores (which the compiler could not move past them), in a fixed order
   constexpr int BLK = 16;
   for (int64_t s0 = 0; s0 < nseg; s0 += BLK) {
-    float x[BLK];
+    vec x[BLK];
 #pragma unroll
-    for (int u = 0; u < BLK; ++u) x[u] = (s0 + u < nseg) ? base[(s0 + u) * E] : 0.0f;
+    for (int u = 0; u < BLK; ++u) x[u] = (s0 + u < nseg) ? base[(s0 + u) * EV] : vec{};
 #pragma unroll
     for (int u = 0; u < BLK; ++u) {
       if (s0 + u < nseg) {
-        if ((s0 + u) % F == 0) base[(s0 + u) * E] = run;
+        if ((s0 + u) % F == 0) base[(s0 + u) * EV] = run;
         run += x[u];
       }
     }
   }
-  base[nseg * E] = run;
-  if (e < (int64_t)DP * DP) {
-    const int a = (int)(e / DP), b = (int)(e % DP);
-    if (S_final && a < d && b < d) S_final[bh * d * d + (int64_t)a * d + b] = run;
+  base[nseg * EV] = run;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int64_t e = V * ev + j;
+    float r;
+    if constexpr (V == 4) r = run[j];
+    else r = run;
+    if (e < (int64_t)DP * DP) {
+      const int a = (int)(e / DP), b = (int)(e % DP);
+      if (S_final && a < d && b < d) S_final[bh * d * d + (int64_t)a * d + b] = r;
+    } else {
+      const int a = (int)(e - (int64_t)DP * DP);
+      if (z_final && a < d) z_final[bh * d + a] = r;
+    }
+  }
+}
+
+// k_scan over nunits units: four elements per thread when that still gives
+// at least 64K threads (four waves per CU); with fewer units one element per
+// thread, whose four times as many waves cover the serial chain's round trips
+// (d128 B8 H8 n2048: 77.0 -> 68.6 us per call with four; the long-context GQA
+// shape, eight units, and the fp32 prefix form, 32, measured slower with four)
+void launch_k_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S_final, float* z_final,
+                   int64_t F, hipStream_t st) {
+  const int64_t E = slot_elems(DP);
+  if (nunits * (E / 4) >= 65536) {
+    k_scan<4><<<dim3((unsigned)nunits, (unsigned)((E / 4 + NT - 1) / NT)), NT, 0, st>>>(ws, nseg, DP, d, S_final,
+                                                                                       z_final, F);
   } else {
-    const int a = (int)(e - (int64_t)DP * DP);
-    if (z_final && a < d) z_final[bh * d + a] = run;
+    k_scan<1><<<dim3((unsigned)nunits, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(ws, nseg, DP, d, S_final, z_final,
+                                                                                   F);
   }
 }
 
@@ -1891,9 +1921,7 @@ int run_causal(const la_internal::Fwd& a, const la_internal::Plan& p) {
   int64_t F = gq ? nbh * p.nseg / (R == 1 ? 2 * kGqaOutGroups : kGqaOutGroups)
                  : px ? nbh * p.nseg / kPrefixOutGroups : 1;
   if (F < 1) F = 1;
-  const int64_t E = slot_elems(DP);
-  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, a.S_final,
-                                                                          a.z_final, F);
+  launch_k_scan(states, nbh, p.nseg, DP, (int)a.d, a.S_final, a.z_final, F, st);
   if (!(q && out)) return (int)hipGetLastError();
   const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
   if constexpr (std::is_same<T, bf16>::value && DP == 128 && C == 32) {
@@ -1961,9 +1989,7 @@ int run_prefix(const la_internal::Fwd& a, const la_internal::Plan& p) {
   int64_t F = px ? nbh * p.nseg / kPrefixOutGroups : 1;
   if (F < 1) F = 1;
   const int64_t GO = p.G * F, nseg_o = (p.nchunks + GO - 1) / GO;
-  const int64_t E = slot_elems(DP);
-  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr,
-                                                                          nullptr, F);
+  launch_k_scan(states, nbh, p.nseg, DP, (int)a.d, nullptr, nullptr, F, st);
   if constexpr (std::is_same<T, float>::value && DP == 64 && C == 64) {
     if (px) {
       k_out_prefix32<PX_NWV><<<dim3((unsigned)(nbh * nseg_o)), 64 * PX_NWV, 0, st>>>(
@@ -2005,8 +2031,7 @@ int run_forward(const la_internal::Fwd& a, const la_internal::Plan& p) {
   else
     k_state<T, DP, C, PM_RELU1><<<dim3((unsigned)(nbh * p.nseg)), NT, 0, st>>>(k, v, a.n, (int)a.d, vec, p.nchunks, p.G,
                                                                               p.nseg, states);
-  const int64_t E = slot_elems(DP);
-  k_scan<<<dim3((unsigned)nbh, (unsigned)((E + NT - 1) / NT)), NT, 0, st>>>(states, p.nseg, DP, (int)a.d, nullptr, nullptr, 1);
+  launch_k_scan(states, nbh, p.nseg, DP, (int)a.d, nullptr, nullptr, 1, st);
   // query runs: about 1024 workgroups in total for 2-byte inputs (several per
   // CU keep more query tiles in flight), about 256 for 4-byte inputs (longer
   // runs, each loading its next, twice as large, tile while it computes)
@@ -2130,9 +2155,7 @@ int launch_prefix(const Fwd& a, const Plan& p) { return dispatch(a, p, 2); }
 
 int launch_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float* S_final, float* z_final,
                 void* stream) {
-  const int64_t E = slot_elems(DP);
-  k_scan<<<dim3((unsigned)nunits, (unsigned)((E + NT - 1) / NT)), NT, 0, reinterpret_cast<hipStream_t>(stream)>>>(
-      ws, nseg, DP, d, S_final, z_final, 1);
+  launch_k_scan(ws, nunits, nseg, DP, d, S_final, z_final, 1, reinterpret_cast<hipStream_t>(stream));
   return (int)hipGetLastError();
 }
 
