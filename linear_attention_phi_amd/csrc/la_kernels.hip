@@ -313,7 +313,9 @@ void launch_k_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float
 // where S_prev(c) is the state before chunk c (the segment's exclusive prefix
 // plus the segment's earlier chunks) and the mask keeps key j for query i iff
 // j <= m_i.  The queries of bucket c go in groups of 16 NWV, one 16-query
-// block per wave, their rows gathered through perm and staged in LDS.  Operands
+// block per wave (in a group of fewer blocks than waves the waves share each
+// block instead: one key block's scores and one block of output features
+// each), their rows gathered through perm and staged in LDS.  Operands
 // (the contraction index k is lane / 16, the other index lane % 16):
 //   S^T  from LDS in operand order: entry (bb, tt, lane) is the float4 over
 //        jj of S[16 tt + 4 (lane / 16) + jj][16 bb + lane % 16], kept in
@@ -351,8 +353,9 @@ void launch_k_scan(float* ws, int64_t nunits, int64_t nseg, int DP, int d, float
 constexpr int PX_RS = 64 + 4;  // row stride (floats) of the LDS tiles
 // NWV waves per workgroup, queries per group QG = 16 NWV (one 16-query block
 // per wave); the state is owned by waves NWV - 4 .. NWV - 1, four tiles each.
-// Four waves (68.6 KB of LDS, so that two workgroups share a CU and cover
-// each other's barriers) measured 146.9 / 179.3 us at B4 H8 n8192 (m = arange
+// Four waves (69.4 KB of LDS, 77.3 KB with the prefix form's shared score
+// buffers, so that two workgroups share a CU and cover each other's
+// barriers) measured 146.9 / 179.3 us at B4 H8 n8192 (m = arange
 // / uniform) against 162.7 / 190.9 us for eight.
 constexpr int PX_NWV = 4;
 // Workgroups of the GQA output launch (one per CU): each walks the chunks of
